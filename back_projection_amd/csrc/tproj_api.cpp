@@ -1,0 +1,275 @@
+// Host C ABI of libtproj: argument checks, kernel selection and launches.
+// Declared in include/tproj.h; the operations are those of the torch-projectors
+// pages (3D->2D forward, 2D->3D back-projection, and their backward passes).
+#include "tproj.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+tp_status fail(tp_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return s;
+}
+
+tp_status ok() {
+  g_detail.clear();
+  return TP_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Pure check of the geometry (no GPU).
+tp_status check_geom(const tp_geom* g) {
+  if (!g) return fail(TP_E_NULL, "geometry pointer is NULL");
+  if (g->B < 1 || g->P < 1) return fail(TP_E_SHAPE, "B=%d and P=%d must be >= 1", g->B, g->P);
+  if (g->D < 2 || g->D > 1024 || (g->D & 1)) return fail(TP_E_SHAPE, "D=%d must be even and in [2, 1024]", g->D);
+  if (g->H < 2 || g->H > 4096 || (g->H & 1)) return fail(TP_E_SHAPE, "H=%d must be even and in [2, 4096]", g->H);
+  if (g->Bv != 1 && g->Bv != g->B) return fail(TP_E_SHAPE, "Bv=%d must be 1 or B=%d", g->Bv, g->B);
+  if (g->Br != 1 && g->Br != g->B) return fail(TP_E_SHAPE, "Br=%d must be 1 or B=%d", g->Br, g->B);
+  if (g->Bs != 0 && g->Bs != 1 && g->Bs != g->B) return fail(TP_E_SHAPE, "Bs=%d must be 0, 1 or B=%d", g->Bs, g->B);
+  if (g->interp != TP_LINEAR && g->interp != TP_CUBIC) return fail(TP_E_VALUE, "interp=%d is not 0 or 1", g->interp);
+  if (!std::isfinite(g->oversampling) || !(g->oversampling > 0.0f))
+    return fail(TP_E_VALUE, "oversampling=%g must be finite and > 0", (double)g->oversampling);
+  if (std::isnan(g->radius_cutoff)) return fail(TP_E_VALUE, "radius_cutoff is NaN");
+  const int64_t npose = (int64_t)g->B * g->P;
+  const int64_t nimg = npose * g->H * (g->H / 2 + 1);
+  if (npose > INT32_MAX / 2 || nimg > ((int64_t)1 << 40))
+    return fail(TP_E_SHAPE, "B*P=%lld poses / %lld pixels exceed the supported size", (long long)npose,
+                (long long)nimg);
+  return TP_OK;
+}
+
+tp_status check_shifts(const tp_geom* g, const float* shifts) {
+  if (shifts == nullptr && g->Bs != 0) return fail(TP_E_VALUE, "shifts is NULL but Bs=%d (must be 0)", g->Bs);
+  if (shifts != nullptr && g->Bs == 0) return fail(TP_E_VALUE, "shifts given but Bs=0");
+  return TP_OK;
+}
+
+tp_status check_ptr(const void* p, const char* name, size_t align) {
+  if (!p) return fail(TP_E_NULL, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(TP_E_VALUE, "%s is not %zu-byte aligned", name, align);
+  return TP_OK;
+}
+
+tp_status check_opt(const void* p, const char* name, size_t align) {
+  if (p && !aligned(p, align)) return fail(TP_E_VALUE, "%s is not %zu-byte aligned", name, align);
+  return TP_OK;
+}
+
+tproj::KGeom kgeom(const tp_geom* g) {
+  tproj::KGeom k;
+  k.B = g->B; k.P = g->P; k.Bv = g->Bv; k.Br = g->Br; k.Bs = g->Bs;
+  k.D = g->D; k.H = g->H; k.half = g->D / 2; k.W = g->D / 2 + 1; k.Wi = g->H / 2 + 1;
+  k.npix = g->H * k.Wi;
+  k.o = g->oversampling;
+  k.r2 = g->radius_cutoff < 0.0f ? -1.0f : g->radius_cutoff * g->radius_cutoff;
+  k.inv_h = 1.0f / (float)g->H;
+  return k;
+}
+
+int64_t vol_elems(const tp_geom* g) { return (int64_t)g->D * g->D * (g->D / 2 + 1); }
+int64_t img_elems(const tp_geom* g) { return (int64_t)g->B * g->P * g->H * (g->H / 2 + 1); }
+
+tp_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(TP_E_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+tp_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(TP_E_DEVICE, "no usable HIP device: %s", hipGetErrorString(e));
+  }
+  return TP_OK;
+}
+
+#define TRY(x)                      \
+  do {                              \
+    tp_status _s = (x);             \
+    if (_s != TP_OK) return _s;     \
+  } while (0)
+#define LAUNCH(x, what)                               \
+  do {                                                \
+    hipError_t _e = (x);                              \
+    if (_e != hipSuccess) return launched(_e, what);  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int tp_abi_version(void) { return TPROJ_ABI_VERSION; }
+
+const char* tp_status_string(tp_status s) {
+  switch (s) {
+    case TP_OK: return "ok";
+    case TP_E_NULL: return "required pointer is NULL";
+    case TP_E_SHAPE: return "invalid shape";
+    case TP_E_VALUE: return "invalid value";
+    case TP_E_DEVICE: return "no usable HIP device";
+    case TP_E_LAUNCH: return "kernel launch failed";
+    case TP_E_WORKSPACE: return "workspace too small";
+  }
+  return "unknown status";
+}
+
+const char* tp_last_error_detail(void) { return g_detail.c_str(); }
+
+tp_status tp_validate(const tp_geom* geom) {
+  TRY(check_geom(geom));
+  return ok();
+}
+
+size_t tp_workspace_size(const tp_geom* geom, int op) {
+  if (check_geom(geom) != TP_OK) return (size_t)-1;
+  if (op < TP_OP_PROJECT || op > TP_OP_BACKPROJECT_BACKWARD) return (size_t)-1;
+  return 0;
+}
+
+tp_status project_3d_to_2d(const tp_geom* geom, const void* vol, const float* rot, const float* shifts, void* out,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace; (void)ws_bytes;
+  TRY(check_geom(geom));
+  TRY(check_shifts(geom, shifts));
+  TRY(check_ptr(vol, "vol", 8));
+  TRY(check_ptr(rot, "rot", 4));
+  TRY(check_opt(shifts, "shifts", 4));
+  TRY(check_ptr(out, "out", 8));
+  TRY(check_device());
+  const tproj::KGeom k = kgeom(geom);
+  hipStream_t st = (hipStream_t)stream;
+  LAUNCH(tproj::launch_project(k, geom->interp, (const float2*)vol, rot, shifts, (float2*)out, st), "project");
+  return ok();
+}
+
+tp_status project_3d_to_2d_backward(const tp_geom* geom, const void* grad_out, const void* vol, const float* rot,
+                                    const float* shifts, void* grad_vol, float* grad_rot, float* grad_shifts,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace; (void)ws_bytes;
+  TRY(check_geom(geom));
+  TRY(check_shifts(geom, shifts));
+  TRY(check_ptr(grad_out, "grad_out", 8));
+  TRY(check_ptr(rot, "rot", 4));
+  TRY(check_opt(shifts, "shifts", 4));
+  TRY(check_opt(grad_vol, "grad_vol", 8));
+  TRY(check_opt(grad_rot, "grad_rot", 4));
+  TRY(check_opt(grad_shifts, "grad_shifts", 4));
+  if ((grad_rot || grad_shifts) && !vol) return fail(TP_E_NULL, "vol is NULL but rotation/shift grads are requested");
+  TRY(check_opt(vol, "vol", 8));
+  if (grad_shifts && !shifts) return fail(TP_E_NULL, "grad_shifts requested without shifts");
+  TRY(check_device());
+  const tproj::KGeom k = kgeom(geom);
+  hipStream_t st = (hipStream_t)stream;
+  if (grad_vol) {
+    LAUNCH(tproj::launch_zero((float*)grad_vol, 2 * vol_elems(geom) * geom->Bv, st), "zero grad_vol");
+    LAUNCH(tproj::launch_spread_atomic(k, geom->interp, (const float2*)grad_out, nullptr, rot, shifts,
+                                       (float2*)grad_vol, nullptr, st),
+           "spread grad_vol");
+  }
+  if (grad_rot || grad_shifts) {
+    if (grad_rot && geom->Br == 1 && geom->B > 1)
+      LAUNCH(tproj::launch_zero(grad_rot, 9 * (int64_t)geom->P, st), "zero grad_rot");
+    else if (grad_rot)
+      LAUNCH(tproj::launch_zero(grad_rot, 9 * (int64_t)geom->Br * geom->P, st), "zero grad_rot");
+    if (grad_shifts && geom->Bs == 1 && geom->B > 1)
+      LAUNCH(tproj::launch_zero(grad_shifts, 2 * (int64_t)geom->P, st), "zero grad_shifts");
+    LAUNCH(tproj::launch_rot_shift_grad(k, geom->interp, (const float2*)vol, nullptr, (const float2*)grad_out,
+                                        nullptr, rot, shifts, grad_rot, grad_shifts, st),
+           "rotation/shift grads");
+  }
+  return ok();
+}
+
+tp_status backproject_2d_to_3d(const tp_geom* geom, const void* images, const float* weights, const float* rot,
+                               const float* shifts, void* data_vol, float* weight_vol, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  (void)workspace; (void)ws_bytes;
+  TRY(check_geom(geom));
+  TRY(check_shifts(geom, shifts));
+  TRY(check_ptr(images, "images", 8));
+  TRY(check_ptr(rot, "rot", 4));
+  TRY(check_opt(shifts, "shifts", 4));
+  TRY(check_ptr(data_vol, "data_vol", 8));
+  if ((weights == nullptr) != (weight_vol == nullptr))
+    return fail(TP_E_NULL, "weights and weight_vol must both be given or both be NULL");
+  TRY(check_opt(weights, "weights", 4));
+  TRY(check_opt(weight_vol, "weight_vol", 4));
+  TRY(check_device());
+  const tproj::KGeom k = kgeom(geom);
+  hipStream_t st = (hipStream_t)stream;
+  LAUNCH(tproj::launch_zero((float*)data_vol, 2 * vol_elems(geom) * geom->Bv, st), "zero data_vol");
+  if (weight_vol) LAUNCH(tproj::launch_zero(weight_vol, vol_elems(geom) * geom->Bv, st), "zero weight_vol");
+  LAUNCH(tproj::launch_spread_atomic(k, geom->interp, (const float2*)images, weights, rot, shifts, (float2*)data_vol,
+                                     weight_vol, st),
+         "back-projection");
+  return ok();
+}
+
+tp_status backproject_2d_to_3d_backward(const tp_geom* geom, const void* grad_data_vol,
+                                        const float* grad_weight_vol, const void* images, const float* weights,
+                                        const float* rot, const float* shifts, void* grad_images,
+                                        float* grad_weights, float* grad_rot, float* grad_shifts, void* workspace,
+                                        size_t ws_bytes, void* stream) {
+  (void)workspace; (void)ws_bytes;
+  TRY(check_geom(geom));
+  TRY(check_shifts(geom, shifts));
+  TRY(check_ptr(grad_data_vol, "grad_data_vol", 8));
+  TRY(check_ptr(rot, "rot", 4));
+  TRY(check_opt(shifts, "shifts", 4));
+  TRY(check_opt(grad_weight_vol, "grad_weight_vol", 4));
+  TRY(check_opt(images, "images", 8));
+  TRY(check_opt(weights, "weights", 4));
+  TRY(check_opt(grad_images, "grad_images", 8));
+  TRY(check_opt(grad_weights, "grad_weights", 4));
+  TRY(check_opt(grad_rot, "grad_rot", 4));
+  TRY(check_opt(grad_shifts, "grad_shifts", 4));
+  if ((grad_rot || grad_shifts) && !images) return fail(TP_E_NULL, "images is NULL but rotation/shift grads are requested");
+  if (grad_rot && grad_weight_vol && !weights)
+    return fail(TP_E_NULL, "weights is NULL but grad_weight_vol and grad_rot are given");
+  if (grad_shifts && !shifts) return fail(TP_E_NULL, "grad_shifts requested without shifts");
+  TRY(check_device());
+  const tproj::KGeom k = kgeom(geom);
+  hipStream_t st = (hipStream_t)stream;
+  if (grad_images)
+    LAUNCH(tproj::launch_project(k, geom->interp, (const float2*)grad_data_vol, rot, shifts, (float2*)grad_images, st),
+           "grad_images");
+  if (grad_weights) {
+    if (grad_weight_vol)
+      LAUNCH(tproj::launch_project_real(k, geom->interp, grad_weight_vol, rot, grad_weights, st), "grad_weights");
+    else
+      LAUNCH(tproj::launch_zero(grad_weights, img_elems(geom), st), "zero grad_weights");
+  }
+  if (grad_rot || grad_shifts) {
+    if (grad_rot && geom->Br == 1 && geom->B > 1)
+      LAUNCH(tproj::launch_zero(grad_rot, 9 * (int64_t)geom->P, st), "zero grad_rot");
+    else if (grad_rot)
+      LAUNCH(tproj::launch_zero(grad_rot, 9 * (int64_t)geom->Br * geom->P, st), "zero grad_rot");
+    if (grad_shifts && geom->Bs == 1 && geom->B > 1)
+      LAUNCH(tproj::launch_zero(grad_shifts, 2 * (int64_t)geom->P, st), "zero grad_shifts");
+    const bool wch = grad_weight_vol != nullptr && weights != nullptr;
+    LAUNCH(tproj::launch_rot_shift_grad(k, geom->interp, (const float2*)grad_data_vol, wch ? grad_weight_vol : nullptr,
+                                        (const float2*)images, wch ? weights : nullptr, rot, shifts, grad_rot,
+                                        grad_shifts, st),
+           "rotation/shift grads");
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -93,29 +93,33 @@ def random_complex(rng, shape) -> np.ndarray:
 
 
 def noisy_blob_projections(rng, H: int, centres, sigma, amp, rots: np.ndarray, snr: float = 0.1,
-                           batch: int = 64) -> np.ndarray:
+                           batch: int = 64, device=None) -> np.ndarray:
     """rfft2 of noisy analytic projections of a blob volume: each rotation maps
     the blob centre c to (R^T c)_xy on the image, the z-integral of a Gaussian
     of width sigma and peak a is a 2D Gaussian of peak a*sqrt(2 pi)*sigma.
-    Gaussian noise with variance var(clean)/snr per image.  complex64
-    [n, H, H//2+1]."""
+    Gaussian noise (numpy-seeded) with variance var(clean)/snr per image.
+    The dense Gaussian sums run with torch on ``device`` (a GPU when present:
+    they are input preparation only).  complex64 [n, H, H//2+1]."""
+    if device is None:
+        device = "cuda" if torch.cuda.is_available() else "cpu"
     n = rots.shape[0]
     out = np.empty((n, H, H // 2 + 1), np.complex64)
-    c = torch.from_numpy(centres.astype(np.float32))
-    s = torch.from_numpy(sigma.astype(np.float32))
-    a2 = torch.from_numpy((amp * np.sqrt(2 * np.pi) * sigma).astype(np.float32))
-    grid = torch.arange(H, dtype=torch.float32) - H // 2
+    c = torch.from_numpy(centres.astype(np.float32)).to(device)
+    s = torch.from_numpy(sigma.astype(np.float32)).to(device)
+    a2 = torch.from_numpy((amp * np.sqrt(2 * np.pi) * sigma).astype(np.float32)).to(device)
+    grid = torch.arange(H, dtype=torch.float32, device=device) - H // 2
+    inv2s2 = 1.0 / (2 * s * s)
     for i0 in range(0, n, batch):
-        R = torch.from_numpy(rots[i0:i0 + batch])             # [b, 3, 3]
+        R = torch.from_numpy(rots[i0:i0 + batch]).to(device)   # [b, 3, 3]
         cp = torch.einsum("bji,nj->bni", R, c)                  # R^T c  -> [b, nb, 3]
-        gx = torch.exp(-(grid[None, :, None] - cp[:, None, :, 0]) ** 2 / (2 * s * s))   # [b, H, nb]
-        gy = torch.exp(-(grid[None, :, None] - cp[:, None, :, 1]) ** 2 / (2 * s * s))
-        img = torch.bmm(gy * a2, gx.transpose(1, 2).contiguous())                       # [b, H(y), H(x)]
+        gx = torch.exp(-torch.square(grid[None, :, None] - cp[:, None, :, 0]) * inv2s2)   # [b, H, nb]
+        gy = torch.exp(-torch.square(grid[None, :, None] - cp[:, None, :, 1]) * inv2s2)
+        img = torch.bmm((gy * a2).contiguous(), gx.transpose(1, 2).contiguous())       # [b, H(y), H(x)]
         var = img.var(dim=(1, 2), keepdim=True)
-        noise = torch.from_numpy(rng.standard_normal(tuple(img.shape), dtype=np.float32))
+        noise = torch.from_numpy(rng.standard_normal(tuple(img.shape), dtype=np.float32)).to(device)
         img = img + noise * torch.sqrt(var / snr)
         img = torch.fft.ifftshift(img, dim=(1, 2))
-        out[i0:i0 + batch] = torch.fft.rfft2(img).numpy()
+        out[i0:i0 + batch] = torch.fft.rfft2(img).cpu().numpy()
     return out
 
 

@@ -1,0 +1,136 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/tproj.h declares, and rejects bad arguments with the
+documented status codes before it enqueues anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import back_projection_amd as bp
+from back_projection_amd import build_lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tproj.h")
+
+TP_OK, TP_E_NULL, TP_E_SHAPE, TP_E_VALUE, TP_E_DEVICE, TP_E_LAUNCH, TP_E_WORKSPACE = range(7)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bp.LIB_PATH):
+        build_lib.build()
+    return bp.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_binding_symbols():
+    assert header_functions() == sorted(bp.HEADER_SYMBOLS)
+
+
+def test_library_exports_every_header_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", bp.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [f for f in header_functions() if f not in exported]
+    assert not missing, missing
+    for f in header_functions():
+        assert hasattr(L, f)
+
+
+def test_abi_version_and_strings(L):
+    assert L.tp_abi_version() == 1
+    for s in range(7):
+        assert L.tp_status_string(s)
+    assert L.tp_status_string(99) == b"unknown status"
+
+
+def geom(**kw):
+    d = dict(B=1, P=4, Bv=1, Br=1, Bs=0, D=16, H=16, interp=1, oversampling=1.0, radius_cutoff=-1.0)
+    d.update(kw)
+    return bp.Geom(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), TP_OK),
+    (dict(D=15), TP_E_SHAPE),
+    (dict(H=7), TP_E_SHAPE),
+    (dict(D=0), TP_E_SHAPE),
+    (dict(D=2048), TP_E_SHAPE),
+    (dict(P=0), TP_E_SHAPE),
+    (dict(B=2, Bv=3), TP_E_SHAPE),
+    (dict(B=2, Br=2, Bv=2, Bs=3), TP_E_SHAPE),
+    (dict(interp=2), TP_E_VALUE),
+    (dict(oversampling=0.0), TP_E_VALUE),
+    (dict(oversampling=float("inf")), TP_E_VALUE),
+    (dict(radius_cutoff=float("nan")), TP_E_VALUE),
+    (dict(B=3, Bv=1, Br=3, Bs=1), TP_OK),
+])
+def test_validate(L, kw, status):
+    g = geom(**kw)
+    assert L.tp_validate(ctypes.byref(g)) == status
+    if status != TP_OK:
+        assert L.tp_last_error_detail()
+
+
+def test_null_geometry(L):
+    assert L.tp_validate(None) == TP_E_NULL
+
+
+def test_workspace_size(L):
+    g = geom()
+    for op in range(4):
+        assert L.tp_workspace_size(ctypes.byref(g), op) == 0
+    assert L.tp_workspace_size(ctypes.byref(g), 7) == ctypes.c_size_t(-1).value
+    bad = geom(D=3)
+    assert L.tp_workspace_size(ctypes.byref(bad), 0) == ctypes.c_size_t(-1).value
+
+
+FAKE = ctypes.c_void_p(0x10000)      # an aligned, never-dereferenced address
+ODD = ctypes.c_void_p(0x10004)       # 4- but not 8-byte aligned
+
+
+def test_entry_points_reject_before_launch(L):
+    g = geom()
+    gp = ctypes.byref(g)
+    # forward
+    assert L.project_3d_to_2d(gp, None, FAKE, None, FAKE, None, 0, None) == TP_E_NULL
+    assert L.project_3d_to_2d(gp, FAKE, None, None, FAKE, None, 0, None) == TP_E_NULL
+    assert L.project_3d_to_2d(gp, FAKE, FAKE, None, None, None, 0, None) == TP_E_NULL
+    assert L.project_3d_to_2d(gp, ODD, FAKE, None, FAKE, None, 0, None) == TP_E_VALUE
+    assert L.project_3d_to_2d(gp, FAKE, FAKE, FAKE, FAKE, None, 0, None) == TP_E_VALUE   # shifts but Bs = 0
+    gs = geom(Bs=1)
+    assert L.project_3d_to_2d(ctypes.byref(gs), FAKE, FAKE, None, FAKE, None, 0, None) == TP_E_VALUE
+    bad = geom(D=9)
+    assert L.project_3d_to_2d(ctypes.byref(bad), FAKE, FAKE, None, FAKE, None, 0, None) == TP_E_SHAPE
+    # forward backward: rotation grads need the volume, shift grads need shifts
+    assert L.project_3d_to_2d_backward(gp, FAKE, None, FAKE, None, None, FAKE, None, None, 0, None) == TP_E_NULL
+    assert L.project_3d_to_2d_backward(gp, FAKE, FAKE, FAKE, None, None, None, FAKE, None, 0, None) == TP_E_NULL
+    assert L.project_3d_to_2d_backward(gp, None, FAKE, FAKE, None, FAKE, None, None, None, 0, None) == TP_E_NULL
+    # back-projection: weights and weight volume come together
+    assert L.backproject_2d_to_3d(gp, FAKE, FAKE, FAKE, None, FAKE, None, None, 0, None) == TP_E_NULL
+    assert L.backproject_2d_to_3d(gp, FAKE, None, FAKE, None, FAKE, FAKE, None, 0, None) == TP_E_NULL
+    assert L.backproject_2d_to_3d(gp, FAKE, None, FAKE, None, None, None, None, 0, None) == TP_E_NULL
+    # back-projection backward
+    assert L.backproject_2d_to_3d_backward(gp, None, None, FAKE, None, FAKE, None, FAKE, None, None, None, None, 0,
+                                           None) == TP_E_NULL
+    assert L.backproject_2d_to_3d_backward(gp, FAKE, None, None, None, FAKE, None, None, None, FAKE, None, None, 0,
+                                           None) == TP_E_NULL
+    assert L.backproject_2d_to_3d_backward(gp, FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, None, None, 0,
+                                           None) == TP_E_NULL
+
+
+def test_python_binding_requires_gpu_tensors():
+    import torch
+    v = torch.zeros((1, 8, 8, 5), dtype=torch.complex64)
+    r = torch.zeros((1, 2, 3, 3), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        bp.project_3d_to_2d(v, r)
+    with pytest.raises(TypeError):
+        bp.project_3d_to_2d(v.to(torch.complex128), r)
