@@ -157,6 +157,8 @@ def project_3d_to_2d(vol, rot, shifts=None, *, H=None, interp="cubic", oversampl
         out = torch.empty((B, P, H, H // 2 + 1), dtype=torch.complex64, device=dev)
     else:
         _req(out, "out", torch.complex64, 4, dev)
+        if tuple(out.shape) != (B, P, H, H // 2 + 1):
+            raise ValueError(f"out must have shape {(B, P, H, H // 2 + 1)}, got {tuple(out.shape)}")
     g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
     ws, nws = _workspace(g, OP_PROJECT, dev)
     _check(lib().project_3d_to_2d(ctypes.byref(g), _ptr(vol), _ptr(rot), _ptr(shifts), _ptr(out), _ptr(ws), nws,
@@ -165,9 +167,10 @@ def project_3d_to_2d(vol, rot, shifts=None, *, H=None, interp="cubic", oversampl
 
 
 def project_3d_to_2d_backward(grad_out, vol, rot, shifts=None, *, interp="cubic", oversampling=1.0,
-                              radius_cutoff=-1.0, need_vol=True, need_rot=True, need_shifts=True):
+                              radius_cutoff=-1.0, need_vol=True, need_rot=True, need_shifts=True,
+                              grad_vol=None, grad_rot=None, grad_shifts=None):
     """Backward of project_3d_to_2d; returns (grad_vol, grad_rot, grad_shifts),
-    None where not requested."""
+    None where not requested.  Preallocated outputs may be passed in."""
     _req(grad_out, "grad_out", torch.complex64, 4)
     dev = grad_out.device
     _req(vol, "vol", torch.complex64, 4, dev)
@@ -178,9 +181,15 @@ def project_3d_to_2d_backward(grad_out, vol, rot, shifts=None, *, interp="cubic"
     Bv, D = vol.shape[0], vol.shape[1]
     Br = rot.shape[0]
     Bs = shifts.shape[0] if shifts is not None else 0
-    gv = torch.empty_like(vol) if need_vol else None
-    gr = torch.empty_like(rot) if need_rot else None
-    gs = torch.empty_like(shifts) if (need_shifts and shifts is not None) else None
+    gv = (grad_vol if grad_vol is not None else torch.empty_like(vol)) if need_vol else None
+    gr = (grad_rot if grad_rot is not None else torch.empty_like(rot)) if need_rot else None
+    gs = (grad_shifts if grad_shifts is not None else torch.empty_like(shifts)) if (
+        need_shifts and shifts is not None) else None
+    for t, ref, name in ((gv, vol, "grad_vol"), (gr, rot, "grad_rot"), (gs, shifts, "grad_shifts")):
+        if t is not None and (t.shape != ref.shape or t.dtype != ref.dtype):
+            raise ValueError(f"{name} must match {tuple(ref.shape)} {ref.dtype}")
+        if t is not None:
+            _req(t, name, ref.dtype, ref.dim(), dev)
     g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
     ws, nws = _workspace(g, OP_PROJECT_BACKWARD, dev)
     _check(lib().project_3d_to_2d_backward(ctypes.byref(g), _ptr(grad_out), _ptr(vol), _ptr(rot), _ptr(shifts),
@@ -189,8 +198,9 @@ def project_3d_to_2d_backward(grad_out, vol, rot, shifts=None, *, interp="cubic"
 
 
 def backproject_2d_to_3d(images, rot, weights=None, shifts=None, *, D=None, Bv=1, interp="cubic", oversampling=1.0,
-                         radius_cutoff=-1.0):
-    """Back-projection (adjoint): returns (data_vol, weight_vol or None)."""
+                         radius_cutoff=-1.0, data_vol=None, weight_vol=None):
+    """Back-projection (adjoint): returns (data_vol, weight_vol or None).
+    Preallocated outputs may be passed in."""
     _req(images, "images", torch.complex64, 4)
     dev = images.device
     _req(rot, "rot", torch.float32, 4, dev)
@@ -202,8 +212,18 @@ def backproject_2d_to_3d(images, rot, weights=None, shifts=None, *, D=None, Bv=1
     Br = rot.shape[0]
     Bs = shifts.shape[0] if shifts is not None else 0
     D = D or H
-    data = torch.empty((Bv, D, D, D // 2 + 1), dtype=torch.complex64, device=dev)
-    wvol = torch.empty((Bv, D, D, D // 2 + 1), dtype=torch.float32, device=dev) if weights is not None else None
+    data = data_vol if data_vol is not None else torch.empty((Bv, D, D, D // 2 + 1), dtype=torch.complex64,
+                                                             device=dev)
+    _req(data, "data_vol", torch.complex64, 4, dev)
+    if tuple(data.shape) != (Bv, D, D, D // 2 + 1):
+        raise ValueError("data_vol has the wrong shape")
+    wvol = None
+    if weights is not None:
+        wvol = weight_vol if weight_vol is not None else torch.empty((Bv, D, D, D // 2 + 1), dtype=torch.float32,
+                                                                     device=dev)
+        _req(wvol, "weight_vol", torch.float32, 4, dev)
+        if tuple(wvol.shape) != (Bv, D, D, D // 2 + 1):
+            raise ValueError("weight_vol has the wrong shape")
     g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
     ws, nws = _workspace(g, OP_BACKPROJECT, dev)
     _check(lib().backproject_2d_to_3d(ctypes.byref(g), _ptr(images), _ptr(weights), _ptr(rot), _ptr(shifts),
