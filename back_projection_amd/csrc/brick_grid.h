@@ -1,0 +1,90 @@
+// Brick decomposition of the sample space shared by host and device code.
+//
+// The gather kernels split tap space (the integer lattice of floor(p)) into
+// cubic bricks of edge S.  A pixel belongs to the brick that holds floor(p);
+// a workgroup stages the brick plus the interpolation halo of the volume in
+// LDS and serves every pixel of a range of poses that falls in it.  Bricks
+// that cannot hold a sample of an orthonormal map (|p| <= o * k_max) are
+// inactive; pixels whose floor(p) lands in no active brick (maps that are not
+// rotations) are served by an edge kernel directly from global memory.
+//
+// Everything here is integer arithmetic so that host and device derive the
+// same work list.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tproj {
+
+struct BrickGrid {
+  int S;          // brick edge (floor(p) values per axis owned by a brick)
+  int nb;         // bricks per axis
+  int nb3;        // nb^3
+  int origin;     // floor(p) value at the low corner of brick 0 (all axes)
+  int pmax_i;     // integer bound on |p| for orthonormal maps (incl. margin)
+  int list_len;   // poses served per volume: P, or B*P when Bv = 1
+  int64_t target; // pixels per work item
+  int dens_q8;    // 256 / o^2, pixel density in sample space (fixed point)
+  int nwork;      // total work items per volume
+};
+
+__host__ __device__ inline int64_t isqrt64(int64_t v) {
+  if (v <= 0) return 0;
+  int64_t r = (int64_t)__builtin_sqrt((double)v);
+  while (r * r > v) --r;
+  while ((r + 1) * (r + 1) <= v) ++r;
+  return r;
+}
+
+__host__ __device__ inline void brick_coords(const BrickGrid& g, int b, int& bi, int& bj, int& bk) {
+  bi = b % g.nb;
+  bj = (b / g.nb) % g.nb;
+  bk = b / (g.nb * g.nb);
+}
+
+// Squared distance from the origin to the closest point of the brick's box
+// [lo, lo + S) (integer corner bound).
+__host__ __device__ inline int64_t brick_near_d2(const BrickGrid& g, int bi, int bj, int bk) {
+  const int idx[3] = {bi, bj, bk};
+  int64_t d2 = 0;
+  for (int a = 0; a < 3; ++a) {
+    const int64_t lo = g.origin + (int64_t)idx[a] * g.S, hi = lo + g.S;
+    int64_t d = 0;
+    if (lo > 0) d = lo;
+    else if (hi < 0) d = -hi;
+    d2 += d * d;
+  }
+  return d2;
+}
+
+__host__ __device__ inline bool brick_active(const BrickGrid& g, int bi, int bj, int bk) {
+  return brick_near_d2(g, bi, bj, bk) <= (int64_t)g.pmax_i * g.pmax_i;
+}
+
+// Number of pose chunks (work items) of a brick: its expected pixel load over
+// the pose list divided by the per-item target.  A random plane through the
+// origin meets a brick at distance rho with probability ~ S / rho and then
+// cuts ~S^2 pixels, so the load per pose is ~ min(1.3 S^2, S^3 / (2 rho)).
+__host__ __device__ inline int brick_chunks(const BrickGrid& g, int bi, int bj, int bk) {
+  if (!brick_active(g, bi, bj, bk)) return 0;
+  const int idx[3] = {bi, bj, bk};
+  int64_t c2 = 0;
+  for (int a = 0; a < 3; ++a) {
+    const int64_t twice_center = 2 * (g.origin + (int64_t)idx[a] * g.S) + g.S;
+    c2 += twice_center * twice_center;
+  }
+  int64_t rho2 = isqrt64(c2);               // twice the centre distance
+  if (rho2 < 1) rho2 = 1;
+  const int64_t S = g.S;
+  int64_t per_pose_x10 = (13 * S * S * rho2 < 10 * S * S * S) ? 13 * S * S * rho2 : 10 * S * S * S;  // x10 x rho2
+  // expected pixels = list_len * per_pose_x10 / (10 * rho2) * dens_q8 / 256
+  const int64_t num = (int64_t)g.list_len * per_pose_x10 * g.dens_q8;
+  const int64_t den = 10 * rho2 * 256 * g.target;
+  int64_t k = (num + den - 1) / den;
+  if (k < 1) k = 1;
+  if (k > g.list_len) k = g.list_len;
+  return (int)k;
+}
+
+}  // namespace tproj

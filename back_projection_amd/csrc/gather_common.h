@@ -1,0 +1,386 @@
+// Gather helpers shared by the direct and the brick-binned kernels:
+// interpolation from global memory (value and derivatives), the slice
+// coordinate, the LDS tile of a brick and the row-by-row enumeration of the
+// pixels of a rotated central slice that fall in a box of sample space.
+//
+// The operation is the rotated central slice of the torch-projectors pages
+// (Spanish "Resumen tecnico" 2, Dutch Methodologie, French "Resume technique"
+// 2) with linear or Catmull-Rom interpolation and per-tap Friedel symmetry.
+#pragma once
+
+#include "brick_grid.h"
+#include "device_common.h"
+
+namespace tproj {
+
+// p = o * R * (kx, ky, 0)^T.  Every kernel computes the slice coordinate with
+// this one expression, so that all of them agree on floor(p).
+__device__ __forceinline__ void slice_coord(const KGeom& g, const float* R, float kx, float ky, float p[3]) {
+  p[0] = g.o * fmaf(R[1], ky, R[0] * kx);
+  p[1] = g.o * fmaf(R[4], ky, R[3] * kx);
+  p[2] = g.o * fmaf(R[7], ky, R[6] * kx);
+}
+
+// ---------------------------------------------------------------------------
+// Interpolation of a complex volume at p (value and, optionally, the three
+// partial derivatives).  Rows of taps along x are read contiguously when all
+// x-taps are direct or all mirrored; otherwise each tap takes the full rule.
+// ---------------------------------------------------------------------------
+template <int NT, bool DERIV>
+__device__ __forceinline__ void interp_c(const float2* __restrict__ V, const KGeom& g, float px, float py, float pz,
+                                         float2& I, float2* dI) {
+  const float flx = safe_floor(px), fly = safe_floor(py), flz = safe_floor(pz);
+  float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
+  axis_weights<NT>(px - flx, wx);
+  axis_weights<NT>(py - fly, wy);
+  axis_weights<NT>(pz - flz, wz);
+  if constexpr (DERIV) {
+    axis_dweights<NT>(px - flx, dx);
+    axis_dweights<NT>(py - fly, dy);
+    axis_dweights<NT>(pz - flz, dz);
+  }
+  const int x0 = (int)flx + first_tap<NT>();
+  const int y0 = (int)fly + first_tap<NT>();
+  const int z0 = (int)flz + first_tap<NT>();
+  // Taps of a sample with |p_a| < D - 3 stay in (-D, D), where one
+  // conditional add/subtract wraps them; any other sample (large
+  // oversampling, non-orthonormal or non-finite R) takes the general rule.
+  const float lim = (float)(g.D - 3);
+  const bool near = fabsf(px) < lim && fabsf(py) < lim && fabsf(pz) < lim;
+  // 0: all x-taps direct; 1: all mirrored; 2: per-tap rule
+  const int mode = !near ? 2 : ((x0 >= 0 && x0 <= g.half - (NT - 1)) ? 0
+                                : ((x0 >= 1 - g.half && x0 <= -NT) ? 1 : 2));
+  I = make_float2(0.f, 0.f);
+  if constexpr (DERIV) { dI[0] = dI[1] = dI[2] = make_float2(0.f, 0.f); }
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+    const int tz = z0 + c;
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      const int ty = y0 + b;
+      float2 r = make_float2(0.f, 0.f), rx = make_float2(0.f, 0.f);
+      if (mode == 0) {
+        const float2* row = V + ((int64_t)wrap_fast(tz, g.D) * g.D + wrap_fast(ty, g.D)) * g.W + x0;
+#pragma unroll
+        for (int a = 0; a < NT; ++a) {
+          const float2 v = row[a];
+          r.x = fmaf(wx[a], v.x, r.x); r.y = fmaf(wx[a], v.y, r.y);
+          if constexpr (DERIV) { rx.x = fmaf(dx[a], v.x, rx.x); rx.y = fmaf(dx[a], v.y, rx.y); }
+        }
+      } else if (mode == 1) {
+        const float2* row = V + ((int64_t)wrap_fast(-tz, g.D) * g.D + wrap_fast(-ty, g.D)) * g.W + (-x0 - (NT - 1));
+#pragma unroll
+        for (int a = 0; a < NT; ++a) {
+          const float2 v = row[NT - 1 - a];
+          r.x = fmaf(wx[a], v.x, r.x); r.y = fmaf(-wx[a], v.y, r.y);
+          if constexpr (DERIV) { rx.x = fmaf(dx[a], v.x, rx.x); rx.y = fmaf(-dx[a], v.y, rx.y); }
+        }
+      } else {
+#pragma unroll
+        for (int a = 0; a < NT; ++a) {
+          bool cj;
+          const int64_t idx = tap_index<true>(g, x0 + a, ty, tz, cj);
+          float2 v = V[idx];
+          if (cj) v.y = -v.y;
+          r.x = fmaf(wx[a], v.x, r.x); r.y = fmaf(wx[a], v.y, r.y);
+          if constexpr (DERIV) { rx.x = fmaf(dx[a], v.x, rx.x); rx.y = fmaf(dx[a], v.y, rx.y); }
+        }
+      }
+      const float wyz = wy[b] * wz[c];
+      I.x = fmaf(wyz, r.x, I.x); I.y = fmaf(wyz, r.y, I.y);
+      if constexpr (DERIV) {
+        dI[0].x = fmaf(wyz, rx.x, dI[0].x); dI[0].y = fmaf(wyz, rx.y, dI[0].y);
+        const float gy = dy[b] * wz[c], gz = wy[b] * dz[c];
+        dI[1].x = fmaf(gy, r.x, dI[1].x); dI[1].y = fmaf(gy, r.y, dI[1].y);
+        dI[2].x = fmaf(gz, r.x, dI[2].x); dI[2].y = fmaf(gz, r.y, dI[2].y);
+      }
+    }
+  }
+}
+
+// Same for a real volume; mirrored taps are not conjugated.
+template <int NT, bool DERIV>
+__device__ __forceinline__ void interp_r(const float* __restrict__ V, const KGeom& g, float px, float py, float pz,
+                                         float& I, float* dI) {
+  const float flx = safe_floor(px), fly = safe_floor(py), flz = safe_floor(pz);
+  float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
+  axis_weights<NT>(px - flx, wx);
+  axis_weights<NT>(py - fly, wy);
+  axis_weights<NT>(pz - flz, wz);
+  if constexpr (DERIV) {
+    axis_dweights<NT>(px - flx, dx);
+    axis_dweights<NT>(py - fly, dy);
+    axis_dweights<NT>(pz - flz, dz);
+  }
+  const int x0 = (int)flx + first_tap<NT>();
+  const int y0 = (int)fly + first_tap<NT>();
+  const int z0 = (int)flz + first_tap<NT>();
+  I = 0.f;
+  if constexpr (DERIV) { dI[0] = dI[1] = dI[2] = 0.f; }
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      float r = 0.f, rx = 0.f;
+#pragma unroll
+      for (int a = 0; a < NT; ++a) {
+        bool cj;
+        const float v = V[tap_index<true>(g, x0 + a, y0 + b, z0 + c, cj)];
+        r = fmaf(wx[a], v, r);
+        if constexpr (DERIV) rx = fmaf(dx[a], v, rx);
+      }
+      const float wyz = wy[b] * wz[c];
+      I = fmaf(wyz, r, I);
+      if constexpr (DERIV) {
+        dI[0] = fmaf(wyz, rx, dI[0]);
+        dI[1] = fmaf(dy[b] * wz[c], r, dI[1]);
+        dI[2] = fmaf(wy[b] * dz[c], r, dI[2]);
+      }
+    }
+  }
+}
+
+
+template <int NT>
+__device__ __forceinline__ float2 interp_global(const float2* __restrict__ V, const KGeom& g, const float p[3]) {
+  float2 I;
+  interp_c<NT, false>(V, g, p[0], p[1], p[2], I, nullptr);
+  return I;
+}
+
+// Value of the Hermitian-extended periodic volume at an integer tap.
+__device__ __forceinline__ float2 tap_value(const float2* __restrict__ V, const KGeom& g, int tx, int ty, int tz) {
+  bool cj;
+  float2 v = V[tap_index<true>(g, tx, ty, tz, cj)];
+  if (cj) v.y = -v.y;
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// LDS tile of one brick: the S^3 owned floor values plus the interpolation
+// halo (1 below and 2 above for cubic, 1 above for linear), 16^3 entries with
+// padded strides.
+// ---------------------------------------------------------------------------
+template <int NT>
+struct Tile {
+  static constexpr int S = 17 - NT;          // 13 (cubic) or 15 (linear)
+  static constexpr int E = 16;               // tile edge = S + NT - 1
+  static constexpr int HL = NT == 4 ? 1 : 0; // halo below
+  static constexpr int SY = 17;              // row stride (padded)
+  static constexpr int SZ = 16 * 17 + 4;     // plane stride (padded)
+  static constexpr int SIZE = E * SZ;
+};
+
+template <int NT>
+__device__ __forceinline__ void stage_tile(float2* tile, const float2* __restrict__ V, const KGeom& g, const int lo[3]) {
+  using Tl = Tile<NT>;
+  for (int i = threadIdx.x; i < Tl::E * Tl::E * Tl::E; i += blockDim.x) {
+    const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
+    tile[z * Tl::SZ + y * Tl::SY + x] = tap_value(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
+  }
+}
+
+// floor(p) relative to the brick's low corner; true if inside [0, S)^3.
+__device__ __forceinline__ bool owned(const float p[3], const int lo[3], int S, int l[3]) {
+  bool in = true;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    l[a] = (int)safe_floor(p[a]) - lo[a];
+    in = in && (l[a] >= 0) && (l[a] < S);
+  }
+  return in;
+}
+
+// Interpolate from the tile; l = floor(p) - lo.
+template <int NT>
+__device__ __forceinline__ float2 interp_tile(const float2* tile, const float p[3], const int l[3]) {
+  using Tl = Tile<NT>;
+  float wx[NT], wy[NT], wz[NT];
+  axis_weights<NT>(p[0] - floorf(p[0]), wx);
+  axis_weights<NT>(p[1] - floorf(p[1]), wy);
+  axis_weights<NT>(p[2] - floorf(p[2]), wz);
+  const float2* base = tile + l[2] * Tl::SZ + l[1] * Tl::SY + l[0];
+  float2 I = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      const float2* row = base + c * Tl::SZ + b * Tl::SY;
+      float2 r = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int a = 0; a < NT; ++a) {
+        const float2 v = row[a];
+        r.x = fmaf(wx[a], v.x, r.x);
+        r.y = fmaf(wx[a], v.y, r.y);
+      }
+      const float wyz = wy[b] * wz[c];
+      I.x = fmaf(wyz, r.x, I.x);
+      I.y = fmaf(wyz, r.y, I.y);
+    }
+  }
+  return I;
+}
+
+// Is floor(p) inside an active brick of the grid?
+__device__ __forceinline__ bool in_active_brick(const BrickGrid& bg, const float p[3]) {
+  int idx[3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const int rel = (int)safe_floor(p[a]) - bg.origin;
+    if (rel < 0 || rel >= bg.nb * bg.S) return false;
+    idx[a] = rel / bg.S;
+  }
+  return brick_active(bg, idx[0], idx[1], idx[2]);
+}
+
+// Pose list of one volume: all (b, n) when the volume is shared, else (v, n).
+__device__ __forceinline__ void list_entry(const KGeom& g, int vsel, int e, int& bimg, int& n) {
+  if (g.Bv == 1) { bimg = e / g.P; n = e - bimg * g.P; }
+  else { bimg = vsel; n = e; }
+}
+
+__device__ __forceinline__ int64_t pixel_index(const KGeom& g, int kx, int ky) {
+  return (int64_t)(ky >= 0 ? ky : ky + g.H) * g.Wi + kx;
+}
+
+// ---------------------------------------------------------------------------
+// Enumeration of the pixels whose sample lies in a box [lo, lo + S)^3 of
+// sample space.  The slice p = A k with A = o [R_:0 R_:1] cuts the box in a
+// convex polygon; its ky extent is bounded through the pseudo-inverse of A,
+// and each image row ky gets the kx interval of the three slab inequalities,
+// widened by a margin.  The owner test on the exactly computed floor(p) then
+// decides, so the enumeration only has to be a superset.
+// ---------------------------------------------------------------------------
+struct SliceRows {
+  float a0[3], a1[3];     // columns of A
+  float bl[3], bh[3];     // box bounds in sample space
+  int ky_lo, ky_hi;       // candidate rows
+};
+
+// Does the plane through the origin spanned by the columns of A meet the box
+// [bl, bh]?  (Conservative by a small margin; a NaN map counts as a hit.)
+__device__ __forceinline__ bool plane_meets_box(const KGeom& g, const float* R, const float bl[3], const float bh[3]) {
+  float a0[3], a1[3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) { a0[a] = g.o * R[3 * a]; a1[a] = g.o * R[3 * a + 1]; }
+  const float n0 = a0[1] * a1[2] - a0[2] * a1[1];
+  const float n1 = a0[2] * a1[0] - a0[0] * a1[2];
+  const float n2 = a0[0] * a1[1] - a0[1] * a1[0];
+  const float c0 = 0.5f * (bl[0] + bh[0]), c1 = 0.5f * (bl[1] + bh[1]), c2 = 0.5f * (bl[2] + bh[2]);
+  const float dist = n0 * c0 + n1 * c1 + n2 * c2;
+  const float rad = 0.5f * (fabsf(n0) * (bh[0] - bl[0]) + fabsf(n1) * (bh[1] - bl[1]) + fabsf(n2) * (bh[2] - bl[2]));
+  const bool miss = fabsf(dist) > rad * 1.001f + 1e-6f * (1.0f + fabsf(dist));
+  return !miss;   // NaN compares false -> not a miss
+}
+
+// Candidate rows of the pixels whose sample lies in the box [bl, bh).
+__device__ __forceinline__ bool slice_rows_box(const KGeom& g, const float* R, const float bl[3], const float bh[3],
+                                               SliceRows& sr) {
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    sr.a0[a] = g.o * R[3 * a];
+    sr.a1[a] = g.o * R[3 * a + 1];
+    sr.bl[a] = bl[a];
+    sr.bh[a] = bh[a];
+  }
+  if (!plane_meets_box(g, R, bl, bh)) return false;
+  int lo_img = -(g.H >> 1), hi_img = (g.H >> 1) - 1;
+  if (g.r2 >= 0.0f) {
+    const int rr = (int)floorf(sqrtf(g.r2)) + 1;
+    lo_img = max(lo_img, -rr);
+    hi_img = min(hi_img, rr);
+  }
+  sr.ky_lo = lo_img;
+  sr.ky_hi = hi_img;
+  const float g00 = sr.a0[0] * sr.a0[0] + sr.a0[1] * sr.a0[1] + sr.a0[2] * sr.a0[2];
+  const float g01 = sr.a0[0] * sr.a1[0] + sr.a0[1] * sr.a1[1] + sr.a0[2] * sr.a1[2];
+  const float g11 = sr.a1[0] * sr.a1[0] + sr.a1[1] * sr.a1[1] + sr.a1[2] * sr.a1[2];
+  const float det = g00 * g11 - g01 * g01;
+  if (det > 1e-6f * g00 * g11 && det == det) {
+    // ky = (row 1 of the pseudo-inverse of A) . p, bounded over the box
+    float kmin = 0.f, kmax = 0.f;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const float u = (g00 * sr.a1[a] - g01 * sr.a0[a]) / det;
+      const float x = u * sr.bl[a], y = u * sr.bh[a];
+      kmin += fminf(x, y);
+      kmax += fmaxf(x, y);
+    }
+    kmin = fmaxf(kmin, (float)lo_img - 2.0f);
+    kmax = fminf(kmax, (float)hi_img + 2.0f);
+    sr.ky_lo = max(sr.ky_lo, (int)floorf(kmin) - 1);
+    sr.ky_hi = min(sr.ky_hi, (int)ceilf(kmax) + 1);
+  }
+  return sr.ky_lo <= sr.ky_hi;
+}
+
+__device__ __forceinline__ bool slice_rows_setup(const KGeom& g, const float* R, const int lo[3], int S,
+                                                 SliceRows& sr) {
+  const float bl[3] = {(float)lo[0], (float)lo[1], (float)lo[2]};
+  const float bh[3] = {(float)(lo[0] + S), (float)(lo[1] + S), (float)(lo[2] + S)};
+  return slice_rows_box(g, R, bl, bh, sr);
+}
+
+// One lane per row ky = r0 + lane: kx interval, count, inclusive scan.
+struct RowBatch {
+  int kx0;     // first candidate kx of this lane's row
+  int incl;    // inclusive prefix of the row counts
+  int total;   // candidates of the batch (wave-uniform)
+};
+
+__device__ __forceinline__ void row_batch(const KGeom& g, const SliceRows& sr, int r0, int lane, RowBatch& rb) {
+  const int ky = r0 + lane;
+  int cnt = 0, kx0 = 0;
+  if (ky <= sr.ky_hi) {
+    const float fky = (float)ky;
+    float xlo = 0.0f, xhi = (float)(g.H >> 1);
+    bool ok = true;
+    if (g.r2 >= 0.0f) {
+      const float rem = g.r2 - fky * fky;
+      if (rem < 0.0f) ok = false;
+      else xhi = fminf(xhi, floorf(sqrtf(rem)) + 1.0f);
+    }
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      const float marg = 1e-2f + 1e-5f * (fabsf(sr.bl[a]) + fabsf(sr.bh[a]));
+      const float rl = sr.bl[a] - marg - sr.a1[a] * fky;
+      const float rh = sr.bh[a] + marg - sr.a1[a] * fky;
+      const float c = sr.a0[a];
+      if (c > 1e-20f) { xlo = fmaxf(xlo, rl / c); xhi = fminf(xhi, rh / c); }
+      else if (c < -1e-20f) { xlo = fmaxf(xlo, rh / c); xhi = fminf(xhi, rl / c); }
+      else if (rl > 0.0f || rh < 0.0f) ok = false;
+    }
+    if (ok && xlo <= xhi) {
+      kx0 = (int)ceilf(xlo);
+      const int kx1 = (int)floorf(xhi);
+      cnt = kx1 >= kx0 ? kx1 - kx0 + 1 : 0;
+    }
+  }
+  int v = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  rb.kx0 = kx0;
+  rb.incl = v;
+  rb.total = __shfl(v, 63, 64);
+}
+
+// Candidate i of the batch (all 64 lanes call this together): its row is the
+// first lane whose inclusive count exceeds i.
+__device__ __forceinline__ void candidate(const RowBatch& rb, int r0, int i, int& kx, int& ky) {
+  int r = 0;
+#pragma unroll
+  for (int step = 32; step >= 1; step >>= 1) {
+    const int v = __shfl(rb.incl, r + step - 1, 64);
+    if (v <= i) r += step;
+  }
+  // every lane takes part in each permute (no lane-dependent branch around them)
+  int before = __shfl(rb.incl, r > 0 ? r - 1 : 0, 64);
+  if (r == 0) before = 0;
+  kx = __shfl(rb.kx0, r, 64) + (i - before);
+  ky = r0 + r;
+}
+
+}  // namespace tproj

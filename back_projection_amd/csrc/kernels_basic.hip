@@ -8,128 +8,10 @@
 // page "Resumen tecnico" 2, Dutch page Methodologie, French page "Resume
 // technique" 2).
 #include "device_common.h"
+#include "gather_common.h"
 #include "kernels.h"
 
 namespace tproj {
-
-// ---------------------------------------------------------------------------
-// Interpolation of a complex volume at p (value and, optionally, the three
-// partial derivatives).  Rows of taps along x are read contiguously when all
-// x-taps are direct or all mirrored; otherwise each tap takes the full rule.
-// ---------------------------------------------------------------------------
-template <int NT, bool DERIV>
-__device__ __forceinline__ void interp_c(const float2* __restrict__ V, const KGeom& g, float px, float py, float pz,
-                                         float2& I, float2* dI) {
-  const float flx = safe_floor(px), fly = safe_floor(py), flz = safe_floor(pz);
-  float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
-  axis_weights<NT>(px - flx, wx);
-  axis_weights<NT>(py - fly, wy);
-  axis_weights<NT>(pz - flz, wz);
-  if constexpr (DERIV) {
-    axis_dweights<NT>(px - flx, dx);
-    axis_dweights<NT>(py - fly, dy);
-    axis_dweights<NT>(pz - flz, dz);
-  }
-  const int x0 = (int)flx + first_tap<NT>();
-  const int y0 = (int)fly + first_tap<NT>();
-  const int z0 = (int)flz + first_tap<NT>();
-  // Taps of a sample with |p_a| < D - 3 stay in (-D, D), where one
-  // conditional add/subtract wraps them; any other sample (large
-  // oversampling, non-orthonormal or non-finite R) takes the general rule.
-  const float lim = (float)(g.D - 3);
-  const bool near = fabsf(px) < lim && fabsf(py) < lim && fabsf(pz) < lim;
-  // 0: all x-taps direct; 1: all mirrored; 2: per-tap rule
-  const int mode = !near ? 2 : ((x0 >= 0 && x0 <= g.half - (NT - 1)) ? 0
-                                : ((x0 >= 1 - g.half && x0 <= -NT) ? 1 : 2));
-  I = make_float2(0.f, 0.f);
-  if constexpr (DERIV) { dI[0] = dI[1] = dI[2] = make_float2(0.f, 0.f); }
-#pragma unroll
-  for (int c = 0; c < NT; ++c) {
-    const int tz = z0 + c;
-#pragma unroll
-    for (int b = 0; b < NT; ++b) {
-      const int ty = y0 + b;
-      float2 r = make_float2(0.f, 0.f), rx = make_float2(0.f, 0.f);
-      if (mode == 0) {
-        const float2* row = V + ((int64_t)wrap_fast(tz, g.D) * g.D + wrap_fast(ty, g.D)) * g.W + x0;
-#pragma unroll
-        for (int a = 0; a < NT; ++a) {
-          const float2 v = row[a];
-          r.x = fmaf(wx[a], v.x, r.x); r.y = fmaf(wx[a], v.y, r.y);
-          if constexpr (DERIV) { rx.x = fmaf(dx[a], v.x, rx.x); rx.y = fmaf(dx[a], v.y, rx.y); }
-        }
-      } else if (mode == 1) {
-        const float2* row = V + ((int64_t)wrap_fast(-tz, g.D) * g.D + wrap_fast(-ty, g.D)) * g.W + (-x0 - (NT - 1));
-#pragma unroll
-        for (int a = 0; a < NT; ++a) {
-          const float2 v = row[NT - 1 - a];
-          r.x = fmaf(wx[a], v.x, r.x); r.y = fmaf(-wx[a], v.y, r.y);
-          if constexpr (DERIV) { rx.x = fmaf(dx[a], v.x, rx.x); rx.y = fmaf(-dx[a], v.y, rx.y); }
-        }
-      } else {
-#pragma unroll
-        for (int a = 0; a < NT; ++a) {
-          bool cj;
-          const int64_t idx = tap_index<true>(g, x0 + a, ty, tz, cj);
-          float2 v = V[idx];
-          if (cj) v.y = -v.y;
-          r.x = fmaf(wx[a], v.x, r.x); r.y = fmaf(wx[a], v.y, r.y);
-          if constexpr (DERIV) { rx.x = fmaf(dx[a], v.x, rx.x); rx.y = fmaf(dx[a], v.y, rx.y); }
-        }
-      }
-      const float wyz = wy[b] * wz[c];
-      I.x = fmaf(wyz, r.x, I.x); I.y = fmaf(wyz, r.y, I.y);
-      if constexpr (DERIV) {
-        dI[0].x = fmaf(wyz, rx.x, dI[0].x); dI[0].y = fmaf(wyz, rx.y, dI[0].y);
-        const float gy = dy[b] * wz[c], gz = wy[b] * dz[c];
-        dI[1].x = fmaf(gy, r.x, dI[1].x); dI[1].y = fmaf(gy, r.y, dI[1].y);
-        dI[2].x = fmaf(gz, r.x, dI[2].x); dI[2].y = fmaf(gz, r.y, dI[2].y);
-      }
-    }
-  }
-}
-
-// Same for a real volume; mirrored taps are not conjugated.
-template <int NT, bool DERIV>
-__device__ __forceinline__ void interp_r(const float* __restrict__ V, const KGeom& g, float px, float py, float pz,
-                                         float& I, float* dI) {
-  const float flx = safe_floor(px), fly = safe_floor(py), flz = safe_floor(pz);
-  float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
-  axis_weights<NT>(px - flx, wx);
-  axis_weights<NT>(py - fly, wy);
-  axis_weights<NT>(pz - flz, wz);
-  if constexpr (DERIV) {
-    axis_dweights<NT>(px - flx, dx);
-    axis_dweights<NT>(py - fly, dy);
-    axis_dweights<NT>(pz - flz, dz);
-  }
-  const int x0 = (int)flx + first_tap<NT>();
-  const int y0 = (int)fly + first_tap<NT>();
-  const int z0 = (int)flz + first_tap<NT>();
-  I = 0.f;
-  if constexpr (DERIV) { dI[0] = dI[1] = dI[2] = 0.f; }
-#pragma unroll
-  for (int c = 0; c < NT; ++c) {
-#pragma unroll
-    for (int b = 0; b < NT; ++b) {
-      float r = 0.f, rx = 0.f;
-#pragma unroll
-      for (int a = 0; a < NT; ++a) {
-        bool cj;
-        const float v = V[tap_index<true>(g, x0 + a, y0 + b, z0 + c, cj)];
-        r = fmaf(wx[a], v, r);
-        if constexpr (DERIV) rx = fmaf(dx[a], v, rx);
-      }
-      const float wyz = wy[b] * wz[c];
-      I = fmaf(wyz, r, I);
-      if constexpr (DERIV) {
-        dI[0] = fmaf(wyz, rx, dI[0]);
-        dI[1] = fmaf(dy[b] * wz[c], r, dI[1]);
-        dI[2] = fmaf(wy[b] * dz[c], r, dI[2]);
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Forward: out[b,n,k] = M * phi * I(V[bv], o R (kx,ky,0)).

@@ -5,12 +5,18 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 
+#include "brick_grid.h"
+#include "brick_kernels.h"
 #include "kernels.h"
+#include "scatter_grid.h"
+#include "scatter_kernels.h"
 
 namespace {
 
@@ -82,6 +88,122 @@ tproj::KGeom kgeom(const tp_geom* g) {
   return k;
 }
 
+// Pixels of one image inside the radius cutoff.
+int64_t pixels_in_mask(const tp_geom* g) {
+  const int64_t half = g->H / 2;
+  if (g->radius_cutoff < 0.0f) return (int64_t)g->H * (half + 1);
+  const double r2 = (double)g->radius_cutoff * g->radius_cutoff;
+  int64_t n = 0;
+  for (int64_t ky = -half; ky < half; ++ky) {
+    const double rem = r2 - (double)(ky * ky);
+    if (rem < 0) continue;
+    int64_t m = (int64_t)std::floor(std::sqrt(rem));
+    while ((m + 1) * (m + 1) + ky * ky <= r2) ++m;
+    while (m >= 0 && m * m + ky * ky > r2) --m;
+    n += std::min(m, half) + 1;
+  }
+  return n;
+}
+
+// Brick grid of the gather kernels for this geometry; ok = false when the
+// brick path does not apply (grid too large) and the direct kernels run.
+struct GatherPlan {
+  bool ok = false;
+  tproj::BrickGrid bg{};
+  size_t ws_bytes = 0;   // prefix table
+};
+
+bool force_direct() {
+  static const bool v = [] {
+    const char* e = std::getenv("TPROJ_KERNELS");
+    return e && std::string(e) == "direct";
+  }();
+  return v;
+}
+
+GatherPlan gather_plan(const tp_geom* g) {
+  GatherPlan pl;
+  if (force_direct()) return pl;
+  tproj::BrickGrid& bg = pl.bg;
+  const int NT = g->interp == TP_CUBIC ? 4 : 2;
+  bg.S = 17 - NT;
+  double kmax = std::sqrt(2.0) * (g->H / 2);
+  if (g->radius_cutoff >= 0.0f) kmax = std::min(kmax, (double)g->radius_cutoff);
+  const double pmax = (double)g->oversampling * kmax;
+  if (pmax > 1e5) return pl;
+  bg.pmax_i = (int)std::ceil(pmax) + 1;
+  bg.origin = -bg.pmax_i - 1;
+  bg.nb = (2 * bg.pmax_i + 2 + bg.S - 1) / bg.S;
+  const int64_t nb3 = (int64_t)bg.nb * bg.nb * bg.nb;
+  if (nb3 > (1 << 20)) return pl;
+  bg.nb3 = (int)nb3;
+  bg.list_len = (g->Bv == 1 ? g->B : 1) * g->P;
+  bg.dens_q8 = std::max(1, (int)std::lround(256.0 / ((double)g->oversampling * g->oversampling)));
+  const int64_t total = (int64_t)g->B * g->P * pixels_in_mask(g);
+  bg.target = std::max<int64_t>(512, total / 4096);
+  int64_t nwork = 0;
+  for (int b = 0; b < bg.nb3; ++b) {
+    int bi, bj, bk;
+    tproj::brick_coords(bg, b, bi, bj, bk);
+    nwork += tproj::brick_chunks(bg, bi, bj, bk);
+  }
+  if (nwork > INT32_MAX / 2) return pl;
+  bg.nwork = (int)nwork;
+  pl.ws_bytes = ((size_t)(bg.nb3 + 1) * sizeof(int) + 255) / 256 * 256;
+  pl.ok = true;
+  return pl;
+}
+
+// Brick plan of the adjoint scatter; ok = false -> direct atomic kernel.
+struct ScatterPlan {
+  bool ok = false;
+  tproj::ScatterGrid sg{};
+  size_t ws_bytes = 0;
+};
+
+ScatterPlan scatter_plan(const tp_geom* g, bool weights) {
+  ScatterPlan pl;
+  if (force_direct()) return pl;
+  tproj::ScatterGrid& sg = pl.sg;
+  const int NT = g->interp == TP_CUBIC ? 4 : 2;
+  const int HL = NT == 4 ? 1 : 0, HH = NT - 1 - HL;
+  sg.S = 16;
+  sg.D = g->D;
+  sg.half = g->D / 2;
+  sg.W = g->D / 2 + 1;
+  sg.nbx = (sg.W + 15) / 16;
+  sg.nby = sg.nbz = (g->D + 15) / 16;
+  sg.nb3 = sg.nbx * sg.nby * sg.nbz;
+  double kmax = std::sqrt(2.0) * (g->H / 2);
+  if (g->radius_cutoff >= 0.0f) kmax = std::min(kmax, (double)g->radius_cutoff);
+  const double pmax = (double)g->oversampling * kmax;
+  if (pmax > 1e5) return pl;
+  const int pmax_i = (int)std::ceil(pmax) + 1;
+  sg.fmin = -pmax_i - 1;
+  sg.fmax = pmax_i;
+  sg.tmin = sg.fmin - HL;
+  sg.tmax = sg.fmax + HH;
+  sg.list_len = (g->Bv == 1 ? g->B : 1) * g->P;
+  sg.dens_q8 = std::max(1, (int)std::lround(256.0 / ((double)g->oversampling * g->oversampling)));
+  const int64_t visits = (int64_t)g->B * g->P * pixels_in_mask(g) * 17 / 10;
+  sg.target = std::max<int64_t>(1024, visits / 4096);
+  sg.weights = weights ? 1 : 0;
+  int64_t nwork = 0, nslots = 0;
+  for (int b = 0; b < sg.nb3; ++b) {
+    int bi, bj, bk;
+    tproj::sbrick_coords(sg, b, bi, bj, bk);
+    const int k = tproj::sbrick_chunks(sg, bi, bj, bk);
+    nwork += k;
+    if (k > 1) nslots += k;
+  }
+  if (nwork > INT32_MAX / 2 || nslots > INT32_MAX / 8) return pl;
+  sg.nwork = (int)nwork;
+  sg.nslots = (int)nslots;
+  pl.ws_bytes = tproj::scatter_ws_bytes(sg, g->Bv);
+  pl.ok = true;
+  return pl;
+}
+
 int64_t vol_elems(const tp_geom* g) { return (int64_t)g->D * g->D * (g->D / 2 + 1); }
 int64_t img_elems(const tp_geom* g) { return (int64_t)g->B * g->P * g->H * (g->H / 2 + 1); }
 
@@ -110,6 +232,39 @@ tp_status check_device() {
     hipError_t _e = (x);                              \
     if (_e != hipSuccess) return launched(_e, what);  \
   } while (0)
+
+// Forward gather: brick-binned kernels when the plan applies, else direct.
+tp_status run_forward(const tp_geom* geom, const tproj::KGeom& k, const float2* vol, const float* rot,
+                      const float* shifts, float2* out, void* workspace, size_t ws_bytes, hipStream_t st) {
+  const GatherPlan pl = gather_plan(geom);
+  if (!pl.ok) {
+    LAUNCH(tproj::launch_project(k, geom->interp, vol, rot, shifts, out, st), "project");
+    return TP_OK;
+  }
+  if (!workspace || ws_bytes < pl.ws_bytes)
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
+  int* prefix = (int*)workspace;
+  LAUNCH(tproj::launch_brick_prefix(pl.bg, prefix, st), "brick work list");
+  LAUNCH(tproj::launch_fwd_brick(k, geom->interp, pl.bg, prefix, vol, rot, shifts, out, st), "project (bricks)");
+  return TP_OK;
+}
+
+tp_status run_scatter(const tp_geom* geom, const tproj::KGeom& k, const float2* Y, const float* Wimg,
+                      const float* rot, const float* shifts, float2* vol, float* wvol, void* workspace,
+                      size_t ws_bytes, hipStream_t st) {
+  const ScatterPlan pl = scatter_plan(geom, Wimg != nullptr);
+  if (!pl.ok) {
+    LAUNCH(tproj::launch_zero((float*)vol, 2 * vol_elems(geom) * geom->Bv, st), "zero volume");
+    if (wvol) LAUNCH(tproj::launch_zero(wvol, vol_elems(geom) * geom->Bv, st), "zero weight volume");
+    LAUNCH(tproj::launch_spread_atomic(k, geom->interp, Y, Wimg, rot, shifts, vol, wvol, st), "scatter");
+    return TP_OK;
+  }
+  if (!workspace || ws_bytes < pl.ws_bytes)
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
+  LAUNCH(tproj::launch_scatter_brick(k, geom->interp, pl.sg, workspace, Y, Wimg, rot, shifts, vol, wvol, st),
+         "scatter (bricks)");
+  return TP_OK;
+}
 
 }  // namespace
 
@@ -140,29 +295,30 @@ tp_status tp_validate(const tp_geom* geom) {
 size_t tp_workspace_size(const tp_geom* geom, int op) {
   if (check_geom(geom) != TP_OK) return (size_t)-1;
   if (op < TP_OP_PROJECT || op > TP_OP_BACKPROJECT_BACKWARD) return (size_t)-1;
-  return 0;
+  if (op == TP_OP_PROJECT || op == TP_OP_BACKPROJECT_BACKWARD) return gather_plan(geom).ws_bytes;
+  if (op == TP_OP_PROJECT_BACKWARD) return scatter_plan(geom, false).ws_bytes;
+  return scatter_plan(geom, true).ws_bytes;
 }
 
 tp_status project_3d_to_2d(const tp_geom* geom, const void* vol, const float* rot, const float* shifts, void* out,
                            void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace; (void)ws_bytes;
   TRY(check_geom(geom));
   TRY(check_shifts(geom, shifts));
   TRY(check_ptr(vol, "vol", 8));
   TRY(check_ptr(rot, "rot", 4));
   TRY(check_opt(shifts, "shifts", 4));
   TRY(check_ptr(out, "out", 8));
+  TRY(check_opt(workspace, "workspace", 8));
   TRY(check_device());
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
-  LAUNCH(tproj::launch_project(k, geom->interp, (const float2*)vol, rot, shifts, (float2*)out, st), "project");
+  TRY(run_forward(geom, k, (const float2*)vol, rot, shifts, (float2*)out, workspace, ws_bytes, st));
   return ok();
 }
 
 tp_status project_3d_to_2d_backward(const tp_geom* geom, const void* grad_out, const void* vol, const float* rot,
                                     const float* shifts, void* grad_vol, float* grad_rot, float* grad_shifts,
                                     void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace; (void)ws_bytes;
   TRY(check_geom(geom));
   TRY(check_shifts(geom, shifts));
   TRY(check_ptr(grad_out, "grad_out", 8));
@@ -171,18 +327,16 @@ tp_status project_3d_to_2d_backward(const tp_geom* geom, const void* grad_out, c
   TRY(check_opt(grad_vol, "grad_vol", 8));
   TRY(check_opt(grad_rot, "grad_rot", 4));
   TRY(check_opt(grad_shifts, "grad_shifts", 4));
+  TRY(check_opt(workspace, "workspace", 8));
   if ((grad_rot || grad_shifts) && !vol) return fail(TP_E_NULL, "vol is NULL but rotation/shift grads are requested");
   TRY(check_opt(vol, "vol", 8));
   if (grad_shifts && !shifts) return fail(TP_E_NULL, "grad_shifts requested without shifts");
   TRY(check_device());
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
-  if (grad_vol) {
-    LAUNCH(tproj::launch_zero((float*)grad_vol, 2 * vol_elems(geom) * geom->Bv, st), "zero grad_vol");
-    LAUNCH(tproj::launch_spread_atomic(k, geom->interp, (const float2*)grad_out, nullptr, rot, shifts,
-                                       (float2*)grad_vol, nullptr, st),
-           "spread grad_vol");
-  }
+  if (grad_vol)
+    TRY(run_scatter(geom, k, (const float2*)grad_out, nullptr, rot, shifts, (float2*)grad_vol, nullptr, workspace,
+                    ws_bytes, st));
   if (grad_rot || grad_shifts) {
     if (grad_rot && geom->Br == 1 && geom->B > 1)
       LAUNCH(tproj::launch_zero(grad_rot, 9 * (int64_t)geom->P, st), "zero grad_rot");
@@ -200,7 +354,6 @@ tp_status project_3d_to_2d_backward(const tp_geom* geom, const void* grad_out, c
 tp_status backproject_2d_to_3d(const tp_geom* geom, const void* images, const float* weights, const float* rot,
                                const float* shifts, void* data_vol, float* weight_vol, void* workspace,
                                size_t ws_bytes, void* stream) {
-  (void)workspace; (void)ws_bytes;
   TRY(check_geom(geom));
   TRY(check_shifts(geom, shifts));
   TRY(check_ptr(images, "images", 8));
@@ -211,14 +364,12 @@ tp_status backproject_2d_to_3d(const tp_geom* geom, const void* images, const fl
     return fail(TP_E_NULL, "weights and weight_vol must both be given or both be NULL");
   TRY(check_opt(weights, "weights", 4));
   TRY(check_opt(weight_vol, "weight_vol", 4));
+  TRY(check_opt(workspace, "workspace", 8));
   TRY(check_device());
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
-  LAUNCH(tproj::launch_zero((float*)data_vol, 2 * vol_elems(geom) * geom->Bv, st), "zero data_vol");
-  if (weight_vol) LAUNCH(tproj::launch_zero(weight_vol, vol_elems(geom) * geom->Bv, st), "zero weight_vol");
-  LAUNCH(tproj::launch_spread_atomic(k, geom->interp, (const float2*)images, weights, rot, shifts, (float2*)data_vol,
-                                     weight_vol, st),
-         "back-projection");
+  TRY(run_scatter(geom, k, (const float2*)images, weights, rot, shifts, (float2*)data_vol, weight_vol, workspace,
+                  ws_bytes, st));
   return ok();
 }
 
@@ -227,7 +378,6 @@ tp_status backproject_2d_to_3d_backward(const tp_geom* geom, const void* grad_da
                                         const float* rot, const float* shifts, void* grad_images,
                                         float* grad_weights, float* grad_rot, float* grad_shifts, void* workspace,
                                         size_t ws_bytes, void* stream) {
-  (void)workspace; (void)ws_bytes;
   TRY(check_geom(geom));
   TRY(check_shifts(geom, shifts));
   TRY(check_ptr(grad_data_vol, "grad_data_vol", 8));
@@ -240,6 +390,7 @@ tp_status backproject_2d_to_3d_backward(const tp_geom* geom, const void* grad_da
   TRY(check_opt(grad_weights, "grad_weights", 4));
   TRY(check_opt(grad_rot, "grad_rot", 4));
   TRY(check_opt(grad_shifts, "grad_shifts", 4));
+  TRY(check_opt(workspace, "workspace", 8));
   if ((grad_rot || grad_shifts) && !images) return fail(TP_E_NULL, "images is NULL but rotation/shift grads are requested");
   if (grad_rot && grad_weight_vol && !weights)
     return fail(TP_E_NULL, "weights is NULL but grad_weight_vol and grad_rot are given");
@@ -248,8 +399,7 @@ tp_status backproject_2d_to_3d_backward(const tp_geom* geom, const void* grad_da
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
   if (grad_images)
-    LAUNCH(tproj::launch_project(k, geom->interp, (const float2*)grad_data_vol, rot, shifts, (float2*)grad_images, st),
-           "grad_images");
+    TRY(run_forward(geom, k, (const float2*)grad_data_vol, rot, shifts, (float2*)grad_images, workspace, ws_bytes, st));
   if (grad_weights) {
     if (grad_weight_vol)
       LAUNCH(tproj::launch_project_real(k, geom->interp, grad_weight_vol, rot, grad_weights, st), "grad_weights");

@@ -85,8 +85,9 @@ def test_null_geometry(L):
 
 def test_workspace_size(L):
     g = geom()
-    for op in range(4):
-        assert L.tp_workspace_size(ctypes.byref(g), op) == 0
+    sizes = [L.tp_workspace_size(ctypes.byref(g), op) for op in range(4)]
+    assert all(0 <= s < (1 << 32) for s in sizes)
+    assert sizes[0] > 0 and sizes[0] % 256 == 0     # brick work list of the forward gather
     assert L.tp_workspace_size(ctypes.byref(g), 7) == ctypes.c_size_t(-1).value
     bad = geom(D=3)
     assert L.tp_workspace_size(ctypes.byref(bad), 0) == ctypes.c_size_t(-1).value
