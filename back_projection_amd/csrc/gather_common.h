@@ -253,6 +253,7 @@ __device__ __forceinline__ int64_t pixel_index(const KGeom& g, int kx, int ky) {
 // ---------------------------------------------------------------------------
 struct SliceRows {
   float a0[3], a1[3];     // columns of A
+  float r0[3];            // approximate 1 / a0 (0 where |a0| is negligible)
   float bl[3], bh[3];     // box bounds in sample space
   int ky_lo, ky_hi;       // candidate rows
 };
@@ -273,6 +274,38 @@ __device__ __forceinline__ bool plane_meets_box(const KGeom& g, const float* R, 
   return !miss;   // NaN compares false -> not a miss
 }
 
+// Can any image pixel (kx >= 0, |k| <= cutoff, inside the image) have its
+// sample in the box [bl, bh]?  The plane must meet the box, and the box's
+// image in pixel space -- bounded through the pseudo-inverse of A -- must meet
+// the half disc of the image.  Conservative (margins; NaN -> true).
+__device__ __forceinline__ bool slice_meets_box(const KGeom& g, const float* R, const float bl[3], const float bh[3]) {
+  if (!plane_meets_box(g, R, bl, bh)) return false;
+  float a0[3], a1[3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) { a0[a] = g.o * R[3 * a]; a1[a] = g.o * R[3 * a + 1]; }
+  const float g00 = a0[0] * a0[0] + a0[1] * a0[1] + a0[2] * a0[2];
+  const float g01 = a0[0] * a1[0] + a0[1] * a1[1] + a0[2] * a1[2];
+  const float g11 = a1[0] * a1[0] + a1[1] * a1[1] + a1[2] * a1[2];
+  const float det = g00 * g11 - g01 * g01;
+  if (!(det > 1e-6f * g00 * g11)) return true;
+  float x0 = 0.f, x1 = 0.f, y0 = 0.f, y1 = 0.f;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const float ux = (g11 * a0[a] - g01 * a1[a]) / det;   // kx = ux . p
+    const float uy = (g00 * a1[a] - g01 * a0[a]) / det;   // ky = uy . p
+    x0 += fminf(ux * bl[a], ux * bh[a]); x1 += fmaxf(ux * bl[a], ux * bh[a]);
+    y0 += fminf(uy * bl[a], uy * bh[a]); y1 += fmaxf(uy * bl[a], uy * bh[a]);
+  }
+  x0 -= 1.0f; x1 += 1.0f; y0 -= 1.0f; y1 += 1.0f;
+  const float hh = (float)(g.H >> 1);
+  if (x1 < 0.0f || x0 > hh || y1 < -hh || y0 > hh) return false;
+  if (g.r2 >= 0.0f) {
+    const float nx = fminf(fmaxf(0.0f, x0), x1), ny = fminf(fmaxf(0.0f, y0), y1);
+    if (nx * nx + ny * ny > g.r2 + 2.0f * sqrtf(g.r2) + 1.0f) return false;
+  }
+  return true;
+}
+
 // Candidate rows of the pixels whose sample lies in the box [bl, bh).
 __device__ __forceinline__ bool slice_rows_box(const KGeom& g, const float* R, const float bl[3], const float bh[3],
                                                SliceRows& sr) {
@@ -280,6 +313,7 @@ __device__ __forceinline__ bool slice_rows_box(const KGeom& g, const float* R, c
   for (int a = 0; a < 3; ++a) {
     sr.a0[a] = g.o * R[3 * a];
     sr.a1[a] = g.o * R[3 * a + 1];
+    sr.r0[a] = fabsf(sr.a0[a]) > 1e-20f ? __builtin_amdgcn_rcpf(sr.a0[a]) : 0.0f;
     sr.bl[a] = bl[a];
     sr.bh[a] = bh[a];
   }
@@ -342,12 +376,14 @@ __device__ __forceinline__ void row_batch(const KGeom& g, const SliceRows& sr, i
     }
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
-      const float marg = 1e-2f + 1e-5f * (fabsf(sr.bl[a]) + fabsf(sr.bh[a]));
+      // the approximate reciprocal is within a few ulp; the margin (in sample
+      // units) and the owner test on the exact floor(p) absorb it
+      const float marg = 1e-2f + 1e-4f * (fabsf(sr.bl[a]) + fabsf(sr.bh[a]) + fabsf(sr.a1[a] * fky));
       const float rl = sr.bl[a] - marg - sr.a1[a] * fky;
       const float rh = sr.bh[a] + marg - sr.a1[a] * fky;
-      const float c = sr.a0[a];
-      if (c > 1e-20f) { xlo = fmaxf(xlo, rl / c); xhi = fminf(xhi, rh / c); }
-      else if (c < -1e-20f) { xlo = fmaxf(xlo, rh / c); xhi = fminf(xhi, rl / c); }
+      const float c = sr.a0[a], rc = sr.r0[a];
+      if (c > 1e-20f) { xlo = fmaxf(xlo, rl * rc); xhi = fminf(xhi, rh * rc); }
+      else if (c < -1e-20f) { xlo = fmaxf(xlo, rh * rc); xhi = fminf(xhi, rl * rc); }
       else if (rl > 0.0f || rh < 0.0f) ok = false;
     }
     if (ok && xlo <= xhi) {

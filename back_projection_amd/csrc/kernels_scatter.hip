@@ -32,9 +32,11 @@ constexpr int SB = 16;                     // stored brick edge
 constexpr int TSY = 17;                    // tile row stride (u64 entries)
 constexpr int TSZ = 16 * 17 + 8;           // tile plane stride
 constexpr int TSIZE = SB * TSZ;            // 4480 entries
+constexpr int TGUARD = 4;                  // guard entries below index 0
 constexpr int PER_LANE = (TSIZE + 255) / 256;
 constexpr int WINDOW = 16;                 // poses per fixed-point window
 constexpr float FIX_RANGE = 0.9f * 2147483648.0f;
+constexpr int MAX_BANDS = 128;
 
 // Copies of a stored interval [lo, hi) in tap space.  Direct: t = s + D j;
 // mirrored: t = D j - s.  Each copy is clipped to the tap range [tmin, tmax].
@@ -96,9 +98,22 @@ __device__ __forceinline__ bool floor_in(const float p[3], const int lo[3], cons
   return in;
 }
 
-__device__ __forceinline__ unsigned long long pack_fixed(float re, float im) {
-  const long long r = (long long)__float2int_rn(re), i = (long long)__float2int_rn(im);
-  return (unsigned long long)(i * 4294967296LL + r);
+// Fixed-point conversion by the magic-number trick: for |x| < 2^22,
+// fma(w, u, 1.5 * 2^23) rounds w * u to the nearest integer k in one
+// instruction and its bit pattern is 0x4B400000 + k.
+constexpr float MAGIC = 12582912.0f;
+constexpr int MAGIC_BITS = 0x4B400000;
+
+__device__ __forceinline__ int fixed_round(float w, float u) {
+  return __float_as_int(fmaf(w, u, MAGIC)) - MAGIC_BITS;
+}
+
+// One 64-bit word holding re + im * 2^32 (re signed): sums of such words
+// keep both parts exact as long as each partial sum stays within 31 bits.
+__device__ __forceinline__ unsigned long long pack_fixed(int re, int im) {
+  const unsigned int lo = (unsigned int)re;
+  const unsigned int hi = (unsigned int)(im + (re >> 31));
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 __device__ __forceinline__ void unpack_fixed(unsigned long long w, float& re, float& im) {
@@ -157,6 +172,102 @@ __device__ __forceinline__ int find_sbrick(const int* __restrict__ prefix, int n
   return lo;
 }
 
+// Add the in-box taps of one pixel.  Rows outside the box along y or z are
+// skipped; along x the out-of-box taps carry weight 0.  SGN = +1 for a direct
+// box (local x = t + add), -1 for a mirrored one (local x = add - t).
+template <int NT, bool WEIGHTS, int SGN>
+__device__ __forceinline__ void scatter_taps(unsigned long long* tile, unsigned int* wtile, const TBox& box,
+                                             const int f[3], const float wx[NT], const float wy[NT],
+                                             const float wz[NT], float2 c, float wv) {
+  constexpr int HL = NT == 4 ? 1 : 0;
+  const int lx0 = SGN * (f[0] - HL) + box.add[0];   // local x of tap ja = 0
+#pragma unroll
+  for (int jc = 0; jc < NT; ++jc) {
+    const int tz = f[2] - HL + jc;
+    if (tz < box.qlo[2] || tz >= box.qhi[2]) continue;
+    const int lz = SGN * tz + box.add[2];
+#pragma unroll
+    for (int jb = 0; jb < NT; ++jb) {
+      const int ty = f[1] - HL + jb;
+      if (ty < box.qlo[1] || ty >= box.qhi[1]) continue;
+      const int ly = SGN * ty + box.add[1];
+      const float wyz = wy[jb] * wz[jc];
+      const float ur = wyz * c.x, ui = wyz * c.y, uw = wyz * wv;
+      const int rowb = lz * TSZ + ly * TSY + lx0;
+#pragma unroll
+      for (int ja = 0; ja < NT; ++ja) {
+        const int li = rowb + SGN * ja;
+        atomicAdd(&tile[li], pack_fixed(fixed_round(wx[ja], ur), fixed_round(wx[ja], ui)));
+        if constexpr (WEIGHTS) atomicAdd(&wtile[li], (unsigned int)fixed_round(wx[ja], uw));
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Largest |Re|, |Im| (and |Wimg|) of every image per band of pixel radius
+// |k| in [bw * i, bw * (i + 1)).  A brick's window scale is then taken over
+// the bands that can reach the brick only, so large low-frequency values do
+// not coarsen the fixed-point grid of the outer bricks.
+// ---------------------------------------------------------------------------
+template <bool WEIGHTS>
+__global__ void __launch_bounds__(256) k_band_max(const float2* __restrict__ Y, const float* __restrict__ Wimg,
+                                                  float* __restrict__ ymax, float* __restrict__ wmax, KGeom g,
+                                                  ScatterGrid sg) {
+  __shared__ unsigned int bm[MAX_BANDS], bw[MAX_BANDS];
+  for (int bn = blockIdx.x; bn < g.B * g.P; bn += gridDim.x) {
+    for (int i = threadIdx.x; i < sg.nbands; i += blockDim.x) { bm[i] = 0u; bw[i] = 0u; }
+    __syncthreads();
+    const float2* Yb = Y + (int64_t)bn * g.npix;
+    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
+      int ikx, iky;
+      pixel_freq(g, pix, ikx, iky);
+      const float kx = (float)ikx, ky = (float)iky;
+      if (!in_mask(g, kx, ky)) continue;
+      const int band = min((int)(sqrtf(fmaf(kx, kx, ky * ky)) * sg.inv_band_w), sg.nbands - 1);
+      const float2 v = Yb[pix];
+      atomicMax(&bm[band], __float_as_uint(fmaxf(fabsf(v.x), fabsf(v.y))));
+      if constexpr (WEIGHTS) atomicMax(&bw[band], __float_as_uint(fabsf(Wimg[(int64_t)bn * g.npix + pix])));
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < sg.nbands; i += blockDim.x) {
+      ymax[(int64_t)bn * sg.nbands + i] = __uint_as_float(bm[i]);
+      if constexpr (WEIGHTS) wmax[(int64_t)bn * sg.nbands + i] = __uint_as_float(bw[i]);
+    }
+    __syncthreads();
+  }
+}
+
+// Largest value a pose can put into a box: the bands of the pixel radii that
+// map into the box [bl, bh) (|k| between |p| / sigma_max and |p| / sigma_min).
+__device__ __forceinline__ float box_band_max(const KGeom& g, const ScatterGrid& sg, const float* R,
+                                              const float* __restrict__ table, int64_t pose, const float bl[3],
+                                              const float bh[3]) {
+  float g00 = 0.f, g01 = 0.f, g11 = 0.f;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const float c0 = g.o * R[3 * a], c1 = g.o * R[3 * a + 1];
+    g00 = fmaf(c0, c0, g00); g01 = fmaf(c0, c1, g01); g11 = fmaf(c1, c1, g11);
+  }
+  const float d = g00 - g11, rt = sqrtf(fmaf(d, d, 4.f * g01 * g01));
+  const float smax = sqrtf(fmaxf(0.5f * (g00 + g11 + rt), 0.f)), smin = sqrtf(fmaxf(0.5f * (g00 + g11 - rt), 0.f));
+  float dn = 0.f, df = 0.f;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const float n = fmaxf(0.f, fmaxf(bl[a], -bh[a]));
+    const float f = fmaxf(fabsf(bl[a]), fabsf(bh[a]));
+    dn = fmaf(n, n, dn);
+    df = fmaf(f, f, df);
+  }
+  const float kmin = sqrtf(dn) / smax - 1.0f, kmax = sqrtf(df) / smin + 1.0f;
+  int b0 = (int)fmaxf(0.f, kmin * sg.inv_band_w);
+  int b1 = (kmax * sg.inv_band_w < (float)sg.nbands) ? (int)(kmax * sg.inv_band_w) : sg.nbands - 1;   // NaN -> last
+  if (!(kmin == kmin)) b0 = 0;
+  float m = 0.f;
+  for (int i = b0; i <= b1; ++i) m = fmaxf(m, table[pose * sg.nbands + i]);
+  return m;
+}
+
 // ---------------------------------------------------------------------------
 // the scatter kernel
 // ---------------------------------------------------------------------------
@@ -166,15 +277,20 @@ __global__ void __launch_bounds__(256) k_scatter_brick(const float2* __restrict_
                                                        float2* __restrict__ vol, float* __restrict__ wvol,
                                                        float2* __restrict__ ws_c, float* __restrict__ ws_w, KGeom g,
                                                        ScatterGrid sg, const int* __restrict__ prefix,
-                                                       const int* __restrict__ slot) {
+                                                       const int* __restrict__ slot, const float* __restrict__ ymax,
+                                                       const float* __restrict__ wmax) {
   constexpr int HL = NT == 4 ? 1 : 0;      // taps below floor(p)
   constexpr int HH = NT - 1 - HL;          // taps above floor(p)
-  __shared__ unsigned long long tile[TSIZE];
-  __shared__ unsigned int wtile[WEIGHTS ? TSIZE : 1];
+  // Taps outside the box along x are added with weight 0 (no branch); their
+  // row-relative index lies in [-3, 18], which the guard entries below index 0
+  // and the row padding keep inside the arrays.
+  __shared__ unsigned long long tile_mem[TSIZE + TGUARD];
+  __shared__ unsigned int wtile_mem[WEIGHTS ? TSIZE + TGUARD : 1];
+  unsigned long long* tile = tile_mem + TGUARD;
+  unsigned int* wtile = wtile_mem + (WEIGHTS ? TGUARD : 0);
   __shared__ int hits[256];
+  __shared__ float hit_m[256], hit_w[256], hit_c[256];
   __shared__ int wave_n[4];
-  __shared__ unsigned int red_m[2];
-  __shared__ float red_c[4];
 
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= sg.nwork) return;
@@ -199,7 +315,10 @@ __global__ void __launch_bounds__(256) k_scatter_brick(const float2* __restrict_
       if constexpr (WEIGHTS) wtile[idx] = 0u;
     }
   }
-  if (tid < 2) red_m[tid] = 0u;
+  if (tid < TGUARD) {
+    tile_mem[tid] = 0ull;
+    if constexpr (WEIGHTS) wtile_mem[tid] = 0u;
+  }
   __syncthreads();
 
   // preimage boxes: direct copies of x, y, z, then mirrored copies (per-axis
@@ -239,71 +358,49 @@ __global__ void __launch_bounds__(256) k_scatter_brick(const float2* __restrict_
     for (int a = 0; a < 3; ++a) { bl[a] = (float)flo[a]; bh[a] = (float)fhi[a]; }
 
     for (int64_t eb = e0; eb < e1; eb += 256) {
-      // ---- hit detection: one pose per lane ----
+      // ---- hit detection: one pose per lane, with its window bounds ----
       bool hit = false;
+      float hm = 0.f, hw = 0.f, hc = 0.f;
       const int64_t e = eb + tid;
       if (e < e1) {
         int bimg, n;
         list_entry(g, vsel, (int)e, bimg, n);
         const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-        hit = scatter_pose_ok(contrib_bound<NT>(g, R)) && plane_meets_box(g, R, bl, bh);
+        hc = contrib_bound<NT>(g, R);
+        hit = scatter_pose_ok(hc) && slice_meets_box(g, R, bl, bh);
+        if (hit) {
+          const int64_t pose = (int64_t)bimg * g.P + n;
+          hm = box_band_max(g, sg, R, ymax, pose, bl, bh);
+          if constexpr (WEIGHTS) hw = box_band_max(g, sg, R, wmax, pose, bl, bh);
+        }
       }
       const unsigned long long m = __ballot(hit);
       if (lane == 0) wave_n[wave] = __popcll(m);
       __syncthreads();
       int before = 0, nh = 0;
       for (int v = 0; v < 4; ++v) { if (v < wave) before += wave_n[v]; nh += wave_n[v]; }
-      if (hit) hits[before + __popcll(m & ((1ull << lane) - 1ull))] = (int)e;
+      if (hit) {
+        const int slot_i = before + __popcll(m & ((1ull << lane) - 1ull));
+        hits[slot_i] = (int)e;
+        hit_m[slot_i] = hm;
+        hit_w[slot_i] = hw;
+        hit_c[slot_i] = hc;
+      }
       __syncthreads();
 
       for (int hb = 0; hb < nh; hb += WINDOW) {
         const int nw = min(WINDOW, nh - hb);
-        // ---- pass 1: largest |value| and the per-voxel contribution bound ----
-        float mloc = 0.f, mwloc = 0.f, cloc = 0.f;
-        for (int h = wave; h < nw; h += 4) {
-          int bimg, n;
-          list_entry(g, vsel, hits[hb + h], bimg, n);
-          const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-          cloc += contrib_bound<NT>(g, R);
-          SliceRows rows;
-          if (!slice_rows_box(g, R, bl, bh, rows)) continue;
-          const int64_t ib = ((int64_t)bimg * g.P + n) * g.npix;
-          for (int r0 = rows.ky_lo; r0 <= rows.ky_hi; r0 += 64) {
-            RowBatch rb;
-            row_batch(g, rows, r0, lane, rb);
-            for (int base = 0; base < rb.total; base += 64) {
-              const int i = base + lane;
-              int kx, ky;
-              candidate(rb, r0, i, kx, ky);
-              if (i >= rb.total) continue;
-              const float fkx = (float)kx, fky = (float)ky;
-              float p[3];
-              slice_coord(g, R, fkx, fky, p);
-              int f[3];
-              if (!floor_in(p, flo, fhi, f) || !in_mask(g, fkx, fky)) continue;
-              const int64_t k = ib + pixel_index(g, kx, ky);
-              const float2 yv = Y[k];
-              mloc = fmaxf(mloc, fmaxf(fabsf(yv.x), fabsf(yv.y)));
-              if (WEIGHTS) mwloc = fmaxf(mwloc, fabsf(Wimg[k]));
-            }
-          }
+        // window scale: largest value and per-voxel contribution bound
+        float M = 0.f, MW = 0.f, C = 0.f;
+        for (int h = 0; h < nw; ++h) {
+          M = fmaxf(M, hit_m[hb + h]);
+          MW = fmaxf(MW, hit_w[hb + h]);
+          C += hit_c[hb + h];
         }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          mloc = fmaxf(mloc, __shfl_xor(mloc, off, 64));
-          mwloc = fmaxf(mwloc, __shfl_xor(mwloc, off, 64));
-        }
-        if (lane == 0) {
-          atomicMax(&red_m[0], __float_as_uint(mloc));
-          if (WEIGHTS) atomicMax(&red_m[1], __float_as_uint(mwloc));
-          red_c[wave] = cloc;
-        }
-        __syncthreads();
-        const float M = __uint_as_float(red_m[0]), MW = __uint_as_float(red_m[1]);
-        const float C = red_c[0] + red_c[1] + red_c[2] + red_c[3];
-        // |re|, |im| <= sqrt(2) M per unit weight; weights of a tap are <= 1
-        const float scale = M > 0.f ? (FIX_RANGE - C) / (1.41421356f * M * C) : 0.f;
-        const float wscale = (WEIGHTS && MW > 0.f) ? (FIX_RANGE - C) / (MW * C) : 0.f;
+        // |re|, |im| <= sqrt(2) M per unit weight (the phase rotates); every
+        // contribution also stays below 2^22 for the magic rounding
+        const float scale = M > 0.f ? fminf(FIX_RANGE - C, 0.99f * 4194304.0f * C) / (1.41421356f * M * C) : 0.f;
+        const float wscale = (WEIGHTS && MW > 0.f) ? fminf(FIX_RANGE - C, 0.99f * 4194304.0f * C) / (MW * C) : 0.f;
 
         // ---- pass 2: accumulate the in-box taps ----
         for (int h = wave; h < nw; h += 4) {
@@ -339,28 +436,12 @@ __global__ void __launch_bounds__(256) k_scatter_brick(const float2* __restrict_
               axis_weights<NT>(p[1] - floorf(p[1]), wy);
               axis_weights<NT>(p[2] - floorf(p[2]), wz);
 #pragma unroll
-              for (int jc = 0; jc < NT; ++jc) {
-                const int tz = f[2] - HL + jc;
-                if (tz < box.qlo[2] || tz >= box.qhi[2]) continue;
-                const int lz = box.sgn * tz + box.add[2];
-#pragma unroll
-                for (int jb = 0; jb < NT; ++jb) {
-                  const int ty = f[1] - HL + jb;
-                  if (ty < box.qlo[1] || ty >= box.qhi[1]) continue;
-                  const int ly = box.sgn * ty + box.add[1];
-                  const float wyz = wy[jb] * wz[jc];
-                  const float ur = wyz * c.x, ui = wyz * c.y, uw = wyz * wv;
-                  const int rowb = lz * TSZ + ly * TSY;
-#pragma unroll
-                  for (int ja = 0; ja < NT; ++ja) {
-                    const int tx = f[0] - HL + ja;
-                    if (tx < box.qlo[0] || tx >= box.qhi[0]) continue;
-                    const int li = rowb + box.sgn * tx + box.add[0];
-                    atomicAdd(&tile[li], pack_fixed(wx[ja] * ur, wx[ja] * ui));
-                    if constexpr (WEIGHTS) atomicAdd(&wtile[li], (unsigned int)__float2int_rn(wx[ja] * uw));
-                  }
-                }
+              for (int ja = 0; ja < NT; ++ja) {
+                const int tx = f[0] - HL + ja;
+                if (tx < box.qlo[0] || tx >= box.qhi[0]) wx[ja] = 0.f;
               }
+              if (box.sgn > 0) scatter_taps<NT, WEIGHTS, 1>(tile, wtile, box, f, wx, wy, wz, c, wv);
+              else scatter_taps<NT, WEIGHTS, -1>(tile, wtile, box, f, wx, wy, wz, c, wv);
             }
           }
         }
@@ -389,7 +470,6 @@ __global__ void __launch_bounds__(256) k_scatter_brick(const float2* __restrict_
             }
           }
         }
-        if (tid < 2) red_m[tid] = 0u;
         __syncthreads();
       }
     }
@@ -500,10 +580,14 @@ __global__ void __launch_bounds__(256) k_scatter_edge(const float2* __restrict__
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
+static size_t band_bytes(const ScatterGrid& sg) {
+  return ((size_t)sg.npose * sg.nbands * sizeof(float) * (sg.weights ? 2 : 1) + 255) / 256 * 256;
+}
+
 size_t scatter_ws_bytes(const ScatterGrid& sg, int Bv) {
   const size_t tables = ((size_t)(sg.nb3 + 1) * 2 * sizeof(int) + 255) / 256 * 256;
   const size_t per_tile = (size_t)TSIZE * (sizeof(float2) + (sg.weights ? sizeof(float) : 0));
-  return tables + (size_t)sg.nslots * Bv * per_tile;
+  return tables + band_bytes(sg) + (size_t)sg.nslots * Bv * per_tile;
 }
 
 hipError_t launch_scatter_brick(const KGeom& g, int interp, const ScatterGrid& sg, void* workspace, const float2* Y,
@@ -512,16 +596,25 @@ hipError_t launch_scatter_brick(const KGeom& g, int interp, const ScatterGrid& s
   int* prefix = (int*)workspace;
   int* slot = prefix + (sg.nb3 + 1);
   const size_t tables = ((size_t)(sg.nb3 + 1) * 2 * sizeof(int) + 255) / 256 * 256;
-  float2* ws_c = (float2*)((char*)workspace + tables);
+  float* ymax = (float*)((char*)workspace + tables);
+  float* wmax = ymax + (size_t)sg.npose * sg.nbands;
+  float2* ws_c = (float2*)((char*)workspace + tables + band_bytes(sg));
   float* ws_w = (float*)(ws_c + (size_t)sg.nslots * g.Bv * TSIZE);
   hipLaunchKernelGGL(k_sbrick_prefix, dim3(1), dim3(1024), 0, st, sg, prefix, slot);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  {
+    const int nb = sg.npose < 65535 ? sg.npose : 65535;
+    if (Wimg) hipLaunchKernelGGL((k_band_max<true>), dim3(nb), dim3(256), 0, st, Y, Wimg, ymax, wmax, g, sg);
+    else hipLaunchKernelGGL((k_band_max<false>), dim3(nb), dim3(256), 0, st, Y, Wimg, ymax, wmax, g, sg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid(sg.nwork, g.Bv), blk(256);
   const bool wt = Wimg != nullptr;
 #define TP_SCATTER(NT_, W_)                                                                                      \
   hipLaunchKernelGGL((k_scatter_brick<NT_, W_>), grid, blk, 0, st, Y, Wimg, rot, shifts, vol, wvol, ws_c, ws_w, g, \
-                     sg, prefix, slot)
+                     sg, prefix, slot, ymax, wmax)
   if (interp == 1) { if (wt) TP_SCATTER(4, true); else TP_SCATTER(4, false); }
   else { if (wt) TP_SCATTER(2, true); else TP_SCATTER(2, false); }
 #undef TP_SCATTER

@@ -31,6 +31,9 @@ struct ScatterGrid {
   int nwork;          // work items per volume
   int nslots;         // workspace partial tiles per volume (bricks with > 1 chunk)
   int weights;        // 1: the weight channel is accumulated too
+  int npose;          // B * P images
+  int nbands;         // radial bands of the per-image maxima (<= 128)
+  float inv_band_w;   // 1 / band width (pixels)
 };
 
 __host__ __device__ inline void sbrick_coords(const ScatterGrid& g, int b, int& bi, int& bj, int& bk) {

@@ -188,6 +188,13 @@ ScatterPlan scatter_plan(const tp_geom* g, bool weights) {
   const int64_t visits = (int64_t)g->B * g->P * pixels_in_mask(g) * 17 / 10;
   sg.target = std::max<int64_t>(1024, visits / 4096);
   sg.weights = weights ? 1 : 0;
+  sg.npose = g->B * g->P;
+  {
+    const double kimg = std::sqrt(2.0) * (g->H / 2) + 1.0;
+    const double bw = std::max(1.0, std::ceil(kimg / 64.0));
+    sg.nbands = (int)std::ceil(kimg / bw) + 1;
+    sg.inv_band_w = (float)(1.0 / bw);
+  }
   int64_t nwork = 0, nslots = 0;
   for (int b = 0; b < sg.nb3; ++b) {
     int bi, bj, bk;
