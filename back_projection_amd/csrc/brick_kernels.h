@@ -14,5 +14,12 @@ hipError_t launch_brick_prefix(const BrickGrid& bg, int* prefix, hipStream_t st)
 // then the brick kernel; out is fully written.
 hipError_t launch_fwd_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* vol,
                             const float* rot, const float* shifts, float2* out, hipStream_t st);
+// same for a real volume (weight channel), no phase
+hipError_t launch_fwd_brick_real(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix,
+                                 const float* vol, const float* rot, float* out, hipStream_t st);
+// rotation / shift gradients accumulated (atomically) into zeroed outputs
+hipError_t launch_grad_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* volc,
+                             const float* volr, const float2* U, const float* Ur, const float* rot,
+                             const float* shifts, float* grad_rot, float* grad_s, hipStream_t st);
 
 }  // namespace tproj

@@ -1,20 +1,27 @@
 // Brick-binned gather kernels of libtproj for gfx950.
 //
 // k_brick_prefix   work list: prefix sums of the pose chunks of every brick
-// k_fwd_brick      3D->2D forward: a workgroup stages one tap-space brick of
-//                  the (Hermitian-extended, periodic) volume plus the
-//                  interpolation halo in LDS, then every wavefront walks the
-//                  poses of its chunk, enumerates the pixels whose floor(p)
-//                  falls in the brick (row by row, from the slab
-//                  inequalities of the rotated central slice) and
-//                  interpolates them from LDS.
-// k_fwd_edge       writes the masked pixels (zeros) and serves the rare
-//                  pixels whose floor(p) lies in no active brick.
+// k_fwd_brick      3D->2D forward (complex volume, with the shift phase) or
+//                  its real counterpart (weight channel): a workgroup stages
+//                  one tap-space brick of the Hermitian-extended periodic
+//                  volume plus the interpolation halo in LDS; for blocks of
+//                  256 poses it tests one pose per lane against the brick,
+//                  and each wavefront then walks the hit poses, enumerating
+//                  (row by row, from the slab inequalities of the rotated
+//                  slice) the pixels whose floor(p) falls in the brick and
+//                  interpolating them from LDS.
+// k_grad_brick     rotation / shift gradients on the same decomposition: the
+//                  value and the three partial derivatives of the
+//                  interpolant come from the LDS tile; each wavefront reduces
+//                  its pixels of a pose to 8 sums and adds them to the pose's
+//                  gradient with global atomics.
+// *_edge           masked pixels and the rare samples outside every active
+//                  brick (maps that are not rotations), from global memory.
 //
-// The operation is the rotated central slice with linear or Catmull-Rom
-// interpolation, per-tap Friedel symmetry and Fourier-phase shifts
-// (torch-projectors pages: Spanish "Resumen tecnico" 2, Dutch Methodologie,
-// French "Resume technique" 2).
+// The operations are the rotated central slice with linear or Catmull-Rom
+// interpolation, per-tap Friedel symmetry, Fourier-phase shifts and the
+// gradients w.r.t. rotations and shifts (torch-projectors pages: Spanish
+// "Resumen tecnico" 2, Dutch Methodologie, French "Resume technique" 2).
 #include "brick_grid.h"
 #include "brick_kernels.h"
 #include "device_common.h"
@@ -39,7 +46,6 @@ __global__ void __launch_bounds__(1024) k_brick_prefix(BrickGrid bg, int* __rest
       brick_coords(bg, b, bi, bj, bk);
       k = brick_chunks(bg, bi, bj, bk);
     }
-    // inclusive scan within the wave
     int v = k;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -59,7 +65,7 @@ __global__ void __launch_bounds__(1024) k_brick_prefix(BrickGrid bg, int* __rest
 
 // Locate work item w: brick b with prefix[b] <= w < prefix[b + 1].
 __device__ __forceinline__ int find_brick(const int* __restrict__ prefix, int nb3, int w) {
-  int lo = 0, hi = nb3;          // invariant: prefix[lo] <= w < prefix[hi]
+  int lo = 0, hi = nb3;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (prefix[mid] <= w) lo = mid; else hi = mid;
@@ -68,14 +74,106 @@ __device__ __forceinline__ int find_brick(const int* __restrict__ prefix, int nb
 }
 
 // ---------------------------------------------------------------------------
+// element helpers (complex tile with Friedel conjugation, or real tile)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float2 tap_load(const float2* __restrict__ V, const KGeom& g, int tx, int ty, int tz) {
+  return tap_value(V, g, tx, ty, tz);
+}
+__device__ __forceinline__ float tap_load(const float* __restrict__ V, const KGeom& g, int tx, int ty, int tz) {
+  bool cj;
+  return V[tap_index<true>(g, tx, ty, tz, cj)];
+}
+__device__ __forceinline__ float2 zero_of(float2) { return make_float2(0.f, 0.f); }
+__device__ __forceinline__ float zero_of(float) { return 0.f; }
+__device__ __forceinline__ void fma_into(float w, float2 v, float2& a) { a.x = fmaf(w, v.x, a.x); a.y = fmaf(w, v.y, a.y); }
+__device__ __forceinline__ void fma_into(float w, float v, float& a) { a = fmaf(w, v, a); }
+
+template <int NT, typename T>
+__device__ __forceinline__ void stage_tile_t(T* tile, const T* __restrict__ V, const KGeom& g, const int lo[3]) {
+  using Tl = Tile<NT>;
+  for (int i = threadIdx.x; i < Tl::E * Tl::E * Tl::E; i += blockDim.x) {
+    const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
+    tile[z * Tl::SZ + y * Tl::SY + x] = tap_load(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
+  }
+}
+
+// Value (and, with DERIV, the partial derivatives along x, y, z) of the
+// interpolant from the tile; l = floor(p) - lo.
+template <int NT, bool DERIV, typename T>
+__device__ __forceinline__ void interp_tile_t(const T* tile, const float p[3], const int l[3], T& I, T* dI) {
+  using Tl = Tile<NT>;
+  float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
+  const float fx = p[0] - floorf(p[0]), fy = p[1] - floorf(p[1]), fz = p[2] - floorf(p[2]);
+  axis_weights<NT>(fx, wx);
+  axis_weights<NT>(fy, wy);
+  axis_weights<NT>(fz, wz);
+  if constexpr (DERIV) {
+    axis_dweights<NT>(fx, dx);
+    axis_dweights<NT>(fy, dy);
+    axis_dweights<NT>(fz, dz);
+  }
+  const T* base = tile + l[2] * Tl::SZ + l[1] * Tl::SY + l[0];
+  T z0 = zero_of(T{});
+  I = z0;
+  if constexpr (DERIV) { dI[0] = z0; dI[1] = z0; dI[2] = z0; }
+#pragma unroll
+  for (int c = 0; c < NT; ++c) {
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      const T* row = base + c * Tl::SZ + b * Tl::SY;
+      T r = z0, rx = z0;
+#pragma unroll
+      for (int a = 0; a < NT; ++a) {
+        const T v = row[a];
+        fma_into(wx[a], v, r);
+        if constexpr (DERIV) fma_into(dx[a], v, rx);
+      }
+      const float wyz = wy[b] * wz[c];
+      fma_into(wyz, r, I);
+      if constexpr (DERIV) {
+        fma_into(wyz, rx, dI[0]);
+        fma_into(dy[b] * wz[c], r, dI[1]);
+        fma_into(wy[b] * dz[c], r, dI[2]);
+      }
+    }
+  }
+}
+
+// One pose per lane of a block of 256: does its slice reach the box?  The hit
+// poses are compacted into hits[]; returns their count (block-uniform).
+__device__ __forceinline__ int detect_hits(const KGeom& g, const float* __restrict__ rot, int vsel, int64_t eb,
+                                           int64_t e1, const float bl[3], const float bh[3], int* hits,
+                                           int* wave_n) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  bool hit = false;
+  const int64_t e = eb + tid;
+  if (e < e1) {
+    int bimg, n;
+    list_entry(g, vsel, (int)e, bimg, n);
+    hit = slice_meets_box(g, rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n), bl, bh);
+  }
+  const unsigned long long m = __ballot(hit);
+  if (lane == 0) wave_n[wave] = __popcll(m);
+  __syncthreads();
+  int before = 0, nh = 0;
+  for (int v = 0; v < 4; ++v) { if (v < wave) before += wave_n[v]; nh += wave_n[v]; }
+  if (hit) hits[before + __popcll(m & ((1ull << lane) - 1ull))] = (int)e;
+  __syncthreads();
+  return nh;
+}
+
+// ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <int NT>
-__global__ void __launch_bounds__(256) k_fwd_brick(const float2* __restrict__ vol, const float* __restrict__ rot,
-                                                   const float* __restrict__ shifts, float2* __restrict__ out,
-                                                   KGeom g, BrickGrid bg, const int* __restrict__ prefix) {
+template <int NT, typename T>
+__global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, const float* __restrict__ rot,
+                                                   const float* __restrict__ shifts, T* __restrict__ out, KGeom g,
+                                                   BrickGrid bg, const int* __restrict__ prefix) {
   using Tl = Tile<NT>;
-  __shared__ float2 tile[Tl::SIZE];
+  constexpr bool CPLX = sizeof(T) == 8;
+  __shared__ T tile[Tl::SIZE];
+  __shared__ int hits[256];
+  __shared__ int wave_n[4];
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
   const int b = find_brick(prefix, bg.nb3, w);
@@ -83,47 +181,69 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const float2* __restrict__ vo
   int bi, bj, bk;
   brick_coords(bg, b, bi, bj, bk);
   const int lo[3] = {bg.origin + bi * bg.S, bg.origin + bj * bg.S, bg.origin + bk * bg.S};
-  const float2* V = vol + (int64_t)vsel * g.D * g.D * g.W;
-
-  stage_tile<NT>(tile, V, g, lo);
+  const float bl[3] = {(float)lo[0], (float)lo[1], (float)lo[2]};
+  const float bh[3] = {(float)(lo[0] + bg.S), (float)(lo[1] + bg.S), (float)(lo[2] + bg.S)};
+  stage_tile_t<NT>(tile, vol + (int64_t)vsel * g.D * g.D * g.W, g, lo);
   __syncthreads();
 
   const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int64_t e = e0 + wave; e < e1; e += 4) {
-    int bimg, n;
-    list_entry(g, vsel, (int)e, bimg, n);
-    const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-    const float* s = shifts ? shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n) : nullptr;
-    SliceRows rows;
-    if (!slice_rows_setup(g, R, lo, bg.S, rows)) continue;
-    float2* O = out + ((int64_t)bimg * g.P + n) * g.npix;
-    for (int r0 = rows.ky_lo; r0 <= rows.ky_hi; r0 += 64) {
-      RowBatch rb;
-      row_batch(g, rows, r0, lane, rb);
-      for (int base = 0; base < rb.total; base += 64) {   // wave-uniform loop
-        const int i = base + lane;
-        int kx, ky;
-        candidate(rb, r0, i, kx, ky);
-        if (i >= rb.total) continue;
-        const float fkx = (float)kx, fky = (float)ky;
-        float p[3];
-        slice_coord(g, R, fkx, fky, p);
-        int l[3];
-        if (!owned(p, lo, bg.S, l) || !in_mask(g, fkx, fky)) continue;
-        float2 I = interp_tile<NT>(tile, p, l);
-        if (s) I = cmul(shift_phase(fkx, fky, s[0], s[1], g.inv_h), I);
-        O[pixel_index(g, kx, ky)] = I;
+  for (int64_t eb = e0; eb < e1; eb += 256) {
+    const int nh = detect_hits(g, rot, vsel, eb, e1, bl, bh, hits, wave_n);
+    for (int h = wave; h < nh; h += 4) {
+      int bimg, n;
+      list_entry(g, vsel, hits[h], bimg, n);
+      const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+      const float* s = (CPLX && shifts) ? shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n) : nullptr;
+      SliceRows rows;
+      if (!slice_rows_box(g, R, bl, bh, rows)) continue;
+      T* O = out + ((int64_t)bimg * g.P + n) * g.npix;
+      for (int r0 = rows.ky_lo; r0 <= rows.ky_hi; r0 += 64) {
+        RowBatch rb;
+        row_batch(g, rows, r0, lane, rb);
+        for (int base = 0; base < rb.total; base += 64) {   // wave-uniform loop
+          const int i = base + lane;
+          int kx, ky;
+          candidate(rb, r0, i, kx, ky);
+          if (i >= rb.total) continue;
+          const float fkx = (float)kx, fky = (float)ky;
+          float p[3];
+          slice_coord(g, R, fkx, fky, p);
+          int l[3];
+          if (!owned(p, lo, bg.S, l) || !in_mask(g, fkx, fky)) continue;
+          T I;
+          interp_tile_t<NT, false>(tile, p, l, I, (T*)nullptr);
+          if constexpr (CPLX) {
+            if (s) I = cmul(shift_phase(fkx, fky, s[0], s[1], g.inv_h), I);
+          }
+          O[pixel_index(g, kx, ky)] = I;
+        }
       }
     }
+    __syncthreads();   // hits[] is rewritten by the next block of poses
   }
 }
 
+// |p| <= pmax_i puts floor(p) in an active brick (the brick's nearest point to
+// the origin is at most |p| away); only larger samples need the full test.
+__device__ __forceinline__ bool served_by_bricks(const BrickGrid& bg, const float p[3]) {
+  const float r2 = p[0] * p[0] + p[1] * p[1] + p[2] * p[2];
+  const float pm = (float)bg.pmax_i;
+  if (r2 <= pm * pm * 0.999f) return true;
+  return in_active_brick(bg, p);
+}
+
+__device__ __forceinline__ float2 interp_global_t(const float2* __restrict__ V, const KGeom& g, const float p[3],
+                                                  int interp) {
+  return interp == 1 ? interp_global<4>(V, g, p) : interp_global<2>(V, g, p);
+}
+
 // Masked pixels -> 0; pixels outside every active brick -> direct gather.
-template <int NT>
-__global__ void __launch_bounds__(256) k_fwd_edge(const float2* __restrict__ vol, const float* __restrict__ rot,
-                                                  const float* __restrict__ shifts, float2* __restrict__ out, KGeom g,
+template <int NT, typename T>
+__global__ void __launch_bounds__(256) k_fwd_edge(const T* __restrict__ vol, const float* __restrict__ rot,
+                                                  const float* __restrict__ shifts, T* __restrict__ out, KGeom g,
                                                   BrickGrid bg) {
+  constexpr bool CPLX = sizeof(T) == 8;
   const int pix = blockIdx.x * blockDim.x + threadIdx.x;
   if (pix >= g.npix) return;
   int ikx, iky;
@@ -133,18 +253,193 @@ __global__ void __launch_bounds__(256) k_fwd_edge(const float2* __restrict__ vol
   const int64_t nvol = (int64_t)g.D * g.D * g.W;
   for (int bn = blockIdx.y; bn < g.B * g.P; bn += gridDim.y) {
     const int bimg = bn / g.P, n = bn - bimg * g.P;
-    float2* o = out + (int64_t)bn * g.npix + pix;
-    if (!m) { *o = make_float2(0.f, 0.f); continue; }
+    T* o = out + (int64_t)bn * g.npix + pix;
+    if (!m) { *o = zero_of(T{}); continue; }
     const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
     float p[3];
     slice_coord(g, R, kx, ky, p);
-    if (in_active_brick(bg, p)) continue;
-    float2 I = interp_global<NT>(vol + nvol * (g.Bv == 1 ? 0 : bimg), g, p);
-    if (shifts) {
-      const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
-      I = cmul(shift_phase(kx, ky, s[0], s[1], g.inv_h), I);
+    if (served_by_bricks(bg, p)) continue;
+    if constexpr (CPLX) {
+      float2 I = interp_global<NT>(vol + nvol * (g.Bv == 1 ? 0 : bimg), g, p);
+      if (shifts) {
+        const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
+        I = cmul(shift_phase(kx, ky, s[0], s[1], g.inv_h), I);
+      }
+      *o = I;
+    } else {
+      float I;
+      interp_r<NT, false>(vol + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, nullptr);
+      *o = I;
     }
-    *o = I;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// rotation / shift gradients
+//   gR[i][j] += o * sum_k M (Re(conj(U) phi dI_i(Vc)) + Ur dI_i(Vr)) k3_j
+//   gs       += (2 pi / H) sum_k M (kx, ky) Im(conj(U) phi I(Vc))
+// ---------------------------------------------------------------------------
+template <bool CPLX>
+__device__ __forceinline__ void add_grads(const KGeom& g, float* acc, float* __restrict__ grad_rot,
+                                          float* __restrict__ grad_s, int bimg, int n) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc[q] += __shfl_xor(acc[q], off, 64);
+  }
+  if (lane == 0) {
+    if (grad_rot) {
+      float* gr = grad_rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+#pragma unroll
+      for (int q = 0; q < 6; ++q) atomicAdd(gr + 3 * (q >> 1) + (q & 1), g.o * acc[q]);
+    }
+    if (CPLX && grad_s) {
+      float* gs = grad_s + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
+      atomicAdd(gs, 6.283185307179586f * g.inv_h * acc[6]);
+      atomicAdd(gs + 1, 6.283185307179586f * g.inv_h * acc[7]);
+    }
+  }
+}
+
+template <int NT, bool CPLX, bool REAL>
+__global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ volc, const float* __restrict__ volr,
+                                                    const float2* __restrict__ U, const float* __restrict__ Ur,
+                                                    const float* __restrict__ rot, const float* __restrict__ shifts,
+                                                    float* __restrict__ grad_rot, float* __restrict__ grad_s, KGeom g,
+                                                    BrickGrid bg, const int* __restrict__ prefix) {
+  using Tl = Tile<NT>;
+  __shared__ float2 tc[CPLX ? Tl::SIZE : 1];
+  __shared__ float tr[REAL ? Tl::SIZE : 1];
+  __shared__ int hits[256];
+  __shared__ int wave_n[4];
+  const int w = blockIdx.x, vsel = blockIdx.y;
+  if (w >= bg.nwork) return;
+  const int b = find_brick(prefix, bg.nb3, w);
+  const int chunk = w - prefix[b], nchunk = prefix[b + 1] - prefix[b];
+  int bi, bj, bk;
+  brick_coords(bg, b, bi, bj, bk);
+  const int lo[3] = {bg.origin + bi * bg.S, bg.origin + bj * bg.S, bg.origin + bk * bg.S};
+  const float bl[3] = {(float)lo[0], (float)lo[1], (float)lo[2]};
+  const float bh[3] = {(float)(lo[0] + bg.S), (float)(lo[1] + bg.S), (float)(lo[2] + bg.S)};
+  const int64_t nvol = (int64_t)g.D * g.D * g.W;
+  if constexpr (CPLX) stage_tile_t<NT>(tc, volc + (int64_t)vsel * nvol, g, lo);
+  if constexpr (REAL) stage_tile_t<NT>(tr, volr + (int64_t)vsel * nvol, g, lo);
+  __syncthreads();
+
+  const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int64_t eb = e0; eb < e1; eb += 256) {
+    const int nh = detect_hits(g, rot, vsel, eb, e1, bl, bh, hits, wave_n);
+    for (int h = wave; h < nh; h += 4) {
+      int bimg, n;
+      list_entry(g, vsel, hits[h], bimg, n);
+      const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+      const float* s = (CPLX && shifts) ? shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n) : nullptr;
+      SliceRows rows;
+      if (!slice_rows_box(g, R, bl, bh, rows)) continue;
+      const int64_t ib = ((int64_t)bimg * g.P + n) * g.npix;
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+      for (int r0 = rows.ky_lo; r0 <= rows.ky_hi; r0 += 64) {
+        RowBatch rb;
+        row_batch(g, rows, r0, lane, rb);
+        for (int base = 0; base < rb.total; base += 64) {
+          const int i = base + lane;
+          int kx, ky;
+          candidate(rb, r0, i, kx, ky);
+          if (i >= rb.total) continue;
+          const float fkx = (float)kx, fky = (float)ky;
+          float p[3];
+          slice_coord(g, R, fkx, fky, p);
+          int l[3];
+          if (!owned(p, lo, bg.S, l) || !in_mask(g, fkx, fky)) continue;
+          const int64_t k = ib + pixel_index(g, kx, ky);
+          float e[3] = {0.f, 0.f, 0.f};
+          if constexpr (CPLX) {
+            float2 I, dI[3];
+            interp_tile_t<NT, true>(tc, p, l, I, dI);
+            float2 phi = make_float2(1.f, 0.f);
+            if (s) phi = shift_phase(fkx, fky, s[0], s[1], g.inv_h);
+            const float2 cu = cmulc(U[k], phi);   // conj(U) * phi
+#pragma unroll
+            for (int a = 0; a < 3; ++a) e[a] = cu.x * dI[a].x - cu.y * dI[a].y;
+            const float im = cu.x * I.y + cu.y * I.x;
+            acc[6] = fmaf(fkx, im, acc[6]);
+            acc[7] = fmaf(fky, im, acc[7]);
+          }
+          if constexpr (REAL) {
+            float I, dI[3];
+            interp_tile_t<NT, true>(tr, p, l, I, dI);
+            const float wv = Ur[k];
+#pragma unroll
+            for (int a = 0; a < 3; ++a) e[a] = fmaf(wv, dI[a], e[a]);
+          }
+#pragma unroll
+          for (int a = 0; a < 3; ++a) {
+            acc[2 * a] = fmaf(e[a], fkx, acc[2 * a]);
+            acc[2 * a + 1] = fmaf(e[a], fky, acc[2 * a + 1]);
+          }
+        }
+      }
+      add_grads<CPLX>(g, acc, grad_rot, grad_s, bimg, n);
+    }
+    __syncthreads();
+  }
+}
+
+// Pixels outside every active brick: their gradient terms from global memory.
+template <int NT, bool CPLX, bool REAL>
+__global__ void __launch_bounds__(256) k_grad_edge(const float2* __restrict__ volc, const float* __restrict__ volr,
+                                                   const float2* __restrict__ U, const float* __restrict__ Ur,
+                                                   const float* __restrict__ rot, const float* __restrict__ shifts,
+                                                   float* __restrict__ grad_rot, float* __restrict__ grad_s, KGeom g,
+                                                   BrickGrid bg) {
+  const int pix = blockIdx.x * blockDim.x + threadIdx.x;
+  if (pix >= g.npix) return;
+  int ikx, iky;
+  pixel_freq(g, pix, ikx, iky);
+  const float kx = (float)ikx, ky = (float)iky;
+  if (!in_mask(g, kx, ky)) return;
+  const int64_t nvol = (int64_t)g.D * g.D * g.W;
+  for (int bn = blockIdx.y; bn < g.B * g.P; bn += gridDim.y) {
+    const int bimg = bn / g.P, n = bn - bimg * g.P;
+    const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+    float p[3];
+    slice_coord(g, R, kx, ky, p);
+    if (served_by_bricks(bg, p)) continue;
+    const int64_t k = (int64_t)bn * g.npix + pix;
+    float e[3] = {0.f, 0.f, 0.f}, im = 0.f;
+    if constexpr (CPLX) {
+      float2 I, dI[3];
+      interp_c<NT, true>(volc + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, dI);
+      float2 phi = make_float2(1.f, 0.f);
+      if (shifts) {
+        const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
+        phi = shift_phase(kx, ky, s[0], s[1], g.inv_h);
+      }
+      const float2 cu = cmulc(U[k], phi);
+      for (int a = 0; a < 3; ++a) e[a] = cu.x * dI[a].x - cu.y * dI[a].y;
+      im = cu.x * I.y + cu.y * I.x;
+    }
+    if constexpr (REAL) {
+      float I, dI[3];
+      interp_r<NT, true>(volr + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, dI);
+      for (int a = 0; a < 3; ++a) e[a] = fmaf(Ur[k], dI[a], e[a]);
+    }
+    if (grad_rot) {
+      float* gr = grad_rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+      for (int a = 0; a < 3; ++a) {
+        atomicAdd(gr + 3 * a, g.o * e[a] * kx);
+        atomicAdd(gr + 3 * a + 1, g.o * e[a] * ky);
+      }
+    }
+    if (CPLX && grad_s) {
+      float* gs = grad_s + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
+      atomicAdd(gs, 6.283185307179586f * g.inv_h * kx * im);
+      atomicAdd(gs + 1, 6.283185307179586f * g.inv_h * ky * im);
+    }
   }
 }
 
@@ -156,17 +451,59 @@ hipError_t launch_brick_prefix(const BrickGrid& bg, int* prefix, hipStream_t st)
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* vol,
-                            const float* rot, const float* shifts, float2* out, hipStream_t st) {
+static dim3 edge_grid(const KGeom& g) {
   const int gy = g.B * g.P < 65535 ? g.B * g.P : 65535;
-  const dim3 eg((g.npix + 255) / 256, gy), blk(256);
-  if (interp == 1) hipLaunchKernelGGL((k_fwd_edge<4>), eg, blk, 0, st, vol, rot, shifts, out, g, bg);
-  else hipLaunchKernelGGL((k_fwd_edge<2>), eg, blk, 0, st, vol, rot, shifts, out, g, bg);
+  return dim3((g.npix + 255) / 256, gy);
+}
+
+template <typename T>
+static hipError_t fwd_t(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const T* vol,
+                        const float* rot, const float* shifts, T* out, hipStream_t st) {
+  const dim3 blk(256);
+  if (interp == 1) hipLaunchKernelGGL((k_fwd_edge<4, T>), edge_grid(g), blk, 0, st, vol, rot, shifts, out, g, bg);
+  else hipLaunchKernelGGL((k_fwd_edge<2, T>), edge_grid(g), blk, 0, st, vol, rot, shifts, out, g, bg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || bg.nwork == 0) return e;
   const dim3 grid(bg.nwork, g.Bv);
-  if (interp == 1) hipLaunchKernelGGL((k_fwd_brick<4>), grid, blk, 0, st, vol, rot, shifts, out, g, bg, prefix);
-  else hipLaunchKernelGGL((k_fwd_brick<2>), grid, blk, 0, st, vol, rot, shifts, out, g, bg, prefix);
+  if (interp == 1) hipLaunchKernelGGL((k_fwd_brick<4, T>), grid, blk, 0, st, vol, rot, shifts, out, g, bg, prefix);
+  else hipLaunchKernelGGL((k_fwd_brick<2, T>), grid, blk, 0, st, vol, rot, shifts, out, g, bg, prefix);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* vol,
+                            const float* rot, const float* shifts, float2* out, hipStream_t st) {
+  return fwd_t<float2>(g, interp, bg, prefix, vol, rot, shifts, out, st);
+}
+
+hipError_t launch_fwd_brick_real(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix,
+                                 const float* vol, const float* rot, float* out, hipStream_t st) {
+  return fwd_t<float>(g, interp, bg, prefix, vol, rot, nullptr, out, st);
+}
+
+template <int NT, bool C, bool R>
+static void grad_launch(const KGeom& g, const BrickGrid& bg, const int* prefix, const float2* volc, const float* volr,
+                        const float2* U, const float* Ur, const float* rot, const float* shifts, float* grad_rot,
+                        float* grad_s, hipStream_t st) {
+  const dim3 blk(256);
+  hipLaunchKernelGGL((k_grad_edge<NT, C, R>), edge_grid(g), blk, 0, st, volc, volr, U, Ur, rot, shifts, grad_rot,
+                     grad_s, g, bg);
+  if (bg.nwork == 0) return;
+  hipLaunchKernelGGL((k_grad_brick<NT, C, R>), dim3(bg.nwork, g.Bv), blk, 0, st, volc, volr, U, Ur, rot, shifts,
+                     grad_rot, grad_s, g, bg, prefix);
+}
+
+hipError_t launch_grad_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* volc,
+                             const float* volr, const float2* U, const float* Ur, const float* rot,
+                             const float* shifts, float* grad_rot, float* grad_s, hipStream_t st) {
+  const bool c = volc != nullptr, r = volr != nullptr;
+#define TP_GRAD(NT_)                                                                                            \
+  do {                                                                                                          \
+    if (c && r) grad_launch<NT_, true, true>(g, bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st);  \
+    else if (c) grad_launch<NT_, true, false>(g, bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st); \
+    else if (r) grad_launch<NT_, false, true>(g, bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st); \
+  } while (0)
+  if (interp == 1) TP_GRAD(4); else TP_GRAD(2);
+#undef TP_GRAD
   return hipGetLastError();
 }
 

@@ -240,6 +240,16 @@ tp_status check_device() {
     if (_e != hipSuccess) return launched(_e, what);  \
   } while (0)
 
+size_t workspace_need(const tp_geom* g, int op);
+
+// The workspace is checked before anything is enqueued.
+tp_status check_workspace(const tp_geom* g, int op, const void* ws, size_t ws_bytes) {
+  const size_t need = workspace_need(g, op);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, need);
+  return TP_OK;
+}
+
 // Forward gather: brick-binned kernels when the plan applies, else direct.
 tp_status run_forward(const tp_geom* geom, const tproj::KGeom& k, const float2* vol, const float* rot,
                       const float* shifts, float2* out, void* workspace, size_t ws_bytes, hipStream_t st) {
@@ -253,6 +263,43 @@ tp_status run_forward(const tp_geom* geom, const tproj::KGeom& k, const float2* 
   int* prefix = (int*)workspace;
   LAUNCH(tproj::launch_brick_prefix(pl.bg, prefix, st), "brick work list");
   LAUNCH(tproj::launch_fwd_brick(k, geom->interp, pl.bg, prefix, vol, rot, shifts, out, st), "project (bricks)");
+  return TP_OK;
+}
+
+// Rotation / shift gradients into zeroed outputs: bricks, else direct.
+tp_status run_grads(const tp_geom* geom, const tproj::KGeom& k, const float2* volc, const float* volr,
+                    const float2* U, const float* Ur, const float* rot, const float* shifts, float* grad_rot,
+                    float* grad_shifts, void* workspace, size_t ws_bytes, hipStream_t st) {
+  if (grad_rot) LAUNCH(tproj::launch_zero(grad_rot, 9 * (int64_t)geom->Br * geom->P, st), "zero grad_rot");
+  if (grad_shifts) LAUNCH(tproj::launch_zero(grad_shifts, 2 * (int64_t)geom->Bs * geom->P, st), "zero grad_shifts");
+  const GatherPlan pl = gather_plan(geom);
+  if (!pl.ok) {
+    LAUNCH(tproj::launch_rot_shift_grad(k, geom->interp, volc, volr, U, Ur, rot, shifts, grad_rot, grad_shifts, st),
+           "rotation/shift grads");
+    return TP_OK;
+  }
+  if (!workspace || ws_bytes < pl.ws_bytes)
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
+  int* prefix = (int*)workspace;
+  LAUNCH(tproj::launch_brick_prefix(pl.bg, prefix, st), "brick work list");
+  LAUNCH(tproj::launch_grad_brick(k, geom->interp, pl.bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot,
+                                  grad_shifts, st),
+         "rotation/shift grads (bricks)");
+  return TP_OK;
+}
+
+tp_status run_forward_real(const tp_geom* geom, const tproj::KGeom& k, const float* vol, const float* rot,
+                           float* out, void* workspace, size_t ws_bytes, hipStream_t st) {
+  const GatherPlan pl = gather_plan(geom);
+  if (!pl.ok) {
+    LAUNCH(tproj::launch_project_real(k, geom->interp, vol, rot, out, st), "real projection");
+    return TP_OK;
+  }
+  if (!workspace || ws_bytes < pl.ws_bytes)
+    return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
+  int* prefix = (int*)workspace;
+  LAUNCH(tproj::launch_brick_prefix(pl.bg, prefix, st), "brick work list");
+  LAUNCH(tproj::launch_fwd_brick_real(k, geom->interp, pl.bg, prefix, vol, rot, out, st), "real projection (bricks)");
   return TP_OK;
 }
 
@@ -302,10 +349,21 @@ tp_status tp_validate(const tp_geom* geom) {
 size_t tp_workspace_size(const tp_geom* geom, int op) {
   if (check_geom(geom) != TP_OK) return (size_t)-1;
   if (op < TP_OP_PROJECT || op > TP_OP_BACKPROJECT_BACKWARD) return (size_t)-1;
-  if (op == TP_OP_PROJECT || op == TP_OP_BACKPROJECT_BACKWARD) return gather_plan(geom).ws_bytes;
-  if (op == TP_OP_PROJECT_BACKWARD) return scatter_plan(geom, false).ws_bytes;
+  return workspace_need(geom, op);
+}
+
+}  // extern "C"
+
+namespace {
+size_t workspace_need(const tp_geom* geom, int op) {
+  const size_t gather = gather_plan(geom).ws_bytes;
+  if (op == TP_OP_PROJECT || op == TP_OP_BACKPROJECT_BACKWARD) return gather;
+  if (op == TP_OP_PROJECT_BACKWARD) return std::max(gather, scatter_plan(geom, false).ws_bytes);
   return scatter_plan(geom, true).ws_bytes;
 }
+}  // namespace
+
+extern "C" {
 
 tp_status project_3d_to_2d(const tp_geom* geom, const void* vol, const float* rot, const float* shifts, void* out,
                            void* workspace, size_t ws_bytes, void* stream) {
@@ -316,6 +374,7 @@ tp_status project_3d_to_2d(const tp_geom* geom, const void* vol, const float* ro
   TRY(check_opt(shifts, "shifts", 4));
   TRY(check_ptr(out, "out", 8));
   TRY(check_opt(workspace, "workspace", 8));
+  TRY(check_workspace(geom, TP_OP_PROJECT, workspace, ws_bytes));
   TRY(check_device());
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
@@ -338,23 +397,16 @@ tp_status project_3d_to_2d_backward(const tp_geom* geom, const void* grad_out, c
   if ((grad_rot || grad_shifts) && !vol) return fail(TP_E_NULL, "vol is NULL but rotation/shift grads are requested");
   TRY(check_opt(vol, "vol", 8));
   if (grad_shifts && !shifts) return fail(TP_E_NULL, "grad_shifts requested without shifts");
+  TRY(check_workspace(geom, TP_OP_PROJECT_BACKWARD, workspace, ws_bytes));
   TRY(check_device());
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
   if (grad_vol)
     TRY(run_scatter(geom, k, (const float2*)grad_out, nullptr, rot, shifts, (float2*)grad_vol, nullptr, workspace,
                     ws_bytes, st));
-  if (grad_rot || grad_shifts) {
-    if (grad_rot && geom->Br == 1 && geom->B > 1)
-      LAUNCH(tproj::launch_zero(grad_rot, 9 * (int64_t)geom->P, st), "zero grad_rot");
-    else if (grad_rot)
-      LAUNCH(tproj::launch_zero(grad_rot, 9 * (int64_t)geom->Br * geom->P, st), "zero grad_rot");
-    if (grad_shifts && geom->Bs == 1 && geom->B > 1)
-      LAUNCH(tproj::launch_zero(grad_shifts, 2 * (int64_t)geom->P, st), "zero grad_shifts");
-    LAUNCH(tproj::launch_rot_shift_grad(k, geom->interp, (const float2*)vol, nullptr, (const float2*)grad_out,
-                                        nullptr, rot, shifts, grad_rot, grad_shifts, st),
-           "rotation/shift grads");
-  }
+  if (grad_rot || grad_shifts)
+    TRY(run_grads(geom, k, (const float2*)vol, nullptr, (const float2*)grad_out, nullptr, rot, shifts, grad_rot,
+                  grad_shifts, workspace, ws_bytes, st));
   return ok();
 }
 
@@ -372,6 +424,7 @@ tp_status backproject_2d_to_3d(const tp_geom* geom, const void* images, const fl
   TRY(check_opt(weights, "weights", 4));
   TRY(check_opt(weight_vol, "weight_vol", 4));
   TRY(check_opt(workspace, "workspace", 8));
+  TRY(check_workspace(geom, TP_OP_BACKPROJECT, workspace, ws_bytes));
   TRY(check_device());
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
@@ -402,6 +455,7 @@ tp_status backproject_2d_to_3d_backward(const tp_geom* geom, const void* grad_da
   if (grad_rot && grad_weight_vol && !weights)
     return fail(TP_E_NULL, "weights is NULL but grad_weight_vol and grad_rot are given");
   if (grad_shifts && !shifts) return fail(TP_E_NULL, "grad_shifts requested without shifts");
+  TRY(check_workspace(geom, TP_OP_BACKPROJECT_BACKWARD, workspace, ws_bytes));
   TRY(check_device());
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
@@ -409,22 +463,14 @@ tp_status backproject_2d_to_3d_backward(const tp_geom* geom, const void* grad_da
     TRY(run_forward(geom, k, (const float2*)grad_data_vol, rot, shifts, (float2*)grad_images, workspace, ws_bytes, st));
   if (grad_weights) {
     if (grad_weight_vol)
-      LAUNCH(tproj::launch_project_real(k, geom->interp, grad_weight_vol, rot, grad_weights, st), "grad_weights");
+      TRY(run_forward_real(geom, k, grad_weight_vol, rot, grad_weights, workspace, ws_bytes, st));
     else
       LAUNCH(tproj::launch_zero(grad_weights, img_elems(geom), st), "zero grad_weights");
   }
   if (grad_rot || grad_shifts) {
-    if (grad_rot && geom->Br == 1 && geom->B > 1)
-      LAUNCH(tproj::launch_zero(grad_rot, 9 * (int64_t)geom->P, st), "zero grad_rot");
-    else if (grad_rot)
-      LAUNCH(tproj::launch_zero(grad_rot, 9 * (int64_t)geom->Br * geom->P, st), "zero grad_rot");
-    if (grad_shifts && geom->Bs == 1 && geom->B > 1)
-      LAUNCH(tproj::launch_zero(grad_shifts, 2 * (int64_t)geom->P, st), "zero grad_shifts");
     const bool wch = grad_weight_vol != nullptr && weights != nullptr;
-    LAUNCH(tproj::launch_rot_shift_grad(k, geom->interp, (const float2*)grad_data_vol, wch ? grad_weight_vol : nullptr,
-                                        (const float2*)images, wch ? weights : nullptr, rot, shifts, grad_rot,
-                                        grad_shifts, st),
-           "rotation/shift grads");
+    TRY(run_grads(geom, k, (const float2*)grad_data_vol, wch ? grad_weight_vol : nullptr, (const float2*)images,
+                  wch ? weights : nullptr, rot, shifts, grad_rot, grad_shifts, workspace, ws_bytes, st));
   }
   return ok();
 }
