@@ -22,6 +22,7 @@ struct KGeom {
   float o;                  // oversampling
   float r2;                 // radius^2, < 0: no cutoff
   float inv_h;              // 1 / H
+  float kmax;               // largest |k| of an in-mask pixel
 };
 
 // floor() clamped to +-2^24 (NaN -> -2^24) so that the int conversion and the

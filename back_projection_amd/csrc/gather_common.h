@@ -221,6 +221,19 @@ __device__ __forceinline__ float2 interp_tile(const float2* tile, const float p[
   return I;
 }
 
+// Largest |p| = |A k| over the in-mask pixels of a pose: kmax * sigma_max(A).
+__device__ __forceinline__ float pose_pmax(const KGeom& g, const float* R) {
+  float g00 = 0.f, g01 = 0.f, g11 = 0.f;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const float c0 = g.o * R[3 * a], c1 = g.o * R[3 * a + 1];
+    g00 = fmaf(c0, c0, g00); g01 = fmaf(c0, c1, g01); g11 = fmaf(c1, c1, g11);
+  }
+  const float d = g00 - g11;
+  const float lmax = 0.5f * (g00 + g11 + sqrtf(fmaf(d, d, 4.f * g01 * g01)));
+  return g.kmax * sqrtf(lmax) * 1.00001f;   // NaN for a NaN map
+}
+
 // Is floor(p) inside an active brick of the grid?
 __device__ __forceinline__ bool in_active_brick(const BrickGrid& bg, const float p[3]) {
   int idx[3];

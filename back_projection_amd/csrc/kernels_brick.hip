@@ -239,23 +239,26 @@ __device__ __forceinline__ float2 interp_global_t(const float2* __restrict__ V, 
 }
 
 // Masked pixels -> 0; pixels outside every active brick -> direct gather.
+// A pose whose largest sample radius is below the brick grid's bound is
+// served entirely by the bricks; only its masked pixels are written here.
 template <int NT, typename T>
 __global__ void __launch_bounds__(256) k_fwd_edge(const T* __restrict__ vol, const float* __restrict__ rot,
                                                   const float* __restrict__ shifts, T* __restrict__ out, KGeom g,
                                                   BrickGrid bg) {
   constexpr bool CPLX = sizeof(T) == 8;
   const int pix = blockIdx.x * blockDim.x + threadIdx.x;
-  if (pix >= g.npix) return;
-  int ikx, iky;
-  pixel_freq(g, pix, ikx, iky);
+  int ikx = 0, iky = 0;
+  if (pix < g.npix) pixel_freq(g, pix, ikx, iky);
   const float kx = (float)ikx, ky = (float)iky;
-  const bool m = in_mask(g, kx, ky);
+  const bool m = pix < g.npix && in_mask(g, kx, ky);
   const int64_t nvol = (int64_t)g.D * g.D * g.W;
   for (int bn = blockIdx.y; bn < g.B * g.P; bn += gridDim.y) {
     const int bimg = bn / g.P, n = bn - bimg * g.P;
+    if (pix >= g.npix) continue;
     T* o = out + (int64_t)bn * g.npix + pix;
     if (!m) { *o = zero_of(T{}); continue; }
     const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+    if (pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i) continue;
     float p[3];
     slice_coord(g, R, kx, ky, p);
     if (served_by_bricks(bg, p)) continue;
@@ -406,6 +409,7 @@ __global__ void __launch_bounds__(256) k_grad_edge(const float2* __restrict__ vo
   for (int bn = blockIdx.y; bn < g.B * g.P; bn += gridDim.y) {
     const int bimg = bn / g.P, n = bn - bimg * g.P;
     const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+    if (pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i) continue;
     float p[3];
     slice_coord(g, R, kx, ky, p);
     if (served_by_bricks(bg, p)) continue;
@@ -452,7 +456,7 @@ hipError_t launch_brick_prefix(const BrickGrid& bg, int* prefix, hipStream_t st)
 }
 
 static dim3 edge_grid(const KGeom& g) {
-  const int gy = g.B * g.P < 65535 ? g.B * g.P : 65535;
+  const int gy = g.B * g.P < 2048 ? g.B * g.P : 2048;
   return dim3((g.npix + 255) / 256, gy);
 }
 

@@ -504,10 +504,11 @@ __global__ void __launch_bounds__(256) k_scatter_reduce(float2* __restrict__ vol
                                                         const float2* __restrict__ ws_c, const float* __restrict__ ws_w,
                                                         KGeom g, ScatterGrid sg, const int* __restrict__ prefix,
                                                         const int* __restrict__ slot) {
-  const int64_t nvol = (int64_t)g.D * g.D * g.W;
+  const int64_t nvol = (int64_t)g.D * g.D * g.W;   // < 2^31 for D <= 1024
   const int vsel = blockIdx.y;
-  for (int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v < nvol; v += (int64_t)gridDim.x * blockDim.x) {
-    const int x = (int)(v % g.W), y = (int)((v / g.W) % g.D), z = (int)(v / ((int64_t)g.W * g.D));
+  for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < (int)nvol; v += gridDim.x * blockDim.x) {
+    const int xy = v % (g.W * g.D), z = v / (g.W * g.D);
+    const int x = xy % g.W, y = xy / g.W;
     const int bi = x / SB, bj = y / SB, bk = z / SB;
     const int b = (bk * sg.nby + bj) * sg.nbx + bi;
     const int k = prefix[b + 1] - prefix[b];
@@ -545,10 +546,13 @@ __global__ void __launch_bounds__(256) k_scatter_edge(const float2* __restrict__
   for (int bn = blockIdx.y; bn < g.B * g.P; bn += gridDim.y) {
     const int bimg = bn / g.P, n = bn - bimg * g.P;
     const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+    const bool pose_ok = scatter_pose_ok(contrib_bound<NT>(g, R));
+    // every sample of the pose inside the served floor range: nothing to do
+    if (pose_ok && pose_pmax(g, R) <= 0.9995f * (float)(sg.fmax)) continue;
     float p[3];
     slice_coord(g, R, kx, ky, p);
     int f[3];
-    if (scatter_pose_ok(contrib_bound<NT>(g, R)) && floor_in(p, lo, hi, f)) continue;
+    if (pose_ok && floor_in(p, lo, hi, f)) continue;
     float2 c = Y[(int64_t)bn * g.npix + pix];
     if (shifts) {
       const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
@@ -630,7 +634,7 @@ hipError_t launch_scatter_brick(const KGeom& g, int interp, const ScatterGrid& s
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int gy = g.B * g.P < 65535 ? g.B * g.P : 65535;
+  const int gy = g.B * g.P < 2048 ? g.B * g.P : 2048;
   const dim3 eg((g.npix + 255) / 256, gy);
   if (interp == 1) {
     if (wt) hipLaunchKernelGGL((k_scatter_edge<4, true>), eg, blk, 0, st, Y, Wimg, rot, shifts, vol, wvol, g, sg);

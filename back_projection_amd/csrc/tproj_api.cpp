@@ -85,6 +85,12 @@ tproj::KGeom kgeom(const tp_geom* g) {
   k.o = g->oversampling;
   k.r2 = g->radius_cutoff < 0.0f ? -1.0f : g->radius_cutoff * g->radius_cutoff;
   k.inv_h = 1.0f / (float)g->H;
+  {
+    const double h = g->H / 2;
+    double km = std::sqrt(2.0) * h;
+    if (g->radius_cutoff >= 0.0f) km = std::min(km, (double)g->radius_cutoff);
+    k.kmax = (float)(km * (1.0 + 1e-6));
+  }
   return k;
 }
 
