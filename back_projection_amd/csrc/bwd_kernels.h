@@ -1,0 +1,29 @@
+// Launchers of the brick-binned back-projection / backward kernels (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "brick_grid.h"
+#include "device_common.h"
+
+namespace tproj {
+
+struct BwdGrid {
+  BrickGrid bg;       // tap-space bricks (as the forward gather)
+  int npose;          // B * P images
+  int nbands;         // radial bands of the per-image maxima (<= 128)
+  float inv_band_w;   // 1 / band width (pixels)
+};
+
+// Workspace bytes: work list, band maxima, one partial tile per work item.
+size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights);
+
+// Writes vol (and wvol when Wimg != NULL) completely with the adjoint of the
+// forward.  With volc != NULL the rotation / shift gradients of the forward
+// are accumulated into grad_rot / grad_s (zeroed by the caller; either may be
+// NULL) in the same pass; volc is the forward's volume.
+hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* workspace, const float2* Y,
+                      const float* Wimg, const float2* volc, const float* rot, const float* shifts, float2* vol,
+                      float* wvol, float* grad_rot, float* grad_s, hipStream_t st);
+
+}  // namespace tproj

@@ -246,6 +246,25 @@ __device__ __forceinline__ bool in_active_brick(const BrickGrid& bg, const float
   return brick_active(bg, idx[0], idx[1], idx[2]);
 }
 
+// |p| <= pmax_i puts floor(p) in an active brick (the brick's nearest point to
+// the origin is at most |p| away); only larger samples need the full test.
+__device__ __forceinline__ bool served_by_bricks(const BrickGrid& bg, const float p[3]) {
+  const float r2 = p[0] * p[0] + p[1] * p[1] + p[2] * p[2];
+  const float pm = (float)bg.pmax_i;
+  if (r2 <= pm * pm * 0.999f) return true;
+  return in_active_brick(bg, p);
+}
+
+// Locate work item w: brick b with prefix[b] <= w < prefix[b + 1].
+__device__ __forceinline__ int find_brick(const int* __restrict__ prefix, int nb3, int w) {
+  int lo = 0, hi = nb3;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= w) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
 // Pose list of one volume: all (b, n) when the volume is shared, else (v, n).
 __device__ __forceinline__ void list_entry(const KGeom& g, int vsel, int e, int& bimg, int& n) {
   if (g.Bv == 1) { bimg = e / g.P; n = e - bimg * g.P; }

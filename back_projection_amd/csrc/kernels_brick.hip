@@ -63,16 +63,6 @@ __global__ void __launch_bounds__(1024) k_brick_prefix(BrickGrid bg, int* __rest
   }
 }
 
-// Locate work item w: brick b with prefix[b] <= w < prefix[b + 1].
-__device__ __forceinline__ int find_brick(const int* __restrict__ prefix, int nb3, int w) {
-  int lo = 0, hi = nb3;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= w) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 // ---------------------------------------------------------------------------
 // element helpers (complex tile with Friedel conjugation, or real tile)
 // ---------------------------------------------------------------------------
@@ -222,15 +212,6 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
     }
     __syncthreads();   // hits[] is rewritten by the next block of poses
   }
-}
-
-// |p| <= pmax_i puts floor(p) in an active brick (the brick's nearest point to
-// the origin is at most |p| away); only larger samples need the full test.
-__device__ __forceinline__ bool served_by_bricks(const BrickGrid& bg, const float p[3]) {
-  const float r2 = p[0] * p[0] + p[1] * p[1] + p[2] * p[2];
-  const float pm = (float)bg.pmax_i;
-  if (r2 <= pm * pm * 0.999f) return true;
-  return in_active_brick(bg, p);
 }
 
 __device__ __forceinline__ float2 interp_global_t(const float2* __restrict__ V, const KGeom& g, const float p[3],

@@ -1,0 +1,612 @@
+// Backward / adjoint kernels of libtproj for gfx950: the 2D->3D
+// back-projection (with the weight channel) and the fused backward of the
+// 3D->2D forward (volume, rotation and shift gradients in one pass).
+//
+// The back-projection is the exact adjoint of the rotated-central-slice
+// forward: every in-mask pixel adds w * conj(phi) * Y to each of its taps
+// (conjugated where the tap is a Friedel mate) and w * Wimg to the weight
+// volume (French page, "Resume technique" 2: accumulation with weights for CTF
+// correction; Dutch page, Methodologie: Friedel symmetry).  The rotation and
+// shift gradients follow from differentiating the forward (Spanish page,
+// "Resumen tecnico" 2: gradients for inputs, rotations and shifts).
+//
+// Decomposition: the same tap-space bricks as the forward gather.  A pixel
+// belongs to the brick holding floor(p), so every pixel is visited once and all
+// its taps fall in the brick's 16^3 halo tile.  The workgroup accumulates the
+// taps of its pixels in that tile in LDS and writes the tile to a workspace
+// slot; a fold kernel then adds, for every stored voxel, the tile entries of
+// all its preimages in tap space (direct copies, and conjugated Friedel mates)
+// in a fixed order.  Float atomics in LDS are slow on this GPU while 64-bit
+// integer ones are not, so the tile holds fixed-point words (re + im * 2^32,
+// one ds_add_u64 per tap).  Taps are accumulated in windows of up to 16 poses
+// whose scale is set, before the window, from per-image maxima in radial
+// bands of |k| and a bound on the contributions a voxel can receive; no sum
+// can overflow, and integer sums make the result deterministic.  With the
+// volume gradient, the same pass also interpolates the forward volume (second
+// LDS tile) for the rotation and shift gradients.
+#include "brick_grid.h"
+#include "brick_kernels.h"
+#include "bwd_kernels.h"
+#include "device_common.h"
+#include "gather_common.h"
+
+namespace tproj {
+
+namespace {
+
+constexpr int TE = 16;                     // tile edge
+constexpr int TSY = 17;                    // padded strides (as the gather tile)
+constexpr int TSZ = 16 * 17 + 4;
+constexpr int TSIZE = TE * TSZ;            // 4416 padded entries
+constexpr int TLOG = TE * TE * TE;         // 4096 logical entries
+constexpr int PER_LANE = TLOG / 256;       // 16
+constexpr int WINDOW = 16;                 // poses per fixed-point window
+constexpr float FIX_RANGE = 0.9f * 2147483648.0f;
+constexpr int MAX_BANDS = 128;
+
+// Fixed-point conversion by the magic-number trick: for |w u| < 2^22,
+// fma(w, u, 1.5 * 2^23) rounds w * u to the nearest integer k in one
+// instruction and its bit pattern is 0x4B400000 + k.
+constexpr float MAGIC = 12582912.0f;
+constexpr int MAGIC_BITS = 0x4B400000;
+
+__device__ __forceinline__ int fixed_round(float w, float u) {
+  return __float_as_int(fmaf(w, u, MAGIC)) - MAGIC_BITS;
+}
+
+// One 64-bit word holding re + im * 2^32 (re signed): sums of such words keep
+// both parts exact as long as each partial sum stays within 31 bits.
+__device__ __forceinline__ unsigned long long pack_fixed(int re, int im) {
+  const unsigned int lo = (unsigned int)re;
+  const unsigned int hi = (unsigned int)(im + (re >> 31));
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+__device__ __forceinline__ void unpack_fixed(unsigned long long w, float& re, float& im) {
+  const long long v = (long long)w;
+  const int r = (int)(unsigned int)(w & 0xffffffffull);
+  const int i = (int)((v - (long long)r) >> 32);
+  re = (float)r;
+  im = (float)i;
+}
+
+__device__ __forceinline__ int padded_index(int idx) { return (idx >> 8) * TSZ + ((idx >> 4) & 15) * TSY + (idx & 15); }
+
+// Bound on the pixels of one pose that can reach one voxel: the voxel's
+// support box (edge NT) cuts the slice in a disc of radius NT*sqrt(3)/2 in
+// sample space, i.e. an ellipse in pixel space whose semi-axes are that radius
+// over the singular values of A = o [R_:0 R_:1]; (2a+1)^2 bounds its pixels.
+template <int NT>
+__device__ __forceinline__ float contrib_bound(const KGeom& g, const float* R) {
+  float g00 = 0.f, g01 = 0.f, g11 = 0.f;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const float c0 = g.o * R[3 * a], c1 = g.o * R[3 * a + 1];
+    g00 = fmaf(c0, c0, g00); g01 = fmaf(c0, c1, g01); g11 = fmaf(c1, c1, g11);
+  }
+  const float d = g00 - g11;
+  const float lam = 0.5f * (g00 + g11 - sqrtf(fmaf(d, d, 4.f * g01 * g01)));
+  const float sig = sqrtf(fmaxf(lam, 0.f));
+  const float a = (0.8660254f * NT) / sig;   // inf for a degenerate map
+  const float c = 2.f * a + 1.f;
+  return c * c;                              // NaN map -> NaN
+}
+// Poses with a larger bound (degenerate maps) go to the edge kernel.
+__device__ __forceinline__ bool pose_ok(float cb) { return cb <= 4096.0f; }
+
+// Largest value a pose can put into the brick [bl, bh): the bands of the pixel
+// radii |k| in [|p| / sigma_max, |p| / sigma_min] for p in the brick.
+__device__ __forceinline__ float box_band_max(const KGeom& g, const BwdGrid& bw, const float* R,
+                                              const float* __restrict__ table, int64_t pose, const float bl[3],
+                                              const float bh[3]) {
+  float g00 = 0.f, g01 = 0.f, g11 = 0.f;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const float c0 = g.o * R[3 * a], c1 = g.o * R[3 * a + 1];
+    g00 = fmaf(c0, c0, g00); g01 = fmaf(c0, c1, g01); g11 = fmaf(c1, c1, g11);
+  }
+  const float d = g00 - g11, rt = sqrtf(fmaf(d, d, 4.f * g01 * g01));
+  const float smax = sqrtf(fmaxf(0.5f * (g00 + g11 + rt), 0.f)), smin = sqrtf(fmaxf(0.5f * (g00 + g11 - rt), 0.f));
+  float dn = 0.f, df = 0.f;
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    const float n = fmaxf(0.f, fmaxf(bl[a], -bh[a]));
+    const float f = fmaxf(fabsf(bl[a]), fabsf(bh[a]));
+    dn = fmaf(n, n, dn);
+    df = fmaf(f, f, df);
+  }
+  const float kmin = sqrtf(dn) / smax - 1.0f, kmax = sqrtf(df) / smin + 1.0f;
+  int b0 = (int)fmaxf(0.f, kmin * bw.inv_band_w);
+  if (!(kmin == kmin)) b0 = 0;
+  const int b1 = (kmax * bw.inv_band_w < (float)bw.nbands) ? (int)(kmax * bw.inv_band_w) : bw.nbands - 1;
+  float m = 0.f;
+  for (int i = b0; i <= b1; ++i) m = fmaxf(m, table[pose * bw.nbands + i]);
+  return m;
+}
+
+__device__ __forceinline__ int floor_div(int a, int b) {  // b > 0
+  return a >= 0 ? a / b : -((-a + b - 1) / b);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Largest |Re|, |Im| (and |Wimg|) of every image per band of pixel radius
+// |k| in [bw * i, bw * (i + 1)).
+// ---------------------------------------------------------------------------
+template <bool WEIGHTS>
+__global__ void __launch_bounds__(256) k_band_max(const float2* __restrict__ Y, const float* __restrict__ Wimg,
+                                                  float* __restrict__ ymax, float* __restrict__ wmax, KGeom g,
+                                                  BwdGrid bw) {
+  __shared__ unsigned int bm[MAX_BANDS], bwm[MAX_BANDS];
+  for (int bn = blockIdx.x; bn < g.B * g.P; bn += gridDim.x) {
+    for (int i = threadIdx.x; i < bw.nbands; i += blockDim.x) { bm[i] = 0u; bwm[i] = 0u; }
+    __syncthreads();
+    const float2* Yb = Y + (int64_t)bn * g.npix;
+    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
+      int ikx, iky;
+      pixel_freq(g, pix, ikx, iky);
+      const float kx = (float)ikx, ky = (float)iky;
+      if (!in_mask(g, kx, ky)) continue;
+      const int band = min((int)(sqrtf(fmaf(kx, kx, ky * ky)) * bw.inv_band_w), bw.nbands - 1);
+      const float2 v = Yb[pix];
+      atomicMax(&bm[band], __float_as_uint(fmaxf(fabsf(v.x), fabsf(v.y))));
+      if constexpr (WEIGHTS) atomicMax(&bwm[band], __float_as_uint(fabsf(Wimg[(int64_t)bn * g.npix + pix])));
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < bw.nbands; i += blockDim.x) {
+      ymax[(int64_t)bn * bw.nbands + i] = __uint_as_float(bm[i]);
+      if constexpr (WEIGHTS) wmax[(int64_t)bn * bw.nbands + i] = __uint_as_float(bwm[i]);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the brick kernel: scatter (SCAT, optional weight channel) and/or the
+// rotation / shift gradients of the forward (GRAD)
+// ---------------------------------------------------------------------------
+template <int NT, bool WEIGHTS, bool GRAD>
+__global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y, const float* __restrict__ Wimg,
+                                                   const float2* __restrict__ vol, const float* __restrict__ rot,
+                                                   const float* __restrict__ shifts, float* __restrict__ grad_rot,
+                                                   float* __restrict__ grad_s, float2* __restrict__ part_c,
+                                                   float* __restrict__ part_w, KGeom g, BwdGrid bw,
+                                                   const int* __restrict__ prefix, const float* __restrict__ ymax,
+                                                   const float* __restrict__ wmax) {
+  const BrickGrid& bg = bw.bg;
+  __shared__ unsigned long long acc_t[TSIZE];
+  __shared__ unsigned int acc_w[WEIGHTS ? TSIZE : 1];
+  __shared__ float2 vt[GRAD ? TSIZE : 1];
+  __shared__ int hits[256];
+  __shared__ float hit_m[256], hit_w[256], hit_c[256];
+  __shared__ int wave_n[4];
+
+  const int w = blockIdx.x, vsel = blockIdx.y;
+  if (w >= bg.nwork) return;
+  const int b = find_brick(prefix, bg.nb3, w);
+  const int chunk = w - prefix[b], nchunk = prefix[b + 1] - prefix[b];
+  int bi, bj, bk;
+  brick_coords(bg, b, bi, bj, bk);
+  const int lo[3] = {bg.origin + bi * bg.S, bg.origin + bj * bg.S, bg.origin + bk * bg.S};
+  const float bl[3] = {(float)lo[0], (float)lo[1], (float)lo[2]};
+  const float bh[3] = {(float)(lo[0] + bg.S), (float)(lo[1] + bg.S), (float)(lo[2] + bg.S)};
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nvol = (int64_t)g.D * g.D * g.W;
+
+  float2 acc[PER_LANE];
+  float accw[PER_LANE];
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) {
+    acc[i] = make_float2(0.f, 0.f);
+    accw[i] = 0.f;
+  }
+  for (int i = tid; i < TSIZE; i += 256) {
+    acc_t[i] = 0ull;
+    if constexpr (WEIGHTS) acc_w[i] = 0u;
+  }
+  if constexpr (GRAD) {
+    using Tl = Tile<NT>;
+    const float2* V = vol + (int64_t)vsel * nvol;
+    for (int i = tid; i < TLOG; i += 256) {
+      const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
+      vt[z * TSZ + y * TSY + x] = tap_value(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
+    }
+  }
+  __syncthreads();
+
+  const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
+  for (int64_t eb = e0; eb < e1; eb += 256) {
+    // ---- hit detection: one pose per lane, with its window bounds ----
+    bool hit = false;
+    float hm = 0.f, hw = 0.f, hc = 0.f;
+    const int64_t e = eb + tid;
+    if (e < e1) {
+      int bimg, n;
+      list_entry(g, vsel, (int)e, bimg, n);
+      const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+      hc = contrib_bound<NT>(g, R);
+      hit = pose_ok(hc) && slice_meets_box(g, R, bl, bh);
+      if (hit) {
+        const int64_t pose = (int64_t)bimg * g.P + n;
+        hm = box_band_max(g, bw, R, ymax, pose, bl, bh);
+        if constexpr (WEIGHTS) hw = box_band_max(g, bw, R, wmax, pose, bl, bh);
+      }
+    }
+    const unsigned long long m = __ballot(hit);
+    if (lane == 0) wave_n[wave] = __popcll(m);
+    __syncthreads();
+    int before = 0, nh = 0;
+    for (int v = 0; v < 4; ++v) { if (v < wave) before += wave_n[v]; nh += wave_n[v]; }
+    if (hit) {
+      const int sl = before + __popcll(m & ((1ull << lane) - 1ull));
+      hits[sl] = (int)e;
+      hit_m[sl] = hm;
+      hit_w[sl] = hw;
+      hit_c[sl] = hc;
+    }
+    __syncthreads();
+
+    for (int hb = 0; hb < nh; hb += WINDOW) {
+      const int nw = min(WINDOW, nh - hb);
+      float M = 0.f, MW = 0.f, C = 0.f;
+      for (int h = 0; h < nw; ++h) {
+        M = fmaxf(M, hit_m[hb + h]);
+        MW = fmaxf(MW, hit_w[hb + h]);
+        C += hit_c[hb + h];
+      }
+      // |re|, |im| <= sqrt(2) M per unit weight (the phase rotates); every
+      // contribution also stays below 2^22 for the magic rounding
+      const float lim = fminf(FIX_RANGE - C, 0.99f * 4194304.0f * C);
+      const float scale = M > 0.f ? lim / (1.41421356f * M * C) : 0.f;
+      const float wscale = (WEIGHTS && MW > 0.f) ? lim / (MW * C) : 0.f;
+
+      for (int h = wave; h < nw; h += 4) {
+        int bimg, n;
+        list_entry(g, vsel, hits[hb + h], bimg, n);
+        const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+        const float* s = shifts ? shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n) : nullptr;
+        SliceRows rows;
+        if (!slice_rows_box(g, R, bl, bh, rows)) continue;
+        const int64_t ib = ((int64_t)bimg * g.P + n) * g.npix;
+        float gacc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) gacc[q] = 0.f;
+        for (int r0 = rows.ky_lo; r0 <= rows.ky_hi; r0 += 64) {
+          RowBatch rb;
+          row_batch(g, rows, r0, lane, rb);
+          for (int base = 0; base < rb.total; base += 64) {   // wave-uniform loop
+            const int i = base + lane;
+            int kx, ky;
+            candidate(rb, r0, i, kx, ky);
+            if (i >= rb.total) continue;
+            const float fkx = (float)kx, fky = (float)ky;
+            float p[3];
+            slice_coord(g, R, fkx, fky, p);
+            int l[3];
+            if (!owned(p, lo, bg.S, l) || !in_mask(g, fkx, fky)) continue;
+            const int64_t k = ib + pixel_index(g, kx, ky);
+            float2 c = Y[k];
+            if (s) c = cmulc(shift_phase(fkx, fky, s[0], s[1], g.inv_h), c);   // conj(phi) * Y
+            float wx[NT], wy[NT], wz[NT];
+            const float fx = p[0] - floorf(p[0]), fy = p[1] - floorf(p[1]), fz = p[2] - floorf(p[2]);
+            axis_weights<NT>(fx, wx);
+            axis_weights<NT>(fy, wy);
+            axis_weights<NT>(fz, wz);
+            if constexpr (GRAD) {
+              // d/dR and d/ds of Re<G, phi I(V)>: conj(G) phi = conj(c)
+              float dx[NT], dy[NT], dz[NT];
+              axis_dweights<NT>(fx, dx);
+              axis_dweights<NT>(fy, dy);
+              axis_dweights<NT>(fz, dz);
+              float2 I = make_float2(0.f, 0.f), d0 = I, d1 = I, d2 = I;
+#pragma unroll
+              for (int jc = 0; jc < NT; ++jc)
+#pragma unroll
+                for (int jb = 0; jb < NT; ++jb) {
+                  const float2* row = vt + (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
+                  float2 r = make_float2(0.f, 0.f), rx = r;
+#pragma unroll
+                  for (int ja = 0; ja < NT; ++ja) {
+                    const float2 v = row[ja];
+                    r.x = fmaf(wx[ja], v.x, r.x); r.y = fmaf(wx[ja], v.y, r.y);
+                    rx.x = fmaf(dx[ja], v.x, rx.x); rx.y = fmaf(dx[ja], v.y, rx.y);
+                  }
+                  const float wyz = wy[jb] * wz[jc], gy = dy[jb] * wz[jc], gz = wy[jb] * dz[jc];
+                  I.x = fmaf(wyz, r.x, I.x); I.y = fmaf(wyz, r.y, I.y);
+                  d0.x = fmaf(wyz, rx.x, d0.x); d0.y = fmaf(wyz, rx.y, d0.y);
+                  d1.x = fmaf(gy, r.x, d1.x); d1.y = fmaf(gy, r.y, d1.y);
+                  d2.x = fmaf(gz, r.x, d2.x); d2.y = fmaf(gz, r.y, d2.y);
+                }
+              const float e0_ = c.x * d0.x + c.y * d0.y, e1_ = c.x * d1.x + c.y * d1.y, e2_ = c.x * d2.x + c.y * d2.y;
+              const float im = c.x * I.y - c.y * I.x;
+              gacc[0] = fmaf(e0_, fkx, gacc[0]); gacc[1] = fmaf(e0_, fky, gacc[1]);
+              gacc[2] = fmaf(e1_, fkx, gacc[2]); gacc[3] = fmaf(e1_, fky, gacc[3]);
+              gacc[4] = fmaf(e2_, fkx, gacc[4]); gacc[5] = fmaf(e2_, fky, gacc[5]);
+              gacc[6] = fmaf(fkx, im, gacc[6]); gacc[7] = fmaf(fky, im, gacc[7]);
+            }
+            // scatter all taps (they all lie in the halo tile)
+            const float cr = c.x * scale, ci = c.y * scale;
+            const float wv = WEIGHTS ? Wimg[k] * wscale : 0.f;
+#pragma unroll
+            for (int jc = 0; jc < NT; ++jc)
+#pragma unroll
+              for (int jb = 0; jb < NT; ++jb) {
+                const float wyz = wy[jb] * wz[jc];
+                const float ur = wyz * cr, ui = wyz * ci, uw = wyz * wv;
+                const int rowb = (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
+#pragma unroll
+                for (int ja = 0; ja < NT; ++ja) {
+                  atomicAdd(&acc_t[rowb + ja], pack_fixed(fixed_round(wx[ja], ur), fixed_round(wx[ja], ui)));
+                  if constexpr (WEIGHTS) atomicAdd(&acc_w[rowb + ja], (unsigned int)fixed_round(wx[ja], uw));
+                }
+              }
+          }
+        }
+        if constexpr (GRAD) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) gacc[q] += __shfl_xor(gacc[q], off, 64);
+          }
+          if (lane == 0) {
+            if (grad_rot) {
+              float* gr = grad_rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+#pragma unroll
+              for (int q = 0; q < 6; ++q) atomicAdd(gr + 3 * (q >> 1) + (q & 1), g.o * gacc[q]);
+            }
+            if (grad_s) {
+              float* gs = grad_s + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
+              atomicAdd(gs, 6.283185307179586f * g.inv_h * gacc[6]);
+              atomicAdd(gs + 1, 6.283185307179586f * g.inv_h * gacc[7]);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // ---- flush the window into the float accumulators ----
+      const float inv = scale > 0.f ? 1.0f / scale : 0.f;
+      const float winv = wscale > 0.f ? 1.0f / wscale : 0.f;
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i) {
+        const int pi = padded_index(tid + 256 * i);
+        const unsigned long long v = acc_t[pi];
+        if (v != 0ull) {
+          float re, im;
+          unpack_fixed(v, re, im);
+          acc[i].x = fmaf(re, inv, acc[i].x);
+          acc[i].y = fmaf(im, inv, acc[i].y);
+          acc_t[pi] = 0ull;
+        }
+        if constexpr (WEIGHTS) {
+          const unsigned int u = acc_w[pi];
+          if (u != 0u) {
+            accw[i] = fmaf((float)(int)u, winv, accw[i]);
+            acc_w[pi] = 0u;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- this work item's partial tile (tap space, logical order) ----
+  const int64_t slot = ((int64_t)vsel * bg.nwork + w) * TLOG;
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) {
+    part_c[slot + tid + 256 * i] = acc[i];
+    if constexpr (WEIGHTS) part_w[slot + tid + 256 * i] = accw[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fold: every stored voxel sums the tile entries of all its tap-space
+// preimages -- direct copies (x, y, z) + D j and, for 1 <= x <= D/2 - 1, the
+// conjugated Friedel mates (-x, -y, -z) + D j -- over every brick tile and
+// chunk that holds them, in a fixed order.
+// ---------------------------------------------------------------------------
+template <int NT, bool WEIGHTS>
+__global__ void __launch_bounds__(256) k_bwd_fold(float2* __restrict__ vol, float* __restrict__ wvol,
+                                                  const float2* __restrict__ part_c, const float* __restrict__ part_w,
+                                                  KGeom g, BwdGrid bw, const int* __restrict__ prefix) {
+  const BrickGrid& bg = bw.bg;
+  constexpr int HL = NT == 4 ? 1 : 0;
+  const int nvol = g.D * g.D * g.W;
+  const int vsel = blockIdx.y;
+  const int tlo = bg.origin - HL, thi = bg.origin + (bg.nb - 1) * bg.S - HL + TE - 1;   // covered taps
+  for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < nvol; v += gridDim.x * blockDim.x) {
+    const int xy = v % (g.W * g.D), z = v / (g.W * g.D);
+    const int x = xy % g.W, y = xy / g.W;
+    float2 a = make_float2(0.f, 0.f);
+    float aw = 0.f;
+    for (int kind = 0; kind < 2; ++kind) {
+      if (kind == 1 && !(x >= 1 && x <= g.half - 1)) break;
+      const int sx = kind ? -x : x, sy = kind ? -y : y, sz = kind ? -z : z;
+      float2 part = make_float2(0.f, 0.f);
+      float partw = 0.f;
+      for (int tz = sz + g.D * floor_div(tlo - sz + g.D - 1, g.D); tz <= thi; tz += g.D) {
+        const int iz0 = max(0, floor_div(tz - bg.origin + HL - TE, bg.S) + 1), iz1 = min(bg.nb - 1, floor_div(tz - bg.origin + HL, bg.S));
+        for (int ty = sy + g.D * floor_div(tlo - sy + g.D - 1, g.D); ty <= thi; ty += g.D) {
+          const int iy0 = max(0, floor_div(ty - bg.origin + HL - TE, bg.S) + 1), iy1 = min(bg.nb - 1, floor_div(ty - bg.origin + HL, bg.S));
+          for (int tx = sx + g.D * floor_div(tlo - sx + g.D - 1, g.D); tx <= thi; tx += g.D) {
+            const int ix0 = max(0, floor_div(tx - bg.origin + HL - TE, bg.S) + 1), ix1 = min(bg.nb - 1, floor_div(tx - bg.origin + HL, bg.S));
+            for (int iz = iz0; iz <= iz1; ++iz)
+              for (int iy = iy0; iy <= iy1; ++iy)
+                for (int ix = ix0; ix <= ix1; ++ix) {
+                  const int bb = (iz * bg.nb + iy) * bg.nb + ix;
+                  const int k0 = prefix[bb], k1 = prefix[bb + 1];
+                  if (k0 == k1) continue;
+                  const int lx = tx - (bg.origin + ix * bg.S - HL), ly = ty - (bg.origin + iy * bg.S - HL),
+                            lz = tz - (bg.origin + iz * bg.S - HL);
+                  const int64_t li = (int64_t)lz * 256 + ly * 16 + lx;
+                  for (int c = k0; c < k1; ++c) {
+                    const int64_t o = ((int64_t)vsel * bg.nwork + c) * TLOG + li;
+                    const float2 t = part_c[o];
+                    part.x += t.x;
+                    part.y += t.y;
+                    if constexpr (WEIGHTS) partw += part_w[o];
+                  }
+                }
+          }
+        }
+      }
+      a.x += part.x;
+      a.y += kind ? -part.y : part.y;
+      aw += partw;
+    }
+    vol[(int64_t)nvol * vsel + v] = a;
+    if constexpr (WEIGHTS) wvol[(int64_t)nvol * vsel + v] = aw;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pixels the bricks do not serve (degenerate maps, samples outside every
+// active brick): their taps with global atomics (after the fold) and, with
+// GRAD, their gradient terms.
+// ---------------------------------------------------------------------------
+template <int NT, bool WEIGHTS, bool GRAD>
+__global__ void __launch_bounds__(256) k_bwd_edge(const float2* __restrict__ Y, const float* __restrict__ Wimg,
+                                                  const float2* __restrict__ volc, const float* __restrict__ rot,
+                                                  const float* __restrict__ shifts, float2* __restrict__ vol,
+                                                  float* __restrict__ wvol, float* __restrict__ grad_rot,
+                                                  float* __restrict__ grad_s, KGeom g, BwdGrid bw) {
+  const BrickGrid& bg = bw.bg;
+  const int pix = blockIdx.x * blockDim.x + threadIdx.x;
+  if (pix >= g.npix) return;
+  int ikx, iky;
+  pixel_freq(g, pix, ikx, iky);
+  const float kx = (float)ikx, ky = (float)iky;
+  if (!in_mask(g, kx, ky)) return;
+  const int64_t nvol = (int64_t)g.D * g.D * g.W;
+  for (int bn = blockIdx.y; bn < g.B * g.P; bn += gridDim.y) {
+    const int bimg = bn / g.P, n = bn - bimg * g.P;
+    const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+    const bool ok = pose_ok(contrib_bound<NT>(g, R));
+    if (ok && pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i) continue;
+    float p[3];
+    slice_coord(g, R, kx, ky, p);
+    if (ok && served_by_bricks(bg, p)) continue;
+    float2 c = Y[(int64_t)bn * g.npix + pix];
+    float2 phi = make_float2(1.f, 0.f);
+    if (shifts) {
+      const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
+      phi = shift_phase(kx, ky, s[0], s[1], g.inv_h);
+    }
+    if constexpr (GRAD) {
+      float2 I, dI[3];
+      interp_c<NT, true>(volc + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, dI);
+      const float2 cu = cmulc(c, phi);   // conj(G) * phi
+      float e[3];
+      for (int a = 0; a < 3; ++a) e[a] = cu.x * dI[a].x - cu.y * dI[a].y;
+      const float im = cu.x * I.y + cu.y * I.x;
+      if (grad_rot) {
+        float* gr = grad_rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+        for (int a = 0; a < 3; ++a) {
+          atomicAdd(gr + 3 * a, g.o * e[a] * kx);
+          atomicAdd(gr + 3 * a + 1, g.o * e[a] * ky);
+        }
+      }
+      if (grad_s) {
+        float* gs = grad_s + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
+        atomicAdd(gs, 6.283185307179586f * g.inv_h * kx * im);
+        atomicAdd(gs + 1, 6.283185307179586f * g.inv_h * ky * im);
+      }
+    }
+    c = cmulc(phi, c);   // conj(phi) * Y
+    const float wimg = WEIGHTS ? Wimg[(int64_t)bn * g.npix + pix] : 0.f;
+    float2* V = vol + nvol * (g.Bv == 1 ? 0 : bimg);
+    float* VW = WEIGHTS ? wvol + nvol * (g.Bv == 1 ? 0 : bimg) : nullptr;
+    const float flx = safe_floor(p[0]), fly = safe_floor(p[1]), flz = safe_floor(p[2]);
+    float wx[NT], wy[NT], wz[NT];
+    axis_weights<NT>(p[0] - flx, wx);
+    axis_weights<NT>(p[1] - fly, wy);
+    axis_weights<NT>(p[2] - flz, wz);
+    const int x0 = (int)flx + first_tap<NT>(), y0 = (int)fly + first_tap<NT>(), z0 = (int)flz + first_tap<NT>();
+    for (int cc = 0; cc < NT; ++cc)
+      for (int bb = 0; bb < NT; ++bb)
+        for (int aa = 0; aa < NT; ++aa) {
+          bool cj;
+          const int64_t idx = tap_index<true>(g, x0 + aa, y0 + bb, z0 + cc, cj);
+          const float wt = wx[aa] * wy[bb] * wz[cc];
+          float* dst = reinterpret_cast<float*>(V + idx);
+          unsafeAtomicAdd(dst, wt * c.x);
+          unsafeAtomicAdd(dst + 1, cj ? -wt * c.y : wt * c.y);
+          if constexpr (WEIGHTS) unsafeAtomicAdd(VW + idx, wt * wimg);
+        }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights) {
+  const size_t prefix = align256((size_t)(bw.bg.nb3 + 1) * sizeof(int));
+  const size_t bands = align256((size_t)bw.npose * bw.nbands * sizeof(float) * (weights ? 2 : 1));
+  const size_t parts = (size_t)bw.bg.nwork * Bv * TLOG * (sizeof(float2) + (weights ? sizeof(float) : 0));
+  return prefix + bands + parts;
+}
+
+hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* workspace, const float2* Y,
+                      const float* Wimg, const float2* volc, const float* rot, const float* shifts, float2* vol,
+                      float* wvol, float* grad_rot, float* grad_s, hipStream_t st) {
+  const bool weights = Wimg != nullptr, grad = volc != nullptr;
+  int* prefix = (int*)workspace;
+  const size_t off_b = align256((size_t)(bw.bg.nb3 + 1) * sizeof(int));
+  float* ymax = (float*)((char*)workspace + off_b);
+  float* wmax = ymax + (size_t)bw.npose * bw.nbands;
+  const size_t off_p = off_b + align256((size_t)bw.npose * bw.nbands * sizeof(float) * (weights ? 2 : 1));
+  float2* part_c = (float2*)((char*)workspace + off_p);
+  float* part_w = (float*)(part_c + (size_t)bw.bg.nwork * g.Bv * TLOG);
+  hipError_t e = launch_brick_prefix(bw.bg, prefix, st);
+  if (e != hipSuccess) return e;
+  const int nb = bw.npose < 65535 ? bw.npose : 65535;
+  if (weights) hipLaunchKernelGGL((k_band_max<true>), dim3(nb), dim3(256), 0, st, Y, Wimg, ymax, wmax, g, bw);
+  else hipLaunchKernelGGL((k_band_max<false>), dim3(nb), dim3(256), 0, st, Y, Wimg, ymax, wmax, g, bw);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 blk(256);
+  if (bw.bg.nwork > 0) {
+    const dim3 grid(bw.bg.nwork, g.Bv);
+#define TP_BWD(NT_, W_, G_)                                                                                    \
+  hipLaunchKernelGGL((k_bwd_brick<NT_, W_, G_>), grid, blk, 0, st, Y, Wimg, volc, rot, shifts, grad_rot, grad_s, \
+                     part_c, part_w, g, bw, prefix, ymax, wmax)
+    if (interp == 1) {
+      if (grad) TP_BWD(4, false, true); else if (weights) TP_BWD(4, true, false); else TP_BWD(4, false, false);
+    } else {
+      if (grad) TP_BWD(2, false, true); else if (weights) TP_BWD(2, true, false); else TP_BWD(2, false, false);
+    }
+#undef TP_BWD
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int64_t nvol = (int64_t)g.D * g.D * g.W;
+    const int blocks = (int)((nvol + 255) / 256 < 8192 ? (nvol + 255) / 256 : 8192);
+    const dim3 fg(blocks, g.Bv);
+    if (interp == 1) {
+      if (weights) hipLaunchKernelGGL((k_bwd_fold<4, true>), fg, blk, 0, st, vol, wvol, part_c, part_w, g, bw, prefix);
+      else hipLaunchKernelGGL((k_bwd_fold<4, false>), fg, blk, 0, st, vol, wvol, part_c, part_w, g, bw, prefix);
+    } else {
+      if (weights) hipLaunchKernelGGL((k_bwd_fold<2, true>), fg, blk, 0, st, vol, wvol, part_c, part_w, g, bw, prefix);
+      else hipLaunchKernelGGL((k_bwd_fold<2, false>), fg, blk, 0, st, vol, wvol, part_c, part_w, g, bw, prefix);
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int gy = g.B * g.P < 2048 ? g.B * g.P : 2048;
+  const dim3 eg((g.npix + 255) / 256, gy);
+#define TP_EDGE(NT_, W_, G_)                                                                                  \
+  hipLaunchKernelGGL((k_bwd_edge<NT_, W_, G_>), eg, blk, 0, st, Y, Wimg, volc, rot, shifts, vol, wvol, grad_rot, \
+                     grad_s, g, bw)
+  if (interp == 1) {
+    if (grad) TP_EDGE(4, false, true); else if (weights) TP_EDGE(4, true, false); else TP_EDGE(4, false, false);
+  } else {
+    if (grad) TP_EDGE(2, false, true); else if (weights) TP_EDGE(2, true, false); else TP_EDGE(2, false, false);
+  }
+#undef TP_EDGE
+  return hipGetLastError();
+}
+
+}  // namespace tproj

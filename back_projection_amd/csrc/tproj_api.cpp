@@ -15,8 +15,7 @@
 #include "brick_grid.h"
 #include "brick_kernels.h"
 #include "kernels.h"
-#include "scatter_grid.h"
-#include "scatter_kernels.h"
+#include "bwd_kernels.h"
 
 namespace {
 
@@ -160,59 +159,26 @@ GatherPlan gather_plan(const tp_geom* g) {
   return pl;
 }
 
-// Brick plan of the adjoint scatter; ok = false -> direct atomic kernel.
-struct ScatterPlan {
+// Brick plan of the back-projection (the forward's tap-space bricks plus the
+// radial band tables of the fixed-point scale); ok = false -> direct kernels.
+struct BwdPlan {
   bool ok = false;
-  tproj::ScatterGrid sg{};
+  tproj::BwdGrid bw{};
   size_t ws_bytes = 0;
 };
 
-ScatterPlan scatter_plan(const tp_geom* g, bool weights) {
-  ScatterPlan pl;
-  if (force_direct()) return pl;
-  tproj::ScatterGrid& sg = pl.sg;
-  const int NT = g->interp == TP_CUBIC ? 4 : 2;
-  const int HL = NT == 4 ? 1 : 0, HH = NT - 1 - HL;
-  sg.S = 16;
-  sg.D = g->D;
-  sg.half = g->D / 2;
-  sg.W = g->D / 2 + 1;
-  sg.nbx = (sg.W + 15) / 16;
-  sg.nby = sg.nbz = (g->D + 15) / 16;
-  sg.nb3 = sg.nbx * sg.nby * sg.nbz;
-  double kmax = std::sqrt(2.0) * (g->H / 2);
-  if (g->radius_cutoff >= 0.0f) kmax = std::min(kmax, (double)g->radius_cutoff);
-  const double pmax = (double)g->oversampling * kmax;
-  if (pmax > 1e5) return pl;
-  const int pmax_i = (int)std::ceil(pmax) + 1;
-  sg.fmin = -pmax_i - 1;
-  sg.fmax = pmax_i;
-  sg.tmin = sg.fmin - HL;
-  sg.tmax = sg.fmax + HH;
-  sg.list_len = (g->Bv == 1 ? g->B : 1) * g->P;
-  sg.dens_q8 = std::max(1, (int)std::lround(256.0 / ((double)g->oversampling * g->oversampling)));
-  const int64_t visits = (int64_t)g->B * g->P * pixels_in_mask(g) * 17 / 10;
-  sg.target = std::max<int64_t>(1024, visits / 4096);
-  sg.weights = weights ? 1 : 0;
-  sg.npose = g->B * g->P;
-  {
-    const double kimg = std::sqrt(2.0) * (g->H / 2) + 1.0;
-    const double bw = std::max(1.0, std::ceil(kimg / 64.0));
-    sg.nbands = (int)std::ceil(kimg / bw) + 1;
-    sg.inv_band_w = (float)(1.0 / bw);
-  }
-  int64_t nwork = 0, nslots = 0;
-  for (int b = 0; b < sg.nb3; ++b) {
-    int bi, bj, bk;
-    tproj::sbrick_coords(sg, b, bi, bj, bk);
-    const int k = tproj::sbrick_chunks(sg, bi, bj, bk);
-    nwork += k;
-    if (k > 1) nslots += k;
-  }
-  if (nwork > INT32_MAX / 2 || nslots > INT32_MAX / 8) return pl;
-  sg.nwork = (int)nwork;
-  sg.nslots = (int)nslots;
-  pl.ws_bytes = tproj::scatter_ws_bytes(sg, g->Bv);
+BwdPlan bwd_plan(const tp_geom* g, bool weights) {
+  BwdPlan pl;
+  const GatherPlan gp = gather_plan(g);
+  if (!gp.ok) return pl;
+  tproj::BwdGrid& bw = pl.bw;
+  bw.bg = gp.bg;
+  bw.npose = g->B * g->P;
+  const double kimg = std::sqrt(2.0) * (g->H / 2) + 1.0;
+  const double band = std::max(1.0, std::ceil(kimg / 64.0));
+  bw.nbands = (int)std::ceil(kimg / band) + 1;
+  bw.inv_band_w = (float)(1.0 / band);
+  pl.ws_bytes = tproj::bwd_ws_bytes(bw, g->Bv, weights);
   pl.ok = true;
   return pl;
 }
@@ -309,20 +275,29 @@ tp_status run_forward_real(const tp_geom* geom, const tproj::KGeom& k, const flo
   return TP_OK;
 }
 
-tp_status run_scatter(const tp_geom* geom, const tproj::KGeom& k, const float2* Y, const float* Wimg,
-                      const float* rot, const float* shifts, float2* vol, float* wvol, void* workspace,
-                      size_t ws_bytes, hipStream_t st) {
-  const ScatterPlan pl = scatter_plan(geom, Wimg != nullptr);
+// Back-projection of Y (and of the weight images Wimg into wvol): bricks,
+// else zeroed volumes and direct atomics.  With volc, the rotation / shift
+// gradients of the forward are computed in the same pass (the caller zeroes
+// them); without the brick plan they go to the direct gradient kernel.
+tp_status run_bwd(const tp_geom* geom, const tproj::KGeom& k, const float2* Y, const float* Wimg,
+                  const float2* volc, const float* rot, const float* shifts, float2* vol, float* wvol,
+                  float* grad_rot, float* grad_shifts, void* workspace, size_t ws_bytes, hipStream_t st) {
+  const BwdPlan pl = bwd_plan(geom, Wimg != nullptr);
   if (!pl.ok) {
     LAUNCH(tproj::launch_zero((float*)vol, 2 * vol_elems(geom) * geom->Bv, st), "zero volume");
     if (wvol) LAUNCH(tproj::launch_zero(wvol, vol_elems(geom) * geom->Bv, st), "zero weight volume");
     LAUNCH(tproj::launch_spread_atomic(k, geom->interp, Y, Wimg, rot, shifts, vol, wvol, st), "scatter");
+    if (volc)
+      LAUNCH(tproj::launch_rot_shift_grad(k, geom->interp, volc, nullptr, Y, nullptr, rot, shifts, grad_rot,
+                                          grad_shifts, st),
+             "rotation/shift grads");
     return TP_OK;
   }
   if (!workspace || ws_bytes < pl.ws_bytes)
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
-  LAUNCH(tproj::launch_scatter_brick(k, geom->interp, pl.sg, workspace, Y, Wimg, rot, shifts, vol, wvol, st),
-         "scatter (bricks)");
+  LAUNCH(tproj::launch_bwd(k, geom->interp, pl.bw, workspace, Y, Wimg, volc, rot, shifts, vol, wvol, grad_rot,
+                           grad_shifts, st),
+         "back-projection (bricks)");
   return TP_OK;
 }
 
@@ -364,8 +339,8 @@ namespace {
 size_t workspace_need(const tp_geom* geom, int op) {
   const size_t gather = gather_plan(geom).ws_bytes;
   if (op == TP_OP_PROJECT || op == TP_OP_BACKPROJECT_BACKWARD) return gather;
-  if (op == TP_OP_PROJECT_BACKWARD) return std::max(gather, scatter_plan(geom, false).ws_bytes);
-  return scatter_plan(geom, true).ws_bytes;
+  if (op == TP_OP_PROJECT_BACKWARD) return std::max(gather, bwd_plan(geom, false).ws_bytes);
+  return bwd_plan(geom, true).ws_bytes;
 }
 }  // namespace
 
@@ -407,12 +382,20 @@ tp_status project_3d_to_2d_backward(const tp_geom* geom, const void* grad_out, c
   TRY(check_device());
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
-  if (grad_vol)
-    TRY(run_scatter(geom, k, (const float2*)grad_out, nullptr, rot, shifts, (float2*)grad_vol, nullptr, workspace,
-                    ws_bytes, st));
-  if (grad_rot || grad_shifts)
+  if (grad_vol && (grad_rot || grad_shifts)) {
+    // one pass: the adjoint scatter and the rotation / shift gradients
+    if (grad_rot) LAUNCH(tproj::launch_zero(grad_rot, 9 * (int64_t)geom->Br * geom->P, st), "zero grad_rot");
+    if (grad_shifts)
+      LAUNCH(tproj::launch_zero(grad_shifts, 2 * (int64_t)geom->Bs * geom->P, st), "zero grad_shifts");
+    TRY(run_bwd(geom, k, (const float2*)grad_out, nullptr, (const float2*)vol, rot, shifts, (float2*)grad_vol,
+                nullptr, grad_rot, grad_shifts, workspace, ws_bytes, st));
+  } else if (grad_vol) {
+    TRY(run_bwd(geom, k, (const float2*)grad_out, nullptr, nullptr, rot, shifts, (float2*)grad_vol, nullptr,
+                nullptr, nullptr, workspace, ws_bytes, st));
+  } else if (grad_rot || grad_shifts) {
     TRY(run_grads(geom, k, (const float2*)vol, nullptr, (const float2*)grad_out, nullptr, rot, shifts, grad_rot,
                   grad_shifts, workspace, ws_bytes, st));
+  }
   return ok();
 }
 
@@ -434,8 +417,8 @@ tp_status backproject_2d_to_3d(const tp_geom* geom, const void* images, const fl
   TRY(check_device());
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
-  TRY(run_scatter(geom, k, (const float2*)images, weights, rot, shifts, (float2*)data_vol, weight_vol, workspace,
-                  ws_bytes, st));
+  TRY(run_bwd(geom, k, (const float2*)images, weights, nullptr, rot, shifts, (float2*)data_vol, weight_vol, nullptr,
+              nullptr, workspace, ws_bytes, st));
   return ok();
 }
 
