@@ -25,6 +25,7 @@
 #include "brick_grid.h"
 #include "brick_kernels.h"
 #include "device_common.h"
+#include "enum_block.h"
 #include "gather_common.h"
 
 namespace tproj {
@@ -129,32 +130,20 @@ __device__ __forceinline__ void interp_tile_t(const T* tile, const float p[3], c
   }
 }
 
-// One pose per lane of a block of 256: does its slice reach the box?  The hit
-// poses are compacted into hits[]; returns their count (block-uniform).
-__device__ __forceinline__ int detect_hits(const KGeom& g, const float* __restrict__ rot, int vsel, int64_t eb,
-                                           int64_t e1, const float bl[3], const float bh[3], int* hits,
-                                           int* wave_n) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  bool hit = false;
-  const int64_t e = eb + tid;
-  if (e < e1) {
-    int bimg, n;
-    list_entry(g, vsel, (int)e, bimg, n);
-    hit = slice_meets_box(g, rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n), bl, bh);
-  }
-  const unsigned long long m = __ballot(hit);
-  if (lane == 0) wave_n[wave] = __popcll(m);
-  __syncthreads();
-  int before = 0, nh = 0;
-  for (int v = 0; v < 4; ++v) { if (v < wave) before += wave_n[v]; nh += wave_n[v]; }
-  if (hit) hits[before + __popcll(m & ((1ull << lane) - 1ull))] = (int)e;
-  __syncthreads();
-  return nh;
+// One pose per thread of the pass: does its slice reach the box?
+__device__ __forceinline__ bool pose_hits(const KGeom& g, const float* __restrict__ rot, int vsel, int64_t e,
+                                          int64_t e1, const float bl[3], const float bh[3]) {
+  if (e >= e1) return false;
+  int bimg, n;
+  list_entry(g, vsel, (int)e, bimg, n);
+  return slice_meets_box(g, rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n), bl, bh);
 }
 
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
+constexpr int FWD_WIN = 32;
+
 template <int NT, typename T>
 __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, const float* __restrict__ rot,
                                                    const float* __restrict__ shifts, T* __restrict__ out, KGeom g,
@@ -162,8 +151,7 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
   using Tl = Tile<NT>;
   constexpr bool CPLX = sizeof(T) == 8;
   __shared__ T tile[Tl::SIZE];
-  __shared__ int hits[256];
-  __shared__ int wave_n[4];
+  __shared__ EnumShared<FWD_WIN> es;
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
   const int b = find_brick(prefix, bg.nb3, w);
@@ -178,45 +166,37 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
 
   const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int64_t eb = e0; eb < e1; eb += 256) {
-    const int nh = detect_hits(g, rot, vsel, eb, e1, bl, bh, hits, wave_n);
-    for (int h = wave; h < nh; h += 4) {
-      int bimg, n;
-      list_entry(g, vsel, hits[h], bimg, n);
-      const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-      const float* s = (CPLX && shifts) ? shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n) : nullptr;
-      SliceRows rows;
-      if (!slice_rows_box(g, R, bl, bh, rows)) continue;
-      T* O = out + ((int64_t)bimg * g.P + n) * g.npix;
-      for (int r0 = rows.ky_lo; r0 <= rows.ky_hi; r0 += 64) {
-        RowBatch rb;
-        row_batch(g, rows, r0, lane, rb);
-        for (int base = 0; base < rb.total; base += 64) {   // wave-uniform loop
-          const int i = base + lane;
-          int kx, ky;
-          candidate(rb, r0, i, kx, ky);
-          if (i >= rb.total) continue;
+  for (int64_t eb = e0; eb < e1; eb += EB_THREADS) {
+    int slot;
+    const int64_t e = eb + threadIdx.x;
+    const int nh = compact_hits(es, pose_hits(g, rot, vsel, e, e1, bl, bh), (int)e, slot);
+    for (int hw = 0; hw < nh; hw += FWD_WIN) {
+      const int nw = min(FWD_WIN, nh - hw);
+      window_setup(es, g, rot, CPLX ? shifts : nullptr, vsel, hw, nw, bl, bh);
+      const int nrows = es.hrow[nw];
+      for (int qb = 0; qb < nrows; qb += EB_ROWS) {
+        const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh);
+        for (int i = wave * 64 + lane; i < ncand; i += EB_THREADS) {
+          int h, kx, ky;
+          candidate_at(es, i, h, kx, ky);
           const float fkx = (float)kx, fky = (float)ky;
+          const float4 c0 = es.geo0[h], c1 = es.geo1[h];
           float p[3];
-          slice_coord(g, R, fkx, fky, p);
+          slice_coord_cols(g, c0, c1, fkx, fky, p);
           int l[3];
           if (!owned(p, lo, bg.S, l) || !in_mask(g, fkx, fky)) continue;
           T I;
           interp_tile_t<NT, false>(tile, p, l, I, (T*)nullptr);
           if constexpr (CPLX) {
-            if (s) I = cmul(shift_phase(fkx, fky, s[0], s[1], g.inv_h), I);
+            if (shifts) I = cmul(shift_phase(fkx, fky, c1.z, c1.w, g.inv_h), I);
           }
-          O[pixel_index(g, kx, ky)] = I;
+          out[(int64_t)es.hpose[h] * g.npix + pixel_index(g, kx, ky)] = I;
         }
+        __syncthreads();   // the next row stage rewrites the rows
       }
+      __syncthreads();     // the next window rewrites the hit table
     }
-    __syncthreads();   // hits[] is rewritten by the next block of poses
   }
-}
-
-__device__ __forceinline__ float2 interp_global_t(const float2* __restrict__ V, const KGeom& g, const float p[3],
-                                                  int interp) {
-  return interp == 1 ? interp_global<4>(V, g, p) : interp_global<2>(V, g, p);
 }
 
 // Masked pixels -> 0; pixels outside every active brick -> direct gather.
@@ -262,29 +242,13 @@ __global__ void __launch_bounds__(256) k_fwd_edge(const T* __restrict__ vol, con
 // rotation / shift gradients
 //   gR[i][j] += o * sum_k M (Re(conj(U) phi dI_i(Vc)) + Ur dI_i(Vr)) k3_j
 //   gs       += (2 pi / H) sum_k M (kx, ky) Im(conj(U) phi I(Vc))
+// Each candidate lane computes its 8 terms; a segmented sum over the lanes of
+// one hit (candidates are ordered by hit) leaves the hit's partial in its last
+// lane, which adds it to a per-wavefront, per-hit sum in LDS.  At the end of a
+// window the four wavefronts' sums go to the pose's gradient with global
+// atomics.
 // ---------------------------------------------------------------------------
-template <bool CPLX>
-__device__ __forceinline__ void add_grads(const KGeom& g, float* acc, float* __restrict__ grad_rot,
-                                          float* __restrict__ grad_s, int bimg, int n) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc[q] += __shfl_xor(acc[q], off, 64);
-  }
-  if (lane == 0) {
-    if (grad_rot) {
-      float* gr = grad_rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-#pragma unroll
-      for (int q = 0; q < 6; ++q) atomicAdd(gr + 3 * (q >> 1) + (q & 1), g.o * acc[q]);
-    }
-    if (CPLX && grad_s) {
-      float* gs = grad_s + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
-      atomicAdd(gs, 6.283185307179586f * g.inv_h * acc[6]);
-      atomicAdd(gs + 1, 6.283185307179586f * g.inv_h * acc[7]);
-    }
-  }
-}
+constexpr int GRAD_WIN = 32;
 
 template <int NT, bool CPLX, bool REAL>
 __global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ volc, const float* __restrict__ volr,
@@ -295,8 +259,8 @@ __global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ v
   using Tl = Tile<NT>;
   __shared__ float2 tc[CPLX ? Tl::SIZE : 1];
   __shared__ float tr[REAL ? Tl::SIZE : 1];
-  __shared__ int hits[256];
-  __shared__ int wave_n[4];
+  __shared__ EnumShared<GRAD_WIN> es;
+  __shared__ float gw[4][GRAD_WIN][8];
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
   const int b = find_brick(prefix, bg.nb3, w);
@@ -309,67 +273,72 @@ __global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ v
   const int64_t nvol = (int64_t)g.D * g.D * g.W;
   if constexpr (CPLX) stage_tile_t<NT>(tc, volc + (int64_t)vsel * nvol, g, lo);
   if constexpr (REAL) stage_tile_t<NT>(tr, volr + (int64_t)vsel * nvol, g, lo);
+  for (int i = threadIdx.x; i < 4 * GRAD_WIN * 8; i += EB_THREADS) (&gw[0][0][0])[i] = 0.f;
   __syncthreads();
 
   const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int64_t eb = e0; eb < e1; eb += 256) {
-    const int nh = detect_hits(g, rot, vsel, eb, e1, bl, bh, hits, wave_n);
-    for (int h = wave; h < nh; h += 4) {
-      int bimg, n;
-      list_entry(g, vsel, hits[h], bimg, n);
-      const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-      const float* s = (CPLX && shifts) ? shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n) : nullptr;
-      SliceRows rows;
-      if (!slice_rows_box(g, R, bl, bh, rows)) continue;
-      const int64_t ib = ((int64_t)bimg * g.P + n) * g.npix;
-      float acc[8];
+  for (int64_t eb = e0; eb < e1; eb += EB_THREADS) {
+    int slot;
+    const int64_t e = eb + threadIdx.x;
+    const int nh = compact_hits(es, pose_hits(g, rot, vsel, e, e1, bl, bh), (int)e, slot);
+    for (int hw = 0; hw < nh; hw += GRAD_WIN) {
+      const int nw = min(GRAD_WIN, nh - hw);
+      window_setup(es, g, rot, CPLX ? shifts : nullptr, vsel, hw, nw, bl, bh);
+      const int nrows = es.hrow[nw];
+      for (int qb = 0; qb < nrows; qb += EB_ROWS) {
+        const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh);
+        for (int c0 = wave * 64; c0 < ncand; c0 += EB_THREADS) {   // wave-uniform: the sums need every lane
+          const int i = c0 + lane;
+          float acc[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-      for (int r0 = rows.ky_lo; r0 <= rows.ky_hi; r0 += 64) {
-        RowBatch rb;
-        row_batch(g, rows, r0, lane, rb);
-        for (int base = 0; base < rb.total; base += 64) {
-          const int i = base + lane;
-          int kx, ky;
-          candidate(rb, r0, i, kx, ky);
-          if (i >= rb.total) continue;
-          const float fkx = (float)kx, fky = (float)ky;
-          float p[3];
-          slice_coord(g, R, fkx, fky, p);
-          int l[3];
-          if (!owned(p, lo, bg.S, l) || !in_mask(g, fkx, fky)) continue;
-          const int64_t k = ib + pixel_index(g, kx, ky);
-          float e[3] = {0.f, 0.f, 0.f};
-          if constexpr (CPLX) {
-            float2 I, dI[3];
-            interp_tile_t<NT, true>(tc, p, l, I, dI);
-            float2 phi = make_float2(1.f, 0.f);
-            if (s) phi = shift_phase(fkx, fky, s[0], s[1], g.inv_h);
-            const float2 cu = cmulc(U[k], phi);   // conj(U) * phi
+          for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+          int key = EB_SENTINEL;
+          if (i < ncand) {
+            int h, kx, ky;
+            candidate_at(es, i, h, kx, ky);
+            key = h;
+            const float fkx = (float)kx, fky = (float)ky;
+            const float4 c0v = es.geo0[h], c1v = es.geo1[h];
+            float p[3];
+            slice_coord_cols(g, c0v, c1v, fkx, fky, p);
+            int l[3];
+            if (owned(p, lo, bg.S, l) && in_mask(g, fkx, fky)) {
+              const int64_t k = (int64_t)es.hpose[h] * g.npix + pixel_index(g, kx, ky);
+              float e3[3] = {0.f, 0.f, 0.f};
+              if constexpr (CPLX) {
+                float2 I, dI[3];
+                interp_tile_t<NT, true>(tc, p, l, I, dI);
+                float2 phi = make_float2(1.f, 0.f);
+                if (shifts) phi = shift_phase(fkx, fky, c1v.z, c1v.w, g.inv_h);
+                const float2 cu = cmulc(U[k], phi);   // conj(U) * phi
 #pragma unroll
-            for (int a = 0; a < 3; ++a) e[a] = cu.x * dI[a].x - cu.y * dI[a].y;
-            const float im = cu.x * I.y + cu.y * I.x;
-            acc[6] = fmaf(fkx, im, acc[6]);
-            acc[7] = fmaf(fky, im, acc[7]);
+                for (int a = 0; a < 3; ++a) e3[a] = cu.x * dI[a].x - cu.y * dI[a].y;
+                const float im = cu.x * I.y + cu.y * I.x;
+                acc[6] = fkx * im;
+                acc[7] = fky * im;
+              }
+              if constexpr (REAL) {
+                float I, dI[3];
+                interp_tile_t<NT, true>(tr, p, l, I, dI);
+                const float wv = Ur[k];
+#pragma unroll
+                for (int a = 0; a < 3; ++a) e3[a] = fmaf(wv, dI[a], e3[a]);
+              }
+#pragma unroll
+              for (int a = 0; a < 3; ++a) {
+                acc[2 * a] = e3[a] * fkx;
+                acc[2 * a + 1] = e3[a] * fky;
+              }
+            }
           }
-          if constexpr (REAL) {
-            float I, dI[3];
-            interp_tile_t<NT, true>(tr, p, l, I, dI);
-            const float wv = Ur[k];
-#pragma unroll
-            for (int a = 0; a < 3; ++a) e[a] = fmaf(wv, dI[a], e[a]);
-          }
-#pragma unroll
-          for (int a = 0; a < 3; ++a) {
-            acc[2 * a] = fmaf(e[a], fkx, acc[2 * a]);
-            acc[2 * a + 1] = fmaf(e[a], fky, acc[2 * a + 1]);
-          }
+          grad_collect<GRAD_WIN>(acc, key, gw);
         }
+        __syncthreads();
       }
-      add_grads<CPLX>(g, acc, grad_rot, grad_s, bimg, n);
+      grad_flush<GRAD_WIN>(g, es, gw, nw, grad_rot, CPLX ? grad_s : nullptr);
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 

@@ -28,6 +28,7 @@
 #include "brick_kernels.h"
 #include "bwd_kernels.h"
 #include "device_common.h"
+#include "enum_block.h"
 #include "gather_common.h"
 
 namespace tproj {
@@ -178,9 +179,9 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
   __shared__ unsigned long long acc_t[TSIZE];
   __shared__ unsigned int acc_w[WEIGHTS ? TSIZE : 1];
   __shared__ float2 vt[GRAD ? TSIZE : 1];
-  __shared__ int hits[256];
-  __shared__ float hit_m[256], hit_w[256], hit_c[256];
-  __shared__ int wave_n[4];
+  __shared__ EnumShared<WINDOW> es;
+  __shared__ float hit_m[EB_THREADS], hit_w[EB_THREADS], hit_c[EB_THREADS];
+  __shared__ float gw[GRAD ? 4 : 1][WINDOW][8];
 
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
@@ -201,25 +202,26 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
     acc[i] = make_float2(0.f, 0.f);
     accw[i] = 0.f;
   }
-  for (int i = tid; i < TSIZE; i += 256) {
+  for (int i = tid; i < TSIZE; i += EB_THREADS) {
     acc_t[i] = 0ull;
     if constexpr (WEIGHTS) acc_w[i] = 0u;
   }
   if constexpr (GRAD) {
     using Tl = Tile<NT>;
     const float2* V = vol + (int64_t)vsel * nvol;
-    for (int i = tid; i < TLOG; i += 256) {
+    for (int i = tid; i < TLOG; i += EB_THREADS) {
       const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
       vt[z * TSZ + y * TSY + x] = tap_value(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
     }
+    for (int i = tid; i < 4 * WINDOW * 8; i += EB_THREADS) (&gw[0][0][0])[i] = 0.f;
   }
   __syncthreads();
 
   const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
-  for (int64_t eb = e0; eb < e1; eb += 256) {
-    // ---- hit detection: one pose per lane, with its window bounds ----
+  for (int64_t eb = e0; eb < e1; eb += EB_THREADS) {
+    // ---- hit detection: one pose per thread, with its window bounds ----
     bool hit = false;
-    float hm = 0.f, hw = 0.f, hc = 0.f;
+    float hm = 0.f, hwm = 0.f, hc = 0.f;
     const int64_t e = eb + tid;
     if (e < e1) {
       int bimg, n;
@@ -230,20 +232,15 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
       if (hit) {
         const int64_t pose = (int64_t)bimg * g.P + n;
         hm = box_band_max(g, bw, R, ymax, pose, bl, bh);
-        if constexpr (WEIGHTS) hw = box_band_max(g, bw, R, wmax, pose, bl, bh);
+        if constexpr (WEIGHTS) hwm = box_band_max(g, bw, R, wmax, pose, bl, bh);
       }
     }
-    const unsigned long long m = __ballot(hit);
-    if (lane == 0) wave_n[wave] = __popcll(m);
-    __syncthreads();
-    int before = 0, nh = 0;
-    for (int v = 0; v < 4; ++v) { if (v < wave) before += wave_n[v]; nh += wave_n[v]; }
-    if (hit) {
-      const int sl = before + __popcll(m & ((1ull << lane) - 1ull));
-      hits[sl] = (int)e;
-      hit_m[sl] = hm;
-      hit_w[sl] = hw;
-      hit_c[sl] = hc;
+    int slot;
+    const int nh = compact_hits(es, hit, (int)e, slot);
+    if (slot >= 0) {
+      hit_m[slot] = hm;
+      hit_w[slot] = hwm;
+      hit_c[slot] = hc;
     }
     __syncthreads();
 
@@ -261,109 +258,89 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
       const float scale = M > 0.f ? lim / (1.41421356f * M * C) : 0.f;
       const float wscale = (WEIGHTS && MW > 0.f) ? lim / (MW * C) : 0.f;
 
-      for (int h = wave; h < nw; h += 4) {
-        int bimg, n;
-        list_entry(g, vsel, hits[hb + h], bimg, n);
-        const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-        const float* s = shifts ? shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n) : nullptr;
-        SliceRows rows;
-        if (!slice_rows_box(g, R, bl, bh, rows)) continue;
-        const int64_t ib = ((int64_t)bimg * g.P + n) * g.npix;
-        float gacc[8];
+      window_setup(es, g, rot, shifts, vsel, hb, nw, bl, bh);
+      const int nrows = es.hrow[nw];
+      for (int qb = 0; qb < nrows; qb += EB_ROWS) {
+        const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh);
+        for (int c0 = wave * 64; c0 < ncand; c0 += EB_THREADS) {   // wave-uniform (segmented sums)
+          const int i = c0 + lane;
+          float gacc[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) gacc[q] = 0.f;
-        for (int r0 = rows.ky_lo; r0 <= rows.ky_hi; r0 += 64) {
-          RowBatch rb;
-          row_batch(g, rows, r0, lane, rb);
-          for (int base = 0; base < rb.total; base += 64) {   // wave-uniform loop
-            const int i = base + lane;
-            int kx, ky;
-            candidate(rb, r0, i, kx, ky);
-            if (i >= rb.total) continue;
+          for (int q = 0; q < 8; ++q) gacc[q] = 0.f;
+          int key = EB_SENTINEL;
+          if (i < ncand) {
+            int h, kx, ky;
+            candidate_at(es, i, h, kx, ky);
+            key = h;
             const float fkx = (float)kx, fky = (float)ky;
+            const float4 c0v = es.geo0[h], c1v = es.geo1[h];
             float p[3];
-            slice_coord(g, R, fkx, fky, p);
+            slice_coord_cols(g, c0v, c1v, fkx, fky, p);
             int l[3];
-            if (!owned(p, lo, bg.S, l) || !in_mask(g, fkx, fky)) continue;
-            const int64_t k = ib + pixel_index(g, kx, ky);
-            float2 c = Y[k];
-            if (s) c = cmulc(shift_phase(fkx, fky, s[0], s[1], g.inv_h), c);   // conj(phi) * Y
-            float wx[NT], wy[NT], wz[NT];
-            const float fx = p[0] - floorf(p[0]), fy = p[1] - floorf(p[1]), fz = p[2] - floorf(p[2]);
-            axis_weights<NT>(fx, wx);
-            axis_weights<NT>(fy, wy);
-            axis_weights<NT>(fz, wz);
-            if constexpr (GRAD) {
-              // d/dR and d/ds of Re<G, phi I(V)>: conj(G) phi = conj(c)
-              float dx[NT], dy[NT], dz[NT];
-              axis_dweights<NT>(fx, dx);
-              axis_dweights<NT>(fy, dy);
-              axis_dweights<NT>(fz, dz);
-              float2 I = make_float2(0.f, 0.f), d0 = I, d1 = I, d2 = I;
+            if (owned(p, lo, bg.S, l) && in_mask(g, fkx, fky)) {
+              const int64_t k = (int64_t)es.hpose[h] * g.npix + pixel_index(g, kx, ky);
+              float2 c = Y[k];
+              if (shifts) c = cmulc(shift_phase(fkx, fky, c1v.z, c1v.w, g.inv_h), c);   // conj(phi) * Y
+              float wx[NT], wy[NT], wz[NT];
+              const float fx = p[0] - floorf(p[0]), fy = p[1] - floorf(p[1]), fz = p[2] - floorf(p[2]);
+              axis_weights<NT>(fx, wx);
+              axis_weights<NT>(fy, wy);
+              axis_weights<NT>(fz, wz);
+              if constexpr (GRAD) {
+                // d/dR and d/ds of Re<G, phi I(V)>: conj(G) phi = conj(c)
+                float dx[NT], dy[NT], dz[NT];
+                axis_dweights<NT>(fx, dx);
+                axis_dweights<NT>(fy, dy);
+                axis_dweights<NT>(fz, dz);
+                float2 I = make_float2(0.f, 0.f), d0 = I, d1 = I, d2 = I;
+#pragma unroll
+                for (int jc = 0; jc < NT; ++jc)
+#pragma unroll
+                  for (int jb = 0; jb < NT; ++jb) {
+                    const float2* row = vt + (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
+                    float2 r = make_float2(0.f, 0.f), rx = r;
+#pragma unroll
+                    for (int ja = 0; ja < NT; ++ja) {
+                      const float2 v = row[ja];
+                      r.x = fmaf(wx[ja], v.x, r.x); r.y = fmaf(wx[ja], v.y, r.y);
+                      rx.x = fmaf(dx[ja], v.x, rx.x); rx.y = fmaf(dx[ja], v.y, rx.y);
+                    }
+                    const float wyz = wy[jb] * wz[jc], gy = dy[jb] * wz[jc], gz = wy[jb] * dz[jc];
+                    I.x = fmaf(wyz, r.x, I.x); I.y = fmaf(wyz, r.y, I.y);
+                    d0.x = fmaf(wyz, rx.x, d0.x); d0.y = fmaf(wyz, rx.y, d0.y);
+                    d1.x = fmaf(gy, r.x, d1.x); d1.y = fmaf(gy, r.y, d1.y);
+                    d2.x = fmaf(gz, r.x, d2.x); d2.y = fmaf(gz, r.y, d2.y);
+                  }
+                const float t0 = c.x * d0.x + c.y * d0.y, t1 = c.x * d1.x + c.y * d1.y, t2 = c.x * d2.x + c.y * d2.y;
+                const float im = c.x * I.y - c.y * I.x;
+                gacc[0] = t0 * fkx; gacc[1] = t0 * fky;
+                gacc[2] = t1 * fkx; gacc[3] = t1 * fky;
+                gacc[4] = t2 * fkx; gacc[5] = t2 * fky;
+                gacc[6] = fkx * im; gacc[7] = fky * im;
+              }
+              // scatter all taps (they all lie in the halo tile)
+              const float cr = c.x * scale, ci = c.y * scale;
+              const float wv = WEIGHTS ? Wimg[k] * wscale : 0.f;
 #pragma unroll
               for (int jc = 0; jc < NT; ++jc)
 #pragma unroll
                 for (int jb = 0; jb < NT; ++jb) {
-                  const float2* row = vt + (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
-                  float2 r = make_float2(0.f, 0.f), rx = r;
+                  const float wyz = wy[jb] * wz[jc];
+                  const float ur = wyz * cr, ui = wyz * ci, uw = wyz * wv;
+                  const int rowb = (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
 #pragma unroll
                   for (int ja = 0; ja < NT; ++ja) {
-                    const float2 v = row[ja];
-                    r.x = fmaf(wx[ja], v.x, r.x); r.y = fmaf(wx[ja], v.y, r.y);
-                    rx.x = fmaf(dx[ja], v.x, rx.x); rx.y = fmaf(dx[ja], v.y, rx.y);
+                    atomicAdd(&acc_t[rowb + ja], pack_fixed(fixed_round(wx[ja], ur), fixed_round(wx[ja], ui)));
+                    if constexpr (WEIGHTS) atomicAdd(&acc_w[rowb + ja], (unsigned int)fixed_round(wx[ja], uw));
                   }
-                  const float wyz = wy[jb] * wz[jc], gy = dy[jb] * wz[jc], gz = wy[jb] * dz[jc];
-                  I.x = fmaf(wyz, r.x, I.x); I.y = fmaf(wyz, r.y, I.y);
-                  d0.x = fmaf(wyz, rx.x, d0.x); d0.y = fmaf(wyz, rx.y, d0.y);
-                  d1.x = fmaf(gy, r.x, d1.x); d1.y = fmaf(gy, r.y, d1.y);
-                  d2.x = fmaf(gz, r.x, d2.x); d2.y = fmaf(gz, r.y, d2.y);
                 }
-              const float e0_ = c.x * d0.x + c.y * d0.y, e1_ = c.x * d1.x + c.y * d1.y, e2_ = c.x * d2.x + c.y * d2.y;
-              const float im = c.x * I.y - c.y * I.x;
-              gacc[0] = fmaf(e0_, fkx, gacc[0]); gacc[1] = fmaf(e0_, fky, gacc[1]);
-              gacc[2] = fmaf(e1_, fkx, gacc[2]); gacc[3] = fmaf(e1_, fky, gacc[3]);
-              gacc[4] = fmaf(e2_, fkx, gacc[4]); gacc[5] = fmaf(e2_, fky, gacc[5]);
-              gacc[6] = fmaf(fkx, im, gacc[6]); gacc[7] = fmaf(fky, im, gacc[7]);
             }
-            // scatter all taps (they all lie in the halo tile)
-            const float cr = c.x * scale, ci = c.y * scale;
-            const float wv = WEIGHTS ? Wimg[k] * wscale : 0.f;
-#pragma unroll
-            for (int jc = 0; jc < NT; ++jc)
-#pragma unroll
-              for (int jb = 0; jb < NT; ++jb) {
-                const float wyz = wy[jb] * wz[jc];
-                const float ur = wyz * cr, ui = wyz * ci, uw = wyz * wv;
-                const int rowb = (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
-#pragma unroll
-                for (int ja = 0; ja < NT; ++ja) {
-                  atomicAdd(&acc_t[rowb + ja], pack_fixed(fixed_round(wx[ja], ur), fixed_round(wx[ja], ui)));
-                  if constexpr (WEIGHTS) atomicAdd(&acc_w[rowb + ja], (unsigned int)fixed_round(wx[ja], uw));
-                }
-              }
           }
+          if constexpr (GRAD) grad_collect<WINDOW>(gacc, key, gw);
         }
-        if constexpr (GRAD) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) gacc[q] += __shfl_xor(gacc[q], off, 64);
-          }
-          if (lane == 0) {
-            if (grad_rot) {
-              float* gr = grad_rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-#pragma unroll
-              for (int q = 0; q < 6; ++q) atomicAdd(gr + 3 * (q >> 1) + (q & 1), g.o * gacc[q]);
-            }
-            if (grad_s) {
-              float* gs = grad_s + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
-              atomicAdd(gs, 6.283185307179586f * g.inv_h * gacc[6]);
-              atomicAdd(gs + 1, 6.283185307179586f * g.inv_h * gacc[7]);
-            }
-          }
-        }
+        __syncthreads();
       }
-      __syncthreads();
+      if constexpr (GRAD) grad_flush<WINDOW>(g, es, gw, nw, grad_rot, grad_s);
       // ---- flush the window into the float accumulators ----
       const float inv = scale > 0.f ? 1.0f / scale : 0.f;
       const float winv = wscale > 0.f ? 1.0f / wscale : 0.f;
@@ -391,13 +368,14 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
   }
 
   // ---- this work item's partial tile (tap space, logical order) ----
-  const int64_t slot = ((int64_t)vsel * bg.nwork + w) * TLOG;
+  const int64_t slot0 = ((int64_t)vsel * bg.nwork + w) * TLOG;
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
-    part_c[slot + tid + 256 * i] = acc[i];
-    if constexpr (WEIGHTS) part_w[slot + tid + 256 * i] = accw[i];
+    part_c[slot0 + tid + 256 * i] = acc[i];
+    if constexpr (WEIGHTS) part_w[slot0 + tid + 256 * i] = accw[i];
   }
 }
+
 
 // ---------------------------------------------------------------------------
 // Fold: every stored voxel sums the tile entries of all its tap-space
