@@ -28,7 +28,7 @@ import torch
 
 __all__ = [
     "project_3d_to_2d", "project_3d_to_2d_backward", "backproject_2d_to_3d", "backproject_2d_to_3d_backward",
-    "TprojError", "lib", "Geom", "LIB_PATH", "HEADER_SYMBOLS",
+    "TprojError", "lib", "Geom", "LIB_PATH", "HEADER_SYMBOLS", "timing_enable", "timing_read", "KERNEL_CLASSES",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +38,7 @@ LIB_PATH = os.path.join(_PKG, "libtproj.so")
 HEADER_SYMBOLS = (
     "project_3d_to_2d", "project_3d_to_2d_backward", "backproject_2d_to_3d", "backproject_2d_to_3d_backward",
     "tp_workspace_size", "tp_validate", "tp_status_string", "tp_last_error_detail", "tp_abi_version",
+    "tp_timing_enable", "tp_timing_read",
 )
 
 OP_PROJECT, OP_PROJECT_BACKWARD, OP_BACKPROJECT, OP_BACKPROJECT_BACKWARD = 0, 1, 2, 3
@@ -83,6 +84,10 @@ def lib():
         L.tp_status_string.restype = ctypes.c_char_p
         L.tp_last_error_detail.restype = ctypes.c_char_p
         L.tp_abi_version.restype = ctypes.c_int
+        L.tp_timing_enable.argtypes = [ctypes.c_int]
+        L.tp_timing_enable.restype = ctypes.c_int
+        L.tp_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        L.tp_timing_read.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -90,6 +95,23 @@ def lib():
 def _check(status: int):
     if status != 0:
         raise TprojError(status, lib().tp_last_error_detail().decode())
+
+
+# kernel classes of tp_timing_read (include/tproj.h)
+KERNEL_CLASSES = {"forward": 0, "backward": 1, "gradient": 2, "fold": 3}
+
+
+def timing_enable(on: bool = True):
+    """Start (or stop) event timing of the brick kernels (tp_timing_enable)."""
+    _check(lib().tp_timing_enable(1 if on else 0))
+
+
+def timing_read(kernel_class: str):
+    """(summed milliseconds, launches) of one kernel class since the last read (tp_timing_read)."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check(lib().tp_timing_read(KERNEL_CLASSES[kernel_class], ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def _interp(x) -> int:

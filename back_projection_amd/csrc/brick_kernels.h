@@ -5,6 +5,7 @@
 
 #include "brick_grid.h"
 #include "device_common.h"
+#include "timing.h"
 
 namespace tproj {
 
@@ -13,13 +14,16 @@ hipError_t launch_brick_prefix(const BrickGrid& bg, int* prefix, hipStream_t st)
 // forward: edge kernel (masked pixels, samples outside the active bricks)
 // then the brick kernel; out is fully written.
 hipError_t launch_fwd_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* vol,
-                            const float* rot, const float* shifts, float2* out, hipStream_t st);
+                            const float* rot, const float* shifts, float2* out, hipStream_t st,
+                            const EvPair* ev = nullptr);
 // same for a real volume (weight channel), no phase
 hipError_t launch_fwd_brick_real(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix,
-                                 const float* vol, const float* rot, float* out, hipStream_t st);
+                                 const float* vol, const float* rot, float* out, hipStream_t st,
+                                 const EvPair* ev = nullptr);
 // rotation / shift gradients accumulated (atomically) into zeroed outputs
 hipError_t launch_grad_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* volc,
                              const float* volr, const float2* U, const float* Ur, const float* rot,
-                             const float* shifts, float* grad_rot, float* grad_s, hipStream_t st);
+                             const float* shifts, float* grad_rot, float* grad_s, hipStream_t st,
+                             const EvPair* ev = nullptr);
 
 }  // namespace tproj

@@ -5,6 +5,7 @@
 
 #include "brick_grid.h"
 #include "device_common.h"
+#include "timing.h"
 
 namespace tproj {
 
@@ -24,6 +25,7 @@ size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights);
 // NULL) in the same pass; volc is the forward's volume.
 hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* workspace, const float2* Y,
                       const float* Wimg, const float2* volc, const float* rot, const float* shifts, float2* vol,
-                      float* wvol, float* grad_rot, float* grad_s, hipStream_t st);
+                      float* wvol, float* grad_rot, float* grad_s, hipStream_t st, const EvPair* ev_brick = nullptr,
+                      const EvPair* ev_fold = nullptr);
 
 }  // namespace tproj

@@ -3,20 +3,25 @@
 //
 // A workgroup of 256 threads walks its brick's pose list in passes of 256
 // poses.  Each pass:
-//   1. one pose per thread is tested against the brick; the hit poses are
-//      compacted into a list;
+//   1. one pose per thread is tested against the brick; the hits are kept as
+//      a bit mask;
 //   2. the hits are taken in windows of up to WIN; one thread per hit sets up
 //      the hit's geometry in LDS and bounds its image rows (ky);
-//   3. the rows of the window are laid out one after the other and handled
-//      256 at a time, one per thread: each thread derives the kx interval of
-//      its row from the slab inequalities of the brick and a block-wide scan
-//      turns the interval lengths into candidate offsets;
-//   4. the candidates (kx, ky, hit) of those rows are dealt to the four
-//      wavefronts in chunks of 64, so the lanes stay full across row and hit
-//      boundaries; each lane finds its row by binary search in LDS.
-// The enumeration is a superset of the owned pixels (margins on the
-// intervals); the owner test on floor(p), computed with the one slice_coord
-// expression, decides.
+//   3. the rows of the window are laid out one after the other and handled up
+//      to 256 at a time, one per thread: each thread derives the kx interval
+//      of its row from the slab inequalities of the brick, a block-wide scan
+//      turns the interval lengths into candidate offsets, and each row writes
+//      its index into a per-candidate byte table (a stage takes rows while
+//      their candidates fit the table);
+//   4. the candidates (kx, ky, hit) are dealt to the four wavefronts in
+//      chunks of 64, so the lanes stay full across row and hit boundaries; a
+//      lane finds its row with one table read.
+// The brick kernels are bound by LDS latency more than by anything else: a
+// dependent LDS read waits behind all the LDS traffic (atomics included) the
+// wavefronts have queued, so a candidate's path holds as few of them as
+// possible.  The enumeration is a superset of the owned pixels (margins on
+// the intervals); the owner test on floor(p), computed with the one
+// slice_coord expression, decides.
 #pragma once
 
 #include "gather_common.h"
@@ -25,45 +30,54 @@ namespace tproj {
 
 constexpr int EB_THREADS = 256;
 constexpr int EB_ROWS = 256;
+constexpr int EB_CMAX = 2048;            // candidates per row stage (a row has at most H/2 + 1 <= 2048)
 constexpr int EB_SENTINEL = 0x7fffffff;
 
 template <int WIN>
 struct EnumShared {
-  int hits[EB_THREADS];      // list entries of the hit poses of this pass
+  unsigned long long hitmask[4];   // hit poses of this pass (bit = thread)
   int wave_n[4];
   int wtot[4];
-  float4 geo0[WIN];          // R[0] R[3] R[6] R[1]   (rotation columns 0 and 1)
-  float4 geo1[WIN];          // R[4] R[7] sx sy
-  int hpose[WIN];            // image index b * P + n
-  int hrow[WIN + 1];         // first row of each hit; hrow[nw] = rows of the window
-  int hky[WIN];              // ky of each hit's first row
-  int rpre[EB_ROWS + 1];     // candidates before row r
-  int rkx[EB_ROWS];          // first candidate kx of row r
-  int rkh[EB_ROWS];          // (hit << 16) | (ky & 0xffff)
+  int nr, nc;                      // rows and candidates of the current row stage
+  float4 geo0[WIN];                // R[0] R[3] R[6] R[1]   (rotation columns 0 and 1)
+  float4 geo1[WIN];                // R[4] R[7] sx sy
+  int hpose[WIN];                  // image index b * P + n
+  int hrow[WIN + 1];               // first row of each hit; hrow[nw] = rows of the window
+  int hky[WIN];                    // ky of each hit's first row
+  int rstart[EB_ROWS];             // first candidate of row r
+  int rinfo[EB_ROWS];              // kx0 | (ky & 0xfff) << 11 | hit << 23
+  unsigned char crow[EB_CMAX];     // row of candidate i
 };
 
-// Compact the hit flags of one pass (one pose per thread) into es.hits;
-// returns the hit count (block-uniform) and this thread's slot (-1: no hit).
+// Record the hit flags of one pass (one pose per thread); returns the hit
+// count (block-uniform).
 template <int WIN>
-__device__ __forceinline__ int compact_hits(EnumShared<WIN>& es, bool hit, int e, int& slot) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ int compact_hits(EnumShared<WIN>& es, bool hit) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const unsigned long long m = __ballot(hit);
-  if (lane == 0) es.wave_n[wave] = __popcll(m);
+  if (lane == 0) es.hitmask[wave] = m;
   __syncthreads();
-  int before = 0, nh = 0;
+  int nh = 0;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int c = es.wave_n[v];
-    if (v < wave) before += c;
-    nh += c;
-  }
-  slot = -1;
-  if (hit) {
-    slot = before + __popcll(m & ((1ull << lane) - 1ull));
-    es.hits[slot] = e;
-  }
-  __syncthreads();
+  for (int v = 0; v < 4; ++v) nh += __popcll(es.hitmask[v]);
+  __syncthreads();   // every thread has read the mask before the next pass rewrites it
   return nh;
+}
+
+// Thread offset (within the pass) of the j-th hit (j < the hit count).
+template <int WIN>
+__device__ __forceinline__ int nth_hit(const EnumShared<WIN>& es, int j) {
+  int v = 0;
+  unsigned long long m = es.hitmask[0];
+  while (j >= __popcll(m)) {
+    j -= __popcll(m);
+    m = es.hitmask[++v];
+  }
+  int bit = 0;   // position of the j-th set bit of m
+#pragma unroll
+  for (int step = 32; step >= 1; step >>= 1)
+    if (__popcll(m & ((1ull << (bit + step)) - 1ull)) <= j) bit += step;
+  return 64 * v + bit;
 }
 
 // Slice coordinate from the two rotation columns; the same arithmetic as
@@ -75,11 +89,19 @@ __device__ __forceinline__ void slice_coord_cols(const KGeom& g, const float4& c
   p[2] = g.o * fmaf(c1.y, ky, c0.z * kx);
 }
 
-// Window set-up: threads t < nw take hit hw + t.  Writes the geometry, the
-// image index and the row range of every hit, then the row prefix.
+// The first two rotation columns as a row-major 3x3 array (column 2 unused).
+__device__ __forceinline__ void cols_to_r9(const float4& c0, const float4& c1, float R[9]) {
+  R[0] = c0.x; R[1] = c0.w; R[2] = 0.f;
+  R[3] = c0.y; R[4] = c1.x; R[5] = 0.f;
+  R[6] = c0.z; R[7] = c1.y; R[8] = 0.f;
+}
+
+// Window set-up: threads t < nw take hit hw + t of the pass that starts at
+// list entry eb.  Writes the geometry, the image index and the row range of
+// every hit, then the row prefix.
 template <int WIN>
 __device__ __forceinline__ void window_setup(EnumShared<WIN>& es, const KGeom& g, const float* __restrict__ rot,
-                                             const float* __restrict__ shifts, int vsel, int hw, int nw,
+                                             const float* __restrict__ shifts, int vsel, int64_t eb, int hw, int nw,
                                              const float bl[3], const float bh[3]) {
   static_assert(WIN <= 64, "one wavefront sets up a window");
   const int tid = threadIdx.x;
@@ -87,7 +109,7 @@ __device__ __forceinline__ void window_setup(EnumShared<WIN>& es, const KGeom& g
     int nrows = 0;
     if (tid < nw) {
       int bimg, n;
-      list_entry(g, vsel, es.hits[hw + tid], bimg, n);
+      list_entry(g, vsel, (int)(eb + nth_hit(es, hw + tid)), bimg, n);
       const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
       float sx = 0.f, sy = 0.f;
       if (shifts) {
@@ -149,11 +171,13 @@ __device__ __forceinline__ void row_interval(const KGeom& g, const float a0[3], 
   }
 }
 
-// Row stage: rows qb .. qb + 255 of the window, one per thread.  Returns the
-// number of candidates of these rows (block-uniform).
+// Row stage: rows qb, qb + 1, ... of the window, one per thread, as many as
+// fit EB_ROWS rows and EB_CMAX candidates.  Returns the candidate count and,
+// in nr, the rows taken (both block-uniform; nr >= 1 while rows remain, as one
+// row has at most H/2 + 1 <= EB_CMAX candidates).
 template <int WIN>
 __device__ __forceinline__ int row_stage(EnumShared<WIN>& es, const KGeom& g, int qb, int nrows, int nw,
-                                         const float bl[3], const float bh[3]) {
+                                         const float bl[3], const float bh[3], int& nr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = qb + tid;
   int cnt = 0, kx0 = 0, h = 0, ky = 0;
@@ -183,25 +207,68 @@ __device__ __forceinline__ int row_stage(EnumShared<WIN>& es, const KGeom& g, in
 #pragma unroll
   for (int w = 0; w < 4; ++w)
     if (w < wave) carry += es.wtot[w];
-  es.rpre[tid + 1] = carry + v;
-  if (tid == 0) es.rpre[0] = 0;
-  es.rkx[tid] = kx0;
-  es.rkh[tid] = (h << 16) | (ky & 0xffff);
+  const int incl = carry + v, start = incl - cnt;
+  // the rows whose candidates fit the table: a prefix of the rows, since the
+  // inclusive counts grow
+  const bool take = q < nrows && incl <= EB_CMAX;
+  const unsigned long long tm = __ballot(take);
+  if (lane == 0) es.wave_n[wave] = __popcll(tm);
+  if (take) {
+    es.rstart[tid] = start;
+    es.rinfo[tid] = kx0 | ((ky & 0xfff) << 11) | (h << 23);
+    for (int j = 0; j < cnt; ++j) es.crow[start + j] = (unsigned char)tid;
+  }
   __syncthreads();
-  return es.rpre[EB_ROWS];
+  const int n_taken = es.wave_n[0] + es.wave_n[1] + es.wave_n[2] + es.wave_n[3];
+  if (tid == n_taken - 1) es.nc = incl;
+  __syncthreads();
+  nr = n_taken;
+  return es.nc;
 }
 
 // Candidate i (< the row stage's count): its hit, kx and ky.
 template <int WIN>
 __device__ __forceinline__ void candidate_at(const EnumShared<WIN>& es, int i, int& h, int& kx, int& ky) {
-  int r = 0;
-#pragma unroll
-  for (int step = EB_ROWS / 2; step >= 1; step >>= 1)
-    if (es.rpre[r + step] <= i) r += step;
-  const int hk = es.rkh[r];
-  h = hk >> 16;
-  ky = (int)(short)(hk & 0xffff);
-  kx = es.rkx[r] + (i - es.rpre[r]);
+  const int r = es.crow[i];
+  const int info = es.rinfo[r];
+  h = info >> 23;
+  ky = (int)((unsigned)info << 9) >> 20;   // bits 11..22, sign-extended
+  kx = (info & 0x7ff) + (i - es.rstart[r]);
+}
+
+// A candidate pixel with what the per-pixel work needs: its hit (key), whether
+// the brick owns it and it lies in the mask (act), the sample p, floor(p)
+// relative to the brick (l), the image element and the pose's shifts.
+struct Cand {
+  int key;
+  bool act;
+  float kx, ky;
+  float p[3];
+  int l[3];
+  int64_t k;
+  float sx, sy;
+};
+
+// Candidate i of the current row stage (i >= ncand: key = EB_SENTINEL).
+template <int WIN>
+__device__ __forceinline__ void cand_prep(const EnumShared<WIN>& es, const KGeom& g, int i, int ncand, const int lo[3],
+                                          int S, Cand& c) {
+  c.key = EB_SENTINEL;
+  c.act = false;
+  c.k = 0;
+  if (i < ncand) {
+    int h, kx, ky;
+    candidate_at(es, i, h, kx, ky);
+    c.key = h;
+    c.kx = (float)kx;
+    c.ky = (float)ky;
+    const float4 c0 = es.geo0[h], c1 = es.geo1[h];
+    slice_coord_cols(g, c0, c1, c.kx, c.ky, c.p);
+    c.sx = c1.z;
+    c.sy = c1.w;
+    c.act = owned(c.p, lo, S, c.l) && in_mask(g, c.kx, c.ky);
+    c.k = (int64_t)es.hpose[h] * g.npix + pixel_index(g, kx, ky);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -242,21 +309,19 @@ __device__ __forceinline__ bool seg_tail(int key) {
 
 // ---------------------------------------------------------------------------
 // Per-hit rotation / shift gradient sums: a segmented sum over the lanes of
-// one hit leaves the hit's partial in its last lane, which adds it to a
-// per-wavefront, per-hit sum in LDS (no two lanes of a wavefront share a hit
-// there, so no atomics).  At the end of a window the four wavefronts' sums go
-// to the pose's gradient with global atomics, scaled by o (rotation) or
-// 2 pi / H (shifts).
+// one hit leaves the hit's partial in its last lane, which adds it to the
+// hit's sum in LDS (an atomic add whose result is not waited for).  At the
+// end of a window the sums go to the pose's gradient with global atomics,
+// scaled by o (rotation) or 2 pi / H (shifts).
 // ---------------------------------------------------------------------------
 template <int WIN>
-__device__ __forceinline__ void grad_flush(const KGeom& g, const EnumShared<WIN>& es, float (*gw)[WIN][8], int nw,
+__device__ __forceinline__ void grad_flush(const KGeom& g, const EnumShared<WIN>& es, float (*gw)[8], int nw,
                                            float* __restrict__ grad_rot, float* __restrict__ grad_s) {
   const int tid = threadIdx.x;
   if (tid < nw * 8) {
     const int h = tid >> 3, q = tid & 7;
-    const float v = gw[0][h][q] + gw[1][h][q] + gw[2][h][q] + gw[3][h][q];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) gw[w][h][q] = 0.f;
+    const float v = gw[h][q];
+    gw[h][q] = 0.f;
     const int pose = es.hpose[h];
     const int bimg = pose / g.P, n = pose - bimg * g.P;
     if (q < 6) {
@@ -268,13 +333,11 @@ __device__ __forceinline__ void grad_flush(const KGeom& g, const EnumShared<WIN>
 }
 
 // Per-lane terms -> per-hit sums (all 64 lanes of the wavefront call this).
-template <int WIN>
-__device__ __forceinline__ void grad_collect(float (&acc)[8], int key, float (*gw)[WIN][8]) {
+__device__ __forceinline__ void grad_collect(float (&acc)[8], int key, float (*gw)[8]) {
   seg_scan(acc, key);
   if (seg_tail(key)) {
-    float* d = gw[threadIdx.x >> 6][key];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) d[q] += acc[q];
+    for (int q = 0; q < 8; ++q) atomicAdd(&gw[key][q], acc[q]);
   }
 }
 

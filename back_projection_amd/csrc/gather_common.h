@@ -171,15 +171,6 @@ struct Tile {
   static constexpr int SIZE = E * SZ;
 };
 
-template <int NT>
-__device__ __forceinline__ void stage_tile(float2* tile, const float2* __restrict__ V, const KGeom& g, const int lo[3]) {
-  using Tl = Tile<NT>;
-  for (int i = threadIdx.x; i < Tl::E * Tl::E * Tl::E; i += blockDim.x) {
-    const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
-    tile[z * Tl::SZ + y * Tl::SY + x] = tap_value(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
-  }
-}
-
 // floor(p) relative to the brick's low corner; true if inside [0, S)^3.
 __device__ __forceinline__ bool owned(const float p[3], const int lo[3], int S, int l[3]) {
   bool in = true;
@@ -191,34 +182,81 @@ __device__ __forceinline__ bool owned(const float p[3], const int lo[3], int S, 
   return in;
 }
 
-// Interpolate from the tile; l = floor(p) - lo.
-template <int NT>
-__device__ __forceinline__ float2 interp_tile(const float2* tile, const float p[3], const int l[3]) {
+// ---------------------------------------------------------------------------
+// element helpers (complex tile with Friedel conjugation, or real tile)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float2 tap_load(const float2* __restrict__ V, const KGeom& g, int tx, int ty, int tz) {
+  return tap_value(V, g, tx, ty, tz);
+}
+__device__ __forceinline__ float tap_load(const float* __restrict__ V, const KGeom& g, int tx, int ty, int tz) {
+  bool cj;
+  return V[tap_index<true>(g, tx, ty, tz, cj)];
+}
+__device__ __forceinline__ float2 zero_of(float2) { return make_float2(0.f, 0.f); }
+__device__ __forceinline__ float zero_of(float) { return 0.f; }
+__device__ __forceinline__ void fma_into(float w, float2 v, float2& a) { a.x = fmaf(w, v.x, a.x); a.y = fmaf(w, v.y, a.y); }
+__device__ __forceinline__ void fma_into(float w, float v, float& a) { a = fmaf(w, v, a); }
+
+template <int NT, typename T>
+__device__ __forceinline__ void stage_tile_t(T* tile, const T* __restrict__ V, const KGeom& g, const int lo[3]) {
   using Tl = Tile<NT>;
-  float wx[NT], wy[NT], wz[NT];
-  axis_weights<NT>(p[0] - floorf(p[0]), wx);
-  axis_weights<NT>(p[1] - floorf(p[1]), wy);
-  axis_weights<NT>(p[2] - floorf(p[2]), wz);
-  const float2* base = tile + l[2] * Tl::SZ + l[1] * Tl::SY + l[0];
-  float2 I = make_float2(0.f, 0.f);
+  for (int i = threadIdx.x; i < Tl::E * Tl::E * Tl::E; i += blockDim.x) {
+    const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
+    tile[z * Tl::SZ + y * Tl::SY + x] = tap_load(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
+  }
+}
+
+// Value (and, with DERIV, the partial derivatives along x, y, z) of the
+// interpolant from the tile; l = floor(p) - lo.
+// Value (and, with DERIV, the partial derivatives along x, y, z) of the
+// interpolant from the tile, for the axis weights w* (and their derivatives
+// d*) of the sample; l = floor(p) - lo.
+template <int NT, bool DERIV, typename T>
+__device__ __forceinline__ void interp_tile_w(const T* tile, const int l[3], const float wx[NT], const float wy[NT],
+                                              const float wz[NT], const float dx[NT], const float dy[NT],
+                                              const float dz[NT], T& I, T* dI) {
+  using Tl = Tile<NT>;
+  const T* base = tile + l[2] * Tl::SZ + l[1] * Tl::SY + l[0];
+  T z0 = zero_of(T{});
+  I = z0;
+  if constexpr (DERIV) { dI[0] = z0; dI[1] = z0; dI[2] = z0; }
 #pragma unroll
   for (int c = 0; c < NT; ++c) {
 #pragma unroll
     for (int b = 0; b < NT; ++b) {
-      const float2* row = base + c * Tl::SZ + b * Tl::SY;
-      float2 r = make_float2(0.f, 0.f);
+      const T* row = base + c * Tl::SZ + b * Tl::SY;
+      T r = z0, rx = z0;
 #pragma unroll
       for (int a = 0; a < NT; ++a) {
-        const float2 v = row[a];
-        r.x = fmaf(wx[a], v.x, r.x);
-        r.y = fmaf(wx[a], v.y, r.y);
+        const T v = row[a];
+        fma_into(wx[a], v, r);
+        if constexpr (DERIV) fma_into(dx[a], v, rx);
       }
       const float wyz = wy[b] * wz[c];
-      I.x = fmaf(wyz, r.x, I.x);
-      I.y = fmaf(wyz, r.y, I.y);
+      fma_into(wyz, r, I);
+      if constexpr (DERIV) {
+        fma_into(wyz, rx, dI[0]);
+        fma_into(dy[b] * wz[c], r, dI[1]);
+        fma_into(wy[b] * dz[c], r, dI[2]);
+      }
     }
   }
-  return I;
+}
+
+// Same, computing the weights from p.
+template <int NT, bool DERIV, typename T>
+__device__ __forceinline__ void interp_tile_t(const T* tile, const float p[3], const int l[3], T& I, T* dI) {
+  float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
+  const float fx = p[0] - floorf(p[0]), fy = p[1] - floorf(p[1]), fz = p[2] - floorf(p[2]);
+  axis_weights<NT>(fx, wx);
+  axis_weights<NT>(fy, wy);
+  axis_weights<NT>(fz, wz);
+  if constexpr (DERIV) {
+    axis_dweights<NT>(fx, dx);
+    axis_dweights<NT>(fy, dy);
+    axis_dweights<NT>(fz, dz);
+  }
+  interp_tile_w<NT, DERIV>(tile, l, wx, wy, wz, dx, dy, dz, I, dI);
 }
 
 // Largest |p| = |A k| over the in-mask pixels of a pose: kmax * sigma_max(A).

@@ -64,72 +64,6 @@ __global__ void __launch_bounds__(1024) k_brick_prefix(BrickGrid bg, int* __rest
   }
 }
 
-// ---------------------------------------------------------------------------
-// element helpers (complex tile with Friedel conjugation, or real tile)
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ float2 tap_load(const float2* __restrict__ V, const KGeom& g, int tx, int ty, int tz) {
-  return tap_value(V, g, tx, ty, tz);
-}
-__device__ __forceinline__ float tap_load(const float* __restrict__ V, const KGeom& g, int tx, int ty, int tz) {
-  bool cj;
-  return V[tap_index<true>(g, tx, ty, tz, cj)];
-}
-__device__ __forceinline__ float2 zero_of(float2) { return make_float2(0.f, 0.f); }
-__device__ __forceinline__ float zero_of(float) { return 0.f; }
-__device__ __forceinline__ void fma_into(float w, float2 v, float2& a) { a.x = fmaf(w, v.x, a.x); a.y = fmaf(w, v.y, a.y); }
-__device__ __forceinline__ void fma_into(float w, float v, float& a) { a = fmaf(w, v, a); }
-
-template <int NT, typename T>
-__device__ __forceinline__ void stage_tile_t(T* tile, const T* __restrict__ V, const KGeom& g, const int lo[3]) {
-  using Tl = Tile<NT>;
-  for (int i = threadIdx.x; i < Tl::E * Tl::E * Tl::E; i += blockDim.x) {
-    const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
-    tile[z * Tl::SZ + y * Tl::SY + x] = tap_load(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
-  }
-}
-
-// Value (and, with DERIV, the partial derivatives along x, y, z) of the
-// interpolant from the tile; l = floor(p) - lo.
-template <int NT, bool DERIV, typename T>
-__device__ __forceinline__ void interp_tile_t(const T* tile, const float p[3], const int l[3], T& I, T* dI) {
-  using Tl = Tile<NT>;
-  float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
-  const float fx = p[0] - floorf(p[0]), fy = p[1] - floorf(p[1]), fz = p[2] - floorf(p[2]);
-  axis_weights<NT>(fx, wx);
-  axis_weights<NT>(fy, wy);
-  axis_weights<NT>(fz, wz);
-  if constexpr (DERIV) {
-    axis_dweights<NT>(fx, dx);
-    axis_dweights<NT>(fy, dy);
-    axis_dweights<NT>(fz, dz);
-  }
-  const T* base = tile + l[2] * Tl::SZ + l[1] * Tl::SY + l[0];
-  T z0 = zero_of(T{});
-  I = z0;
-  if constexpr (DERIV) { dI[0] = z0; dI[1] = z0; dI[2] = z0; }
-#pragma unroll
-  for (int c = 0; c < NT; ++c) {
-#pragma unroll
-    for (int b = 0; b < NT; ++b) {
-      const T* row = base + c * Tl::SZ + b * Tl::SY;
-      T r = z0, rx = z0;
-#pragma unroll
-      for (int a = 0; a < NT; ++a) {
-        const T v = row[a];
-        fma_into(wx[a], v, r);
-        if constexpr (DERIV) fma_into(dx[a], v, rx);
-      }
-      const float wyz = wy[b] * wz[c];
-      fma_into(wyz, r, I);
-      if constexpr (DERIV) {
-        fma_into(wyz, rx, dI[0]);
-        fma_into(dy[b] * wz[c], r, dI[1]);
-        fma_into(wy[b] * dz[c], r, dI[2]);
-      }
-    }
-  }
-}
-
 // One pose per thread of the pass: does its slice reach the box?
 __device__ __forceinline__ bool pose_hits(const KGeom& g, const float* __restrict__ rot, int vsel, int64_t e,
                                           int64_t e1, const float bl[3], const float bh[3]) {
@@ -167,32 +101,31 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
   const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int64_t eb = e0; eb < e1; eb += EB_THREADS) {
-    int slot;
-    const int64_t e = eb + threadIdx.x;
-    const int nh = compact_hits(es, pose_hits(g, rot, vsel, e, e1, bl, bh), (int)e, slot);
+    const int nh = compact_hits(es, pose_hits(g, rot, vsel, eb + threadIdx.x, e1, bl, bh));
     for (int hw = 0; hw < nh; hw += FWD_WIN) {
       const int nw = min(FWD_WIN, nh - hw);
-      window_setup(es, g, rot, CPLX ? shifts : nullptr, vsel, hw, nw, bl, bh);
+      window_setup(es, g, rot, CPLX ? shifts : nullptr, vsel, eb, hw, nw, bl, bh);
       const int nrows = es.hrow[nw];
-      for (int qb = 0; qb < nrows; qb += EB_ROWS) {
-        const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh);
+      for (int qb = 0; qb < nrows;) {
+        int nr;
+        const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh, nr);
+        // software pipeline: the next candidate is looked up while this one
+        // is interpolated
+        Cand nx;
+        cand_prep(es, g, wave * 64 + lane, ncand, lo, bg.S, nx);
         for (int i = wave * 64 + lane; i < ncand; i += EB_THREADS) {
-          int h, kx, ky;
-          candidate_at(es, i, h, kx, ky);
-          const float fkx = (float)kx, fky = (float)ky;
-          const float4 c0 = es.geo0[h], c1 = es.geo1[h];
-          float p[3];
-          slice_coord_cols(g, c0, c1, fkx, fky, p);
-          int l[3];
-          if (!owned(p, lo, bg.S, l) || !in_mask(g, fkx, fky)) continue;
+          const Cand cu = nx;
+          if (i + EB_THREADS < ncand) cand_prep(es, g, i + EB_THREADS, ncand, lo, bg.S, nx);
+          if (!cu.act) continue;
           T I;
-          interp_tile_t<NT, false>(tile, p, l, I, (T*)nullptr);
+          interp_tile_t<NT, false>(tile, cu.p, cu.l, I, (T*)nullptr);
           if constexpr (CPLX) {
-            if (shifts) I = cmul(shift_phase(fkx, fky, c1.z, c1.w, g.inv_h), I);
+            if (shifts) I = cmul(shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h), I);
           }
-          out[(int64_t)es.hpose[h] * g.npix + pixel_index(g, kx, ky)] = I;
+          out[cu.k] = I;
         }
         __syncthreads();   // the next row stage rewrites the rows
+        qb += nr;
       }
       __syncthreads();     // the next window rewrites the hit table
     }
@@ -200,40 +133,41 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
 }
 
 // Masked pixels -> 0; pixels outside every active brick -> direct gather.
-// A pose whose largest sample radius is below the brick grid's bound is
-// served entirely by the bricks; only its masked pixels are written here.
+// One workgroup per pose: a pose whose largest sample radius is below the
+// brick grid's bound is served entirely by the bricks, and only its masked
+// pixels are written here.
 template <int NT, typename T>
 __global__ void __launch_bounds__(256) k_fwd_edge(const T* __restrict__ vol, const float* __restrict__ rot,
                                                   const float* __restrict__ shifts, T* __restrict__ out, KGeom g,
                                                   BrickGrid bg) {
   constexpr bool CPLX = sizeof(T) == 8;
-  const int pix = blockIdx.x * blockDim.x + threadIdx.x;
-  int ikx = 0, iky = 0;
-  if (pix < g.npix) pixel_freq(g, pix, ikx, iky);
-  const float kx = (float)ikx, ky = (float)iky;
-  const bool m = pix < g.npix && in_mask(g, kx, ky);
   const int64_t nvol = (int64_t)g.D * g.D * g.W;
-  for (int bn = blockIdx.y; bn < g.B * g.P; bn += gridDim.y) {
+  for (int bn = blockIdx.x; bn < g.B * g.P; bn += gridDim.x) {
     const int bimg = bn / g.P, n = bn - bimg * g.P;
-    if (pix >= g.npix) continue;
-    T* o = out + (int64_t)bn * g.npix + pix;
-    if (!m) { *o = zero_of(T{}); continue; }
     const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-    if (pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i) continue;
-    float p[3];
-    slice_coord(g, R, kx, ky, p);
-    if (served_by_bricks(bg, p)) continue;
-    if constexpr (CPLX) {
-      float2 I = interp_global<NT>(vol + nvol * (g.Bv == 1 ? 0 : bimg), g, p);
-      if (shifts) {
-        const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
-        I = cmul(shift_phase(kx, ky, s[0], s[1], g.inv_h), I);
+    const bool inside = pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i;
+    T* O = out + (int64_t)bn * g.npix;
+    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
+      int ikx, iky;
+      pixel_freq(g, pix, ikx, iky);
+      const float kx = (float)ikx, ky = (float)iky;
+      if (!in_mask(g, kx, ky)) { O[pix] = zero_of(T{}); continue; }
+      if (inside) continue;
+      float p[3];
+      slice_coord(g, R, kx, ky, p);
+      if (served_by_bricks(bg, p)) continue;
+      if constexpr (CPLX) {
+        float2 I = interp_global<NT>(vol + nvol * (g.Bv == 1 ? 0 : bimg), g, p);
+        if (shifts) {
+          const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
+          I = cmul(shift_phase(kx, ky, s[0], s[1], g.inv_h), I);
+        }
+        O[pix] = I;
+      } else {
+        float I;
+        interp_r<NT, false>(vol + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, nullptr);
+        O[pix] = I;
       }
-      *o = I;
-    } else {
-      float I;
-      interp_r<NT, false>(vol + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, nullptr);
-      *o = I;
     }
   }
 }
@@ -260,7 +194,7 @@ __global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ v
   __shared__ float2 tc[CPLX ? Tl::SIZE : 1];
   __shared__ float tr[REAL ? Tl::SIZE : 1];
   __shared__ EnumShared<GRAD_WIN> es;
-  __shared__ float gw[4][GRAD_WIN][8];
+  __shared__ float gw[GRAD_WIN][8];
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
   const int b = find_brick(prefix, bg.nb3, w);
@@ -273,68 +207,70 @@ __global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ v
   const int64_t nvol = (int64_t)g.D * g.D * g.W;
   if constexpr (CPLX) stage_tile_t<NT>(tc, volc + (int64_t)vsel * nvol, g, lo);
   if constexpr (REAL) stage_tile_t<NT>(tr, volr + (int64_t)vsel * nvol, g, lo);
-  for (int i = threadIdx.x; i < 4 * GRAD_WIN * 8; i += EB_THREADS) (&gw[0][0][0])[i] = 0.f;
+  for (int i = threadIdx.x; i < GRAD_WIN * 8; i += EB_THREADS) (&gw[0][0])[i] = 0.f;
   __syncthreads();
 
   const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int64_t eb = e0; eb < e1; eb += EB_THREADS) {
-    int slot;
-    const int64_t e = eb + threadIdx.x;
-    const int nh = compact_hits(es, pose_hits(g, rot, vsel, e, e1, bl, bh), (int)e, slot);
+    const int nh = compact_hits(es, pose_hits(g, rot, vsel, eb + threadIdx.x, e1, bl, bh));
     for (int hw = 0; hw < nh; hw += GRAD_WIN) {
       const int nw = min(GRAD_WIN, nh - hw);
-      window_setup(es, g, rot, CPLX ? shifts : nullptr, vsel, hw, nw, bl, bh);
+      window_setup(es, g, rot, CPLX ? shifts : nullptr, vsel, eb, hw, nw, bl, bh);
       const int nrows = es.hrow[nw];
-      for (int qb = 0; qb < nrows; qb += EB_ROWS) {
-        const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh);
+      for (int qb = 0; qb < nrows;) {
+        int nr;
+        const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh, nr);
+        // software pipeline: the next batch's candidate and upstream values are
+        // fetched while this batch is processed
+        Cand nx;
+        cand_prep(es, g, wave * 64 + lane, ncand, lo, bg.S, nx);
+        float2 unx = (CPLX && nx.act) ? U[nx.k] : make_float2(0.f, 0.f);
+        float urnx = (REAL && nx.act) ? Ur[nx.k] : 0.f;
         for (int c0 = wave * 64; c0 < ncand; c0 += EB_THREADS) {   // wave-uniform: the sums need every lane
-          const int i = c0 + lane;
+          const Cand cu = nx;
+          const float2 ucu = unx;
+          const float urcu = urnx;
+          if (c0 + EB_THREADS < ncand) {
+            cand_prep(es, g, c0 + EB_THREADS + lane, ncand, lo, bg.S, nx);
+            if constexpr (CPLX) unx = nx.act ? U[nx.k] : make_float2(0.f, 0.f);
+            if constexpr (REAL) urnx = nx.act ? Ur[nx.k] : 0.f;
+          }
           float acc[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-          int key = EB_SENTINEL;
-          if (i < ncand) {
-            int h, kx, ky;
-            candidate_at(es, i, h, kx, ky);
-            key = h;
-            const float fkx = (float)kx, fky = (float)ky;
-            const float4 c0v = es.geo0[h], c1v = es.geo1[h];
-            float p[3];
-            slice_coord_cols(g, c0v, c1v, fkx, fky, p);
-            int l[3];
-            if (owned(p, lo, bg.S, l) && in_mask(g, fkx, fky)) {
-              const int64_t k = (int64_t)es.hpose[h] * g.npix + pixel_index(g, kx, ky);
-              float e3[3] = {0.f, 0.f, 0.f};
-              if constexpr (CPLX) {
-                float2 I, dI[3];
-                interp_tile_t<NT, true>(tc, p, l, I, dI);
-                float2 phi = make_float2(1.f, 0.f);
-                if (shifts) phi = shift_phase(fkx, fky, c1v.z, c1v.w, g.inv_h);
-                const float2 cu = cmulc(U[k], phi);   // conj(U) * phi
+          const int key = cu.key;
+          if (cu.act) {
+            const float fkx = cu.kx, fky = cu.ky;
+            float e3[3] = {0.f, 0.f, 0.f};
+            if constexpr (CPLX) {
+              float2 I, dI[3];
+              interp_tile_t<NT, true>(tc, cu.p, cu.l, I, dI);
+              float2 phi = make_float2(1.f, 0.f);
+              if (shifts) phi = shift_phase(fkx, fky, cu.sx, cu.sy, g.inv_h);
+              const float2 cc = cmulc(ucu, phi);   // conj(U) * phi
 #pragma unroll
-                for (int a = 0; a < 3; ++a) e3[a] = cu.x * dI[a].x - cu.y * dI[a].y;
-                const float im = cu.x * I.y + cu.y * I.x;
-                acc[6] = fkx * im;
-                acc[7] = fky * im;
-              }
-              if constexpr (REAL) {
-                float I, dI[3];
-                interp_tile_t<NT, true>(tr, p, l, I, dI);
-                const float wv = Ur[k];
+              for (int a = 0; a < 3; ++a) e3[a] = cc.x * dI[a].x - cc.y * dI[a].y;
+              const float im = cc.x * I.y + cc.y * I.x;
+              acc[6] = fkx * im;
+              acc[7] = fky * im;
+            }
+            if constexpr (REAL) {
+              float I, dI[3];
+              interp_tile_t<NT, true>(tr, cu.p, cu.l, I, dI);
 #pragma unroll
-                for (int a = 0; a < 3; ++a) e3[a] = fmaf(wv, dI[a], e3[a]);
-              }
+              for (int a = 0; a < 3; ++a) e3[a] = fmaf(urcu, dI[a], e3[a]);
+            }
 #pragma unroll
-              for (int a = 0; a < 3; ++a) {
-                acc[2 * a] = e3[a] * fkx;
-                acc[2 * a + 1] = e3[a] * fky;
-              }
+            for (int a = 0; a < 3; ++a) {
+              acc[2 * a] = e3[a] * fkx;
+              acc[2 * a + 1] = e3[a] * fky;
             }
           }
-          grad_collect<GRAD_WIN>(acc, key, gw);
+          grad_collect(acc, key, gw);
         }
         __syncthreads();
+        qb += nr;
       }
       grad_flush<GRAD_WIN>(g, es, gw, nw, grad_rot, CPLX ? grad_s : nullptr);
       __syncthreads();
@@ -342,57 +278,58 @@ __global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ v
   }
 }
 
-// Pixels outside every active brick: their gradient terms from global memory.
+// Pixels outside every active brick: their gradient terms from global memory
+// (one workgroup per pose; poses inside the brick grid are skipped whole).
 template <int NT, bool CPLX, bool REAL>
 __global__ void __launch_bounds__(256) k_grad_edge(const float2* __restrict__ volc, const float* __restrict__ volr,
                                                    const float2* __restrict__ U, const float* __restrict__ Ur,
                                                    const float* __restrict__ rot, const float* __restrict__ shifts,
                                                    float* __restrict__ grad_rot, float* __restrict__ grad_s, KGeom g,
                                                    BrickGrid bg) {
-  const int pix = blockIdx.x * blockDim.x + threadIdx.x;
-  if (pix >= g.npix) return;
-  int ikx, iky;
-  pixel_freq(g, pix, ikx, iky);
-  const float kx = (float)ikx, ky = (float)iky;
-  if (!in_mask(g, kx, ky)) return;
   const int64_t nvol = (int64_t)g.D * g.D * g.W;
-  for (int bn = blockIdx.y; bn < g.B * g.P; bn += gridDim.y) {
+  for (int bn = blockIdx.x; bn < g.B * g.P; bn += gridDim.x) {
     const int bimg = bn / g.P, n = bn - bimg * g.P;
     const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
     if (pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i) continue;
-    float p[3];
-    slice_coord(g, R, kx, ky, p);
-    if (served_by_bricks(bg, p)) continue;
-    const int64_t k = (int64_t)bn * g.npix + pix;
-    float e[3] = {0.f, 0.f, 0.f}, im = 0.f;
-    if constexpr (CPLX) {
-      float2 I, dI[3];
-      interp_c<NT, true>(volc + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, dI);
-      float2 phi = make_float2(1.f, 0.f);
-      if (shifts) {
-        const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
-        phi = shift_phase(kx, ky, s[0], s[1], g.inv_h);
+    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
+      int ikx, iky;
+      pixel_freq(g, pix, ikx, iky);
+      const float kx = (float)ikx, ky = (float)iky;
+      if (!in_mask(g, kx, ky)) continue;
+      float p[3];
+      slice_coord(g, R, kx, ky, p);
+      if (served_by_bricks(bg, p)) continue;
+      const int64_t k = (int64_t)bn * g.npix + pix;
+      float e[3] = {0.f, 0.f, 0.f}, im = 0.f;
+      if constexpr (CPLX) {
+        float2 I, dI[3];
+        interp_c<NT, true>(volc + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, dI);
+        float2 phi = make_float2(1.f, 0.f);
+        if (shifts) {
+          const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
+          phi = shift_phase(kx, ky, s[0], s[1], g.inv_h);
+        }
+        const float2 cu = cmulc(U[k], phi);
+        for (int a = 0; a < 3; ++a) e[a] = cu.x * dI[a].x - cu.y * dI[a].y;
+        im = cu.x * I.y + cu.y * I.x;
       }
-      const float2 cu = cmulc(U[k], phi);
-      for (int a = 0; a < 3; ++a) e[a] = cu.x * dI[a].x - cu.y * dI[a].y;
-      im = cu.x * I.y + cu.y * I.x;
-    }
-    if constexpr (REAL) {
-      float I, dI[3];
-      interp_r<NT, true>(volr + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, dI);
-      for (int a = 0; a < 3; ++a) e[a] = fmaf(Ur[k], dI[a], e[a]);
-    }
-    if (grad_rot) {
-      float* gr = grad_rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-      for (int a = 0; a < 3; ++a) {
-        atomicAdd(gr + 3 * a, g.o * e[a] * kx);
-        atomicAdd(gr + 3 * a + 1, g.o * e[a] * ky);
+      if constexpr (REAL) {
+        float I, dI[3];
+        interp_r<NT, true>(volr + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, dI);
+        for (int a = 0; a < 3; ++a) e[a] = fmaf(Ur[k], dI[a], e[a]);
       }
-    }
-    if (CPLX && grad_s) {
-      float* gs = grad_s + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
-      atomicAdd(gs, 6.283185307179586f * g.inv_h * kx * im);
-      atomicAdd(gs + 1, 6.283185307179586f * g.inv_h * ky * im);
+      if (grad_rot) {
+        float* gr = grad_rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+        for (int a = 0; a < 3; ++a) {
+          atomicAdd(gr + 3 * a, g.o * e[a] * kx);
+          atomicAdd(gr + 3 * a + 1, g.o * e[a] * ky);
+        }
+      }
+      if (CPLX && grad_s) {
+        float* gs = grad_s + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
+        atomicAdd(gs, 6.283185307179586f * g.inv_h * kx * im);
+        atomicAdd(gs + 1, 6.283185307179586f * g.inv_h * ky * im);
+      }
     }
   }
 }
@@ -405,56 +342,64 @@ hipError_t launch_brick_prefix(const BrickGrid& bg, int* prefix, hipStream_t st)
   return hipGetLastError();
 }
 
-static dim3 edge_grid(const KGeom& g) {
-  const int gy = g.B * g.P < 2048 ? g.B * g.P : 2048;
-  return dim3((g.npix + 255) / 256, gy);
-}
+// One workgroup per pose (grid-stride beyond 16384 poses).
+static dim3 edge_grid(const KGeom& g) { return dim3(g.B * g.P < 16384 ? g.B * g.P : 16384); }
 
 template <typename T>
 static hipError_t fwd_t(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const T* vol,
-                        const float* rot, const float* shifts, T* out, hipStream_t st) {
+                        const float* rot, const float* shifts, T* out, hipStream_t st, const EvPair* ev) {
   const dim3 blk(256);
   if (interp == 1) hipLaunchKernelGGL((k_fwd_edge<4, T>), edge_grid(g), blk, 0, st, vol, rot, shifts, out, g, bg);
   else hipLaunchKernelGGL((k_fwd_edge<2, T>), edge_grid(g), blk, 0, st, vol, rot, shifts, out, g, bg);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || bg.nwork == 0) return e;
+  ev_begin(ev, st);   // recorded even when no brick kernel runs
+  if (e != hipSuccess || bg.nwork == 0) {
+    ev_end(ev, st);
+    return e;
+  }
   const dim3 grid(bg.nwork, g.Bv);
   if (interp == 1) hipLaunchKernelGGL((k_fwd_brick<4, T>), grid, blk, 0, st, vol, rot, shifts, out, g, bg, prefix);
   else hipLaunchKernelGGL((k_fwd_brick<2, T>), grid, blk, 0, st, vol, rot, shifts, out, g, bg, prefix);
+  ev_end(ev, st);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* vol,
-                            const float* rot, const float* shifts, float2* out, hipStream_t st) {
-  return fwd_t<float2>(g, interp, bg, prefix, vol, rot, shifts, out, st);
+                            const float* rot, const float* shifts, float2* out, hipStream_t st, const EvPair* ev) {
+  return fwd_t<float2>(g, interp, bg, prefix, vol, rot, shifts, out, st, ev);
 }
 
 hipError_t launch_fwd_brick_real(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix,
-                                 const float* vol, const float* rot, float* out, hipStream_t st) {
-  return fwd_t<float>(g, interp, bg, prefix, vol, rot, nullptr, out, st);
+                                 const float* vol, const float* rot, float* out, hipStream_t st, const EvPair* ev) {
+  return fwd_t<float>(g, interp, bg, prefix, vol, rot, nullptr, out, st, ev);
 }
 
 template <int NT, bool C, bool R>
 static void grad_launch(const KGeom& g, const BrickGrid& bg, const int* prefix, const float2* volc, const float* volr,
                         const float2* U, const float* Ur, const float* rot, const float* shifts, float* grad_rot,
-                        float* grad_s, hipStream_t st) {
+                        float* grad_s, hipStream_t st, const EvPair* ev) {
   const dim3 blk(256);
   hipLaunchKernelGGL((k_grad_edge<NT, C, R>), edge_grid(g), blk, 0, st, volc, volr, U, Ur, rot, shifts, grad_rot,
                      grad_s, g, bg);
-  if (bg.nwork == 0) return;
+  ev_begin(ev, st);   // recorded even when no brick kernel runs
+  if (bg.nwork == 0) {
+    ev_end(ev, st);
+    return;
+  }
   hipLaunchKernelGGL((k_grad_brick<NT, C, R>), dim3(bg.nwork, g.Bv), blk, 0, st, volc, volr, U, Ur, rot, shifts,
                      grad_rot, grad_s, g, bg, prefix);
+  ev_end(ev, st);
 }
 
 hipError_t launch_grad_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* volc,
                              const float* volr, const float2* U, const float* Ur, const float* rot,
-                             const float* shifts, float* grad_rot, float* grad_s, hipStream_t st) {
+                             const float* shifts, float* grad_rot, float* grad_s, hipStream_t st, const EvPair* ev) {
   const bool c = volc != nullptr, r = volr != nullptr;
-#define TP_GRAD(NT_)                                                                                            \
-  do {                                                                                                          \
-    if (c && r) grad_launch<NT_, true, true>(g, bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st);  \
-    else if (c) grad_launch<NT_, true, false>(g, bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st); \
-    else if (r) grad_launch<NT_, false, true>(g, bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st); \
+#define TP_GRAD(NT_)                                                                                                 \
+  do {                                                                                                               \
+    if (c && r) grad_launch<NT_, true, true>(g, bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st, ev);  \
+    else if (c) grad_launch<NT_, true, false>(g, bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st, ev); \
+    else if (r) grad_launch<NT_, false, true>(g, bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st, ev); \
   } while (0)
   if (interp == 1) TP_GRAD(4); else TP_GRAD(2);
 #undef TP_GRAD

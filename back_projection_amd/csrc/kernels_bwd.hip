@@ -180,8 +180,8 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
   __shared__ unsigned int acc_w[WEIGHTS ? TSIZE : 1];
   __shared__ float2 vt[GRAD ? TSIZE : 1];
   __shared__ EnumShared<WINDOW> es;
-  __shared__ float hit_m[EB_THREADS], hit_w[EB_THREADS], hit_c[EB_THREADS];
-  __shared__ float gw[GRAD ? 4 : 1][WINDOW][8];
+  __shared__ float hit_m[WINDOW], hit_w[WINDOW], hit_c[WINDOW];
+  __shared__ float gw[WINDOW][8];
 
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
@@ -213,74 +213,78 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
       const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
       vt[z * TSZ + y * TSY + x] = tap_value(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
     }
-    for (int i = tid; i < 4 * WINDOW * 8; i += EB_THREADS) (&gw[0][0][0])[i] = 0.f;
+    for (int i = tid; i < WINDOW * 8; i += EB_THREADS) (&gw[0][0])[i] = 0.f;
   }
   __syncthreads();
 
   const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
   for (int64_t eb = e0; eb < e1; eb += EB_THREADS) {
-    // ---- hit detection: one pose per thread, with its window bounds ----
+    // ---- hit detection: one pose per thread (degenerate maps go to the edge kernel) ----
     bool hit = false;
-    float hm = 0.f, hwm = 0.f, hc = 0.f;
     const int64_t e = eb + tid;
     if (e < e1) {
       int bimg, n;
       list_entry(g, vsel, (int)e, bimg, n);
       const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-      hc = contrib_bound<NT>(g, R);
-      hit = pose_ok(hc) && slice_meets_box(g, R, bl, bh);
-      if (hit) {
-        const int64_t pose = (int64_t)bimg * g.P + n;
-        hm = box_band_max(g, bw, R, ymax, pose, bl, bh);
-        if constexpr (WEIGHTS) hwm = box_band_max(g, bw, R, wmax, pose, bl, bh);
-      }
+      hit = pose_ok(contrib_bound<NT>(g, R)) && slice_meets_box(g, R, bl, bh);
     }
-    int slot;
-    const int nh = compact_hits(es, hit, (int)e, slot);
-    if (slot >= 0) {
-      hit_m[slot] = hm;
-      hit_w[slot] = hwm;
-      hit_c[slot] = hc;
-    }
-    __syncthreads();
+    const int nh = compact_hits(es, hit);
 
     for (int hb = 0; hb < nh; hb += WINDOW) {
       const int nw = min(WINDOW, nh - hb);
+      window_setup(es, g, rot, shifts, vsel, eb, hb, nw, bl, bh);
+      // per hit: the bound on contributions to one tap and the largest value
+      // it can bring to this brick
+      if (tid < nw) {
+        float R[9];
+        cols_to_r9(es.geo0[tid], es.geo1[tid], R);
+        const int64_t pose = es.hpose[tid];
+        hit_c[tid] = contrib_bound<NT>(g, R);
+        hit_m[tid] = box_band_max(g, bw, R, ymax, pose, bl, bh);
+        hit_w[tid] = WEIGHTS ? box_band_max(g, bw, R, wmax, pose, bl, bh) : 0.f;
+      }
+      __syncthreads();
       float M = 0.f, MW = 0.f, C = 0.f;
       for (int h = 0; h < nw; ++h) {
-        M = fmaxf(M, hit_m[hb + h]);
-        MW = fmaxf(MW, hit_w[hb + h]);
-        C += hit_c[hb + h];
+        M = fmaxf(M, hit_m[h]);
+        MW = fmaxf(MW, hit_w[h]);
+        C += hit_c[h];
       }
       // |re|, |im| <= sqrt(2) M per unit weight (the phase rotates); every
       // contribution also stays below 2^22 for the magic rounding
       const float lim = fminf(FIX_RANGE - C, 0.99f * 4194304.0f * C);
       const float scale = M > 0.f ? lim / (1.41421356f * M * C) : 0.f;
       const float wscale = (WEIGHTS && MW > 0.f) ? lim / (MW * C) : 0.f;
-
-      window_setup(es, g, rot, shifts, vsel, hb, nw, bl, bh);
       const int nrows = es.hrow[nw];
-      for (int qb = 0; qb < nrows; qb += EB_ROWS) {
-        const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh);
+      for (int qb = 0; qb < nrows;) {
+        int nr;
+        const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh, nr);
+        // software pipeline: the next batch's candidate and image values are
+        // fetched while this batch is processed
+        Cand nx;
+        cand_prep(es, g, wave * 64 + lane, ncand, lo, bg.S, nx);
+        float2 ynx = nx.act ? Y[nx.k] : make_float2(0.f, 0.f);
+        float wnx = (WEIGHTS && nx.act) ? Wimg[nx.k] : 0.f;
         for (int c0 = wave * 64; c0 < ncand; c0 += EB_THREADS) {   // wave-uniform (segmented sums)
-          const int i = c0 + lane;
+          const Cand cu = nx;
+          const float2 ycu = ynx;
+          const float wcu = wnx;
+          if (c0 + EB_THREADS < ncand) {
+            cand_prep(es, g, c0 + EB_THREADS + lane, ncand, lo, bg.S, nx);
+            ynx = nx.act ? Y[nx.k] : make_float2(0.f, 0.f);
+            if constexpr (WEIGHTS) wnx = nx.act ? Wimg[nx.k] : 0.f;
+          }
           float gacc[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q) gacc[q] = 0.f;
-          int key = EB_SENTINEL;
-          if (i < ncand) {
-            int h, kx, ky;
-            candidate_at(es, i, h, kx, ky);
-            key = h;
-            const float fkx = (float)kx, fky = (float)ky;
-            const float4 c0v = es.geo0[h], c1v = es.geo1[h];
-            float p[3];
-            slice_coord_cols(g, c0v, c1v, fkx, fky, p);
-            int l[3];
-            if (owned(p, lo, bg.S, l) && in_mask(g, fkx, fky)) {
-              const int64_t k = (int64_t)es.hpose[h] * g.npix + pixel_index(g, kx, ky);
-              float2 c = Y[k];
-              if (shifts) c = cmulc(shift_phase(fkx, fky, c1v.z, c1v.w, g.inv_h), c);   // conj(phi) * Y
+          const int key = cu.key;
+          if (cu.act) {
+            {
+              const float fkx = cu.kx, fky = cu.ky;
+              const float* p = cu.p;
+              const int* l = cu.l;
+              float2 c = ycu;
+              if (shifts) c = cmulc(shift_phase(fkx, fky, cu.sx, cu.sy, g.inv_h), c);   // conj(phi) * Y
               float wx[NT], wy[NT], wz[NT];
               const float fx = p[0] - floorf(p[0]), fy = p[1] - floorf(p[1]), fz = p[2] - floorf(p[2]);
               axis_weights<NT>(fx, wx);
@@ -292,25 +296,9 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
                 axis_dweights<NT>(fx, dx);
                 axis_dweights<NT>(fy, dy);
                 axis_dweights<NT>(fz, dz);
-                float2 I = make_float2(0.f, 0.f), d0 = I, d1 = I, d2 = I;
-#pragma unroll
-                for (int jc = 0; jc < NT; ++jc)
-#pragma unroll
-                  for (int jb = 0; jb < NT; ++jb) {
-                    const float2* row = vt + (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
-                    float2 r = make_float2(0.f, 0.f), rx = r;
-#pragma unroll
-                    for (int ja = 0; ja < NT; ++ja) {
-                      const float2 v = row[ja];
-                      r.x = fmaf(wx[ja], v.x, r.x); r.y = fmaf(wx[ja], v.y, r.y);
-                      rx.x = fmaf(dx[ja], v.x, rx.x); rx.y = fmaf(dx[ja], v.y, rx.y);
-                    }
-                    const float wyz = wy[jb] * wz[jc], gy = dy[jb] * wz[jc], gz = wy[jb] * dz[jc];
-                    I.x = fmaf(wyz, r.x, I.x); I.y = fmaf(wyz, r.y, I.y);
-                    d0.x = fmaf(wyz, rx.x, d0.x); d0.y = fmaf(wyz, rx.y, d0.y);
-                    d1.x = fmaf(gy, r.x, d1.x); d1.y = fmaf(gy, r.y, d1.y);
-                    d2.x = fmaf(gz, r.x, d2.x); d2.y = fmaf(gz, r.y, d2.y);
-                  }
+                float2 I, dI[3];
+                interp_tile_w<NT, true>(vt, l, wx, wy, wz, dx, dy, dz, I, dI);
+                const float2 d0 = dI[0], d1 = dI[1], d2 = dI[2];
                 const float t0 = c.x * d0.x + c.y * d0.y, t1 = c.x * d1.x + c.y * d1.y, t2 = c.x * d2.x + c.y * d2.y;
                 const float im = c.x * I.y - c.y * I.x;
                 gacc[0] = t0 * fkx; gacc[1] = t0 * fky;
@@ -320,7 +308,7 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
               }
               // scatter all taps (they all lie in the halo tile)
               const float cr = c.x * scale, ci = c.y * scale;
-              const float wv = WEIGHTS ? Wimg[k] * wscale : 0.f;
+              const float wv = WEIGHTS ? wcu * wscale : 0.f;
 #pragma unroll
               for (int jc = 0; jc < NT; ++jc)
 #pragma unroll
@@ -336,9 +324,10 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
                 }
             }
           }
-          if constexpr (GRAD) grad_collect<WINDOW>(gacc, key, gw);
+          if constexpr (GRAD) grad_collect(gacc, key, gw);
         }
         __syncthreads();
+        qb += nr;
       }
       if constexpr (GRAD) grad_flush<WINDOW>(g, es, gw, nw, grad_rot, grad_s);
       // ---- flush the window into the float accumulators ----
@@ -449,68 +438,68 @@ __global__ void __launch_bounds__(256) k_bwd_edge(const float2* __restrict__ Y, 
                                                   float* __restrict__ wvol, float* __restrict__ grad_rot,
                                                   float* __restrict__ grad_s, KGeom g, BwdGrid bw) {
   const BrickGrid& bg = bw.bg;
-  const int pix = blockIdx.x * blockDim.x + threadIdx.x;
-  if (pix >= g.npix) return;
-  int ikx, iky;
-  pixel_freq(g, pix, ikx, iky);
-  const float kx = (float)ikx, ky = (float)iky;
-  if (!in_mask(g, kx, ky)) return;
   const int64_t nvol = (int64_t)g.D * g.D * g.W;
-  for (int bn = blockIdx.y; bn < g.B * g.P; bn += gridDim.y) {
+  for (int bn = blockIdx.x; bn < g.B * g.P; bn += gridDim.x) {
     const int bimg = bn / g.P, n = bn - bimg * g.P;
     const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
     const bool ok = pose_ok(contrib_bound<NT>(g, R));
-    if (ok && pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i) continue;
-    float p[3];
-    slice_coord(g, R, kx, ky, p);
-    if (ok && served_by_bricks(bg, p)) continue;
-    float2 c = Y[(int64_t)bn * g.npix + pix];
-    float2 phi = make_float2(1.f, 0.f);
-    if (shifts) {
-      const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
-      phi = shift_phase(kx, ky, s[0], s[1], g.inv_h);
-    }
-    if constexpr (GRAD) {
-      float2 I, dI[3];
-      interp_c<NT, true>(volc + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, dI);
-      const float2 cu = cmulc(c, phi);   // conj(G) * phi
-      float e[3];
-      for (int a = 0; a < 3; ++a) e[a] = cu.x * dI[a].x - cu.y * dI[a].y;
-      const float im = cu.x * I.y + cu.y * I.x;
-      if (grad_rot) {
-        float* gr = grad_rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-        for (int a = 0; a < 3; ++a) {
-          atomicAdd(gr + 3 * a, g.o * e[a] * kx);
-          atomicAdd(gr + 3 * a + 1, g.o * e[a] * ky);
+    if (ok && pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i) continue;   // served whole by the bricks
+    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
+      int ikx, iky;
+      pixel_freq(g, pix, ikx, iky);
+      const float kx = (float)ikx, ky = (float)iky;
+      if (!in_mask(g, kx, ky)) continue;
+      float p[3];
+      slice_coord(g, R, kx, ky, p);
+      if (ok && served_by_bricks(bg, p)) continue;
+      float2 c = Y[(int64_t)bn * g.npix + pix];
+      float2 phi = make_float2(1.f, 0.f);
+      if (shifts) {
+        const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
+        phi = shift_phase(kx, ky, s[0], s[1], g.inv_h);
+      }
+      if constexpr (GRAD) {
+        float2 I, dI[3];
+        interp_c<NT, true>(volc + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, dI);
+        const float2 cu = cmulc(c, phi);   // conj(G) * phi
+        float e[3];
+        for (int a = 0; a < 3; ++a) e[a] = cu.x * dI[a].x - cu.y * dI[a].y;
+        const float im = cu.x * I.y + cu.y * I.x;
+        if (grad_rot) {
+          float* gr = grad_rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+          for (int a = 0; a < 3; ++a) {
+            atomicAdd(gr + 3 * a, g.o * e[a] * kx);
+            atomicAdd(gr + 3 * a + 1, g.o * e[a] * ky);
+          }
+        }
+        if (grad_s) {
+          float* gs = grad_s + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
+          atomicAdd(gs, 6.283185307179586f * g.inv_h * kx * im);
+          atomicAdd(gs + 1, 6.283185307179586f * g.inv_h * ky * im);
         }
       }
-      if (grad_s) {
-        float* gs = grad_s + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
-        atomicAdd(gs, 6.283185307179586f * g.inv_h * kx * im);
-        atomicAdd(gs + 1, 6.283185307179586f * g.inv_h * ky * im);
-      }
+      c = cmulc(phi, c);   // conj(phi) * Y
+      const float wimg = WEIGHTS ? Wimg[(int64_t)bn * g.npix + pix] : 0.f;
+      float2* V = vol + nvol * (g.Bv == 1 ? 0 : bimg);
+      float* VW = WEIGHTS ? wvol + nvol * (g.Bv == 1 ? 0 : bimg) : nullptr;
+      const float flx = safe_floor(p[0]), fly = safe_floor(p[1]), flz = safe_floor(p[2]);
+      float wx[NT], wy[NT], wz[NT];
+      axis_weights<NT>(p[0] - flx, wx);
+      axis_weights<NT>(p[1] - fly, wy);
+      axis_weights<NT>(p[2] - flz, wz);
+      const int x0 = (int)flx + first_tap<NT>(), y0 = (int)fly + first_tap<NT>(), z0 = (int)flz + first_tap<NT>();
+      for (int cc = 0; cc < NT; ++cc)
+        for (int bb = 0; bb < NT; ++bb)
+          for (int aa = 0; aa < NT; ++aa) {
+            bool cj;
+            const int64_t idx = tap_index<true>(g, x0 + aa, y0 + bb, z0 + cc, cj);
+            const float wt = wx[aa] * wy[bb] * wz[cc];
+            float* dst = reinterpret_cast<float*>(V + idx);
+            unsafeAtomicAdd(dst, wt * c.x);
+            unsafeAtomicAdd(dst + 1, cj ? -wt * c.y : wt * c.y);
+            if constexpr (WEIGHTS) unsafeAtomicAdd(VW + idx, wt * wimg);
+          }
     }
-    c = cmulc(phi, c);   // conj(phi) * Y
-    const float wimg = WEIGHTS ? Wimg[(int64_t)bn * g.npix + pix] : 0.f;
-    float2* V = vol + nvol * (g.Bv == 1 ? 0 : bimg);
-    float* VW = WEIGHTS ? wvol + nvol * (g.Bv == 1 ? 0 : bimg) : nullptr;
-    const float flx = safe_floor(p[0]), fly = safe_floor(p[1]), flz = safe_floor(p[2]);
-    float wx[NT], wy[NT], wz[NT];
-    axis_weights<NT>(p[0] - flx, wx);
-    axis_weights<NT>(p[1] - fly, wy);
-    axis_weights<NT>(p[2] - flz, wz);
-    const int x0 = (int)flx + first_tap<NT>(), y0 = (int)fly + first_tap<NT>(), z0 = (int)flz + first_tap<NT>();
-    for (int cc = 0; cc < NT; ++cc)
-      for (int bb = 0; bb < NT; ++bb)
-        for (int aa = 0; aa < NT; ++aa) {
-          bool cj;
-          const int64_t idx = tap_index<true>(g, x0 + aa, y0 + bb, z0 + cc, cj);
-          const float wt = wx[aa] * wy[bb] * wz[cc];
-          float* dst = reinterpret_cast<float*>(V + idx);
-          unsafeAtomicAdd(dst, wt * c.x);
-          unsafeAtomicAdd(dst + 1, cj ? -wt * c.y : wt * c.y);
-          if constexpr (WEIGHTS) unsafeAtomicAdd(VW + idx, wt * wimg);
-        }
   }
 }
 
@@ -528,7 +517,8 @@ size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights) {
 
 hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* workspace, const float2* Y,
                       const float* Wimg, const float2* volc, const float* rot, const float* shifts, float2* vol,
-                      float* wvol, float* grad_rot, float* grad_s, hipStream_t st) {
+                      float* wvol, float* grad_rot, float* grad_s, hipStream_t st, const EvPair* ev_brick,
+                      const EvPair* ev_fold) {
   const bool weights = Wimg != nullptr, grad = volc != nullptr;
   int* prefix = (int*)workspace;
   const size_t off_b = align256((size_t)(bw.bg.nb3 + 1) * sizeof(int));
@@ -545,6 +535,7 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 blk(256);
+  ev_begin(ev_brick, st);   // recorded even when no brick kernel runs
   if (bw.bg.nwork > 0) {
     const dim3 grid(bw.bg.nwork, g.Bv);
 #define TP_BWD(NT_, W_, G_)                                                                                    \
@@ -557,12 +548,14 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
     }
 #undef TP_BWD
     e = hipGetLastError();
-    if (e != hipSuccess) return e;
   }
+  ev_end(ev_brick, st);
+  if (e != hipSuccess) return e;
   {
     const int64_t nvol = (int64_t)g.D * g.D * g.W;
     const int blocks = (int)((nvol + 255) / 256 < 8192 ? (nvol + 255) / 256 : 8192);
     const dim3 fg(blocks, g.Bv);
+    ev_begin(ev_fold, st);
     if (interp == 1) {
       if (weights) hipLaunchKernelGGL((k_bwd_fold<4, true>), fg, blk, 0, st, vol, wvol, part_c, part_w, g, bw, prefix);
       else hipLaunchKernelGGL((k_bwd_fold<4, false>), fg, blk, 0, st, vol, wvol, part_c, part_w, g, bw, prefix);
@@ -570,11 +563,11 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
       if (weights) hipLaunchKernelGGL((k_bwd_fold<2, true>), fg, blk, 0, st, vol, wvol, part_c, part_w, g, bw, prefix);
       else hipLaunchKernelGGL((k_bwd_fold<2, false>), fg, blk, 0, st, vol, wvol, part_c, part_w, g, bw, prefix);
     }
+    ev_end(ev_fold, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int gy = g.B * g.P < 2048 ? g.B * g.P : 2048;
-  const dim3 eg((g.npix + 255) / 256, gy);
+  const dim3 eg(g.B * g.P < 16384 ? g.B * g.P : 16384);   // one workgroup per pose
 #define TP_EDGE(NT_, W_, G_)                                                                                  \
   hipLaunchKernelGGL((k_bwd_edge<NT_, W_, G_>), eg, blk, 0, st, Y, Wimg, volc, rot, shifts, vol, wvol, grad_rot, \
                      grad_s, g, bw)

@@ -10,7 +10,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "brick_grid.h"
 #include "brick_kernels.h"
@@ -126,9 +128,36 @@ bool force_direct() {
   return v;
 }
 
+// ---- event timing of the brick kernels (tp_timing_enable / tp_timing_read) ----
+struct TimedLaunch {
+  int cls;
+  tproj::EvPair ev;
+};
+std::mutex g_kt_mu;
+bool g_kt_on = false;
+std::vector<TimedLaunch> g_kt;
+
+// A fresh event pair for one launch of kernel class cls (both events NULL
+// when timing is off or the events cannot be created).
+tproj::EvPair kt_copy(int cls) {
+  std::lock_guard<std::mutex> lk(g_kt_mu);
+  TimedLaunch t{cls, {}};
+  if (!g_kt_on) return t.ev;
+  if (hipEventCreate(&t.ev.a) != hipSuccess) return tproj::EvPair{};
+  if (hipEventCreate(&t.ev.b) != hipSuccess) {
+    (void)hipEventDestroy(t.ev.a);
+    return tproj::EvPair{};
+  }
+  g_kt.push_back(t);
+  return t.ev;
+}
+
 GatherPlan gather_plan(const tp_geom* g) {
   GatherPlan pl;
   if (force_direct()) return pl;
+  // the brick enumeration packs kx <= H/2 into 11 bits and one image row's
+  // candidates into its 2048-entry table
+  if (g->H / 2 > 2047) return pl;
   tproj::BrickGrid& bg = pl.bg;
   const int NT = g->interp == TP_CUBIC ? 4 : 2;
   bg.S = 17 - NT;
@@ -234,7 +263,9 @@ tp_status run_forward(const tp_geom* geom, const tproj::KGeom& k, const float2* 
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
   int* prefix = (int*)workspace;
   LAUNCH(tproj::launch_brick_prefix(pl.bg, prefix, st), "brick work list");
-  LAUNCH(tproj::launch_fwd_brick(k, geom->interp, pl.bg, prefix, vol, rot, shifts, out, st), "project (bricks)");
+  const tproj::EvPair ev = kt_copy(TP_KT_FORWARD);
+  LAUNCH(tproj::launch_fwd_brick(k, geom->interp, pl.bg, prefix, vol, rot, shifts, out, st, ev.a ? &ev : nullptr),
+         "project (bricks)");
   return TP_OK;
 }
 
@@ -254,8 +285,9 @@ tp_status run_grads(const tp_geom* geom, const tproj::KGeom& k, const float2* vo
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
   int* prefix = (int*)workspace;
   LAUNCH(tproj::launch_brick_prefix(pl.bg, prefix, st), "brick work list");
+  const tproj::EvPair ev = kt_copy(TP_KT_GRADIENT);
   LAUNCH(tproj::launch_grad_brick(k, geom->interp, pl.bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot,
-                                  grad_shifts, st),
+                                  grad_shifts, st, ev.a ? &ev : nullptr),
          "rotation/shift grads (bricks)");
   return TP_OK;
 }
@@ -271,7 +303,9 @@ tp_status run_forward_real(const tp_geom* geom, const tproj::KGeom& k, const flo
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
   int* prefix = (int*)workspace;
   LAUNCH(tproj::launch_brick_prefix(pl.bg, prefix, st), "brick work list");
-  LAUNCH(tproj::launch_fwd_brick_real(k, geom->interp, pl.bg, prefix, vol, rot, out, st), "real projection (bricks)");
+  const tproj::EvPair ev = kt_copy(TP_KT_FORWARD);
+  LAUNCH(tproj::launch_fwd_brick_real(k, geom->interp, pl.bg, prefix, vol, rot, out, st, ev.a ? &ev : nullptr),
+         "real projection (bricks)");
   return TP_OK;
 }
 
@@ -295,8 +329,9 @@ tp_status run_bwd(const tp_geom* geom, const tproj::KGeom& k, const float2* Y, c
   }
   if (!workspace || ws_bytes < pl.ws_bytes)
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
+  const tproj::EvPair eb = kt_copy(TP_KT_BACKWARD), ef = kt_copy(TP_KT_FOLD);
   LAUNCH(tproj::launch_bwd(k, geom->interp, pl.bw, workspace, Y, Wimg, volc, rot, shifts, vol, wvol, grad_rot,
-                           grad_shifts, st),
+                           grad_shifts, st, eb.a ? &eb : nullptr, ef.a ? &ef : nullptr),
          "back-projection (bricks)");
   return TP_OK;
 }
@@ -321,6 +356,40 @@ const char* tp_status_string(tp_status s) {
 }
 
 const char* tp_last_error_detail(void) { return g_detail.c_str(); }
+
+tp_status tp_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_kt_mu);
+  g_kt_on = on != 0;
+  return ok();
+}
+
+tp_status tp_timing_read(int kernel_class, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return fail(TP_E_NULL, "total_ms and launches must not be NULL");
+  if (kernel_class < 0 || kernel_class >= TP_KT_COUNT) return fail(TP_E_VALUE, "unknown kernel class %d", kernel_class);
+  std::lock_guard<std::mutex> lk(g_kt_mu);
+  double sum = 0.0;
+  int64_t n = 0;
+  tp_status st = TP_OK;
+  std::vector<TimedLaunch> keep;
+  for (const TimedLaunch& t : g_kt) {
+    if (t.cls != kernel_class) {
+      keep.push_back(t);
+      continue;
+    }
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(t.ev.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t.ev.a, t.ev.b);
+    if (e != hipSuccess && st == TP_OK) st = fail(TP_E_LAUNCH, "event timing failed: %s", hipGetErrorString(e));
+    (void)hipEventDestroy(t.ev.a);
+    (void)hipEventDestroy(t.ev.b);
+    sum += ms;
+    ++n;
+  }
+  g_kt.swap(keep);
+  *total_ms = sum;
+  *launches = n;
+  return st == TP_OK ? ok() : st;
+}
 
 tp_status tp_validate(const tp_geom* geom) {
   TRY(check_geom(geom));

@@ -14,6 +14,8 @@ the other workloads go to stderr (and to --details FILE).
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import math
 import os
@@ -31,7 +33,49 @@ UNIT = "projections/s"
 # channels x 128 B/clk x 2.4 GHz), as is the fp32 vector rate.
 HBM_PEAK_GBS = 8000.0
 L2_PEAK_GBS = 8 * 16 * 128 * 2.4          # = 39321.6 GB/s
+LDS_PEAK_GBS = 256 * 128 * 2.4            # 256 CUs x 128 B/clk x 2.4 GHz = 78643.2 GB/s
 FP32_VECTOR_TFLOPS = 157.3
+
+
+# HBM traffic per launch of a kernel class, from two rocprofv3 PMC runs of this
+# script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
+# same counter reads for a plain device copy of known size (--copy-calibration).
+# A figure is valid only for the kernel sources it was taken on: it is
+# reported when the digest of back_projection_amd/csrc matches, else null.
+TRAFFIC = {
+    # profiles/k_bwd_brick_D128_cubic_hbm_traffic.txt
+    "backward": {"sources_sha256": "5b18a80e25c0166ca98a78779f2be1092a2f837bf09ac88d1434da2e46095682",
+                 "fetch_bytes": 3065248278, "write_bytes": 485664224},
+}
+
+
+def sources_digest():
+    d = hashlib.sha256()
+    csrc = os.path.join(ROOT, "back_projection_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            d.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                d.update(f.read())
+    return d.hexdigest()
+
+
+def measured_traffic(kclass):
+    t = TRAFFIC.get(kclass)
+    if not t or t["sources_sha256"] != sources_digest():
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
+
+def copy_calibration(torch, gib=1):
+    """A plain device-to-device copy of `gib` GiB, three times (for the PMC scale factor)."""
+    n = gib << 28   # float32 elements
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    eprint(f"[bench] copied {gib} GiB three times ({n * 4} bytes read and written per copy)")
 
 
 def eprint(*a):
@@ -46,26 +90,25 @@ def in_mask_pixels(H, r):
     return int(m.sum())
 
 
-def kernel_model(w, op):
-    """Algorithmic bytes of one launch of `op` on workload `w` (per pose x poses).
-    tap bytes: in-mask pixels x taps x 8 B (complex tap read or accumulate);
-    hbm bytes: compulsory reads/writes of images, volumes and pose params."""
+def kernel_model(w, kclass, ws_bytes=0):
+    """Algorithmic bytes of one launch of a brick-kernel class on workload `w`.
+    tap bytes: in-mask pixels x taps x 8 B per complex tap read (gather) or
+    accumulated (scatter); the fused backward does both.  hbm bytes: what the
+    launch must read or write in HBM at least (images, volume, pose params;
+    for the fold, the partial tiles and the volume)."""
     T = 64 if w.interp == 1 else 8
     npose = w.B * w.P
     n_in = in_mask_pixels(w.H, w.radius)
     img = npose * w.H * (w.H // 2 + 1) * 8
-    vol = w.vol.size * 8 if w.vol is not None else w.D * w.D * (w.D // 2 + 1) * 8
+    vol = w.D * w.D * (w.D // 2 + 1) * 8
     params = npose * (9 + 2) * 4
-    tap = npose * n_in * T * 8
-    if op == "forward":
-        hbm = img + vol + params
-    elif op == "backward_vol":
-        hbm = img + vol + params
-    elif op == "backward_rot":
-        hbm = img + vol + params + npose * 11 * 4
-    else:
-        raise ValueError(op)
-    return {"tap_bytes": tap, "hbm_bytes": hbm, "n_in": n_in, "poses": npose, "taps": T}
+    per_px = {"forward": T * 8, "backward": 2 * T * 8, "gradient": T * 8, "fold": 0}[kclass]
+    hbm = {"forward": img + vol + params,
+           "backward": img + vol + params + npose * 11 * 4,
+           "gradient": img + vol + params + npose * 11 * 4,
+           "fold": ws_bytes + vol}[kclass]
+    return {"tap_bytes": npose * n_in * per_px, "tap_bytes_per_pixel": per_px, "hbm_bytes": hbm, "n_in": n_in,
+            "poses": npose, "taps": T}
 
 
 def time_calls(fn, n, torch):
@@ -154,11 +197,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-sample", type=int, default=8192, help="poses of the oracle CPU baseline")
+    ap.add_argument("--cpu-sample", type=int, default=16384, help="poses of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-workloads", action="store_true", help="also time the other four workloads (stderr)")
     ap.add_argument("--details", default=None, help="write per-kernel details as JSON to this file")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (scale factor of the HBM traffic counters)")
+    ap.add_argument("--sources-digest", action="store_true", help="print the digest of the kernel sources and exit")
     args = ap.parse_args()
+    if args.sources_digest:
+        print(sources_digest())
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -175,6 +224,9 @@ def main():
         eprint("bench.py needs a GPU")
         sys.exit(1)
     bp.lib()   # fail loudly if the HIP library is missing
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()
     w = workloads.make(3)
@@ -205,6 +257,9 @@ def main():
     st = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    for k in bp.KERNEL_CLASSES:          # drop anything recorded before
+        bp.timing_read(k)
+    bp.timing_enable(True)               # event pairs around every brick kernel of the timed steps
     wall0 = time.perf_counter()
     e0.record(st)
     for _ in range(args.steps):
@@ -212,47 +267,50 @@ def main():
     e1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    bp.timing_enable(False)
     total_ms = e0.elapsed_time(e1)
     ms_per_step = total_ms / args.steps
     value = npose / (ms_per_step * 1e-3)
     eprint(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (event), wall {wall / args.steps * 1e3:.3f} "
            f"ms/step -> {value:.1f} proj/s")
 
-    # per-kernel breakdown, each call timed live with events on the same stream
-    n = max(3, args.steps)
-    parts = {
-        "forward": fwd,
-        "backward_vol": lambda: bp.project_3d_to_2d_backward(tg, tv, tr, ts, interp="cubic", radius_cutoff=r,
-                                                             need_rot=False, need_shifts=False, grad_vol=gv),
-        "backward_rot": lambda: bp.project_3d_to_2d_backward(tg, tv, tr, ts, interp="cubic", radius_cutoff=r,
-                                                             need_vol=False, grad_rot=gr, grad_shifts=gs),
-    }
+    # per-kernel averages over the timed region (library event pairs on the launch stream)
+    g = bp.Geom(B=1, P=w.P, Bv=1, Br=1, Bs=1, D=w.D, H=w.H, interp=1, oversampling=1.0, radius_cutoff=r)
+    ws_bwd = bp.lib().tp_workspace_size(ctypes.byref(g), bp.OP_PROJECT_BACKWARD)
     kernels = {}
-    for name, fn in parts.items():
-        ms, _ = time_calls(fn, n, torch)
-        m = kernel_model(w, name)
-        kernels[name] = {
-            "ms": round(ms, 4),
+    for k in bp.KERNEL_CLASSES:
+        tot, n = bp.timing_read(k)
+        if n == 0:
+            continue
+        ms = tot / n
+        m = kernel_model(w, k, ws_bwd)
+        kernels[k] = {
+            "launches": n,
+            "avg_ms": round(ms, 4),
+            "share_of_step": round(tot / total_ms, 4),
             "tap_GBps": round(m["tap_bytes"] / (ms * 1e-3) / 1e9, 1),
             "hbm_GBps": round(m["hbm_bytes"] / (ms * 1e-3) / 1e9, 1),
             "l2_frac": round(m["tap_bytes"] / (ms * 1e-3) / 1e9 / L2_PEAK_GBS, 4),
+            "lds_frac": round(m["tap_bytes"] / (ms * 1e-3) / 1e9 / LDS_PEAK_GBS, 4),
             "hbm_frac": round(m["hbm_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             **m,
         }
-        eprint(f"[bench] {name}: {kernels[name]}")
-    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+        eprint(f"[bench] kernel {k}: {kernels[k]}")
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
     kd = kernels[dom]
-    achieved = kd["tap_bytes"] / (kd["ms"] * 1e-3) / 1e9
+    achieved = kd["tap_bytes"] / (kd["avg_ms"] * 1e-3) / 1e9
+    traffic = measured_traffic(dom)
     roofline = {
         "bound": "l2",
         "achieved": round(achieved, 1),
         "peak": round(L2_PEAK_GBS, 1),
         "unit": "GB/s",
         "frac": round(achieved / L2_PEAK_GBS, 4),
-        "traffic": None,
+        "traffic": traffic,
         "kernel": dom,
-        "hbm": {"achieved": round(kd["hbm_bytes"] / (kd["ms"] * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": kd["hbm_frac"]},
+        "hbm": {"achieved": round(kd["hbm_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["hbm_frac"]},
+        "lds": {"achieved": round(achieved, 1), "peak": round(LDS_PEAK_GBS, 1), "unit": "GB/s",
+                "frac": kd["lds_frac"]},
     }
 
     details = {"kernels": kernels, "ms_per_step": ms_per_step}

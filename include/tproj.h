@@ -149,6 +149,25 @@ tp_status backproject_2d_to_3d_backward(const tp_geom* geom, const void* grad_da
  * (0 when none).  Returns (size_t)-1 for an invalid geometry.              */
 size_t tp_workspace_size(const tp_geom* geom, int op);
 
+/* Event timing of the brick kernels (benchmarks, profiling).  Kernel classes: */
+enum {
+  TP_KT_FORWARD = 0,   /* forward gather brick kernel (complex or real volume)           */
+  TP_KT_BACKWARD = 1,  /* back-projection brick kernel (rotation/shift grads fused in)    */
+  TP_KT_GRADIENT = 2,  /* rotation/shift gradient brick kernel                           */
+  TP_KT_FOLD = 3,      /* fold of the back-projection partial tiles into the volume      */
+  TP_KT_COUNT = 4
+};
+/* on != 0: from now on every call records a pair of HIP events on its stream
+ * around each brick kernel it launches (the events are created by the library
+ * and destroyed by tp_timing_read); on = 0 stops recording.  Process-wide host
+ * state; calls that record must not run concurrently with tp_timing_read. */
+tp_status tp_timing_enable(int on);
+/* Waits for the recorded events of one kernel class, returns their summed
+ * elapsed milliseconds and their count since the previous read of that class,
+ * and forgets them.  TP_E_NULL for NULL outputs, TP_E_VALUE for an unknown
+ * class, TP_E_LAUNCH if an event query fails.                              */
+tp_status tp_timing_read(int kernel_class, double* total_ms, int64_t* launches);
+
 /* Host-only argument check of a geometry (no GPU needed).                  */
 tp_status tp_validate(const tp_geom* geom);
 

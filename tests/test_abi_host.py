@@ -135,3 +135,16 @@ def test_python_binding_requires_gpu_tensors():
         bp.project_3d_to_2d(v, r)
     with pytest.raises(TypeError):
         bp.project_3d_to_2d(v.to(torch.complex128), r)
+
+
+def test_timing_api_host_side(L):
+    """Event timing: state switches and reads need no GPU when nothing was recorded."""
+    ms, n = ctypes.c_double(-1.0), ctypes.c_int64(-1)
+    assert L.tp_timing_read(0, ctypes.byref(ms), ctypes.byref(n)) == TP_OK
+    assert (ms.value, n.value) == (0.0, 0)
+    assert L.tp_timing_enable(1) == TP_OK
+    assert L.tp_timing_enable(0) == TP_OK
+    assert L.tp_timing_read(4, ctypes.byref(ms), ctypes.byref(n)) == TP_E_VALUE
+    assert L.tp_timing_read(-1, ctypes.byref(ms), ctypes.byref(n)) == TP_E_VALUE
+    assert L.tp_timing_read(1, None, ctypes.byref(n)) == TP_E_NULL
+    assert bp.timing_read("fold") == (0.0, 0)
