@@ -272,6 +272,45 @@ __device__ __forceinline__ void cand_prep(const EnumShared<WIN>& es, const KGeom
 }
 
 // ---------------------------------------------------------------------------
+// Bank-spreading lane permutation.  The LDS serves a 64-bit access for eight
+// consecutive lanes at a time, and lanes whose addresses share a bank pair
+// (16 pairs of 4-byte banks per 8-byte column) serialise.  Every tap of a
+// pixel sits at the same offset from the pixel's first tap, so the bank pair
+// of the first tap (key 0..15) decides all of the pixel's conflicts.  The
+// lanes are ranked by key and rank r moves to lane (r % 8) * 8 + r / 8: each
+// group of eight consecutive lanes then holds keys spread over the whole
+// range.  Inactive lanes (key < 0) go last.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int spread_dest(int key) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const unsigned long long act = __ballot(key >= 0);
+  const bool a = key >= 0;
+  unsigned long long less = 0ull, eq = act;
+#pragma unroll
+  for (int j = 3; j >= 0; --j) {
+    const unsigned long long bj = __ballot(a && ((key >> j) & 1)) ;
+    if (a && ((key >> j) & 1)) {
+      less |= eq & ~bj;
+      eq &= bj;
+    } else {
+      eq &= ~bj;
+    }
+  }
+  const int r = a ? __popcll(less) + __popcll(eq & below) : __popcll(act) + __popcll(~act & below);
+  return ((r & 7) << 3) | (r >> 3);
+}
+
+// Send v to lane dest (each lane a distinct dest), and fetch from lane src.
+__device__ __forceinline__ int lane_send(int v, int dest) { return __builtin_amdgcn_ds_permute(dest << 2, v); }
+__device__ __forceinline__ float lane_send(float v, int dest) {
+  return __int_as_float(__builtin_amdgcn_ds_permute(dest << 2, __float_as_int(v)));
+}
+__device__ __forceinline__ float lane_fetch(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
+// ---------------------------------------------------------------------------
 // Segmented sums across a wavefront whose lanes carry sorted keys (the hit of
 // the candidate; EB_SENTINEL past the end): after seg_scan, each lane holds
 // the sum of its key's values from the key's first lane up to itself.  DPP

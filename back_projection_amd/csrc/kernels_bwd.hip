@@ -167,6 +167,61 @@ __global__ void __launch_bounds__(256) k_band_max(const float2* __restrict__ Y, 
 // the brick kernel: scatter (SCAT, optional weight channel) and/or the
 // rotation / shift gradients of the forward (GRAD)
 // ---------------------------------------------------------------------------
+#ifndef BWD_UNROLL
+#define BWD_UNROLL 2
+#endif
+
+// One pixel of the back-projection, in the lane the bank-spreading permutation
+// gave it: pk packs (active, l) with l = floor(p) - lo; f holds the fractional
+// parts of p.  The gather phase interpolates the forward volume's tile (value
+// and partial derivatives, for the rotation / shift gradients); the scatter
+// phase adds c = conj(phi) Y (and the weight image value) with the taps'
+// weights to the accumulator tiles.  Every LDS read of an iteration is issued
+// before its atomics: a read issued after them waits for them to drain.
+template <int NT>
+__device__ __forceinline__ void bwd_gather(int pk, float fx, float fy, float fz, const float2* vt, float2& I,
+                                           float2* dI) {
+  I = make_float2(0.f, 0.f);
+  dI[0] = dI[1] = dI[2] = I;
+  if (!(pk & 1)) return;
+  const int l[3] = {(pk >> 1) & 15, (pk >> 5) & 15, (pk >> 9) & 15};
+  float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
+  axis_weights<NT>(fx, wx);
+  axis_weights<NT>(fy, wy);
+  axis_weights<NT>(fz, wz);
+  axis_dweights<NT>(fx, dx);
+  axis_dweights<NT>(fy, dy);
+  axis_dweights<NT>(fz, dz);
+  interp_tile_w<NT, true>(vt, l, wx, wy, wz, dx, dy, dz, I, dI);
+}
+
+template <int NT, bool WEIGHTS>
+__device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz, float2 c, float wimg,
+                                            unsigned long long* acc_t, unsigned int* acc_w, float scale,
+                                            float wscale) {
+  if (!(pk & 1)) return;
+  const int l[3] = {(pk >> 1) & 15, (pk >> 5) & 15, (pk >> 9) & 15};
+  float wx[NT], wy[NT], wz[NT];
+  axis_weights<NT>(fx, wx);
+  axis_weights<NT>(fy, wy);
+  axis_weights<NT>(fz, wz);
+  const float cr = c.x * scale, ci = c.y * scale;
+  const float wv = WEIGHTS ? wimg * wscale : 0.f;
+#pragma unroll
+  for (int jc = 0; jc < NT; ++jc)
+#pragma unroll
+    for (int jb = 0; jb < NT; ++jb) {
+      const float wyz = wy[jb] * wz[jc];
+      const float ur = wyz * cr, ui = wyz * ci, uw = wyz * wv;
+      const int rowb = (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
+#pragma unroll
+      for (int ja = 0; ja < NT; ++ja) {
+        atomicAdd(&acc_t[rowb + ja], pack_fixed(fixed_round(wx[ja], ur), fixed_round(wx[ja], ui)));
+        if constexpr (WEIGHTS) atomicAdd(&acc_w[rowb + ja], (unsigned int)fixed_round(wx[ja], uw));
+      }
+    }
+}
+
 template <int NT, bool WEIGHTS, bool GRAD>
 __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y, const float* __restrict__ Wimg,
                                                    const float2* __restrict__ vol, const float* __restrict__ rot,
@@ -259,72 +314,62 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
       for (int qb = 0; qb < nrows;) {
         int nr;
         const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh, nr);
-        // software pipeline: the next batch's candidate and image values are
-        // fetched while this batch is processed
-        Cand nx;
-        cand_prep(es, g, wave * 64 + lane, ncand, lo, bg.S, nx);
-        float2 ynx = nx.act ? Y[nx.k] : make_float2(0.f, 0.f);
-        float wnx = (WEIGHTS && nx.act) ? Wimg[nx.k] : 0.f;
-        for (int c0 = wave * 64; c0 < ncand; c0 += EB_THREADS) {   // wave-uniform (segmented sums)
-          const Cand cu = nx;
-          const float2 ycu = ynx;
-          const float wcu = wnx;
-          if (c0 + EB_THREADS < ncand) {
-            cand_prep(es, g, c0 + EB_THREADS + lane, ncand, lo, bg.S, nx);
-            ynx = nx.act ? Y[nx.k] : make_float2(0.f, 0.f);
-            if constexpr (WEIGHTS) wnx = nx.act ? Wimg[nx.k] : 0.f;
+        for (int c0 = wave * 64; c0 < ncand; c0 += BWD_UNROLL * EB_THREADS) {   // wave-uniform (permutes, sums)
+          constexpr int U = BWD_UNROLL;
+          Cand cu[U];
+          float2 c[U];
+          int dest[U], mpk[U];
+          float mf[U][3], wimg[U];
+          float2 mc[U];
+          float mw[U];
+          // phase 1: look up, load, move each pixel to its bank-spreading lane
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            cand_prep(es, g, c0 + u * EB_THREADS + lane, ncand, lo, bg.S, cu[u]);
+            c[u] = make_float2(0.f, 0.f);
+            wimg[u] = 0.f;
+            float f[3] = {0.f, 0.f, 0.f};
+            int pk = 0, key = -1;
+            if (cu[u].act) {
+              c[u] = Y[cu[u].k];
+              if (shifts) c[u] = cmulc(shift_phase(cu[u].kx, cu[u].ky, cu[u].sx, cu[u].sy, g.inv_h), c[u]);
+              if constexpr (WEIGHTS) wimg[u] = Wimg[cu[u].k];
+#pragma unroll
+              for (int a = 0; a < 3; ++a) f[a] = cu[u].p[a] - floorf(cu[u].p[a]);
+              pk = 1 | (cu[u].l[0] << 1) | (cu[u].l[1] << 5) | (cu[u].l[2] << 9);
+              key = (cu[u].l[0] + cu[u].l[1] * TSY + cu[u].l[2] * TSZ) & 15;
+            }
+            dest[u] = spread_dest(key);
+            mpk[u] = lane_send(pk, dest[u]);
+#pragma unroll
+            for (int a = 0; a < 3; ++a) mf[u][a] = lane_send(f[a], dest[u]);
+            mc[u] = make_float2(lane_send(c[u].x, dest[u]), lane_send(c[u].y, dest[u]));
+            mw[u] = WEIGHTS ? lane_send(wimg[u], dest[u]) : 0.f;
           }
-          float gacc[8];
+          // phase 2 (gradients): gather, back to the pixel's own lane, per-pose sums;
+          // d/dR and d/ds of Re<G, phi I(V)> with conj(G) phi = conj(c)
+          if constexpr (GRAD) {
 #pragma unroll
-          for (int q = 0; q < 8; ++q) gacc[q] = 0.f;
-          const int key = cu.key;
-          if (cu.act) {
-            {
-              const float fkx = cu.kx, fky = cu.ky;
-              const float* p = cu.p;
-              const int* l = cu.l;
-              float2 c = ycu;
-              if (shifts) c = cmulc(shift_phase(fkx, fky, cu.sx, cu.sy, g.inv_h), c);   // conj(phi) * Y
-              float wx[NT], wy[NT], wz[NT];
-              const float fx = p[0] - floorf(p[0]), fy = p[1] - floorf(p[1]), fz = p[2] - floorf(p[2]);
-              axis_weights<NT>(fx, wx);
-              axis_weights<NT>(fy, wy);
-              axis_weights<NT>(fz, wz);
-              if constexpr (GRAD) {
-                // d/dR and d/ds of Re<G, phi I(V)>: conj(G) phi = conj(c)
-                float dx[NT], dy[NT], dz[NT];
-                axis_dweights<NT>(fx, dx);
-                axis_dweights<NT>(fy, dy);
-                axis_dweights<NT>(fz, dz);
-                float2 I, dI[3];
-                interp_tile_w<NT, true>(vt, l, wx, wy, wz, dx, dy, dz, I, dI);
-                const float2 d0 = dI[0], d1 = dI[1], d2 = dI[2];
-                const float t0 = c.x * d0.x + c.y * d0.y, t1 = c.x * d1.x + c.y * d1.y, t2 = c.x * d2.x + c.y * d2.y;
-                const float im = c.x * I.y - c.y * I.x;
-                gacc[0] = t0 * fkx; gacc[1] = t0 * fky;
-                gacc[2] = t1 * fkx; gacc[3] = t1 * fky;
-                gacc[4] = t2 * fkx; gacc[5] = t2 * fky;
-                gacc[6] = fkx * im; gacc[7] = fky * im;
-              }
-              // scatter all taps (they all lie in the halo tile)
-              const float cr = c.x * scale, ci = c.y * scale;
-              const float wv = WEIGHTS ? wcu * wscale : 0.f;
+            for (int u = 0; u < U; ++u) {
+              float2 I, dI[3];
+              bwd_gather<NT>(mpk[u], mf[u][0], mf[u][1], mf[u][2], vt, I, dI);
+              I = make_float2(lane_fetch(I.x, dest[u]), lane_fetch(I.y, dest[u]));
 #pragma unroll
-              for (int jc = 0; jc < NT; ++jc)
-#pragma unroll
-                for (int jb = 0; jb < NT; ++jb) {
-                  const float wyz = wy[jb] * wz[jc];
-                  const float ur = wyz * cr, ui = wyz * ci, uw = wyz * wv;
-                  const int rowb = (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
-#pragma unroll
-                  for (int ja = 0; ja < NT; ++ja) {
-                    atomicAdd(&acc_t[rowb + ja], pack_fixed(fixed_round(wx[ja], ur), fixed_round(wx[ja], ui)));
-                    if constexpr (WEIGHTS) atomicAdd(&acc_w[rowb + ja], (unsigned int)fixed_round(wx[ja], uw));
-                  }
-                }
+              for (int a = 0; a < 3; ++a)
+                dI[a] = make_float2(lane_fetch(dI[a].x, dest[u]), lane_fetch(dI[a].y, dest[u]));
+              const float2 cc = c[u];
+              const float t0 = cc.x * dI[0].x + cc.y * dI[0].y, t1 = cc.x * dI[1].x + cc.y * dI[1].y;
+              const float t2 = cc.x * dI[2].x + cc.y * dI[2].y;
+              const float im = cc.x * I.y - cc.y * I.x;
+              const float fkx = cu[u].act ? cu[u].kx : 0.f, fky = cu[u].act ? cu[u].ky : 0.f;
+              float gacc[8] = {t0 * fkx, t0 * fky, t1 * fkx, t1 * fky, t2 * fkx, t2 * fky, fkx * im, fky * im};
+              grad_collect(gacc, cu[u].key, gw);
             }
           }
-          if constexpr (GRAD) grad_collect(gacc, key, gw);
+          // phase 3: the taps into the accumulator tile (nothing waits on them)
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            bwd_scatter<NT, WEIGHTS>(mpk[u], mf[u][0], mf[u][1], mf[u][2], mc[u], mw[u], acc_t, acc_w, scale, wscale);
         }
         __syncthreads();
         qb += nr;
