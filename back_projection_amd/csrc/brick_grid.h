@@ -64,8 +64,10 @@ __host__ __device__ inline bool brick_active(const BrickGrid& g, int bi, int bj,
 
 // Number of pose chunks (work items) of a brick: its expected pixel load over
 // the pose list divided by the per-item target.  A random plane through the
-// origin meets a brick at distance rho with probability ~ S / rho and then
-// cuts ~S^2 pixels, so the load per pose is ~ min(1.3 S^2, S^3 / (2 rho)).
+// origin meets a brick at distance rho >> S with probability ~0.75 S / rho
+// (the cube's mean half-width over rho); the slice is a half plane, which
+// halves that, and a hit cuts ~0.67 S^2 pixels (the cube's volume over its
+// mean width).  So the load per pose is ~min(0.67 S^2, S^3 / (4 rho)).
 __host__ __device__ inline int brick_chunks(const BrickGrid& g, int bi, int bj, int bk) {
   if (!brick_active(g, bi, bj, bk)) return 0;
   const int idx[3] = {bi, bj, bk};
@@ -77,10 +79,12 @@ __host__ __device__ inline int brick_chunks(const BrickGrid& g, int bi, int bj, 
   int64_t rho2 = isqrt64(c2);               // twice the centre distance
   if (rho2 < 1) rho2 = 1;
   const int64_t S = g.S;
-  int64_t per_pose_x10 = (13 * S * S * rho2 < 10 * S * S * S) ? 13 * S * S * rho2 : 10 * S * S * S;  // x10 x rho2
-  // expected pixels = list_len * per_pose_x10 / (10 * rho2) * dens_q8 / 256
-  const int64_t num = (int64_t)g.list_len * per_pose_x10 * g.dens_q8;
-  const int64_t den = 10 * rho2 * 256 * g.target;
+  // 100 * rho2 * (pixels per pose) = min(67 S^2 rho2, 50 S^3 * ... ): S^3 / (4 rho) = S^3 / (2 rho2)
+  const int64_t a1 = 67 * S * S * rho2, a2 = 50 * S * S * S;
+  const int64_t per_pose_x100 = a1 < a2 ? a1 : a2;
+  // expected pixels = list_len * per_pose_x100 / (100 * rho2) * dens_q8 / 256
+  const int64_t num = (int64_t)g.list_len * per_pose_x100 * g.dens_q8;
+  const int64_t den = 100 * rho2 * 256 * g.target;
   int64_t k = (num + den - 1) / den;
   if (k < 1) k = 1;
   if (k > g.list_len) k = g.list_len;

@@ -1,72 +1,74 @@
 // Block-wide enumeration of the pixels whose slice sample falls in one brick,
 // shared by the brick kernels (forward gather, gradients, back-projection).
 //
-// A workgroup of 256 threads walks its brick's pose list in passes of 256
-// poses.  Each pass:
-//   1. one pose per thread is tested against the brick; the hits are kept as
-//      a bit mask;
+// A workgroup of NW wavefronts walks its brick's pose list in passes of one
+// pose per thread.  Each pass:
+//   1. every thread tests its pose against the brick; the hits are kept as a
+//      bit mask;
 //   2. the hits are taken in windows of up to WIN; one thread per hit sets up
 //      the hit's geometry in LDS and bounds its image rows (ky);
-//   3. the rows of the window are laid out one after the other and handled up
-//      to 256 at a time, one per thread: each thread derives the kx interval
-//      of its row from the slab inequalities of the brick, a block-wide scan
-//      turns the interval lengths into candidate offsets, and each row writes
-//      its index into a per-candidate byte table (a stage takes rows while
-//      their candidates fit the table);
-//   4. the candidates (kx, ky, hit) are dealt to the four wavefronts in
-//      chunks of 64, so the lanes stay full across row and hit boundaries; a
-//      lane finds its row with one table read.
-// The brick kernels are bound by LDS latency more than by anything else: a
-// dependent LDS read waits behind all the LDS traffic (atomics included) the
-// wavefronts have queued, so a candidate's path holds as few of them as
-// possible.  The enumeration is a superset of the owned pixels (margins on
-// the intervals); the owner test on floor(p), computed with the one
-// slice_coord expression, decides.
+//   3. the rows of the window are laid out one after the other and handled
+//      one per thread: each thread derives the kx interval of its row from
+//      the slab inequalities of the brick, a block-wide scan turns the
+//      interval lengths into candidate offsets, and each row writes its index
+//      into a per-candidate table (a stage takes rows while their candidates
+//      fit the table);
+//   4. the candidates (kx, ky, hit) are dealt to the wavefronts in chunks of
+//      64, so the lanes stay full across row and hit boundaries; a lane finds
+//      its row with one table read.
+// The enumeration is a superset of the owned pixels (margins on the
+// intervals); the owner test on floor(p), computed with the one slice_coord
+// expression, decides.
 #pragma once
+
+#include <type_traits>
 
 #include "gather_common.h"
 
 namespace tproj {
 
-constexpr int EB_THREADS = 256;
-constexpr int EB_ROWS = 256;
 constexpr int EB_CMAX = 2048;            // candidates per row stage (a row has at most H/2 + 1 <= 2048)
 constexpr int EB_SENTINEL = 0x7fffffff;
 
-template <int WIN>
+// WIN hits per window, NW wavefronts per workgroup (one pose and one row per
+// thread).
+template <int WIN, int NW>
 struct EnumShared {
-  unsigned long long hitmask[4];   // hit poses of this pass (bit = thread)
-  int wave_n[4];
-  int wtot[4];
+  static constexpr int THREADS = NW * 64;
+  static constexpr int ROWS = NW * 64;
+  using RowIndex = std::conditional_t<(ROWS <= 256), unsigned char, unsigned short>;
+  unsigned long long hitmask[NW];  // hit poses of this pass (bit = thread)
+  int wave_n[NW];
+  int wtot[NW];
   int nr, nc;                      // rows and candidates of the current row stage
   float4 geo0[WIN];                // R[0] R[3] R[6] R[1]   (rotation columns 0 and 1)
   float4 geo1[WIN];                // R[4] R[7] sx sy
   int hpose[WIN];                  // image index b * P + n
   int hrow[WIN + 1];               // first row of each hit; hrow[nw] = rows of the window
   int hky[WIN];                    // ky of each hit's first row
-  int rstart[EB_ROWS];             // first candidate of row r
-  int rinfo[EB_ROWS];              // kx0 | (ky & 0xfff) << 11 | hit << 23
-  unsigned char crow[EB_CMAX];     // row of candidate i
+  int rstart[ROWS];                // first candidate of row r
+  int rinfo[ROWS];                 // kx0 | (ky & 0xfff) << 11 | hit << 23
+  RowIndex crow[EB_CMAX];          // row of candidate i
 };
 
 // Record the hit flags of one pass (one pose per thread); returns the hit
 // count (block-uniform).
-template <int WIN>
-__device__ __forceinline__ int compact_hits(EnumShared<WIN>& es, bool hit) {
+template <int WIN, int NW>
+__device__ __forceinline__ int compact_hits(EnumShared<WIN, NW>& es, bool hit) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const unsigned long long m = __ballot(hit);
   if (lane == 0) es.hitmask[wave] = m;
   __syncthreads();
   int nh = 0;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) nh += __popcll(es.hitmask[v]);
+  for (int v = 0; v < NW; ++v) nh += __popcll(es.hitmask[v]);
   __syncthreads();   // every thread has read the mask before the next pass rewrites it
   return nh;
 }
 
 // Thread offset (within the pass) of the j-th hit (j < the hit count).
-template <int WIN>
-__device__ __forceinline__ int nth_hit(const EnumShared<WIN>& es, int j) {
+template <int WIN, int NW>
+__device__ __forceinline__ int nth_hit(const EnumShared<WIN, NW>& es, int j) {
   int v = 0;
   unsigned long long m = es.hitmask[0];
   while (j >= __popcll(m)) {
@@ -99,8 +101,8 @@ __device__ __forceinline__ void cols_to_r9(const float4& c0, const float4& c1, f
 // Window set-up: threads t < nw take hit hw + t of the pass that starts at
 // list entry eb.  Writes the geometry, the image index and the row range of
 // every hit, then the row prefix.
-template <int WIN>
-__device__ __forceinline__ void window_setup(EnumShared<WIN>& es, const KGeom& g, const float* __restrict__ rot,
+template <int WIN, int NW>
+__device__ __forceinline__ void window_setup(EnumShared<WIN, NW>& es, const KGeom& g, const float* __restrict__ rot,
                                              const float* __restrict__ shifts, int vsel, int64_t eb, int hw, int nw,
                                              const float bl[3], const float bh[3]) {
   static_assert(WIN <= 64, "one wavefront sets up a window");
@@ -172,11 +174,11 @@ __device__ __forceinline__ void row_interval(const KGeom& g, const float a0[3], 
 }
 
 // Row stage: rows qb, qb + 1, ... of the window, one per thread, as many as
-// fit EB_ROWS rows and EB_CMAX candidates.  Returns the candidate count and,
+// fit the workgroup's threads and EB_CMAX candidates.  Returns the candidate count and,
 // in nr, the rows taken (both block-uniform; nr >= 1 while rows remain, as one
 // row has at most H/2 + 1 <= EB_CMAX candidates).
-template <int WIN>
-__device__ __forceinline__ int row_stage(EnumShared<WIN>& es, const KGeom& g, int qb, int nrows, int nw,
+template <int WIN, int NW>
+__device__ __forceinline__ int row_stage(EnumShared<WIN, NW>& es, const KGeom& g, int qb, int nrows, int nw,
                                          const float bl[3], const float bh[3], int& nr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = qb + tid;
@@ -205,7 +207,7 @@ __device__ __forceinline__ int row_stage(EnumShared<WIN>& es, const KGeom& g, in
   __syncthreads();
   int carry = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w)
+  for (int w = 0; w < NW; ++w)
     if (w < wave) carry += es.wtot[w];
   const int incl = carry + v, start = incl - cnt;
   // the rows whose candidates fit the table: a prefix of the rows, since the
@@ -216,10 +218,12 @@ __device__ __forceinline__ int row_stage(EnumShared<WIN>& es, const KGeom& g, in
   if (take) {
     es.rstart[tid] = start;
     es.rinfo[tid] = kx0 | ((ky & 0xfff) << 11) | (h << 23);
-    for (int j = 0; j < cnt; ++j) es.crow[start + j] = (unsigned char)tid;
+    for (int j = 0; j < cnt; ++j) es.crow[start + j] = (typename EnumShared<WIN, NW>::RowIndex)tid;
   }
   __syncthreads();
-  const int n_taken = es.wave_n[0] + es.wave_n[1] + es.wave_n[2] + es.wave_n[3];
+  int n_taken = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) n_taken += es.wave_n[w];
   if (tid == n_taken - 1) es.nc = incl;
   __syncthreads();
   nr = n_taken;
@@ -227,8 +231,8 @@ __device__ __forceinline__ int row_stage(EnumShared<WIN>& es, const KGeom& g, in
 }
 
 // Candidate i (< the row stage's count): its hit, kx and ky.
-template <int WIN>
-__device__ __forceinline__ void candidate_at(const EnumShared<WIN>& es, int i, int& h, int& kx, int& ky) {
+template <int WIN, int NW>
+__device__ __forceinline__ void candidate_at(const EnumShared<WIN, NW>& es, int i, int& h, int& kx, int& ky) {
   const int r = es.crow[i];
   const int info = es.rinfo[r];
   h = info >> 23;
@@ -250,8 +254,8 @@ struct Cand {
 };
 
 // Candidate i of the current row stage (i >= ncand: key = EB_SENTINEL).
-template <int WIN>
-__device__ __forceinline__ void cand_prep(const EnumShared<WIN>& es, const KGeom& g, int i, int ncand, const int lo[3],
+template <int WIN, int NW>
+__device__ __forceinline__ void cand_prep(const EnumShared<WIN, NW>& es, const KGeom& g, int i, int ncand, const int lo[3],
                                           int S, Cand& c) {
   c.key = EB_SENTINEL;
   c.act = false;
@@ -309,6 +313,9 @@ __device__ __forceinline__ float lane_send(float v, int dest) {
 __device__ __forceinline__ float lane_fetch(float v, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
+__device__ __forceinline__ float2 lane_fetch(float2 v, int src) {
+  return make_float2(lane_fetch(v.x, src), lane_fetch(v.y, src));
+}
 
 // ---------------------------------------------------------------------------
 // Segmented sums across a wavefront whose lanes carry sorted keys (the hit of
@@ -353,8 +360,8 @@ __device__ __forceinline__ bool seg_tail(int key) {
 // end of a window the sums go to the pose's gradient with global atomics,
 // scaled by o (rotation) or 2 pi / H (shifts).
 // ---------------------------------------------------------------------------
-template <int WIN>
-__device__ __forceinline__ void grad_flush(const KGeom& g, const EnumShared<WIN>& es, float (*gw)[8], int nw,
+template <int WIN, int NW>
+__device__ __forceinline__ void grad_flush(const KGeom& g, const EnumShared<WIN, NW>& es, float (*gw)[8], int nw,
                                            float* __restrict__ grad_rot, float* __restrict__ grad_s) {
   const int tid = threadIdx.x;
   if (tid < nw * 8) {

@@ -220,8 +220,10 @@ __device__ __forceinline__ void interp_tile_w(const T* tile, const int l[3], con
   T z0 = zero_of(T{});
   I = z0;
   if constexpr (DERIV) { dI[0] = z0; dI[1] = z0; dI[2] = z0; }
+  // contract x within each row, then y within each plane, then z
 #pragma unroll
   for (int c = 0; c < NT; ++c) {
+    T s = z0, sx = z0, sy = z0;   // plane sums: wy*r, wy*rx, dy*r
 #pragma unroll
     for (int b = 0; b < NT; ++b) {
       const T* row = base + c * Tl::SZ + b * Tl::SY;
@@ -232,13 +234,17 @@ __device__ __forceinline__ void interp_tile_w(const T* tile, const int l[3], con
         fma_into(wx[a], v, r);
         if constexpr (DERIV) fma_into(dx[a], v, rx);
       }
-      const float wyz = wy[b] * wz[c];
-      fma_into(wyz, r, I);
+      fma_into(wy[b], r, s);
       if constexpr (DERIV) {
-        fma_into(wyz, rx, dI[0]);
-        fma_into(dy[b] * wz[c], r, dI[1]);
-        fma_into(wy[b] * dz[c], r, dI[2]);
+        fma_into(wy[b], rx, sx);
+        fma_into(dy[b], r, sy);
       }
+    }
+    fma_into(wz[c], s, I);
+    if constexpr (DERIV) {
+      fma_into(wz[c], sx, dI[0]);
+      fma_into(wz[c], sy, dI[1]);
+      fma_into(dz[c], s, dI[2]);
     }
   }
 }

@@ -77,6 +77,7 @@ __device__ __forceinline__ bool pose_hits(const KGeom& g, const float* __restric
 // forward
 // ---------------------------------------------------------------------------
 constexpr int FWD_WIN = 32;
+constexpr int FWD_NW = 4;   // wavefronts per workgroup
 
 template <int NT, typename T>
 __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, const float* __restrict__ rot,
@@ -85,7 +86,7 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
   using Tl = Tile<NT>;
   constexpr bool CPLX = sizeof(T) == 8;
   __shared__ T tile[Tl::SIZE];
-  __shared__ EnumShared<FWD_WIN> es;
+  __shared__ EnumShared<FWD_WIN, FWD_NW> es;
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
   const int b = find_brick(prefix, bg.nb3, w);
@@ -100,7 +101,7 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
 
   const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int64_t eb = e0; eb < e1; eb += EB_THREADS) {
+  for (int64_t eb = e0; eb < e1; eb += FWD_NW * 64) {
     const int nh = compact_hits(es, pose_hits(g, rot, vsel, eb + threadIdx.x, e1, bl, bh));
     for (int hw = 0; hw < nh; hw += FWD_WIN) {
       const int nw = min(FWD_WIN, nh - hw);
@@ -109,20 +110,40 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
       for (int qb = 0; qb < nrows;) {
         int nr;
         const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh, nr);
-        // software pipeline: the next candidate is looked up while this one
-        // is interpolated
-        Cand nx;
-        cand_prep(es, g, wave * 64 + lane, ncand, lo, bg.S, nx);
-        for (int i = wave * 64 + lane; i < ncand; i += EB_THREADS) {
-          const Cand cu = nx;
-          if (i + EB_THREADS < ncand) cand_prep(es, g, i + EB_THREADS, ncand, lo, bg.S, nx);
-          if (!cu.act) continue;
-          T I;
-          interp_tile_t<NT, false>(tile, cu.p, cu.l, I, (T*)nullptr);
-          if constexpr (CPLX) {
-            if (shifts) I = cmul(shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h), I);
+        for (int c0 = wave * 64; c0 < ncand; c0 += FWD_NW * 64) {   // wave-uniform (lane permutes)
+          Cand cu;
+          cand_prep(es, g, c0 + lane, ncand, lo, bg.S, cu);
+          // the interpolation runs in the lane the bank-spreading order gives
+          // the pixel; the value comes back to the pixel's own lane
+          float f[3] = {0.f, 0.f, 0.f};
+          int pk = 0, key = -1;
+          if (cu.act) {
+#pragma unroll
+            for (int a = 0; a < 3; ++a) f[a] = cu.p[a] - floorf(cu.p[a]);
+            pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
+            key = (cu.l[0] + cu.l[1] * Tl::SY + cu.l[2] * Tl::SZ) & 15;
           }
-          out[cu.k] = I;
+          const int dest = spread_dest(key);
+          const int mpk = lane_send(pk, dest);
+          float mf[3];
+#pragma unroll
+          for (int a = 0; a < 3; ++a) mf[a] = lane_send(f[a], dest);
+          T I = zero_of(T{});
+          if (mpk & 1) {
+            const int ml[3] = {(mpk >> 1) & 15, (mpk >> 5) & 15, (mpk >> 9) & 15};
+            float wx[NT], wy[NT], wz[NT];
+            axis_weights<NT>(mf[0], wx);
+            axis_weights<NT>(mf[1], wy);
+            axis_weights<NT>(mf[2], wz);
+            interp_tile_w<NT, false>(tile, ml, wx, wy, wz, wx, wy, wz, I, (T*)nullptr);
+          }
+          I = lane_fetch(I, dest);
+          if (cu.act) {
+            if constexpr (CPLX) {
+              if (shifts) I = cmul(shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h), I);
+            }
+            out[cu.k] = I;
+          }
         }
         __syncthreads();   // the next row stage rewrites the rows
         qb += nr;
@@ -183,6 +204,7 @@ __global__ void __launch_bounds__(256) k_fwd_edge(const T* __restrict__ vol, con
 // atomics.
 // ---------------------------------------------------------------------------
 constexpr int GRAD_WIN = 32;
+constexpr int GRAD_NW = 4;
 
 template <int NT, bool CPLX, bool REAL>
 __global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ volc, const float* __restrict__ volr,
@@ -193,7 +215,7 @@ __global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ v
   using Tl = Tile<NT>;
   __shared__ float2 tc[CPLX ? Tl::SIZE : 1];
   __shared__ float tr[REAL ? Tl::SIZE : 1];
-  __shared__ EnumShared<GRAD_WIN> es;
+  __shared__ EnumShared<GRAD_WIN, GRAD_NW> es;
   __shared__ float gw[GRAD_WIN][8];
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
@@ -207,12 +229,12 @@ __global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ v
   const int64_t nvol = (int64_t)g.D * g.D * g.W;
   if constexpr (CPLX) stage_tile_t<NT>(tc, volc + (int64_t)vsel * nvol, g, lo);
   if constexpr (REAL) stage_tile_t<NT>(tr, volr + (int64_t)vsel * nvol, g, lo);
-  for (int i = threadIdx.x; i < GRAD_WIN * 8; i += EB_THREADS) (&gw[0][0])[i] = 0.f;
+  for (int i = threadIdx.x; i < GRAD_WIN * 8; i += GRAD_NW * 64) (&gw[0][0])[i] = 0.f;
   __syncthreads();
 
   const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int64_t eb = e0; eb < e1; eb += EB_THREADS) {
+  for (int64_t eb = e0; eb < e1; eb += GRAD_NW * 64) {
     const int nh = compact_hits(es, pose_hits(g, rot, vsel, eb + threadIdx.x, e1, bl, bh));
     for (int hw = 0; hw < nh; hw += GRAD_WIN) {
       const int nw = min(GRAD_WIN, nh - hw);
@@ -227,12 +249,12 @@ __global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ v
         cand_prep(es, g, wave * 64 + lane, ncand, lo, bg.S, nx);
         float2 unx = (CPLX && nx.act) ? U[nx.k] : make_float2(0.f, 0.f);
         float urnx = (REAL && nx.act) ? Ur[nx.k] : 0.f;
-        for (int c0 = wave * 64; c0 < ncand; c0 += EB_THREADS) {   // wave-uniform: the sums need every lane
+        for (int c0 = wave * 64; c0 < ncand; c0 += GRAD_NW * 64) {   // wave-uniform: the sums need every lane
           const Cand cu = nx;
           const float2 ucu = unx;
           const float urcu = urnx;
-          if (c0 + EB_THREADS < ncand) {
-            cand_prep(es, g, c0 + EB_THREADS + lane, ncand, lo, bg.S, nx);
+          if (c0 + GRAD_NW * 64 < ncand) {
+            cand_prep(es, g, c0 + GRAD_NW * 64 + lane, ncand, lo, bg.S, nx);
             if constexpr (CPLX) unx = nx.act ? U[nx.k] : make_float2(0.f, 0.f);
             if constexpr (REAL) urnx = nx.act ? Ur[nx.k] : 0.f;
           }

@@ -40,7 +40,12 @@ constexpr int TSY = 17;                    // padded strides (as the gather tile
 constexpr int TSZ = 16 * 17 + 4;
 constexpr int TSIZE = TE * TSZ;            // 4416 padded entries
 constexpr int TLOG = TE * TE * TE;         // 4096 logical entries
-constexpr int PER_LANE = TLOG / 256;       // 16
+#ifndef BWD_NW
+#define BWD_NW 4
+#endif
+constexpr int BNW = BWD_NW;                 // wavefronts per workgroup of the brick kernel
+constexpr int BTHREADS = BNW * 64;
+constexpr int PER_LANE = TLOG / BTHREADS;   // partial-tile entries per thread
 constexpr int WINDOW = 16;                 // poses per fixed-point window
 constexpr float FIX_RANGE = 0.9f * 2147483648.0f;
 constexpr int MAX_BANDS = 128;
@@ -223,7 +228,7 @@ __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz
 }
 
 template <int NT, bool WEIGHTS, bool GRAD>
-__global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y, const float* __restrict__ Wimg,
+__global__ void __launch_bounds__(BTHREADS) k_bwd_brick(const float2* __restrict__ Y, const float* __restrict__ Wimg,
                                                    const float2* __restrict__ vol, const float* __restrict__ rot,
                                                    const float* __restrict__ shifts, float* __restrict__ grad_rot,
                                                    float* __restrict__ grad_s, float2* __restrict__ part_c,
@@ -234,7 +239,7 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
   __shared__ unsigned long long acc_t[TSIZE];
   __shared__ unsigned int acc_w[WEIGHTS ? TSIZE : 1];
   __shared__ float2 vt[GRAD ? TSIZE : 1];
-  __shared__ EnumShared<WINDOW> es;
+  __shared__ EnumShared<WINDOW, BNW> es;
   __shared__ float hit_m[WINDOW], hit_w[WINDOW], hit_c[WINDOW];
   __shared__ float gw[WINDOW][8];
 
@@ -257,23 +262,23 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
     acc[i] = make_float2(0.f, 0.f);
     accw[i] = 0.f;
   }
-  for (int i = tid; i < TSIZE; i += EB_THREADS) {
+  for (int i = tid; i < TSIZE; i += BTHREADS) {
     acc_t[i] = 0ull;
     if constexpr (WEIGHTS) acc_w[i] = 0u;
   }
   if constexpr (GRAD) {
     using Tl = Tile<NT>;
     const float2* V = vol + (int64_t)vsel * nvol;
-    for (int i = tid; i < TLOG; i += EB_THREADS) {
+    for (int i = tid; i < TLOG; i += BTHREADS) {
       const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
       vt[z * TSZ + y * TSY + x] = tap_value(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
     }
-    for (int i = tid; i < WINDOW * 8; i += EB_THREADS) (&gw[0][0])[i] = 0.f;
+    for (int i = tid; i < WINDOW * 8; i += BTHREADS) (&gw[0][0])[i] = 0.f;
   }
   __syncthreads();
 
   const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
-  for (int64_t eb = e0; eb < e1; eb += EB_THREADS) {
+  for (int64_t eb = e0; eb < e1; eb += BTHREADS) {
     // ---- hit detection: one pose per thread (degenerate maps go to the edge kernel) ----
     bool hit = false;
     const int64_t e = eb + tid;
@@ -314,7 +319,7 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
       for (int qb = 0; qb < nrows;) {
         int nr;
         const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh, nr);
-        for (int c0 = wave * 64; c0 < ncand; c0 += BWD_UNROLL * EB_THREADS) {   // wave-uniform (permutes, sums)
+        for (int c0 = wave * 64; c0 < ncand; c0 += BWD_UNROLL * BTHREADS) {   // wave-uniform (permutes, sums)
           constexpr int U = BWD_UNROLL;
           Cand cu[U];
           float2 c[U];
@@ -325,7 +330,7 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
           // phase 1: look up, load, move each pixel to its bank-spreading lane
 #pragma unroll
           for (int u = 0; u < U; ++u) {
-            cand_prep(es, g, c0 + u * EB_THREADS + lane, ncand, lo, bg.S, cu[u]);
+            cand_prep(es, g, c0 + u * BTHREADS + lane, ncand, lo, bg.S, cu[u]);
             c[u] = make_float2(0.f, 0.f);
             wimg[u] = 0.f;
             float f[3] = {0.f, 0.f, 0.f};
@@ -380,7 +385,7 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
       const float winv = wscale > 0.f ? 1.0f / wscale : 0.f;
 #pragma unroll
       for (int i = 0; i < PER_LANE; ++i) {
-        const int pi = padded_index(tid + 256 * i);
+        const int pi = padded_index(tid + BTHREADS * i);
         const unsigned long long v = acc_t[pi];
         if (v != 0ull) {
           float re, im;
@@ -405,8 +410,8 @@ __global__ void __launch_bounds__(256) k_bwd_brick(const float2* __restrict__ Y,
   const int64_t slot0 = ((int64_t)vsel * bg.nwork + w) * TLOG;
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
-    part_c[slot0 + tid + 256 * i] = acc[i];
-    if constexpr (WEIGHTS) part_w[slot0 + tid + 256 * i] = accw[i];
+    part_c[slot0 + tid + BTHREADS * i] = acc[i];
+    if constexpr (WEIGHTS) part_w[slot0 + tid + BTHREADS * i] = accw[i];
   }
 }
 
@@ -584,7 +589,7 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
   if (bw.bg.nwork > 0) {
     const dim3 grid(bw.bg.nwork, g.Bv);
 #define TP_BWD(NT_, W_, G_)                                                                                    \
-  hipLaunchKernelGGL((k_bwd_brick<NT_, W_, G_>), grid, blk, 0, st, Y, Wimg, volc, rot, shifts, grad_rot, grad_s, \
+  hipLaunchKernelGGL((k_bwd_brick<NT_, W_, G_>), grid, dim3(BTHREADS), 0, st, Y, Wimg, volc, rot, shifts, grad_rot, grad_s, \
                      part_c, part_w, g, bw, prefix, ymax, wmax)
     if (interp == 1) {
       if (grad) TP_BWD(4, false, true); else if (weights) TP_BWD(4, true, false); else TP_BWD(4, false, false);
