@@ -428,9 +428,12 @@ __global__ void __launch_bounds__(256) k_bwd_fold(float2* __restrict__ vol, floa
                                                   KGeom g, BwdGrid bw, const int* __restrict__ prefix) {
   const BrickGrid& bg = bw.bg;
   constexpr int HL = NT == 4 ? 1 : 0;
+  constexpr int SB = 17 - NT;   // brick edge (bg.S)
   const int nvol = g.D * g.D * g.W;
   const int vsel = blockIdx.y;
-  const int tlo = bg.origin - HL, thi = bg.origin + (bg.nb - 1) * bg.S - HL + TE - 1;   // covered taps
+  const int tlo = bg.origin - HL, thi = bg.origin + (bg.nb - 1) * SB - HL + TE - 1;   // covered taps
+  const float2* pc = part_c + (int64_t)vsel * bg.nwork * TLOG;
+  const float* pw = WEIGHTS ? part_w + (int64_t)vsel * bg.nwork * TLOG : nullptr;
   for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < nvol; v += gridDim.x * blockDim.x) {
     const int xy = v % (g.W * g.D), z = v / (g.W * g.D);
     const int x = xy % g.W, y = xy / g.W;
@@ -442,26 +445,41 @@ __global__ void __launch_bounds__(256) k_bwd_fold(float2* __restrict__ vol, floa
       float2 part = make_float2(0.f, 0.f);
       float partw = 0.f;
       for (int tz = sz + g.D * floor_div(tlo - sz + g.D - 1, g.D); tz <= thi; tz += g.D) {
-        const int iz0 = max(0, floor_div(tz - bg.origin + HL - TE, bg.S) + 1), iz1 = min(bg.nb - 1, floor_div(tz - bg.origin + HL, bg.S));
+        const int iz0 = max(0, floor_div(tz - bg.origin + HL - TE, SB) + 1), iz1 = min(bg.nb - 1, floor_div(tz - bg.origin + HL, SB));
         for (int ty = sy + g.D * floor_div(tlo - sy + g.D - 1, g.D); ty <= thi; ty += g.D) {
-          const int iy0 = max(0, floor_div(ty - bg.origin + HL - TE, bg.S) + 1), iy1 = min(bg.nb - 1, floor_div(ty - bg.origin + HL, bg.S));
+          const int iy0 = max(0, floor_div(ty - bg.origin + HL - TE, SB) + 1), iy1 = min(bg.nb - 1, floor_div(ty - bg.origin + HL, SB));
           for (int tx = sx + g.D * floor_div(tlo - sx + g.D - 1, g.D); tx <= thi; tx += g.D) {
-            const int ix0 = max(0, floor_div(tx - bg.origin + HL - TE, bg.S) + 1), ix1 = min(bg.nb - 1, floor_div(tx - bg.origin + HL, bg.S));
+            const int ix0 = max(0, floor_div(tx - bg.origin + HL - TE, SB) + 1), ix1 = min(bg.nb - 1, floor_div(tx - bg.origin + HL, SB));
             for (int iz = iz0; iz <= iz1; ++iz)
               for (int iy = iy0; iy <= iy1; ++iy)
                 for (int ix = ix0; ix <= ix1; ++ix) {
                   const int bb = (iz * bg.nb + iy) * bg.nb + ix;
                   const int k0 = prefix[bb], k1 = prefix[bb + 1];
-                  if (k0 == k1) continue;
-                  const int lx = tx - (bg.origin + ix * bg.S - HL), ly = ty - (bg.origin + iy * bg.S - HL),
-                            lz = tz - (bg.origin + iz * bg.S - HL);
+                  const int lx = tx - (bg.origin + ix * SB - HL), ly = ty - (bg.origin + iy * SB - HL),
+                            lz = tz - (bg.origin + iz * SB - HL);
                   const int64_t li = (int64_t)lz * 256 + ly * 16 + lx;
-                  for (int c = k0; c < k1; ++c) {
-                    const int64_t o = ((int64_t)vsel * bg.nwork + c) * TLOG + li;
-                    const float2 t = part_c[o];
+                  // four chunks at a time, so that several loads are in flight
+                  int c = k0;
+                  for (; c + 4 <= k1; c += 4) {
+                    float2 t[4];
+                    float tw[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                      t[j] = pc[(int64_t)(c + j) * TLOG + li];
+                      if constexpr (WEIGHTS) tw[j] = pw[(int64_t)(c + j) * TLOG + li];
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                      part.x += t[j].x;
+                      part.y += t[j].y;
+                      if constexpr (WEIGHTS) partw += tw[j];
+                    }
+                  }
+                  for (; c < k1; ++c) {
+                    const float2 t = pc[(int64_t)c * TLOG + li];
                     part.x += t.x;
                     part.y += t.y;
-                    if constexpr (WEIGHTS) partw += part_w[o];
+                    if constexpr (WEIGHTS) partw += pw[(int64_t)c * TLOG + li];
                   }
                 }
           }

@@ -152,7 +152,9 @@ tproj::EvPair kt_copy(int cls) {
   return t.ev;
 }
 
-GatherPlan gather_plan(const tp_geom* g) {
+// items: work items aimed at (the pixel load split evenly); min_px: least
+// pixels per item, so that small problems do not drown in per-item costs.
+GatherPlan gather_plan(const tp_geom* g, int64_t items = 4096, int64_t min_px = 2048) {
   GatherPlan pl;
   if (force_direct()) return pl;
   // the brick enumeration packs kx <= H/2 into 11 bits and one image row's
@@ -174,7 +176,7 @@ GatherPlan gather_plan(const tp_geom* g) {
   bg.list_len = (g->Bv == 1 ? g->B : 1) * g->P;
   bg.dens_q8 = std::max(1, (int)std::lround(256.0 / ((double)g->oversampling * g->oversampling)));
   const int64_t total = (int64_t)g->B * g->P * pixels_in_mask(g);
-  bg.target = std::max<int64_t>(512, total / 4096);
+  bg.target = std::max<int64_t>(min_px, total / items);
   int64_t nwork = 0;
   for (int b = 0; b < bg.nb3; ++b) {
     int bi, bj, bk;
@@ -198,7 +200,9 @@ struct BwdPlan {
 
 BwdPlan bwd_plan(const tp_geom* g, bool weights) {
   BwdPlan pl;
-  const GatherPlan gp = gather_plan(g);
+  // each work item writes a 16^3 partial tile that the fold reads back: fewer,
+  // larger items than the gather
+  const GatherPlan gp = gather_plan(g, 4096, 8192);
   if (!gp.ok) return pl;
   tproj::BwdGrid& bw = pl.bw;
   bw.bg = gp.bg;
