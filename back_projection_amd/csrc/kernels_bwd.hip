@@ -45,7 +45,7 @@ constexpr int TLOG = TE * TE * TE;         // 4096 logical entries
 #endif
 constexpr int BNW = BWD_NW;                 // wavefronts per workgroup of the brick kernel
 constexpr int BTHREADS = BNW * 64;
-constexpr int PER_LANE = TLOG / BTHREADS;   // partial-tile entries per thread
+constexpr int PER_LANE = (TLOG + BTHREADS - 1) / BTHREADS;   // partial-tile entries per thread
 constexpr int WINDOW = 16;                 // poses per fixed-point window
 constexpr float FIX_RANGE = 0.9f * 2147483648.0f;
 constexpr int MAX_BANDS = 128;
@@ -175,6 +175,9 @@ __global__ void __launch_bounds__(256) k_band_max(const float2* __restrict__ Y, 
 #ifndef BWD_UNROLL
 #define BWD_UNROLL 2
 #endif
+#ifndef BWD_MIN_WAVES
+#define BWD_MIN_WAVES 1
+#endif
 
 // One pixel of the back-projection, in the lane the bank-spreading permutation
 // gave it: pk packs (active, l) with l = floor(p) - lo; f holds the fractional
@@ -228,7 +231,7 @@ __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz
 }
 
 template <int NT, bool WEIGHTS, bool GRAD>
-__global__ void __launch_bounds__(BTHREADS) k_bwd_brick(const float2* __restrict__ Y, const float* __restrict__ Wimg,
+__global__ void __launch_bounds__(BTHREADS, BWD_MIN_WAVES) k_bwd_brick(const float2* __restrict__ Y, const float* __restrict__ Wimg,
                                                    const float2* __restrict__ vol, const float* __restrict__ rot,
                                                    const float* __restrict__ shifts, float* __restrict__ grad_rot,
                                                    float* __restrict__ grad_s, float2* __restrict__ part_c,
@@ -385,6 +388,7 @@ __global__ void __launch_bounds__(BTHREADS) k_bwd_brick(const float2* __restrict
       const float winv = wscale > 0.f ? 1.0f / wscale : 0.f;
 #pragma unroll
       for (int i = 0; i < PER_LANE; ++i) {
+        if (TLOG % BTHREADS != 0 && tid + BTHREADS * i >= TLOG) break;
         const int pi = padded_index(tid + BTHREADS * i);
         const unsigned long long v = acc_t[pi];
         if (v != 0ull) {
@@ -410,6 +414,7 @@ __global__ void __launch_bounds__(BTHREADS) k_bwd_brick(const float2* __restrict
   const int64_t slot0 = ((int64_t)vsel * bg.nwork + w) * TLOG;
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
+    if (TLOG % BTHREADS != 0 && tid + BTHREADS * i >= TLOG) break;
     part_c[slot0 + tid + BTHREADS * i] = acc[i];
     if constexpr (WEIGHTS) part_w[slot0 + tid + BTHREADS * i] = accw[i];
   }

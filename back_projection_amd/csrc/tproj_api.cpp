@@ -212,6 +212,10 @@ BwdPlan bwd_plan(const tp_geom* g, bool weights) {
   bw.nbands = (int)std::ceil(kimg / band) + 1;
   bw.inv_band_w = (float)(1.0 / band);
   pl.ws_bytes = tproj::bwd_ws_bytes(bw, g->Bv, weights);
+  // every active brick writes at least one partial tile: very large boxes
+  // with few poses would need more scratch than they are worth; those use the
+  // direct kernels
+  if (pl.ws_bytes > ((size_t)4 << 30)) return BwdPlan{};
   pl.ok = true;
   return pl;
 }

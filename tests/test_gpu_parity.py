@@ -31,6 +31,9 @@ SMALL = [
     ("linear-oversampled", 12, 12, 3, 2, 2, 2, 0, 0, 2.5, -1.0, True, "rot"),
     ("cubic-general-map", 32, 32, 6, 1, 1, 1, 1, 1, 1.0, 16.0, False, "wild"),
     ("cubic-H-neq-D", 18, 30, 9, 1, 1, 1, 1, 1, 1.0, 14.0, True, "rot"),
+    ("cubic-oversampled-cut", 14, 16, 4, 1, 1, 1, 1, 1, 2.0, 7.0, True, "rot"),
+    ("linear-bcast-shifts", 16, 18, 5, 2, 2, 2, 1, 0, 1.0, -1.0, False, "rot"),
+    ("cubic-tiny-D", 8, 8, 6, 1, 1, 1, 1, 1, 1.0, -1.0, False, "rot"),
 ]
 
 
@@ -245,3 +248,48 @@ def test_workload4_full_sampled():
     drest, wrest = bp.backproject_2d_to_3d(ti_all - ti, tr, tw_all - tw, None, D=D, interp="cubic")
     assert rel(dvol + drest, dall) <= BWD_TOL
     assert rel(wvol + wrest, wall) <= BWD_TOL
+
+
+def test_direct_path_large_image():
+    """H = 4096 is past the brick enumeration's limits: the direct kernels run.
+    (o = 1/4 keeps |p| <= 50 inside a few periods of the D = 64 box, where fp32
+    sample coordinates hold the forward tolerance.)"""
+    D, H, r, o = 64, 4096, 200.0, 0.25
+    rng = np.random.default_rng(41)
+    vol = workloads.random_complex(rng, (1, D, D, D // 2 + 1))
+    rot = workloads.random_rotations(rng, 2).reshape(1, 2, 3, 3)
+    sh = rng.uniform(-3, 3, (1, 2, 2)).astype(np.float32)
+    g = workloads.random_complex(rng, (1, 2, H, H // 2 + 1))
+    tv, tr, ts, tg = dev(vol, rot, sh, g)
+    log("[parity] direct path, H=4096")
+    out = bp.project_3d_to_2d(tv, tr, ts, H=H, radius_cutoff=r, oversampling=o)
+    assert rel(out, oracle.project(vol, rot, sh, H=H, interp=1, r=r, o=o)) <= FWD_TOL
+    gv, gr, gs = bp.project_3d_to_2d_backward(tg, tv, tr, ts, radius_cutoff=r, oversampling=o)
+    rgv, rgr, rgs = oracle.project_backward(g, vol, rot, sh, interp=1, r=r, o=o)
+    assert rel(gv, rgv) <= BWD_TOL and rel(gr, rgr) <= BWD_TOL and rel(gs, rgs) <= BWD_TOL
+
+
+def test_large_volume_sampled():
+    """D = 384 (cubic, cutoff D/2, shifts): sampled poses against the oracle and
+    the adjoint identity for the volume gradient over the whole launch."""
+    D, H, P, r = 384, 384, 40, 192.0
+    rng = np.random.default_rng(43)
+    vol = workloads.random_complex(rng, (1, D, D, D // 2 + 1))
+    rot = workloads.random_rotations(rng, P).reshape(1, P, 3, 3)
+    sh = rng.uniform(-6, 6, (1, P, 2)).astype(np.float32)
+    idx = np.sort(rng.choice(P, 3, replace=False))
+    log(f"[parity] large volume D={D}, P={P}, sampled poses {idx.tolist()}")
+    tv, tr, ts = dev(vol, rot, sh)
+    out = bp.project_3d_to_2d(tv, tr, ts, radius_cutoff=r)
+    ref = oracle.project(vol, rot[:, idx], sh[:, idx], interp=1, r=r)
+    assert rel(out[:, idx], ref) <= FWD_TOL, rel(out[:, idx], ref)
+    g = workloads.random_complex(rng, (1, P, H, H // 2 + 1))
+    tg, = dev(g)
+    gv, gr, gs = bp.project_3d_to_2d_backward(tg, tv, tr, ts, radius_cutoff=r)
+    _, rgr, rgs = oracle.project_backward(g[:, idx], vol, rot[:, idx], sh[:, idx], interp=1, r=r,
+                                          need_vol=False)
+    assert rel(gr[:, idx], rgr) <= BWD_TOL, rel(gr[:, idx], rgr)
+    assert rel(gs[:, idx], rgs) <= BWD_TOL, rel(gs[:, idx], rgs)
+    lhs = np.real(np.vdot(host(out).astype(np.complex128).ravel(), g.astype(np.complex128).ravel()))
+    rhs = np.real(np.vdot(vol.astype(np.complex128).ravel(), host(gv).astype(np.complex128).ravel()))
+    assert abs(lhs - rhs) <= 1e-5 * np.linalg.norm(host(out)) * np.linalg.norm(g), (lhs, rhs)
