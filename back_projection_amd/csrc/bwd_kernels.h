@@ -16,6 +16,8 @@ struct BwdGrid {
   float inv_band_w;   // 1 / band width (pixels)
 };
 
+// Brick edge S of the back-projection bricks for an interpolation kind.
+int bwd_brick_edge(int interp);
 // Workspace bytes: work list, band maxima, one partial tile per work item.
 size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights);
 

@@ -211,12 +211,11 @@ __device__ __forceinline__ void stage_tile_t(T* tile, const T* __restrict__ V, c
 // Value (and, with DERIV, the partial derivatives along x, y, z) of the
 // interpolant from the tile, for the axis weights w* (and their derivatives
 // d*) of the sample; l = floor(p) - lo.
-template <int NT, bool DERIV, typename T>
+template <int NT, bool DERIV, typename T, int SY = Tile<NT>::SY, int SZ = Tile<NT>::SZ>
 __device__ __forceinline__ void interp_tile_w(const T* tile, const int l[3], const float wx[NT], const float wy[NT],
                                               const float wz[NT], const float dx[NT], const float dy[NT],
                                               const float dz[NT], T& I, T* dI) {
-  using Tl = Tile<NT>;
-  const T* base = tile + l[2] * Tl::SZ + l[1] * Tl::SY + l[0];
+  const T* base = tile + l[2] * SZ + l[1] * SY + l[0];
   T z0 = zero_of(T{});
   I = z0;
   if constexpr (DERIV) { dI[0] = z0; dI[1] = z0; dI[2] = z0; }
@@ -226,7 +225,7 @@ __device__ __forceinline__ void interp_tile_w(const T* tile, const int l[3], con
     T s = z0, sx = z0, sy = z0;   // plane sums: wy*r, wy*rx, dy*r
 #pragma unroll
     for (int b = 0; b < NT; ++b) {
-      const T* row = base + c * Tl::SZ + b * Tl::SY;
+      const T* row = base + c * SZ + b * SY;
       T r = z0, rx = z0;
 #pragma unroll
       for (int a = 0; a < NT; ++a) {

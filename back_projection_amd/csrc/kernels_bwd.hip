@@ -35,11 +35,19 @@ namespace tproj {
 
 namespace {
 
-constexpr int TE = 16;                     // tile edge
-constexpr int TSY = 17;                    // padded strides (as the gather tile)
-constexpr int TSZ = 16 * 17 + 4;
-constexpr int TSIZE = TE * TSZ;            // 4416 padded entries
-constexpr int TLOG = TE * TE * TE;         // 4096 logical entries
+#ifndef BWD_EDGE
+#define BWD_EDGE 16
+#endif
+// Tile edge of the back-projection bricks: brick edge S = TE - NT + 1 plus the
+// interpolation halo.  16^3 tiles use padded strides like the gather tile;
+// 14^3 tiles (unpadded, S = 11 cubic) fit three fused workgroups per CU in
+// LDS but measured slower (more hits per pixel, and the register budget of
+// three waves per SIMD spills).
+constexpr int TE = BWD_EDGE;
+constexpr int TSY = TE == 16 ? 17 : TE;
+constexpr int TSZ = TE == 16 ? 16 * 17 + 4 : TE * TE;
+constexpr int TSIZE = TE * TSZ;            // padded entries
+constexpr int TLOG = TE * TE * TE;         // logical entries
 #ifndef BWD_NW
 #define BWD_NW 4
 #endif
@@ -61,11 +69,16 @@ __device__ __forceinline__ int fixed_round(float w, float u) {
 }
 
 // One 64-bit word holding re + im * 2^32 (re signed): sums of such words keep
-// both parts exact as long as each partial sum stays within 31 bits.
-__device__ __forceinline__ unsigned long long pack_fixed(int re, int im) {
-  const unsigned int lo = (unsigned int)re;
-  const unsigned int hi = (unsigned int)(im + (re >> 31));
-  return ((unsigned long long)hi << 32) | lo;
+// both parts exact as long as each partial sum stays within 31 bits.  The two
+// magic-number results side by side are (0x4B400000 + re) + 2^32 (0x4B400000
+// + im); one 64-bit subtraction of the two offsets leaves re + 2^32 im in
+// two's complement (the borrow of a negative re lands in the high word).
+constexpr unsigned long long MAGIC_PAIR = 0x4B4000004B400000ull;
+
+__device__ __forceinline__ unsigned long long fixed_pair(float w, float ur, float ui) {
+  const unsigned long long lo = __float_as_uint(fmaf(w, ur, MAGIC));
+  const unsigned long long hi = __float_as_uint(fmaf(w, ui, MAGIC));
+  return ((hi << 32) | lo) - MAGIC_PAIR;
 }
 
 __device__ __forceinline__ void unpack_fixed(unsigned long long w, float& re, float& im) {
@@ -76,7 +89,9 @@ __device__ __forceinline__ void unpack_fixed(unsigned long long w, float& re, fl
   im = (float)i;
 }
 
-__device__ __forceinline__ int padded_index(int idx) { return (idx >> 8) * TSZ + ((idx >> 4) & 15) * TSY + (idx & 15); }
+__device__ __forceinline__ int padded_index(int idx) {
+  return (idx / (TE * TE)) * TSZ + ((idx / TE) % TE) * TSY + idx % TE;
+}
 
 // Bound on the pixels of one pose that can reach one voxel: the voxel's
 // support box (edge NT) cuts the slice in a disc of radius NT*sqrt(3)/2 in
@@ -200,7 +215,7 @@ __device__ __forceinline__ void bwd_gather(int pk, float fx, float fy, float fz,
   axis_dweights<NT>(fx, dx);
   axis_dweights<NT>(fy, dy);
   axis_dweights<NT>(fz, dz);
-  interp_tile_w<NT, true>(vt, l, wx, wy, wz, dx, dy, dz, I, dI);
+  interp_tile_w<NT, true, float2, TSY, TSZ>(vt, l, wx, wy, wz, dx, dy, dz, I, dI);
 }
 
 template <int NT, bool WEIGHTS>
@@ -224,7 +239,7 @@ __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz
       const int rowb = (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
 #pragma unroll
       for (int ja = 0; ja < NT; ++ja) {
-        atomicAdd(&acc_t[rowb + ja], pack_fixed(fixed_round(wx[ja], ur), fixed_round(wx[ja], ui)));
+        atomicAdd(&acc_t[rowb + ja], fixed_pair(wx[ja], ur, ui));
         if constexpr (WEIGHTS) atomicAdd(&acc_w[rowb + ja], (unsigned int)fixed_round(wx[ja], uw));
       }
     }
@@ -273,7 +288,7 @@ __global__ void __launch_bounds__(BTHREADS, BWD_MIN_WAVES) k_bwd_brick(const flo
     using Tl = Tile<NT>;
     const float2* V = vol + (int64_t)vsel * nvol;
     for (int i = tid; i < TLOG; i += BTHREADS) {
-      const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
+      const int x = i % TE, y = (i / TE) % TE, z = i / (TE * TE);
       vt[z * TSZ + y * TSY + x] = tap_value(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
     }
     for (int i = tid; i < WINDOW * 8; i += BTHREADS) (&gw[0][0])[i] = 0.f;
@@ -433,7 +448,7 @@ __global__ void __launch_bounds__(256) k_bwd_fold(float2* __restrict__ vol, floa
                                                   KGeom g, BwdGrid bw, const int* __restrict__ prefix) {
   const BrickGrid& bg = bw.bg;
   constexpr int HL = NT == 4 ? 1 : 0;
-  constexpr int SB = 17 - NT;   // brick edge (bg.S)
+  constexpr int SB = TE - NT + 1;   // brick edge (bg.S)
   const int nvol = g.D * g.D * g.W;
   const int vsel = blockIdx.y;
   const int tlo = bg.origin - HL, thi = bg.origin + (bg.nb - 1) * SB - HL + TE - 1;   // covered taps
@@ -462,7 +477,7 @@ __global__ void __launch_bounds__(256) k_bwd_fold(float2* __restrict__ vol, floa
                   const int k0 = prefix[bb], k1 = prefix[bb + 1];
                   const int lx = tx - (bg.origin + ix * SB - HL), ly = ty - (bg.origin + iy * SB - HL),
                             lz = tz - (bg.origin + iz * SB - HL);
-                  const int64_t li = (int64_t)lz * 256 + ly * 16 + lx;
+                  const int64_t li = (int64_t)lz * (TE * TE) + ly * TE + lx;
                   // four chunks at a time, so that several loads are in flight
                   int c = k0;
                   for (; c + 4 <= k1; c += 4) {
@@ -580,6 +595,8 @@ __global__ void __launch_bounds__(256) k_bwd_edge(const float2* __restrict__ Y, 
 // launcher
 // ---------------------------------------------------------------------------
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+int bwd_brick_edge(int interp) { return TE - (interp == 1 ? 4 : 2) + 1; }
 
 size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights) {
   const size_t prefix = align256((size_t)(bw.bg.nb3 + 1) * sizeof(int));

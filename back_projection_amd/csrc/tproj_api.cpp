@@ -154,7 +154,7 @@ tproj::EvPair kt_copy(int cls) {
 
 // items: work items aimed at (the pixel load split evenly); min_px: least
 // pixels per item, so that small problems do not drown in per-item costs.
-GatherPlan gather_plan(const tp_geom* g, int64_t items = 4096, int64_t min_px = 2048) {
+GatherPlan gather_plan(const tp_geom* g, int64_t items = 4096, int64_t min_px = 2048, int S = 0) {
   GatherPlan pl;
   if (force_direct()) return pl;
   // the brick enumeration packs kx <= H/2 into 11 bits and one image row's
@@ -162,7 +162,7 @@ GatherPlan gather_plan(const tp_geom* g, int64_t items = 4096, int64_t min_px = 
   if (g->H / 2 > 2047) return pl;
   tproj::BrickGrid& bg = pl.bg;
   const int NT = g->interp == TP_CUBIC ? 4 : 2;
-  bg.S = 17 - NT;
+  bg.S = S > 0 ? S : 17 - NT;
   double kmax = std::sqrt(2.0) * (g->H / 2);
   if (g->radius_cutoff >= 0.0f) kmax = std::min(kmax, (double)g->radius_cutoff);
   const double pmax = (double)g->oversampling * kmax;
@@ -202,7 +202,7 @@ BwdPlan bwd_plan(const tp_geom* g, bool weights) {
   BwdPlan pl;
   // each work item writes a 16^3 partial tile that the fold reads back: fewer,
   // larger items than the gather
-  const GatherPlan gp = gather_plan(g, 4096, 8192);
+  const GatherPlan gp = gather_plan(g, 4096, 8192, tproj::bwd_brick_edge(g->interp));
   if (!gp.ok) return pl;
   tproj::BwdGrid& bw = pl.bw;
   bw.bg = gp.bg;
