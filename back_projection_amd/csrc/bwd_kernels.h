@@ -22,12 +22,9 @@ int bwd_brick_edge(int interp);
 size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights);
 
 // Writes vol (and wvol when Wimg != NULL) completely with the adjoint of the
-// forward.  With volc != NULL the rotation / shift gradients of the forward
-// are accumulated into grad_rot / grad_s (zeroed by the caller; either may be
-// NULL) in the same pass; volc is the forward's volume.
+// forward (the back-projection of Y, and of the weight images Wimg).
 hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* workspace, const float2* Y,
-                      const float* Wimg, const float2* volc, const float* rot, const float* shifts, float2* vol,
-                      float* wvol, float* grad_rot, float* grad_s, hipStream_t st, const EvPair* ev_brick = nullptr,
-                      const EvPair* ev_fold = nullptr);
+                      const float* Wimg, const float* rot, const float* shifts, float2* vol, float* wvol,
+                      hipStream_t st, const EvPair* ev_brick = nullptr, const EvPair* ev_fold = nullptr);
 
 }  // namespace tproj

@@ -423,13 +423,6 @@ __device__ __forceinline__ bool slice_rows_box(const KGeom& g, const float* R, c
   return sr.ky_lo <= sr.ky_hi;
 }
 
-__device__ __forceinline__ bool slice_rows_setup(const KGeom& g, const float* R, const int lo[3], int S,
-                                                 SliceRows& sr) {
-  const float bl[3] = {(float)lo[0], (float)lo[1], (float)lo[2]};
-  const float bh[3] = {(float)(lo[0] + S), (float)(lo[1] + S), (float)(lo[2] + S)};
-  return slice_rows_box(g, R, bl, bh, sr);
-}
-
 // One lane per row ky = r0 + lane: kx interval, count, inclusive scan.
 struct RowBatch {
   int kx0;     // first candidate kx of this lane's row

@@ -4,17 +4,14 @@
 // k_fwd_brick      3D->2D forward (complex volume, with the shift phase) or
 //                  its real counterpart (weight channel): a workgroup stages
 //                  one tap-space brick of the Hermitian-extended periodic
-//                  volume plus the interpolation halo in LDS; for blocks of
-//                  256 poses it tests one pose per lane against the brick,
-//                  and each wavefront then walks the hit poses, enumerating
-//                  (row by row, from the slab inequalities of the rotated
-//                  slice) the pixels whose floor(p) falls in the brick and
-//                  interpolating them from LDS.
+//                  volume plus the interpolation halo in LDS, enumerates the
+//                  pixels of its pose chunk whose floor(p) falls in the brick
+//                  (enum_block.h) and interpolates them from LDS, each pixel
+//                  in the lane the bank-spreading order gives it.
 // k_grad_brick     rotation / shift gradients on the same decomposition: the
 //                  value and the three partial derivatives of the
-//                  interpolant come from the LDS tile; each wavefront reduces
-//                  its pixels of a pose to 8 sums and adds them to the pose's
-//                  gradient with global atomics.
+//                  interpolant come from the LDS tile; segmented wavefront
+//                  sums per pose, then one global atomic per pose and term.
 // *_edge           masked pixels and the rare samples outside every active
 //                  brick (maps that are not rotations), from global memory.
 //
@@ -243,53 +240,69 @@ __global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ v
       for (int qb = 0; qb < nrows;) {
         int nr;
         const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh, nr);
-        // software pipeline: the next batch's candidate and upstream values are
-        // fetched while this batch is processed
-        Cand nx;
-        cand_prep(es, g, wave * 64 + lane, ncand, lo, bg.S, nx);
-        float2 unx = (CPLX && nx.act) ? U[nx.k] : make_float2(0.f, 0.f);
-        float urnx = (REAL && nx.act) ? Ur[nx.k] : 0.f;
-        for (int c0 = wave * 64; c0 < ncand; c0 += GRAD_NW * 64) {   // wave-uniform: the sums need every lane
-          const Cand cu = nx;
-          const float2 ucu = unx;
-          const float urcu = urnx;
-          if (c0 + GRAD_NW * 64 < ncand) {
-            cand_prep(es, g, c0 + GRAD_NW * 64 + lane, ncand, lo, bg.S, nx);
-            if constexpr (CPLX) unx = nx.act ? U[nx.k] : make_float2(0.f, 0.f);
-            if constexpr (REAL) urnx = nx.act ? Ur[nx.k] : 0.f;
+        for (int c0 = wave * 64; c0 < ncand; c0 += GRAD_NW * 64) {   // wave-uniform: permutes, sums
+          Cand cu;
+          cand_prep(es, g, c0 + lane, ncand, lo, bg.S, cu);
+          float2 uc = make_float2(0.f, 0.f);
+          float ur = 0.f, f[3] = {0.f, 0.f, 0.f};
+          int pk = 0, key = -1;
+          if (cu.act) {
+            if constexpr (CPLX) uc = U[cu.k];
+            if constexpr (REAL) ur = Ur[cu.k];
+#pragma unroll
+            for (int a = 0; a < 3; ++a) f[a] = cu.p[a] - floorf(cu.p[a]);
+            pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
+            key = (cu.l[0] + cu.l[1] * Tl::SY + cu.l[2] * Tl::SZ) & 15;
+          }
+          // the interpolation runs in the lane the bank-spreading order gives
+          // the pixel; value and derivatives come back to the pixel's lane
+          const int dest = spread_dest(key);
+          const int mpk = lane_send(pk, dest);
+          float mf[3];
+#pragma unroll
+          for (int a = 0; a < 3; ++a) mf[a] = lane_send(f[a], dest);
+          float2 Ic = make_float2(0.f, 0.f), dIc[3] = {Ic, Ic, Ic};
+          float Ir = 0.f, dIr[3] = {0.f, 0.f, 0.f};
+          if (mpk & 1) {
+            const int ml[3] = {(mpk >> 1) & 15, (mpk >> 5) & 15, (mpk >> 9) & 15};
+            float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
+            axis_weights<NT>(mf[0], wx);
+            axis_weights<NT>(mf[1], wy);
+            axis_weights<NT>(mf[2], wz);
+            axis_dweights<NT>(mf[0], dx);
+            axis_dweights<NT>(mf[1], dy);
+            axis_dweights<NT>(mf[2], dz);
+            if constexpr (CPLX) interp_tile_w<NT, true>(tc, ml, wx, wy, wz, dx, dy, dz, Ic, dIc);
+            if constexpr (REAL) interp_tile_w<NT, true>(tr, ml, wx, wy, wz, dx, dy, dz, Ir, dIr);
           }
           float acc[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-          const int key = cu.key;
-          if (cu.act) {
-            const float fkx = cu.kx, fky = cu.ky;
-            float e3[3] = {0.f, 0.f, 0.f};
-            if constexpr (CPLX) {
-              float2 I, dI[3];
-              interp_tile_t<NT, true>(tc, cu.p, cu.l, I, dI);
-              float2 phi = make_float2(1.f, 0.f);
-              if (shifts) phi = shift_phase(fkx, fky, cu.sx, cu.sy, g.inv_h);
-              const float2 cc = cmulc(ucu, phi);   // conj(U) * phi
+          float e3[3] = {0.f, 0.f, 0.f};
+          const float fkx = cu.act ? cu.kx : 0.f, fky = cu.act ? cu.ky : 0.f;
+          if constexpr (CPLX) {
+            Ic = lane_fetch(Ic, dest);
 #pragma unroll
-              for (int a = 0; a < 3; ++a) e3[a] = cc.x * dI[a].x - cc.y * dI[a].y;
-              const float im = cc.x * I.y + cc.y * I.x;
-              acc[6] = fkx * im;
-              acc[7] = fky * im;
-            }
-            if constexpr (REAL) {
-              float I, dI[3];
-              interp_tile_t<NT, true>(tr, cu.p, cu.l, I, dI);
+            for (int a = 0; a < 3; ++a) dIc[a] = lane_fetch(dIc[a], dest);
+            float2 phi = make_float2(1.f, 0.f);
+            if (shifts && cu.act) phi = shift_phase(fkx, fky, cu.sx, cu.sy, g.inv_h);
+            const float2 cc = cmulc(uc, phi);   // conj(U) * phi
 #pragma unroll
-              for (int a = 0; a < 3; ++a) e3[a] = fmaf(urcu, dI[a], e3[a]);
-            }
-#pragma unroll
-            for (int a = 0; a < 3; ++a) {
-              acc[2 * a] = e3[a] * fkx;
-              acc[2 * a + 1] = e3[a] * fky;
-            }
+            for (int a = 0; a < 3; ++a) e3[a] = cc.x * dIc[a].x - cc.y * dIc[a].y;
+            const float im = cc.x * Ic.y + cc.y * Ic.x;
+            acc[6] = fkx * im;
+            acc[7] = fky * im;
           }
-          grad_collect(acc, key, gw);
+          if constexpr (REAL) {
+#pragma unroll
+            for (int a = 0; a < 3; ++a) e3[a] = fmaf(ur, lane_fetch(dIr[a], dest), e3[a]);
+          }
+#pragma unroll
+          for (int a = 0; a < 3; ++a) {
+            acc[2 * a] = e3[a] * fkx;
+            acc[2 * a + 1] = e3[a] * fky;
+          }
+          grad_collect(acc, cu.key, gw);
         }
         __syncthreads();
         qb += nr;

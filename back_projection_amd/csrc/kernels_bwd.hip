@@ -1,14 +1,12 @@
-// Backward / adjoint kernels of libtproj for gfx950: the 2D->3D
-// back-projection (with the weight channel) and the fused backward of the
-// 3D->2D forward (volume, rotation and shift gradients in one pass).
+// Back-projection kernels of libtproj for gfx950: the 2D->3D accumulation
+// (with the weight channel), which is also the volume gradient of the 3D->2D
+// forward.
 //
 // The back-projection is the exact adjoint of the rotated-central-slice
 // forward: every in-mask pixel adds w * conj(phi) * Y to each of its taps
 // (conjugated where the tap is a Friedel mate) and w * Wimg to the weight
 // volume (French page, "Resume technique" 2: accumulation with weights for CTF
-// correction; Dutch page, Methodologie: Friedel symmetry).  The rotation and
-// shift gradients follow from differentiating the forward (Spanish page,
-// "Resumen tecnico" 2: gradients for inputs, rotations and shifts).
+// correction; Dutch page, Methodologie: Friedel symmetry).
 //
 // Decomposition: the same tap-space bricks as the forward gather.  A pixel
 // belongs to the brick holding floor(p), so every pixel is visited once and all
@@ -21,9 +19,7 @@
 // one ds_add_u64 per tap).  Taps are accumulated in windows of up to 16 poses
 // whose scale is set, before the window, from per-image maxima in radial
 // bands of |k| and a bound on the contributions a voxel can receive; no sum
-// can overflow, and integer sums make the result deterministic.  With the
-// volume gradient, the same pass also interpolates the forward volume (second
-// LDS tile) for the rotation and shift gradients.
+// can overflow, and integer sums make the result deterministic.
 #include "brick_grid.h"
 #include "brick_kernels.h"
 #include "bwd_kernels.h"
@@ -184,8 +180,7 @@ __global__ void __launch_bounds__(256) k_band_max(const float2* __restrict__ Y, 
 }
 
 // ---------------------------------------------------------------------------
-// the brick kernel: scatter (SCAT, optional weight channel) and/or the
-// rotation / shift gradients of the forward (GRAD)
+// the brick kernel: the taps of every pixel the brick owns into its LDS tile
 // ---------------------------------------------------------------------------
 #ifndef BWD_UNROLL
 #define BWD_UNROLL 2
@@ -194,30 +189,10 @@ __global__ void __launch_bounds__(256) k_band_max(const float2* __restrict__ Y, 
 #define BWD_MIN_WAVES 1
 #endif
 
-// One pixel of the back-projection, in the lane the bank-spreading permutation
-// gave it: pk packs (active, l) with l = floor(p) - lo; f holds the fractional
-// parts of p.  The gather phase interpolates the forward volume's tile (value
-// and partial derivatives, for the rotation / shift gradients); the scatter
-// phase adds c = conj(phi) Y (and the weight image value) with the taps'
-// weights to the accumulator tiles.  Every LDS read of an iteration is issued
-// before its atomics: a read issued after them waits for them to drain.
-template <int NT>
-__device__ __forceinline__ void bwd_gather(int pk, float fx, float fy, float fz, const float2* vt, float2& I,
-                                           float2* dI) {
-  I = make_float2(0.f, 0.f);
-  dI[0] = dI[1] = dI[2] = I;
-  if (!(pk & 1)) return;
-  const int l[3] = {(pk >> 1) & 15, (pk >> 5) & 15, (pk >> 9) & 15};
-  float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
-  axis_weights<NT>(fx, wx);
-  axis_weights<NT>(fy, wy);
-  axis_weights<NT>(fz, wz);
-  axis_dweights<NT>(fx, dx);
-  axis_dweights<NT>(fy, dy);
-  axis_dweights<NT>(fz, dz);
-  interp_tile_w<NT, true, float2, TSY, TSZ>(vt, l, wx, wy, wz, dx, dy, dz, I, dI);
-}
-
+// One pixel, in the lane the bank-spreading permutation gave it: pk packs
+// (active, l) with l = floor(p) - lo; f holds the fractional parts of p.  Adds
+// c = conj(phi) Y (and the weight image value) with the taps' weights to the
+// accumulator tiles.
 template <int NT, bool WEIGHTS>
 __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz, float2 c, float wimg,
                                             unsigned long long* acc_t, unsigned int* acc_w, float scale,
@@ -245,21 +220,21 @@ __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz
     }
 }
 
-template <int NT, bool WEIGHTS, bool GRAD>
-__global__ void __launch_bounds__(BTHREADS, BWD_MIN_WAVES) k_bwd_brick(const float2* __restrict__ Y, const float* __restrict__ Wimg,
-                                                   const float2* __restrict__ vol, const float* __restrict__ rot,
-                                                   const float* __restrict__ shifts, float* __restrict__ grad_rot,
-                                                   float* __restrict__ grad_s, float2* __restrict__ part_c,
-                                                   float* __restrict__ part_w, KGeom g, BwdGrid bw,
-                                                   const int* __restrict__ prefix, const float* __restrict__ ymax,
-                                                   const float* __restrict__ wmax) {
+template <int NT, bool WEIGHTS>
+__global__ void __launch_bounds__(BTHREADS, BWD_MIN_WAVES) k_bwd_brick(const float2* __restrict__ Y,
+                                                                      const float* __restrict__ Wimg,
+                                                                      const float* __restrict__ rot,
+                                                                      const float* __restrict__ shifts,
+                                                                      float2* __restrict__ part_c,
+                                                                      float* __restrict__ part_w, KGeom g,
+                                                                      BwdGrid bw, const int* __restrict__ prefix,
+                                                                      const float* __restrict__ ymax,
+                                                                      const float* __restrict__ wmax) {
   const BrickGrid& bg = bw.bg;
   __shared__ unsigned long long acc_t[TSIZE];
   __shared__ unsigned int acc_w[WEIGHTS ? TSIZE : 1];
-  __shared__ float2 vt[GRAD ? TSIZE : 1];
   __shared__ EnumShared<WINDOW, BNW> es;
   __shared__ float hit_m[WINDOW], hit_w[WINDOW], hit_c[WINDOW];
-  __shared__ float gw[WINDOW][8];
 
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
@@ -271,7 +246,6 @@ __global__ void __launch_bounds__(BTHREADS, BWD_MIN_WAVES) k_bwd_brick(const flo
   const float bl[3] = {(float)lo[0], (float)lo[1], (float)lo[2]};
   const float bh[3] = {(float)(lo[0] + bg.S), (float)(lo[1] + bg.S), (float)(lo[2] + bg.S)};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t nvol = (int64_t)g.D * g.D * g.W;
 
   float2 acc[PER_LANE];
   float accw[PER_LANE];
@@ -283,15 +257,6 @@ __global__ void __launch_bounds__(BTHREADS, BWD_MIN_WAVES) k_bwd_brick(const flo
   for (int i = tid; i < TSIZE; i += BTHREADS) {
     acc_t[i] = 0ull;
     if constexpr (WEIGHTS) acc_w[i] = 0u;
-  }
-  if constexpr (GRAD) {
-    using Tl = Tile<NT>;
-    const float2* V = vol + (int64_t)vsel * nvol;
-    for (int i = tid; i < TLOG; i += BTHREADS) {
-      const int x = i % TE, y = (i / TE) % TE, z = i / (TE * TE);
-      vt[z * TSZ + y * TSY + x] = tap_value(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
-    }
-    for (int i = tid; i < WINDOW * 8; i += BTHREADS) (&gw[0][0])[i] = 0.f;
   }
   __syncthreads();
 
@@ -337,59 +302,37 @@ __global__ void __launch_bounds__(BTHREADS, BWD_MIN_WAVES) k_bwd_brick(const flo
       for (int qb = 0; qb < nrows;) {
         int nr;
         const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh, nr);
-        for (int c0 = wave * 64; c0 < ncand; c0 += BWD_UNROLL * BTHREADS) {   // wave-uniform (permutes, sums)
+        for (int c0 = wave * 64; c0 < ncand; c0 += BWD_UNROLL * BTHREADS) {   // wave-uniform (lane permutes)
           constexpr int U = BWD_UNROLL;
-          Cand cu[U];
-          float2 c[U];
           int dest[U], mpk[U];
-          float mf[U][3], wimg[U];
+          float mf[U][3];
           float2 mc[U];
           float mw[U];
-          // phase 1: look up, load, move each pixel to its bank-spreading lane
+          // look up, load, move each pixel to its bank-spreading lane ...
 #pragma unroll
           for (int u = 0; u < U; ++u) {
-            cand_prep(es, g, c0 + u * BTHREADS + lane, ncand, lo, bg.S, cu[u]);
-            c[u] = make_float2(0.f, 0.f);
-            wimg[u] = 0.f;
-            float f[3] = {0.f, 0.f, 0.f};
+            Cand cu;
+            cand_prep(es, g, c0 + u * BTHREADS + lane, ncand, lo, bg.S, cu);
+            float2 c = make_float2(0.f, 0.f);
+            float wimg = 0.f, f[3] = {0.f, 0.f, 0.f};
             int pk = 0, key = -1;
-            if (cu[u].act) {
-              c[u] = Y[cu[u].k];
-              if (shifts) c[u] = cmulc(shift_phase(cu[u].kx, cu[u].ky, cu[u].sx, cu[u].sy, g.inv_h), c[u]);
-              if constexpr (WEIGHTS) wimg[u] = Wimg[cu[u].k];
+            if (cu.act) {
+              c = Y[cu.k];
+              if (shifts) c = cmulc(shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h), c);   // conj(phi) * Y
+              if constexpr (WEIGHTS) wimg = Wimg[cu.k];
 #pragma unroll
-              for (int a = 0; a < 3; ++a) f[a] = cu[u].p[a] - floorf(cu[u].p[a]);
-              pk = 1 | (cu[u].l[0] << 1) | (cu[u].l[1] << 5) | (cu[u].l[2] << 9);
-              key = (cu[u].l[0] + cu[u].l[1] * TSY + cu[u].l[2] * TSZ) & 15;
+              for (int a = 0; a < 3; ++a) f[a] = cu.p[a] - floorf(cu.p[a]);
+              pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
+              key = (cu.l[0] + cu.l[1] * TSY + cu.l[2] * TSZ) & 15;
             }
             dest[u] = spread_dest(key);
             mpk[u] = lane_send(pk, dest[u]);
 #pragma unroll
             for (int a = 0; a < 3; ++a) mf[u][a] = lane_send(f[a], dest[u]);
-            mc[u] = make_float2(lane_send(c[u].x, dest[u]), lane_send(c[u].y, dest[u]));
-            mw[u] = WEIGHTS ? lane_send(wimg[u], dest[u]) : 0.f;
+            mc[u] = make_float2(lane_send(c.x, dest[u]), lane_send(c.y, dest[u]));
+            mw[u] = WEIGHTS ? lane_send(wimg, dest[u]) : 0.f;
           }
-          // phase 2 (gradients): gather, back to the pixel's own lane, per-pose sums;
-          // d/dR and d/ds of Re<G, phi I(V)> with conj(G) phi = conj(c)
-          if constexpr (GRAD) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-              float2 I, dI[3];
-              bwd_gather<NT>(mpk[u], mf[u][0], mf[u][1], mf[u][2], vt, I, dI);
-              I = make_float2(lane_fetch(I.x, dest[u]), lane_fetch(I.y, dest[u]));
-#pragma unroll
-              for (int a = 0; a < 3; ++a)
-                dI[a] = make_float2(lane_fetch(dI[a].x, dest[u]), lane_fetch(dI[a].y, dest[u]));
-              const float2 cc = c[u];
-              const float t0 = cc.x * dI[0].x + cc.y * dI[0].y, t1 = cc.x * dI[1].x + cc.y * dI[1].y;
-              const float t2 = cc.x * dI[2].x + cc.y * dI[2].y;
-              const float im = cc.x * I.y - cc.y * I.x;
-              const float fkx = cu[u].act ? cu[u].kx : 0.f, fky = cu[u].act ? cu[u].ky : 0.f;
-              float gacc[8] = {t0 * fkx, t0 * fky, t1 * fkx, t1 * fky, t2 * fkx, t2 * fky, fkx * im, fky * im};
-              grad_collect(gacc, cu[u].key, gw);
-            }
-          }
-          // phase 3: the taps into the accumulator tile (nothing waits on them)
+          // ... then all the taps (nothing waits on these atomics)
 #pragma unroll
           for (int u = 0; u < U; ++u)
             bwd_scatter<NT, WEIGHTS>(mpk[u], mf[u][0], mf[u][1], mf[u][2], mc[u], mw[u], acc_t, acc_w, scale, wscale);
@@ -397,7 +340,6 @@ __global__ void __launch_bounds__(BTHREADS, BWD_MIN_WAVES) k_bwd_brick(const flo
         __syncthreads();
         qb += nr;
       }
-      if constexpr (GRAD) grad_flush<WINDOW>(g, es, gw, nw, grad_rot, grad_s);
       // ---- flush the window into the float accumulators ----
       const float inv = scale > 0.f ? 1.0f / scale : 0.f;
       const float winv = wscale > 0.f ? 1.0f / wscale : 0.f;
@@ -434,7 +376,6 @@ __global__ void __launch_bounds__(BTHREADS, BWD_MIN_WAVES) k_bwd_brick(const flo
     if constexpr (WEIGHTS) part_w[slot0 + tid + BTHREADS * i] = accw[i];
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // Fold: every stored voxel sums the tile entries of all its tap-space
@@ -516,22 +457,21 @@ __global__ void __launch_bounds__(256) k_bwd_fold(float2* __restrict__ vol, floa
 
 // ---------------------------------------------------------------------------
 // Pixels the bricks do not serve (degenerate maps, samples outside every
-// active brick): their taps with global atomics (after the fold) and, with
-// GRAD, their gradient terms.
+// active brick): their taps with global atomics, after the fold.  One
+// workgroup per pose; a pose served whole by the bricks is skipped.
 // ---------------------------------------------------------------------------
-template <int NT, bool WEIGHTS, bool GRAD>
+template <int NT, bool WEIGHTS>
 __global__ void __launch_bounds__(256) k_bwd_edge(const float2* __restrict__ Y, const float* __restrict__ Wimg,
-                                                  const float2* __restrict__ volc, const float* __restrict__ rot,
-                                                  const float* __restrict__ shifts, float2* __restrict__ vol,
-                                                  float* __restrict__ wvol, float* __restrict__ grad_rot,
-                                                  float* __restrict__ grad_s, KGeom g, BwdGrid bw) {
+                                                  const float* __restrict__ rot, const float* __restrict__ shifts,
+                                                  float2* __restrict__ vol, float* __restrict__ wvol, KGeom g,
+                                                  BwdGrid bw) {
   const BrickGrid& bg = bw.bg;
   const int64_t nvol = (int64_t)g.D * g.D * g.W;
   for (int bn = blockIdx.x; bn < g.B * g.P; bn += gridDim.x) {
     const int bimg = bn / g.P, n = bn - bimg * g.P;
     const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
     const bool ok = pose_ok(contrib_bound<NT>(g, R));
-    if (ok && pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i) continue;   // served whole by the bricks
+    if (ok && pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i) continue;
     for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
       int ikx, iky;
       pixel_freq(g, pix, ikx, iky);
@@ -541,32 +481,10 @@ __global__ void __launch_bounds__(256) k_bwd_edge(const float2* __restrict__ Y, 
       slice_coord(g, R, kx, ky, p);
       if (ok && served_by_bricks(bg, p)) continue;
       float2 c = Y[(int64_t)bn * g.npix + pix];
-      float2 phi = make_float2(1.f, 0.f);
       if (shifts) {
         const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
-        phi = shift_phase(kx, ky, s[0], s[1], g.inv_h);
+        c = cmulc(shift_phase(kx, ky, s[0], s[1], g.inv_h), c);   // conj(phi) * Y
       }
-      if constexpr (GRAD) {
-        float2 I, dI[3];
-        interp_c<NT, true>(volc + nvol * (g.Bv == 1 ? 0 : bimg), g, p[0], p[1], p[2], I, dI);
-        const float2 cu = cmulc(c, phi);   // conj(G) * phi
-        float e[3];
-        for (int a = 0; a < 3; ++a) e[a] = cu.x * dI[a].x - cu.y * dI[a].y;
-        const float im = cu.x * I.y + cu.y * I.x;
-        if (grad_rot) {
-          float* gr = grad_rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-          for (int a = 0; a < 3; ++a) {
-            atomicAdd(gr + 3 * a, g.o * e[a] * kx);
-            atomicAdd(gr + 3 * a + 1, g.o * e[a] * ky);
-          }
-        }
-        if (grad_s) {
-          float* gs = grad_s + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
-          atomicAdd(gs, 6.283185307179586f * g.inv_h * kx * im);
-          atomicAdd(gs + 1, 6.283185307179586f * g.inv_h * ky * im);
-        }
-      }
-      c = cmulc(phi, c);   // conj(phi) * Y
       const float wimg = WEIGHTS ? Wimg[(int64_t)bn * g.npix + pix] : 0.f;
       float2* V = vol + nvol * (g.Bv == 1 ? 0 : bimg);
       float* VW = WEIGHTS ? wvol + nvol * (g.Bv == 1 ? 0 : bimg) : nullptr;
@@ -606,10 +524,9 @@ size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights) {
 }
 
 hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* workspace, const float2* Y,
-                      const float* Wimg, const float2* volc, const float* rot, const float* shifts, float2* vol,
-                      float* wvol, float* grad_rot, float* grad_s, hipStream_t st, const EvPair* ev_brick,
-                      const EvPair* ev_fold) {
-  const bool weights = Wimg != nullptr, grad = volc != nullptr;
+                      const float* Wimg, const float* rot, const float* shifts, float2* vol, float* wvol,
+                      hipStream_t st, const EvPair* ev_brick, const EvPair* ev_fold) {
+  const bool weights = Wimg != nullptr;
   int* prefix = (int*)workspace;
   const size_t off_b = align256((size_t)(bw.bg.nb3 + 1) * sizeof(int));
   float* ymax = (float*)((char*)workspace + off_b);
@@ -628,13 +545,13 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
   ev_begin(ev_brick, st);   // recorded even when no brick kernel runs
   if (bw.bg.nwork > 0) {
     const dim3 grid(bw.bg.nwork, g.Bv);
-#define TP_BWD(NT_, W_, G_)                                                                                    \
-  hipLaunchKernelGGL((k_bwd_brick<NT_, W_, G_>), grid, dim3(BTHREADS), 0, st, Y, Wimg, volc, rot, shifts, grad_rot, grad_s, \
-                     part_c, part_w, g, bw, prefix, ymax, wmax)
+#define TP_BWD(NT_, W_)                                                                                        \
+  hipLaunchKernelGGL((k_bwd_brick<NT_, W_>), grid, dim3(BTHREADS), 0, st, Y, Wimg, rot, shifts, part_c, part_w, g, \
+                     bw, prefix, ymax, wmax)
     if (interp == 1) {
-      if (grad) TP_BWD(4, false, true); else if (weights) TP_BWD(4, true, false); else TP_BWD(4, false, false);
+      if (weights) TP_BWD(4, true); else TP_BWD(4, false);
     } else {
-      if (grad) TP_BWD(2, false, true); else if (weights) TP_BWD(2, true, false); else TP_BWD(2, false, false);
+      if (weights) TP_BWD(2, true); else TP_BWD(2, false);
     }
 #undef TP_BWD
     e = hipGetLastError();
@@ -658,15 +575,13 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
     if (e != hipSuccess) return e;
   }
   const dim3 eg(g.B * g.P < 16384 ? g.B * g.P : 16384);   // one workgroup per pose
-#define TP_EDGE(NT_, W_, G_)                                                                                  \
-  hipLaunchKernelGGL((k_bwd_edge<NT_, W_, G_>), eg, blk, 0, st, Y, Wimg, volc, rot, shifts, vol, wvol, grad_rot, \
-                     grad_s, g, bw)
   if (interp == 1) {
-    if (grad) TP_EDGE(4, false, true); else if (weights) TP_EDGE(4, true, false); else TP_EDGE(4, false, false);
+    if (weights) hipLaunchKernelGGL((k_bwd_edge<4, true>), eg, blk, 0, st, Y, Wimg, rot, shifts, vol, wvol, g, bw);
+    else hipLaunchKernelGGL((k_bwd_edge<4, false>), eg, blk, 0, st, Y, Wimg, rot, shifts, vol, wvol, g, bw);
   } else {
-    if (grad) TP_EDGE(2, false, true); else if (weights) TP_EDGE(2, true, false); else TP_EDGE(2, false, false);
+    if (weights) hipLaunchKernelGGL((k_bwd_edge<2, true>), eg, blk, 0, st, Y, Wimg, rot, shifts, vol, wvol, g, bw);
+    else hipLaunchKernelGGL((k_bwd_edge<2, false>), eg, blk, 0, st, Y, Wimg, rot, shifts, vol, wvol, g, bw);
   }
-#undef TP_EDGE
   return hipGetLastError();
 }
 

@@ -318,28 +318,21 @@ tp_status run_forward_real(const tp_geom* geom, const tproj::KGeom& k, const flo
 }
 
 // Back-projection of Y (and of the weight images Wimg into wvol): bricks,
-// else zeroed volumes and direct atomics.  With volc, the rotation / shift
-// gradients of the forward are computed in the same pass (the caller zeroes
-// them); without the brick plan they go to the direct gradient kernel.
-tp_status run_bwd(const tp_geom* geom, const tproj::KGeom& k, const float2* Y, const float* Wimg,
-                  const float2* volc, const float* rot, const float* shifts, float2* vol, float* wvol,
-                  float* grad_rot, float* grad_shifts, void* workspace, size_t ws_bytes, hipStream_t st) {
+// else zeroed volumes and direct atomics.
+tp_status run_bwd(const tp_geom* geom, const tproj::KGeom& k, const float2* Y, const float* Wimg, const float* rot,
+                  const float* shifts, float2* vol, float* wvol, void* workspace, size_t ws_bytes, hipStream_t st) {
   const BwdPlan pl = bwd_plan(geom, Wimg != nullptr);
   if (!pl.ok) {
     LAUNCH(tproj::launch_zero((float*)vol, 2 * vol_elems(geom) * geom->Bv, st), "zero volume");
     if (wvol) LAUNCH(tproj::launch_zero(wvol, vol_elems(geom) * geom->Bv, st), "zero weight volume");
     LAUNCH(tproj::launch_spread_atomic(k, geom->interp, Y, Wimg, rot, shifts, vol, wvol, st), "scatter");
-    if (volc)
-      LAUNCH(tproj::launch_rot_shift_grad(k, geom->interp, volc, nullptr, Y, nullptr, rot, shifts, grad_rot,
-                                          grad_shifts, st),
-             "rotation/shift grads");
     return TP_OK;
   }
   if (!workspace || ws_bytes < pl.ws_bytes)
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
   const tproj::EvPair eb = kt_copy(TP_KT_BACKWARD), ef = kt_copy(TP_KT_FOLD);
-  LAUNCH(tproj::launch_bwd(k, geom->interp, pl.bw, workspace, Y, Wimg, volc, rot, shifts, vol, wvol, grad_rot,
-                           grad_shifts, st, eb.a ? &eb : nullptr, ef.a ? &ef : nullptr),
+  LAUNCH(tproj::launch_bwd(k, geom->interp, pl.bw, workspace, Y, Wimg, rot, shifts, vol, wvol, st,
+                           eb.a ? &eb : nullptr, ef.a ? &ef : nullptr),
          "back-projection (bricks)");
   return TP_OK;
 }
@@ -459,20 +452,14 @@ tp_status project_3d_to_2d_backward(const tp_geom* geom, const void* grad_out, c
   TRY(check_device());
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
-  if (grad_vol && (grad_rot || grad_shifts)) {
-    // one pass: the adjoint scatter and the rotation / shift gradients
-    if (grad_rot) LAUNCH(tproj::launch_zero(grad_rot, 9 * (int64_t)geom->Br * geom->P, st), "zero grad_rot");
-    if (grad_shifts)
-      LAUNCH(tproj::launch_zero(grad_shifts, 2 * (int64_t)geom->Bs * geom->P, st), "zero grad_shifts");
-    TRY(run_bwd(geom, k, (const float2*)grad_out, nullptr, (const float2*)vol, rot, shifts, (float2*)grad_vol,
-                nullptr, grad_rot, grad_shifts, workspace, ws_bytes, st));
-  } else if (grad_vol) {
-    TRY(run_bwd(geom, k, (const float2*)grad_out, nullptr, nullptr, rot, shifts, (float2*)grad_vol, nullptr,
-                nullptr, nullptr, workspace, ws_bytes, st));
-  } else if (grad_rot || grad_shifts) {
+  // the adjoint scatter, then the rotation / shift gradients (the two share
+  // the workspace: they run one after the other on the stream)
+  if (grad_vol)
+    TRY(run_bwd(geom, k, (const float2*)grad_out, nullptr, rot, shifts, (float2*)grad_vol, nullptr, workspace,
+                ws_bytes, st));
+  if (grad_rot || grad_shifts)
     TRY(run_grads(geom, k, (const float2*)vol, nullptr, (const float2*)grad_out, nullptr, rot, shifts, grad_rot,
                   grad_shifts, workspace, ws_bytes, st));
-  }
   return ok();
 }
 
@@ -494,8 +481,8 @@ tp_status backproject_2d_to_3d(const tp_geom* geom, const void* images, const fl
   TRY(check_device());
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
-  TRY(run_bwd(geom, k, (const float2*)images, weights, nullptr, rot, shifts, (float2*)data_vol, weight_vol, nullptr,
-              nullptr, workspace, ws_bytes, st));
+  TRY(run_bwd(geom, k, (const float2*)images, weights, rot, shifts, (float2*)data_vol, weight_vol, workspace,
+              ws_bytes, st));
   return ok();
 }
 

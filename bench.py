@@ -93,7 +93,7 @@ def in_mask_pixels(H, r):
 def kernel_model(w, kclass, ws_bytes=0):
     """Algorithmic bytes of one launch of a brick-kernel class on workload `w`.
     tap bytes: in-mask pixels x taps x 8 B per complex tap read (gather) or
-    accumulated (scatter); the fused backward does both.  hbm bytes: what the
+    accumulated (scatter: the backward class).  hbm bytes: what the
     launch must read or write in HBM at least (images, volume, pose params;
     for the fold, the partial tiles and the volume)."""
     T = 64 if w.interp == 1 else 8
@@ -102,9 +102,9 @@ def kernel_model(w, kclass, ws_bytes=0):
     img = npose * w.H * (w.H // 2 + 1) * 8
     vol = w.D * w.D * (w.D // 2 + 1) * 8
     params = npose * (9 + 2) * 4
-    per_px = {"forward": T * 8, "backward": 2 * T * 8, "gradient": T * 8, "fold": 0}[kclass]
+    per_px = {"forward": T * 8, "backward": T * 8, "gradient": T * 8, "fold": 0}[kclass]
     hbm = {"forward": img + vol + params,
-           "backward": img + vol + params + npose * 11 * 4,
+           "backward": img + vol + params,
            "gradient": img + vol + params + npose * 11 * 4,
            "fold": ws_bytes + vol}[kclass]
     return {"tap_bytes": npose * n_in * per_px, "tap_bytes_per_pixel": per_px, "hbm_bytes": hbm, "n_in": n_in,
