@@ -98,30 +98,43 @@ __device__ __forceinline__ void cols_to_r9(const float4& c0, const float4& c1, f
   R[6] = c0.z; R[7] = c1.y; R[8] = 0.f;
 }
 
+// No per-hit work beyond the set-up.
+struct NoHitHook {
+  __device__ void operator()(bool, const float*, int) const {}
+};
+
 // Window set-up: threads t < nw take hit hw + t of the pass that starts at
 // list entry eb.  Writes the geometry, the image index and the row range of
-// every hit, then the row prefix.
-template <int WIN, int NW>
+// every hit, then the row prefix.  hook(valid, R, pose) runs on every lane of
+// wavefront 0 (valid: the lane holds a hit; R: its rotation, row-major), before
+// the closing barrier, so what it writes to LDS is visible on return.
+template <int WIN, int NW, typename Hook = NoHitHook>
 __device__ __forceinline__ void window_setup(EnumShared<WIN, NW>& es, const KGeom& g, const float* __restrict__ rot,
                                              const float* __restrict__ shifts, int vsel, int64_t eb, int hw, int nw,
-                                             const float bl[3], const float bh[3]) {
+                                             const float bl[3], const float bh[3], Hook hook = Hook()) {
   static_assert(WIN <= 64, "one wavefront sets up a window");
   const int tid = threadIdx.x;
   if (tid < 64) {
-    int nrows = 0;
+    int nrows = 0, pose = 0;
+    float R[9];
+#pragma unroll
+    for (int a = 0; a < 9; ++a) R[a] = 0.f;
     if (tid < nw) {
       int bimg, n;
       list_entry(g, vsel, (int)(eb + nth_hit(es, hw + tid)), bimg, n);
-      const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+      const float* Rg = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+#pragma unroll
+      for (int a = 0; a < 9; ++a) R[a] = Rg[a];
       float sx = 0.f, sy = 0.f;
       if (shifts) {
         const float* s = shifts + 2 * ((int64_t)(g.Bs == 1 ? 0 : bimg) * g.P + n);
         sx = s[0];
         sy = s[1];
       }
+      pose = bimg * g.P + n;
       es.geo0[tid] = make_float4(R[0], R[3], R[6], R[1]);
       es.geo1[tid] = make_float4(R[4], R[7], sx, sy);
-      es.hpose[tid] = bimg * g.P + n;
+      es.hpose[tid] = pose;
       SliceRows sr;
       if (slice_rows_box(g, R, bl, bh, sr)) nrows = sr.ky_hi - sr.ky_lo + 1;
       es.hky[tid] = sr.ky_lo;
@@ -136,6 +149,7 @@ __device__ __forceinline__ void window_setup(EnumShared<WIN, NW>& es, const KGeo
       if (tid == 0) es.hrow[0] = 0;
       if (tid < WIN) es.hrow[tid + 1] = v;
     }
+    hook(tid < nw, R, pose);
   }
   __syncthreads();
 }

@@ -186,7 +186,7 @@ __global__ void __launch_bounds__(256) k_band_max(const float2* __restrict__ Y, 
 #define BWD_UNROLL 2
 #endif
 #ifndef BWD_MIN_WAVES
-#define BWD_MIN_WAVES 1
+#define BWD_MIN_WAVES 4   // wavefronts per SIMD without the weight tile (its LDS allows two with it)
 #endif
 
 // One pixel, in the lane the bank-spreading permutation gave it: pk packs
@@ -221,7 +221,7 @@ __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz
 }
 
 template <int NT, bool WEIGHTS>
-__global__ void __launch_bounds__(BTHREADS, BWD_MIN_WAVES) k_bwd_brick(const float2* __restrict__ Y,
+__global__ void __launch_bounds__(BTHREADS, WEIGHTS ? 2 : BWD_MIN_WAVES) k_bwd_brick(const float2* __restrict__ Y,
                                                                       const float* __restrict__ Wimg,
                                                                       const float* __restrict__ rot,
                                                                       const float* __restrict__ shifts,
@@ -234,7 +234,7 @@ __global__ void __launch_bounds__(BTHREADS, BWD_MIN_WAVES) k_bwd_brick(const flo
   __shared__ unsigned long long acc_t[TSIZE];
   __shared__ unsigned int acc_w[WEIGHTS ? TSIZE : 1];
   __shared__ EnumShared<WINDOW, BNW> es;
-  __shared__ float hit_m[WINDOW], hit_w[WINDOW], hit_c[WINDOW];
+  __shared__ float win_scale[2];
 
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
@@ -275,29 +275,31 @@ __global__ void __launch_bounds__(BTHREADS, BWD_MIN_WAVES) k_bwd_brick(const flo
 
     for (int hb = 0; hb < nh; hb += WINDOW) {
       const int nw = min(WINDOW, nh - hb);
-      window_setup(es, g, rot, shifts, vsel, eb, hb, nw, bl, bh);
-      // per hit: the bound on contributions to one tap and the largest value
-      // it can bring to this brick
-      if (tid < nw) {
-        float R[9];
-        cols_to_r9(es.geo0[tid], es.geo1[tid], R);
-        const int64_t pose = es.hpose[tid];
-        hit_c[tid] = contrib_bound<NT>(g, R);
-        hit_m[tid] = box_band_max(g, bw, R, ymax, pose, bl, bh);
-        hit_w[tid] = WEIGHTS ? box_band_max(g, bw, R, wmax, pose, bl, bh) : 0.f;
-      }
-      __syncthreads();
-      float M = 0.f, MW = 0.f, C = 0.f;
-      for (int h = 0; h < nw; ++h) {
-        M = fmaxf(M, hit_m[h]);
-        MW = fmaxf(MW, hit_w[h]);
-        C += hit_c[h];
-      }
-      // |re|, |im| <= sqrt(2) M per unit weight (the phase rotates); every
-      // contribution also stays below 2^22 for the magic rounding
-      const float lim = fminf(FIX_RANGE - C, 0.99f * 4194304.0f * C);
-      const float scale = M > 0.f ? lim / (1.41421356f * M * C) : 0.f;
-      const float wscale = (WEIGHTS && MW > 0.f) ? lim / (MW * C) : 0.f;
+      // the window's fixed-point scales, from every hit's bound on the
+      // contributions to one tap and the largest value it can bring to this
+      // brick (wavefront 0, one hit per lane)
+      window_setup(es, g, rot, shifts, vsel, eb, hb, nw, bl, bh, [&](bool valid, const float* R, int pose) {
+        float c = 0.f, m = 0.f, mw = 0.f;
+        if (valid) {
+          c = contrib_bound<NT>(g, R);
+          m = box_band_max(g, bw, R, ymax, pose, bl, bh);
+          if constexpr (WEIGHTS) mw = box_band_max(g, bw, R, wmax, pose, bl, bh);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          c += __shfl_xor(c, off, 64);
+          m = fmaxf(m, __shfl_xor(m, off, 64));
+          if constexpr (WEIGHTS) mw = fmaxf(mw, __shfl_xor(mw, off, 64));
+        }
+        if (lane == 0) {
+          // |re|, |im| <= sqrt(2) M per unit weight (the phase rotates); every
+          // contribution also stays below 2^22 for the magic rounding
+          const float lim = fminf(FIX_RANGE - c, 0.99f * 4194304.0f * c);
+          win_scale[0] = m > 0.f ? lim / (1.41421356f * m * c) : 0.f;
+          win_scale[1] = (WEIGHTS && mw > 0.f) ? lim / (mw * c) : 0.f;
+        }
+      });
+      const float scale = win_scale[0], wscale = win_scale[1];
       const int nrows = es.hrow[nw];
       for (int qb = 0; qb < nrows;) {
         int nr;
