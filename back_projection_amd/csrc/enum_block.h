@@ -98,6 +98,24 @@ __device__ __forceinline__ void cols_to_r9(const float4& c0, const float4& c1, f
   R[6] = c0.z; R[7] = c1.y; R[8] = 0.f;
 }
 
+// DPP move of v (lanes the control does not reach get old).
+template <int CTRL, int RM>
+__device__ __forceinline__ int dpp_int(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, RM, 0xf, false);
+}
+
+// Inclusive prefix sum across the wavefront: DPP row shifts within each row
+// of 16 lanes, then the row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  v += dpp_int<0x111, 0xf>(0, v);   // row_shr:1
+  v += dpp_int<0x112, 0xf>(0, v);   // row_shr:2
+  v += dpp_int<0x114, 0xf>(0, v);   // row_shr:4
+  v += dpp_int<0x118, 0xf>(0, v);   // row_shr:8
+  v += dpp_int<0x142, 0xa>(0, v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_int<0x143, 0xc>(0, v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // No per-hit work beyond the set-up.
 struct NoHitHook {
   __device__ void operator()(bool, const float*, int) const {}
@@ -139,12 +157,7 @@ __device__ __forceinline__ void window_setup(EnumShared<WIN, NW>& es, const KGeo
       if (slice_rows_box(g, R, bl, bh, sr)) nrows = sr.ky_hi - sr.ky_lo + 1;
       es.hky[tid] = sr.ky_lo;
     }
-    int v = nrows;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int u = __shfl_up(v, off, 64);
-      if (tid >= off) v += u;
-    }
+    const int v = wave_scan_incl(nrows);
     if (tid <= WIN) {
       if (tid == 0) es.hrow[0] = 0;
       if (tid < WIN) es.hrow[tid + 1] = v;
@@ -211,12 +224,7 @@ __device__ __forceinline__ int row_stage(EnumShared<WIN, NW>& es, const KGeom& g
     for (int a = 0; a < 3; ++a) r0[a] = fabsf(a0[a]) > 1e-20f ? __builtin_amdgcn_rcpf(a0[a]) : 0.0f;
     row_interval(g, a0, a1, r0, bl, bh, ky, kx0, cnt);
   }
-  int v = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int u = __shfl_up(v, off, 64);
-    if (lane >= off) v += u;
-  }
+  const int v = wave_scan_incl(cnt);
   if (lane == 63) es.wtot[wave] = v;
   __syncthreads();
   int carry = 0;
@@ -337,11 +345,6 @@ __device__ __forceinline__ float2 lane_fetch(float2 v, int src) {
 // the sum of its key's values from the key's first lane up to itself.  DPP
 // row shifts, then the row broadcasts of lanes 15 and 31.
 // ---------------------------------------------------------------------------
-template <int CTRL, int RM>
-__device__ __forceinline__ int dpp_int(int old, int v) {
-  return __builtin_amdgcn_update_dpp(old, v, CTRL, RM, 0xf, false);
-}
-
 template <int CTRL, int RM, int N>
 __device__ __forceinline__ void seg_step(float (&v)[N], int key) {
   const int ks = dpp_int<CTRL, RM>(-1, key);

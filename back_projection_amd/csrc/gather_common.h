@@ -415,76 +415,47 @@ __device__ __forceinline__ bool slice_rows_box(const KGeom& g, const float* R, c
       kmin += fminf(x, y);
       kmax += fmaxf(x, y);
     }
+    // the box's shadow on the plane is larger than the section of the plane
+    // by the box (a convex polygon whose corners each lie on the faces of two
+    // different slabs bl_a <= A_a . k <= bh_a); its ky extent is the tighter
+    // bound.  Used only when every pair of slab normals is well conditioned
+    // (the corners then carry errors far below the one-row margin).
+    float pmin = 3.0e38f, pmax = -3.0e38f;
+    bool cond = true;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int a = q == 2 ? 1 : 0, b = q == 0 ? 1 : 2, c = 3 - a - b;
+      const float d = sr.a0[a] * sr.a1[b] - sr.a1[a] * sr.a0[b];
+      const float na = fabsf(sr.a0[a]) + fabsf(sr.a1[a]), nb = fabsf(sr.a0[b]) + fabsf(sr.a1[b]);
+      if (!(fabsf(d) > 1e-3f * na * nb)) {
+        cond = false;
+        continue;
+      }
+      const float inv = 1.0f / d;
+      const float marg = 2e-2f + 1e-4f * (fabsf(sr.bl[c]) + fabsf(sr.bh[c]));
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const float va = (s & 1) ? sr.bh[a] : sr.bl[a], vb = (s & 2) ? sr.bh[b] : sr.bl[b];
+        // [a0 a1; b0 b1] k = [va; vb]
+        const float kx = (va * sr.a1[b] - vb * sr.a1[a]) * inv;
+        const float ky = (vb * sr.a0[a] - va * sr.a0[b]) * inv;
+        const float pc = fmaf(sr.a0[c], kx, sr.a1[c] * ky);
+        if (pc >= sr.bl[c] - marg && pc <= sr.bh[c] + marg) {
+          pmin = fminf(pmin, ky);
+          pmax = fmaxf(pmax, ky);
+        }
+      }
+    }
+    if (cond && pmin <= pmax) {
+      kmin = fmaxf(kmin, pmin);
+      kmax = fminf(kmax, pmax);
+    }
     kmin = fmaxf(kmin, (float)lo_img - 2.0f);
     kmax = fminf(kmax, (float)hi_img + 2.0f);
     sr.ky_lo = max(sr.ky_lo, (int)floorf(kmin) - 1);
     sr.ky_hi = min(sr.ky_hi, (int)ceilf(kmax) + 1);
   }
   return sr.ky_lo <= sr.ky_hi;
-}
-
-// One lane per row ky = r0 + lane: kx interval, count, inclusive scan.
-struct RowBatch {
-  int kx0;     // first candidate kx of this lane's row
-  int incl;    // inclusive prefix of the row counts
-  int total;   // candidates of the batch (wave-uniform)
-};
-
-__device__ __forceinline__ void row_batch(const KGeom& g, const SliceRows& sr, int r0, int lane, RowBatch& rb) {
-  const int ky = r0 + lane;
-  int cnt = 0, kx0 = 0;
-  if (ky <= sr.ky_hi) {
-    const float fky = (float)ky;
-    float xlo = 0.0f, xhi = (float)(g.H >> 1);
-    bool ok = true;
-    if (g.r2 >= 0.0f) {
-      const float rem = g.r2 - fky * fky;
-      if (rem < 0.0f) ok = false;
-      else xhi = fminf(xhi, floorf(sqrtf(rem)) + 1.0f);
-    }
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-      // the approximate reciprocal is within a few ulp; the margin (in sample
-      // units) and the owner test on the exact floor(p) absorb it
-      const float marg = 1e-2f + 1e-4f * (fabsf(sr.bl[a]) + fabsf(sr.bh[a]) + fabsf(sr.a1[a] * fky));
-      const float rl = sr.bl[a] - marg - sr.a1[a] * fky;
-      const float rh = sr.bh[a] + marg - sr.a1[a] * fky;
-      const float c = sr.a0[a], rc = sr.r0[a];
-      if (c > 1e-20f) { xlo = fmaxf(xlo, rl * rc); xhi = fminf(xhi, rh * rc); }
-      else if (c < -1e-20f) { xlo = fmaxf(xlo, rh * rc); xhi = fminf(xhi, rl * rc); }
-      else if (rl > 0.0f || rh < 0.0f) ok = false;
-    }
-    if (ok && xlo <= xhi) {
-      kx0 = (int)ceilf(xlo);
-      const int kx1 = (int)floorf(xhi);
-      cnt = kx1 >= kx0 ? kx1 - kx0 + 1 : 0;
-    }
-  }
-  int v = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int u = __shfl_up(v, off, 64);
-    if (lane >= off) v += u;
-  }
-  rb.kx0 = kx0;
-  rb.incl = v;
-  rb.total = __shfl(v, 63, 64);
-}
-
-// Candidate i of the batch (all 64 lanes call this together): its row is the
-// first lane whose inclusive count exceeds i.
-__device__ __forceinline__ void candidate(const RowBatch& rb, int r0, int i, int& kx, int& ky) {
-  int r = 0;
-#pragma unroll
-  for (int step = 32; step >= 1; step >>= 1) {
-    const int v = __shfl(rb.incl, r + step - 1, 64);
-    if (v <= i) r += step;
-  }
-  // every lane takes part in each permute (no lane-dependent branch around them)
-  int before = __shfl(rb.incl, r > 0 ? r - 1 : 0, 64);
-  if (r == 0) before = 0;
-  kx = __shfl(rb.kx0, r, 64) + (i - before);
-  ky = r0 + r;
 }
 
 }  // namespace tproj
