@@ -152,7 +152,7 @@ size_t tp_workspace_size(const tp_geom* geom, int op);
 /* Event timing of the brick kernels (benchmarks, profiling).  Kernel classes: */
 enum {
   TP_KT_FORWARD = 0,   /* forward gather brick kernel (complex or real volume)           */
-  TP_KT_BACKWARD = 1,  /* back-projection brick kernel (rotation/shift grads fused in)    */
+  TP_KT_BACKWARD = 1,  /* back-projection (scatter) brick kernel                          */
   TP_KT_GRADIENT = 2,  /* rotation/shift gradient brick kernel                           */
   TP_KT_FOLD = 3,      /* fold of the back-projection partial tiles into the volume      */
   TP_KT_COUNT = 4
