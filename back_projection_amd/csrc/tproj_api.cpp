@@ -228,6 +228,8 @@ tp_status launched(hipError_t e, const char* what) {
   return ok();
 }
 
+size_t align_up(size_t n) { return (n + 255) / 256 * 256; }
+
 tp_status check_device() {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
@@ -257,6 +259,39 @@ tp_status check_workspace(const tp_geom* g, int op, const void* ws, size_t ws_by
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, need);
   return TP_OK;
+}
+
+// A second stream per device for the rotation / shift gradients of the
+// forward's backward: they read only the upstream gradient, the volume and the
+// poses, so they run beside the back-projection (the two kernels are limited
+// by different units: memory latency and LDS atomics vs. VALU).  The fork and
+// the join are events recorded on the caller's stream and on this one; one
+// mutex keeps a call's record / wait pairs together.  Default priority.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false, ok = false;
+};
+constexpr int MAX_DEVICES = 64;
+SideStream g_side[MAX_DEVICES];
+std::mutex g_side_mu;
+
+// Call with g_side_mu held.  NULL if the device has no side stream.
+SideStream* side_stream() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  SideStream& ss = g_side[dev];
+  if (!ss.tried) {
+    ss.tried = true;
+    ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) == hipSuccess;
+    if (!ss.ok) (void)hipGetLastError();   // the callers then run serially
+  }
+  return ss.ok ? &ss : nullptr;
 }
 
 // Forward gather: brick-binned kernels when the plan applies, else direct.
@@ -409,7 +444,8 @@ namespace {
 size_t workspace_need(const tp_geom* geom, int op) {
   const size_t gather = gather_plan(geom).ws_bytes;
   if (op == TP_OP_PROJECT || op == TP_OP_BACKPROJECT_BACKWARD) return gather;
-  if (op == TP_OP_PROJECT_BACKWARD) return std::max(gather, bwd_plan(geom, false).ws_bytes);
+  // the back-projection's part, then the gradients' (they may run at once)
+  if (op == TP_OP_PROJECT_BACKWARD) return align_up(bwd_plan(geom, false).ws_bytes) + gather;
   return bwd_plan(geom, true).ws_bytes;
 }
 }  // namespace
@@ -452,12 +488,36 @@ tp_status project_3d_to_2d_backward(const tp_geom* geom, const void* grad_out, c
   TRY(check_device());
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
-  // the adjoint scatter, then the rotation / shift gradients (the two share
-  // the workspace: they run one after the other on the stream)
+  const bool grads = grad_rot || grad_shifts;
+  if (grad_vol && grads) {
+    // gradients on the side stream (workspace after the scatter's part),
+    // the scatter on the caller's stream, then the caller's stream waits
+    const size_t off = align_up(bwd_plan(geom, false).ws_bytes);
+    void* ws2 = workspace ? (char*)workspace + off : nullptr;
+    const size_t n2 = ws_bytes > off ? ws_bytes - off : 0;
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    SideStream* ss = side_stream();
+    if (ss) {
+      hipError_t e = hipEventRecord(ss->fork, st);
+      if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+      if (e != hipSuccess) return fail(TP_E_LAUNCH, "stream fork failed: %s", hipGetErrorString(e));
+      const tp_status sg = run_grads(geom, k, (const float2*)vol, nullptr, (const float2*)grad_out, nullptr, rot,
+                                     shifts, grad_rot, grad_shifts, ws2, n2, ss->s);
+      e = hipEventRecord(ss->join, ss->s);
+      const tp_status sv = sg == TP_OK ? run_bwd(geom, k, (const float2*)grad_out, nullptr, rot, shifts,
+                                                 (float2*)grad_vol, nullptr, workspace, ws_bytes, st)
+                                       : sg;
+      if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->join, 0);
+      if (e != hipSuccess) return fail(TP_E_LAUNCH, "stream join failed: %s", hipGetErrorString(e));
+      if (sv != TP_OK) return sv;
+      return ok();
+    }
+  }
+  // one after the other on the caller's stream
   if (grad_vol)
     TRY(run_bwd(geom, k, (const float2*)grad_out, nullptr, rot, shifts, (float2*)grad_vol, nullptr, workspace,
                 ws_bytes, st));
-  if (grad_rot || grad_shifts)
+  if (grads)
     TRY(run_grads(geom, k, (const float2*)vol, nullptr, (const float2*)grad_out, nullptr, rot, shifts, grad_rot,
                   grad_shifts, workspace, ws_bytes, st));
   return ok();
