@@ -11,11 +11,11 @@ namespace tproj {
 
 // prefix[0..nb3] of the pose chunks of every brick (one workgroup).
 hipError_t launch_brick_prefix(const BrickGrid& bg, int* prefix, hipStream_t st);
-// forward: edge kernel (masked pixels, samples outside the active bricks)
-// then the brick kernel; out is fully written.
+// forward: edge kernel (masked pixels, samples outside the active bricks) on
+// st_edge, brick kernel on st; out is fully written once both are done.
 hipError_t launch_fwd_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* vol,
-                            const float* rot, const float* shifts, float2* out, hipStream_t st,
-                            const EvPair* ev = nullptr);
+                            const float* rot, const float* shifts, float2* out, hipStream_t st, const EvPair* ev,
+                            hipStream_t st_edge);
 // same for a real volume (weight channel), no phase
 hipError_t launch_fwd_brick_real(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix,
                                  const float* vol, const float* rot, float* out, hipStream_t st,

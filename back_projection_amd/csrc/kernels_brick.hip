@@ -380,12 +380,15 @@ hipError_t launch_brick_prefix(const BrickGrid& bg, int* prefix, hipStream_t st)
 // One workgroup per pose (grid-stride beyond 16384 poses).
 static dim3 edge_grid(const KGeom& g) { return dim3(g.B * g.P < 16384 ? g.B * g.P : 16384); }
 
+// The edge kernel goes to st_edge (it writes other pixels than the brick
+// kernel, so the two may run at once), the brick kernel to st.
 template <typename T>
 static hipError_t fwd_t(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const T* vol,
-                        const float* rot, const float* shifts, T* out, hipStream_t st, const EvPair* ev) {
+                        const float* rot, const float* shifts, T* out, hipStream_t st, const EvPair* ev,
+                        hipStream_t st_edge) {
   const dim3 blk(256);
-  if (interp == 1) hipLaunchKernelGGL((k_fwd_edge<4, T>), edge_grid(g), blk, 0, st, vol, rot, shifts, out, g, bg);
-  else hipLaunchKernelGGL((k_fwd_edge<2, T>), edge_grid(g), blk, 0, st, vol, rot, shifts, out, g, bg);
+  if (interp == 1) hipLaunchKernelGGL((k_fwd_edge<4, T>), edge_grid(g), blk, 0, st_edge, vol, rot, shifts, out, g, bg);
+  else hipLaunchKernelGGL((k_fwd_edge<2, T>), edge_grid(g), blk, 0, st_edge, vol, rot, shifts, out, g, bg);
   hipError_t e = hipGetLastError();
   ev_begin(ev, st);   // recorded even when no brick kernel runs
   if (e != hipSuccess || bg.nwork == 0) {
@@ -400,13 +403,14 @@ static hipError_t fwd_t(const KGeom& g, int interp, const BrickGrid& bg, const i
 }
 
 hipError_t launch_fwd_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* vol,
-                            const float* rot, const float* shifts, float2* out, hipStream_t st, const EvPair* ev) {
-  return fwd_t<float2>(g, interp, bg, prefix, vol, rot, shifts, out, st, ev);
+                            const float* rot, const float* shifts, float2* out, hipStream_t st, const EvPair* ev,
+                            hipStream_t st_edge) {
+  return fwd_t<float2>(g, interp, bg, prefix, vol, rot, shifts, out, st, ev, st_edge);
 }
 
 hipError_t launch_fwd_brick_real(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix,
                                  const float* vol, const float* rot, float* out, hipStream_t st, const EvPair* ev) {
-  return fwd_t<float>(g, interp, bg, prefix, vol, rot, nullptr, out, st, ev);
+  return fwd_t<float>(g, interp, bg, prefix, vol, rot, nullptr, out, st, ev, st);
 }
 
 template <int NT, bool C, bool R>

@@ -305,11 +305,28 @@ tp_status run_forward(const tp_geom* geom, const tproj::KGeom& k, const float2* 
   if (!workspace || ws_bytes < pl.ws_bytes)
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
   int* prefix = (int*)workspace;
-  LAUNCH(tproj::launch_brick_prefix(pl.bg, prefix, st), "brick work list");
   const tproj::EvPair ev = kt_copy(TP_KT_FORWARD);
-  LAUNCH(tproj::launch_fwd_brick(k, geom->interp, pl.bg, prefix, vol, rot, shifts, out, st, ev.a ? &ev : nullptr),
-         "project (bricks)");
-  return TP_OK;
+  // the edge kernel on the side stream, beside the work list and the bricks
+  std::lock_guard<std::mutex> lk(g_side_mu);
+  SideStream* ss = side_stream();
+  hipStream_t se = st;
+  if (ss) {
+    hipError_t e = hipEventRecord(ss->fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+    if (e != hipSuccess) return fail(TP_E_LAUNCH, "stream fork failed: %s", hipGetErrorString(e));
+    se = ss->s;
+  }
+  tp_status r = TP_OK;
+  hipError_t e = tproj::launch_brick_prefix(pl.bg, prefix, st);
+  if (e == hipSuccess)
+    e = tproj::launch_fwd_brick(k, geom->interp, pl.bg, prefix, vol, rot, shifts, out, st, ev.a ? &ev : nullptr, se);
+  if (e != hipSuccess) r = fail(TP_E_LAUNCH, "project (bricks): %s", hipGetErrorString(e));
+  if (ss) {
+    hipError_t ej = hipEventRecord(ss->join, ss->s);
+    if (ej == hipSuccess) ej = hipStreamWaitEvent(st, ss->join, 0);
+    if (ej != hipSuccess && r == TP_OK) r = fail(TP_E_LAUNCH, "stream join failed: %s", hipGetErrorString(ej));
+  }
+  return r;
 }
 
 // Rotation / shift gradients into zeroed outputs: bricks, else direct.
