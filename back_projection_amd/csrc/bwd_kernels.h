@@ -23,8 +23,11 @@ size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights);
 
 // Writes vol (and wvol when Wimg != NULL) completely with the adjoint of the
 // forward (the back-projection of Y, and of the weight images Wimg).
+// after_bands (optional) is recorded on st once the band maxima are queued,
+// i.e. just before the brick kernel.
 hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* workspace, const float2* Y,
                       const float* Wimg, const float* rot, const float* shifts, float2* vol, float* wvol,
-                      hipStream_t st, const EvPair* ev_brick = nullptr, const EvPair* ev_fold = nullptr);
+                      hipStream_t st, const EvPair* ev_brick = nullptr, const EvPair* ev_fold = nullptr,
+                      hipEvent_t after_bands = nullptr);
 
 }  // namespace tproj

@@ -418,16 +418,15 @@ static void grad_launch(const KGeom& g, const BrickGrid& bg, const int* prefix, 
                         const float2* U, const float* Ur, const float* rot, const float* shifts, float* grad_rot,
                         float* grad_s, hipStream_t st, const EvPair* ev) {
   const dim3 blk(256);
+  ev_begin(ev, st);   // recorded even when no brick kernel runs
+  if (bg.nwork > 0)
+    hipLaunchKernelGGL((k_grad_brick<NT, C, R>), dim3(bg.nwork, g.Bv), blk, 0, st, volc, volr, U, Ur, rot, shifts,
+                       grad_rot, grad_s, g, bg, prefix);
+  ev_end(ev, st);
+  // the few pixels outside every active brick (both kernels add into the
+  // zeroed outputs, so the order is free)
   hipLaunchKernelGGL((k_grad_edge<NT, C, R>), edge_grid(g), blk, 0, st, volc, volr, U, Ur, rot, shifts, grad_rot,
                      grad_s, g, bg);
-  ev_begin(ev, st);   // recorded even when no brick kernel runs
-  if (bg.nwork == 0) {
-    ev_end(ev, st);
-    return;
-  }
-  hipLaunchKernelGGL((k_grad_brick<NT, C, R>), dim3(bg.nwork, g.Bv), blk, 0, st, volc, volr, U, Ur, rot, shifts,
-                     grad_rot, grad_s, g, bg, prefix);
-  ev_end(ev, st);
 }
 
 hipError_t launch_grad_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* volc,

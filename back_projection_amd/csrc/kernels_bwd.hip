@@ -527,7 +527,7 @@ size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights) {
 
 hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* workspace, const float2* Y,
                       const float* Wimg, const float* rot, const float* shifts, float2* vol, float* wvol,
-                      hipStream_t st, const EvPair* ev_brick, const EvPair* ev_fold) {
+                      hipStream_t st, const EvPair* ev_brick, const EvPair* ev_fold, hipEvent_t after_bands) {
   const bool weights = Wimg != nullptr;
   int* prefix = (int*)workspace;
   const size_t off_b = align256((size_t)(bw.bg.nb3 + 1) * sizeof(int));
@@ -542,6 +542,7 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
   if (weights) hipLaunchKernelGGL((k_band_max<true>), dim3(nb), dim3(256), 0, st, Y, Wimg, ymax, wmax, g, bw);
   else hipLaunchKernelGGL((k_band_max<false>), dim3(nb), dim3(256), 0, st, Y, Wimg, ymax, wmax, g, bw);
   e = hipGetLastError();
+  if (e == hipSuccess && after_bands) e = hipEventRecord(after_bands, st);
   if (e != hipSuccess) return e;
   const dim3 blk(256);
   ev_begin(ev_brick, st);   // recorded even when no brick kernel runs

@@ -370,11 +370,14 @@ tp_status run_forward_real(const tp_geom* geom, const tproj::KGeom& k, const flo
 }
 
 // Back-projection of Y (and of the weight images Wimg into wvol): bricks,
-// else zeroed volumes and direct atomics.
+// else zeroed volumes and direct atomics.  fork (optional) is recorded on st
+// before the main scatter kernel.
 tp_status run_bwd(const tp_geom* geom, const tproj::KGeom& k, const float2* Y, const float* Wimg, const float* rot,
-                  const float* shifts, float2* vol, float* wvol, void* workspace, size_t ws_bytes, hipStream_t st) {
+                  const float* shifts, float2* vol, float* wvol, void* workspace, size_t ws_bytes, hipStream_t st,
+                  hipEvent_t fork = nullptr) {
   const BwdPlan pl = bwd_plan(geom, Wimg != nullptr);
   if (!pl.ok) {
+    if (fork) LAUNCH(hipEventRecord(fork, st), "stream fork");
     LAUNCH(tproj::launch_zero((float*)vol, 2 * vol_elems(geom) * geom->Bv, st), "zero volume");
     if (wvol) LAUNCH(tproj::launch_zero(wvol, vol_elems(geom) * geom->Bv, st), "zero weight volume");
     LAUNCH(tproj::launch_spread_atomic(k, geom->interp, Y, Wimg, rot, shifts, vol, wvol, st), "scatter");
@@ -384,7 +387,7 @@ tp_status run_bwd(const tp_geom* geom, const tproj::KGeom& k, const float2* Y, c
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
   const tproj::EvPair eb = kt_copy(TP_KT_BACKWARD), ef = kt_copy(TP_KT_FOLD);
   LAUNCH(tproj::launch_bwd(k, geom->interp, pl.bw, workspace, Y, Wimg, rot, shifts, vol, wvol, st,
-                           eb.a ? &eb : nullptr, ef.a ? &ef : nullptr),
+                           eb.a ? &eb : nullptr, ef.a ? &ef : nullptr, fork),
          "back-projection (bricks)");
   return TP_OK;
 }
@@ -515,18 +518,18 @@ tp_status project_3d_to_2d_backward(const tp_geom* geom, const void* grad_out, c
     std::lock_guard<std::mutex> lk(g_side_mu);
     SideStream* ss = side_stream();
     if (ss) {
-      hipError_t e = hipEventRecord(ss->fork, st);
-      if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+      // the scatter first (its brick kernel is queued ahead), the gradients
+      // from the point where its band maxima are done
+      TRY(run_bwd(geom, k, (const float2*)grad_out, nullptr, rot, shifts, (float2*)grad_vol, nullptr, workspace,
+                  ws_bytes, st, ss->fork));
+      hipError_t e = hipStreamWaitEvent(ss->s, ss->fork, 0);
       if (e != hipSuccess) return fail(TP_E_LAUNCH, "stream fork failed: %s", hipGetErrorString(e));
       const tp_status sg = run_grads(geom, k, (const float2*)vol, nullptr, (const float2*)grad_out, nullptr, rot,
                                      shifts, grad_rot, grad_shifts, ws2, n2, ss->s);
       e = hipEventRecord(ss->join, ss->s);
-      const tp_status sv = sg == TP_OK ? run_bwd(geom, k, (const float2*)grad_out, nullptr, rot, shifts,
-                                                 (float2*)grad_vol, nullptr, workspace, ws_bytes, st)
-                                       : sg;
       if (e == hipSuccess) e = hipStreamWaitEvent(st, ss->join, 0);
       if (e != hipSuccess) return fail(TP_E_LAUNCH, "stream join failed: %s", hipGetErrorString(e));
-      if (sv != TP_OK) return sv;
+      if (sg != TP_OK) return sg;
       return ok();
     }
   }

@@ -43,9 +43,15 @@ FP32_VECTOR_TFLOPS = 157.3
 # A figure is valid only for the kernel sources it was taken on: it is
 # reported when the digest of back_projection_amd/csrc matches, else null.
 TRAFFIC = {
-    # profiles/k_bwd_brick_D128_cubic_hbm_traffic.txt
-    "backward": {"sources_sha256": "5b18a80e25c0166ca98a78779f2be1092a2f837bf09ac88d1434da2e46095682",
-                 "fetch_bytes": 3065248278, "write_bytes": 485664224},
+    # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
+    "forward": {"sources_sha256": "de048524bc47bcfcdcbaa1769a7f783141050f666d2ffdd2234f488399d09c7f",
+               "fetch_bytes": 345731985, "write_bytes": 1183323861},
+    "backward": {"sources_sha256": "de048524bc47bcfcdcbaa1769a7f783141050f666d2ffdd2234f488399d09c7f",
+                "fetch_bytes": 2865916062, "write_bytes": 188940288},
+    "gradient": {"sources_sha256": "de048524bc47bcfcdcbaa1769a7f783141050f666d2ffdd2234f488399d09c7f",
+                "fetch_bytes": 2804751586, "write_bytes": 120317152},
+    "fold": {"sources_sha256": "de048524bc47bcfcdcbaa1769a7f783141050f666d2ffdd2234f488399d09c7f",
+            "fetch_bytes": 292752890, "write_bytes": 8519680},
 }
 
 
@@ -296,6 +302,29 @@ def main():
             **m,
         }
         eprint(f"[bench] kernel {k}: {kernels[k]}")
+    # The scatter and the gradient kernel share the GPU during the step (two
+    # streams); their live durations above include that sharing.  For
+    # reference, each alone (untimed region, same inputs):
+    isolated = {}
+    for k, call in (("backward", lambda: bp.project_3d_to_2d_backward(
+            tg, tv, tr, ts, interp="cubic", radius_cutoff=r, grad_vol=gv, need_rot=False, need_shifts=False)),
+                    ("gradient", lambda: bp.project_3d_to_2d_backward(
+            tg, tv, tr, ts, interp="cubic", radius_cutoff=r, grad_rot=gr, grad_shifts=gs, need_vol=False))):
+        call()
+        torch.cuda.synchronize()
+        for kk in bp.KERNEL_CLASSES:
+            bp.timing_read(kk)
+        bp.timing_enable(True)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        bp.timing_enable(False)
+        tot, n = bp.timing_read(k)
+        for kk in bp.KERNEL_CLASSES:
+            bp.timing_read(kk)
+        if n:
+            isolated[k] = tot / n
+            eprint(f"[bench] kernel {k} alone: {tot / n:.4f} ms")
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
     kd = kernels[dom]
     achieved = kd["tap_bytes"] / (kd["avg_ms"] * 1e-3) / 1e9
@@ -312,6 +341,12 @@ def main():
         "lds": {"achieved": round(achieved, 1), "peak": round(LDS_PEAK_GBS, 1), "unit": "GB/s",
                 "frac": kd["lds_frac"]},
     }
+    if dom in isolated:
+        a_iso = kd["tap_bytes"] / (isolated[dom] * 1e-3) / 1e9
+        roofline["overlap"] = ("runs beside the other backward kernel on a second stream; achieved uses "
+                               "its live duration in the step")
+        roofline["alone"] = {"avg_ms": round(isolated[dom], 4), "achieved": round(a_iso, 1),
+                             "frac": round(a_iso / L2_PEAK_GBS, 4)}
 
     details = {"kernels": kernels, "ms_per_step": ms_per_step}
     cpu = None
