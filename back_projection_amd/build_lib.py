@@ -1,4 +1,5 @@
-"""Build libtproj.so (gfx950) in-tree with hipcc."""
+"""Build libtproj.so (gfx950) in-tree with hipcc, and the measurement probes
+(libtproj_probes.so, bench.py --peaks)."""
 from __future__ import annotations
 
 import glob
@@ -10,6 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtproj.so")
+PROBES_SRC = os.path.join(PKG, "probes", "probes.hip")
+PROBES_LIB = os.path.join(PKG, "libtproj_probes.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -23,10 +26,10 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose: bool = False) -> str:
+def _hipcc(srcs, out, verbose):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *sources(), "-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -36,8 +39,13 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs:
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    _hipcc([PROBES_SRC], PROBES_LIB, verbose)
+    return _hipcc(sources(), LIB, verbose)
 
 
 if __name__ == "__main__":

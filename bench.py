@@ -84,6 +84,57 @@ def copy_calibration(torch, gib=1):
     eprint(f"[bench] copied {gib} GiB three times ({n * 4} bytes read and written per copy)")
 
 
+def measure_peaks(torch):
+    """The bandwidths the rooflines rest on, measured on this GPU with
+    libtproj_probes.so (include/tproj_probes.h): HBM stream read, 8-byte
+    gathers from a cache-resident buffer, and LDS 4x4x4 tap reads / 64-bit
+    atomics under three bank-key regimes.  Printed to stderr as one JSON
+    object; nothing here runs in the default benchmark."""
+    from back_projection_amd import build_lib
+    P = ctypes.CDLL(build_lib.PROBES_LIB)
+    vp = ctypes.c_void_p
+    P.tpp_stream_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
+    P.tpp_l2_gather.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp]
+    P.tpp_lds_taps.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    blocks = 8192
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def timed(call, reps=5):
+        rc = call()
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed ({rc})")
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3   # seconds per call
+
+    out = {"clock_GHz_assumed": 2.4, "cus": 256}
+    big = torch.empty(1 << 32, dtype=torch.uint8, device="cuda:0")     # 4 GiB
+    big.fill_(1)
+    t = timed(lambda: P.tpp_stream_read(vp(big.data_ptr()), big.numel(), vp(sink.data_ptr()), blocks, st))
+    out["hbm_stream_read_GBps"] = round(big.numel() / t / 1e9, 1)
+    del big
+    for log2, name in ((18, "gather_2MiB_GBps"), (21, "gather_16MiB_GBps"), (24, "gather_128MiB_GBps")):
+        buf = torch.zeros(2 << log2, dtype=torch.float32, device="cuda:0")
+        iters = 64
+        t = timed(lambda: P.tpp_l2_gather(vp(buf.data_ptr()), log2, vp(sink.data_ptr()), iters, blocks, st))
+        out[name] = round(blocks * 256 * iters * 128 / t / 1e9, 1)
+    clk = 256 * 2.4e9
+    for atomic in (0, 1):
+        for mode, name in ((0, "random"), (1, "rank_permuted"), (2, "conflict_free")):
+            iters = 64
+            t = timed(lambda: P.tpp_lds_taps(vp(sink.data_ptr()), mode, atomic, iters, blocks, st))
+            key = ("lds_atomic_" if atomic else "lds_read_") + name + "_taps_per_clk_cu"
+            out[key] = round(blocks * 256 * iters * 64 / t / clk, 2)
+    eprint("[bench] peaks " + json.dumps(out))
+    return out
+
+
 def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -201,12 +252,13 @@ def run_workload_ops(cfg, steps, warmup, bp, workloads, torch, details):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-sample", type=int, default=16384, help="poses of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-workloads", action="store_true", help="also time the other four workloads (stderr)")
     ap.add_argument("--details", default=None, help="write per-kernel details as JSON to this file")
+    ap.add_argument("--peaks", action="store_true", help="measure HBM and L2-resident bandwidths and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale factor of the HBM traffic counters)")
     ap.add_argument("--sources-digest", action="store_true", help="print the digest of the kernel sources and exit")
@@ -232,6 +284,9 @@ def main():
     bp.lib()   # fail loudly if the HIP library is missing
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.peaks:
+        measure_peaks(torch)
         return
     dev = torch.device("cuda:0")
     t0 = time.perf_counter()

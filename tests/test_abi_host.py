@@ -44,6 +44,23 @@ def test_library_exports_every_header_symbol(L):
         assert hasattr(L, f)
 
 
+def test_probe_library_exports_its_header():
+    """libtproj_probes.so (bench.py --peaks) exports what include/tproj_probes.h declares."""
+    if not os.path.exists(build_lib.PROBES_LIB):
+        build_lib.build()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "tproj_probes.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"^int\s+([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)))
+    assert declared == ["tpp_l2_gather", "tpp_lds_taps", "tpp_stream_read"]
+    out = subprocess.run(["nm", "-D", "--defined-only", build_lib.PROBES_LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    assert set(declared) <= exported
+    P = ctypes.CDLL(build_lib.PROBES_LIB)
+    P.tpp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert P.tpp_stream_read(None, 16, None, 1, None) == -1        # rejected on the host, nothing launched
+    assert P.tpp_stream_read(ctypes.c_void_p(0x10000), 24, ctypes.c_void_p(0x10000), 1, None) == -1
+
+
 def test_abi_version_and_strings(L):
     assert L.tp_abi_version() == 1
     for s in range(7):
