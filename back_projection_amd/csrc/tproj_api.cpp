@@ -154,7 +154,7 @@ tproj::EvPair kt_copy(int cls) {
 
 // items: work items aimed at (the pixel load split evenly); min_px: least
 // pixels per item, so that small problems do not drown in per-item costs.
-GatherPlan gather_plan(const tp_geom* g, int64_t items = 4096, int64_t min_px = 2048, int S = 0) {
+GatherPlan gather_plan(const tp_geom* g, int64_t items = 8192, int64_t min_px = 2048, int S = 0) {
   GatherPlan pl;
   if (force_direct()) return pl;
   // the brick enumeration packs kx <= H/2 into 11 bits and one image row's
