@@ -16,7 +16,9 @@
 // all its preimages in tap space (direct copies, and conjugated Friedel mates)
 // in a fixed order.  Float atomics in LDS are slow on this GPU while 64-bit
 // integer ones are not, so the tile holds fixed-point words (re + im * 2^32,
-// one ds_add_u64 per tap).  Taps are accumulated in windows of up to 16 poses
+// one ds_add_u64 per tap; the weight channel, in a launch of its own so that
+// each launch holds one tile, one 32-bit word).  Taps are accumulated in
+// windows of up to 16 poses
 // whose scale is set, before the window, from per-image maxima in radial
 // bands of |k| and a bound on the contributions a voxel can receive; no sum
 // can overflow, and integer sums make the result deterministic.
@@ -36,9 +38,9 @@ namespace {
 #endif
 // Tile edge of the back-projection bricks: brick edge S = TE - NT + 1 plus the
 // interpolation halo.  16^3 tiles use padded strides like the gather tile;
-// 14^3 tiles (unpadded, S = 11 cubic) fit three fused workgroups per CU in
-// LDS but measured slower (more hits per pixel, and the register budget of
-// three waves per SIMD spills).
+// 14^3 tiles (unpadded, S = 11 cubic) hold more workgroups per CU in LDS
+// but measured slower in a kernel that also gathered the volume (more hits per
+// pixel, and spills at the higher occupancy).
 constexpr int TE = BWD_EDGE;
 constexpr int TSY = TE == 16 ? 17 : TE;
 constexpr int TSZ = TE == 16 ? 16 * 17 + 4 : TE * TE;
@@ -186,55 +188,58 @@ __global__ void __launch_bounds__(256) k_band_max(const float2* __restrict__ Y, 
 #define BWD_UNROLL 2
 #endif
 #ifndef BWD_MIN_WAVES
-#define BWD_MIN_WAVES 4   // wavefronts per SIMD without the weight tile (its LDS allows two with it)
+#define BWD_MIN_WAVES 4   // wavefronts per SIMD for the data channel (127 VGPRs, 40 KB LDS)
+#endif
+#ifndef BWD_MIN_WAVES_W
+#define BWD_MIN_WAVES_W 4   // for the weight channel (107 VGPRs; five would spill)
 #endif
 
+// The channels of the brick kernel: the complex data (conj(phi) Y into a
+// fixed-point pair per tap) or the real weights (Wimg into one fixed-point
+// word per tap).  A call with weights runs one launch per channel, so that
+// each holds one tile in LDS.
+constexpr int CH_DATA = 1, CH_WEIGHTS = 2;
+
 // One pixel, in the lane the bank-spreading permutation gave it: pk packs
-// (active, l) with l = floor(p) - lo; f holds the fractional parts of p.  Adds
-// c = conj(phi) Y (and the weight image value) with the taps' weights to the
-// accumulator tiles.
-template <int NT, bool WEIGHTS>
-__device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz, float2 c, float wimg,
-                                            unsigned long long* acc_t, unsigned int* acc_w, float scale,
-                                            float wscale) {
+// (active, l) with l = floor(p) - lo; f holds the fractional parts of p; v is
+// c = conj(phi) Y (data) or (Wimg, 0) (weights).  Adds v with the taps'
+// weights to the accumulator tile.
+template <int NT, int CH>
+__device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz, float2 v,
+                                            unsigned long long* acc_t, unsigned int* acc_w, float scale) {
   if (!(pk & 1)) return;
   const int l[3] = {(pk >> 1) & 15, (pk >> 5) & 15, (pk >> 9) & 15};
   float wx[NT], wy[NT], wz[NT];
   axis_weights<NT>(fx, wx);
   axis_weights<NT>(fy, wy);
   axis_weights<NT>(fz, wz);
-  const float cr = c.x * scale, ci = c.y * scale;
-  const float wv = WEIGHTS ? wimg * wscale : 0.f;
+  const float cr = v.x * scale, ci = v.y * scale;
 #pragma unroll
   for (int jc = 0; jc < NT; ++jc)
 #pragma unroll
     for (int jb = 0; jb < NT; ++jb) {
       const float wyz = wy[jb] * wz[jc];
-      const float ur = wyz * cr, ui = wyz * ci, uw = wyz * wv;
+      const float ur = wyz * cr, ui = wyz * ci;
       const int rowb = (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
 #pragma unroll
       for (int ja = 0; ja < NT; ++ja) {
-        atomicAdd(&acc_t[rowb + ja], fixed_pair(wx[ja], ur, ui));
-        if constexpr (WEIGHTS) atomicAdd(&acc_w[rowb + ja], (unsigned int)fixed_round(wx[ja], uw));
+        if constexpr (CH == CH_DATA) atomicAdd(&acc_t[rowb + ja], fixed_pair(wx[ja], ur, ui));
+        else atomicAdd(&acc_w[rowb + ja], (unsigned int)fixed_round(wx[ja], ur));
       }
     }
 }
 
-template <int NT, bool WEIGHTS>
-__global__ void __launch_bounds__(BTHREADS, WEIGHTS ? 2 : BWD_MIN_WAVES) k_bwd_brick(const float2* __restrict__ Y,
-                                                                      const float* __restrict__ Wimg,
-                                                                      const float* __restrict__ rot,
-                                                                      const float* __restrict__ shifts,
-                                                                      float2* __restrict__ part_c,
-                                                                      float* __restrict__ part_w, KGeom g,
-                                                                      BwdGrid bw, const int* __restrict__ prefix,
-                                                                      const float* __restrict__ ymax,
-                                                                      const float* __restrict__ wmax) {
+template <int NT, int CH>
+__global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_MIN_WAVES_W)
+    k_bwd_brick(const float2* __restrict__ Y, const float* __restrict__ Wimg, const float* __restrict__ rot,
+                const float* __restrict__ shifts, float2* __restrict__ part_c, float* __restrict__ part_w, KGeom g,
+                BwdGrid bw, const int* __restrict__ prefix, const float* __restrict__ vmax) {
+  constexpr bool DATA = CH == CH_DATA;
   const BrickGrid& bg = bw.bg;
-  __shared__ unsigned long long acc_t[TSIZE];
-  __shared__ unsigned int acc_w[WEIGHTS ? TSIZE : 1];
+  __shared__ unsigned long long acc_t[DATA ? TSIZE : 1];
+  __shared__ unsigned int acc_w[DATA ? 1 : TSIZE];
   __shared__ EnumShared<WINDOW, BNW> es;
-  __shared__ float win_scale[2];
+  __shared__ float win_scale;
 
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
@@ -248,15 +253,11 @@ __global__ void __launch_bounds__(BTHREADS, WEIGHTS ? 2 : BWD_MIN_WAVES) k_bwd_b
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   float2 acc[PER_LANE];
-  float accw[PER_LANE];
 #pragma unroll
-  for (int i = 0; i < PER_LANE; ++i) {
-    acc[i] = make_float2(0.f, 0.f);
-    accw[i] = 0.f;
-  }
+  for (int i = 0; i < PER_LANE; ++i) acc[i] = make_float2(0.f, 0.f);
   for (int i = tid; i < TSIZE; i += BTHREADS) {
-    acc_t[i] = 0ull;
-    if constexpr (WEIGHTS) acc_w[i] = 0u;
+    if constexpr (DATA) acc_t[i] = 0ull;
+    else acc_w[i] = 0u;
   }
   __syncthreads();
 
@@ -275,92 +276,93 @@ __global__ void __launch_bounds__(BTHREADS, WEIGHTS ? 2 : BWD_MIN_WAVES) k_bwd_b
 
     for (int hb = 0; hb < nh; hb += WINDOW) {
       const int nw = min(WINDOW, nh - hb);
-      // the window's fixed-point scales, from every hit's bound on the
+      // the window's fixed-point scale, from every hit's bound on the
       // contributions to one tap and the largest value it can bring to this
       // brick (wavefront 0, one hit per lane)
-      window_setup(es, g, rot, shifts, vsel, eb, hb, nw, bl, bh, [&](bool valid, const float* R, int pose) {
-        float c = 0.f, m = 0.f, mw = 0.f;
+      window_setup(es, g, rot, DATA ? shifts : nullptr, vsel, eb, hb, nw, bl, bh,
+                   [&](bool valid, const float* R, int pose) {
+        float c = 0.f, m = 0.f;
         if (valid) {
           c = contrib_bound<NT>(g, R);
-          m = box_band_max(g, bw, R, ymax, pose, bl, bh);
-          if constexpr (WEIGHTS) mw = box_band_max(g, bw, R, wmax, pose, bl, bh);
+          m = box_band_max(g, bw, R, vmax, pose, bl, bh);
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
           c += __shfl_xor(c, off, 64);
           m = fmaxf(m, __shfl_xor(m, off, 64));
-          if constexpr (WEIGHTS) mw = fmaxf(mw, __shfl_xor(mw, off, 64));
         }
         if (lane == 0) {
-          // |re|, |im| <= sqrt(2) M per unit weight (the phase rotates); every
-          // contribution also stays below 2^22 for the magic rounding
+          // data: |re|, |im| <= sqrt(2) M per unit weight (the phase
+          // rotates); every contribution also stays below 2^22 for the magic
+          // rounding
           const float lim = fminf(FIX_RANGE - c, 0.99f * 4194304.0f * c);
-          win_scale[0] = m > 0.f ? lim / (1.41421356f * m * c) : 0.f;
-          win_scale[1] = (WEIGHTS && mw > 0.f) ? lim / (mw * c) : 0.f;
+          win_scale = m > 0.f ? lim / ((DATA ? 1.41421356f : 1.0f) * m * c) : 0.f;
         }
       });
-      const float scale = win_scale[0], wscale = win_scale[1];
+      const float scale = win_scale;
       const int nrows = es.hrow[nw];
       for (int qb = 0; qb < nrows;) {
         int nr;
         const int ncand = row_stage(es, g, qb, nrows, nw, bl, bh, nr);
         for (int c0 = wave * 64; c0 < ncand; c0 += BWD_UNROLL * BTHREADS) {   // wave-uniform (lane permutes)
           constexpr int U = BWD_UNROLL;
-          int dest[U], mpk[U];
+          int mpk[U];
           float mf[U][3];
-          float2 mc[U];
-          float mw[U];
+          float2 mv[U];
           // look up, load, move each pixel to its bank-spreading lane ...
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             Cand cu;
             cand_prep(es, g, c0 + u * BTHREADS + lane, ncand, lo, bg.S, cu);
-            float2 c = make_float2(0.f, 0.f);
-            float wimg = 0.f, f[3] = {0.f, 0.f, 0.f};
+            float2 v = make_float2(0.f, 0.f);
+            float f[3] = {0.f, 0.f, 0.f};
             int pk = 0, key = -1;
             if (cu.act) {
-              c = Y[cu.k];
-              if (shifts) c = cmulc(shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h), c);   // conj(phi) * Y
-              if constexpr (WEIGHTS) wimg = Wimg[cu.k];
+              if constexpr (DATA) {
+                v = Y[cu.k];
+                if (shifts) v = cmulc(shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h), v);   // conj(phi) * Y
+              } else {
+                v.x = Wimg[cu.k];
+              }
 #pragma unroll
               for (int a = 0; a < 3; ++a) f[a] = cu.p[a] - floorf(cu.p[a]);
               pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
               key = (cu.l[0] + cu.l[1] * TSY + cu.l[2] * TSZ) & 15;
             }
-            dest[u] = spread_dest(key);
-            mpk[u] = lane_send(pk, dest[u]);
+            const int dest = spread_dest(key);
+            mpk[u] = lane_send(pk, dest);
 #pragma unroll
-            for (int a = 0; a < 3; ++a) mf[u][a] = lane_send(f[a], dest[u]);
-            mc[u] = make_float2(lane_send(c.x, dest[u]), lane_send(c.y, dest[u]));
-            mw[u] = WEIGHTS ? lane_send(wimg, dest[u]) : 0.f;
+            for (int a = 0; a < 3; ++a) mf[u][a] = lane_send(f[a], dest);
+            mv[u].x = lane_send(v.x, dest);
+            mv[u].y = DATA ? lane_send(v.y, dest) : 0.f;
           }
           // ... then all the taps (nothing waits on these atomics)
 #pragma unroll
           for (int u = 0; u < U; ++u)
-            bwd_scatter<NT, WEIGHTS>(mpk[u], mf[u][0], mf[u][1], mf[u][2], mc[u], mw[u], acc_t, acc_w, scale, wscale);
+            bwd_scatter<NT, CH>(mpk[u], mf[u][0], mf[u][1], mf[u][2], mv[u], acc_t, acc_w, scale);
         }
         __syncthreads();
         qb += nr;
       }
       // ---- flush the window into the float accumulators ----
       const float inv = scale > 0.f ? 1.0f / scale : 0.f;
-      const float winv = wscale > 0.f ? 1.0f / wscale : 0.f;
 #pragma unroll
       for (int i = 0; i < PER_LANE; ++i) {
         if (TLOG % BTHREADS != 0 && tid + BTHREADS * i >= TLOG) break;
         const int pi = padded_index(tid + BTHREADS * i);
-        const unsigned long long v = acc_t[pi];
-        if (v != 0ull) {
-          float re, im;
-          unpack_fixed(v, re, im);
-          acc[i].x = fmaf(re, inv, acc[i].x);
-          acc[i].y = fmaf(im, inv, acc[i].y);
-          acc_t[pi] = 0ull;
-        }
-        if constexpr (WEIGHTS) {
+        if constexpr (DATA) {
+          const unsigned long long v = acc_t[pi];
+          if (v != 0ull) {
+            float re, im;
+            unpack_fixed(v, re, im);
+            acc[i].x = fmaf(re, inv, acc[i].x);
+            acc[i].y = fmaf(im, inv, acc[i].y);
+            acc_t[pi] = 0ull;
+          }
+        } else {
           const unsigned int u = acc_w[pi];
           if (u != 0u) {
-            accw[i] = fmaf((float)(int)u, winv, accw[i]);
+            acc[i].x = fmaf((float)(int)u, inv, acc[i].x);
             acc_w[pi] = 0u;
           }
         }
@@ -374,8 +376,8 @@ __global__ void __launch_bounds__(BTHREADS, WEIGHTS ? 2 : BWD_MIN_WAVES) k_bwd_b
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
     if (TLOG % BTHREADS != 0 && tid + BTHREADS * i >= TLOG) break;
-    part_c[slot0 + tid + BTHREADS * i] = acc[i];
-    if constexpr (WEIGHTS) part_w[slot0 + tid + BTHREADS * i] = accw[i];
+    if constexpr (DATA) part_c[slot0 + tid + BTHREADS * i] = acc[i];
+    else part_w[slot0 + tid + BTHREADS * i] = acc[i].x;
   }
 }
 
@@ -548,16 +550,19 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
   ev_begin(ev_brick, st);   // recorded even when no brick kernel runs
   if (bw.bg.nwork > 0) {
     const dim3 grid(bw.bg.nwork, g.Bv);
-#define TP_BWD(NT_, W_)                                                                                        \
-  hipLaunchKernelGGL((k_bwd_brick<NT_, W_>), grid, dim3(BTHREADS), 0, st, Y, Wimg, rot, shifts, part_c, part_w, g, \
-                     bw, prefix, ymax, wmax)
+#define TP_BWD(NT_, CH_, VMAX)                                                                              \
+  hipLaunchKernelGGL((k_bwd_brick<NT_, CH_>), grid, dim3(BTHREADS), 0, st, Y, Wimg, rot, shifts, part_c, part_w, g, \
+                     bw, prefix, VMAX)
+    // the data channel, then (with weights) the weight channel
     if (interp == 1) {
-      if (weights) TP_BWD(4, true); else TP_BWD(4, false);
+      TP_BWD(4, CH_DATA, ymax);
+      if (weights) TP_BWD(4, CH_WEIGHTS, wmax);
     } else {
-      if (weights) TP_BWD(2, true); else TP_BWD(2, false);
+      TP_BWD(2, CH_DATA, ymax);
+      if (weights) TP_BWD(2, CH_WEIGHTS, wmax);
     }
-#undef TP_BWD
     e = hipGetLastError();
+#undef TP_BWD
   }
   ev_end(ev_brick, st);
   if (e != hipSuccess) return e;
