@@ -218,6 +218,22 @@ def run_workload_ops(cfg, steps, warmup, bp, workloads, torch, details):
         n_in = in_mask_pixels(w.H, w.radius)
         res["tap_bytes"] = w.P * n_in * 64 * 12
         res["l2_frac"] = res["tap_bytes"] / (ms * 1e-3) / (L2_PEAK_GBS * 1e9)
+        # its backward (grad images, grad weights, grad rotations) for random
+        # upstream volume gradients
+        import numpy as np
+        rng = np.random.default_rng(4004)
+        gdv = torch.from_numpy(workloads.random_complex(rng, tuple(dv.shape))).to(dev)
+        gwv = torch.from_numpy(rng.standard_normal(tuple(wv.shape)).astype(np.float32)).to(dev)
+        fb = lambda: bp.backproject_2d_to_3d_backward(gdv, ti, tr, gwv, tw, None)  # noqa: E731
+        for _ in range(warmup):
+            fb()
+        ms_b, _ = time_calls(fb, steps, torch)
+        res["backproject_backward_ms"] = ms_b
+        res["backproject_backward_proj_per_s"] = w.P / (ms_b * 1e-3)
+        # gathers: grad images (8 B taps) and grad weights (4 B), then the
+        # rotation gradient over both channels (12 B)
+        res["backward_tap_bytes"] = w.P * n_in * 64 * 24
+        res["backward_l2_frac"] = res["backward_tap_bytes"] / (ms_b * 1e-3) / (L2_PEAK_GBS * 1e9)
     else:
         tv = torch.from_numpy(w.vol).to(dev)
         tr = torch.from_numpy(w.rot).to(dev)
