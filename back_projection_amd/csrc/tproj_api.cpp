@@ -280,8 +280,16 @@ std::mutex g_side_mu;
 // the cross-stream events (some tens of microseconds): measured, from about
 // 2^20 image pixels for the backward's two big kernels and 2^23 for the
 // forward's small edge kernel.
-bool worth_splitting(const tp_geom* g, int log2_pixels) {
-  return (int64_t)g->B * g->P * g->H * (g->H / 2 + 1) >= (int64_t)1 << log2_pixels;
+// A stream being captured into a graph is never split: the capture then
+// holds exactly the one-stream sequence.
+bool worth_splitting(const tp_geom* g, int log2_pixels, hipStream_t st) {
+  if ((int64_t)g->B * g->P * g->H * (g->H / 2 + 1) < (int64_t)1 << log2_pixels) return false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return cs == hipStreamCaptureStatusNone;
 }
 
 // Call with g_side_mu held.  NULL if the device has no side stream.
@@ -316,7 +324,7 @@ tp_status run_forward(const tp_geom* geom, const tproj::KGeom& k, const float2* 
   const tproj::EvPair ev = kt_copy(TP_KT_FORWARD);
   // the edge kernel on the side stream, beside the work list and the bricks
   std::lock_guard<std::mutex> lk(g_side_mu);
-  SideStream* ss = worth_splitting(geom, 23) ? side_stream() : nullptr;
+  SideStream* ss = worth_splitting(geom, 23, st) ? side_stream() : nullptr;
   hipStream_t se = st;
   if (ss) {
     hipError_t e = hipEventRecord(ss->fork, st);
@@ -517,7 +525,7 @@ tp_status project_3d_to_2d_backward(const tp_geom* geom, const void* grad_out, c
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
   const bool grads = grad_rot || grad_shifts;
-  if (grad_vol && grads && worth_splitting(geom, 20)) {
+  if (grad_vol && grads && worth_splitting(geom, 20, st)) {
     // gradients on the side stream (workspace after the scatter's part),
     // the scatter on the caller's stream, then the caller's stream waits
     const size_t off = align_up(bwd_plan(geom, false).ws_bytes);
