@@ -46,7 +46,7 @@ struct EnumShared {
   int hpose[WIN];                  // image index b * P + n
   int hrow[WIN + 1];               // first row of each hit; hrow[nw] = rows of the window
   int hky[WIN];                    // ky of each hit's first row
-  int rstart[ROWS];                // first candidate of row r
+  unsigned short rstart[ROWS];     // first candidate of row r (< EB_CMAX)
   int rinfo[ROWS];                 // kx0 | (ky & 0xfff) << 11 | hit << 23
   RowIndex crow[EB_CMAX];          // row of candidate i
 };

@@ -138,8 +138,14 @@ __device__ __forceinline__ float box_band_max(const KGeom& g, const BwdGrid& bw,
   int b0 = (int)fmaxf(0.f, kmin * bw.inv_band_w);
   if (!(kmin == kmin)) b0 = 0;
   const int b1 = (kmax * bw.inv_band_w < (float)bw.nbands) ? (int)(kmax * bw.inv_band_w) : bw.nbands - 1;
+  // the first 16 bands of the range as independent loads (one memory round
+  // trip instead of one per band); longer ranges finish in a loop
+  const float* t = table + pose * bw.nbands;
   float m = 0.f;
-  for (int i = b0; i <= b1; ++i) m = fmaxf(m, table[pose * bw.nbands + i]);
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (b0 + j <= b1) m = fmaxf(m, t[b0 + j]);
+  for (int i = b0 + 16; i <= b1; ++i) m = fmaxf(m, t[i]);
   return m;
 }
 
@@ -240,6 +246,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
   __shared__ unsigned int acc_w[DATA ? 1 : TSIZE];
   __shared__ EnumShared<WINDOW, BNW> es;
   __shared__ float win_scale;
+  __shared__ float hit_m[BTHREADS];   // per hit of the pass (by rank): its largest value in this brick
 
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
@@ -265,14 +272,24 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
   for (int64_t eb = e0; eb < e1; eb += BTHREADS) {
     // ---- hit detection: one pose per thread (degenerate maps go to the edge kernel) ----
     bool hit = false;
+    float mh = 0.f;
     const int64_t e = eb + tid;
     if (e < e1) {
       int bimg, n;
       list_entry(g, vsel, (int)e, bimg, n);
       const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
       hit = pose_ok(contrib_bound<NT>(g, R)) && slice_meets_box(g, R, bl, bh);
+      // the band maxima of a hit are looked up here, for the whole pass at
+      // once, rather than on the window set-up's serial path
+      if (hit) mh = box_band_max(g, bw, R, vmax, bimg * g.P + n, bl, bh);
     }
     const int nh = compact_hits(es, hit);
+    if (hit) {
+      int rank = __popcll(es.hitmask[wave] & ((1ull << lane) - 1ull));
+      for (int v = 0; v < wave; ++v) rank += __popcll(es.hitmask[v]);
+      hit_m[rank] = mh;
+    }
+    __syncthreads();
 
     for (int hb = 0; hb < nh; hb += WINDOW) {
       const int nw = min(WINDOW, nh - hb);
@@ -284,7 +301,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
         float c = 0.f, m = 0.f;
         if (valid) {
           c = contrib_bound<NT>(g, R);
-          m = box_band_max(g, bw, R, vmax, pose, bl, bh);
+          m = hit_m[hb + lane];
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
