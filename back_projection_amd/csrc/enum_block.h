@@ -227,22 +227,33 @@ __device__ __forceinline__ int row_stage(EnumShared<WIN, NW>& es, const KGeom& g
   const int v = wave_scan_incl(cnt);
   if (lane == 63) es.wtot[wave] = v;
   __syncthreads();
-  int carry = 0;
+  int carry = 0, total = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w)
-    if (w < wave) carry += es.wtot[w];
+  for (int w = 0; w < NW; ++w) {
+    const int t = es.wtot[w];
+    if (w < wave) carry += t;
+    total += t;
+  }
   const int incl = carry + v, start = incl - cnt;
   // the rows whose candidates fit the table: a prefix of the rows, since the
-  // inclusive counts grow
+  // inclusive counts grow (usually all of them: then every thread knows the
+  // stage's counts without another round through LDS)
+  const bool all = total <= EB_CMAX;   // block-uniform
   const bool take = q < nrows && incl <= EB_CMAX;
-  const unsigned long long tm = __ballot(take);
-  if (lane == 0) es.wave_n[wave] = __popcll(tm);
+  if (!all) {
+    const unsigned long long tm = __ballot(take);
+    if (lane == 0) es.wave_n[wave] = __popcll(tm);
+  }
   if (take) {
     es.rstart[tid] = start;
     es.rinfo[tid] = kx0 | ((ky & 0xfff) << 11) | (h << 23);
     for (int j = 0; j < cnt; ++j) es.crow[start + j] = (typename EnumShared<WIN, NW>::RowIndex)tid;
   }
   __syncthreads();
+  if (all) {
+    nr = min(NW * 64, nrows - qb);
+    return total;
+  }
   int n_taken = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) n_taken += es.wave_n[w];
