@@ -18,7 +18,7 @@
 // integer ones are not, so the tile holds fixed-point words (re + im * 2^32,
 // one ds_add_u64 per tap; the weight channel, in a launch of its own so that
 // each launch holds one tile, one 32-bit word).  Taps are accumulated in
-// windows of up to 16 poses
+// windows of up to 32 poses
 // whose scale is set, before the window, from per-image maxima in radial
 // bands of |k| and a bound on the contributions a voxel can receive; no sum
 // can overflow, and integer sums make the result deterministic.
@@ -52,7 +52,7 @@ constexpr int TLOG = TE * TE * TE;         // logical entries
 constexpr int BNW = BWD_NW;                 // wavefronts per workgroup of the brick kernel
 constexpr int BTHREADS = BNW * 64;
 constexpr int PER_LANE = (TLOG + BTHREADS - 1) / BTHREADS;   // partial-tile entries per thread
-constexpr int WINDOW = 16;                 // poses per fixed-point window
+constexpr int WINDOW = 32;                 // poses per fixed-point window
 constexpr float FIX_RANGE = 0.9f * 2147483648.0f;
 constexpr int MAX_BANDS = 128;
 
@@ -110,6 +110,38 @@ __device__ __forceinline__ float contrib_bound(const KGeom& g, const float* R) {
   const float c = 2.f * a + 1.f;
   return c * c;                              // NaN map -> NaN
 }
+// Bound on the sum of |weights| one voxel receives from all pixels of one
+// pose: |w| = |K(d_x) K(d_y) K(d_z)| <= |K(d_i)| |K(d_j)| for any two axes
+// i, j, and the pixels' (d_i, d_j) form the lattice M Z^2 + shift, with M the
+// rows i, j of A = o [R_:0 R_:1].  Over each unit cell of the (d_i, d_j)
+// plane, |K| |K| is at most the product of the kernel's largest |value| over
+// the two unit intervals (summed over the cells: (2 + 2 * 0.0742)^2 for the
+// cubic kernel, whose side lobes reach 0.0741 at |t| = 4/3; 2^2 for the linear
+// one), and a half-open unit cell holds at most (floor(w_1) + 1)(floor(w_2) +
+// 1) lattice points, w_r being the sum of |row r of M^-1| (the range of pixel
+// coordinate r over the cell).  The best of the three axis pairs is taken.
+// About 18.5 for a rotation (the pixel count bound below gives 63).
+template <int NT>
+__device__ __forceinline__ float weight_sum_bound(const KGeom& g, const float* R) {
+  constexpr float CELLS = NT == 4 ? 4.6152f : 4.0f;   // (2 + 2 * 0.0742)^2 rounded up; 2^2
+  float a0[3], a1[3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) { a0[a] = g.o * R[3 * a]; a1[a] = g.o * R[3 * a + 1]; }
+  float best = 3.0e38f;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const int i = q == 2 ? 1 : 0, j = q == 0 ? 1 : 2;
+    const float d = fabsf(a0[i] * a1[j] - a1[i] * a0[j]);
+    if (d > 1e-6f * (fabsf(a0[i]) + fabsf(a1[i])) * (fabsf(a0[j]) + fabsf(a1[j]))) {
+      // rows of M^-1 = (1/d) [[a1_j, -a1_i], [-a0_j, a0_i]]; widths rounded up
+      const float w1 = (fabsf(a1[j]) + fabsf(a1[i])) / d * 1.0001f + 1e-4f;
+      const float w2 = (fabsf(a0[j]) + fabsf(a0[i])) / d * 1.0001f + 1e-4f;
+      best = fminf(best, (floorf(w1) + 1.0f) * (floorf(w2) + 1.0f));
+    }
+  }
+  return CELLS * best;   // 3e38 * CELLS -> inf for a rank-deficient map
+}
+
 // Poses with a larger bound (degenerate maps) go to the edge kernel.
 __device__ __forceinline__ bool pose_ok(float cb) { return cb <= 4096.0f; }
 
@@ -246,7 +278,6 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
   __shared__ unsigned int acc_w[DATA ? 1 : TSIZE];
   __shared__ EnumShared<WINDOW, BNW> es;
   __shared__ float win_scale;
-  __shared__ float hit_m[BTHREADS];   // per hit of the pass (by rank): its largest value in this brick
 
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
@@ -272,24 +303,14 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
   for (int64_t eb = e0; eb < e1; eb += BTHREADS) {
     // ---- hit detection: one pose per thread (degenerate maps go to the edge kernel) ----
     bool hit = false;
-    float mh = 0.f;
     const int64_t e = eb + tid;
     if (e < e1) {
       int bimg, n;
       list_entry(g, vsel, (int)e, bimg, n);
       const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
       hit = pose_ok(contrib_bound<NT>(g, R)) && slice_meets_box(g, R, bl, bh);
-      // the band maxima of a hit are looked up here, for the whole pass at
-      // once, rather than on the window set-up's serial path
-      if (hit) mh = box_band_max(g, bw, R, vmax, bimg * g.P + n, bl, bh);
     }
     const int nh = compact_hits(es, hit);
-    if (hit) {
-      int rank = __popcll(es.hitmask[wave] & ((1ull << lane) - 1ull));
-      for (int v = 0; v < wave; ++v) rank += __popcll(es.hitmask[v]);
-      hit_m[rank] = mh;
-    }
-    __syncthreads();
 
     for (int hb = 0; hb < nh; hb += WINDOW) {
       const int nw = min(WINDOW, nh - hb);
@@ -300,8 +321,8 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
                    [&](bool valid, const float* R, int pose) {
         float c = 0.f, m = 0.f;
         if (valid) {
-          c = contrib_bound<NT>(g, R);
-          m = hit_m[hb + lane];
+          c = weight_sum_bound<NT>(g, R);
+          m = box_band_max(g, bw, R, vmax, pose, bl, bh);
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -310,9 +331,11 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
         }
         if (lane == 0) {
           // data: |re|, |im| <= sqrt(2) M per unit weight (the phase
-          // rotates); every contribution also stays below 2^22 for the magic
-          // rounding
-          const float lim = fminf(FIX_RANGE - c, 0.99f * 4194304.0f * c);
+          // rotates), so no sum exceeds lim; every single contribution (weight
+          // <= 1) also stays below 2^22 for the magic rounding; the 10 %
+          // headroom of FIX_RANGE absorbs the rounding of the window's at most
+          // a few thousand contributions per tap
+          const float lim = fminf(FIX_RANGE, 0.99f * 4194304.0f * c);
           win_scale = m > 0.f ? lim / ((DATA ? 1.41421356f : 1.0f) * m * c) : 0.f;
         }
       });
