@@ -44,14 +44,14 @@ FP32_VECTOR_TFLOPS = 157.3
 # reported when the digest of back_projection_amd/csrc matches, else null.
 TRAFFIC = {
     # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
-    "forward": {"sources_sha256": "de048524bc47bcfcdcbaa1769a7f783141050f666d2ffdd2234f488399d09c7f",
-               "fetch_bytes": 345731985, "write_bytes": 1183323861},
-    "backward": {"sources_sha256": "de048524bc47bcfcdcbaa1769a7f783141050f666d2ffdd2234f488399d09c7f",
-                "fetch_bytes": 2865916062, "write_bytes": 188940288},
-    "gradient": {"sources_sha256": "de048524bc47bcfcdcbaa1769a7f783141050f666d2ffdd2234f488399d09c7f",
-                "fetch_bytes": 2804751586, "write_bytes": 120317152},
-    "fold": {"sources_sha256": "de048524bc47bcfcdcbaa1769a7f783141050f666d2ffdd2234f488399d09c7f",
-            "fetch_bytes": 292752890, "write_bytes": 8519680},
+    "forward": {"sources_sha256": "b1fefca3d2dab945b404bab588557a07dee329420a5667e55d561f5facdee938",
+               "fetch_bytes": 353983615, "write_bytes": 1183545354},
+    "backward": {"sources_sha256": "b1fefca3d2dab945b404bab588557a07dee329420a5667e55d561f5facdee938",
+                "fetch_bytes": 2943851714, "write_bytes": 200748690},
+    "gradient": {"sources_sha256": "b1fefca3d2dab945b404bab588557a07dee329420a5667e55d561f5facdee938",
+                "fetch_bytes": 2818333861, "write_bytes": 120333792},
+    "fold": {"sources_sha256": "b1fefca3d2dab945b404bab588557a07dee329420a5667e55d561f5facdee938",
+            "fetch_bytes": 292914773, "write_bytes": 8519680},
 }
 
 
