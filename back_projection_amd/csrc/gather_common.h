@@ -197,17 +197,28 @@ __device__ __forceinline__ float zero_of(float) { return 0.f; }
 __device__ __forceinline__ void fma_into(float w, float2 v, float2& a) { a.x = fmaf(w, v.x, a.x); a.y = fmaf(w, v.y, a.y); }
 __device__ __forceinline__ void fma_into(float w, float v, float& a) { a = fmaf(w, v, a); }
 
-template <int NT, typename T>
+// The brick's tile from global memory, THREADS threads: every thread's loads
+// are issued before its LDS stores, so the tile costs one memory round trip.
+template <int NT, int THREADS, typename T>
 __device__ __forceinline__ void stage_tile_t(T* tile, const T* __restrict__ V, const KGeom& g, const int lo[3]) {
   using Tl = Tile<NT>;
-  for (int i = threadIdx.x; i < Tl::E * Tl::E * Tl::E; i += blockDim.x) {
+  constexpr int N = Tl::E * Tl::E * Tl::E;
+  static_assert(N % THREADS == 0, "the tile is a multiple of the workgroup");
+  T v[N / THREADS];
+#pragma unroll
+  for (int k = 0; k < N / THREADS; ++k) {
+    const int i = (int)threadIdx.x + k * THREADS;
     const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
-    tile[z * Tl::SZ + y * Tl::SY + x] = tap_load(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
+    v[k] = tap_load(V, g, lo[0] - Tl::HL + x, lo[1] - Tl::HL + y, lo[2] - Tl::HL + z);
+  }
+#pragma unroll
+  for (int k = 0; k < N / THREADS; ++k) {
+    const int i = (int)threadIdx.x + k * THREADS;
+    const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
+    tile[z * Tl::SZ + y * Tl::SY + x] = v[k];
   }
 }
 
-// Value (and, with DERIV, the partial derivatives along x, y, z) of the
-// interpolant from the tile; l = floor(p) - lo.
 // Value (and, with DERIV, the partial derivatives along x, y, z) of the
 // interpolant from the tile, for the axis weights w* (and their derivatives
 // d*) of the sample; l = floor(p) - lo.

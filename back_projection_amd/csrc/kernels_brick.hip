@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
   const int lo[3] = {bg.origin + bi * bg.S, bg.origin + bj * bg.S, bg.origin + bk * bg.S};
   const float bl[3] = {(float)lo[0], (float)lo[1], (float)lo[2]};
   const float bh[3] = {(float)(lo[0] + bg.S), (float)(lo[1] + bg.S), (float)(lo[2] + bg.S)};
-  stage_tile_t<NT>(tile, vol + (int64_t)vsel * g.D * g.D * g.W, g, lo);
+  stage_tile_t<NT, FWD_NW * 64>(tile, vol + (int64_t)vsel * g.D * g.D * g.W, g, lo);
   __syncthreads();
 
   const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
@@ -224,8 +224,8 @@ __global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ v
   const float bl[3] = {(float)lo[0], (float)lo[1], (float)lo[2]};
   const float bh[3] = {(float)(lo[0] + bg.S), (float)(lo[1] + bg.S), (float)(lo[2] + bg.S)};
   const int64_t nvol = (int64_t)g.D * g.D * g.W;
-  if constexpr (CPLX) stage_tile_t<NT>(tc, volc + (int64_t)vsel * nvol, g, lo);
-  if constexpr (REAL) stage_tile_t<NT>(tr, volr + (int64_t)vsel * nvol, g, lo);
+  if constexpr (CPLX) stage_tile_t<NT, GRAD_NW * 64>(tc, volc + (int64_t)vsel * nvol, g, lo);
+  if constexpr (REAL) stage_tile_t<NT, GRAD_NW * 64>(tr, volr + (int64_t)vsel * nvol, g, lo);
   for (int i = threadIdx.x; i < GRAD_WIN * 8; i += GRAD_NW * 64) (&gw[0][0])[i] = 0.f;
   __syncthreads();
 
