@@ -200,11 +200,11 @@ __global__ void __launch_bounds__(256) k_fwd_edge(const T* __restrict__ vol, con
 // window the four wavefronts' sums go to the pose's gradient with global
 // atomics.
 // ---------------------------------------------------------------------------
-constexpr int GRAD_WIN = 32;
+constexpr int GRAD_WIN = 16;   // hits per window (with 16, the LDS and the registers allow four workgroups per CU)
 constexpr int GRAD_NW = 4;
 
 template <int NT, bool CPLX, bool REAL>
-__global__ void __launch_bounds__(256) k_grad_brick(const float2* __restrict__ volc, const float* __restrict__ volr,
+__global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(const float2* __restrict__ volc, const float* __restrict__ volr,
                                                     const float2* __restrict__ U, const float* __restrict__ Ur,
                                                     const float* __restrict__ rot, const float* __restrict__ shifts,
                                                     float* __restrict__ grad_rot, float* __restrict__ grad_s, KGeom g,
