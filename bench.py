@@ -44,14 +44,14 @@ FP32_VECTOR_TFLOPS = 157.3
 # reported when the digest of back_projection_amd/csrc matches, else null.
 TRAFFIC = {
     # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
-    "forward": {"sources_sha256": "b1fefca3d2dab945b404bab588557a07dee329420a5667e55d561f5facdee938",
-               "fetch_bytes": 353983615, "write_bytes": 1183545354},
-    "backward": {"sources_sha256": "b1fefca3d2dab945b404bab588557a07dee329420a5667e55d561f5facdee938",
-                "fetch_bytes": 2943851714, "write_bytes": 200748690},
-    "gradient": {"sources_sha256": "b1fefca3d2dab945b404bab588557a07dee329420a5667e55d561f5facdee938",
-                "fetch_bytes": 2818333861, "write_bytes": 120333792},
-    "fold": {"sources_sha256": "b1fefca3d2dab945b404bab588557a07dee329420a5667e55d561f5facdee938",
-            "fetch_bytes": 292914773, "write_bytes": 8519680},
+    "forward": {"sources_sha256": "61884ff3a2c45fcf69af7c5dd6cf711c658bc4b0a80ff98d26686e2ea0c4ceb2",
+               "fetch_bytes": 354500375, "write_bytes": 1183542517},
+    "backward": {"sources_sha256": "61884ff3a2c45fcf69af7c5dd6cf711c658bc4b0a80ff98d26686e2ea0c4ceb2",
+                "fetch_bytes": 2944344754, "write_bytes": 200748726},
+    "gradient": {"sources_sha256": "61884ff3a2c45fcf69af7c5dd6cf711c658bc4b0a80ff98d26686e2ea0c4ceb2",
+                "fetch_bytes": 2819737791, "write_bytes": 120333792},
+    "fold": {"sources_sha256": "61884ff3a2c45fcf69af7c5dd6cf711c658bc4b0a80ff98d26686e2ea0c4ceb2",
+            "fetch_bytes": 292871594, "write_bytes": 8519680},
 }
 
 
