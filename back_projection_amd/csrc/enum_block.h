@@ -341,6 +341,52 @@ __device__ __forceinline__ int spread_dest(int key) {
   return ((r & 7) << 3) | (r >> 3);
 }
 
+// ---------------------------------------------------------------------------
+// Plane-rotating lane assignment (cubic footprints of 8-byte entries).  With
+// the padded strides, tap (a, b, c) of a pixel whose first tap has key k sits
+// on bank pair (k + a + b + 4 c) mod 16.  A lane that visits the pixel's four
+// z planes in the order c = (c' + r) mod 4, c' = 0..3, moves all its banks by
+// 4 r (mod 16, as 4 * 4 = 16), so a pixel of class q = k mod 4 can use any of
+// the banks q + 4 t, t = 0..3.  A sixteen-lane group with four pixels of each
+// class is then conflict-free: its slot (q, t) (lane q * 4 + t of the group)
+// takes bank q + 4 t.  The i-th pixel of class q (i < 16) goes to group i / 4,
+// slot (q, i mod 4); the pixels beyond sixteen per class, then the inactive
+// lanes, fill the slots that classes with fewer than sixteen pixels leave
+// free (class by class, from the last group down), where the surplus costs a
+// second pass of the group.  Simulated on the pixels of random rotations:
+// 5.5 passes per wavefront access against 8.5 for the ranking above and 4
+// conflict-free.  The receiving lane gets r from plane_rotation.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int spread_dest_planes(int key) {
+  const int lane = threadIdx.x & 63;
+  const bool a = key >= 0;
+  const unsigned long long act = __ballot(a);
+  const unsigned long long b0 = __ballot(a && (key & 1)), b1 = __ballot(a && (key & 2));
+  const unsigned long long m0 = act & ~b0 & ~b1, m1 = act & b0 & ~b1, m2 = act & ~b0 & b1, m3 = act & b0 & b1;
+  const int n0 = __popcll(m0), n1 = __popcll(m1), n2 = __popcll(m2), n3 = __popcll(m3);
+  const int e0 = max(n0 - 16, 0), e1 = max(n1 - 16, 0), e2 = max(n2 - 16, 0), e3 = max(n3 - 16, 0);
+  const int q = key & 3;
+  const unsigned long long mq = q == 0 ? m0 : (q == 1 ? m1 : (q == 2 ? m2 : m3));
+  const unsigned long long below = (1ull << lane) - 1ull;
+  const int i = __popcll(mq & below);
+  if (a && i < 16) return ((i >> 2) << 4) | (q << 2) | (i & 3);
+  // ordinal among the lanes that fill free slots: surplus pixels by class,
+  // then inactive lanes
+  const int o = a ? (q > 0 ? e0 : 0) + (q > 1 ? e1 : 0) + (q > 2 ? e2 : 0) + i - 16
+                  : e0 + e1 + e2 + e3 + __popcll(~act & below);
+  // free slots: class qh, i = 15 down to n_qh
+  const int c0 = max(16 - n0, 0), c1 = c0 + max(16 - n1, 0), c2 = c1 + max(16 - n2, 0);
+  const int qh = (o >= c0) + (o >= c1) + (o >= c2);
+  const int start = qh == 0 ? 0 : (qh == 1 ? c0 : (qh == 2 ? c1 : c2));
+  const int ih = 15 - (o - start);
+  return ((ih >> 2) << 4) | (qh << 2) | (ih & 3);
+}
+
+// The plane rotation r for the pixel of first-tap key k that
+// spread_dest_planes sent to this lane: bank (k + 4 r) mod 16 = k mod 4 +
+// 4 (lane mod 4).
+__device__ __forceinline__ int plane_rotation(int key) { return ((int)(threadIdx.x & 3) - (key >> 2)) & 3; }
+
 // Send v to lane dest (each lane a distinct dest), and fetch from lane src.
 __device__ __forceinline__ int lane_send(int v, int dest) { return __builtin_amdgcn_ds_permute(dest << 2, v); }
 __device__ __forceinline__ float lane_send(float v, int dest) {

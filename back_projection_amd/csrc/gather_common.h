@@ -219,14 +219,33 @@ __device__ __forceinline__ void stage_tile_t(T* tile, const T* __restrict__ V, c
   }
 }
 
+// w[c] <- w[(c + r) mod 4], r in 0..3 (two rounds of selects).
+__device__ __forceinline__ void rotate4(float w[4], int r) {
+  float t[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) t[c] = (r & 1) ? w[(c + 1) & 3] : w[c];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) w[c] = (r & 2) ? t[(c + 2) & 3] : t[c];
+}
+
 // Value (and, with DERIV, the partial derivatives along x, y, z) of the
 // interpolant from the tile, for the axis weights w* (and their derivatives
 // d*) of the sample; l = floor(p) - lo.
+// zr (cubic only, else 0): the planes are visited in the order
+// c = (c' + zr) mod 4, c' = 0..3 (see spread_dest_planes).
 template <int NT, bool DERIV, typename T, int SY = Tile<NT>::SY, int SZ = Tile<NT>::SZ>
 __device__ __forceinline__ void interp_tile_w(const T* tile, const int l[3], const float wx[NT], const float wy[NT],
-                                              const float wz[NT], const float dx[NT], const float dy[NT],
-                                              const float dz[NT], T& I, T* dI) {
+                                              const float wz_in[NT], const float dx[NT], const float dy[NT],
+                                              const float dz_in[NT], T& I, T* dI, int zr = 0) {
+  static_assert(NT == 4 || NT == 2, "cubic or linear");
   const T* base = tile + l[2] * SZ + l[1] * SY + l[0];
+  float wz[NT], dz[NT];
+#pragma unroll
+  for (int c = 0; c < NT; ++c) { wz[c] = wz_in[c]; dz[c] = DERIV ? dz_in[c] : 0.f; }
+  if constexpr (NT == 4) {
+    rotate4(wz, zr);
+    if constexpr (DERIV) rotate4(dz, zr);
+  }
   T z0 = zero_of(T{});
   I = z0;
   if constexpr (DERIV) { dI[0] = z0; dI[1] = z0; dI[2] = z0; }
@@ -234,9 +253,10 @@ __device__ __forceinline__ void interp_tile_w(const T* tile, const int l[3], con
 #pragma unroll
   for (int c = 0; c < NT; ++c) {
     T s = z0, sx = z0, sy = z0;   // plane sums: wy*r, wy*rx, dy*r
+    const T* plane = base + (NT == 4 ? ((c + zr) & 3) : c) * SZ;
 #pragma unroll
     for (int b = 0; b < NT; ++b) {
-      const T* row = base + c * SZ + b * SY;
+      const T* row = plane + b * SY;
       T r = z0, rx = z0;
 #pragma unroll
       for (int a = 0; a < NT; ++a) {

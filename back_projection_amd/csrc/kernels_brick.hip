@@ -120,7 +120,8 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
             pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
             key = (cu.l[0] + cu.l[1] * Tl::SY + cu.l[2] * Tl::SZ) & 15;
           }
-          const int dest = spread_dest(key);
+          constexpr bool PLANES = NT == 4 && CPLX;   // plane rotation for 8-byte cubic taps
+          const int dest = PLANES ? spread_dest_planes(key) : spread_dest(key);
           const int mpk = lane_send(pk, dest);
           float mf[3];
 #pragma unroll
@@ -132,7 +133,8 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
             axis_weights<NT>(mf[0], wx);
             axis_weights<NT>(mf[1], wy);
             axis_weights<NT>(mf[2], wz);
-            interp_tile_w<NT, false>(tile, ml, wx, wy, wz, wx, wy, wz, I, (T*)nullptr);
+            const int zr = PLANES ? plane_rotation((ml[0] + ml[1] * Tl::SY + ml[2] * Tl::SZ) & 15) : 0;
+            interp_tile_w<NT, false>(tile, ml, wx, wy, wz, wx, wy, wz, I, (T*)nullptr, zr);
           }
           I = lane_fetch(I, dest);
           if (cu.act) {
@@ -256,7 +258,8 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
           }
           // the interpolation runs in the lane the bank-spreading order gives
           // the pixel; value and derivatives come back to the pixel's lane
-          const int dest = spread_dest(key);
+          constexpr bool PLANES = NT == 4 && CPLX;   // plane rotation for 8-byte cubic taps
+          const int dest = PLANES ? spread_dest_planes(key) : spread_dest(key);
           const int mpk = lane_send(pk, dest);
           float mf[3];
 #pragma unroll
@@ -272,8 +275,9 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
             axis_dweights<NT>(mf[0], dx);
             axis_dweights<NT>(mf[1], dy);
             axis_dweights<NT>(mf[2], dz);
-            if constexpr (CPLX) interp_tile_w<NT, true>(tc, ml, wx, wy, wz, dx, dy, dz, Ic, dIc);
-            if constexpr (REAL) interp_tile_w<NT, true>(tr, ml, wx, wy, wz, dx, dy, dz, Ir, dIr);
+            const int zr = PLANES ? plane_rotation((ml[0] + ml[1] * Tl::SY + ml[2] * Tl::SZ) & 15) : 0;
+            if constexpr (CPLX) interp_tile_w<NT, true>(tc, ml, wx, wy, wz, dx, dy, dz, Ic, dIc, zr);
+            if constexpr (REAL) interp_tile_w<NT, true>(tr, ml, wx, wy, wz, dx, dy, dz, Ir, dIr, zr);
           }
           float acc[8];
 #pragma unroll

@@ -242,7 +242,9 @@ constexpr int CH_DATA = 1, CH_WEIGHTS = 2;
 // (active, l) with l = floor(p) - lo; f holds the fractional parts of p; v is
 // c = conj(phi) Y (data) or (Wimg, 0) (weights).  Adds v with the taps'
 // weights to the accumulator tile.
-template <int NT, int CH>
+// With PLANES (cubic data channel, lanes from spread_dest_planes) the z
+// planes are visited in the rotated order that lane's slot asks for.
+template <int NT, int CH, bool PLANES>
 __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz, float2 v,
                                             unsigned long long* acc_t, unsigned int* acc_w, float scale) {
   if (!(pk & 1)) return;
@@ -251,6 +253,11 @@ __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz
   axis_weights<NT>(fx, wx);
   axis_weights<NT>(fy, wy);
   axis_weights<NT>(fz, wz);
+  int zr = 0;
+  if constexpr (PLANES) {
+    zr = plane_rotation((l[0] + l[1] * TSY + l[2] * TSZ) & 15);
+    rotate4(wz, zr);
+  }
   const float cr = v.x * scale, ci = v.y * scale;
 #pragma unroll
   for (int jc = 0; jc < NT; ++jc)
@@ -258,7 +265,7 @@ __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz
     for (int jb = 0; jb < NT; ++jb) {
       const float wyz = wy[jb] * wz[jc];
       const float ur = wyz * cr, ui = wyz * ci;
-      const int rowb = (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
+      const int rowb = (l[2] + (PLANES ? ((jc + zr) & 3) : jc)) * TSZ + (l[1] + jb) * TSY + l[0];
 #pragma unroll
       for (int ja = 0; ja < NT; ++ja) {
         if constexpr (CH == CH_DATA) atomicAdd(&acc_t[rowb + ja], fixed_pair(wx[ja], ur, ui));
@@ -273,6 +280,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
                 const float* __restrict__ shifts, float2* __restrict__ part_c, float* __restrict__ part_w, KGeom g,
                 BwdGrid bw, const int* __restrict__ prefix, const float* __restrict__ vmax) {
   constexpr bool DATA = CH == CH_DATA;
+  constexpr bool PLANES = DATA && NT == 4;   // plane rotation for 8-byte cubic taps
   const BrickGrid& bg = bw.bg;
   __shared__ unsigned long long acc_t[DATA ? TSIZE : 1];
   __shared__ unsigned int acc_w[DATA ? 1 : TSIZE];
@@ -369,7 +377,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
               pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
               key = (cu.l[0] + cu.l[1] * TSY + cu.l[2] * TSZ) & 15;
             }
-            const int dest = spread_dest(key);
+            const int dest = PLANES ? spread_dest_planes(key) : spread_dest(key);
             mpk[u] = lane_send(pk, dest);
 #pragma unroll
             for (int a = 0; a < 3; ++a) mf[u][a] = lane_send(f[a], dest);
@@ -379,7 +387,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
           // ... then all the taps (nothing waits on these atomics)
 #pragma unroll
           for (int u = 0; u < U; ++u)
-            bwd_scatter<NT, CH>(mpk[u], mf[u][0], mf[u][1], mf[u][2], mv[u], acc_t, acc_w, scale);
+            bwd_scatter<NT, CH, PLANES>(mpk[u], mf[u][0], mf[u][1], mf[u][2], mv[u], acc_t, acc_w, scale);
         }
         __syncthreads();
         qb += nr;
