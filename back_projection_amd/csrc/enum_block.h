@@ -358,28 +358,32 @@ __device__ __forceinline__ int spread_dest(int key) {
 // conflict-free.  The receiving lane gets r from plane_rotation.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int spread_dest_planes(int key) {
-  const int lane = threadIdx.x & 63;
   const bool a = key >= 0;
   const unsigned long long act = __ballot(a);
   const unsigned long long b0 = __ballot(a && (key & 1)), b1 = __ballot(a && (key & 2));
-  const unsigned long long m0 = act & ~b0 & ~b1, m1 = act & b0 & ~b1, m2 = act & ~b0 & b1, m3 = act & b0 & b1;
-  const int n0 = __popcll(m0), n1 = __popcll(m1), n2 = __popcll(m2), n3 = __popcll(m3);
+  const int n0 = __popcll(act & ~b0 & ~b1), n1 = __popcll(act & b0 & ~b1), n2 = __popcll(act & ~b0 & b1);
+  const int n3 = __popcll(act) - n0 - n1 - n2;
   const int e0 = max(n0 - 16, 0), e1 = max(n1 - 16, 0), e2 = max(n2 - 16, 0), e3 = max(n3 - 16, 0);
+  // lanes of this lane's class (branch-free: the two class bits select b or ~b)
   const int q = key & 3;
-  const unsigned long long mq = q == 0 ? m0 : (q == 1 ? m1 : (q == 2 ? m2 : m3));
-  const unsigned long long below = (1ull << lane) - 1ull;
-  const int i = __popcll(mq & below);
-  if (a && i < 16) return ((i >> 2) << 4) | (q << 2) | (i & 3);
+  const unsigned long long mq = act & ((q & 1) ? b0 : ~b0) & ((q & 2) ? b1 : ~b1);
+  const int i = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(mq >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)mq, 0u));
+  const int regular = ((i >> 2) << 4) | (q << 2) | (i & 3);
   // ordinal among the lanes that fill free slots: surplus pixels by class,
   // then inactive lanes
-  const int o = a ? (q > 0 ? e0 : 0) + (q > 1 ? e1 : 0) + (q > 2 ? e2 : 0) + i - 16
-                  : e0 + e1 + e2 + e3 + __popcll(~act & below);
+  const unsigned long long idle = ~act;
+  const int k_idle = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(idle >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)idle, 0u));
+  const int before = (q > 0 ? e0 : 0) + (q > 1 ? e1 : 0) + (q > 2 ? e2 : 0);
+  const int o = a ? before + i - 16 : e0 + e1 + e2 + e3 + k_idle;
   // free slots: class qh, i = 15 down to n_qh
   const int c0 = max(16 - n0, 0), c1 = c0 + max(16 - n1, 0), c2 = c1 + max(16 - n2, 0);
-  const int qh = (o >= c0) + (o >= c1) + (o >= c2);
-  const int start = qh == 0 ? 0 : (qh == 1 ? c0 : (qh == 2 ? c1 : c2));
+  int qh = 0, start = 0;
+  if (o >= c0) { qh = 1; start = c0; }
+  if (o >= c1) { qh = 2; start = c1; }
+  if (o >= c2) { qh = 3; start = c2; }
   const int ih = 15 - (o - start);
-  return ((ih >> 2) << 4) | (qh << 2) | (ih & 3);
+  const int spare = ((ih >> 2) << 4) | (qh << 2) | (ih & 3);
+  return (a && i < 16) ? regular : spare;
 }
 
 // The plane rotation r for the pixel of first-tap key k that

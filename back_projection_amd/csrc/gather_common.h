@@ -219,13 +219,17 @@ __device__ __forceinline__ void stage_tile_t(T* tile, const T* __restrict__ V, c
   }
 }
 
-// w[c] <- w[(c + r) mod 4], r in 0..3 (two rounds of selects).
+// w[c] <- w[(c + r) mod 4], r in 0..3: two rounds of bitwise blends under
+// all-ones / all-zero masks (one v_bfi each).  The masks are hidden from the
+// optimiser, which would otherwise turn the blends into a compare per value.
 __device__ __forceinline__ void rotate4(float w[4], int r) {
-  float t[4];
+  int m1 = -(r & 1), m2 = -((r >> 1) & 1);
+  asm volatile("" : "+v"(m1), "+v"(m2));
+  int t[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) t[c] = (r & 1) ? w[(c + 1) & 3] : w[c];
+  for (int c = 0; c < 4; ++c) t[c] = (m1 & __float_as_int(w[(c + 1) & 3])) | (~m1 & __float_as_int(w[c]));
 #pragma unroll
-  for (int c = 0; c < 4; ++c) w[c] = (r & 2) ? t[(c + 2) & 3] : t[c];
+  for (int c = 0; c < 4; ++c) w[c] = __int_as_float((m2 & t[(c + 2) & 3]) | (~m2 & t[c]));
 }
 
 // Value (and, with DERIV, the partial derivatives along x, y, z) of the
