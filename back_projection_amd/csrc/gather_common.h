@@ -398,11 +398,13 @@ __device__ __forceinline__ bool slice_meets_box(const KGeom& g, const float* R, 
   const float g11 = a1[0] * a1[0] + a1[1] * a1[1] + a1[2] * a1[2];
   const float det = g00 * g11 - g01 * g01;
   if (!(det > 1e-6f * g00 * g11)) return true;
+  // (the hardware reciprocal's ulp is far inside the one-pixel margins below)
+  const float rdet = __builtin_amdgcn_rcpf(det);
   float x0 = 0.f, x1 = 0.f, y0 = 0.f, y1 = 0.f;
 #pragma unroll
   for (int a = 0; a < 3; ++a) {
-    const float ux = (g11 * a0[a] - g01 * a1[a]) / det;   // kx = ux . p
-    const float uy = (g00 * a1[a] - g01 * a0[a]) / det;   // ky = uy . p
+    const float ux = (g11 * a0[a] - g01 * a1[a]) * rdet;   // kx = ux . p
+    const float uy = (g00 * a1[a] - g01 * a0[a]) * rdet;   // ky = uy . p
     x0 += fminf(ux * bl[a], ux * bh[a]); x1 += fmaxf(ux * bl[a], ux * bh[a]);
     y0 += fminf(uy * bl[a], uy * bh[a]); y1 += fmaxf(uy * bl[a], uy * bh[a]);
   }
@@ -416,7 +418,9 @@ __device__ __forceinline__ bool slice_meets_box(const KGeom& g, const float* R, 
   return true;
 }
 
-// Candidate rows of the pixels whose sample lies in the box [bl, bh).
+// Candidate rows of the pixels whose sample lies in the box [bl, bh), for a
+// map that passed slice_meets_box with this box.  Reciprocals are the
+// hardware's (an ulp or so): the row bounds carry a margin of one row.
 __device__ __forceinline__ bool slice_rows_box(const KGeom& g, const float* R, const float bl[3], const float bh[3],
                                                SliceRows& sr) {
 #pragma unroll
@@ -427,7 +431,6 @@ __device__ __forceinline__ bool slice_rows_box(const KGeom& g, const float* R, c
     sr.bl[a] = bl[a];
     sr.bh[a] = bh[a];
   }
-  if (!plane_meets_box(g, R, bl, bh)) return false;
   int lo_img = -(g.H >> 1), hi_img = (g.H >> 1) - 1;
   if (g.r2 >= 0.0f) {
     const int rr = (int)floorf(sqrtf(g.r2)) + 1;
@@ -442,10 +445,11 @@ __device__ __forceinline__ bool slice_rows_box(const KGeom& g, const float* R, c
   const float det = g00 * g11 - g01 * g01;
   if (det > 1e-6f * g00 * g11 && det == det) {
     // ky = (row 1 of the pseudo-inverse of A) . p, bounded over the box
+    const float rdet = __builtin_amdgcn_rcpf(det);
     float kmin = 0.f, kmax = 0.f;
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
-      const float u = (g00 * sr.a1[a] - g01 * sr.a0[a]) / det;
+      const float u = (g00 * sr.a1[a] - g01 * sr.a0[a]) * rdet;
       const float x = u * sr.bl[a], y = u * sr.bh[a];
       kmin += fminf(x, y);
       kmax += fmaxf(x, y);
@@ -466,7 +470,7 @@ __device__ __forceinline__ bool slice_rows_box(const KGeom& g, const float* R, c
         cond = false;
         continue;
       }
-      const float inv = 1.0f / d;
+      const float inv = __builtin_amdgcn_rcpf(d);
       const float marg = 2e-2f + 1e-4f * (fabsf(sr.bl[c]) + fabsf(sr.bh[c]));
 #pragma unroll
       for (int s = 0; s < 4; ++s) {

@@ -106,7 +106,7 @@ __device__ __forceinline__ float contrib_bound(const KGeom& g, const float* R) {
   const float d = g00 - g11;
   const float lam = 0.5f * (g00 + g11 - sqrtf(fmaf(d, d, 4.f * g01 * g01)));
   const float sig = sqrtf(fmaxf(lam, 0.f));
-  const float a = (0.8660254f * NT) / sig;   // inf for a degenerate map
+  const float a = (0.8660254f * NT) * __builtin_amdgcn_rcpf(sig);   // inf for a degenerate map
   const float c = 2.f * a + 1.f;
   return c * c;                              // NaN map -> NaN
 }
@@ -134,8 +134,10 @@ __device__ __forceinline__ float weight_sum_bound(const KGeom& g, const float* R
     const float d = fabsf(a0[i] * a1[j] - a1[i] * a0[j]);
     if (d > 1e-6f * (fabsf(a0[i]) + fabsf(a1[i])) * (fabsf(a0[j]) + fabsf(a1[j]))) {
       // rows of M^-1 = (1/d) [[a1_j, -a1_i], [-a0_j, a0_i]]; widths rounded up
-      const float w1 = (fabsf(a1[j]) + fabsf(a1[i])) / d * 1.0001f + 1e-4f;
-      const float w2 = (fabsf(a0[j]) + fabsf(a0[i])) / d * 1.0001f + 1e-4f;
+      // (the factor 1.0001 also covers the hardware reciprocal's ulp)
+      const float rd = __builtin_amdgcn_rcpf(d);
+      const float w1 = (fabsf(a1[j]) + fabsf(a1[i])) * rd * 1.0001f + 1e-4f;
+      const float w2 = (fabsf(a0[j]) + fabsf(a0[i])) * rd * 1.0001f + 1e-4f;
       best = fminf(best, (floorf(w1) + 1.0f) * (floorf(w2) + 1.0f));
     }
   }
@@ -166,7 +168,8 @@ __device__ __forceinline__ float box_band_max(const KGeom& g, const BwdGrid& bw,
     dn = fmaf(n, n, dn);
     df = fmaf(f, f, df);
   }
-  const float kmin = sqrtf(dn) / smax - 1.0f, kmax = sqrtf(df) / smin + 1.0f;
+  // (the one-pixel margins cover the hardware reciprocal's ulp)
+  const float kmin = sqrtf(dn) * __builtin_amdgcn_rcpf(smax) - 1.0f, kmax = sqrtf(df) * __builtin_amdgcn_rcpf(smin) + 1.0f;
   int b0 = (int)fmaxf(0.f, kmin * bw.inv_band_w);
   if (!(kmin == kmin)) b0 = 0;
   const int b1 = (kmax * bw.inv_band_w < (float)bw.nbands) ? (int)(kmax * bw.inv_band_w) : bw.nbands - 1;
@@ -179,6 +182,24 @@ __device__ __forceinline__ float box_band_max(const KGeom& g, const BwdGrid& bw,
     if (b0 + j <= b1) m = fmaxf(m, t[b0 + j]);
   for (int i = b0 + 16; i <= b1; ++i) m = fmaxf(m, t[i]);
   return m;
+}
+
+// c <- the sum of c over the wavefront, m <- the maximum of m (m >= 0), both
+// uniform: inclusive DPP scans (row shifts, then the row broadcasts of lanes
+// 15 and 31) leave the totals in lane 63.
+__device__ __forceinline__ void window_sum_max(float& c, float& m) {
+#define TP_SCAN_STEP(CTRL, RM)                                                      \
+  c += __int_as_float(dpp_int<CTRL, RM>(0, __float_as_int(c)));                  \
+  m = fmaxf(m, __int_as_float(dpp_int<CTRL, RM>(0, __float_as_int(m))));
+  TP_SCAN_STEP(0x111, 0xf)
+  TP_SCAN_STEP(0x112, 0xf)
+  TP_SCAN_STEP(0x114, 0xf)
+  TP_SCAN_STEP(0x118, 0xf)
+  TP_SCAN_STEP(0x142, 0xa)
+  TP_SCAN_STEP(0x143, 0xc)
+#undef TP_SCAN_STEP
+  c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
+  m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
 }
 
 __device__ __forceinline__ int floor_div(int a, int b) {  // b > 0
@@ -332,11 +353,8 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
           c = weight_sum_bound<NT>(g, R);
           m = box_band_max(g, bw, R, vmax, pose, bl, bh);
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-          c += __shfl_xor(c, off, 64);
-          m = fmaxf(m, __shfl_xor(m, off, 64));
-        }
+        // window sum of c and maximum of m (DPP scans: lane 63 ends with both)
+        window_sum_max(c, m);
         if (lane == 0) {
           // data: |re|, |im| <= sqrt(2) M per unit weight (the phase
           // rotates), so no sum exceeds lim; every single contribution (weight
