@@ -27,6 +27,7 @@ struct BrickGrid {
   int64_t target; // pixels per work item
   int dens_q8;    // 256 / o^2, pixel density in sample space (fixed point)
   int nwork;      // total work items per volume
+  int nactive;    // bricks with at least one work item
 };
 
 __host__ __device__ inline int64_t isqrt64(int64_t v) {
@@ -87,8 +88,43 @@ __host__ __device__ inline int brick_chunks(const BrickGrid& g, int bi, int bj, 
   const int64_t den = 100 * rho2 * 256 * g.target;
   int64_t k = (num + den - 1) / den;
   if (k < 1) k = 1;
+  // a chunk holds at most 65535 poses (hit lists store 16-bit offsets)
+  const int64_t kmin = ((int64_t)g.list_len + 65534) / 65535;
+  if (k < kmin) k = kmin;
   if (k > g.list_len) k = g.list_len;
   return (int)k;
+}
+
+// ---------------------------------------------------------------------------
+// Work area of a brick plan (in the caller's workspace, 256-byte aligned
+// parts): the work list -- prefix[0..nb3] of the chunk counts, then the active
+// rank of every brick (bricks with chunks before it) -- the hit count of every
+// work item and volume, and the hit lists.  The list of item (brick b, chunk
+// [e0, e1)) of volume v starts at ((v * nactive + rank(b)) * list_len + e0)
+// and holds up to e1 - e0 16-bit offsets e - e0.
+// ---------------------------------------------------------------------------
+struct BrickWork {
+  int* prefix;              // nb3 + 1 chunk prefix sums, then nb3 active ranks
+  int* counts;              // nvol * nwork hit counts
+  unsigned short* hits;     // nvol * nactive * list_len offsets
+};
+
+__host__ __device__ inline size_t bw_align256(size_t n) { return (n + 255) / 256 * 256; }
+
+inline size_t brick_work_bytes(const BrickGrid& g, int nvol) {
+  return bw_align256((size_t)(2 * g.nb3 + 1) * sizeof(int)) + bw_align256((size_t)nvol * g.nwork * sizeof(int)) +
+         bw_align256((size_t)nvol * g.nactive * g.list_len * sizeof(unsigned short));
+}
+
+inline BrickWork brick_work(const BrickGrid& g, int nvol, void* base) {
+  BrickWork w;
+  char* p = (char*)base;
+  w.prefix = (int*)p;
+  p += bw_align256((size_t)(2 * g.nb3 + 1) * sizeof(int));
+  w.counts = (int*)p;
+  p += bw_align256((size_t)nvol * g.nwork * sizeof(int));
+  w.hits = (unsigned short*)p;
+  return w;
 }
 
 }  // namespace tproj

@@ -37,7 +37,6 @@ struct EnumShared {
   static constexpr int THREADS = NW * 64;
   static constexpr int ROWS = NW * 64;
   using RowIndex = std::conditional_t<(ROWS <= 256), unsigned char, unsigned short>;
-  unsigned long long hitmask[NW];  // hit poses of this pass (bit = thread)
   int wave_n[NW];
   int wtot[NW];
   int nr, nc;                      // rows and candidates of the current row stage
@@ -51,35 +50,65 @@ struct EnumShared {
   RowIndex crow[EB_CMAX];          // row of candidate i
 };
 
-// Record the hit flags of one pass (one pose per thread); returns the hit
-// count (block-uniform).
-template <int WIN, int NW>
-__device__ __forceinline__ int compact_hits(EnumShared<WIN, NW>& es, bool hit) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const unsigned long long m = __ballot(hit);
-  if (lane == 0) es.hitmask[wave] = m;
-  __syncthreads();
-  int nh = 0;
-#pragma unroll
-  for (int v = 0; v < NW; ++v) nh += __popcll(es.hitmask[v]);
-  __syncthreads();   // every thread has read the mask before the next pass rewrites it
-  return nh;
+// ---------------------------------------------------------------------------
+// Hit lists.  Work item w of volume v is brick b with the pose chunk [e0, e1)
+// of the volume's pose list.  A pass of its own (one workgroup of 256 threads
+// per item, one pose per thread at a time) keeps the offsets e - e0 of the
+// chunk's poses that pass the hit test, in order, in the item's list, and
+// their number in counts; the brick kernels then set up windows of hits from
+// the list, skip items without hits before staging their tile, and never test
+// poses themselves.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t hit_slot(const BrickGrid& bg, const int* __restrict__ prefix, int vsel, int b,
+                                            int e0) {
+  return ((int64_t)vsel * bg.nactive + prefix[bg.nb3 + 1 + b]) * bg.list_len + e0;
 }
 
-// Thread offset (within the pass) of the j-th hit (j < the hit count).
-template <int WIN, int NW>
-__device__ __forceinline__ int nth_hit(const EnumShared<WIN, NW>& es, int j) {
-  int v = 0;
-  unsigned long long m = es.hitmask[0];
-  while (j >= __popcll(m)) {
-    j -= __popcll(m);
-    m = es.hitmask[++v];
-  }
-  int bit = 0;   // position of the j-th set bit of m
+// The chunk [e0, e1) of work item w of brick b.
+__device__ __forceinline__ void item_chunk(const BrickGrid& bg, const int* __restrict__ prefix, int b, int w, int& e0,
+                                           int& e1) {
+  const int chunk = w - prefix[b], nchunk = prefix[b + 1] - prefix[b];
+  e0 = (int)((int64_t)bg.list_len * chunk / nchunk);
+  e1 = (int)((int64_t)bg.list_len * (chunk + 1) / nchunk);
+}
+
+// Body of a hit-list kernel (grid: nwork x volumes, 256 threads).
+// test(vsel, e, bl, bh): does pose e of the list reach the box [bl, bh)?
+template <typename Test>
+__device__ __forceinline__ void build_hit_list(const BrickGrid& bg, const int* __restrict__ prefix,
+                                               unsigned short* __restrict__ hits, int* __restrict__ counts,
+                                               Test test) {
+  __shared__ int wcount[4];
+  const int w = blockIdx.x, vsel = blockIdx.y;
+  if (w >= bg.nwork) return;
+  const int b = find_brick(prefix, bg.nb3, w);
+  int bi, bj, bk, e0, e1;
+  brick_coords(bg, b, bi, bj, bk);
+  item_chunk(bg, prefix, b, w, e0, e1);
+  const int lo[3] = {bg.origin + bi * bg.S, bg.origin + bj * bg.S, bg.origin + bk * bg.S};
+  const float bl[3] = {(float)lo[0], (float)lo[1], (float)lo[2]};
+  const float bh[3] = {(float)(lo[0] + bg.S), (float)(lo[1] + bg.S), (float)(lo[2] + bg.S)};
+  unsigned short* out = hits + hit_slot(bg, prefix, vsel, b, e0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int cnt = 0;
+  for (int eb = e0; eb < e1; eb += 256) {
+    const int e = eb + tid;
+    const bool hit = e < e1 && test(vsel, e, bl, bh);
+    const unsigned long long m = __ballot(hit);
+    if (lane == 0) wcount[wave] = __popcll(m);
+    __syncthreads();
+    int before = cnt, total = cnt;
 #pragma unroll
-  for (int step = 32; step >= 1; step >>= 1)
-    if (__popcll(m & ((1ull << (bit + step)) - 1ull)) <= j) bit += step;
-  return 64 * v + bit;
+    for (int v = 0; v < 4; ++v) {
+      const int c = wcount[v];
+      if (v < wave) before += c;
+      total += c;
+    }
+    if (hit) out[before + __popcll(m & ((1ull << lane) - 1ull))] = (unsigned short)(e - e0);
+    cnt = total;
+    __syncthreads();   // every wavefront has read the counts before the next pass
+  }
+  if (tid == 0) counts[(int64_t)vsel * bg.nwork + w] = cnt;
 }
 
 // Slice coordinate from the two rotation columns; the same arithmetic as
@@ -121,15 +150,17 @@ struct NoHitHook {
   __device__ void operator()(bool, const float*, int) const {}
 };
 
-// Window set-up: threads t < nw take hit hw + t of the pass that starts at
-// list entry eb.  Writes the geometry, the image index and the row range of
-// every hit, then the row prefix.  hook(valid, R, pose) runs on every lane of
-// wavefront 0 (valid: the lane holds a hit; R: its rotation, row-major), before
-// the closing barrier, so what it writes to LDS is visible on return.
+// Window set-up: threads t < nw take the hit at list entry e0 + hl[t] (hl:
+// the window's part of the item's hit list).  Writes the geometry, the image
+// index and the row range of every hit, then the row prefix.  hook(valid, R,
+// pose) runs on every lane of wavefront 0 (valid: the lane holds a hit; R: its
+// rotation, row-major), before the closing barrier, so what it writes to LDS
+// is visible on return.
 template <int WIN, int NW, typename Hook = NoHitHook>
 __device__ __forceinline__ void window_setup(EnumShared<WIN, NW>& es, const KGeom& g, const float* __restrict__ rot,
-                                             const float* __restrict__ shifts, int vsel, int64_t eb, int hw, int nw,
-                                             const float bl[3], const float bh[3], Hook hook = Hook()) {
+                                             const float* __restrict__ shifts, int vsel, int e0,
+                                             const unsigned short* __restrict__ hl, int nw, const float bl[3],
+                                             const float bh[3], Hook hook = Hook()) {
   static_assert(WIN <= 64, "one wavefront sets up a window");
   const int tid = threadIdx.x;
   if (tid < 64) {
@@ -139,7 +170,7 @@ __device__ __forceinline__ void window_setup(EnumShared<WIN, NW>& es, const KGeo
     for (int a = 0; a < 9; ++a) R[a] = 0.f;
     if (tid < nw) {
       int bimg, n;
-      list_entry(g, vsel, (int)(eb + nth_hit(es, hw + tid)), bimg, n);
+      list_entry(g, vsel, e0 + (int)hl[tid], bimg, n);
       const float* Rg = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
 #pragma unroll
       for (int a = 0; a < 9; ++a) R[a] = Rg[a];

@@ -1,11 +1,14 @@
 // Brick-binned gather kernels of libtproj for gfx950.
 //
 // k_brick_prefix   work list: prefix sums of the pose chunks of every brick
+//                  and the bricks' active ranks
+// k_hit_lists      per work item, the poses of its chunk whose slice reaches
+//                  the brick (in order)
 // k_fwd_brick      3D->2D forward (complex volume, with the shift phase) or
 //                  its real counterpart (weight channel): a workgroup stages
 //                  one tap-space brick of the Hermitian-extended periodic
 //                  volume plus the interpolation halo in LDS, enumerates the
-//                  pixels of its pose chunk whose floor(p) falls in the brick
+//                  pixels of its hit poses whose floor(p) falls in the brick
 //                  (enum_block.h) and interpolates them from LDS, each pixel
 //                  in the lane the bank-spreading order gives it.
 // k_grad_brick     rotation / shift gradients on the same decomposition: the
@@ -30,9 +33,12 @@ namespace tproj {
 // ---------------------------------------------------------------------------
 // work list
 // ---------------------------------------------------------------------------
+// prefix[0..nb3]: running sums of the bricks' chunk counts; prefix[nb3 + 1 +
+// b]: the active rank of brick b (bricks with chunks before it).  One
+// workgroup; both sums in one 64-bit scan (chunks low, bricks high).
 __global__ void __launch_bounds__(1024) k_brick_prefix(BrickGrid bg, int* __restrict__ prefix) {
-  __shared__ int warp_tot[16];
-  __shared__ int carry;
+  __shared__ long long warp_tot[16];
+  __shared__ long long carry;
   if (threadIdx.x == 0) { carry = 0; prefix[0] = 0; }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -44,30 +50,37 @@ __global__ void __launch_bounds__(1024) k_brick_prefix(BrickGrid bg, int* __rest
       brick_coords(bg, b, bi, bj, bk);
       k = brick_chunks(bg, bi, bj, bk);
     }
-    int v = k;
+    const long long own = (long long)k + (k > 0 ? (1ll << 32) : 0ll);
+    long long v = own;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int u = __shfl_up(v, off, 64);
+      const long long u = __shfl_up(v, off, 64);
       if (lane >= off) v += u;
     }
     if (lane == 63) warp_tot[wave] = v;
     __syncthreads();
-    int before = carry;
+    long long before = carry;
     for (int w = 0; w < wave; ++w) before += warp_tot[w];
-    if (b < bg.nb3) prefix[b + 1] = before + v;
+    if (b < bg.nb3) {
+      prefix[b + 1] = (int)((before + v) & 0xffffffffll);
+      prefix[bg.nb3 + 1 + b] = (int)((before + v - own) >> 32);
+    }
     __syncthreads();
     if (threadIdx.x == 1023) carry = before + v;
     __syncthreads();
   }
 }
 
-// One pose per thread of the pass: does its slice reach the box?
-__device__ __forceinline__ bool pose_hits(const KGeom& g, const float* __restrict__ rot, int vsel, int64_t e,
-                                          int64_t e1, const float bl[3], const float bh[3]) {
-  if (e >= e1) return false;
-  int bimg, n;
-  list_entry(g, vsel, (int)e, bimg, n);
-  return slice_meets_box(g, rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n), bl, bh);
+// Hit lists of the forward and gradient bricks: does the slice of pose e
+// reach the box?
+__global__ void __launch_bounds__(256) k_hit_lists(const float* __restrict__ rot, KGeom g, BrickGrid bg,
+                                                   const int* __restrict__ prefix, unsigned short* __restrict__ hits,
+                                                   int* __restrict__ counts) {
+  build_hit_list(bg, prefix, hits, counts, [&](int vsel, int e, const float* bl, const float* bh) {
+    int bimg, n;
+    list_entry(g, vsel, e, bimg, n);
+    return slice_meets_box(g, rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n), bl, bh);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -79,15 +92,21 @@ constexpr int FWD_NW = 4;   // wavefronts per workgroup
 template <int NT, typename T>
 __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, const float* __restrict__ rot,
                                                    const float* __restrict__ shifts, T* __restrict__ out, KGeom g,
-                                                   BrickGrid bg, const int* __restrict__ prefix) {
+                                                   BrickGrid bg, const int* __restrict__ prefix,
+                                                   const unsigned short* __restrict__ hits,
+                                                   const int* __restrict__ counts) {
   using Tl = Tile<NT>;
   constexpr bool CPLX = sizeof(T) == 8;
   __shared__ T tile[Tl::SIZE];
   __shared__ EnumShared<FWD_WIN, FWD_NW> es;
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
+  const int nh = counts[(int64_t)vsel * bg.nwork + w];
+  if (nh == 0) return;   // block-uniform, before any barrier
   const int b = find_brick(prefix, bg.nb3, w);
-  const int chunk = w - prefix[b], nchunk = prefix[b + 1] - prefix[b];
+  int e0, e1;
+  item_chunk(bg, prefix, b, w, e0, e1);
+  const unsigned short* hl = hits + hit_slot(bg, prefix, vsel, b, e0);
   int bi, bj, bk;
   brick_coords(bg, b, bi, bj, bk);
   const int lo[3] = {bg.origin + bi * bg.S, bg.origin + bj * bg.S, bg.origin + bk * bg.S};
@@ -96,13 +115,11 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
   stage_tile_t<NT, FWD_NW * 64>(tile, vol + (int64_t)vsel * g.D * g.D * g.W, g, lo);
   __syncthreads();
 
-  const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int64_t eb = e0; eb < e1; eb += FWD_NW * 64) {
-    const int nh = compact_hits(es, pose_hits(g, rot, vsel, eb + threadIdx.x, e1, bl, bh));
+  {
     for (int hw = 0; hw < nh; hw += FWD_WIN) {
       const int nw = min(FWD_WIN, nh - hw);
-      window_setup(es, g, rot, CPLX ? shifts : nullptr, vsel, eb, hw, nw, bl, bh);
+      window_setup(es, g, rot, CPLX ? shifts : nullptr, vsel, e0, hl + hw, nw, bl, bh);
       const int nrows = es.hrow[nw];
       for (int qb = 0; qb < nrows;) {
         int nr;
@@ -210,7 +227,9 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
                                                     const float2* __restrict__ U, const float* __restrict__ Ur,
                                                     const float* __restrict__ rot, const float* __restrict__ shifts,
                                                     float* __restrict__ grad_rot, float* __restrict__ grad_s, KGeom g,
-                                                    BrickGrid bg, const int* __restrict__ prefix) {
+                                                    BrickGrid bg, const int* __restrict__ prefix,
+                                                    const unsigned short* __restrict__ hits,
+                                                    const int* __restrict__ counts) {
   using Tl = Tile<NT>;
   __shared__ float2 tc[CPLX ? Tl::SIZE : 1];
   __shared__ float tr[REAL ? Tl::SIZE : 1];
@@ -218,8 +237,12 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
   __shared__ float gw[GRAD_WIN][8];
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
+  const int nh = counts[(int64_t)vsel * bg.nwork + w];
+  if (nh == 0) return;   // block-uniform, before any barrier
   const int b = find_brick(prefix, bg.nb3, w);
-  const int chunk = w - prefix[b], nchunk = prefix[b + 1] - prefix[b];
+  int e0, e1;
+  item_chunk(bg, prefix, b, w, e0, e1);
+  const unsigned short* hl = hits + hit_slot(bg, prefix, vsel, b, e0);
   int bi, bj, bk;
   brick_coords(bg, b, bi, bj, bk);
   const int lo[3] = {bg.origin + bi * bg.S, bg.origin + bj * bg.S, bg.origin + bk * bg.S};
@@ -231,13 +254,11 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
   for (int i = threadIdx.x; i < GRAD_WIN * 8; i += GRAD_NW * 64) (&gw[0][0])[i] = 0.f;
   __syncthreads();
 
-  const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int64_t eb = e0; eb < e1; eb += GRAD_NW * 64) {
-    const int nh = compact_hits(es, pose_hits(g, rot, vsel, eb + threadIdx.x, e1, bl, bh));
+  {
     for (int hw = 0; hw < nh; hw += GRAD_WIN) {
       const int nw = min(GRAD_WIN, nh - hw);
-      window_setup(es, g, rot, CPLX ? shifts : nullptr, vsel, eb, hw, nw, bl, bh);
+      window_setup(es, g, rot, CPLX ? shifts : nullptr, vsel, e0, hl + hw, nw, bl, bh);
       const int nrows = es.hrow[nw];
       for (int qb = 0; qb < nrows;) {
         int nr;
@@ -387,45 +408,54 @@ static dim3 edge_grid(const KGeom& g) { return dim3(g.B * g.P < 16384 ? g.B * g.
 // The edge kernel goes to st_edge (it writes other pixels than the brick
 // kernel, so the two may run at once), the brick kernel to st.
 template <typename T>
-static hipError_t fwd_t(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const T* vol,
+static hipError_t fwd_t(const KGeom& g, int interp, const BrickGrid& bg, const BrickWork& wk, const T* vol,
                         const float* rot, const float* shifts, T* out, hipStream_t st, const EvPair* ev,
                         hipStream_t st_edge) {
   const dim3 blk(256);
   if (interp == 1) hipLaunchKernelGGL((k_fwd_edge<4, T>), edge_grid(g), blk, 0, st_edge, vol, rot, shifts, out, g, bg);
   else hipLaunchKernelGGL((k_fwd_edge<2, T>), edge_grid(g), blk, 0, st_edge, vol, rot, shifts, out, g, bg);
   hipError_t e = hipGetLastError();
+  const dim3 grid(bg.nwork, g.Bv);
+  if (e == hipSuccess && bg.nwork > 0) {
+    hipLaunchKernelGGL(k_hit_lists, grid, blk, 0, st, rot, g, bg, wk.prefix, wk.hits, wk.counts);
+    e = hipGetLastError();
+  }
   ev_begin(ev, st);   // recorded even when no brick kernel runs
   if (e != hipSuccess || bg.nwork == 0) {
     ev_end(ev, st);
     return e;
   }
-  const dim3 grid(bg.nwork, g.Bv);
-  if (interp == 1) hipLaunchKernelGGL((k_fwd_brick<4, T>), grid, blk, 0, st, vol, rot, shifts, out, g, bg, prefix);
-  else hipLaunchKernelGGL((k_fwd_brick<2, T>), grid, blk, 0, st, vol, rot, shifts, out, g, bg, prefix);
+  if (interp == 1)
+    hipLaunchKernelGGL((k_fwd_brick<4, T>), grid, blk, 0, st, vol, rot, shifts, out, g, bg, wk.prefix, wk.hits,
+                       wk.counts);
+  else
+    hipLaunchKernelGGL((k_fwd_brick<2, T>), grid, blk, 0, st, vol, rot, shifts, out, g, bg, wk.prefix, wk.hits,
+                       wk.counts);
   ev_end(ev, st);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* vol,
+hipError_t launch_fwd_brick(const KGeom& g, int interp, const BrickGrid& bg, const BrickWork& wk, const float2* vol,
                             const float* rot, const float* shifts, float2* out, hipStream_t st, const EvPair* ev,
                             hipStream_t st_edge) {
-  return fwd_t<float2>(g, interp, bg, prefix, vol, rot, shifts, out, st, ev, st_edge);
+  return fwd_t<float2>(g, interp, bg, wk, vol, rot, shifts, out, st, ev, st_edge);
 }
 
-hipError_t launch_fwd_brick_real(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix,
+hipError_t launch_fwd_brick_real(const KGeom& g, int interp, const BrickGrid& bg, const BrickWork& wk,
                                  const float* vol, const float* rot, float* out, hipStream_t st, const EvPair* ev) {
-  return fwd_t<float>(g, interp, bg, prefix, vol, rot, nullptr, out, st, ev, st);
+  return fwd_t<float>(g, interp, bg, wk, vol, rot, nullptr, out, st, ev, st);
 }
 
 template <int NT, bool C, bool R>
-static void grad_launch(const KGeom& g, const BrickGrid& bg, const int* prefix, const float2* volc, const float* volr,
-                        const float2* U, const float* Ur, const float* rot, const float* shifts, float* grad_rot,
-                        float* grad_s, hipStream_t st, const EvPair* ev) {
-  const dim3 blk(256);
+static void grad_launch(const KGeom& g, const BrickGrid& bg, const BrickWork& wk, const float2* volc,
+                        const float* volr, const float2* U, const float* Ur, const float* rot, const float* shifts,
+                        float* grad_rot, float* grad_s, hipStream_t st, const EvPair* ev) {
+  const dim3 blk(256), grid(bg.nwork, g.Bv);
+  if (bg.nwork > 0) hipLaunchKernelGGL(k_hit_lists, grid, blk, 0, st, rot, g, bg, wk.prefix, wk.hits, wk.counts);
   ev_begin(ev, st);   // recorded even when no brick kernel runs
   if (bg.nwork > 0)
-    hipLaunchKernelGGL((k_grad_brick<NT, C, R>), dim3(bg.nwork, g.Bv), blk, 0, st, volc, volr, U, Ur, rot, shifts,
-                       grad_rot, grad_s, g, bg, prefix);
+    hipLaunchKernelGGL((k_grad_brick<NT, C, R>), grid, blk, 0, st, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s,
+                       g, bg, wk.prefix, wk.hits, wk.counts);
   ev_end(ev, st);
   // the few pixels outside every active brick (both kernels add into the
   // zeroed outputs, so the order is free)
@@ -433,15 +463,15 @@ static void grad_launch(const KGeom& g, const BrickGrid& bg, const int* prefix, 
                      grad_s, g, bg);
 }
 
-hipError_t launch_grad_brick(const KGeom& g, int interp, const BrickGrid& bg, const int* prefix, const float2* volc,
+hipError_t launch_grad_brick(const KGeom& g, int interp, const BrickGrid& bg, const BrickWork& wk, const float2* volc,
                              const float* volr, const float2* U, const float* Ur, const float* rot,
                              const float* shifts, float* grad_rot, float* grad_s, hipStream_t st, const EvPair* ev) {
   const bool c = volc != nullptr, r = volr != nullptr;
-#define TP_GRAD(NT_)                                                                                                 \
-  do {                                                                                                               \
-    if (c && r) grad_launch<NT_, true, true>(g, bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st, ev);  \
-    else if (c) grad_launch<NT_, true, false>(g, bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st, ev); \
-    else if (r) grad_launch<NT_, false, true>(g, bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st, ev); \
+#define TP_GRAD(NT_)                                                                                             \
+  do {                                                                                                           \
+    if (c && r) grad_launch<NT_, true, true>(g, bg, wk, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st, ev);  \
+    else if (c) grad_launch<NT_, true, false>(g, bg, wk, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st, ev); \
+    else if (r) grad_launch<NT_, false, true>(g, bg, wk, volc, volr, U, Ur, rot, shifts, grad_rot, grad_s, st, ev); \
   } while (0)
   if (interp == 1) TP_GRAD(4); else TP_GRAD(2);
 #undef TP_GRAD

@@ -147,6 +147,20 @@ __device__ __forceinline__ float weight_sum_bound(const KGeom& g, const float* R
 // Poses with a larger bound (degenerate maps) go to the edge kernel.
 __device__ __forceinline__ bool pose_ok(float cb) { return cb <= 4096.0f; }
 
+// Hit lists of the back-projection bricks: the slice of pose e reaches the
+// box and the map is not degenerate.
+template <int NT>
+__global__ void __launch_bounds__(256) k_bwd_hit_lists(const float* __restrict__ rot, KGeom g, BrickGrid bg,
+                                                       const int* __restrict__ prefix,
+                                                       unsigned short* __restrict__ hits, int* __restrict__ counts) {
+  build_hit_list(bg, prefix, hits, counts, [&](int vsel, int e, const float* bl, const float* bh) {
+    int bimg, n;
+    list_entry(g, vsel, e, bimg, n);
+    const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+    return pose_ok(contrib_bound<NT>(g, R)) && slice_meets_box(g, R, bl, bh);
+  });
+}
+
 // Largest value a pose can put into the brick [bl, bh): the bands of the pixel
 // radii |k| in [|p| / sigma_max, |p| / sigma_min] for p in the brick.
 __device__ __forceinline__ float box_band_max(const KGeom& g, const BwdGrid& bw, const float* R,
@@ -299,7 +313,8 @@ template <int NT, int CH>
 __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_MIN_WAVES_W)
     k_bwd_brick(const float2* __restrict__ Y, const float* __restrict__ Wimg, const float* __restrict__ rot,
                 const float* __restrict__ shifts, float2* __restrict__ part_c, float* __restrict__ part_w, KGeom g,
-                BwdGrid bw, const int* __restrict__ prefix, const float* __restrict__ vmax) {
+                BwdGrid bw, const int* __restrict__ prefix, const unsigned short* __restrict__ hits,
+                const int* __restrict__ counts, const float* __restrict__ vmax) {
   constexpr bool DATA = CH == CH_DATA;
   constexpr bool PLANES = DATA && NT == 4;   // plane rotation for 8-byte cubic taps
   const BrickGrid& bg = bw.bg;
@@ -310,14 +325,28 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
 
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
+  const int nh = counts[(int64_t)vsel * bg.nwork + w];
   const int b = find_brick(prefix, bg.nb3, w);
-  const int chunk = w - prefix[b], nchunk = prefix[b + 1] - prefix[b];
+  int e0, e1;
+  item_chunk(bg, prefix, b, w, e0, e1);
+  const unsigned short* hl = hits + hit_slot(bg, prefix, vsel, b, e0);
   int bi, bj, bk;
   brick_coords(bg, b, bi, bj, bk);
   const int lo[3] = {bg.origin + bi * bg.S, bg.origin + bj * bg.S, bg.origin + bk * bg.S};
   const float bl[3] = {(float)lo[0], (float)lo[1], (float)lo[2]};
   const float bh[3] = {(float)(lo[0] + bg.S), (float)(lo[1] + bg.S), (float)(lo[2] + bg.S)};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t slot0 = ((int64_t)vsel * bg.nwork + w) * TLOG;
+  if (nh == 0) {
+    // no hits: the partial tile is zero (the fold reads every slot)
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+      if (TLOG % BTHREADS != 0 && tid + BTHREADS * i >= TLOG) break;
+      if constexpr (DATA) part_c[slot0 + tid + BTHREADS * i] = make_float2(0.f, 0.f);
+      else part_w[slot0 + tid + BTHREADS * i] = 0.f;
+    }
+    return;
+  }
 
   float2 acc[PER_LANE];
 #pragma unroll
@@ -328,25 +357,13 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
   }
   __syncthreads();
 
-  const int64_t e0 = (int64_t)bg.list_len * chunk / nchunk, e1 = (int64_t)bg.list_len * (chunk + 1) / nchunk;
-  for (int64_t eb = e0; eb < e1; eb += BTHREADS) {
-    // ---- hit detection: one pose per thread (degenerate maps go to the edge kernel) ----
-    bool hit = false;
-    const int64_t e = eb + tid;
-    if (e < e1) {
-      int bimg, n;
-      list_entry(g, vsel, (int)e, bimg, n);
-      const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
-      hit = pose_ok(contrib_bound<NT>(g, R)) && slice_meets_box(g, R, bl, bh);
-    }
-    const int nh = compact_hits(es, hit);
-
+  {
     for (int hb = 0; hb < nh; hb += WINDOW) {
       const int nw = min(WINDOW, nh - hb);
       // the window's fixed-point scale, from every hit's bound on the
       // contributions to one tap and the largest value it can bring to this
       // brick (wavefront 0, one hit per lane)
-      window_setup(es, g, rot, DATA ? shifts : nullptr, vsel, eb, hb, nw, bl, bh,
+      window_setup(es, g, rot, DATA ? shifts : nullptr, vsel, e0, hl + hb, nw, bl, bh,
                    [&](bool valid, const float* R, int pose) {
         float c = 0.f, m = 0.f;
         if (valid) {
@@ -438,7 +455,6 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
   }
 
   // ---- this work item's partial tile (tap space, logical order) ----
-  const int64_t slot0 = ((int64_t)vsel * bg.nwork + w) * TLOG;
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
     if (TLOG % BTHREADS != 0 && tid + BTHREADS * i >= TLOG) break;
@@ -587,18 +603,19 @@ static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 int bwd_brick_edge(int interp) { return TE - (interp == 1 ? 4 : 2) + 1; }
 
 size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights) {
-  const size_t prefix = align256((size_t)(bw.bg.nb3 + 1) * sizeof(int));
+  const size_t work = brick_work_bytes(bw.bg, Bv);
   const size_t bands = align256((size_t)bw.npose * bw.nbands * sizeof(float) * (weights ? 2 : 1));
   const size_t parts = (size_t)bw.bg.nwork * Bv * TLOG * (sizeof(float2) + (weights ? sizeof(float) : 0));
-  return prefix + bands + parts;
+  return work + bands + parts;
 }
 
 hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* workspace, const float2* Y,
                       const float* Wimg, const float* rot, const float* shifts, float2* vol, float* wvol,
                       hipStream_t st, const EvPair* ev_brick, const EvPair* ev_fold, hipEvent_t after_bands) {
   const bool weights = Wimg != nullptr;
-  int* prefix = (int*)workspace;
-  const size_t off_b = align256((size_t)(bw.bg.nb3 + 1) * sizeof(int));
+  const BrickWork wk = brick_work(bw.bg, g.Bv, workspace);
+  int* prefix = wk.prefix;
+  const size_t off_b = brick_work_bytes(bw.bg, g.Bv);
   float* ymax = (float*)((char*)workspace + off_b);
   float* wmax = ymax + (size_t)bw.npose * bw.nbands;
   const size_t off_p = off_b + align256((size_t)bw.npose * bw.nbands * sizeof(float) * (weights ? 2 : 1));
@@ -606,6 +623,13 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
   float* part_w = (float*)(part_c + (size_t)bw.bg.nwork * g.Bv * TLOG);
   hipError_t e = launch_brick_prefix(bw.bg, prefix, st);
   if (e != hipSuccess) return e;
+  if (bw.bg.nwork > 0) {
+    const dim3 grid(bw.bg.nwork, g.Bv);
+    if (interp == 1) hipLaunchKernelGGL((k_bwd_hit_lists<4>), grid, dim3(256), 0, st, rot, g, bw.bg, prefix, wk.hits, wk.counts);
+    else hipLaunchKernelGGL((k_bwd_hit_lists<2>), grid, dim3(256), 0, st, rot, g, bw.bg, prefix, wk.hits, wk.counts);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int nb = bw.npose < 65535 ? bw.npose : 65535;
   if (weights) hipLaunchKernelGGL((k_band_max<true>), dim3(nb), dim3(256), 0, st, Y, Wimg, ymax, wmax, g, bw);
   else hipLaunchKernelGGL((k_band_max<false>), dim3(nb), dim3(256), 0, st, Y, Wimg, ymax, wmax, g, bw);
@@ -618,7 +642,7 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
     const dim3 grid(bw.bg.nwork, g.Bv);
 #define TP_BWD(NT_, CH_, VMAX)                                                                              \
   hipLaunchKernelGGL((k_bwd_brick<NT_, CH_>), grid, dim3(BTHREADS), 0, st, Y, Wimg, rot, shifts, part_c, part_w, g, \
-                     bw, prefix, VMAX)
+                     bw, prefix, wk.hits, wk.counts, VMAX)
     // the data channel, then (with weights) the weight channel
     if (interp == 1) {
       TP_BWD(4, CH_DATA, ymax);

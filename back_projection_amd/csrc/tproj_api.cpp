@@ -117,7 +117,7 @@ int64_t pixels_in_mask(const tp_geom* g) {
 struct GatherPlan {
   bool ok = false;
   tproj::BrickGrid bg{};
-  size_t ws_bytes = 0;   // prefix table
+  size_t ws_bytes = 0;   // work area: work list, hit counts, hit lists
 };
 
 bool force_direct() {
@@ -177,15 +177,20 @@ GatherPlan gather_plan(const tp_geom* g, int64_t items = 8192, int64_t min_px = 
   bg.dens_q8 = std::max(1, (int)std::lround(256.0 / ((double)g->oversampling * g->oversampling)));
   const int64_t total = (int64_t)g->B * g->P * pixels_in_mask(g);
   bg.target = std::max<int64_t>(min_px, total / items);
-  int64_t nwork = 0;
+  int64_t nwork = 0, nactive = 0;
   for (int b = 0; b < bg.nb3; ++b) {
     int bi, bj, bk;
     tproj::brick_coords(bg, b, bi, bj, bk);
-    nwork += tproj::brick_chunks(bg, bi, bj, bk);
+    const int k = tproj::brick_chunks(bg, bi, bj, bk);
+    nwork += k;
+    nactive += k > 0;
   }
   if (nwork > INT32_MAX / 2) return pl;
   bg.nwork = (int)nwork;
-  pl.ws_bytes = ((size_t)(bg.nb3 + 1) * sizeof(int) + 255) / 256 * 256;
+  bg.nactive = (int)nactive;
+  // work list, hit counts and hit lists (16-bit offsets: every pose of the
+  // list once per active brick and volume)
+  pl.ws_bytes = tproj::brick_work_bytes(bg, g->Bv);
   pl.ok = true;
   return pl;
 }
@@ -320,7 +325,7 @@ tp_status run_forward(const tp_geom* geom, const tproj::KGeom& k, const float2* 
   }
   if (!workspace || ws_bytes < pl.ws_bytes)
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
-  int* prefix = (int*)workspace;
+  const tproj::BrickWork wk = tproj::brick_work(pl.bg, geom->Bv, workspace);
   const tproj::EvPair ev = kt_copy(TP_KT_FORWARD);
   // the edge kernel on the side stream, beside the work list and the bricks
   std::lock_guard<std::mutex> lk(g_side_mu);
@@ -333,9 +338,9 @@ tp_status run_forward(const tp_geom* geom, const tproj::KGeom& k, const float2* 
     se = ss->s;
   }
   tp_status r = TP_OK;
-  hipError_t e = tproj::launch_brick_prefix(pl.bg, prefix, st);
+  hipError_t e = tproj::launch_brick_prefix(pl.bg, wk.prefix, st);
   if (e == hipSuccess)
-    e = tproj::launch_fwd_brick(k, geom->interp, pl.bg, prefix, vol, rot, shifts, out, st, ev.a ? &ev : nullptr, se);
+    e = tproj::launch_fwd_brick(k, geom->interp, pl.bg, wk, vol, rot, shifts, out, st, ev.a ? &ev : nullptr, se);
   if (e != hipSuccess) r = fail(TP_E_LAUNCH, "project (bricks): %s", hipGetErrorString(e));
   if (ss) {
     hipError_t ej = hipEventRecord(ss->join, ss->s);
@@ -359,10 +364,10 @@ tp_status run_grads(const tp_geom* geom, const tproj::KGeom& k, const float2* vo
   }
   if (!workspace || ws_bytes < pl.ws_bytes)
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
-  int* prefix = (int*)workspace;
-  LAUNCH(tproj::launch_brick_prefix(pl.bg, prefix, st), "brick work list");
+  const tproj::BrickWork wk = tproj::brick_work(pl.bg, geom->Bv, workspace);
+  LAUNCH(tproj::launch_brick_prefix(pl.bg, wk.prefix, st), "brick work list");
   const tproj::EvPair ev = kt_copy(TP_KT_GRADIENT);
-  LAUNCH(tproj::launch_grad_brick(k, geom->interp, pl.bg, prefix, volc, volr, U, Ur, rot, shifts, grad_rot,
+  LAUNCH(tproj::launch_grad_brick(k, geom->interp, pl.bg, wk, volc, volr, U, Ur, rot, shifts, grad_rot,
                                   grad_shifts, st, ev.a ? &ev : nullptr),
          "rotation/shift grads (bricks)");
   return TP_OK;
@@ -377,10 +382,10 @@ tp_status run_forward_real(const tp_geom* geom, const tproj::KGeom& k, const flo
   }
   if (!workspace || ws_bytes < pl.ws_bytes)
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
-  int* prefix = (int*)workspace;
-  LAUNCH(tproj::launch_brick_prefix(pl.bg, prefix, st), "brick work list");
+  const tproj::BrickWork wk = tproj::brick_work(pl.bg, geom->Bv, workspace);
+  LAUNCH(tproj::launch_brick_prefix(pl.bg, wk.prefix, st), "brick work list");
   const tproj::EvPair ev = kt_copy(TP_KT_FORWARD);
-  LAUNCH(tproj::launch_fwd_brick_real(k, geom->interp, pl.bg, prefix, vol, rot, out, st, ev.a ? &ev : nullptr),
+  LAUNCH(tproj::launch_fwd_brick_real(k, geom->interp, pl.bg, wk, vol, rot, out, st, ev.a ? &ev : nullptr),
          "real projection (bricks)");
   return TP_OK;
 }

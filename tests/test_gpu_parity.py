@@ -93,6 +93,22 @@ def test_small_all_ops(case):
         assert rel(gs2, rgs2) <= BWD_TOL, ("bp grad_shifts", rel(gs2, rgs2))
 
 
+def test_more_poses_than_a_chunk_holds():
+    """70000 poses against one volume: the pose list is longer than the 65535
+    poses a work item's hit list can address, so every brick is split."""
+    log("[parity] 70000 poses, D=8")
+    vol, rot, sh, imgs, wts, gdv, gwv = make_small(8, 8, 70000, 1, 1, 1, 1, 1, 1.0, -1.0, True, "rot", 11)
+    tv, tr, ts, ti, tw = dev(vol, rot, sh, imgs, wts)
+    out = bp.project_3d_to_2d(tv, tr, ts, H=8)
+    assert rel(out, oracle.project(vol, rot, sh, H=8, interp=1)) <= FWD_TOL
+    gv, gr, gs = bp.project_3d_to_2d_backward(ti, tv, tr, ts)
+    rgv, rgr, rgs = oracle.project_backward(imgs, vol, rot, sh, interp=1)
+    assert rel(gv, rgv) <= BWD_TOL and rel(gr, rgr) <= BWD_TOL and rel(gs, rgs) <= BWD_TOL
+    dvol, wvol = bp.backproject_2d_to_3d(ti, tr, tw, ts, D=8)
+    rdv, rwv = oracle.backproject(imgs, rot, wts, sh, D=8, interp=1)
+    assert rel(dvol, rdv) <= BWD_TOL and rel(wvol, rwv) <= BWD_TOL
+
+
 def test_requested_outputs_only():
     """NULL outputs are skipped; a missing weight upstream gives zero grad_weights."""
     vol, rot, sh, imgs, wts, gdv, gwv = make_small(16, 16, 3, 1, 1, 1, 1, 1, 1.0, -1.0, True, "rot", 5)
