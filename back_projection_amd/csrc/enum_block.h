@@ -74,11 +74,16 @@ __device__ __forceinline__ void item_chunk(const BrickGrid& bg, const int* __res
 
 // Body of a hit-list kernel (grid: nwork x volumes, 256 threads).
 // test(vsel, e, bl, bh): does pose e of the list reach the box [bl, bh)?
+// Each thread tests HL_K poses per pass (pose eb + j * 256 + thread, tests
+// issued together, so a long chunk costs few memory round trips); the hits
+// of sub-pass j precede those of sub-pass j + 1, which keeps the list in
+// pose order.
+constexpr int HL_K = 8;
 template <typename Test>
 __device__ __forceinline__ void build_hit_list(const BrickGrid& bg, const int* __restrict__ prefix,
                                                unsigned short* __restrict__ hits, int* __restrict__ counts,
                                                Test test) {
-  __shared__ int wcount[4];
+  __shared__ int wcount[HL_K][4];
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
   const int b = find_brick(prefix, bg.nb3, w);
@@ -90,22 +95,34 @@ __device__ __forceinline__ void build_hit_list(const BrickGrid& bg, const int* _
   const float bh[3] = {(float)(lo[0] + bg.S), (float)(lo[1] + bg.S), (float)(lo[2] + bg.S)};
   unsigned short* out = hits + hit_slot(bg, prefix, vsel, b, e0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const unsigned long long below = (1ull << lane) - 1ull;
   int cnt = 0;
-  for (int eb = e0; eb < e1; eb += 256) {
-    const int e = eb + tid;
-    const bool hit = e < e1 && test(vsel, e, bl, bh);
-    const unsigned long long m = __ballot(hit);
-    if (lane == 0) wcount[wave] = __popcll(m);
-    __syncthreads();
-    int before = cnt, total = cnt;
+  for (int eb = e0; eb < e1; eb += 256 * HL_K) {
+    bool hit[HL_K];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int c = wcount[v];
-      if (v < wave) before += c;
-      total += c;
+    for (int j = 0; j < HL_K; ++j) {
+      const int e = eb + j * 256 + tid;
+      hit[j] = e < e1 && test(vsel, e, bl, bh);
     }
-    if (hit) out[before + __popcll(m & ((1ull << lane) - 1ull))] = (unsigned short)(e - e0);
-    cnt = total;
+    unsigned long long m[HL_K];
+#pragma unroll
+    for (int j = 0; j < HL_K; ++j) {
+      m[j] = __ballot(hit[j]);
+      if (lane == 0) wcount[j][wave] = __popcll(m[j]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < HL_K; ++j) {
+      int before = cnt, total = cnt;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int c = wcount[j][v];
+        if (v < wave) before += c;
+        total += c;
+      }
+      if (hit[j]) out[before + __popcll(m[j] & below)] = (unsigned short)(eb + j * 256 + tid - e0);
+      cnt = total;
+    }
     __syncthreads();   // every wavefront has read the counts before the next pass
   }
   if (tid == 0) counts[(int64_t)vsel * bg.nwork + w] = cnt;

@@ -44,14 +44,14 @@ FP32_VECTOR_TFLOPS = 157.3
 # reported when the digest of back_projection_amd/csrc matches, else null.
 TRAFFIC = {
     # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
-    "forward": {"sources_sha256": "61884ff3a2c45fcf69af7c5dd6cf711c658bc4b0a80ff98d26686e2ea0c4ceb2",
-               "fetch_bytes": 354500375, "write_bytes": 1183542517},
-    "backward": {"sources_sha256": "61884ff3a2c45fcf69af7c5dd6cf711c658bc4b0a80ff98d26686e2ea0c4ceb2",
-                "fetch_bytes": 2944344754, "write_bytes": 200748726},
-    "gradient": {"sources_sha256": "61884ff3a2c45fcf69af7c5dd6cf711c658bc4b0a80ff98d26686e2ea0c4ceb2",
-                "fetch_bytes": 2819737791, "write_bytes": 120333792},
-    "fold": {"sources_sha256": "61884ff3a2c45fcf69af7c5dd6cf711c658bc4b0a80ff98d26686e2ea0c4ceb2",
-            "fetch_bytes": 292871594, "write_bytes": 8519680},
+    "forward": {"sources_sha256": "5adff4850c998855001fb34d15d25409de741ea373e70794b2e3d8d9f6ab31a2",
+               "fetch_bytes": 317374140, "write_bytes": 1183304064},
+    "backward": {"sources_sha256": "5adff4850c998855001fb34d15d25409de741ea373e70794b2e3d8d9f6ab31a2",
+                "fetch_bytes": 2826802982, "write_bytes": 188940288},
+    "gradient": {"sources_sha256": "5adff4850c998855001fb34d15d25409de741ea373e70794b2e3d8d9f6ab31a2",
+                "fetch_bytes": 2785301375, "write_bytes": 120424608},
+    "fold": {"sources_sha256": "5adff4850c998855001fb34d15d25409de741ea373e70794b2e3d8d9f6ab31a2",
+            "fetch_bytes": 292611606, "write_bytes": 8519680},
 }
 
 
