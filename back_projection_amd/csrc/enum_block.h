@@ -461,8 +461,16 @@ template <int CTRL, int RM, int N>
 __device__ __forceinline__ void seg_step(float (&v)[N], int key) {
   const int ks = dpp_int<CTRL, RM>(-1, key);
   const float m = ks == key ? 1.0f : 0.0f;
+  if constexpr (RM == 0xf) {
+    // every lane is written (lanes without a source read 0), so the moved
+    // value needs no old value and can fuse into the multiply-add
 #pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = fmaf(m, __int_as_float(dpp_int<CTRL, RM>(0, __float_as_int(v[q]))), v[q]);
+    for (int q = 0; q < N; ++q)
+      v[q] = fmaf(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[q]), CTRL, RM, 0xf, true)), m, v[q]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < N; ++q) v[q] = fmaf(m, __int_as_float(dpp_int<CTRL, RM>(0, __float_as_int(v[q]))), v[q]);
+  }
 }
 
 template <int N>
