@@ -34,6 +34,9 @@
  *   - every op is differentiable w.r.t. its inputs, rotations and shifts
  *     [es TS2, nl M]; complex gradients follow dL/dRe + i dL/dIm.
  *   - radius cutoff (reading): pixel kept iff r < 0 or kx^2 + ky^2 <= r^2.
+ *   - 2D -> 2D forward and backward [nl M, es TS2, fr TS2]: the same
+ *     definitions one dimension down (2x2 map, 2D rfft source); see the
+ *     section of that name below.
  *
  * All entry points return 0 on success and a negative value on a bad argument.
  * Complex arrays are interleaved (re, im) doubles.
@@ -542,6 +545,300 @@ int oracle_backproject_backward(int B, int P, int Bv, int Br, int Bs, int D, int
         for (int q = 0; q < 2; ++q) grad_shifts[2 * ((size_t)bsel(g.Bs, b) * P + n) + q] += gr[11 * bn + 9 + q];
     }
     free(gr);
+  }
+  return 0;
+}
+
+/* ================================================================== */
+/* 2D -> 2D: rotation of 2D Fourier data and its adjoint              */
+/* ================================================================== */
+/* The pages list 2D -> 2D forward (rotation of 2D Fourier data) and 2D -> 2D
+ * backward (accumulation into a 2D reconstruction) next to the 3D ops
+ * [nl M ops 1-2, es TS2, fr TS2].  Readings, mirroring the 3D ops: the source
+ * is an rfft image X[y][x] of box D (x halved); the sample of output pixel
+ * (kx, ky) is p = o * R * (kx, ky)^T with a 2x2 map R (rows/cols (x, y));
+ * taps are looked up with the same per-tap Friedel rule in 2D; shifts,
+ * cutoff, weights and gradients are defined exactly as for the 3D ops. */
+
+/* Stored entry of the 2D tap (tx, ty): m = tx mod D; m <= D/2 -> (ty mod D,
+ * m); otherwise the conjugated mate (-ty mod D, D - m). */
+static long tap_index2(int D, long tx, long ty, int* conj) {
+  long half = D / 2, m = pmod(tx, D);
+  if (m <= half) { *conj = 0; return pmod(ty, D) * (half + 1) + m; }
+  *conj = 1;
+  return pmod(-ty, D) * (half + 1) + (D - m);
+}
+
+static void slice_coord2(const double* R, double o, double kx, double ky, double p[2]) {
+  for (int i = 0; i < 2; ++i) p[i] = o * (R[2 * i + 0] * kx + R[2 * i + 1] * ky);
+}
+
+/* I(p) of the complex source and, if dI != NULL, dI/dp_0, dI/dp_1. */
+static void interp2_complex(const double* X, int D, int interp, const double p[2], double I[2], double* dI) {
+  long f[2]; int n[2];
+  for (int a = 0; a < 2; ++a) taps_of(interp, p[a], &f[a], &n[a]);
+  I[0] = I[1] = 0.0;
+  if (dI) for (int q = 0; q < 4; ++q) dI[q] = 0.0;
+  for (int b = 0; b < n[1]; ++b) {
+    long ty = f[1] + b; double dy = p[1] - (double)ty;
+    for (int a = 0; a < n[0]; ++a) {
+      long tx = f[0] + a; double dx = p[0] - (double)tx;
+      int cj; long idx = tap_index2(D, tx, ty, &cj);
+      double vr = X[2 * idx], vi = cj ? -X[2 * idx + 1] : X[2 * idx + 1];
+      double wx = kw(interp, dx), wy = kw(interp, dy), w = wx * wy;
+      I[0] += w * vr; I[1] += w * vi;
+      if (dI) {
+        double gx = kdw(interp, dx) * wy, gy = wx * kdw(interp, dy);
+        dI[0] += gx * vr; dI[1] += gx * vi;
+        dI[2] += gy * vr; dI[3] += gy * vi;
+      }
+    }
+  }
+}
+
+static void interp2_real(const double* W, int D, int interp, const double p[2], double* I, double* dI) {
+  long f[2]; int n[2];
+  for (int a = 0; a < 2; ++a) taps_of(interp, p[a], &f[a], &n[a]);
+  *I = 0.0;
+  if (dI) dI[0] = dI[1] = 0.0;
+  for (int b = 0; b < n[1]; ++b) {
+    long ty = f[1] + b; double dy = p[1] - (double)ty;
+    for (int a = 0; a < n[0]; ++a) {
+      long tx = f[0] + a; double dx = p[0] - (double)tx;
+      int cj; long idx = tap_index2(D, tx, ty, &cj);
+      double v = W[idx], wx = kw(interp, dx), wy = kw(interp, dy);
+      *I += wx * wy * v;
+      if (dI) { dI[0] += kdw(interp, dx) * wy * v; dI[1] += wx * kdw(interp, dy) * v; }
+    }
+  }
+}
+
+/* Adjoints of the two interpolations. */
+static void spread2_complex(double* X, int D, int interp, const double p[2], double cr, double ci) {
+  long f[2]; int n[2];
+  for (int a = 0; a < 2; ++a) taps_of(interp, p[a], &f[a], &n[a]);
+  for (int b = 0; b < n[1]; ++b) {
+    long ty = f[1] + b; double wy = kw(interp, p[1] - (double)ty);
+    for (int a = 0; a < n[0]; ++a) {
+      long tx = f[0] + a; double w = kw(interp, p[0] - (double)tx) * wy;
+      int cj; long idx = tap_index2(D, tx, ty, &cj);
+      X[2 * idx] += w * cr;
+      X[2 * idx + 1] += w * (cj ? -ci : ci);
+    }
+  }
+}
+
+static void spread2_real(double* W, int D, int interp, const double p[2], double v) {
+  long f[2]; int n[2];
+  for (int a = 0; a < 2; ++a) taps_of(interp, p[a], &f[a], &n[a]);
+  for (int b = 0; b < n[1]; ++b) {
+    long ty = f[1] + b; double wy = kw(interp, p[1] - (double)ty);
+    for (int a = 0; a < n[0]; ++a) {
+      long tx = f[0] + a;
+      int cj; long idx = tap_index2(D, tx, ty, &cj);
+      W[idx] += kw(interp, p[0] - (double)tx) * wy * v;
+    }
+  }
+}
+
+static size_t src2_elems(const geom_t* g) { return (size_t)g->D * (g->D / 2 + 1); }
+
+/* out[b][n] = M * phi * I(X[bx], o R k). */
+int oracle_project2d(int B, int P, int Bv, int Br, int Bs, int D, int H, int interp, double o, double r,
+                     const double* src, const double* rot, const double* shifts, double* out) {
+  geom_t g = {B, P, Bv, Br, shifts ? Bs : 0, D, H, interp, o, r};
+  int e = check_geom(&g); if (e) return e;
+  if (!src || !rot || !out) return -7;
+  size_t nx = src2_elems(&g), ni = img_elems(&g);
+  int W2 = H / 2 + 1;
+  long total = (long)B * P;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bn = 0; bn < total; ++bn) {
+    int b = (int)(bn / P), n = (int)(bn % P);
+    const double* X = src + 2 * nx * bsel(Bv, b);
+    const double* R = rot + 4 * ((size_t)bsel(Br, b) * P + n);
+    const double* s = shifts ? shifts + 2 * ((size_t)bsel(g.Bs, b) * P + n) : NULL;
+    double* O = out + 2 * ni * (size_t)bn;
+    for (int iy = 0; iy < H; ++iy)
+      for (int ix = 0; ix < W2; ++ix) {
+        double kx, ky; pixel_freq(H, iy, ix, &kx, &ky);
+        double* q = O + 2 * ((size_t)iy * W2 + ix);
+        if (!in_mask(r, kx, ky)) { q[0] = q[1] = 0.0; continue; }
+        double p[2], I[2], pr, pi;
+        slice_coord2(R, o, kx, ky, p);
+        interp2_complex(X, D, interp, p, I, NULL);
+        shift_phase(s, H, kx, ky, &pr, &pi);
+        q[0] = pr * I[0] - pi * I[1];
+        q[1] = pr * I[1] + pi * I[0];
+      }
+  }
+  return 0;
+}
+
+/* Accumulation of images (and real weights) into Bv 2D reconstructions: the
+ * adjoint of oracle_project2d (weights: real, unshifted). */
+int oracle_backproject2d(int B, int P, int Bv, int Br, int Bs, int D, int H, int interp, double o, double r,
+                         const double* images, const double* weights, const double* rot, const double* shifts,
+                         double* data_img, double* weight_img) {
+  geom_t g = {B, P, Bv, Br, shifts ? Bs : 0, D, H, interp, o, r};
+  int e = check_geom(&g); if (e) return e;
+  if (!images || !rot || !data_img) return -7;
+  if ((weights == NULL) != (weight_img == NULL)) return -7;
+  size_t nx = src2_elems(&g), ni = img_elems(&g);
+  int W2 = H / 2 + 1;
+  memset(data_img, 0, sizeof(double) * 2 * nx * Bv);
+  if (weight_img) memset(weight_img, 0, sizeof(double) * nx * Bv);
+  /* one pass in (b, n) order: the result does not depend on thread count */
+  for (long bn = 0; bn < (long)B * P; ++bn) {
+    int b = (int)(bn / P), n = (int)(bn % P), bv = bsel(Bv, b);
+    const double* R = rot + 4 * ((size_t)bsel(Br, b) * P + n);
+    const double* s = shifts ? shifts + 2 * ((size_t)bsel(g.Bs, b) * P + n) : NULL;
+    const double* Y = images + 2 * ni * (size_t)bn;
+    for (int iy = 0; iy < H; ++iy)
+      for (int ix = 0; ix < W2; ++ix) {
+        double kx, ky; pixel_freq(H, iy, ix, &kx, &ky);
+        if (!in_mask(r, kx, ky)) continue;
+        size_t k = (size_t)iy * W2 + ix;
+        double p[2], pr, pi;
+        slice_coord2(R, o, kx, ky, p);
+        shift_phase(s, H, kx, ky, &pr, &pi);
+        double yr = Y[2 * k], yi = Y[2 * k + 1];
+        spread2_complex(data_img + 2 * nx * bv, D, interp, p, pr * yr + pi * yi, pr * yi - pi * yr);
+        if (weights) spread2_real(weight_img + nx * bv, D, interp, p, weights[ni * (size_t)bn + k]);
+      }
+  }
+  return 0;
+}
+
+/* gR (2x2) and gs of one projection: derivative of Re<U, phi I(Xc)> +
+ * <Ur, I(Xr)> w.r.t. R and s; same formulas as the 3D ops with k2 = (kx, ky). */
+static void rot_shift_grad2_one(const geom_t* g, const double* Xc, const double* Xr, const double* U,
+                                const double* Ur, const double* R, const double* s, double gR[4], double gs[2]) {
+  int W2 = g->H / 2 + 1;
+  for (int q = 0; q < 4; ++q) gR[q] = 0.0;
+  gs[0] = gs[1] = 0.0;
+  for (int iy = 0; iy < g->H; ++iy)
+    for (int ix = 0; ix < W2; ++ix) {
+      double kx, ky; pixel_freq(g->H, iy, ix, &kx, &ky);
+      if (!in_mask(g->r, kx, ky)) continue;
+      size_t k = (size_t)iy * W2 + ix;
+      double p[2], k2[2] = {kx, ky}, e[2] = {0.0, 0.0};
+      slice_coord2(R, g->o, kx, ky, p);
+      if (Xc) {
+        double I[2], dI[4], pr, pi;
+        interp2_complex(Xc, g->D, g->interp, p, I, dI);
+        shift_phase(s, g->H, kx, ky, &pr, &pi);
+        double ur = U[2 * k], ui = U[2 * k + 1];
+        for (int i = 0; i < 2; ++i) {
+          double ar = pr * dI[2 * i] - pi * dI[2 * i + 1], ai = pr * dI[2 * i + 1] + pi * dI[2 * i];
+          e[i] += ur * ar + ui * ai;
+        }
+        double yr = pr * I[0] - pi * I[1], yi = pr * I[1] + pi * I[0];
+        double im = ur * yi - ui * yr;
+        gs[0] += 2.0 * M_PI / g->H * kx * im;
+        gs[1] += 2.0 * M_PI / g->H * ky * im;
+      }
+      if (Xr) {
+        double I, dI[2];
+        interp2_real(Xr, g->D, g->interp, p, &I, dI);
+        for (int i = 0; i < 2; ++i) e[i] += Ur[k] * dI[i];
+      }
+      for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) gR[2 * i + j] += g->o * e[i] * k2[j];
+    }
+}
+
+/* Sum the per-projection gR/gs of every (b, n) into the (broadcast) outputs. */
+static int rot_shift_grads2(const geom_t* g, const double* Xc, const double* Xr, const double* U, const double* Ur,
+                            const double* rot, const double* shifts, double* grad_rot, double* grad_shifts) {
+  size_t nx = src2_elems(g), ni = img_elems(g);
+  long total = (long)g->B * g->P;
+  double* gr = (double*)calloc((size_t)total * 6, sizeof(double));
+  if (!gr) return -8;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long bn = 0; bn < total; ++bn) {
+    int b = (int)(bn / g->P), n = (int)(bn % g->P);
+    const double* R = rot + 4 * ((size_t)bsel(g->Br, b) * g->P + n);
+    const double* s = shifts ? shifts + 2 * ((size_t)bsel(g->Bs, b) * g->P + n) : NULL;
+    rot_shift_grad2_one(g, Xc ? Xc + 2 * nx * bsel(g->Bv, b) : NULL, Xr ? Xr + nx * bsel(g->Bv, b) : NULL,
+                        U + 2 * ni * (size_t)bn, Ur ? Ur + ni * (size_t)bn : NULL, R, s, gr + 6 * bn,
+                        gr + 6 * bn + 4);
+  }
+  if (grad_rot) memset(grad_rot, 0, sizeof(double) * 4 * (size_t)g->Br * g->P);
+  if (grad_shifts) memset(grad_shifts, 0, sizeof(double) * 2 * (size_t)g->Bs * g->P);
+  for (long bn = 0; bn < total; ++bn) {
+    int b = (int)(bn / g->P), n = (int)(bn % g->P);
+    if (grad_rot)
+      for (int q = 0; q < 4; ++q) grad_rot[4 * ((size_t)bsel(g->Br, b) * g->P + n) + q] += gr[6 * bn + q];
+    if (grad_shifts)
+      for (int q = 0; q < 2; ++q) grad_shifts[2 * ((size_t)bsel(g->Bs, b) * g->P + n) + q] += gr[6 * bn + 4 + q];
+  }
+  free(gr);
+  return 0;
+}
+
+/* Backward of oracle_project2d: grad_src = adjoint(grad_out), grad_rot,
+ * grad_shifts.  Any output may be NULL. */
+int oracle_project2d_backward(int B, int P, int Bv, int Br, int Bs, int D, int H, int interp, double o, double r,
+                              const double* grad_out, const double* src, const double* rot, const double* shifts,
+                              double* grad_src, double* grad_rot, double* grad_shifts) {
+  geom_t g = {B, P, Bv, Br, shifts ? Bs : 0, D, H, interp, o, r};
+  int e = check_geom(&g); if (e) return e;
+  if (!grad_out || !rot) return -7;
+  if ((grad_rot || grad_shifts) && !src) return -7;
+  if (grad_shifts && !shifts) return -7;
+  if (grad_src) {
+    e = oracle_backproject2d(B, P, Bv, Br, Bs, D, H, interp, o, r, grad_out, NULL, rot, shifts, grad_src, NULL);
+    if (e) return e;
+  }
+  if (grad_rot || grad_shifts) return rot_shift_grads2(&g, src, NULL, grad_out, NULL, rot, shifts, grad_rot, grad_shifts);
+  return 0;
+}
+
+/* Backward of oracle_backproject2d: grad_images = M phi I(grad_data),
+ * grad_weights = M I_real(grad_weight), grad_rot / grad_shifts with (source,
+ * upstream) = (grad_data, images) plus the real channel (grad_weight,
+ * weights).  Any output may be NULL. */
+int oracle_backproject2d_backward(int B, int P, int Bv, int Br, int Bs, int D, int H, int interp, double o,
+                                  double r, const double* grad_data, const double* grad_weight,
+                                  const double* images, const double* weights, const double* rot,
+                                  const double* shifts, double* grad_images, double* grad_weights,
+                                  double* grad_rot, double* grad_shifts) {
+  geom_t g = {B, P, Bv, Br, shifts ? Bs : 0, D, H, interp, o, r};
+  int e = check_geom(&g); if (e) return e;
+  if (!grad_data || !rot) return -7;
+  if (grad_weights && !grad_weight) return -7;
+  if ((grad_rot || grad_shifts) && !images) return -7;
+  if (grad_rot && grad_weight && !weights) return -7;
+  if (grad_shifts && !shifts) return -7;
+  if (grad_images) {
+    e = oracle_project2d(B, P, Bv, Br, Bs, D, H, interp, o, r, grad_data, rot, shifts, grad_images);
+    if (e) return e;
+  }
+  if (grad_weights) {
+    size_t nx = src2_elems(&g), ni = img_elems(&g);
+    int W2 = H / 2 + 1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bn = 0; bn < (long)B * P; ++bn) {
+      int b = (int)(bn / P), n = (int)(bn % P);
+      const double* R = rot + 4 * ((size_t)bsel(Br, b) * P + n);
+      double* out = grad_weights + ni * (size_t)bn;
+      for (int iy = 0; iy < H; ++iy)
+        for (int ix = 0; ix < W2; ++ix) {
+          double kx, ky; pixel_freq(H, iy, ix, &kx, &ky);
+          size_t k = (size_t)iy * W2 + ix;
+          if (!in_mask(r, kx, ky)) { out[k] = 0.0; continue; }
+          double p[2], I;
+          slice_coord2(R, o, kx, ky, p);
+          interp2_real(grad_weight + nx * bsel(Bv, b), D, interp, p, &I, NULL);
+          out[k] = I;
+        }
+    }
+  }
+  if (grad_rot || grad_shifts) {
+    int use_w = grad_weight != NULL && weights != NULL;
+    return rot_shift_grads2(&g, grad_data, use_w ? grad_weight : NULL, images, use_w ? weights : NULL, rot, shifts,
+                            grad_rot, grad_shifts);
   }
   return 0;
 }
