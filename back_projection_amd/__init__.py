@@ -12,12 +12,18 @@ Methodologie, French "Resume technique" 2):
   project_3d_to_2d_backward      volume, rotation and shift gradients
   backproject_2d_to_3d           accumulate rfft images (+ real weights)
   backproject_2d_to_3d_backward  image, weight, rotation and shift gradients
+  project_2d_to_2d               rotation of a 2D rfft source (Dutch page, op. 1)
+  project_2d_to_2d_backward      source, rotation and shift gradients
+  backproject_2d_to_2d           accumulation into 2D reconstructions (op. 2)
+  backproject_2d_to_2d_backward  image, weight, rotation and shift gradients
 
 Tensor layout (CUDA/HIP tensors, contiguous):
   vol      complex64 [Bv, D, D, D//2+1]      weight vol float32 [Bv, D, D, D//2+1]
   images   complex64 [B, P, H, H//2+1]       weights    float32 [B, P, H, H//2+1]
   rot      float32   [Br, P, 3, 3]           shifts     float32 [Bs, P, 2]
-with each of Bv, Br, Bs equal to 1 or B.
+with each of Bv, Br, Bs equal to 1 or B.  The 2D -> 2D calls take a source
+complex64 [Bv, D, D//2+1] (weight source float32 [Bv, D, D//2+1]) and
+rot float32 [Br, P, 2, 2].
 """
 from __future__ import annotations
 
@@ -28,6 +34,7 @@ import torch
 
 __all__ = [
     "project_3d_to_2d", "project_3d_to_2d_backward", "backproject_2d_to_3d", "backproject_2d_to_3d_backward",
+    "project_2d_to_2d", "project_2d_to_2d_backward", "backproject_2d_to_2d", "backproject_2d_to_2d_backward",
     "TprojError", "lib", "Geom", "LIB_PATH", "HEADER_SYMBOLS", "timing_enable", "timing_read", "KERNEL_CLASSES",
 ]
 
@@ -37,11 +44,13 @@ LIB_PATH = os.path.join(_PKG, "libtproj.so")
 # Every symbol that include/tproj.h declares.
 HEADER_SYMBOLS = (
     "project_3d_to_2d", "project_3d_to_2d_backward", "backproject_2d_to_3d", "backproject_2d_to_3d_backward",
+    "project_2d_to_2d", "project_2d_to_2d_backward", "backproject_2d_to_2d", "backproject_2d_to_2d_backward",
     "tp_workspace_size", "tp_validate", "tp_status_string", "tp_last_error_detail", "tp_abi_version",
     "tp_timing_enable", "tp_timing_read",
 )
 
 OP_PROJECT, OP_PROJECT_BACKWARD, OP_BACKPROJECT, OP_BACKPROJECT_BACKWARD = 0, 1, 2, 3
+OP_PROJECT_2D, OP_PROJECT_2D_BACKWARD, OP_BACKPROJECT_2D, OP_BACKPROJECT_2D_BACKWARD = 4, 5, 6, 7
 
 
 class TprojError(RuntimeError):
@@ -74,8 +83,13 @@ def lib():
         L.project_3d_to_2d_backward.argtypes = [G, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.backproject_2d_to_3d.argtypes = [G, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.backproject_2d_to_3d_backward.argtypes = [G] + [_vp] * 11 + [ctypes.c_size_t, _vp]
+        L.project_2d_to_2d.argtypes = L.project_3d_to_2d.argtypes
+        L.project_2d_to_2d_backward.argtypes = L.project_3d_to_2d_backward.argtypes
+        L.backproject_2d_to_2d.argtypes = L.backproject_2d_to_3d.argtypes
+        L.backproject_2d_to_2d_backward.argtypes = L.backproject_2d_to_3d_backward.argtypes
         for f in ("project_3d_to_2d", "project_3d_to_2d_backward", "backproject_2d_to_3d",
-                  "backproject_2d_to_3d_backward", "tp_validate"):
+                  "backproject_2d_to_3d_backward", "project_2d_to_2d", "project_2d_to_2d_backward",
+                  "backproject_2d_to_2d", "backproject_2d_to_2d_backward", "tp_validate"):
             getattr(L, f).restype = ctypes.c_int
         L.tp_validate.argtypes = [G]
         L.tp_workspace_size.argtypes = [G, ctypes.c_int]
@@ -282,4 +296,116 @@ def backproject_2d_to_3d_backward(grad_data_vol, images, rot, grad_weight_vol=No
     _check(lib().backproject_2d_to_3d_backward(ctypes.byref(g), _ptr(grad_data_vol), _ptr(grad_weight_vol),
                                                _ptr(images), _ptr(weights), _ptr(rot), _ptr(shifts), _ptr(gi),
                                                _ptr(gw), _ptr(gr), _ptr(gs), _ptr(ws), nws, _stream(dev)))
+    return gi, gw, gr, gs
+
+
+# ---------------------------------------------------------------------------
+# 2D -> 2D
+# ---------------------------------------------------------------------------
+def project_2d_to_2d(src, rot, shifts=None, *, H=None, interp="cubic", oversampling=1.0, radius_cutoff=-1.0,
+                     B=None, out=None):
+    """Forward: out[b, n] = M * phi * I(src[bv], o R (kx, ky)).  Returns out
+    (complex64 [B, P, H, H//2+1])."""
+    _req(src, "src", torch.complex64, 3)
+    dev = src.device
+    _req(rot, "rot", torch.float32, 4, dev)
+    if tuple(rot.shape[2:]) != (2, 2):
+        raise ValueError(f"rot must be [Br, P, 2, 2], got {tuple(rot.shape)}")
+    if shifts is not None:
+        _req(shifts, "shifts", torch.float32, 3, dev)
+    Bv, D = src.shape[0], src.shape[1]
+    Br, P = rot.shape[0], rot.shape[1]
+    Bs = shifts.shape[0] if shifts is not None else 0
+    B = B or _batch(Bv, Br, Bs)
+    H = H or D
+    if out is None:
+        out = torch.empty((B, P, H, H // 2 + 1), dtype=torch.complex64, device=dev)
+    else:
+        _req(out, "out", torch.complex64, 4, dev)
+        if tuple(out.shape) != (B, P, H, H // 2 + 1):
+            raise ValueError(f"out must have shape {(B, P, H, H // 2 + 1)}, got {tuple(out.shape)}")
+    g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
+    ws, nws = _workspace(g, OP_PROJECT_2D, dev)
+    _check(lib().project_2d_to_2d(ctypes.byref(g), _ptr(src), _ptr(rot), _ptr(shifts), _ptr(out), _ptr(ws), nws,
+                                  _stream(dev)))
+    return out
+
+
+def project_2d_to_2d_backward(grad_out, src, rot, shifts=None, *, interp="cubic", oversampling=1.0,
+                              radius_cutoff=-1.0, need_src=True, need_rot=True, need_shifts=True):
+    """Backward of project_2d_to_2d; returns (grad_src, grad_rot, grad_shifts),
+    None where not requested."""
+    _req(grad_out, "grad_out", torch.complex64, 4)
+    dev = grad_out.device
+    _req(src, "src", torch.complex64, 3, dev)
+    _req(rot, "rot", torch.float32, 4, dev)
+    if shifts is not None:
+        _req(shifts, "shifts", torch.float32, 3, dev)
+    B, P, H = grad_out.shape[0], grad_out.shape[1], grad_out.shape[2]
+    Bv, D = src.shape[0], src.shape[1]
+    Br = rot.shape[0]
+    Bs = shifts.shape[0] if shifts is not None else 0
+    gx = torch.empty_like(src) if need_src else None
+    gr = torch.empty_like(rot) if need_rot else None
+    gs = torch.empty_like(shifts) if (need_shifts and shifts is not None) else None
+    g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
+    ws, nws = _workspace(g, OP_PROJECT_2D_BACKWARD, dev)
+    _check(lib().project_2d_to_2d_backward(ctypes.byref(g), _ptr(grad_out), _ptr(src), _ptr(rot), _ptr(shifts),
+                                           _ptr(gx), _ptr(gr), _ptr(gs), _ptr(ws), nws, _stream(dev)))
+    return gx, gr, gs
+
+
+def backproject_2d_to_2d(images, rot, weights=None, shifts=None, *, D=None, Bv=1, interp="cubic",
+                         oversampling=1.0, radius_cutoff=-1.0):
+    """Accumulation into 2D reconstructions (adjoint of project_2d_to_2d):
+    returns (data, weight or None), complex64 / float32 [Bv, D, D//2+1]."""
+    _req(images, "images", torch.complex64, 4)
+    dev = images.device
+    _req(rot, "rot", torch.float32, 4, dev)
+    if weights is not None:
+        _req(weights, "weights", torch.float32, 4, dev)
+    if shifts is not None:
+        _req(shifts, "shifts", torch.float32, 3, dev)
+    B, P, H = images.shape[0], images.shape[1], images.shape[2]
+    Br = rot.shape[0]
+    Bs = shifts.shape[0] if shifts is not None else 0
+    D = D or H
+    data = torch.empty((Bv, D, D // 2 + 1), dtype=torch.complex64, device=dev)
+    wimg = torch.empty((Bv, D, D // 2 + 1), dtype=torch.float32, device=dev) if weights is not None else None
+    g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
+    ws, nws = _workspace(g, OP_BACKPROJECT_2D, dev)
+    _check(lib().backproject_2d_to_2d(ctypes.byref(g), _ptr(images), _ptr(weights), _ptr(rot), _ptr(shifts),
+                                      _ptr(data), _ptr(wimg), _ptr(ws), nws, _stream(dev)))
+    return data, wimg
+
+
+def backproject_2d_to_2d_backward(grad_data, images, rot, grad_weight=None, weights=None, shifts=None, *,
+                                  interp="cubic", oversampling=1.0, radius_cutoff=-1.0, need_images=True,
+                                  need_weights=True, need_rot=True, need_shifts=True):
+    """Backward of backproject_2d_to_2d; returns (grad_images, grad_weights,
+    grad_rot, grad_shifts), None where not requested."""
+    _req(grad_data, "grad_data", torch.complex64, 3)
+    dev = grad_data.device
+    _req(images, "images", torch.complex64, 4, dev)
+    _req(rot, "rot", torch.float32, 4, dev)
+    if grad_weight is not None:
+        _req(grad_weight, "grad_weight", torch.float32, 3, dev)
+    if weights is not None:
+        _req(weights, "weights", torch.float32, 4, dev)
+    if shifts is not None:
+        _req(shifts, "shifts", torch.float32, 3, dev)
+    B, P, H = images.shape[0], images.shape[1], images.shape[2]
+    Bv, D = grad_data.shape[0], grad_data.shape[1]
+    Br = rot.shape[0]
+    Bs = shifts.shape[0] if shifts is not None else 0
+    gi = torch.empty_like(images) if need_images else None
+    gw = torch.empty((B, P, H, H // 2 + 1), dtype=torch.float32, device=dev) if (
+        need_weights and weights is not None) else None
+    gr = torch.empty_like(rot) if need_rot else None
+    gs = torch.empty_like(shifts) if (need_shifts and shifts is not None) else None
+    g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
+    ws, nws = _workspace(g, OP_BACKPROJECT_2D_BACKWARD, dev)
+    _check(lib().backproject_2d_to_2d_backward(ctypes.byref(g), _ptr(grad_data), _ptr(grad_weight), _ptr(images),
+                                               _ptr(weights), _ptr(rot), _ptr(shifts), _ptr(gi), _ptr(gw), _ptr(gr),
+                                               _ptr(gs), _ptr(ws), nws, _stream(dev)))
     return gi, gw, gr, gs

@@ -18,6 +18,7 @@
 #include "brick_kernels.h"
 #include "kernels.h"
 #include "bwd_kernels.h"
+#include "kernels_2d.h"
 
 namespace {
 
@@ -475,14 +476,49 @@ tp_status tp_validate(const tp_geom* geom) {
 
 size_t tp_workspace_size(const tp_geom* geom, int op) {
   if (check_geom(geom) != TP_OK) return (size_t)-1;
-  if (op < TP_OP_PROJECT || op > TP_OP_BACKPROJECT_BACKWARD) return (size_t)-1;
+  if (op < TP_OP_PROJECT || op > TP_OP_BACKPROJECT_2D_BACKWARD) return (size_t)-1;
   return workspace_need(geom, op);
 }
 
 }  // extern "C"
 
 namespace {
+// Workspace of the 2D -> 2D ops: the periodic extension of the complex source
+// (Ec) and of the real one (Er), the per-image maxima (mx) and the partial
+// sums of the accumulation, each 256-byte aligned and present only when the
+// op uses it.
+struct Ws2 {
+  float2* ec = nullptr;
+  float* er = nullptr;
+  float* mx = nullptr;
+  void* parts = nullptr;
+  size_t bytes = 0;
+};
+
+Ws2 ws2_layout(const tp_geom* g, int op, void* base) {
+  const tproj::KGeom k = kgeom(g);
+  const size_t ne = (size_t)g->Bv * g->D * (g->D + 1);
+  const bool ec = op != TP_OP_BACKPROJECT_2D;
+  const bool er = op == TP_OP_BACKPROJECT_2D_BACKWARD;
+  const bool bp = op == TP_OP_PROJECT_2D_BACKWARD || op == TP_OP_BACKPROJECT_2D;
+  Ws2 w;
+  char* p = (char*)base;
+  size_t off = 0;
+  if (ec) { w.ec = (float2*)(p + off); off += align_up(ne * sizeof(float2)); }
+  if (er) { w.er = (float*)(p + off); off += align_up(ne * sizeof(float)); }
+  if (bp) {
+    w.mx = (float*)(p + off);
+    off += align_up((size_t)g->B * g->P * sizeof(float));
+    w.parts = p + off;
+    off += align_up(tproj::twod_bp_parts_bytes(k, op == TP_OP_BACKPROJECT_2D));
+  }
+  w.bytes = off;
+  if (!base) w.ec = nullptr, w.er = nullptr, w.mx = nullptr, w.parts = nullptr;
+  return w;
+}
+
 size_t workspace_need(const tp_geom* geom, int op) {
+  if (op >= TP_OP_PROJECT_2D) return ws2_layout(geom, op, nullptr).bytes;
   const size_t gather = gather_plan(geom).ws_bytes;
   if (op == TP_OP_PROJECT || op == TP_OP_BACKPROJECT_BACKWARD) return gather;
   // the back-projection's part, then the gradients' (they may run at once)
@@ -625,6 +661,133 @@ tp_status backproject_2d_to_3d_backward(const tp_geom* geom, const void* grad_da
     const bool wch = grad_weight_vol != nullptr && weights != nullptr;
     TRY(run_grads(geom, k, (const float2*)grad_data_vol, wch ? grad_weight_vol : nullptr, (const float2*)images,
                   wch ? weights : nullptr, rot, shifts, grad_rot, grad_shifts, workspace, ws_bytes, st));
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+// 2D -> 2D
+// ---------------------------------------------------------------------------
+tp_status project_2d_to_2d(const tp_geom* geom, const void* src, const float* rot, const float* shifts, void* out,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  TRY(check_geom(geom));
+  TRY(check_shifts(geom, shifts));
+  TRY(check_ptr(src, "src", 8));
+  TRY(check_ptr(rot, "rot", 4));
+  TRY(check_opt(shifts, "shifts", 4));
+  TRY(check_ptr(out, "out", 8));
+  TRY(check_opt(workspace, "workspace", 8));
+  TRY(check_workspace(geom, TP_OP_PROJECT_2D, workspace, ws_bytes));
+  TRY(check_device());
+  const tproj::KGeom k = kgeom(geom);
+  hipStream_t st = (hipStream_t)stream;
+  const Ws2 w = ws2_layout(geom, TP_OP_PROJECT_2D, workspace);
+  LAUNCH(tproj::launch2_expand_c(k, (const float2*)src, w.ec, st), "2D source extension");
+  LAUNCH(tproj::launch2_gather_c(k, geom->interp, w.ec, rot, shifts, (float2*)out, st), "2D projection");
+  return ok();
+}
+
+tp_status project_2d_to_2d_backward(const tp_geom* geom, const void* grad_out, const void* src, const float* rot,
+                                    const float* shifts, void* grad_src, float* grad_rot, float* grad_shifts,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  TRY(check_geom(geom));
+  TRY(check_shifts(geom, shifts));
+  TRY(check_ptr(grad_out, "grad_out", 8));
+  TRY(check_ptr(rot, "rot", 4));
+  TRY(check_opt(shifts, "shifts", 4));
+  TRY(check_opt(grad_src, "grad_src", 8));
+  TRY(check_opt(grad_rot, "grad_rot", 4));
+  TRY(check_opt(grad_shifts, "grad_shifts", 4));
+  TRY(check_opt(workspace, "workspace", 8));
+  if ((grad_rot || grad_shifts) && !src) return fail(TP_E_NULL, "src is NULL but rotation/shift grads are requested");
+  TRY(check_opt(src, "src", 8));
+  if (grad_shifts && !shifts) return fail(TP_E_NULL, "grad_shifts requested without shifts");
+  TRY(check_workspace(geom, TP_OP_PROJECT_2D_BACKWARD, workspace, ws_bytes));
+  TRY(check_device());
+  const tproj::KGeom k = kgeom(geom);
+  hipStream_t st = (hipStream_t)stream;
+  const Ws2 w = ws2_layout(geom, TP_OP_PROJECT_2D_BACKWARD, workspace);
+  if (grad_src)
+    LAUNCH(tproj::launch2_bp(k, geom->interp, (const float2*)grad_out, nullptr, rot, shifts, w.mx, w.parts,
+                             (float2*)grad_src, nullptr, st),
+           "2D accumulation");
+  if (grad_rot || grad_shifts) {
+    if (grad_rot) LAUNCH(tproj::launch_zero(grad_rot, 4 * (int64_t)geom->Br * geom->P, st), "zero grad_rot");
+    if (grad_shifts) LAUNCH(tproj::launch_zero(grad_shifts, 2 * (int64_t)geom->Bs * geom->P, st), "zero grad_shifts");
+    LAUNCH(tproj::launch2_expand_c(k, (const float2*)src, w.ec, st), "2D source extension");
+    LAUNCH(tproj::launch2_grad(k, geom->interp, w.ec, nullptr, (const float2*)grad_out, nullptr, rot, shifts, grad_rot,
+                               grad_shifts, st),
+           "2D rotation/shift grads");
+  }
+  return ok();
+}
+
+tp_status backproject_2d_to_2d(const tp_geom* geom, const void* images, const float* weights, const float* rot,
+                               const float* shifts, void* data, float* weight_out, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  TRY(check_geom(geom));
+  TRY(check_shifts(geom, shifts));
+  TRY(check_ptr(images, "images", 8));
+  TRY(check_ptr(rot, "rot", 4));
+  TRY(check_opt(shifts, "shifts", 4));
+  TRY(check_opt(weights, "weights", 4));
+  TRY(check_ptr(data, "data", 8));
+  TRY(check_opt(weight_out, "weight_out", 4));
+  TRY(check_opt(workspace, "workspace", 8));
+  if ((weights == nullptr) != (weight_out == nullptr))
+    return fail(TP_E_NULL, "weights and weight_out must both be given or both be NULL");
+  TRY(check_workspace(geom, TP_OP_BACKPROJECT_2D, workspace, ws_bytes));
+  TRY(check_device());
+  const tproj::KGeom k = kgeom(geom);
+  hipStream_t st = (hipStream_t)stream;
+  const Ws2 w = ws2_layout(geom, TP_OP_BACKPROJECT_2D, workspace);
+  LAUNCH(tproj::launch2_bp(k, geom->interp, (const float2*)images, weights, rot, shifts, w.mx, w.parts, (float2*)data,
+                           weight_out, st),
+         "2D accumulation");
+  return ok();
+}
+
+tp_status backproject_2d_to_2d_backward(const tp_geom* geom, const void* grad_data, const float* grad_weight,
+                                        const void* images, const float* weights, const float* rot,
+                                        const float* shifts, void* grad_images, float* grad_weights,
+                                        float* grad_rot, float* grad_shifts, void* workspace, size_t ws_bytes,
+                                        void* stream) {
+  TRY(check_geom(geom));
+  TRY(check_shifts(geom, shifts));
+  TRY(check_ptr(grad_data, "grad_data", 8));
+  TRY(check_ptr(rot, "rot", 4));
+  TRY(check_opt(shifts, "shifts", 4));
+  TRY(check_opt(grad_weight, "grad_weight", 4));
+  TRY(check_opt(images, "images", 8));
+  TRY(check_opt(weights, "weights", 4));
+  TRY(check_opt(grad_images, "grad_images", 8));
+  TRY(check_opt(grad_weights, "grad_weights", 4));
+  TRY(check_opt(grad_rot, "grad_rot", 4));
+  TRY(check_opt(grad_shifts, "grad_shifts", 4));
+  TRY(check_opt(workspace, "workspace", 8));
+  if ((grad_rot || grad_shifts) && !images) return fail(TP_E_NULL, "images is NULL but rotation/shift grads are requested");
+  if (grad_rot && grad_weight && !weights) return fail(TP_E_NULL, "weights is NULL but grad_weight and grad_rot are given");
+  if (grad_shifts && !shifts) return fail(TP_E_NULL, "grad_shifts requested without shifts");
+  TRY(check_workspace(geom, TP_OP_BACKPROJECT_2D_BACKWARD, workspace, ws_bytes));
+  TRY(check_device());
+  const tproj::KGeom k = kgeom(geom);
+  hipStream_t st = (hipStream_t)stream;
+  const Ws2 w = ws2_layout(geom, TP_OP_BACKPROJECT_2D_BACKWARD, workspace);
+  LAUNCH(tproj::launch2_expand_c(k, (const float2*)grad_data, w.ec, st), "2D source extension");
+  if (grad_weight) LAUNCH(tproj::launch2_expand_r(k, grad_weight, w.er, st), "2D weight extension");
+  if (grad_images)
+    LAUNCH(tproj::launch2_gather_c(k, geom->interp, w.ec, rot, shifts, (float2*)grad_images, st), "2D projection");
+  if (grad_weights) {
+    if (grad_weight) LAUNCH(tproj::launch2_gather_r(k, geom->interp, w.er, rot, grad_weights, st), "2D weight projection");
+    else LAUNCH(tproj::launch_zero(grad_weights, img_elems(geom), st), "zero grad_weights");
+  }
+  if (grad_rot || grad_shifts) {
+    if (grad_rot) LAUNCH(tproj::launch_zero(grad_rot, 4 * (int64_t)geom->Br * geom->P, st), "zero grad_rot");
+    if (grad_shifts) LAUNCH(tproj::launch_zero(grad_shifts, 2 * (int64_t)geom->Bs * geom->P, st), "zero grad_shifts");
+    const bool wch = grad_weight != nullptr && weights != nullptr;
+    LAUNCH(tproj::launch2_grad(k, geom->interp, w.ec, wch ? w.er : nullptr, (const float2*)images,
+                               wch ? weights : nullptr, rot, shifts, grad_rot, grad_shifts, st),
+           "2D rotation/shift grads");
   }
   return ok();
 }

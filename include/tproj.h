@@ -95,7 +95,10 @@ typedef struct {
 } tp_geom;
 
 /* Operation ids for tp_workspace_size. */
-enum { TP_OP_PROJECT = 0, TP_OP_PROJECT_BACKWARD = 1, TP_OP_BACKPROJECT = 2, TP_OP_BACKPROJECT_BACKWARD = 3 };
+enum {
+  TP_OP_PROJECT = 0, TP_OP_PROJECT_BACKWARD = 1, TP_OP_BACKPROJECT = 2, TP_OP_BACKPROJECT_BACKWARD = 3,
+  TP_OP_PROJECT_2D = 4, TP_OP_PROJECT_2D_BACKWARD = 5, TP_OP_BACKPROJECT_2D = 6, TP_OP_BACKPROJECT_2D_BACKWARD = 7
+};
 
 /* 3D -> 2D forward (rotated central slice; Spanish page 2, French page 2).
  *   vol     [Bv][D][D][D/2+1] complex64, read
@@ -144,6 +147,47 @@ tp_status backproject_2d_to_3d_backward(const tp_geom* geom, const void* grad_da
                                         const float* rot, const float* shifts, void* grad_images,
                                         float* grad_weights, float* grad_rot, float* grad_shifts, void* workspace,
                                         size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * 2D -> 2D (rotation of 2D Fourier data and accumulation into a 2D
+ * reconstruction; Dutch page Methodologie, operations 1 and 2; Spanish page
+ * 2).  The same definitions as the 3D calls one dimension down: the source is
+ * a 2D rfft image of box D, the maps are 2x2, p = o * R * (kx, ky):
+ *   src      [Bv][D][D/2+1] complex64 (the 2D reconstruction / reference)
+ *   rot      [Br][P][2][2] float32, row-major, rows and columns (x, y)
+ *   shifts, images, weights, masks, phases, Friedel rule: as above.
+ * geom is the same struct (D = the source box).  Workspace: the periodic
+ * Hermitian extension of the source(s) and, for the accumulation, per
+ * workgroup partial sums (tp_workspace_size with the TP_OP_*_2D ids).
+ * ------------------------------------------------------------------------- */
+
+/* out [B][P][H][H/2+1] complex64 = M * phi * I(src[bv], o R k)             */
+tp_status project_2d_to_2d(const tp_geom* geom, const void* src, const float* rot, const float* shifts, void* out,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* Backward of project_2d_to_2d: grad_src [Bv][D][D/2+1] complex64 (the
+ * accumulation of grad_out), grad_rot [Br][P][2][2] (o * sum_k M Re(conj(G)
+ * phi dI/dp_i) k_j), grad_shifts [Bs][P][2]; each NULL if not requested; src
+ * is needed for grad_rot / grad_shifts.                                    */
+tp_status project_2d_to_2d_backward(const tp_geom* geom, const void* grad_out, const void* src, const float* rot,
+                                    const float* shifts, void* grad_src, float* grad_rot, float* grad_shifts,
+                                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Accumulation into 2D reconstructions (the adjoint of project_2d_to_2d),
+ * with real weights: data [Bv][D][D/2+1] complex64, weight_out
+ * [Bv][D][D/2+1] float32 (NULL iff weights NULL), both written.             */
+tp_status backproject_2d_to_2d(const tp_geom* geom, const void* images, const float* weights, const float* rot,
+                               const float* shifts, void* data, float* weight_out, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/* Backward of backproject_2d_to_2d (as backproject_2d_to_3d_backward, with
+ * grad_data [Bv][D][D/2+1] complex64 and grad_weight [Bv][D][D/2+1] float32
+ * or NULL; grad_rot is [Br][P][2][2]).                                      */
+tp_status backproject_2d_to_2d_backward(const tp_geom* geom, const void* grad_data, const float* grad_weight,
+                                        const void* images, const float* weights, const float* rot,
+                                        const float* shifts, void* grad_images, float* grad_weights,
+                                        float* grad_rot, float* grad_shifts, void* workspace, size_t ws_bytes,
+                                        void* stream);
 
 /* Bytes of workspace the operation `op` (TP_OP_*) needs for this geometry
  * (0 when none).  Returns (size_t)-1 for an invalid geometry.  The brick

@@ -1,0 +1,128 @@
+"""GPU parity of the 2D -> 2D ops (through the C ABI) against the fp64 CPU
+oracle: rotation of 2D Fourier data, the accumulation into 2D
+reconstructions, and both backward passes.  Tolerances (relative L2 over the
+whole output) as for the 3D ops: 1e-5 for gathers, 1e-4 for accumulations and
+gradients.  The cases span the LDS path (D <= 128) and the global-memory path
+(D > 128), ragged rows, cutoffs, oversampling, batch broadcasting,
+non-Hermitian sources and general (non-orthonormal, some degenerate) maps.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import back_projection_amd as bp
+import oracle
+from back_projection_amd import workloads
+from tests.helpers import dev, log, rel
+
+pytestmark = pytest.mark.gpu
+
+FWD_TOL = 1e-5
+BWD_TOL = 1e-4
+
+# name, D, H, P, B, Bv, Br, Bs, interp, o, r, hermitian, map kind
+CASES = [
+    ("cubic-basic", 16, 16, 5, 1, 1, 1, 1, 1, 1.0, -1.0, True, "rot"),
+    ("linear-ragged-cut", 24, 20, 7, 1, 1, 1, 0, 0, 1.0, 9.5, True, "rot"),
+    ("cubic-bcast-src", 20, 24, 4, 2, 1, 2, 1, 1, 1.5, 10.0, False, "rot"),
+    ("cubic-bcast-rot", 16, 16, 3, 3, 3, 1, 3, 1, 1.0, -1.0, False, "rot"),
+    ("linear-oversampled", 12, 12, 3, 2, 2, 2, 0, 0, 2.5, -1.0, True, "rot"),
+    ("cubic-general-map", 32, 32, 6, 1, 1, 1, 1, 1, 1.0, 16.0, False, "wild"),
+    ("cubic-degenerate", 16, 16, 4, 1, 1, 1, 1, 1, 1.0, -1.0, False, "flat"),
+    ("cubic-many-poses", 64, 64, 300, 1, 1, 1, 1, 1, 1.0, 32.0, True, "rot"),
+    ("cubic-D128-lds", 128, 128, 20, 1, 1, 1, 1, 1, 1.0, 64.0, True, "rot"),
+    ("cubic-D192-global", 192, 160, 6, 1, 1, 1, 1, 1, 1.0, 70.0, True, "rot"),
+]
+
+
+def rotations2d(rng, n):
+    a = rng.uniform(0, 2 * np.pi, n)
+    return np.stack([np.stack([np.cos(a), -np.sin(a)], -1), np.stack([np.sin(a), np.cos(a)], -1)], -2)
+
+
+def make2d(D, H, P, B, Bv, Br, Bs, interp, o, r, herm, kind, seed):
+    rng = np.random.default_rng(seed)
+    if herm:
+        src = np.fft.rfft2(rng.standard_normal((Bv, D, D))).astype(np.complex64)
+    else:
+        src = workloads.random_complex(rng, (Bv, D, D // 2 + 1))
+    rot = rotations2d(rng, Br * P).reshape(Br, P, 2, 2)
+    if kind == "wild":
+        rot = rot * rng.uniform(0.5, 2.0, (Br, P, 1, 1)) + 0.3 * rng.standard_normal((Br, P, 2, 2))
+    if kind == "flat":   # rank-one maps on every other pose (the direct path)
+        rot[:, ::2, 1, :] = rot[:, ::2, 0, :] * 0.5
+    rot = rot.astype(np.float32)
+    sh = rng.uniform(-4, 4, (Bs, P, 2)).astype(np.float32) if Bs else None
+    imgs = workloads.random_complex(rng, (B, P, H, H // 2 + 1))
+    wts = rng.random((B, P, H, H // 2 + 1)).astype(np.float32)
+    gd = workloads.random_complex(rng, (Bv, D, D // 2 + 1))
+    gw = rng.standard_normal((Bv, D, D // 2 + 1)).astype(np.float32)
+    return src, rot, sh, imgs, wts, gd, gw
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_2d_all_ops(case):
+    name, D, H, P, B, Bv, Br, Bs, interp, o, r, herm, kind = case
+    log(f"[parity2d] {name}")
+    src, rot, sh, imgs, wts, gd, gw = make2d(D, H, P, B, Bv, Br, Bs, interp, o, r, herm, kind,
+                                             seed=zlib.crc32(name.encode()))
+    ts, tr, tsh, ti, tw, tgd, tgw = dev(src, rot, sh, imgs, wts, gd, gw)
+    kw = dict(interp=interp, oversampling=o, radius_cutoff=r)
+    okw = dict(interp=interp, o=o, r=r)
+
+    out = bp.project_2d_to_2d(ts, tr, tsh, H=H, B=B, **kw)
+    assert rel(out, oracle.project2d(src, rot, sh, H=H, B=B, **okw)) <= FWD_TOL
+
+    gx, gr, gs = bp.project_2d_to_2d_backward(ti, ts, tr, tsh, **kw)
+    rgx, rgr, rgs = oracle.project2d_backward(imgs, src, rot, sh, **okw)
+    assert rel(gx, rgx) <= BWD_TOL, ("grad_src", rel(gx, rgx))
+    assert rel(gr, rgr) <= BWD_TOL, ("grad_rot", rel(gr, rgr))
+    if sh is not None:
+        assert rel(gs, rgs) <= BWD_TOL, ("grad_shifts", rel(gs, rgs))
+
+    d, w = bp.backproject_2d_to_2d(ti, tr, tw, tsh, D=D, Bv=Bv, **kw)
+    rd, rw = oracle.backproject2d(imgs, rot, wts, sh, D=D, Bv=Bv, **okw)
+    assert rel(d, rd) <= BWD_TOL, ("bp data", rel(d, rd))
+    assert rel(w, rw) <= BWD_TOL, ("bp weights", rel(w, rw))
+
+    gi, gwo, gr2, gs2 = bp.backproject_2d_to_2d_backward(tgd, ti, tr, tgw, tw, tsh, **kw)
+    rgi, rgwo, rgr2, rgs2 = oracle.backproject2d_backward(gd, imgs, rot, gw, wts, sh, **okw)
+    assert rel(gi, rgi) <= FWD_TOL, ("grad_images", rel(gi, rgi))
+    assert rel(gwo, rgwo) <= FWD_TOL, ("grad_weights", rel(gwo, rgwo))
+    assert rel(gr2, rgr2) <= BWD_TOL, ("bp grad_rot", rel(gr2, rgr2))
+    if sh is not None:
+        assert rel(gs2, rgs2) <= BWD_TOL, ("bp grad_shifts", rel(gs2, rgs2))
+
+
+def test_2d_requested_outputs_and_empty_weights():
+    src, rot, sh, imgs, wts, gd, gw = make2d(16, 16, 3, 1, 1, 1, 1, 1, 1.0, -1.0, True, "rot", 3)
+    ts, tr, tsh, ti, tw, tgd = dev(src, rot, sh, imgs, wts, gd)
+    gx, gr, gs = bp.project_2d_to_2d_backward(ti, ts, tr, tsh, need_src=False, need_shifts=False)
+    assert gx is None and gs is None
+    _, rgr, _ = oracle.project2d_backward(imgs, src, rot, sh, interp=1)
+    assert rel(gr, rgr) <= BWD_TOL
+    d, none = bp.backproject_2d_to_2d(ti, tr, None, tsh, D=16)
+    assert none is None
+    assert rel(d, oracle.backproject2d(imgs, rot, None, sh, D=16, interp=1)[0]) <= BWD_TOL
+    gi, gwo, _, _ = bp.backproject_2d_to_2d_backward(tgd, ti, tr, None, tw, tsh, need_rot=False, need_shifts=False)
+    assert float(gwo.abs().max()) == 0.0
+    assert rel(gi, oracle.project2d(gd, rot, sh, H=16, interp=1)) <= FWD_TOL
+
+
+def test_2d_adjoint_identity_fp32():
+    """<F x, y> = <x, F* y> for the GPU forward and accumulation themselves."""
+    rng = np.random.default_rng(4)
+    D = H = 64
+    P = 50
+    x = workloads.random_complex(rng, (1, D, D // 2 + 1))
+    y = workloads.random_complex(rng, (1, P, H, H // 2 + 1))
+    rot = rotations2d(rng, P).reshape(1, P, 2, 2).astype(np.float32)
+    sh = rng.uniform(-3, 3, (1, P, 2)).astype(np.float32)
+    tx, ty, tr, tsh = dev(x, y, rot, sh)
+    Fx = bp.project_2d_to_2d(tx, tr, tsh, radius_cutoff=30.0)
+    Fty, _ = bp.backproject_2d_to_2d(ty, tr, None, tsh, D=D, radius_cutoff=30.0)
+    lhs = float(torch.sum(torch.conj(Fx) * ty).real)
+    rhs = float(torch.sum(torch.conj(tx) * Fty).real)
+    assert abs(lhs - rhs) <= 1e-5 * (abs(lhs) + float(Fx.abs().norm() * ty.abs().norm()))
