@@ -234,3 +234,46 @@ def upstream_grads(seed: int, B: int, P: int, H: int, block: int = 256) -> np.nd
             blk = random_complex(g, (block, H, H // 2 + 1))
             out[b, j0:j0 + block] = blk[:min(block, P - j0)]
     return out
+
+
+# ---------------------------------------------------------------------------
+# 2D -> 2D workload (the 2D analogue of workload 3)
+# ---------------------------------------------------------------------------
+NAME_2D = ("2D D128 cubic forward+backward (source, rotation, shift grads) and accumulation with weights, "
+           "16384 poses, shifts U(-5,5), r=64")
+
+
+def random_rotations_2d(rng, n: int) -> np.ndarray:
+    """float32 [n, 2, 2] rotations by angles uniform in [0, 2 pi)."""
+    a = rng.uniform(0.0, 2.0 * np.pi, n)
+    c, s = np.cos(a), np.sin(a)
+    return np.stack([np.stack([c, -s], -1), np.stack([s, c], -1)], -2).astype(np.float32)
+
+
+def blob_image_rfft(rng, D: int, n_blobs: int, radius: float) -> np.ndarray:
+    """rfft2 (after ifftshift) of a real D x D image of isotropic 2D Gaussians,
+    centres uniform in a disc about the box centre, sigma ~ U(1,3), amplitude
+    ~ U(0.5,1); complex64 [D, D//2+1], DC at index 0."""
+    f = np.zeros((D, D), np.float32)
+    ang = rng.uniform(0, 2 * np.pi, n_blobs)
+    rad = radius * np.sqrt(rng.random(n_blobs))
+    sig = rng.uniform(1.0, 3.0, n_blobs)
+    amp = rng.uniform(0.5, 1.0, n_blobs)
+    y, x = np.meshgrid(np.arange(D), np.arange(D), indexing="ij")
+    for a, r, s_, m in zip(ang, rad, sig, amp):
+        cx, cy = D // 2 + r * np.cos(a), D // 2 + r * np.sin(a)
+        f += (m * np.exp(-((x - cx) ** 2 + (y - cy) ** 2) / (2 * s_ * s_))).astype(np.float32)
+    return np.fft.rfft2(np.fft.ifftshift(f)).astype(np.complex64)
+
+
+def make_2d(P: int = 16384, D: int = 128) -> dict:
+    """Seeded 2D workload: source, rotations, shifts, upstream gradients,
+    images and CTF^2-like weights for the accumulation."""
+    rng = np.random.default_rng(2002)
+    src = blob_image_rfft(rng, D, 200, D / 3)[None]
+    rot = random_rotations_2d(rng, P)[None]
+    shifts = random_shifts(rng, P, 5.0)[None]
+    grad_out = upstream_grads(2101, 1, P, D)
+    weights = ctf2_like_weights(np.random.default_rng(2111), P, D, P)[None]
+    return dict(name=NAME_2D, D=D, H=D, P=P, radius=64.0, src=src, rot=rot, shifts=shifts, grad_out=grad_out,
+                weights=weights)

@@ -265,6 +265,43 @@ def run_workload_ops(cfg, steps, warmup, bp, workloads, torch, details):
     details.setdefault("workloads", {})[str(cfg)] = res
 
 
+def run_2d(steps, warmup, bp, workloads, torch, details):
+    """The 2D -> 2D ops on the 2D analogue of the D=128 cubic workload
+    (stderr/details only): forward, its full backward (source, rotation and
+    shift grads), the accumulation with weights and its backward."""
+    w = workloads.make_2d()
+    dev = torch.device("cuda:0")
+    ts, tr, tsh, tg, tw = (torch.from_numpy(w[k]).to(dev) for k in ("src", "rot", "shifts", "grad_out", "weights"))
+    r, D, P = w["radius"], w["D"], w["P"]
+    n_in = in_mask_pixels(w["H"], r)
+    out = torch.empty((1, P, D, D // 2 + 1), dtype=torch.complex64, device=dev)
+    calls = {
+        "forward": lambda: bp.project_2d_to_2d(ts, tr, tsh, out=out, radius_cutoff=r),
+        "backward": lambda: bp.project_2d_to_2d_backward(tg, ts, tr, tsh, radius_cutoff=r),
+        "accumulate_weights": lambda: bp.backproject_2d_to_2d(tg, tr, tw, tsh, D=D, radius_cutoff=r),
+    }
+    # backward of the accumulation: upstream gradients of the data (the source
+    # serves) and of the weight reconstruction (uniform random)
+    gw = torch.rand((1, D, D // 2 + 1), dtype=torch.float32, device=dev)
+    calls["accumulate_backward"] = lambda: bp.backproject_2d_to_2d_backward(ts, tg, tr, gw, tw, tsh, radius_cutoff=r)
+    # tap bytes per in-mask pixel: 16 taps x 8 B (complex), x 12 B with the
+    # real weight channel; the gradient passes gather value and derivatives
+    # from the same taps
+    taps = {"forward": 128, "backward": 256, "accumulate_weights": 192, "accumulate_backward": 2 * 192}
+    res = {"workload": w["name"]}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        ms, _ = time_calls(fn, steps, torch)
+        tb = P * n_in * taps[name]
+        res[name] = {"ms": round(ms, 4), "proj_per_s": round(P / (ms * 1e-3), 1),
+                     "tap_GBps": round(tb / (ms * 1e-3) / 1e9, 1),
+                     "l2_frac": round(tb / (ms * 1e-3) / 1e9 / L2_PEAK_GBS, 4)}
+    res["fwd_bwd_proj_per_s"] = round(P / ((res["forward"]["ms"] + res["backward"]["ms"]) * 1e-3), 1)
+    eprint(f"[bench] 2d: {json.dumps(res)}")
+    details["2d"] = res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +310,7 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=16384, help="poses of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-workloads", action="store_true", help="also time the other four workloads (stderr)")
+    ap.add_argument("--twod", action="store_true", help="also time the 2D -> 2D ops on their D=128 workload (stderr)")
     ap.add_argument("--details", default=None, help="write per-kernel details as JSON to this file")
     ap.add_argument("--peaks", action="store_true", help="measure HBM and L2-resident bandwidths and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -428,6 +466,9 @@ def main():
         torch.cuda.empty_cache()
         for cfg in (1, 2, 4, 5):
             run_workload_ops(cfg, max(3, args.steps // 2), 1, bp, workloads, torch, details)
+    if args.twod or args.all_workloads:
+        torch.cuda.empty_cache()
+        run_2d(max(3, args.steps // 2), 1, bp, workloads, torch, details)
     if args.details:
         with open(args.details, "w") as f:
             json.dump(details, f, indent=1)
