@@ -1,7 +1,7 @@
 // Launchers of the 2D -> 2D kernels (host side).  The geometry is the 3D one
 // with D the box of the 2D source ([Bv][D][D/2+1]) and 2x2 maps
 // ([Br][P][2][2], row-major).  E is the periodic Hermitian extension of a
-// source, [Bv][D][D+1] (rows padded).
+// source, [Bv][e2_size(D)] (layout below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -10,6 +10,13 @@
 #include "device_common.h"
 
 namespace tproj {
+
+// Layout of the periodic extension E: positions x, y in [-2, D + 2) (a margin
+// of two beyond the box on every side, so that no tap of a sample reduced to
+// [0, D) needs a wrap), row stride D + 5 entries.
+__host__ __device__ inline int e2_rows(int D) { return D + 4; }
+__host__ __device__ inline int e2_stride(int D) { return D + 5; }
+__host__ __device__ inline int64_t e2_size(int D) { return (int64_t)e2_rows(D) * e2_stride(D); }
 
 hipError_t launch_zero(float* p, int64_t n, hipStream_t st);
 

@@ -4,11 +4,13 @@
 // operations 1 and 2; Spanish "Resumen tecnico" 2; French "Resume technique" 2).
 //
 // The 2D source is small (a D x (D/2+1) rfft image), so every kernel works on
-// its periodic Hermitian extension E[y][x], x, y in [0, D): a pre-pass writes
-// E once (x <= D/2 as stored, x > D/2 the conjugated Friedel mate), and a tap
-// (tx, ty) is then E[ty mod D][tx mod D] -- no per-tap branch.  Rows of E are
-// padded to D + 1 entries, so the bank pair of an 8-byte entry changes with
-// both coordinates.
+// its periodic Hermitian extension E[y][x]: a pre-pass writes E once for x, y
+// in [-2, D + 2) (the entry of (x mod D, y mod D): as stored for x mod D <=
+// D/2, else the conjugated Friedel mate).  A sample's floor is reduced to
+// [0, D) once per axis; its taps then lie in the margin-extended box, at fixed
+// offsets from the first one -- no per-tap wrap or branch, rows of contiguous
+// taps.  The row stride is D + 5 entries, so the bank pair of an 8-byte entry
+// changes with both coordinates.
 //
 // k2_expand     source -> E (complex, or real for the weight channel)
 // k2_gather     forward: M * phi * I(E, p); E staged in LDS when it fits
@@ -52,17 +54,18 @@ __device__ __forceinline__ float conj_of(float v) { return v; }
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) k2_expand(const T* __restrict__ X, T* __restrict__ E, KGeom g) {
-  const int D = g.D, ES = D + 1;
-  const int64_t n = (int64_t)g.Bv * D * D;
+  const int D = g.D, EW = e2_rows(D), ES = e2_stride(D);
+  const int64_t n = (int64_t)g.Bv * EW * EW;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int x = (int)(i % D);
-    const int y = (int)((i / D) % D);
-    const int v = (int)(i / ((int64_t)D * D));
+    const int xp = (int)(i % EW);
+    const int yp = (int)((i / EW) % EW);
+    const int v = (int)(i / ((int64_t)EW * EW));
+    const int x = pmod_int(xp - 2, D), y = pmod_int(yp - 2, D);
     const T* Xv = X + (int64_t)v * D * g.W;
     T val;
     if (x <= g.half) val = Xv[(int64_t)y * g.W + x];
     else val = conj_of(Xv[(int64_t)((D - y) % D) * g.W + (D - x)]);
-    E[((int64_t)v * D + y) * ES + x] = val;
+    E[(int64_t)v * e2_size(D) + (int64_t)yp * ES + xp] = val;
   }
 }
 
@@ -73,25 +76,26 @@ __device__ __forceinline__ void slice_coord2(const KGeom& g, const float* R, flo
   py = g.o * fmaf(R[3], ky, R[2] * kx);
 }
 
-// Tap columns and row offsets of E for the sample p (NT per axis).
+// floor(p) reduced to [0, D): floor - D floor(floor / D), exact for the
+// integer-valued floats that safe_floor returns (one correction step covers
+// the rounding of the quotient).
+__device__ __forceinline__ int reduce_mod(float fl, const KGeom& g) {
+  const float D = (float)g.D;
+  float m = fl - D * floorf(fl * (1.0f / D));
+  m = m >= D ? m - D : m;
+  m = m < 0.f ? m + D : m;
+  return (int)m;
+}
+
+// Index in E of the first tap of the sample p (NT per axis; the others at
+// + b * stride + a), and the fractional parts.
 template <int NT>
-__device__ __forceinline__ void taps2(const KGeom& g, float px, float py, float& fx, float& fy, int xi[NT],
-                                      int yo[NT]) {
+__device__ __forceinline__ int taps2(const KGeom& g, float px, float py, float& fx, float& fy) {
   const float flx = safe_floor(px), fly = safe_floor(py);
   fx = px - flx;
   fy = py - fly;
-  const int x0 = pmod_int((int)flx + first_tap<NT>(), g.D), y0 = pmod_int((int)fly + first_tap<NT>(), g.D);
-#pragma unroll
-  for (int a = 0; a < NT; ++a) {
-    // x0 + a < D + NT - 1 <= 3 D for every even D >= 2: two wraps suffice
-    int x = x0 + a, y = y0 + a;
-    x = x >= g.D ? x - g.D : x;
-    x = x >= g.D ? x - g.D : x;
-    y = y >= g.D ? y - g.D : y;
-    y = y >= g.D ? y - g.D : y;
-    xi[a] = x;
-    yo[a] = y * (g.D + 1);
-  }
+  const int x0 = reduce_mod(flx, g), y0 = reduce_mod(fly, g);
+  return (y0 + 2 + first_tap<NT>()) * e2_stride(g.D) + (x0 + 2 + first_tap<NT>());
 }
 
 __device__ __forceinline__ float2 zero2(float2) { return make_float2(0.f, 0.f); }
@@ -101,16 +105,17 @@ __device__ __forceinline__ void fma2(float w, float v, float& a) { a = fmaf(w, v
 
 // Value (and with DERIV the derivatives along x and y) of the interpolant.
 template <int NT, bool DERIV, typename T>
-__device__ __forceinline__ void interp2(const T* E, const int xi[NT], const int yo[NT], const float wx[NT],
-                                        const float wy[NT], const float dx[NT], const float dy[NT], T& I, T* dI) {
+__device__ __forceinline__ void interp2(const T* E, int base, int ES, const float wx[NT], const float wy[NT],
+                                        const float dx[NT], const float dy[NT], T& I, T* dI) {
   I = zero2(T{});
   if constexpr (DERIV) { dI[0] = zero2(T{}); dI[1] = zero2(T{}); }
 #pragma unroll
   for (int b = 0; b < NT; ++b) {
     T r = zero2(T{}), rx = zero2(T{});
+    const T* row = E + base + b * ES;
 #pragma unroll
     for (int a = 0; a < NT; ++a) {
-      const T v = E[yo[b] + xi[a]];
+      const T v = row[a];
       fma2(wx[a], v, r);
       if constexpr (DERIV) fma2(dx[a], v, rx);
     }
@@ -125,7 +130,7 @@ __device__ __forceinline__ void interp2(const T* E, const int xi[NT], const int 
 // E of volume v into LDS (rows padded as in global memory).
 template <typename T>
 __device__ __forceinline__ void stage_e(T* lds, const T* __restrict__ E, const KGeom& g, int v) {
-  const int n = g.D * (g.D + 1);
+  const int n = (int)e2_size(g.D);
   const T* src = E + (int64_t)v * n;
   for (int i = threadIdx.x; i < n; i += blockDim.x) lds[i] = src[i];
 }
@@ -140,7 +145,8 @@ __global__ void __launch_bounds__(T2) k2_gather(const T* __restrict__ E, const f
                                                 int list_len) {
   extern __shared__ __align__(16) unsigned char smem2[];
   const int vsel = blockIdx.y;
-  const T* src = E + (int64_t)vsel * g.D * (g.D + 1);
+  const T* src = E + (int64_t)vsel * e2_size(g.D);
+  const int ES = e2_stride(g.D);
   if constexpr (LDS) {
     stage_e((T*)smem2, E, g, vsel);
     __syncthreads();
@@ -164,13 +170,12 @@ __global__ void __launch_bounds__(T2) k2_gather(const T* __restrict__ E, const f
       const float kx = (float)ikx, ky = (float)iky;
       if (!in_mask(g, kx, ky)) { O[pix] = zero2(T{}); continue; }
       float px, py, fx, fy, wx[NT], wy[NT];
-      int xi[NT], yo[NT];
       slice_coord2(g, R, kx, ky, px, py);
-      taps2<NT>(g, px, py, fx, fy, xi, yo);
+      const int base = taps2<NT>(g, px, py, fx, fy);
       axis_weights<NT>(fx, wx);
       axis_weights<NT>(fy, wy);
       T I;
-      interp2<NT, false>(src, xi, yo, wx, wy, wx, wy, I, (T*)nullptr);
+      interp2<NT, false>(src, base, ES, wx, wy, wx, wy, I, (T*)nullptr);
       if constexpr (CPLX) {
         if (shifts) I = cmul(shift_phase(kx, ky, sx, sy, g.inv_h), I);
       }
@@ -218,7 +223,8 @@ __global__ void __launch_bounds__(T2) k2_grad(const float2* __restrict__ Ec, con
   extern __shared__ __align__(16) unsigned char smem2[];
   __shared__ float red[17 * 6];
   const int vsel = blockIdx.y;
-  const int64_t ne = (int64_t)g.D * (g.D + 1);
+  const int64_t ne = e2_size(g.D);
+  const int ES = e2_stride(g.D);
   const float2* srcc = CPLX ? Ec + vsel * ne : nullptr;
   const float* srcr = REAL ? Er + vsel * ne : nullptr;
   if constexpr (LDS) {
@@ -249,9 +255,8 @@ __global__ void __launch_bounds__(T2) k2_grad(const float2* __restrict__ Ec, con
       const float kx = (float)ikx, ky = (float)iky;
       if (!in_mask(g, kx, ky)) continue;
       float px, py, fx, fy, wx[NT], wy[NT], dx[NT], dy[NT];
-      int xi[NT], yo[NT];
       slice_coord2(g, R, kx, ky, px, py);
-      taps2<NT>(g, px, py, fx, fy, xi, yo);
+      const int base = taps2<NT>(g, px, py, fx, fy);
       axis_weights<NT>(fx, wx);
       axis_weights<NT>(fy, wy);
       axis_dweights<NT>(fx, dx);
@@ -259,7 +264,7 @@ __global__ void __launch_bounds__(T2) k2_grad(const float2* __restrict__ Ec, con
       float e0 = 0.f, e1 = 0.f, im = 0.f;
       if constexpr (CPLX) {
         float2 I, dI[2];
-        interp2<NT, true>(srcc, xi, yo, wx, wy, dx, dy, I, dI);
+        interp2<NT, true>(srcc, base, ES, wx, wy, dx, dy, I, dI);
         float2 phi = make_float2(1.f, 0.f);
         if (shifts) phi = shift_phase(kx, ky, sx, sy, g.inv_h);
         const float2 cc = cmulc(U[img + pix], phi);   // conj(U) * phi
@@ -269,7 +274,7 @@ __global__ void __launch_bounds__(T2) k2_grad(const float2* __restrict__ Ec, con
       }
       if constexpr (REAL) {
         float I, dI[2];
-        interp2<NT, true>(srcr, xi, yo, wx, wy, dx, dy, I, dI);
+        interp2<NT, true>(srcr, base, ES, wx, wy, dx, dy, I, dI);
         const float ur = Ur[img + pix];
         e0 = fmaf(ur, dI[0], e0);
         e1 = fmaf(ur, dI[1], e1);
@@ -387,8 +392,8 @@ __global__ void __launch_bounds__(T2) k2_bp(const float2* __restrict__ Y, const 
   __shared__ float win_scale;
   Acc* acc_t = (Acc*)smem2;
   const int vsel = blockIdx.y;
-  const int ne = g.D * (g.D + 1);
-  constexpr int PER = 17;   // entries per thread: ceil(128 * 129 / 1024)
+  const int ne = (int)e2_size(g.D), ES = e2_stride(g.D);
+  constexpr int PER = 18;   // entries per thread: ceil(132 * 133 / 1024), D <= 128
   float2 sum[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) sum[i] = make_float2(0.f, 0.f);
@@ -439,9 +444,8 @@ __global__ void __launch_bounds__(T2) k2_bp(const float2* __restrict__ Y, const 
         const float kx = (float)ikx, ky = (float)iky;
         if (!in_mask(g, kx, ky)) continue;
         float px, py, fx, fy, wx[NT], wy[NT];
-        int xi[NT], yo[NT];
-        slice_coord2(g, R, kx, ky, px, py);
-        taps2<NT>(g, px, py, fx, fy, xi, yo);
+          slice_coord2(g, R, kx, ky, px, py);
+        const int base = taps2<NT>(g, px, py, fx, fy);
         axis_weights<NT>(fx, wx);
         axis_weights<NT>(fy, wy);
         float2 c;
@@ -456,10 +460,11 @@ __global__ void __launch_bounds__(T2) k2_bp(const float2* __restrict__ Y, const 
 #pragma unroll
         for (int b = 0; b < NT; ++b) {
           const float ur = wy[b] * c.x, ui = wy[b] * c.y;
+          Acc* row = acc_t + base + b * ES;
 #pragma unroll
           for (int a = 0; a < NT; ++a) {
-            if constexpr (WEIGHTS) atomicAdd(&acc_t[yo[b] + xi[a]], (unsigned int)fix_round2(wx[a], ur));
-            else atomicAdd(&acc_t[yo[b] + xi[a]], fix_pair2(wx[a], ur, ui));
+            if constexpr (WEIGHTS) atomicAdd(&row[a], (unsigned int)fix_round2(wx[a], ur));
+            else atomicAdd(&row[a], fix_pair2(wx[a], ur, ui));
           }
         }
       }
@@ -504,7 +509,8 @@ template <int NT, bool WEIGHTS, bool ALL>
 __global__ void __launch_bounds__(256) k2_bp_direct(const float2* __restrict__ Y, const float* __restrict__ Wimg,
                                                     const float* __restrict__ rot, const float* __restrict__ shifts,
                                                     void* __restrict__ parts, KGeom g, int nparts) {
-  const int ne = g.D * (g.D + 1);
+  const int64_t ne = e2_size(g.D);
+  const int ES = e2_stride(g.D);
   for (int bn = blockIdx.x; bn < g.B * g.P; bn += gridDim.x) {
     const int bimg = bn / g.P, n = bn - bimg * g.P;
     const float* R = rot + 4 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
@@ -523,9 +529,8 @@ __global__ void __launch_bounds__(256) k2_bp_direct(const float2* __restrict__ Y
       const float kx = (float)ikx, ky = (float)iky;
       if (!in_mask(g, kx, ky)) continue;
       float px, py, fx, fy, wx[NT], wy[NT];
-      int xi[NT], yo[NT];
       slice_coord2(g, R, kx, ky, px, py);
-      taps2<NT>(g, px, py, fx, fy, xi, yo);
+      const int base = taps2<NT>(g, px, py, fx, fy);
       axis_weights<NT>(fx, wx);
       axis_weights<NT>(fy, wy);
       float2 c;
@@ -538,7 +543,7 @@ __global__ void __launch_bounds__(256) k2_bp_direct(const float2* __restrict__ Y
       for (int b = 0; b < NT; ++b)
         for (int a = 0; a < NT; ++a) {
           const float w = wx[a] * wy[b];
-          const int64_t k = slot + yo[b] + xi[a];
+          const int64_t k = slot + base + b * ES + a;
           if constexpr (WEIGHTS) unsafeAtomicAdd((float*)parts + k, w * c.x);
           else {
             unsafeAtomicAdd((float*)parts + 2 * k, w * c.x);
@@ -549,36 +554,58 @@ __global__ void __launch_bounds__(256) k2_bp_direct(const float2* __restrict__ Y
   }
 }
 
-// Stored entry (v, y, x) = sum over the partial Es of E(y, x) and, for
-// 1 <= x <= D/2 - 1, of conj(E(-y mod D, D - x)) (no conjugate for the real
-// weight channel), in a fixed order.
+// Sum of the entries of E at (x + i D, y + j D), i, j in {-1, 0, 1}, inside
+// the margin-extended box [-2, D + 2)^2 (every tap that aliases to (x, y)).
+template <typename T>
+__device__ __forceinline__ T periodic_sum(const T* E, int D, int x, int y) {
+  T s = zero2(T{});
+  const int ES = e2_stride(D);
+#pragma unroll
+  for (int j = -1; j <= 1; ++j) {
+    const int yy = y + j * D;
+    if (yy < -2 || yy >= D + 2) continue;
+#pragma unroll
+    for (int i = -1; i <= 1; ++i) {
+      const int xx = x + i * D;
+      if (xx < -2 || xx >= D + 2) continue;
+      const T v = E[(int64_t)(yy + 2) * ES + (xx + 2)];
+      if constexpr (sizeof(T) == 8) { s.x += v.x; s.y += v.y; }
+      else s += v;
+    }
+  }
+  return s;
+}
+
+// Stored entry (v, y, x) = sum over the partial Es of every position that
+// aliases to (x, y) and, for 1 <= x <= D/2 - 1, of the conjugate of every
+// position that aliases to the Friedel mate (D - x, -y mod D) (no conjugate
+// for the real weight channel), in a fixed order.
 template <typename T>
 __global__ void __launch_bounds__(256) k2_fold(const T* __restrict__ parts, T* __restrict__ out, KGeom g,
                                                int nparts) {
-  const int D = g.D, ES = D + 1;
-  const int64_t ne = (int64_t)D * ES;
+  const int D = g.D;
+  const int64_t ne = e2_size(D);
   const int64_t n = (int64_t)g.Bv * D * g.W;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const int x = (int)(i % g.W);
     const int y = (int)((i / g.W) % D);
     const int v = (int)(i / ((int64_t)g.W * D));
     const bool mate = x >= 1 && x <= g.half - 1;
-    const int64_t k0 = (int64_t)y * ES + x, k1 = (int64_t)((D - y) % D) * ES + (D - x);
     T s = zero2(T{});
     for (int p = 0; p < nparts; ++p) {
       const T* E = parts + ((int64_t)v * nparts + p) * ne;
-      const T a = E[k0];
+      const T a = periodic_sum(E, D, x, y);
       if constexpr (sizeof(T) == 8) {
         s.x += a.x;
         s.y += a.y;
         if (mate) {
-          const T b = E[k1];
+          const T b = periodic_sum(E, D, D - x, (D - y) % D);
           s.x += b.x;
           s.y -= b.y;
         }
       } else {
         s += a;
-        if (mate) s += E[k1];
+        if (mate) s += periodic_sum(E, D, D - x, (D - y) % D);
       }
     }
     out[i] = s;
@@ -591,7 +618,7 @@ __global__ void __launch_bounds__(256) k2_fold(const T* __restrict__ parts, T* _
 // launchers
 // ---------------------------------------------------------------------------
 int twod_lds_fits(const KGeom& g, size_t bytes_per_entry) {
-  return (size_t)g.D * (g.D + 1) * bytes_per_entry <= (size_t)150 * 1024 && g.D <= 128;
+  return (size_t)e2_size(g.D) * bytes_per_entry <= (size_t)150 * 1024 && g.D <= 128;
 }
 
 static int list_len2(const KGeom& g) { return (g.Bv == 1 ? g.B : 1) * g.P; }
@@ -614,11 +641,11 @@ int twod_parts(const KGeom& g) {
 }
 
 hipError_t launch2_expand_c(const KGeom& g, const float2* X, float2* E, hipStream_t st) {
-  hipLaunchKernelGGL((k2_expand<float2>), dim3(blocks_for((int64_t)g.Bv * g.D * g.D)), dim3(256), 0, st, X, E, g);
+  hipLaunchKernelGGL((k2_expand<float2>), dim3(blocks_for((int64_t)g.Bv * e2_size(g.D))), dim3(256), 0, st, X, E, g);
   return hipGetLastError();
 }
 hipError_t launch2_expand_r(const KGeom& g, const float* X, float* E, hipStream_t st) {
-  hipLaunchKernelGGL((k2_expand<float>), dim3(blocks_for((int64_t)g.Bv * g.D * g.D)), dim3(256), 0, st, X, E, g);
+  hipLaunchKernelGGL((k2_expand<float>), dim3(blocks_for((int64_t)g.Bv * e2_size(g.D))), dim3(256), 0, st, X, E, g);
   return hipGetLastError();
 }
 
@@ -627,7 +654,7 @@ static hipError_t gather_t(const KGeom& g, int interp, const T* E, const float* 
                            hipStream_t st) {
   const int L = list_len2(g);
   const bool lds = twod_lds_fits(g, sizeof(T));
-  const size_t sh = lds ? (size_t)g.D * (g.D + 1) * sizeof(T) : 0;
+  const size_t sh = lds ? (size_t)e2_size(g.D) * sizeof(T) : 0;
   const dim3 grid(L < twod_parts(g) ? L : twod_parts(g), g.Bv), blk(T2);
 #define TP2(NT_, L_)                                                                    \
   do {                                                                                  \
@@ -656,7 +683,7 @@ hipError_t launch2_grad(const KGeom& g, int interp, const float2* Ec, const floa
   const bool c = Ec != nullptr, r = Er != nullptr;
   const size_t per = (c ? sizeof(float2) : 0) + (r ? sizeof(float) : 0);
   const bool lds = twod_lds_fits(g, per);
-  const size_t sh = lds ? (size_t)g.D * (g.D + 1) * per : 0;
+  const size_t sh = lds ? (size_t)e2_size(g.D) * per : 0;
   const dim3 grid(L < twod_parts(g) ? L : twod_parts(g), g.Bv), blk(T2);
 #define TP2G(NT_, C_, R_)                                                                                         \
   do {                                                                                                            \
@@ -678,7 +705,7 @@ hipError_t launch2_grad(const KGeom& g, int interp, const float2* Ec, const floa
 }
 
 size_t twod_bp_parts_bytes(const KGeom& g, bool weights) {
-  const size_t ne = (size_t)g.D * (g.D + 1);
+  const size_t ne = (size_t)e2_size(g.D);
   const size_t np = twod_lds_fits(g, sizeof(unsigned long long)) ? (size_t)twod_parts(g) : 1;
   return (size_t)g.Bv * np * ne * (sizeof(float2) + (weights ? sizeof(float) : 0));
 }
@@ -688,7 +715,7 @@ hipError_t launch2_bp(const KGeom& g, int interp, const float2* Y, const float* 
   const int L = list_len2(g);
   const bool lds = twod_lds_fits(g, sizeof(unsigned long long));
   const int np = lds ? twod_parts(g) : 1;
-  const size_t ne = (size_t)g.D * (g.D + 1);
+  const size_t ne = (size_t)e2_size(g.D);
   float2* pc = (float2*)parts;
   float* pw = (float*)(pc + (size_t)g.Bv * np * ne);
   const dim3 eg(g.B * g.P < 16384 ? g.B * g.P : 16384);

@@ -497,7 +497,7 @@ struct Ws2 {
 
 Ws2 ws2_layout(const tp_geom* g, int op, void* base) {
   const tproj::KGeom k = kgeom(g);
-  const size_t ne = (size_t)g->Bv * g->D * (g->D + 1);
+  const size_t ne = (size_t)g->Bv * tproj::e2_size(g->D);
   const bool ec = op != TP_OP_BACKPROJECT_2D;
   const bool er = op == TP_OP_BACKPROJECT_2D_BACKWARD;
   const bool bp = op == TP_OP_PROJECT_2D_BACKWARD || op == TP_OP_BACKPROJECT_2D;

@@ -105,8 +105,8 @@ def test_workspace_size(L):
     sizes = [L.tp_workspace_size(ctypes.byref(g), op) for op in range(8)]
     assert all(0 <= s < (1 << 32) for s in sizes)
     assert sizes[0] > 0 and sizes[0] % 256 == 0     # brick work list of the forward gather
-    # 2D ops: the source extension [Bv][D][D+1] complex64 at least
-    assert all(s >= g.Bv * g.D * (g.D + 1) * 8 for s in (sizes[4], sizes[5], sizes[7]))
+    # 2D ops: the source extension [Bv][D+4][D+5] complex64 at least
+    assert all(s >= g.Bv * (g.D + 4) * (g.D + 5) * 8 for s in (sizes[4], sizes[5], sizes[7]))
     assert sizes[6] > 0 and all(s % 256 == 0 for s in sizes[4:])
     assert L.tp_workspace_size(ctypes.byref(g), 8) == ctypes.c_size_t(-1).value
     bad = geom(D=3)
