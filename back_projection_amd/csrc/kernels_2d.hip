@@ -579,36 +579,59 @@ __device__ __forceinline__ T periodic_sum(const T* E, int D, int x, int y) {
 // Stored entry (v, y, x) = sum over the partial Es of every position that
 // aliases to (x, y) and, for 1 <= x <= D/2 - 1, of the conjugate of every
 // position that aliases to the Friedel mate (D - x, -y mod D) (no conjugate
-// for the real weight channel), in a fixed order.
+// for the real weight channel), in a fixed order.  A workgroup takes
+// FOLD_E consecutive entries; its FOLD_S slices of threads each sum every
+// FOLD_S-th partial, and the slices are then added in slice order, so the
+// result does not depend on scheduling.
+constexpr int FOLD_E = 16, FOLD_S = 16;
+
 template <typename T>
-__global__ void __launch_bounds__(256) k2_fold(const T* __restrict__ parts, T* __restrict__ out, KGeom g,
-                                               int nparts) {
+__global__ void __launch_bounds__(FOLD_E * FOLD_S) k2_fold(const T* __restrict__ parts, T* __restrict__ out,
+                                                           KGeom g, int nparts) {
+  __shared__ T red[FOLD_S][FOLD_E];
   const int D = g.D;
   const int64_t ne = e2_size(D);
   const int64_t n = (int64_t)g.Bv * D * g.W;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    const int x = (int)(i % g.W);
-    const int y = (int)((i / g.W) % D);
-    const int v = (int)(i / ((int64_t)g.W * D));
-    const bool mate = x >= 1 && x <= g.half - 1;
+  const int le = threadIdx.x % FOLD_E, sl = threadIdx.x / FOLD_E;
+  for (int64_t i0 = (int64_t)blockIdx.x * FOLD_E; i0 < n; i0 += (int64_t)gridDim.x * FOLD_E) {
+    const int64_t i = i0 + le;
     T s = zero2(T{});
-    for (int p = 0; p < nparts; ++p) {
-      const T* E = parts + ((int64_t)v * nparts + p) * ne;
-      const T a = periodic_sum(E, D, x, y);
-      if constexpr (sizeof(T) == 8) {
-        s.x += a.x;
-        s.y += a.y;
-        if (mate) {
-          const T b = periodic_sum(E, D, D - x, (D - y) % D);
-          s.x += b.x;
-          s.y -= b.y;
+    if (i < n) {
+      const int x = (int)(i % g.W);
+      const int y = (int)((i / g.W) % D);
+      const int v = (int)(i / ((int64_t)g.W * D));
+      const bool mate = x >= 1 && x <= g.half - 1;
+      for (int p = sl; p < nparts; p += FOLD_S) {
+        const T* E = parts + ((int64_t)v * nparts + p) * ne;
+        const T a = periodic_sum(E, D, x, y);
+        if constexpr (sizeof(T) == 8) {
+          s.x += a.x;
+          s.y += a.y;
+          if (mate) {
+            const T b = periodic_sum(E, D, D - x, (D - y) % D);
+            s.x += b.x;
+            s.y -= b.y;
+          }
+        } else {
+          s += a;
+          if (mate) s += periodic_sum(E, D, D - x, (D - y) % D);
         }
-      } else {
-        s += a;
-        if (mate) s += periodic_sum(E, D, D - x, (D - y) % D);
       }
     }
-    out[i] = s;
+    red[sl][le] = s;
+    __syncthreads();
+    if (sl == 0 && i < n) {
+      T t = red[0][le];
+#pragma unroll
+      for (int k = 1; k < FOLD_S; ++k) {
+        if constexpr (sizeof(T) == 8) {
+          t.x += red[k][le].x;
+          t.y += red[k][le].y;
+        } else t += red[k][le];
+      }
+      out[i] = t;
+    }
+    __syncthreads();
   }
 }
 
@@ -683,6 +706,14 @@ hipError_t launch2_grad(const KGeom& g, int interp, const float2* Ec, const floa
   const bool c = Ec != nullptr, r = Er != nullptr;
   const size_t per = (c ? sizeof(float2) : 0) + (r ? sizeof(float) : 0);
   const bool lds = twod_lds_fits(g, per);
+  // Both channels together may not fit in LDS where each one does: then one
+  // launch per channel (the gradient terms of the two add up through the same
+  // atomics; the real channel has no phase, so no shift term).
+  if (c && r && !lds && twod_lds_fits(g, sizeof(float2))) {
+    const hipError_t e = launch2_grad(g, interp, Ec, nullptr, U, nullptr, rot, shifts, grad_rot, grad_s, st);
+    if (e != hipSuccess) return e;
+    return launch2_grad(g, interp, nullptr, Er, nullptr, Ur, rot, shifts, grad_rot, grad_s, st);
+  }
   const size_t sh = lds ? (size_t)e2_size(g.D) * per : 0;
   const dim3 grid(L < twod_parts(g) ? L : twod_parts(g), g.Bv), blk(T2);
 #define TP2G(NT_, C_, R_)                                                                                         \
@@ -750,9 +781,10 @@ hipError_t launch2_bp(const KGeom& g, int interp, const float2* Y, const float* 
 #undef TP2D
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned fb = blocks_for((int64_t)g.Bv * g.D * g.W);
-    if (W) hipLaunchKernelGGL((k2_fold<float>), dim3(fb), dim3(256), 0, st, pw, wout, g, np);
-    else hipLaunchKernelGGL((k2_fold<float2>), dim3(fb), dim3(256), 0, st, pc, out, g, np);
+    const int64_t ng = ((int64_t)g.Bv * g.D * g.W + FOLD_E - 1) / FOLD_E;
+    const dim3 fb((unsigned)(ng < 16384 ? ng : 16384)), ft(FOLD_E * FOLD_S);
+    if (W) hipLaunchKernelGGL((k2_fold<float>), fb, ft, 0, st, pw, wout, g, np);
+    else hipLaunchKernelGGL((k2_fold<float2>), fb, ft, 0, st, pc, out, g, np);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -41,25 +41,27 @@ FP32_VECTOR_TFLOPS = 157.3
 # script (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
 # same counter reads for a plain device copy of known size (--copy-calibration).
 # A figure is valid only for the kernel sources it was taken on: it is
-# reported when the digest of back_projection_amd/csrc matches, else null.
+# reported when the digest of the 3D kernel sources matches, else null.
 TRAFFIC = {
     # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
-    "forward": {"sources_sha256": "5adff4850c998855001fb34d15d25409de741ea373e70794b2e3d8d9f6ab31a2",
-               "fetch_bytes": 317374140, "write_bytes": 1183304064},
-    "backward": {"sources_sha256": "5adff4850c998855001fb34d15d25409de741ea373e70794b2e3d8d9f6ab31a2",
-                "fetch_bytes": 2826802982, "write_bytes": 188940288},
-    "gradient": {"sources_sha256": "5adff4850c998855001fb34d15d25409de741ea373e70794b2e3d8d9f6ab31a2",
-                "fetch_bytes": 2785301375, "write_bytes": 120424608},
-    "fold": {"sources_sha256": "5adff4850c998855001fb34d15d25409de741ea373e70794b2e3d8d9f6ab31a2",
-            "fetch_bytes": 292611606, "write_bytes": 8519680},
+    "forward": {"sources_sha256": "6f1e073bc60799fa4cb05bd1cd640a9b99322dca3a5309371bd35e53a0ceb16c",
+               "fetch_bytes": 317289690, "write_bytes": 1183322197},
+    "backward": {"sources_sha256": "6f1e073bc60799fa4cb05bd1cd640a9b99322dca3a5309371bd35e53a0ceb16c",
+                "fetch_bytes": 2826516415, "write_bytes": 188940288},
+    "gradient": {"sources_sha256": "6f1e073bc60799fa4cb05bd1cd640a9b99322dca3a5309371bd35e53a0ceb16c",
+                "fetch_bytes": 2785175420, "write_bytes": 120424608},
+    "fold": {"sources_sha256": "6f1e073bc60799fa4cb05bd1cd640a9b99322dca3a5309371bd35e53a0ceb16c",
+            "fetch_bytes": 292592149, "write_bytes": 8519680},
 }
 
 
 def sources_digest():
+    """Digest of the sources the 3D kernels are built and launched from (the
+    2D-only kernel files are left out: the 3D kernels do not include them)."""
     d = hashlib.sha256()
     csrc = os.path.join(ROOT, "back_projection_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        if name.endswith((".hip", ".h", ".cpp")) and "_2d" not in name:
             d.update(name.encode())
             with open(os.path.join(csrc, name), "rb") as f:
                 d.update(f.read())
