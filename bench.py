@@ -304,6 +304,48 @@ def run_2d(steps, warmup, bp, workloads, torch, details):
     details["2d"] = res
 
 
+def run_sweep(steps, warmup, bp, workloads, torch, details):
+    """The 3D ops on the pages' axes (box size, poses per call, linear vs cubic):
+    forward alone and forward + full backward (volume, rotation, shift grads),
+    radius D/2, shifts U(-5,5) (stderr/details only)."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    rows = []
+    eprint("[bench] sweep:  D  interp     poses   fwd ms  fwd+bwd ms   fwd proj/s  fwd+bwd proj/s  fwd L2 frac")
+    for D in (32, 64, 128, 256):
+        rng = np.random.default_rng(3000 + D)
+        vol = workloads.rfft_volume(workloads.blob_volume_real(D, *workloads.blob_params(rng, 200, D / 3)))
+        tv = torch.from_numpy(vol[None]).to(dev)
+        n_in = in_mask_pixels(D, D / 2)
+        for P in (1024, 16384):
+            tr = torch.from_numpy(workloads.random_rotations(rng, P)[None]).to(dev)
+            ts = torch.from_numpy(workloads.random_shifts(rng, P, 5.0)[None]).to(dev)
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(3100 + D + P)
+            tg = torch.randn((1, P, D, D // 2 + 1), dtype=torch.complex64, device=dev, generator=gen)
+            out = torch.empty_like(tg)
+            for interp in ("linear", "cubic"):
+                fw = lambda: bp.project_3d_to_2d(tv, tr, ts, interp=interp, radius_cutoff=D / 2, out=out)
+                bw = lambda: bp.project_3d_to_2d_backward(tg, tv, tr, ts, interp=interp, radius_cutoff=D / 2)
+                for _ in range(warmup):
+                    fw()
+                    bw()
+                f_ms, _ = time_calls(fw, steps, torch)
+                b_ms, _ = time_calls(bw, steps, torch)
+                taps = 8 if interp == "linear" else 64
+                l2 = P * n_in * taps * 8 / (f_ms * 1e-3) / 1e9 / L2_PEAK_GBS
+                r = {"D": D, "interp": interp, "poses": P, "fwd_ms": round(f_ms, 4), "fwd_bwd_ms": round(f_ms + b_ms, 4),
+                     "fwd_proj_per_s": round(P / (f_ms * 1e-3), 1),
+                     "fwd_bwd_proj_per_s": round(P / ((f_ms + b_ms) * 1e-3), 1), "fwd_l2_frac": round(l2, 4)}
+                rows.append(r)
+                eprint("[bench] sweep: %4d  %-7s %8d %8.3f %11.3f %12.0f %15.0f %12.3f" % (
+                    D, interp, P, f_ms, f_ms + b_ms, r["fwd_proj_per_s"], r["fwd_bwd_proj_per_s"], l2))
+            del tg, out
+        del tv
+        torch.cuda.empty_cache()
+    details["sweep"] = rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,6 +354,7 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=16384, help="poses of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-workloads", action="store_true", help="also time the other four workloads (stderr)")
+    ap.add_argument("--sweep", action="store_true", help="also time the 3D ops over box size, poses and kernel (stderr)")
     ap.add_argument("--twod", action="store_true", help="also time the 2D -> 2D ops on their D=128 workload (stderr)")
     ap.add_argument("--details", default=None, help="write per-kernel details as JSON to this file")
     ap.add_argument("--peaks", action="store_true", help="measure HBM and L2-resident bandwidths and exit")
@@ -468,6 +511,9 @@ def main():
         torch.cuda.empty_cache()
         for cfg in (1, 2, 4, 5):
             run_workload_ops(cfg, max(3, args.steps // 2), 1, bp, workloads, torch, details)
+    if args.sweep:
+        torch.cuda.empty_cache()
+        run_sweep(5, 1, bp, workloads, torch, details)
     if args.twod or args.all_workloads:
         torch.cuda.empty_cache()
         run_2d(max(3, args.steps // 2), 1, bp, workloads, torch, details)
