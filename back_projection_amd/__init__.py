@@ -35,7 +35,9 @@ import torch
 __all__ = [
     "project_3d_to_2d", "project_3d_to_2d_backward", "backproject_2d_to_3d", "backproject_2d_to_3d_backward",
     "project_2d_to_2d", "project_2d_to_2d_backward", "backproject_2d_to_2d", "backproject_2d_to_2d_backward",
-    "TprojError", "lib", "Geom", "LIB_PATH", "HEADER_SYMBOLS", "timing_enable", "timing_read", "KERNEL_CLASSES",
+    "volume_rfft", "images_irfft", "weight_images", "finish_reconstruction",
+    "TprojError", "lib", "Geom", "LIB_PATH", "HEADER_SYMBOLS", "SPECTRAL_SYMBOLS", "timing_enable", "timing_read",
+    "KERNEL_CLASSES",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -47,6 +49,12 @@ HEADER_SYMBOLS = (
     "project_2d_to_2d", "project_2d_to_2d_backward", "backproject_2d_to_2d", "backproject_2d_to_2d_backward",
     "tp_workspace_size", "tp_validate", "tp_status_string", "tp_last_error_detail", "tp_abi_version",
     "tp_timing_enable", "tp_timing_read",
+)
+
+# Every symbol that include/tproj_spectral.h declares.
+SPECTRAL_SYMBOLS = (
+    "tp_volume_rfft_workspace", "tp_volume_rfft", "tp_images_irfft_workspace", "tp_images_irfft",
+    "tp_weight_images", "tp_finish_reconstruction",
 )
 
 OP_PROJECT, OP_PROJECT_BACKWARD, OP_BACKPROJECT, OP_BACKPROJECT_BACKWARD = 0, 1, 2, 3
@@ -102,6 +110,16 @@ def lib():
         L.tp_timing_enable.restype = ctypes.c_int
         L.tp_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.tp_timing_read.restype = ctypes.c_int
+        L.tp_volume_rfft_workspace.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.tp_volume_rfft_workspace.restype = ctypes.c_size_t
+        L.tp_volume_rfft.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.tp_images_irfft_workspace.argtypes = [ctypes.c_int, ctypes.c_int64]
+        L.tp_images_irfft_workspace.restype = ctypes.c_size_t
+        L.tp_images_irfft.argtypes = [ctypes.c_int, ctypes.c_int64, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        L.tp_weight_images.argtypes = [ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp, _vp]
+        L.tp_finish_reconstruction.argtypes = [ctypes.c_int64, _vp, _vp, ctypes.c_float, _vp, _vp]
+        for f in ("tp_volume_rfft", "tp_images_irfft", "tp_weight_images", "tp_finish_reconstruction"):
+            getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -409,3 +427,95 @@ def backproject_2d_to_2d_backward(grad_data, images, rot, grad_weight=None, weig
                                                _ptr(weights), _ptr(rot), _ptr(shifts), _ptr(gi), _ptr(gw), _ptr(gr),
                                                _ptr(gs), _ptr(ws), nws, _stream(dev)))
     return gi, gw, gr, gs
+
+
+# ---------------------------------------------------------------------------
+# Steps either side of the path (include/tproj_spectral.h)
+# ---------------------------------------------------------------------------
+def _spectral_ws(n, device):
+    if n == ctypes.c_size_t(-1).value:
+        raise TprojError(4, lib().tp_last_error_detail().decode())
+    return (torch.empty(n, dtype=torch.uint8, device=device), n) if n else (None, 0)
+
+
+def volume_rfft(vol, pad=1, out=None):
+    """Real volume(s) [Bv, D, D, D] (or [D, D, D]) float32, centre at D/2 ->
+    zero-padded to N = pad * D, centre moved to index 0, rfftn: complex64
+    [Bv, N, N, N//2+1] (tp_volume_rfft)."""
+    if vol.dim() == 3:
+        vol = vol.unsqueeze(0)
+    _req(vol, "vol", torch.float32, 4)
+    Bv, D = vol.shape[0], vol.shape[-1]
+    if tuple(vol.shape[1:]) != (D, D, D):
+        raise ValueError(f"vol must be [Bv, D, D, D], got {tuple(vol.shape)}")
+    N = int(pad) * D
+    dev = vol.device
+    if out is None:
+        out = torch.empty((Bv, N, N, N // 2 + 1), dtype=torch.complex64, device=dev)
+    _req(out, "out", torch.complex64, 4, dev)
+    if tuple(out.shape) != (Bv, N, N, N // 2 + 1):
+        raise ValueError(f"out must be {(Bv, N, N, N // 2 + 1)}, got {tuple(out.shape)}")
+    with torch.cuda.device(dev):
+        ws, nws = _spectral_ws(lib().tp_volume_rfft_workspace(D, int(pad), Bv), dev)
+        _check(lib().tp_volume_rfft(D, int(pad), Bv, _ptr(vol), _ptr(out), _ptr(ws), nws, _stream(dev)))
+    return out
+
+
+def images_irfft(images, out=None):
+    """Spectra [..., H, H//2+1] complex64 -> real images [..., H, H] float32:
+    normalised inverse DFT, index 0 moved to the centre (tp_images_irfft)."""
+    if not isinstance(images, torch.Tensor) or images.dim() < 2:
+        raise ValueError("images must be a tensor [..., H, H//2+1]")
+    _req(images, "images", torch.complex64, images.dim())
+    H = images.shape[-2]
+    if images.shape[-1] != H // 2 + 1:
+        raise ValueError(f"images must be [..., H, H//2+1], got {tuple(images.shape)}")
+    n = images.numel() // (H * (H // 2 + 1))
+    dev = images.device
+    shape = tuple(images.shape[:-2]) + (H, H)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=dev)
+    _req(out, "out", torch.float32, len(shape), dev)
+    if tuple(out.shape) != shape:
+        raise ValueError(f"out must be {shape}, got {tuple(out.shape)}")
+    with torch.cuda.device(dev):
+        ws, nws = _spectral_ws(lib().tp_images_irfft_workspace(H, n), dev)
+        _check(lib().tp_images_irfft(H, n, _ptr(images), _ptr(out), _ptr(ws), nws, _stream(dev)))
+    return out
+
+
+def weight_images(images, weights, out=None):
+    """images * weights (per-image CTF multiply): weights' shape must match
+    the trailing dims of images (e.g. [P, H, H//2+1] for [B, P, H, H//2+1])
+    (tp_weight_images).  out may be images (in place)."""
+    _req(images, "images", torch.complex64, images.dim())
+    _req(weights, "weights", torch.float32, weights.dim(), images.device)
+    if weights.dim() > images.dim() or tuple(images.shape[images.dim() - weights.dim():]) != tuple(weights.shape):
+        raise ValueError(f"weights {tuple(weights.shape)} must match the trailing dims of images {tuple(images.shape)}")
+    if out is None:
+        out = torch.empty_like(images)
+    _req(out, "out", torch.complex64, images.dim(), images.device)
+    if out.shape != images.shape:
+        raise ValueError("out must have the shape of images")
+    dev = images.device
+    with torch.cuda.device(dev):
+        _check(lib().tp_weight_images(images.numel(), weights.numel(), _ptr(images), _ptr(weights), _ptr(out),
+                                      _stream(dev)))
+    return out
+
+
+def finish_reconstruction(data, weights, lam=0.0, out=None):
+    """data / (weights + lam) where that is > 0, else 0 (tp_finish_reconstruction);
+    data complex64 and weights float32 of one shape."""
+    _req(data, "data", torch.complex64, data.dim())
+    _req(weights, "weights", torch.float32, data.dim(), data.device)
+    if weights.shape != data.shape:
+        raise ValueError(f"weights {tuple(weights.shape)} must have the shape of data {tuple(data.shape)}")
+    if out is None:
+        out = torch.empty_like(data)
+    _req(out, "out", torch.complex64, data.dim(), data.device)
+    dev = data.device
+    with torch.cuda.device(dev):
+        _check(lib().tp_finish_reconstruction(data.numel(), _ptr(data), _ptr(weights), float(lam), _ptr(out),
+                                              _stream(dev)))
+    return out

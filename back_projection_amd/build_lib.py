@@ -26,10 +26,10 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _hipcc(srcs, out, verbose):
+def _hipcc(srcs, out, verbose, libs=()):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = out + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", tmp, *libs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,7 +45,8 @@ def _hipcc(srcs, out, verbose):
 
 def build(verbose: bool = False) -> str:
     _hipcc([PROBES_SRC], PROBES_LIB, verbose)
-    return _hipcc(sources(), LIB, verbose)
+    # hipFFT serves the FFT steps of the spectral front and back ends
+    return _hipcc(sources(), LIB, verbose, libs=("-L/opt/rocm/lib", "-lhipfft", "-Wl,-rpath,/opt/rocm/lib"))
 
 
 if __name__ == "__main__":

@@ -416,6 +416,12 @@ tp_status run_bwd(const tp_geom* geom, const tproj::KGeom& k, const float2* Y, c
 
 }  // namespace
 
+namespace tproj {
+// Status helpers shared with the other entry-point files of the library.
+tp_status api_fail(tp_status s, const char* msg) { return fail(s, "%s", msg); }
+tp_status api_ok() { return ok(); }
+}  // namespace tproj
+
 extern "C" {
 
 int tp_abi_version(void) { return TPROJ_ABI_VERSION; }

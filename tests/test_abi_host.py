@@ -24,8 +24,8 @@ def L():
     return bp.lib()
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)
     return sorted(set(n for n in names if n not in ("if", "while")))
@@ -42,6 +42,38 @@ def test_library_exports_every_header_symbol(L):
     assert not missing, missing
     for f in header_functions():
         assert hasattr(L, f)
+
+
+SPECTRAL_HEADER = os.path.join(ROOT, "include", "tproj_spectral.h")
+
+
+def test_spectral_header_declares_the_binding_symbols(L):
+    assert header_functions(SPECTRAL_HEADER) == sorted(bp.SPECTRAL_SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", bp.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    assert set(bp.SPECTRAL_SYMBOLS) <= exported
+    for f in bp.SPECTRAL_SYMBOLS:
+        assert hasattr(L, f)
+
+
+def test_spectral_entry_points_reject_bad_arguments(L):
+    """Checked before anything is enqueued (no device needed)."""
+    assert L.tp_volume_rfft(7, 1, 1, None, None, None, 0, None) == TP_E_SHAPE        # odd D
+    assert L.tp_volume_rfft(64, 0, 1, None, None, None, 0, None) == TP_E_SHAPE       # pad 0
+    assert L.tp_volume_rfft(512, 4, 1, None, None, None, 0, None) == TP_E_SHAPE      # N > 1024
+    assert L.tp_volume_rfft(64, 2, 1, None, None, None, 0, None) == TP_E_NULL
+    assert L.tp_volume_rfft_workspace(63, 1, 1) == ctypes.c_size_t(-1).value
+    assert L.tp_images_irfft(9, 1, None, None, None, 0, None) == TP_E_SHAPE
+    assert L.tp_images_irfft(64, 0, None, None, None, 0, None) == TP_OK               # nothing to do
+    assert L.tp_images_irfft(64, 3, None, None, None, 0, None) == TP_E_NULL
+    assert L.tp_images_irfft_workspace(64, 0) == 0
+    assert L.tp_weight_images(10, 3, None, None, None, None) == TP_E_SHAPE            # 3 does not divide 10
+    assert L.tp_weight_images(0, 1, None, None, None, None) == TP_OK
+    assert L.tp_weight_images(12, 3, None, None, None, None) == TP_E_NULL
+    assert L.tp_finish_reconstruction(4, None, None, ctypes.c_float(-1.0), None, None) == TP_E_VALUE
+    assert L.tp_finish_reconstruction(4, None, None, ctypes.c_float(float("nan")), None, None) == TP_E_VALUE
+    assert L.tp_finish_reconstruction(4, None, None, ctypes.c_float(0.5), None, None) == TP_E_NULL
+    assert b"lambda" in L.tp_last_error_detail() or b"required" in L.tp_last_error_detail()
 
 
 def test_probe_library_exports_its_header():

@@ -1,0 +1,181 @@
+"""GPU parity of the steps either side of the path (include/tproj_spectral.h,
+through the C ABI) against the fp64 oracle (oracle/spectral.py).
+
+Tolerances: the FFT steps are fp32 transforms (relative rounding error of a
+few 1e-7 even at N = 256, growing like log N), held to 1e-5 relative L2 like
+the forward gather; the weight multiply and the finishing division do one
+fp32 operation per entry (error <= 2^-24 relative), held to 1e-6.  Spectra
+fed to the back end are rfft2 transforms of real images, so they are
+Hermitian where the inverse transform assumes it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import back_projection_amd as bp
+import oracle
+from oracle import spectral as S
+from back_projection_amd import workloads
+from tests.helpers import dev, host, log, rel
+
+pytestmark = pytest.mark.gpu
+
+FFT_TOL = 1e-5
+EW_TOL = 1e-6
+
+
+@pytest.mark.parametrize("D,pad,Bv", [(16, 1, 1), (16, 2, 2), (24, 3, 1), (30, 2, 1), (128, 2, 1)])
+def test_volume_rfft(D, pad, Bv):
+    log(f"[spectral] volume_rfft D={D} pad={pad} Bv={Bv}")
+    rng = np.random.default_rng(100 + D + pad)
+    if D >= 64:      # a blob volume at full size
+        vol = workloads.blob_volume_real(D, *workloads.blob_params(rng, 800, D / 3))[None]
+    else:
+        vol = rng.standard_normal((Bv, D, D, D)).astype(np.float32)
+    out = bp.volume_rfft(dev(vol)[0], pad=pad)
+    torch.cuda.synchronize()
+    ref = S.volume_rfft(vol, pad)
+    assert out.shape == ref.shape
+    e = rel(out, ref)
+    log(f"  rel L2 {e:.2e}")
+    assert e <= FFT_TOL
+    # the input is left as it was
+    np.testing.assert_array_equal(host(dev(vol)[0]), vol)
+
+
+def test_volume_rfft_does_not_modify_its_input_and_repeats_bitwise():
+    rng = np.random.default_rng(3)
+    vol = rng.standard_normal((1, 32, 32, 32)).astype(np.float32)
+    tv = dev(vol)[0]
+    a = bp.volume_rfft(tv, pad=2)
+    b = bp.volume_rfft(tv, pad=2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(tv), vol)
+    assert torch.equal(a, b)
+
+
+def real_image_spectra(rng, n, H):
+    img = rng.standard_normal((n, H, H)).astype(np.float32)
+    return np.fft.rfft2(img).astype(np.complex64)
+
+
+@pytest.mark.parametrize("H,n", [(8, 3), (30, 5), (128, 7)])
+def test_images_irfft(H, n):
+    log(f"[spectral] images_irfft H={H} n={n}")
+    rng = np.random.default_rng(200 + H)
+    spec = real_image_spectra(rng, n, H)
+    ts = dev(spec)[0]
+    out = bp.images_irfft(ts)
+    torch.cuda.synchronize()
+    e = rel(out, S.images_irfft(spec))
+    log(f"  rel L2 {e:.2e}")
+    assert e <= FFT_TOL
+    np.testing.assert_array_equal(host(ts), spec)            # input untouched
+
+
+def test_images_irfft_full_batch_sampled():
+    """The D = 128 workload's image count (16384 spectra of 128 x 65) in one
+    call; 64 sampled images checked against the oracle one by one."""
+    H, n = 128, 16384
+    log(f"[spectral] images_irfft H={H} n={n} (sampled)")
+    rng = np.random.default_rng(300)
+    spec = np.empty((n, H, H // 2 + 1), np.complex64)
+    for i in range(0, n, 2048):
+        spec[i:i + 2048] = real_image_spectra(rng, 2048, H)
+    out = bp.images_irfft(dev(spec)[0])
+    torch.cuda.synchronize()
+    idx = np.sort(rng.choice(n, 64, replace=False))
+    got = host(out[torch.from_numpy(idx).to(out.device)])
+    ref = S.images_irfft(spec[idx])
+    e = rel(got, ref)
+    log(f"  rel L2 {e:.2e}")
+    assert e <= FFT_TOL
+
+
+def test_front_end_projection_back_end_chain():
+    """Real volume -> volume_rfft -> project_3d_to_2d -> images_irfft on the GPU
+    against the same chain in the oracle (D = 32, cubic, pad 1 and 2 with the
+    matching oversampling)."""
+    D, P = 32, 6
+    rng = np.random.default_rng(400)
+    vol = workloads.blob_volume_real(D, *workloads.blob_params(rng, 60, D / 3))[None]
+    rot = workloads.random_rotations(rng, P)[None]
+    sh = workloads.random_shifts(rng, P, 3.0)[None]
+    for pad in (1, 2):
+        log(f"[spectral] chain D={D} pad={pad}")
+        tv, tr, ts = dev(vol, rot, sh)
+        V = bp.volume_rfft(tv, pad=pad)
+        Y = bp.project_3d_to_2d(V, tr, ts, H=D, interp="cubic", oversampling=float(pad), radius_cutoff=D / 2)
+        img = bp.images_irfft(Y)
+        torch.cuda.synchronize()
+        Vr = S.volume_rfft(vol, pad)
+        Yr = oracle.project(Vr, rot, sh, H=D, interp=1, o=float(pad), r=D / 2)
+        ref = S.images_irfft(Yr)
+        e = rel(img, ref)
+        log(f"  rel L2 {e:.2e}")
+        assert e <= FFT_TOL
+
+
+def test_weight_images_broadcast_and_in_place():
+    log("[spectral] weight_images")
+    rng = np.random.default_rng(500)
+    B, P, H = 2, 5, 30
+    img = (rng.standard_normal((B, P, H, H // 2 + 1)) + 1j * rng.standard_normal((B, P, H, H // 2 + 1))).astype(
+        np.complex64)
+    w = workloads.ctf2_like_weights(rng, P, H, P).astype(np.float32)
+    ti, tw = dev(img, w)
+    out = bp.weight_images(ti, tw)
+    ref = S.weight_images(img, w)
+    torch.cuda.synchronize()
+    assert rel(out, ref) <= EW_TOL
+    bp.weight_images(ti, tw, out=ti)                              # in place
+    torch.cuda.synchronize()
+    assert rel(ti, ref) <= EW_TOL
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.25])
+def test_finish_reconstruction(lam):
+    log(f"[spectral] finish lambda={lam}")
+    rng = np.random.default_rng(600)
+    shape = (1, 24, 24, 13)
+    data = (rng.standard_normal(shape) + 1j * rng.standard_normal(shape)).astype(np.complex64)
+    # weights away from -lambda except exact zeros and clearly negative entries
+    w = rng.uniform(1e-2, 4.0, shape).astype(np.float32)
+    sel = rng.random(shape)
+    w[sel < 0.1] = 0.0
+    w[sel > 0.95] = -1.0
+    td, tw = dev(data, w)
+    out = bp.finish_reconstruction(td, tw, lam)
+    torch.cuda.synchronize()
+    ref = S.finish_reconstruction(data, w, lam)
+    got = host(out)
+    zero = (w.astype(np.float64) + lam) <= 0
+    assert np.all(got[zero] == 0)
+    assert rel(got, ref) <= EW_TOL
+
+
+def test_finishing_recovers_the_source_on_the_gpu():
+    """The oracle pin's exact-recovery case, run with the GPU ops: CTF-weighted
+    lattice projections, accumulation with weights w^2, finishing."""
+    import itertools
+    log("[spectral] finish recovers source (2D lattice poses)")
+    rng = np.random.default_rng(700)
+    D = 16
+    src = (rng.standard_normal((1, D, D // 2 + 1)) + 1j * rng.standard_normal((1, D, D // 2 + 1))).astype(np.complex64)
+    rots = []
+    for perm in itertools.permutations(range(2)):
+        for sg in itertools.product((1, -1), repeat=2):
+            R = np.zeros((2, 2), np.float32)
+            for i in range(2):
+                R[i, perm[i]] = sg[i]
+            rots.append(R)
+    rot = np.array(rots)[None]
+    w = rng.uniform(0.2, 1.0, (1, 8, D, D // 2 + 1)).astype(np.float32)
+    ts, tr, tw = dev(src, rot, w)
+    obs = bp.weight_images(bp.project_2d_to_2d(ts, tr, interp="linear"), tw[0])
+    data, wsum = bp.backproject_2d_to_2d(bp.weight_images(obs, tw[0]), tr, tw * tw, D=D, interp="linear")
+    rec = bp.finish_reconstruction(data, wsum)
+    torch.cuda.synchronize()
+    e = rel(rec, src)
+    log(f"  rel L2 {e:.2e}")
+    assert e <= 1e-5
