@@ -346,6 +346,68 @@ def run_sweep(steps, warmup, bp, workloads, torch, details):
     details["sweep"] = rows
 
 
+def run_oversampling(bp, workloads, torch, details, D=128, P_acc=24, n_blobs=80):
+    """Interpolation against oversampling: accuracy (FRC with the analytic
+    slices, real-space gain by radius) and time of cubic at 1x against linear
+    with a 2x zero-padded volume, padded offline (the projection alone) or on
+    the fly (front end + projection), and cubic at 2x (stderr/details only)."""
+    import numpy as np
+    from back_projection_amd import accuracy as acc
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(4000)
+    model = acc.blob_model(rng, D, n_blobs, 0.4 * D)
+    vol = acc.real_volume(D, model)
+    rot = workloads.random_rotations(rng, P_acc)
+    ref = acc.analytic_slices(model, rot, D, D, D / 2)
+    tv = torch.from_numpy(vol[None]).to(dev)
+    tr = torch.from_numpy(rot[None]).to(dev)
+    V1 = bp.volume_rfft(tv, pad=1)
+    V2 = bp.volume_rfft(tv, pad=2)
+    methods = {"linear 1x": (V1, "linear", 1.0), "cubic 1x": (V1, "cubic", 1.0),
+               "linear 2x": (V2, "linear", 2.0), "cubic 2x": (V2, "cubic", 2.0)}
+    ref_img = bp.images_irfft(torch.from_numpy(ref.astype(np.complex64)).to(dev)).cpu().numpy()
+    ring_fr = (0.25, 0.5, 0.75, 0.9, 1.0)
+    edges = (0.0, 0.2, 0.4, 0.6, 0.8)
+    res = {"workload": f"D{D} blob volume ({n_blobs} Gaussians, sigma U(1,1.5), centres within 0.4 D), "
+                       f"{P_acc} uniform rotations, radius D/2, the samples' exact transform as truth",
+           "rings_frac_nyquist": ring_fr, "gain_bands_frac_half_box": edges, "methods": {}}
+    eprint("[bench] oversampling: method      FRC at " + " ".join("%5.2f" % f for f in ring_fr) +
+           "  | 1-FRC mean  | gain by radius " + " ".join("%.1f-%.1f" % e for e in zip(edges[:-1], edges[1:])))
+    for name, (V, interp, o) in methods.items():
+        Y = bp.project_3d_to_2d(V, tr, H=D, interp=interp, oversampling=o, radius_cutoff=D / 2)
+        img = bp.images_irfft(Y).cpu().numpy()
+        Yh = Y.cpu().numpy()[0]
+        f = acc.frc(Yh, ref, D)
+        at = [float(f[int(round(x * D / 2))]) for x in ring_fr]
+        g = acc.radial_gain(img[0], ref_img, edges)
+        res["methods"][name] = {"frc": at, "one_minus_frc_mean": float(np.mean(1 - f[1:])), "gain": g.tolist()}
+        eprint("[bench] oversampling: %-10s        " % name + " ".join("%.4f" % x for x in at) +
+               "  | %.2e    | " % np.mean(1 - f[1:]) + "   ".join("%.3f" % x for x in g))
+    # time: 16384 and 1024 poses (rotations repeated from a seeded set)
+    for P in (1024, 16384):
+        trP = torch.from_numpy(workloads.random_rotations(np.random.default_rng(4100 + P), P)[None]).to(dev)
+        out = torch.empty((1, P, D, D // 2 + 1), dtype=torch.complex64, device=dev)
+        calls = {
+            "cubic 1x": lambda: bp.project_3d_to_2d(V1, trP, H=D, interp="cubic", radius_cutoff=D / 2, out=out),
+            "linear 2x offline": lambda: bp.project_3d_to_2d(V2, trP, H=D, interp="linear", oversampling=2.0,
+                                                             radius_cutoff=D / 2, out=out),
+            "linear 2x on the fly": lambda: bp.project_3d_to_2d(bp.volume_rfft(tv, pad=2), trP, H=D, interp="linear",
+                                                                oversampling=2.0, radius_cutoff=D / 2, out=out),
+            "cubic 2x offline": lambda: bp.project_3d_to_2d(V2, trP, H=D, interp="cubic", oversampling=2.0,
+                                                            radius_cutoff=D / 2, out=out),
+            "front end 2x alone": lambda: bp.volume_rfft(tv, pad=2, out=V2),
+        }
+        tt = {}
+        for name, fn in calls.items():
+            fn()
+            ms, _ = time_calls(fn, 5, torch)
+            tt[name] = round(ms, 4)
+        res[f"time_ms_{P}_poses"] = tt
+        eprint(f"[bench] oversampling: {P} poses, ms per call: " + ", ".join(f"{k} {v:.3f}" for k, v in tt.items()))
+        del out
+    details["oversampling"] = res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +417,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-workloads", action="store_true", help="also time the other four workloads (stderr)")
     ap.add_argument("--sweep", action="store_true", help="also time the 3D ops over box size, poses and kernel (stderr)")
+    ap.add_argument("--oversampling", action="store_true",
+                    help="also run the interpolation vs oversampling accuracy study and timing (stderr)")
     ap.add_argument("--twod", action="store_true", help="also time the 2D -> 2D ops on their D=128 workload (stderr)")
     ap.add_argument("--details", default=None, help="write per-kernel details as JSON to this file")
     ap.add_argument("--peaks", action="store_true", help="measure HBM and L2-resident bandwidths and exit")
@@ -514,6 +578,9 @@ def main():
     if args.sweep:
         torch.cuda.empty_cache()
         run_sweep(5, 1, bp, workloads, torch, details)
+    if args.oversampling:
+        torch.cuda.empty_cache()
+        run_oversampling(bp, workloads, torch, details)
     if args.twod or args.all_workloads:
         torch.cuda.empty_cache()
         run_2d(max(3, args.steps // 2), 1, bp, workloads, torch, details)
