@@ -581,11 +581,14 @@ tp_status project_3d_to_2d_backward(const tp_geom* geom, const void* grad_out, c
     std::lock_guard<std::mutex> lk(g_side_mu);
     SideStream* ss = side_stream();
     if (ss) {
-      // the scatter first (its brick kernel is queued ahead), the gradients
-      // from the point where its band maxima are done
+      // the scatter first (its kernels are queued ahead), the gradients from
+      // the start of the call, so that they overlap the scatter's set-up and
+      // band-maximum pass
+      hipError_t e = hipEventRecord(ss->fork, st);
+      if (e != hipSuccess) return fail(TP_E_LAUNCH, "stream fork failed: %s", hipGetErrorString(e));
       TRY(run_bwd(geom, k, (const float2*)grad_out, nullptr, rot, shifts, (float2*)grad_vol, nullptr, workspace,
-                  ws_bytes, st, ss->fork));
-      hipError_t e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+                  ws_bytes, st));
+      e = hipStreamWaitEvent(ss->s, ss->fork, 0);
       if (e != hipSuccess) return fail(TP_E_LAUNCH, "stream fork failed: %s", hipGetErrorString(e));
       const tp_status sg = run_grads(geom, k, (const float2*)vol, nullptr, (const float2*)grad_out, nullptr, rot,
                                      shifts, grad_rot, grad_shifts, ws2, n2, ss->s);
