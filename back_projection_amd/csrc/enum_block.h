@@ -516,7 +516,30 @@ __device__ __forceinline__ void grad_flush(const KGeom& g, const EnumShared<WIN,
 }
 
 // Per-lane terms -> per-hit sums (all 64 lanes of the wavefront call this).
+// Keys rise along the lanes (candidates are ordered by hit), so a wavefront
+// whose first and last lanes share a key holds one key only: its sums are a
+// plain wavefront sum (one DPP add per term and step, no key masks), left in
+// lane 63.
 __device__ __forceinline__ void grad_collect(float (&acc)[8], int key, float (*gw)[8]) {
+  const int k0 = __builtin_amdgcn_readfirstlane(key);
+  if (k0 != EB_SENTINEL && k0 == __builtin_amdgcn_readlane(key, 63)) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      float v = acc[q];
+      v += __int_as_float(dpp_int<0x111, 0xf>(0, __float_as_int(v)));   // row_shr:1
+      v += __int_as_float(dpp_int<0x112, 0xf>(0, __float_as_int(v)));   // row_shr:2
+      v += __int_as_float(dpp_int<0x114, 0xf>(0, __float_as_int(v)));   // row_shr:4
+      v += __int_as_float(dpp_int<0x118, 0xf>(0, __float_as_int(v)));   // row_shr:8
+      v += __int_as_float(dpp_int<0x142, 0xa>(0, __float_as_int(v)));   // row_bcast:15
+      v += __int_as_float(dpp_int<0x143, 0xc>(0, __float_as_int(v)));   // row_bcast:31
+      acc[q] = v;
+    }
+    if ((threadIdx.x & 63) == 63) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) atomicAdd(&gw[k0][q], acc[q]);
+    }
+    return;
+  }
   seg_scan(acc, key);
   if (seg_tail(key)) {
 #pragma unroll
