@@ -44,14 +44,14 @@ FP32_VECTOR_TFLOPS = 157.3
 # reported when the digest of the 3D kernel sources matches, else null.
 TRAFFIC = {
     # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
-    "forward": {"sources_sha256": "c6c307da9c46fe4904c554d049eabe7bcebbc98b716dca2b691580b094469f1a",
-               "fetch_bytes": 317383343, "write_bytes": 1183434250},
-    "backward": {"sources_sha256": "c6c307da9c46fe4904c554d049eabe7bcebbc98b716dca2b691580b094469f1a",
-                "fetch_bytes": 2826679800, "write_bytes": 188940288},
-    "gradient": {"sources_sha256": "c6c307da9c46fe4904c554d049eabe7bcebbc98b716dca2b691580b094469f1a",
-                "fetch_bytes": 2784945125, "write_bytes": 120424608},
-    "fold": {"sources_sha256": "c6c307da9c46fe4904c554d049eabe7bcebbc98b716dca2b691580b094469f1a",
-            "fetch_bytes": 292803116, "write_bytes": 8519680},
+    "forward": {"sources_sha256": "76bf783eef7663ab042a9756cf04b7e02726406855a84dc4286e10df6c551925",
+               "fetch_bytes": 317611481, "write_bytes": 1183370645},
+    "backward": {"sources_sha256": "76bf783eef7663ab042a9756cf04b7e02726406855a84dc4286e10df6c551925",
+                "fetch_bytes": 2826245213, "write_bytes": 188940288},
+    "gradient": {"sources_sha256": "76bf783eef7663ab042a9756cf04b7e02726406855a84dc4286e10df6c551925",
+                "fetch_bytes": 2785186605, "write_bytes": 120424608},
+    "fold": {"sources_sha256": "76bf783eef7663ab042a9756cf04b7e02726406855a84dc4286e10df6c551925",
+            "fetch_bytes": 292601386, "write_bytes": 8519680},
 }
 
 

@@ -126,3 +126,44 @@ def test_2d_adjoint_identity_fp32():
     lhs = float(torch.sum(torch.conj(Fx) * ty).real)
     rhs = float(torch.sum(torch.conj(tx) * Fty).real)
     assert abs(lhs - rhs) <= 1e-5 * (abs(lhs) + float(Fx.abs().norm() * ty.abs().norm()))
+
+
+def test_2d_workload_full_sampled():
+    """The D = 128 2D workload (16384 poses) in the launch configuration the
+    bench times: the forward checked on 64 sampled poses; the backward and the
+    accumulation with weights given upstream data that is nonzero only on
+    those poses, so the full launch must reproduce the oracle run on them (and
+    exact zeros for the other poses' rotation/shift grads); the adjoint
+    identity over the full launch."""
+    w = workloads.make_2d()
+    P, D, r = w["P"], w["D"], w["radius"]
+    rng = np.random.default_rng(2222)
+    idx = np.sort(rng.choice(P, 64, replace=False))
+    log(f"[parity2d] full workload D={D} P={P}, {len(idx)} sampled poses")
+    ts, tr, tsh = dev(w["src"], w["rot"], w["shifts"])
+    out = bp.project_2d_to_2d(ts, tr, tsh, radius_cutoff=r)
+    ref = oracle.project2d(w["src"], w["rot"][:, idx], w["shifts"][:, idx], interp=1, r=r)
+    assert rel(out[:, idx], ref) <= FWD_TOL, rel(out[:, idx], ref)
+    gsub = workloads.random_complex(np.random.default_rng(2223), (1, len(idx), D, D // 2 + 1))
+    wsub = w["weights"][:, idx]
+    ti = torch.from_numpy(idx).cuda()
+    tg = torch.zeros((1, P, D, D // 2 + 1), dtype=torch.complex64, device="cuda:0")
+    tg[:, ti] = torch.from_numpy(gsub).cuda()
+    tw = torch.zeros((1, P, D, D // 2 + 1), dtype=torch.float32, device="cuda:0")
+    tw[:, ti] = torch.from_numpy(wsub).cuda()
+    gx, gr, gs = bp.project_2d_to_2d_backward(tg, ts, tr, tsh, radius_cutoff=r)
+    rgx, rgr, rgs = oracle.project2d_backward(gsub, w["src"], w["rot"][:, idx], w["shifts"][:, idx], interp=1, r=r)
+    assert rel(gx, rgx) <= BWD_TOL, rel(gx, rgx)
+    assert rel(gr[:, ti], rgr) <= BWD_TOL, rel(gr[:, ti], rgr)
+    assert rel(gs[:, ti], rgs) <= BWD_TOL, rel(gs[:, ti], rgs)
+    rest = torch.from_numpy(np.setdiff1d(np.arange(P), idx)).cuda()
+    assert float(gr[:, rest].abs().max()) == 0.0 and float(gs[:, rest].abs().max()) == 0.0
+    data, wt = bp.backproject_2d_to_2d(tg, tr, tw, tsh, D=D, radius_cutoff=r)
+    rdata, rwt = oracle.backproject2d(gsub, w["rot"][:, idx], weights=wsub, shifts=w["shifts"][:, idx], D=D,
+                                      interp=1, r=r)
+    assert rel(data, rdata) <= BWD_TOL, rel(data, rdata)
+    assert rel(wt, rwt) <= BWD_TOL, rel(wt, rwt)
+    # adjoint identity over the full launch: <P S, G> = <S, P^T G>
+    lhs = np.real(np.vdot(out[:, ti].cpu().numpy().astype(np.complex128).ravel(), gsub.astype(np.complex128).ravel()))
+    rhs = np.real(np.vdot(w["src"].astype(np.complex128).ravel(), gx.cpu().numpy().astype(np.complex128).ravel()))
+    assert abs(lhs - rhs) <= 1e-5 * np.linalg.norm(out[:, ti].cpu().numpy()) * np.linalg.norm(gsub)
