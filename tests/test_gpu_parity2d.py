@@ -167,3 +167,24 @@ def test_2d_workload_full_sampled():
     lhs = np.real(np.vdot(out[:, ti].cpu().numpy().astype(np.complex128).ravel(), gsub.astype(np.complex128).ravel()))
     rhs = np.real(np.vdot(w["src"].astype(np.complex128).ravel(), gx.cpu().numpy().astype(np.complex128).ravel()))
     assert abs(lhs - rhs) <= 1e-5 * np.linalg.norm(out[:, ti].cpu().numpy()) * np.linalg.norm(gsub)
+
+
+def test_2d_empty_and_degenerate():
+    """A zero source rotates to exact zeros; r = 0 keeps only DC; zero images
+    accumulate to exact zeros; the identity map at H = D returns the stored
+    source itself (cubic weights at lattice points are exactly 1 and 0)."""
+    D = 16
+    rng = np.random.default_rng(19)
+    src = workloads.random_complex(rng, (1, D, D // 2 + 1))
+    ts = dev(src)[0]
+    tr = torch.from_numpy(rotations2d(rng, 1)[None].astype(np.float32)).cuda()
+    z = bp.project_2d_to_2d(torch.zeros_like(ts), tr)
+    assert float(z.abs().max()) == 0.0
+    h = bp.project_2d_to_2d(ts, tr, radius_cutoff=0.0).cpu().numpy()[0, 0]
+    assert np.count_nonzero(h) <= 1 and abs(h[0, 0] - src[0, 0, 0]) < 1e-6 * abs(src[0, 0, 0])
+    gz, _ = bp.backproject_2d_to_2d(torch.zeros((1, 1, D, D // 2 + 1), dtype=torch.complex64, device="cuda:0"), tr,
+                                    D=D)
+    assert float(gz.abs().max()) == 0.0
+    eye = torch.eye(2, dtype=torch.float32, device="cuda:0")[None, None].contiguous()
+    same = bp.project_2d_to_2d(ts, eye, interp="cubic").cpu().numpy()[0, 0]
+    assert np.array_equal(same, src[0])
