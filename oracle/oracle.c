@@ -80,10 +80,13 @@ static double tent_w(double d) {
   return x < 1.0 ? 1.0 - x : 0.0;
 }
 
-/* dW/dd of the tent kernel.  At d = 0 the one-sided value that belongs to the
- * cell [floor(p), floor(p)+1) is used (reading: right derivative in p). */
+/* dW/dd of the tent kernel, taken on the half-open cell [floor(p), floor(p)+1)
+ * (reading: right derivative in p).  The two taps of that cell sit at
+ * d = p - t in [0, 1) (tap floor(p), slope -1) and d in [-1, 0) (tap
+ * floor(p)+1, slope +1); both ends of the cell are closed on the side of p,
+ * so at an integer p the tap one step above still carries slope +1. */
 static double tent_dw(double d) {
-  if (d >= 1.0 || d <= -1.0) return 0.0;
+  if (d >= 1.0 || d < -1.0) return 0.0;
   return d >= 0.0 ? -1.0 : 1.0;
 }
 

@@ -109,7 +109,8 @@ def test_tent_kernel_properties():
         assert abs(w.sum() - 1) < 1e-15
         assert abs(w[1] - f) < 1e-15
         assert oracle.kernel_dweight(0, f) == -1.0 and oracle.kernel_dweight(0, f - 1) == 1.0
-    assert oracle.kernel_dweight(0, 0.0) == -1.0  # right derivative in p at the knot
+    assert oracle.kernel_dweight(0, 0.0) == -1.0  # right derivative in p at the knot:
+    assert oracle.kernel_dweight(0, -1.0) == 1.0  # the upper tap of the cell keeps slope +1
 
 
 # ---------------------------------------------------------------------------
