@@ -156,6 +156,45 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _typ(t, name, dtype, ndim):
+    """Type and rank of one argument (no device access)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    return t
+
+
+def _shape(t, name, shape):
+    """Full shape of one argument against what the geometry implies: the C ABI
+    receives only pointers and the geometry, so a mis-shaped tensor would be
+    read or written out of bounds on the device."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _bcast(B, **sizes):
+    """Each broadcast batch size (Bv, Br, Bs; 0 = absent) is 1 or B."""
+    for name, n in sizes.items():
+        if n and n not in (1, B):
+            raise ValueError(f"{name} = {n} must be 1 or the batch size {B}")
+
+
+def _placed(device, **tensors):
+    """Every given tensor on `device` and contiguous (after the shape checks)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a GPU device")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
 def _req(t, name, dtype, ndim, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -197,22 +236,26 @@ def project_3d_to_2d(vol, rot, shifts=None, *, H=None, interp="cubic", oversampl
                      B=None, out=None):
     """Forward: out[b, n] = M * phi * I(vol[bv], o R (kx, ky, 0)).  Returns out
     (complex64 [B, P, H, H//2+1])."""
-    _req(vol, "vol", torch.complex64, 4)
-    dev = vol.device
-    _req(rot, "rot", torch.float32, 4, dev)
+    _typ(vol, "vol", torch.complex64, 4)
+    _typ(rot, "rot", torch.float32, 4)
     if shifts is not None:
-        _req(shifts, "shifts", torch.float32, 3, dev)
+        _typ(shifts, "shifts", torch.float32, 3)
     Bv, D = vol.shape[0], vol.shape[1]
     Br, P = rot.shape[0], rot.shape[1]
     Bs = shifts.shape[0] if shifts is not None else 0
     B = B or _batch(Bv, Br, Bs)
     H = H or D
+    _shape(vol, "vol", (Bv, D, D, D // 2 + 1))
+    _shape(rot, "rot", (Br, P, 3, 3))
+    _shape(shifts, "shifts", (Bs, P, 2))
+    _bcast(B, Bv=Bv, Br=Br, Bs=Bs)
+    if out is not None:
+        _typ(out, "out", torch.complex64, 4)
+        _shape(out, "out", (B, P, H, H // 2 + 1))
+    dev = vol.device
+    _placed(dev, vol=vol, rot=rot, shifts=shifts, out=out)
     if out is None:
         out = torch.empty((B, P, H, H // 2 + 1), dtype=torch.complex64, device=dev)
-    else:
-        _req(out, "out", torch.complex64, 4, dev)
-        if tuple(out.shape) != (B, P, H, H // 2 + 1):
-            raise ValueError(f"out must have shape {(B, P, H, H // 2 + 1)}, got {tuple(out.shape)}")
     g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
     ws, nws = _workspace(g, OP_PROJECT, dev)
     _check(lib().project_3d_to_2d(ctypes.byref(g), _ptr(vol), _ptr(rot), _ptr(shifts), _ptr(out), _ptr(ws), nws,
@@ -225,25 +268,33 @@ def project_3d_to_2d_backward(grad_out, vol, rot, shifts=None, *, interp="cubic"
                               grad_vol=None, grad_rot=None, grad_shifts=None):
     """Backward of project_3d_to_2d; returns (grad_vol, grad_rot, grad_shifts),
     None where not requested.  Preallocated outputs may be passed in."""
-    _req(grad_out, "grad_out", torch.complex64, 4)
-    dev = grad_out.device
-    _req(vol, "vol", torch.complex64, 4, dev)
-    _req(rot, "rot", torch.float32, 4, dev)
+    _typ(grad_out, "grad_out", torch.complex64, 4)
+    _typ(vol, "vol", torch.complex64, 4)
+    _typ(rot, "rot", torch.float32, 4)
     if shifts is not None:
-        _req(shifts, "shifts", torch.float32, 3, dev)
+        _typ(shifts, "shifts", torch.float32, 3)
     B, P, H = grad_out.shape[0], grad_out.shape[1], grad_out.shape[2]
     Bv, D = vol.shape[0], vol.shape[1]
     Br = rot.shape[0]
     Bs = shifts.shape[0] if shifts is not None else 0
+    _shape(grad_out, "grad_out", (B, P, H, H // 2 + 1))
+    _shape(vol, "vol", (Bv, D, D, D // 2 + 1))
+    _shape(rot, "rot", (Br, P, 3, 3))
+    _shape(shifts, "shifts", (Bs, P, 2))
+    _bcast(B, Bv=Bv, Br=Br, Bs=Bs)
+    outs = {}
+    for t, ref, name, need in ((grad_vol, vol, "grad_vol", need_vol), (grad_rot, rot, "grad_rot", need_rot),
+                               (grad_shifts, shifts, "grad_shifts", need_shifts and shifts is not None)):
+        if need and t is not None:
+            _typ(t, name, ref.dtype, ref.dim())
+            _shape(t, name, ref.shape)
+            outs[name] = t
+    dev = grad_out.device
+    _placed(dev, grad_out=grad_out, vol=vol, rot=rot, shifts=shifts, **outs)
     gv = (grad_vol if grad_vol is not None else torch.empty_like(vol)) if need_vol else None
     gr = (grad_rot if grad_rot is not None else torch.empty_like(rot)) if need_rot else None
     gs = (grad_shifts if grad_shifts is not None else torch.empty_like(shifts)) if (
         need_shifts and shifts is not None) else None
-    for t, ref, name in ((gv, vol, "grad_vol"), (gr, rot, "grad_rot"), (gs, shifts, "grad_shifts")):
-        if t is not None and (t.shape != ref.shape or t.dtype != ref.dtype):
-            raise ValueError(f"{name} must match {tuple(ref.shape)} {ref.dtype}")
-        if t is not None:
-            _req(t, name, ref.dtype, ref.dim(), dev)
     g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
     ws, nws = _workspace(g, OP_PROJECT_BACKWARD, dev)
     _check(lib().project_3d_to_2d_backward(ctypes.byref(g), _ptr(grad_out), _ptr(vol), _ptr(rot), _ptr(shifts),
@@ -255,29 +306,36 @@ def backproject_2d_to_3d(images, rot, weights=None, shifts=None, *, D=None, Bv=1
                          radius_cutoff=-1.0, data_vol=None, weight_vol=None):
     """Back-projection (adjoint): returns (data_vol, weight_vol or None).
     Preallocated outputs may be passed in."""
-    _req(images, "images", torch.complex64, 4)
-    dev = images.device
-    _req(rot, "rot", torch.float32, 4, dev)
+    _typ(images, "images", torch.complex64, 4)
+    _typ(rot, "rot", torch.float32, 4)
     if weights is not None:
-        _req(weights, "weights", torch.float32, 4, dev)
+        _typ(weights, "weights", torch.float32, 4)
     if shifts is not None:
-        _req(shifts, "shifts", torch.float32, 3, dev)
+        _typ(shifts, "shifts", torch.float32, 3)
     B, P, H = images.shape[0], images.shape[1], images.shape[2]
     Br = rot.shape[0]
     Bs = shifts.shape[0] if shifts is not None else 0
     D = D or H
+    _shape(images, "images", (B, P, H, H // 2 + 1))
+    _shape(weights, "weights", (B, P, H, H // 2 + 1))
+    _shape(rot, "rot", (Br, P, 3, 3))
+    _shape(shifts, "shifts", (Bs, P, 2))
+    _bcast(B, Bv=Bv, Br=Br, Bs=Bs)
+    if data_vol is not None:
+        _typ(data_vol, "data_vol", torch.complex64, 4)
+        _shape(data_vol, "data_vol", (Bv, D, D, D // 2 + 1))
+    if weights is not None and weight_vol is not None:
+        _typ(weight_vol, "weight_vol", torch.float32, 4)
+        _shape(weight_vol, "weight_vol", (Bv, D, D, D // 2 + 1))
+    dev = images.device
+    _placed(dev, images=images, rot=rot, weights=weights, shifts=shifts, data_vol=data_vol,
+            weight_vol=weight_vol if weights is not None else None)
     data = data_vol if data_vol is not None else torch.empty((Bv, D, D, D // 2 + 1), dtype=torch.complex64,
                                                              device=dev)
-    _req(data, "data_vol", torch.complex64, 4, dev)
-    if tuple(data.shape) != (Bv, D, D, D // 2 + 1):
-        raise ValueError("data_vol has the wrong shape")
     wvol = None
     if weights is not None:
         wvol = weight_vol if weight_vol is not None else torch.empty((Bv, D, D, D // 2 + 1), dtype=torch.float32,
                                                                      device=dev)
-        _req(wvol, "weight_vol", torch.float32, 4, dev)
-        if tuple(wvol.shape) != (Bv, D, D, D // 2 + 1):
-            raise ValueError("weight_vol has the wrong shape")
     g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
     ws, nws = _workspace(g, OP_BACKPROJECT, dev)
     _check(lib().backproject_2d_to_3d(ctypes.byref(g), _ptr(images), _ptr(weights), _ptr(rot), _ptr(shifts),
@@ -290,20 +348,29 @@ def backproject_2d_to_3d_backward(grad_data_vol, images, rot, grad_weight_vol=No
                                   need_weights=True, need_rot=True, need_shifts=True):
     """Backward of backproject_2d_to_3d; returns (grad_images, grad_weights,
     grad_rot, grad_shifts), None where not requested."""
-    _req(grad_data_vol, "grad_data_vol", torch.complex64, 4)
-    dev = grad_data_vol.device
-    _req(images, "images", torch.complex64, 4, dev)
-    _req(rot, "rot", torch.float32, 4, dev)
+    _typ(grad_data_vol, "grad_data_vol", torch.complex64, 4)
+    _typ(images, "images", torch.complex64, 4)
+    _typ(rot, "rot", torch.float32, 4)
     if grad_weight_vol is not None:
-        _req(grad_weight_vol, "grad_weight_vol", torch.float32, 4, dev)
+        _typ(grad_weight_vol, "grad_weight_vol", torch.float32, 4)
     if weights is not None:
-        _req(weights, "weights", torch.float32, 4, dev)
+        _typ(weights, "weights", torch.float32, 4)
     if shifts is not None:
-        _req(shifts, "shifts", torch.float32, 3, dev)
+        _typ(shifts, "shifts", torch.float32, 3)
     B, P, H = images.shape[0], images.shape[1], images.shape[2]
     Bv, D = grad_data_vol.shape[0], grad_data_vol.shape[1]
     Br = rot.shape[0]
     Bs = shifts.shape[0] if shifts is not None else 0
+    _shape(grad_data_vol, "grad_data_vol", (Bv, D, D, D // 2 + 1))
+    _shape(grad_weight_vol, "grad_weight_vol", (Bv, D, D, D // 2 + 1))
+    _shape(images, "images", (B, P, H, H // 2 + 1))
+    _shape(weights, "weights", (B, P, H, H // 2 + 1))
+    _shape(rot, "rot", (Br, P, 3, 3))
+    _shape(shifts, "shifts", (Bs, P, 2))
+    _bcast(B, Bv=Bv, Br=Br, Bs=Bs)
+    dev = grad_data_vol.device
+    _placed(dev, grad_data_vol=grad_data_vol, images=images, rot=rot, grad_weight_vol=grad_weight_vol,
+            weights=weights, shifts=shifts)
     gi = torch.empty_like(images) if need_images else None
     gw = torch.empty((B, P, H, H // 2 + 1), dtype=torch.float32, device=dev) if (
         need_weights and weights is not None) else None
@@ -324,24 +391,26 @@ def project_2d_to_2d(src, rot, shifts=None, *, H=None, interp="cubic", oversampl
                      B=None, out=None):
     """Forward: out[b, n] = M * phi * I(src[bv], o R (kx, ky)).  Returns out
     (complex64 [B, P, H, H//2+1])."""
-    _req(src, "src", torch.complex64, 3)
-    dev = src.device
-    _req(rot, "rot", torch.float32, 4, dev)
-    if tuple(rot.shape[2:]) != (2, 2):
-        raise ValueError(f"rot must be [Br, P, 2, 2], got {tuple(rot.shape)}")
+    _typ(src, "src", torch.complex64, 3)
+    _typ(rot, "rot", torch.float32, 4)
     if shifts is not None:
-        _req(shifts, "shifts", torch.float32, 3, dev)
+        _typ(shifts, "shifts", torch.float32, 3)
     Bv, D = src.shape[0], src.shape[1]
     Br, P = rot.shape[0], rot.shape[1]
     Bs = shifts.shape[0] if shifts is not None else 0
     B = B or _batch(Bv, Br, Bs)
     H = H or D
+    _shape(src, "src", (Bv, D, D // 2 + 1))
+    _shape(rot, "rot", (Br, P, 2, 2))
+    _shape(shifts, "shifts", (Bs, P, 2))
+    _bcast(B, Bv=Bv, Br=Br, Bs=Bs)
+    if out is not None:
+        _typ(out, "out", torch.complex64, 4)
+        _shape(out, "out", (B, P, H, H // 2 + 1))
+    dev = src.device
+    _placed(dev, src=src, rot=rot, shifts=shifts, out=out)
     if out is None:
         out = torch.empty((B, P, H, H // 2 + 1), dtype=torch.complex64, device=dev)
-    else:
-        _req(out, "out", torch.complex64, 4, dev)
-        if tuple(out.shape) != (B, P, H, H // 2 + 1):
-            raise ValueError(f"out must have shape {(B, P, H, H // 2 + 1)}, got {tuple(out.shape)}")
     g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
     ws, nws = _workspace(g, OP_PROJECT_2D, dev)
     _check(lib().project_2d_to_2d(ctypes.byref(g), _ptr(src), _ptr(rot), _ptr(shifts), _ptr(out), _ptr(ws), nws,
@@ -353,16 +422,22 @@ def project_2d_to_2d_backward(grad_out, src, rot, shifts=None, *, interp="cubic"
                               radius_cutoff=-1.0, need_src=True, need_rot=True, need_shifts=True):
     """Backward of project_2d_to_2d; returns (grad_src, grad_rot, grad_shifts),
     None where not requested."""
-    _req(grad_out, "grad_out", torch.complex64, 4)
-    dev = grad_out.device
-    _req(src, "src", torch.complex64, 3, dev)
-    _req(rot, "rot", torch.float32, 4, dev)
+    _typ(grad_out, "grad_out", torch.complex64, 4)
+    _typ(src, "src", torch.complex64, 3)
+    _typ(rot, "rot", torch.float32, 4)
     if shifts is not None:
-        _req(shifts, "shifts", torch.float32, 3, dev)
+        _typ(shifts, "shifts", torch.float32, 3)
     B, P, H = grad_out.shape[0], grad_out.shape[1], grad_out.shape[2]
     Bv, D = src.shape[0], src.shape[1]
     Br = rot.shape[0]
     Bs = shifts.shape[0] if shifts is not None else 0
+    _shape(grad_out, "grad_out", (B, P, H, H // 2 + 1))
+    _shape(src, "src", (Bv, D, D // 2 + 1))
+    _shape(rot, "rot", (Br, P, 2, 2))
+    _shape(shifts, "shifts", (Bs, P, 2))
+    _bcast(B, Bv=Bv, Br=Br, Bs=Bs)
+    dev = grad_out.device
+    _placed(dev, grad_out=grad_out, src=src, rot=rot, shifts=shifts)
     gx = torch.empty_like(src) if need_src else None
     gr = torch.empty_like(rot) if need_rot else None
     gs = torch.empty_like(shifts) if (need_shifts and shifts is not None) else None
@@ -377,17 +452,23 @@ def backproject_2d_to_2d(images, rot, weights=None, shifts=None, *, D=None, Bv=1
                          oversampling=1.0, radius_cutoff=-1.0):
     """Accumulation into 2D reconstructions (adjoint of project_2d_to_2d):
     returns (data, weight or None), complex64 / float32 [Bv, D, D//2+1]."""
-    _req(images, "images", torch.complex64, 4)
-    dev = images.device
-    _req(rot, "rot", torch.float32, 4, dev)
+    _typ(images, "images", torch.complex64, 4)
+    _typ(rot, "rot", torch.float32, 4)
     if weights is not None:
-        _req(weights, "weights", torch.float32, 4, dev)
+        _typ(weights, "weights", torch.float32, 4)
     if shifts is not None:
-        _req(shifts, "shifts", torch.float32, 3, dev)
+        _typ(shifts, "shifts", torch.float32, 3)
     B, P, H = images.shape[0], images.shape[1], images.shape[2]
     Br = rot.shape[0]
     Bs = shifts.shape[0] if shifts is not None else 0
     D = D or H
+    _shape(images, "images", (B, P, H, H // 2 + 1))
+    _shape(weights, "weights", (B, P, H, H // 2 + 1))
+    _shape(rot, "rot", (Br, P, 2, 2))
+    _shape(shifts, "shifts", (Bs, P, 2))
+    _bcast(B, Bv=Bv, Br=Br, Bs=Bs)
+    dev = images.device
+    _placed(dev, images=images, rot=rot, weights=weights, shifts=shifts)
     data = torch.empty((Bv, D, D // 2 + 1), dtype=torch.complex64, device=dev)
     wimg = torch.empty((Bv, D, D // 2 + 1), dtype=torch.float32, device=dev) if weights is not None else None
     g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
@@ -402,20 +483,29 @@ def backproject_2d_to_2d_backward(grad_data, images, rot, grad_weight=None, weig
                                   need_weights=True, need_rot=True, need_shifts=True):
     """Backward of backproject_2d_to_2d; returns (grad_images, grad_weights,
     grad_rot, grad_shifts), None where not requested."""
-    _req(grad_data, "grad_data", torch.complex64, 3)
-    dev = grad_data.device
-    _req(images, "images", torch.complex64, 4, dev)
-    _req(rot, "rot", torch.float32, 4, dev)
+    _typ(grad_data, "grad_data", torch.complex64, 3)
+    _typ(images, "images", torch.complex64, 4)
+    _typ(rot, "rot", torch.float32, 4)
     if grad_weight is not None:
-        _req(grad_weight, "grad_weight", torch.float32, 3, dev)
+        _typ(grad_weight, "grad_weight", torch.float32, 3)
     if weights is not None:
-        _req(weights, "weights", torch.float32, 4, dev)
+        _typ(weights, "weights", torch.float32, 4)
     if shifts is not None:
-        _req(shifts, "shifts", torch.float32, 3, dev)
+        _typ(shifts, "shifts", torch.float32, 3)
     B, P, H = images.shape[0], images.shape[1], images.shape[2]
     Bv, D = grad_data.shape[0], grad_data.shape[1]
     Br = rot.shape[0]
     Bs = shifts.shape[0] if shifts is not None else 0
+    _shape(grad_data, "grad_data", (Bv, D, D // 2 + 1))
+    _shape(grad_weight, "grad_weight", (Bv, D, D // 2 + 1))
+    _shape(images, "images", (B, P, H, H // 2 + 1))
+    _shape(weights, "weights", (B, P, H, H // 2 + 1))
+    _shape(rot, "rot", (Br, P, 2, 2))
+    _shape(shifts, "shifts", (Bs, P, 2))
+    _bcast(B, Bv=Bv, Br=Br, Bs=Bs)
+    dev = grad_data.device
+    _placed(dev, grad_data=grad_data, images=images, rot=rot, grad_weight=grad_weight, weights=weights,
+            shifts=shifts)
     gi = torch.empty_like(images) if need_images else None
     gw = torch.empty((B, P, H, H // 2 + 1), dtype=torch.float32, device=dev) if (
         need_weights and weights is not None) else None

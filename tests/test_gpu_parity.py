@@ -315,7 +315,9 @@ def test_lattice_rotations_are_exact():
     """The 24 signed permutations map every pixel to a lattice point, where
     both kernels take the stored entry itself (weights exactly 1 and 0): the
     GPU forward must equal the oracle bit for bit, Friedel conjugation
-    included."""
+    included.  The backward there meets the linear kernel's kink: the volume,
+    rotation and shift gradients (linear and cubic) must match the oracle's
+    derivative of the cell [floor(p), floor(p)+1)."""
     import itertools
     D = 16
     rng = np.random.default_rng(29)
@@ -329,9 +331,25 @@ def test_lattice_rotations_are_exact():
             if np.linalg.det(R) > 0:
                 mats.append(R)
     rot = np.array(mats)[None]
-    log(f"[parity] {rot.shape[1]} lattice rotations, D={D}")
-    tv, tr = dev(vol, rot)
+    P = rot.shape[1]
+    sh = rng.uniform(-3, 3, (1, P, 2)).astype(np.float32)
+    g = workloads.random_complex(rng, (1, P, D, D // 2 + 1))
+    wts = rng.random((1, P, D, D // 2 + 1)).astype(np.float32)
+    gwv = rng.standard_normal((1, D, D, D // 2 + 1)).astype(np.float32)
+    log(f"[parity] {P} lattice rotations, D={D}")
+    tv, tr, ts, tg, tw, tgw = dev(vol, rot, sh, g, wts, gwv)
     for interp, code in (("linear", 0), ("cubic", 1)):
         out = host(bp.project_3d_to_2d(tv, tr, interp=interp))
         ref = oracle.project(vol, rot, interp=code).astype(np.complex64)
         assert np.array_equal(out, ref), (interp, float(np.abs(out - ref).max()))
+        gv, gr, gs = bp.project_3d_to_2d_backward(tg, tv, tr, ts, interp=interp)
+        rgv, rgr, rgs = oracle.project_backward(g, vol, rot, sh, interp=code)
+        errs = (rel(gv, rgv), rel(gr, rgr), rel(gs, rgs))
+        log(f"[parity] lattice {interp}: grad_vol {errs[0]:.2e} grad_rot {errs[1]:.2e} grad_shifts {errs[2]:.2e}")
+        assert max(errs) <= BWD_TOL, (interp, errs)
+        assert np.all(host(gr)[..., 2] == 0)
+        # back-projection backward: images g, weights, grad volumes (vol, gwv)
+        gi, gw, gr2, gs2 = bp.backproject_2d_to_3d_backward(tv, tg, tr, tgw, tw, ts, interp=interp)
+        rgi, rgw, rgr2, rgs2 = oracle.backproject_backward(vol, g, rot, gwv, wts, sh, interp=code)
+        errs = (rel(gi, rgi), rel(gw, rgw), rel(gr2, rgr2), rel(gs2, rgs2))
+        assert max(errs) <= BWD_TOL, (interp, errs)

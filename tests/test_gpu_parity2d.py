@@ -188,3 +188,43 @@ def test_2d_empty_and_degenerate():
     eye = torch.eye(2, dtype=torch.float32, device="cuda:0")[None, None].contiguous()
     same = bp.project_2d_to_2d(ts, eye, interp="cubic").cpu().numpy()[0, 0]
     assert np.array_equal(same, src[0])
+
+
+def test_2d_lattice_maps_gradients():
+    """The eight signed permutations put every sample on a lattice point: the
+    forward is exact and the gradients (linear: derivative of the cell
+    [floor(p), floor(p)+1); cubic) match the oracle."""
+    import itertools
+    D = 16
+    rng = np.random.default_rng(23)
+    src = workloads.random_complex(rng, (1, D, D // 2 + 1))
+    mats = []
+    for perm in itertools.permutations(range(2)):
+        for sg in itertools.product((1, -1), repeat=2):
+            M = np.zeros((2, 2), np.float32)
+            for i in range(2):
+                M[i, perm[i]] = sg[i]
+            mats.append(M)
+    rot = np.array(mats)[None]
+    P = rot.shape[1]
+    sh = rng.uniform(-3, 3, (1, P, 2)).astype(np.float32)
+    g = workloads.random_complex(rng, (1, P, D, D // 2 + 1))
+    imgs = workloads.random_complex(rng, (1, P, D, D // 2 + 1))
+    wts = rng.random((1, P, D, D // 2 + 1)).astype(np.float32)
+    gd = workloads.random_complex(rng, (1, D, D // 2 + 1))
+    gw = rng.standard_normal((1, D, D // 2 + 1)).astype(np.float32)
+    ts, tr, tsh, tg, ti, tw, tgd, tgw = dev(src, rot, sh, g, imgs, wts, gd, gw)
+    log(f"[parity2d] {P} signed permutations, D={D}")
+    for interp, code in (("linear", 0), ("cubic", 1)):
+        out = bp.project_2d_to_2d(ts, tr, tsh, interp=interp).cpu().numpy()
+        ref = oracle.project2d(src, rot, sh, interp=code)
+        assert rel(out, ref) <= FWD_TOL, (interp, rel(out, ref))
+        gx, gr, gs = bp.project_2d_to_2d_backward(tg, ts, tr, tsh, interp=interp)
+        rgx, rgr, rgs = oracle.project2d_backward(g, src, rot, sh, interp=code)
+        errs = (rel(gx, rgx), rel(gr, rgr), rel(gs, rgs))
+        log(f"[parity2d] lattice {interp}: grad_src {errs[0]:.2e} grad_rot {errs[1]:.2e} grad_shifts {errs[2]:.2e}")
+        assert max(errs) <= BWD_TOL, (interp, errs)
+        gi, gwo, gr2, gs2 = bp.backproject_2d_to_2d_backward(tgd, ti, tr, tgw, tw, tsh, interp=interp)
+        rgi, rgwo, rgr2, rgs2 = oracle.backproject2d_backward(gd, imgs, rot, gw, wts, sh, interp=code)
+        errs = (rel(gi, rgi), rel(gwo, rgwo), rel(gr2, rgr2), rel(gs2, rgs2))
+        assert max(errs) <= BWD_TOL, (interp, errs)
