@@ -35,7 +35,7 @@ import torch
 __all__ = [
     "project_3d_to_2d", "project_3d_to_2d_backward", "backproject_2d_to_3d", "backproject_2d_to_3d_backward",
     "project_2d_to_2d", "project_2d_to_2d_backward", "backproject_2d_to_2d", "backproject_2d_to_2d_backward",
-    "volume_rfft", "images_irfft", "weight_images", "finish_reconstruction",
+    "project_3d_to_2d_noalloc", "NOALLOC_SCRATCH_BYTES", "volume_rfft", "images_irfft", "weight_images", "finish_reconstruction",
     "TprojError", "lib", "Geom", "LIB_PATH", "HEADER_SYMBOLS", "SPECTRAL_SYMBOLS", "timing_enable", "timing_read",
     "KERNEL_CLASSES",
 ]
@@ -48,8 +48,12 @@ HEADER_SYMBOLS = (
     "project_3d_to_2d", "project_3d_to_2d_backward", "backproject_2d_to_3d", "backproject_2d_to_3d_backward",
     "project_2d_to_2d", "project_2d_to_2d_backward", "backproject_2d_to_2d", "backproject_2d_to_2d_backward",
     "tp_workspace_size", "tp_validate", "tp_status_string", "tp_last_error_detail", "tp_abi_version",
-    "tp_timing_enable", "tp_timing_read",
+    "tp_timing_enable", "tp_timing_read", "project_3d_to_2d_noalloc",
 )
+
+# TP_NOALLOC_SCRATCH_BYTES of include/tproj.h: the static work area of
+# project_3d_to_2d_noalloc (per GPU).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every symbol that include/tproj_spectral.h declares.
 SPECTRAL_SYMBOLS = (
@@ -91,6 +95,8 @@ def lib():
         L.project_3d_to_2d_backward.argtypes = [G, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.backproject_2d_to_3d.argtypes = [G, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
         L.backproject_2d_to_3d_backward.argtypes = [G] + [_vp] * 11 + [ctypes.c_size_t, _vp]
+        L.project_3d_to_2d_noalloc.argtypes = [G, _vp, _vp, _vp, _vp, _vp]
+        L.project_3d_to_2d_noalloc.restype = ctypes.c_int
         L.project_2d_to_2d.argtypes = L.project_3d_to_2d.argtypes
         L.project_2d_to_2d_backward.argtypes = L.project_3d_to_2d_backward.argtypes
         L.backproject_2d_to_2d.argtypes = L.backproject_2d_to_3d.argtypes
@@ -260,6 +266,34 @@ def project_3d_to_2d(vol, rot, shifts=None, *, H=None, interp="cubic", oversampl
     ws, nws = _workspace(g, OP_PROJECT, dev)
     _check(lib().project_3d_to_2d(ctypes.byref(g), _ptr(vol), _ptr(rot), _ptr(shifts), _ptr(out), _ptr(ws), nws,
                                   _stream(dev)))
+    return out
+
+
+def project_3d_to_2d_noalloc(vol, rot, shifts, out, *, interp="cubic", oversampling=1.0, radius_cutoff=-1.0):
+    """project_3d_to_2d for callers that cannot allocate: no workspace, no
+    output allocation (out, complex64 [B, P, H, H//2+1], is required and gives
+    B and H).  The library's static per-GPU work area holds the scratch;
+    geometries that need more than NOALLOC_SCRATCH_BYTES are rejected.
+    Calls that overlap on one GPU race (they share that area)."""
+    _typ(vol, "vol", torch.complex64, 4)
+    _typ(rot, "rot", torch.float32, 4)
+    _typ(out, "out", torch.complex64, 4)
+    if shifts is not None:
+        _typ(shifts, "shifts", torch.float32, 3)
+    Bv, D = vol.shape[0], vol.shape[1]
+    Br, P = rot.shape[0], rot.shape[1]
+    Bs = shifts.shape[0] if shifts is not None else 0
+    B, H = out.shape[0], out.shape[2]
+    _shape(vol, "vol", (Bv, D, D, D // 2 + 1))
+    _shape(rot, "rot", (Br, P, 3, 3))
+    _shape(shifts, "shifts", (Bs, P, 2))
+    _shape(out, "out", (B, P, H, H // 2 + 1))
+    _bcast(B, Bv=Bv, Br=Br, Bs=Bs)
+    dev = vol.device
+    _placed(dev, vol=vol, rot=rot, shifts=shifts, out=out)
+    g = Geom(B, P, Bv, Br, Bs, D, H, _interp(interp), float(oversampling), float(radius_cutoff))
+    _check(lib().project_3d_to_2d_noalloc(ctypes.byref(g), _ptr(vol), _ptr(rot), _ptr(shifts), _ptr(out),
+                                          _stream(dev)))
     return out
 
 

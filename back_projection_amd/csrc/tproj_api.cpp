@@ -20,6 +20,14 @@
 #include "bwd_kernels.h"
 #include "kernels_2d.h"
 
+// The static work area of project_3d_to_2d_noalloc: a file-scope device
+// array, so every GPU the library runs on holds its own copy for the life of
+// the process.  Host code never uses the array's name as an address (on the
+// host it only names the symbol); the device address of the current GPU's
+// copy comes from hipGetSymbolAddress, once per device on that device's first
+// call (scratch_address below), and only that address is passed on.
+static __device__ __align__(256) unsigned char scratch[TP_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_detail;
@@ -317,8 +325,11 @@ SideStream* side_stream() {
 }
 
 // Forward gather: brick-binned kernels when the plan applies, else direct.
+// may_alloc = false: no timing events and no side stream (whose first use
+// creates a stream and events): everything on st.
 tp_status run_forward(const tp_geom* geom, const tproj::KGeom& k, const float2* vol, const float* rot,
-                      const float* shifts, float2* out, void* workspace, size_t ws_bytes, hipStream_t st) {
+                      const float* shifts, float2* out, void* workspace, size_t ws_bytes, hipStream_t st,
+                      bool may_alloc = true) {
   const GatherPlan pl = gather_plan(geom);
   if (!pl.ok) {
     LAUNCH(tproj::launch_project(k, geom->interp, vol, rot, shifts, out, st), "project");
@@ -327,10 +338,10 @@ tp_status run_forward(const tp_geom* geom, const tproj::KGeom& k, const float2* 
   if (!workspace || ws_bytes < pl.ws_bytes)
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
   const tproj::BrickWork wk = tproj::brick_work(pl.bg, geom->Bv, workspace);
-  const tproj::EvPair ev = kt_copy(TP_KT_FORWARD);
+  const tproj::EvPair ev = may_alloc ? kt_copy(TP_KT_FORWARD) : tproj::EvPair{};
   // the edge kernel on the side stream, beside the work list and the bricks
   std::lock_guard<std::mutex> lk(g_side_mu);
-  SideStream* ss = worth_splitting(geom, 23, st) ? side_stream() : nullptr;
+  SideStream* ss = may_alloc && worth_splitting(geom, 23, st) ? side_stream() : nullptr;
   hipStream_t se = st;
   if (ss) {
     hipError_t e = hipEventRecord(ss->fork, st);
@@ -411,6 +422,38 @@ tp_status run_bwd(const tp_geom* geom, const tproj::KGeom& k, const float2* Y, c
   LAUNCH(tproj::launch_bwd(k, geom->interp, pl.bw, workspace, Y, Wimg, rot, shifts, vol, wvol, st,
                            eb.a ? &eb : nullptr, ef.a ? &ef : nullptr, fork),
          "back-projection (bricks)");
+  return TP_OK;
+}
+
+// ---- the static work area of project_3d_to_2d_noalloc (declared above) ----
+struct ScratchAddr {
+  void* ptr = nullptr;
+  bool tried = false;
+  hipError_t err = hipSuccess;
+};
+ScratchAddr g_scratch[MAX_DEVICES];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array.
+tp_status scratch_address(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+    (void)hipGetLastError();
+    return fail(TP_E_DEVICE, "no usable HIP device for the static scratch");
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  ScratchAddr& sa = g_scratch[dev];
+  if (!sa.tried) {
+    sa.tried = true;
+    sa.err = hipGetSymbolAddress(&sa.ptr, HIP_SYMBOL(scratch));
+    if (sa.err != hipSuccess || sa.ptr == nullptr) {
+      (void)hipGetLastError();
+      sa.ptr = nullptr;
+      if (sa.err == hipSuccess) sa.err = hipErrorInvalidSymbol;
+    }
+  }
+  if (!sa.ptr) return fail(TP_E_DEVICE, "address of the static scratch on device %d: %s", dev, hipGetErrorString(sa.err));
+  *ptr = sa.ptr;
   return TP_OK;
 }
 
@@ -549,6 +592,29 @@ tp_status project_3d_to_2d(const tp_geom* geom, const void* vol, const float* ro
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
   TRY(run_forward(geom, k, (const float2*)vol, rot, shifts, (float2*)out, workspace, ws_bytes, st));
+  return ok();
+}
+
+tp_status project_3d_to_2d_noalloc(const tp_geom* geom, const void* vol, const float* rot, const float* shifts,
+                                   void* out, void* stream) {
+  TRY(check_geom(geom));
+  TRY(check_shifts(geom, shifts));
+  TRY(check_ptr(vol, "vol", 8));
+  TRY(check_ptr(rot, "rot", 4));
+  TRY(check_opt(shifts, "shifts", 4));
+  TRY(check_ptr(out, "out", 8));
+  const size_t need = workspace_need(geom, TP_OP_PROJECT);
+  if (need > TP_NOALLOC_SCRATCH_BYTES)
+    return fail(TP_E_WORKSPACE, "this geometry needs %zu bytes of scratch, more than the %zu bytes of the static "
+                "array of project_3d_to_2d_noalloc (use project_3d_to_2d with a workspace)",
+                need, (size_t)TP_NOALLOC_SCRATCH_BYTES);
+  TRY(check_device());
+  void* ws = nullptr;
+  TRY(scratch_address(&ws));
+  const tproj::KGeom k = kgeom(geom);
+  hipStream_t st = (hipStream_t)stream;
+  TRY(run_forward(geom, k, (const float2*)vol, rot, shifts, (float2*)out, ws, TP_NOALLOC_SCRATCH_BYTES, st,
+                  /*may_alloc=*/false));
   return ok();
 }
 

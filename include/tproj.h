@@ -189,6 +189,24 @@ tp_status backproject_2d_to_2d_backward(const tp_geom* geom, const void* grad_da
                                         float* grad_rot, float* grad_shifts, void* workspace, size_t ws_bytes,
                                         void* stream);
 
+/* Allocation-free variant of project_3d_to_2d, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * project_3d_to_2d, minus the workspace: the forward's work area (work list
+ * and hit lists, tp_workspace_size(geom, TP_OP_PROJECT) bytes) lives in a
+ * library-owned static device array of TP_NOALLOC_SCRATCH_BYTES, one per GPU,
+ * held until the process ends.  A geometry that needs more is rejected with
+ * TP_E_WORKSPACE before anything is enqueued (D = 128 with 16384 poses needs
+ * about 24 MB).  The call enqueues on `stream` only (no side stream, no
+ * timing events) and allocates nothing.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (two streams, two threads) race
+ * and must be serialised by the caller.  The array keeps the last call's
+ * contents; the kernels rewrite every part of it they read, so nothing needs
+ * clearing between calls.                                                   */
+#define TP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+tp_status project_3d_to_2d_noalloc(const tp_geom* geom, const void* vol, const float* rot, const float* shifts,
+                                   void* out, void* stream);
+
 /* Bytes of workspace the operation `op` (TP_OP_*) needs for this geometry
  * (0 when none).  Returns (size_t)-1 for an invalid geometry.  The brick
  * kernels keep there their work list and per work item the list of poses

@@ -200,3 +200,27 @@ def test_timing_api_host_side(L):
     assert L.tp_timing_read(-1, ctypes.byref(ms), ctypes.byref(n)) == TP_E_VALUE
     assert L.tp_timing_read(1, None, ctypes.byref(n)) == TP_E_NULL
     assert bp.timing_read("fold") == (0.0, 0)
+
+
+def test_noalloc_forward_rejects_before_launch(L):
+    """The allocation-free forward checks its arguments and the size of its
+    static work area on the host; on a machine without a GPU a valid call
+    stops at the device check (TP_E_DEVICE), never at a launch."""
+    g = geom()
+    gp = ctypes.byref(g)
+    assert L.project_3d_to_2d_noalloc(gp, None, FAKE, None, FAKE, None) == TP_E_NULL
+    assert L.project_3d_to_2d_noalloc(gp, FAKE, FAKE, None, None, None) == TP_E_NULL
+    assert L.project_3d_to_2d_noalloc(gp, ODD, FAKE, None, FAKE, None) == TP_E_VALUE
+    assert L.project_3d_to_2d_noalloc(gp, FAKE, FAKE, FAKE, FAKE, None) == TP_E_VALUE    # shifts but Bs = 0
+    big = geom(P=65536, D=128, H=128, radius_cutoff=64.0)
+    need = L.tp_workspace_size(ctypes.byref(big), 0)
+    assert need > bp.NOALLOC_SCRATCH_BYTES
+    assert L.project_3d_to_2d_noalloc(ctypes.byref(big), FAKE, FAKE, None, FAKE, None) == TP_E_WORKSPACE
+    assert b"static" in L.tp_last_error_detail()
+    # the D = 128 workload with 16384 poses fits
+    cfg = geom(P=16384, D=128, H=128, Bs=1, radius_cutoff=64.0)
+    assert L.tp_workspace_size(ctypes.byref(cfg), 0) <= bp.NOALLOC_SCRATCH_BYTES
+    import torch
+    if not torch.cuda.is_available():
+        assert L.project_3d_to_2d_noalloc(gp, FAKE, FAKE, None, FAKE, None) == TP_E_DEVICE
+        assert L.project_3d_to_2d(gp, FAKE, FAKE, None, FAKE, FAKE, 1 << 20, None) == TP_E_DEVICE
