@@ -158,18 +158,64 @@ __device__ __forceinline__ float2 tap_value(const float2* __restrict__ V, const 
 
 // ---------------------------------------------------------------------------
 // LDS tile of one brick: the S^3 owned floor values plus the interpolation
-// halo (1 below and 2 above for cubic, 1 above for linear), 16^3 entries with
-// padded strides.
+// halo (1 below and 2 above for cubic, 1 above for linear), 16^3 entries.
+//
+// Cubic tiles use the bank-split layout: entry (x, y, z) sits at
+//   (x & 3) + 16 (x >> 2) + 64 y + 4 (z & 3) + 1024 (z >> 2)
+// (dense, 4096 entries), so that the bank pair of an 8-byte entry (address
+// mod 16) is (x & 3) + 4 (z & 3), whatever y is.  A pixel's 4^3 taps cover
+// every (x & 3, z & 3) pair once per y row, and a lane may visit its x taps
+// and its z taps in any cyclic order: with the order chosen from the lane's
+// slot in its group of 16 (split_taps), the 16 lanes of a group touch 16
+// distinct bank pairs at every step of the tap loop, for any pixels they
+// hold.  Measured on random footprints: the conflict-free LDS rate (15.3
+// reads and 10.3 64-bit atomics per clock per CU, against 7.1 and 7.0 for
+// padded strides with the lanes ranked by bank key).
+// Linear tiles keep padded strides (rows of 17, planes of 276 entries) and the
+// rank permutation of the lanes (spread_dest).
 // ---------------------------------------------------------------------------
 template <int NT>
 struct Tile {
   static constexpr int S = 17 - NT;          // 13 (cubic) or 15 (linear)
   static constexpr int E = 16;               // tile edge = S + NT - 1
   static constexpr int HL = NT == 4 ? 1 : 0; // halo below
-  static constexpr int SY = 17;              // row stride (padded)
-  static constexpr int SZ = 16 * 17 + 4;     // plane stride (padded)
-  static constexpr int SIZE = E * SZ;
+  static constexpr bool SPLIT = NT == 4;     // bank-split layout (cubic)
+  static constexpr int SY = SPLIT ? 64 : 17;             // y stride
+  static constexpr int SZ = 16 * 17 + 4;     // plane stride (padded layout)
+  static constexpr int SIZE = SPLIT ? 4096 : E * SZ;
 };
+
+__device__ __forceinline__ int split_x(int x) { return (x & 3) + ((x >> 2) << 4); }
+__device__ __forceinline__ int split_z(int z) { return ((z & 3) << 2) + ((z >> 2) << 10); }
+
+// Address of tile entry (x, y, z) in [0, 16)^3.
+template <int NT>
+__device__ __forceinline__ int tile_addr(int x, int y, int z) {
+  if constexpr (Tile<NT>::SPLIT) return split_x(x) + 64 * y + split_z(z);
+  else return z * Tile<NT>::SZ + y * Tile<NT>::SY + x;
+}
+
+// The tap order of one lane in the bank-split tile, for the pixel whose first
+// tap is tile entry l: its slot (lane & 3, (lane >> 2) & 3) fixes the
+// rotations t (x) and r (z) that put the lane's step-(a, c) tap in bank pair
+// ((lane + a) & 3) + 4 (((lane >> 2) + c) & 3).  Step (a, b, c) reads entry
+// xo[a] + zo[c] + 64 b, i.e. the tap (l0 + ((a + t) & 3), l1 + b,
+// l2 + ((c + r) & 3)), whose x and z weights are those of index (a + t) & 3
+// and (c + r) & 3.
+struct SplitTaps {
+  int xo[4], zo[4];
+  int t, r;
+};
+__device__ __forceinline__ void split_taps(const int l[3], SplitTaps& s) {
+  const int lane = (int)threadIdx.x;
+  s.t = ((lane & 3) - l[0]) & 3;
+  s.r = (((lane >> 2) & 3) - l[2]) & 3;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s.xo[j] = split_x(l[0] + ((j + s.t) & 3));
+    s.zo[j] = split_z(l[2] + ((j + s.r) & 3)) + 64 * l[1];
+  }
+}
 
 // floor(p) relative to the brick's low corner; true if inside [0, S)^3.
 __device__ __forceinline__ bool owned(const float p[3], const int lo[3], int S, int l[3]) {
@@ -215,7 +261,7 @@ __device__ __forceinline__ void stage_tile_t(T* tile, const T* __restrict__ V, c
   for (int k = 0; k < N / THREADS; ++k) {
     const int i = (int)threadIdx.x + k * THREADS;
     const int x = i & 15, y = (i >> 4) & 15, z = i >> 8;
-    tile[z * Tl::SZ + y * Tl::SY + x] = v[k];
+    tile[tile_addr<NT>(x, y, z)] = v[k];
   }
 }
 
@@ -233,23 +279,15 @@ __device__ __forceinline__ void rotate4(float w[4], int r) {
 }
 
 // Value (and, with DERIV, the partial derivatives along x, y, z) of the
-// interpolant from the tile, for the axis weights w* (and their derivatives
-// d*) of the sample; l = floor(p) - lo.
-// zr (cubic only, else 0): the planes are visited in the order
-// c = (c' + zr) mod 4, c' = 0..3 (see spread_dest_planes).
+// interpolant from a padded-stride tile (linear kernels), for the axis weights
+// w* (and their derivatives d*) of the sample; l = floor(p) - lo.
 template <int NT, bool DERIV, typename T, int SY = Tile<NT>::SY, int SZ = Tile<NT>::SZ>
 __device__ __forceinline__ void interp_tile_w(const T* tile, const int l[3], const float wx[NT], const float wy[NT],
-                                              const float wz_in[NT], const float dx[NT], const float dy[NT],
-                                              const float dz_in[NT], T& I, T* dI, int zr = 0) {
+                                              const float wz[NT], const float dx[NT], const float dy[NT],
+                                              const float dz[NT], T& I, T* dI) {
   static_assert(NT == 4 || NT == 2, "cubic or linear");
+  static_assert(!Tile<NT>::SPLIT, "bank-split tiles are read with interp_split");
   const T* base = tile + l[2] * SZ + l[1] * SY + l[0];
-  float wz[NT], dz[NT];
-#pragma unroll
-  for (int c = 0; c < NT; ++c) { wz[c] = wz_in[c]; dz[c] = DERIV ? dz_in[c] : 0.f; }
-  if constexpr (NT == 4) {
-    rotate4(wz, zr);
-    if constexpr (DERIV) rotate4(dz, zr);
-  }
   T z0 = zero_of(T{});
   I = z0;
   if constexpr (DERIV) { dI[0] = z0; dI[1] = z0; dI[2] = z0; }
@@ -257,7 +295,7 @@ __device__ __forceinline__ void interp_tile_w(const T* tile, const int l[3], con
 #pragma unroll
   for (int c = 0; c < NT; ++c) {
     T s = z0, sx = z0, sy = z0;   // plane sums: wy*r, wy*rx, dy*r
-    const T* plane = base + (NT == 4 ? ((c + zr) & 3) : c) * SZ;
+    const T* plane = base + c * SZ;
 #pragma unroll
     for (int b = 0; b < NT; ++b) {
       const T* row = plane + b * SY;
@@ -283,20 +321,60 @@ __device__ __forceinline__ void interp_tile_w(const T* tile, const int l[3], con
   }
 }
 
-// Same, computing the weights from p.
-template <int NT, bool DERIV, typename T>
-__device__ __forceinline__ void interp_tile_t(const T* tile, const float p[3], const int l[3], T& I, T* dI) {
-  float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
-  const float fx = p[0] - floorf(p[0]), fy = p[1] - floorf(p[1]), fz = p[2] - floorf(p[2]);
-  axis_weights<NT>(fx, wx);
-  axis_weights<NT>(fy, wy);
-  axis_weights<NT>(fz, wz);
-  if constexpr (DERIV) {
-    axis_dweights<NT>(fx, dx);
-    axis_dweights<NT>(fy, dy);
-    axis_dweights<NT>(fz, dz);
+// Value (and, with DERIV, the partial derivatives along x, y, z) of the
+// cubic interpolant from a bank-split tile, in this lane's tap order
+// (split_taps); l = floor(p) - lo is the tile entry of the first tap, w* / d*
+// the axis weights (and derivatives) in tap order.  Contracts y within each
+// column, then x within each plane, then z.
+template <bool DERIV, typename T>
+__device__ __forceinline__ void interp_split(const T* tile, const int l[3], const float wx_in[4], const float wy[4],
+                                             const float wz_in[4], const float dx_in[4], const float dy[4],
+                                             const float dz_in[4], T& I, T* dI) {
+  SplitTaps st;
+  split_taps(l, st);
+  float wx[4], wz[4], dx[4], dz[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    wx[j] = wx_in[j];
+    wz[j] = wz_in[j];
+    dx[j] = DERIV ? dx_in[j] : 0.f;
+    dz[j] = DERIV ? dz_in[j] : 0.f;
   }
-  interp_tile_w<NT, DERIV>(tile, l, wx, wy, wz, dx, dy, dz, I, dI);
+  rotate4(wx, st.t);
+  rotate4(wz, st.r);
+  if constexpr (DERIV) {
+    rotate4(dx, st.t);
+    rotate4(dz, st.r);
+  }
+  const T z0 = zero_of(T{});
+  I = z0;
+  if constexpr (DERIV) { dI[0] = z0; dI[1] = z0; dI[2] = z0; }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    T p = z0, px = z0, py = z0;   // plane sums: wx*q, dx*q, wx*qy
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const T* col = tile + st.xo[a] + st.zo[c];
+      T q = z0, qy = z0;          // column sums: wy*v, dy*v
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const T v = col[64 * b];
+        fma_into(wy[b], v, q);
+        if constexpr (DERIV) fma_into(dy[b], v, qy);
+      }
+      fma_into(wx[a], q, p);
+      if constexpr (DERIV) {
+        fma_into(dx[a], q, px);
+        fma_into(wx[a], qy, py);
+      }
+    }
+    fma_into(wz[c], p, I);
+    if constexpr (DERIV) {
+      fma_into(wz[c], px, dI[0]);
+      fma_into(wz[c], py, dI[1]);
+      fma_into(dz[c], p, dI[2]);
+    }
+  }
 }
 
 // Largest |p| = |A k| over the in-mask pixels of a pose: kmax * sigma_max(A).

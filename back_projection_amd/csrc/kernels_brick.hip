@@ -127,38 +127,52 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
         for (int c0 = wave * 64; c0 < ncand; c0 += FWD_NW * 64) {   // wave-uniform (lane permutes)
           Cand cu;
           cand_prep(es, g, c0 + lane, ncand, lo, bg.S, cu);
-          // the interpolation runs in the lane the bank-spreading order gives
-          // the pixel; the value comes back to the pixel's own lane
-          float f[3] = {0.f, 0.f, 0.f};
-          int pk = 0, key = -1;
-          if (cu.act) {
-#pragma unroll
-            for (int a = 0; a < 3; ++a) f[a] = cu.p[a] - floorf(cu.p[a]);
-            pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
-            key = (cu.l[0] + cu.l[1] * Tl::SY + cu.l[2] * Tl::SZ) & 15;
-          }
-          constexpr bool PLANES = NT == 4 && CPLX;   // plane rotation for 8-byte cubic taps
-          const int dest = PLANES ? spread_dest_planes(key) : spread_dest(key);
-          const int mpk = lane_send(pk, dest);
-          float mf[3];
-#pragma unroll
-          for (int a = 0; a < 3; ++a) mf[a] = lane_send(f[a], dest);
-          T I = zero_of(T{});
-          if (mpk & 1) {
-            const int ml[3] = {(mpk >> 1) & 15, (mpk >> 5) & 15, (mpk >> 9) & 15};
-            float wx[NT], wy[NT], wz[NT];
-            axis_weights<NT>(mf[0], wx);
-            axis_weights<NT>(mf[1], wy);
-            axis_weights<NT>(mf[2], wz);
-            const int zr = PLANES ? plane_rotation((ml[0] + ml[1] * Tl::SY + ml[2] * Tl::SZ) & 15) : 0;
-            interp_tile_w<NT, false>(tile, ml, wx, wy, wz, wx, wy, wz, I, (T*)nullptr, zr);
-          }
-          I = lane_fetch(I, dest);
-          if (cu.act) {
-            if constexpr (CPLX) {
-              if (shifts) I = cmul(shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h), I);
+          if constexpr (Tl::SPLIT) {
+            // each lane interpolates its own pixel, in its slot's tap order
+            if (cu.act) {
+              float wx[4], wy[4], wz[4];
+              axis_weights<4>(cu.p[0] - floorf(cu.p[0]), wx);
+              axis_weights<4>(cu.p[1] - floorf(cu.p[1]), wy);
+              axis_weights<4>(cu.p[2] - floorf(cu.p[2]), wz);
+              T I;
+              interp_split<false>(tile, cu.l, wx, wy, wz, wx, wy, wz, I, (T*)nullptr);
+              if constexpr (CPLX) {
+                if (shifts) I = cmul(shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h), I);
+              }
+              out[cu.k] = I;
             }
-            out[cu.k] = I;
+          } else {
+            // the interpolation runs in the lane the bank-spreading order gives
+            // the pixel; the value comes back to the pixel's own lane
+            float f[3] = {0.f, 0.f, 0.f};
+            int pk = 0, key = -1;
+            if (cu.act) {
+#pragma unroll
+              for (int a = 0; a < 3; ++a) f[a] = cu.p[a] - floorf(cu.p[a]);
+              pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
+              key = (cu.l[0] + cu.l[1] * Tl::SY + cu.l[2] * Tl::SZ) & 15;
+            }
+            const int dest = spread_dest(key);
+            const int mpk = lane_send(pk, dest);
+            float mf[3];
+#pragma unroll
+            for (int a = 0; a < 3; ++a) mf[a] = lane_send(f[a], dest);
+            T I = zero_of(T{});
+            if (mpk & 1) {
+              const int ml[3] = {(mpk >> 1) & 15, (mpk >> 5) & 15, (mpk >> 9) & 15};
+              float wx[NT], wy[NT], wz[NT];
+              axis_weights<NT>(mf[0], wx);
+              axis_weights<NT>(mf[1], wy);
+              axis_weights<NT>(mf[2], wz);
+              interp_tile_w<NT, false>(tile, ml, wx, wy, wz, wx, wy, wz, I, (T*)nullptr);
+            }
+            I = lane_fetch(I, dest);
+            if (cu.act) {
+              if constexpr (CPLX) {
+                if (shifts) I = cmul(shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h), I);
+              }
+              out[cu.k] = I;
+            }
           }
         }
         __syncthreads();   // the next row stage rewrites the rows
@@ -267,38 +281,65 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
           Cand cu;
           cand_prep(es, g, c0 + lane, ncand, lo, bg.S, cu);
           float2 uc = make_float2(0.f, 0.f);
-          float ur = 0.f, f[3] = {0.f, 0.f, 0.f};
-          int pk = 0, key = -1;
-          if (cu.act) {
-            if constexpr (CPLX) uc = U[cu.k];
-            if constexpr (REAL) ur = Ur[cu.k];
-#pragma unroll
-            for (int a = 0; a < 3; ++a) f[a] = cu.p[a] - floorf(cu.p[a]);
-            pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
-            key = (cu.l[0] + cu.l[1] * Tl::SY + cu.l[2] * Tl::SZ) & 15;
-          }
-          // the interpolation runs in the lane the bank-spreading order gives
-          // the pixel; value and derivatives come back to the pixel's lane
-          constexpr bool PLANES = NT == 4 && CPLX;   // plane rotation for 8-byte cubic taps
-          const int dest = PLANES ? spread_dest_planes(key) : spread_dest(key);
-          const int mpk = lane_send(pk, dest);
-          float mf[3];
-#pragma unroll
-          for (int a = 0; a < 3; ++a) mf[a] = lane_send(f[a], dest);
+          float ur = 0.f;
           float2 Ic = make_float2(0.f, 0.f), dIc[3] = {Ic, Ic, Ic};
           float Ir = 0.f, dIr[3] = {0.f, 0.f, 0.f};
-          if (mpk & 1) {
-            const int ml[3] = {(mpk >> 1) & 15, (mpk >> 5) & 15, (mpk >> 9) & 15};
-            float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
-            axis_weights<NT>(mf[0], wx);
-            axis_weights<NT>(mf[1], wy);
-            axis_weights<NT>(mf[2], wz);
-            axis_dweights<NT>(mf[0], dx);
-            axis_dweights<NT>(mf[1], dy);
-            axis_dweights<NT>(mf[2], dz);
-            const int zr = PLANES ? plane_rotation((ml[0] + ml[1] * Tl::SY + ml[2] * Tl::SZ) & 15) : 0;
-            if constexpr (CPLX) interp_tile_w<NT, true>(tc, ml, wx, wy, wz, dx, dy, dz, Ic, dIc, zr);
-            if constexpr (REAL) interp_tile_w<NT, true>(tr, ml, wx, wy, wz, dx, dy, dz, Ir, dIr, zr);
+          if constexpr (Tl::SPLIT) {
+            // each lane interpolates its own pixel, in its slot's tap order
+            if (cu.act) {
+              if constexpr (CPLX) uc = U[cu.k];
+              if constexpr (REAL) ur = Ur[cu.k];
+              float wx[4], wy[4], wz[4], dx[4], dy[4], dz[4];
+              const float fx = cu.p[0] - floorf(cu.p[0]), fy = cu.p[1] - floorf(cu.p[1]),
+                          fz = cu.p[2] - floorf(cu.p[2]);
+              axis_weights<4>(fx, wx);
+              axis_weights<4>(fy, wy);
+              axis_weights<4>(fz, wz);
+              axis_dweights<4>(fx, dx);
+              axis_dweights<4>(fy, dy);
+              axis_dweights<4>(fz, dz);
+              if constexpr (CPLX) interp_split<true>(tc, cu.l, wx, wy, wz, dx, dy, dz, Ic, dIc);
+              if constexpr (REAL) interp_split<true>(tr, cu.l, wx, wy, wz, dx, dy, dz, Ir, dIr);
+            }
+          } else {
+            float f[3] = {0.f, 0.f, 0.f};
+            int pk = 0, key = -1;
+            if (cu.act) {
+              if constexpr (CPLX) uc = U[cu.k];
+              if constexpr (REAL) ur = Ur[cu.k];
+#pragma unroll
+              for (int a = 0; a < 3; ++a) f[a] = cu.p[a] - floorf(cu.p[a]);
+              pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
+              key = (cu.l[0] + cu.l[1] * Tl::SY + cu.l[2] * Tl::SZ) & 15;
+            }
+            // the interpolation runs in the lane the bank-spreading order gives
+            // the pixel; value and derivatives come back to the pixel's lane
+            const int dest = spread_dest(key);
+            const int mpk = lane_send(pk, dest);
+            float mf[3];
+#pragma unroll
+            for (int a = 0; a < 3; ++a) mf[a] = lane_send(f[a], dest);
+            if (mpk & 1) {
+              const int ml[3] = {(mpk >> 1) & 15, (mpk >> 5) & 15, (mpk >> 9) & 15};
+              float wx[NT], wy[NT], wz[NT], dx[NT], dy[NT], dz[NT];
+              axis_weights<NT>(mf[0], wx);
+              axis_weights<NT>(mf[1], wy);
+              axis_weights<NT>(mf[2], wz);
+              axis_dweights<NT>(mf[0], dx);
+              axis_dweights<NT>(mf[1], dy);
+              axis_dweights<NT>(mf[2], dz);
+              if constexpr (CPLX) interp_tile_w<NT, true>(tc, ml, wx, wy, wz, dx, dy, dz, Ic, dIc);
+              if constexpr (REAL) interp_tile_w<NT, true>(tr, ml, wx, wy, wz, dx, dy, dz, Ir, dIr);
+            }
+            if constexpr (CPLX) {
+              Ic = lane_fetch(Ic, dest);
+#pragma unroll
+              for (int a = 0; a < 3; ++a) dIc[a] = lane_fetch(dIc[a], dest);
+            }
+            if constexpr (REAL) {
+#pragma unroll
+              for (int a = 0; a < 3; ++a) dIr[a] = lane_fetch(dIr[a], dest);
+            }
           }
           float acc[8];
 #pragma unroll
@@ -306,9 +347,6 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
           float e3[3] = {0.f, 0.f, 0.f};
           const float fkx = cu.act ? cu.kx : 0.f, fky = cu.act ? cu.ky : 0.f;
           if constexpr (CPLX) {
-            Ic = lane_fetch(Ic, dest);
-#pragma unroll
-            for (int a = 0; a < 3; ++a) dIc[a] = lane_fetch(dIc[a], dest);
             float2 phi = make_float2(1.f, 0.f);
             if (shifts && cu.act) phi = shift_phase(fkx, fky, cu.sx, cu.sy, g.inv_h);
             const float2 cc = cmulc(uc, phi);   // conj(U) * phi
@@ -320,7 +358,7 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
           }
           if constexpr (REAL) {
 #pragma unroll
-            for (int a = 0; a < 3; ++a) e3[a] = fmaf(ur, lane_fetch(dIr[a], dest), e3[a]);
+            for (int a = 0; a < 3; ++a) e3[a] = fmaf(ur, dIr[a], e3[a]);
           }
 #pragma unroll
           for (int a = 0; a < 3; ++a) {

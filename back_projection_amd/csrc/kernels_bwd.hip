@@ -87,8 +87,22 @@ __device__ __forceinline__ void unpack_fixed(unsigned long long w, float& re, fl
   im = (float)i;
 }
 
-__device__ __forceinline__ int padded_index(int idx) {
-  return (idx / (TE * TE)) * TSZ + ((idx / TE) % TE) * TSY + idx % TE;
+// Accumulator tile layout: cubic 16^3 tiles use the bank-split layout of the
+// gather tiles (gather_common.h), each lane adding its pixel's taps in its
+// slot's rotated order (conflict-free for any pixels); other tiles use the
+// padded strides with the lanes ranked by bank key.
+template <int NT>
+struct AccTile {
+  static constexpr bool SPLIT = NT == 4 && TE == 16;
+  static constexpr int SIZE = SPLIT ? TLOG : TSIZE;
+};
+
+// Accumulator address of logical tile entry idx = x + TE (y + TE z).
+template <int NT>
+__device__ __forceinline__ int acc_index(int idx) {
+  const int x = idx % TE, y = (idx / TE) % TE, z = idx / (TE * TE);
+  if constexpr (AccTile<NT>::SPLIT) return split_x(x) + 64 * y + split_z(z);
+  else return z * TSZ + y * TSY + x;
 }
 
 // Bound on the pixels of one pose that can reach one voxel: the voxel's
@@ -273,13 +287,11 @@ __global__ void __launch_bounds__(256) k_band_max(const float2* __restrict__ Y, 
 // each holds one tile in LDS.
 constexpr int CH_DATA = 1, CH_WEIGHTS = 2;
 
-// One pixel, in the lane the bank-spreading permutation gave it: pk packs
-// (active, l) with l = floor(p) - lo; f holds the fractional parts of p; v is
-// c = conj(phi) Y (data) or (Wimg, 0) (weights).  Adds v with the taps'
-// weights to the accumulator tile.
-// With PLANES (cubic data channel, lanes from spread_dest_planes) the z
-// planes are visited in the rotated order that lane's slot asks for.
-template <int NT, int CH, bool PLANES>
+// One pixel, in the lane the bank-spreading permutation gave it (padded
+// tiles): pk packs (active, l) with l = floor(p) - lo; f holds the fractional
+// parts of p; v is c = conj(phi) Y (data) or (Wimg, 0) (weights).  Adds v
+// with the taps' weights to the accumulator tile.
+template <int NT, int CH>
 __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz, float2 v,
                                             unsigned long long* acc_t, unsigned int* acc_w, float scale) {
   if (!(pk & 1)) return;
@@ -288,11 +300,6 @@ __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz
   axis_weights<NT>(fx, wx);
   axis_weights<NT>(fy, wy);
   axis_weights<NT>(fz, wz);
-  int zr = 0;
-  if constexpr (PLANES) {
-    zr = plane_rotation((l[0] + l[1] * TSY + l[2] * TSZ) & 15);
-    rotate4(wz, zr);
-  }
   const float cr = v.x * scale, ci = v.y * scale;
 #pragma unroll
   for (int jc = 0; jc < NT; ++jc)
@@ -300,11 +307,47 @@ __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz
     for (int jb = 0; jb < NT; ++jb) {
       const float wyz = wy[jb] * wz[jc];
       const float ur = wyz * cr, ui = wyz * ci;
-      const int rowb = (l[2] + (PLANES ? ((jc + zr) & 3) : jc)) * TSZ + (l[1] + jb) * TSY + l[0];
+      const int rowb = (l[2] + jc) * TSZ + (l[1] + jb) * TSY + l[0];
 #pragma unroll
       for (int ja = 0; ja < NT; ++ja) {
         if constexpr (CH == CH_DATA) atomicAdd(&acc_t[rowb + ja], fixed_pair(wx[ja], ur, ui));
         else atomicAdd(&acc_w[rowb + ja], (unsigned int)fixed_round(wx[ja], ur));
+      }
+    }
+}
+
+// One cubic pixel into a bank-split accumulator tile, in this lane's own tap
+// order (split_taps): l = floor(p) - lo, f the fractional parts of p, v as
+// above.  The y weights are folded into the value once per row, the x and z
+// weights once per column.
+template <int CH>
+__device__ __forceinline__ void bwd_scatter_split(const int l[3], float fx, float fy, float fz, float2 v,
+                                                  unsigned long long* acc_t, unsigned int* acc_w, float scale) {
+  float wx[4], wy[4], wz[4];
+  axis_weights<4>(fx, wx);
+  axis_weights<4>(fy, wy);
+  axis_weights<4>(fz, wz);
+  SplitTaps st;
+  split_taps(l, st);
+  rotate4(wx, st.t);
+  rotate4(wz, st.r);
+  const float cr = v.x * scale, ci = v.y * scale;
+  float yr[4], yi[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    yr[b] = wy[b] * cr;
+    yi[b] = wy[b] * ci;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const float wxz = wx[a] * wz[c];
+      const int col = st.xo[a] + st.zo[c];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if constexpr (CH == CH_DATA) atomicAdd(&acc_t[col + 64 * b], fixed_pair(wxz, yr[b], yi[b]));
+        else atomicAdd(&acc_w[col + 64 * b], (unsigned int)fixed_round(wxz, yr[b]));
       }
     }
 }
@@ -316,10 +359,11 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
                 BwdGrid bw, const int* __restrict__ prefix, const unsigned short* __restrict__ hits,
                 const int* __restrict__ counts, const float* __restrict__ vmax) {
   constexpr bool DATA = CH == CH_DATA;
-  constexpr bool PLANES = DATA && NT == 4;   // plane rotation for 8-byte cubic taps
+  constexpr bool SPLIT = AccTile<NT>::SPLIT;
+  constexpr int ASIZE = AccTile<NT>::SIZE;
   const BrickGrid& bg = bw.bg;
-  __shared__ unsigned long long acc_t[DATA ? TSIZE : 1];
-  __shared__ unsigned int acc_w[DATA ? 1 : TSIZE];
+  __shared__ unsigned long long acc_t[DATA ? ASIZE : 1];
+  __shared__ unsigned int acc_w[DATA ? 1 : ASIZE];
   __shared__ EnumShared<WINDOW, BNW> es;
   __shared__ float win_scale;
 
@@ -351,7 +395,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
   float2 acc[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) acc[i] = make_float2(0.f, 0.f);
-  for (int i = tid; i < TSIZE; i += BTHREADS) {
+  for (int i = tid; i < ASIZE; i += BTHREADS) {
     if constexpr (DATA) acc_t[i] = 0ull;
     else acc_w[i] = 0u;
   }
@@ -392,7 +436,8 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
           int mpk[U];
           float mf[U][3];
           float2 mv[U];
-          // look up, load, move each pixel to its bank-spreading lane ...
+          // look up and load each pixel (and, for padded tiles, move it to its
+          // bank-spreading lane) ...
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             Cand cu;
@@ -412,17 +457,32 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
               pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
               key = (cu.l[0] + cu.l[1] * TSY + cu.l[2] * TSZ) & 15;
             }
-            const int dest = PLANES ? spread_dest_planes(key) : spread_dest(key);
-            mpk[u] = lane_send(pk, dest);
+            if constexpr (SPLIT) {
+              mpk[u] = pk;
 #pragma unroll
-            for (int a = 0; a < 3; ++a) mf[u][a] = lane_send(f[a], dest);
-            mv[u].x = lane_send(v.x, dest);
-            mv[u].y = DATA ? lane_send(v.y, dest) : 0.f;
+              for (int a = 0; a < 3; ++a) mf[u][a] = f[a];
+              mv[u] = v;
+            } else {
+              const int dest = spread_dest(key);
+              mpk[u] = lane_send(pk, dest);
+#pragma unroll
+              for (int a = 0; a < 3; ++a) mf[u][a] = lane_send(f[a], dest);
+              mv[u].x = lane_send(v.x, dest);
+              mv[u].y = DATA ? lane_send(v.y, dest) : 0.f;
+            }
           }
           // ... then all the taps (nothing waits on these atomics)
 #pragma unroll
-          for (int u = 0; u < U; ++u)
-            bwd_scatter<NT, CH, PLANES>(mpk[u], mf[u][0], mf[u][1], mf[u][2], mv[u], acc_t, acc_w, scale);
+          for (int u = 0; u < U; ++u) {
+            if constexpr (SPLIT) {
+              if (mpk[u] & 1) {
+                const int l[3] = {(mpk[u] >> 1) & 15, (mpk[u] >> 5) & 15, (mpk[u] >> 9) & 15};
+                bwd_scatter_split<CH>(l, mf[u][0], mf[u][1], mf[u][2], mv[u], acc_t, acc_w, scale);
+              }
+            } else {
+              bwd_scatter<NT, CH>(mpk[u], mf[u][0], mf[u][1], mf[u][2], mv[u], acc_t, acc_w, scale);
+            }
+          }
         }
         __syncthreads();
         qb += nr;
@@ -432,7 +492,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
 #pragma unroll
       for (int i = 0; i < PER_LANE; ++i) {
         if (TLOG % BTHREADS != 0 && tid + BTHREADS * i >= TLOG) break;
-        const int pi = padded_index(tid + BTHREADS * i);
+        const int pi = acc_index<NT>(tid + BTHREADS * i);
         if constexpr (DATA) {
           const unsigned long long v = acc_t[pi];
           if (v != 0ull) {

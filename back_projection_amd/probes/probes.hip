@@ -4,8 +4,9 @@
 //   tpp_l2_gather    8-byte reads at hashed indices of a small, cache-resident
 //                    buffer (the tap access pattern without LDS staging)
 //   tpp_lds_taps     4x4x4 tap reads or 64-bit atomics per lane from a 16^3
-//                    tile in LDS with the projection kernels' padded strides
-//                    (1, 17, 276 entries), under controlled bank keys
+//                    tile in LDS with padded strides (1, 17, 276 entries)
+//                    under controlled bank keys, or in the bank-split layout
+//                    with per-lane rotated tap order
 // Each kernel folds what it reads into one float per thread (sink), so that
 // nothing is optimised away.  Argument checks on the host; -1 on bad input,
 // else the HIP status of the launch.
@@ -95,9 +96,18 @@ __device__ __forceinline__ int key_rank(int key) {
   return __popcll(less) + __popcll(eq & below);
 }
 
+// Bank-split layout of a 16^3 tile of 8-byte entries: entry (x, y, z) at
+// (x & 3) + 16 (x >> 2) + 64 y + 4 (z & 3) + 1024 (z >> 2), dense (4096
+// entries), so that its bank pair (address mod 16) is (x & 3) + 4 (z & 3).
+__device__ __forceinline__ int split_x(int x) { return (x & 3) + ((x >> 2) << 4); }
+__device__ __forceinline__ int split_z(int z) { return ((z & 3) << 2) + ((z >> 2) << 10); }
+
 // mode 0: random bases; 1: random bases, lanes permuted by rank of the bank
 // key (rank r to lane (r % 8) * 8 + r / 8); 2: every 16-lane group holds 16
-// distinct keys.  ATOMIC: ds_add_u64 instead of reads.
+// distinct keys; 3: random bases in the bank-split layout, each lane visiting
+// its footprint's x and z taps in the rotated order that puts its accesses in
+// bank pair (lane mod 16) + the step's offset.  ATOMIC: ds_add_u64 instead of
+// reads.
 template <int MODE, bool ATOMIC>
 __global__ void __launch_bounds__(THREADS) k_lds_taps(int iters, float* __restrict__ sink) {
   __shared__ unsigned long long tile[TILE];
@@ -108,6 +118,28 @@ __global__ void __launch_bounds__(THREADS) k_lds_taps(int iters, float* __restri
   for (int it = 0; it < iters; ++it) {
     const unsigned h = mix(blockIdx.x * 7919u + threadIdx.x * 131u + (unsigned)it * 977u);
     int x = (int)(h % 13u), y = (int)((h >> 8) % 13u), z = (int)((h >> 16) % 13u);
+    if constexpr (MODE == 3) {
+      // slot (lane & 3, (lane >> 2) & 3): x taps from rotation t, z taps from r
+      const int t = ((lane & 3) - x) & 3, r = (((lane >> 2) & 3) - z) & 3;
+      int xo[4], zo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xo[j] = split_x(x + ((j + t) & 3));
+        zo[j] = split_z(z + ((j + r) & 3)) + 64 * y;
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          unsigned long long* col = tile + xo[a] + zo[c];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            if constexpr (ATOMIC) atomicAdd(&col[64 * b], (unsigned long long)(it + 1));
+            else acc += col[64 * b];
+          }
+        }
+      continue;
+    }
     if constexpr (MODE == 2) pick_key(h, lane & 15, x, y, z);
     if constexpr (MODE == 1) {
       const int r = key_rank((x + 17 * y + 276 * z) & 15);
@@ -155,17 +187,19 @@ int tpp_l2_gather(const void* buf, int log2_entries, float* sink, int iters, int
 }
 
 int tpp_lds_taps(float* sink, int mode, int atomic, int iters, int blocks, void* stream) {
-  if (!sink || mode < 0 || mode > 2 || iters < 1 || blocks < 1 || blocks > 65535) return -1;
+  if (!sink || mode < 0 || mode > 3 || iters < 1 || blocks < 1 || blocks > 65535) return -1;
   const hipStream_t st = (hipStream_t)stream;
 #define TPP_LDS(M, A) hipLaunchKernelGGL((k_lds_taps<M, A>), dim3(blocks), dim3(THREADS), 0, st, iters, sink)
   if (atomic) {
     if (mode == 0) TPP_LDS(0, true);
     else if (mode == 1) TPP_LDS(1, true);
-    else TPP_LDS(2, true);
+    else if (mode == 2) TPP_LDS(2, true);
+    else TPP_LDS(3, true);
   } else {
     if (mode == 0) TPP_LDS(0, false);
     else if (mode == 1) TPP_LDS(1, false);
-    else TPP_LDS(2, false);
+    else if (mode == 2) TPP_LDS(2, false);
+    else TPP_LDS(3, false);
   }
 #undef TPP_LDS
   return (int)hipGetLastError();

@@ -128,7 +128,7 @@ def measure_peaks(torch):
         out[name] = round(blocks * 256 * iters * 128 / t / 1e9, 1)
     clk = 256 * 2.4e9
     for atomic in (0, 1):
-        for mode, name in ((0, "random"), (1, "rank_permuted"), (2, "conflict_free")):
+        for mode, name in ((0, "random"), (1, "rank_permuted"), (2, "conflict_free"), (3, "bank_split_rotated")):
             iters = 64
             t = timed(lambda: P.tpp_lds_taps(vp(sink.data_ptr()), mode, atomic, iters, blocks, st))
             key = ("lds_atomic_" if atomic else "lds_read_") + name + "_taps_per_clk_cu"
@@ -184,17 +184,38 @@ def time_calls(fn, n, torch):
     return sum(per) / n, per
 
 
-def cpu_baseline(w, sample, eprint):
-    """The oracle, untouched, on the first `sample` poses of the workload."""
+def cpu_baseline(w, sample, eprint, sample_1core=512):
+    """The oracle, untouched, on the first `sample` poses of the workload with
+    all the OpenMP threads it gets, then on the first `sample_1core` poses with
+    one thread."""
     import oracle
     P = min(sample, w.P)
+    threads = oracle.num_threads()
     t0 = time.perf_counter()
     oracle.project(w.vol, w.rot[:, :P], w.shifts[:, :P], interp=w.interp, r=w.radius)
     oracle.project_backward(w.grad_out[:, :P], w.vol, w.rot[:, :P], w.shifts[:, :P], interp=w.interp, r=w.radius)
     dt = time.perf_counter() - t0
-    res = {"value": round(P * w.B / dt, 2), "unit": UNIT, "cores": oracle.num_threads(), "kind": "oracle",
+    P1 = min(sample_1core, w.P)
+    oracle.set_num_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.project(w.vol, w.rot[:, :P1], w.shifts[:, :P1], interp=w.interp, r=w.radius)
+        oracle.project_backward(w.grad_out[:, :P1], w.vol, w.rot[:, :P1], w.shifts[:, :P1], interp=w.interp,
+                                r=w.radius)
+        dt1 = time.perf_counter() - t1
+    finally:
+        oracle.set_num_threads(threads)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
+    res = {"value": round(P * w.B / dt, 2), "unit": UNIT, "cores": threads, "kind": "oracle",
            "sample": f"first {P} of {w.P} poses of the D=128 cubic workload, forward + full backward, "
-                     f"fp64 C oracle with OpenMP ({dt:.1f} s)"}
+                     f"fp64 C oracle with OpenMP over {threads} threads ({dt:.1f} s)",
+           "single_core": {"value": round(P1 * w.B / dt1, 2), "unit": UNIT, "cores": 1,
+                           "sample": f"first {P1} poses, one thread ({dt1:.1f} s)"},
+           "nproc": affinity, "cpu_count": os.cpu_count(),
+           "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
     eprint(f"[bench] cpu baseline: {res}")
     return res
 
@@ -481,9 +502,7 @@ def main():
     st = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    for k in bp.KERNEL_CLASSES:          # drop anything recorded before
-        bp.timing_read(k)
-    bp.timing_enable(True)               # event pairs around every brick kernel of the timed steps
+    # the headline: K steps with no instrumentation inside the timed region
     wall0 = time.perf_counter()
     e0.record(st)
     for _ in range(args.steps):
@@ -491,12 +510,27 @@ def main():
     e1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    bp.timing_enable(False)
     total_ms = e0.elapsed_time(e1)
     ms_per_step = total_ms / args.steps
     value = npose / (ms_per_step * 1e-3)
     eprint(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (event), wall {wall / args.steps * 1e3:.3f} "
            f"ms/step -> {value:.1f} proj/s")
+
+    # a second pass of K steps with the library's event pairs around every
+    # brick kernel (on the stream each kernel is launched on), for the
+    # per-kernel durations in the step
+    for k in bp.KERNEL_CLASSES:          # drop anything recorded before
+        bp.timing_read(k)
+    bp.timing_enable(True)
+    ei0, ei1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ei0.record(st)
+    for _ in range(args.steps):
+        step()
+    ei1.record(st)
+    torch.cuda.synchronize()
+    bp.timing_enable(False)
+    instr_ms = ei0.elapsed_time(ei1) / args.steps
+    eprint(f"[bench] instrumented pass: {instr_ms:.3f} ms/step (per-kernel events on)")
 
     # per-kernel averages over the timed region (library event pairs on the launch stream)
     g = bp.Geom(B=1, P=w.P, Bv=1, Br=1, Bs=1, D=w.D, H=w.H, interp=1, oversampling=1.0, radius_cutoff=r)
@@ -511,7 +545,7 @@ def main():
         kernels[k] = {
             "launches": n,
             "avg_ms": round(ms, 4),
-            "share_of_step": round(tot / total_ms, 4),
+            "share_of_step": round(tot / (instr_ms * args.steps), 4),
             "tap_GBps": round(m["tap_bytes"] / (ms * 1e-3) / 1e9, 1),
             "hbm_GBps": round(m["hbm_bytes"] / (ms * 1e-3) / 1e9, 1),
             "l2_frac": round(m["tap_bytes"] / (ms * 1e-3) / 1e9 / L2_PEAK_GBS, 4),
@@ -566,7 +600,7 @@ def main():
         roofline["alone"] = {"avg_ms": round(isolated[dom], 4), "achieved": round(a_iso, 1),
                              "frac": round(a_iso / L2_PEAK_GBS, 4)}
 
-    details = {"kernels": kernels, "ms_per_step": ms_per_step}
+    details = {"kernels": kernels, "ms_per_step": ms_per_step, "instrumented_ms_per_step": instr_ms}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_sample, eprint)

@@ -35,9 +35,12 @@ int tpp_l2_gather(const void* buf, int log2_entries, float* sink, int iters, int
  * entries (atomic = 0) or adds to them with 64-bit atomics (atomic = 1).
  * mode 0: random footprints; 1: random footprints with the lanes of each
  * wavefront permuted by the bank key of the footprint's first entry (rank r
- * to lane (r % 8) * 8 + r / 8, as the projection kernels do); 2: footprints
- * chosen so that every group of 16 consecutive lanes holds 16 distinct keys
- * (the conflict-free case).                                               */
+ * to lane (r % 8) * 8 + r / 8); 2: footprints chosen so that every group of
+ * 16 consecutive lanes holds 16 distinct keys (the conflict-free case);
+ * 3: random footprints in the bank-split layout (entry (x, y, z) at
+ * (x & 3) + 16 (x >> 2) + 64 y + 4 (z & 3) + 1024 (z >> 2)), each lane
+ * visiting its x and z taps in the rotated order that gives lane l the bank
+ * pair (l mod 16) plus the step's common offset.                          */
 int tpp_lds_taps(float* sink, int mode, int atomic, int iters, int blocks, void* stream);
 
 #ifdef __cplusplus

@@ -66,6 +66,8 @@ def _load():
         lib.oracle_kernel_dweight.argtypes = [_I, _D]
         lib.oracle_kernel_dweight.restype = _D
         lib.oracle_num_threads.restype = _I
+        lib.oracle_set_num_threads.argtypes = [_I]
+        lib.oracle_set_num_threads.restype = _I
         _lib = lib
     return _lib
 
@@ -87,6 +89,11 @@ def _check(rc, name):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """OpenMP threads of later calls (returns the count now in effect)."""
+    return int(_load().oracle_set_num_threads(int(n)))
 
 
 def kernel_weight(interp: int, d: float) -> float:

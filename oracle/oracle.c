@@ -854,3 +854,15 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Set the number of OpenMP threads of later calls (n >= 1; the benchmark
+ * times the oracle on all host cores and on one).  Returns the new count. */
+int oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}
