@@ -402,45 +402,6 @@ __device__ __forceinline__ float2 lane_fetch(float2 v, int src) {
 }
 
 // ---------------------------------------------------------------------------
-// Segmented sums across a wavefront whose lanes carry sorted keys (the hit of
-// the candidate; EB_SENTINEL past the end): after seg_scan, each lane holds
-// the sum of its key's values from the key's first lane up to itself.  DPP
-// row shifts, then the row broadcasts of lanes 15 and 31.
-// ---------------------------------------------------------------------------
-template <int CTRL, int RM, int N>
-__device__ __forceinline__ void seg_step(float (&v)[N], int key) {
-  const int ks = dpp_int<CTRL, RM>(-1, key);
-  const float m = ks == key ? 1.0f : 0.0f;
-  if constexpr (RM == 0xf) {
-    // every lane is written (lanes without a source read 0), so the moved
-    // value needs no old value and can fuse into the multiply-add
-#pragma unroll
-    for (int q = 0; q < N; ++q)
-      v[q] = fmaf(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[q]), CTRL, RM, 0xf, true)), m, v[q]);
-  } else {
-#pragma unroll
-    for (int q = 0; q < N; ++q) v[q] = fmaf(m, __int_as_float(dpp_int<CTRL, RM>(0, __float_as_int(v[q]))), v[q]);
-  }
-}
-
-template <int N>
-__device__ __forceinline__ void seg_scan(float (&v)[N], int key) {
-  seg_step<0x111, 0xf>(v, key);   // row_shr:1
-  seg_step<0x112, 0xf>(v, key);   // row_shr:2
-  seg_step<0x114, 0xf>(v, key);   // row_shr:4
-  seg_step<0x118, 0xf>(v, key);   // row_shr:8
-  seg_step<0x142, 0xa>(v, key);   // row_bcast:15 into rows 1 and 3
-  seg_step<0x143, 0xc>(v, key);   // row_bcast:31 into rows 2 and 3
-}
-
-// Is this lane the last of its key's run?
-__device__ __forceinline__ bool seg_tail(int key) {
-  const int lane = threadIdx.x & 63;
-  const int next = __shfl_down(key, 1, 64);
-  return key != EB_SENTINEL && (lane == 63 || next != key);
-}
-
-// ---------------------------------------------------------------------------
 // Per-hit rotation / shift gradient sums: a segmented sum over the lanes of
 // one hit leaves the hit's partial in its last lane, which adds it to the
 // hit's sum in LDS (an atomic add whose result is not waited for).  At the
@@ -465,35 +426,59 @@ __device__ __forceinline__ void grad_flush(const KGeom& g, const EnumShared<WIN,
   }
 }
 
-// Per-lane terms -> per-hit sums (all 64 lanes of the wavefront call this).
-// Keys rise along the lanes (candidates are ordered by hit), so a wavefront
-// whose first and last lanes share a key holds one key only: its sums are a
-// plain wavefront sum (one DPP add per term and step, no key masks), left in
-// lane 63.
-__device__ __forceinline__ void grad_collect(float (&acc)[8], int key, float (*gw)[8]) {
-  const int k0 = __builtin_amdgcn_readfirstlane(key);
-  if (k0 != EB_SENTINEL && k0 == __builtin_amdgcn_readlane(key, 63)) {
+// Per-lane terms -> per-hit sums (all 64 lanes of the wavefront call this),
+// added to gw[key][term] in LDS.  Keys rise along the lanes (candidates are
+// ordered by hit; idle lanes hold EB_SENTINEL), so the wavefront holds one or
+// a few runs of keys; each run is summed by a butterfly reduce-scatter with
+// the other keys' terms masked out: in three steps a lane keeps half of its
+// terms and adds its partner's share of them (lanes 1, 2 and 4 apart), after
+// which lane i holds term 4 b0 + 2 b1 + b2 (b_j: bit j of i) summed over 8
+// lanes; a step 8 lanes apart completes the row of 16, and two row swaps the
+// wavefront.  Lanes 0-7 then add the 8 totals to LDS.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float wave_term_sum(const float (&t)[8]) {
+  const int lane = threadIdx.x & 63;
+  const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4;
+  float u[4], v[2];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      float v = acc[q];
-      v += __int_as_float(dpp_int<0x111, 0xf>(0, __float_as_int(v)));   // row_shr:1
-      v += __int_as_float(dpp_int<0x112, 0xf>(0, __float_as_int(v)));   // row_shr:2
-      v += __int_as_float(dpp_int<0x114, 0xf>(0, __float_as_int(v)));   // row_shr:4
-      v += __int_as_float(dpp_int<0x118, 0xf>(0, __float_as_int(v)));   // row_shr:8
-      v += __int_as_float(dpp_int<0x142, 0xa>(0, __float_as_int(v)));   // row_bcast:15
-      v += __int_as_float(dpp_int<0x143, 0xc>(0, __float_as_int(v)));   // row_bcast:31
-      acc[q] = v;
-    }
-    if ((threadIdx.x & 63) == 63) {
+  for (int j = 0; j < 4; ++j)   // partner lane ^ 1 (quad_perm 1,0,3,2)
+    u[j] = (b0 ? t[j + 4] : t[j]) + dpp_f<0xB1>(b0 ? t[j] : t[j + 4]);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) atomicAdd(&gw[k0][q], acc[q]);
-    }
+  for (int j = 0; j < 2; ++j)   // partner lane ^ 2 (quad_perm 2,3,0,1)
+    v[j] = (b1 ? u[j + 2] : u[j]) + dpp_f<0x4E>(b1 ? u[j] : u[j + 2]);
+  // partner 4 lanes away in the row (row_ror:4): opposite bit 2, same bits 0-1
+  float w = (b2 ? v[1] : v[0]) + dpp_f<0x124>(b2 ? v[0] : v[1]);
+  w += dpp_f<0x128>(w);         // 8 lanes away (row_ror:8): the same term
+  // rows 0 + 1 and 2 + 3, then the two halves
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(w), __float_as_uint(w), false, false);
+  w = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(w), __float_as_uint(w), false, false);
+  return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
+
+__device__ __forceinline__ void grad_collect(const float (&acc)[8], int key, float (*gw)[8]) {
+  const int lane = threadIdx.x & 63;
+  const int term = ((lane & 1) << 2) | (lane & 2) | ((lane >> 2) & 1);
+  int k = __builtin_amdgcn_readfirstlane(key);
+  if (k == EB_SENTINEL) return;
+  if (k == __builtin_amdgcn_readlane(key, 63)) {   // one key: no masks
+    const float s = wave_term_sum(acc);
+    if (lane < 8) atomicAdd(&gw[k][term], s);
     return;
   }
-  seg_scan(acc, key);
-  if (seg_tail(key)) {
+  for (;;) {   // wave-uniform loop over the runs of keys
+    float t[8];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) atomicAdd(&gw[key][q], acc[q]);
+    for (int q = 0; q < 8; ++q) t[q] = key == k ? acc[q] : 0.f;
+    const float s = wave_term_sum(t);
+    if (lane < 8) atomicAdd(&gw[k][term], s);
+    const unsigned long long later = __ballot(key > k && key != EB_SENTINEL);
+    if (later == 0ull) break;
+    k = __builtin_amdgcn_readlane(key, __builtin_ctzll(later));
   }
 }
 
