@@ -1,19 +1,18 @@
 // Block-wide enumeration of the pixels whose slice sample falls in one brick,
 // shared by the brick kernels (forward gather, gradients, back-projection).
 //
-// A workgroup of NW wavefronts walks its brick's pose list in passes of one
-// pose per thread.  Each pass:
-//   1. every thread tests its pose against the brick; the hits are kept as a
-//      bit mask;
-//   2. the hits are taken in windows of up to WIN; one thread per hit sets up
+// A separate pass (k_hit_lists / k_bwd_hit_lists) has already listed, per
+// work item (a brick and a chunk of its poses), the poses whose slice reaches
+// the brick.  A workgroup of NW wavefronts walks that list:
+//   1. the hits are taken in windows of up to WIN; one thread per hit sets up
 //      the hit's geometry in LDS and bounds its image rows (ky);
-//   3. the rows of the window are laid out one after the other and handled
+//   2. the rows of the window are laid out one after the other and handled
 //      one per thread: each thread derives the kx interval of its row from
 //      the slab inequalities of the brick, a block-wide scan turns the
 //      interval lengths into candidate offsets, and each row writes its index
 //      into a per-candidate table (a stage takes rows while their candidates
 //      fit the table);
-//   4. the candidates (kx, ky, hit) are dealt to the wavefronts in chunks of
+//   3. the candidates (kx, ky, hit) are dealt to the wavefronts in chunks of
 //      64, so the lanes stay full across row and hit boundaries; a lane finds
 //      its row with one table read.
 // The enumeration is a superset of the owned pixels (margins on the
@@ -411,6 +410,7 @@ __device__ __forceinline__ float2 lane_fetch(float2 v, int src) {
 template <int WIN, int NW>
 __device__ __forceinline__ void grad_flush(const KGeom& g, const EnumShared<WIN, NW>& es, float (*gw)[8], int nw,
                                            float* __restrict__ grad_rot, float* __restrict__ grad_s) {
+  static_assert(WIN * 8 <= NW * 64, "one thread per hit and term");
   const int tid = threadIdx.x;
   if (tid < nw * 8) {
     const int h = tid >> 3, q = tid & 7;

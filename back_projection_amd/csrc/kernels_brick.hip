@@ -9,12 +9,15 @@
 //                  one tap-space brick of the Hermitian-extended periodic
 //                  volume plus the interpolation halo in LDS, enumerates the
 //                  pixels of its hit poses whose floor(p) falls in the brick
-//                  (enum_block.h) and interpolates them from LDS, each pixel
-//                  in the lane the bank-spreading order gives it.
+//                  (enum_block.h) and interpolates them from LDS (cubic: a
+//                  bank-split tile read in a per-lane rotated tap order;
+//                  linear: a padded tile, each pixel in the lane a
+//                  bank-spreading order gives it).
 // k_grad_brick     rotation / shift gradients on the same decomposition: the
 //                  value and the three partial derivatives of the
-//                  interpolant come from the LDS tile; segmented wavefront
-//                  sums per pose, then one global atomic per pose and term.
+//                  interpolant come from the LDS tile; per-pose wavefront
+//                  sums by a butterfly reduce-scatter, per-window sums in
+//                  LDS, then one global atomic per pose and term.
 // *_edge           masked pixels and the rare samples outside every active
 //                  brick (maps that are not rotations), from global memory.
 //
@@ -86,7 +89,10 @@ __global__ void __launch_bounds__(256) k_hit_lists(const float* __restrict__ rot
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-constexpr int FWD_WIN = 32;
+// hits per window: 64 with the cubic tile (about 3% faster than 32 at D=128);
+// 32 with the larger padded linear tile, so that four workgroups fit a CU's LDS
+template <int NT>
+constexpr int FWD_WIN = NT == 4 ? 64 : 32;
 constexpr int FWD_NW = 4;   // wavefronts per workgroup
 
 template <int NT, typename T>
@@ -98,7 +104,7 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
   using Tl = Tile<NT>;
   constexpr bool CPLX = sizeof(T) == 8;
   __shared__ T tile[Tl::SIZE];
-  __shared__ EnumShared<FWD_WIN, FWD_NW> es;
+  __shared__ EnumShared<FWD_WIN<NT>, FWD_NW> es;
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
   const int nh = counts[(int64_t)vsel * bg.nwork + w];
@@ -117,8 +123,8 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   {
-    for (int hw = 0; hw < nh; hw += FWD_WIN) {
-      const int nw = min(FWD_WIN, nh - hw);
+    for (int hw = 0; hw < nh; hw += FWD_WIN<NT>) {
+      const int nw = min(FWD_WIN<NT>, nh - hw);
       window_setup(es, g, rot, CPLX ? shifts : nullptr, vsel, e0, hl + hw, nw, bl, bh);
       const int nrows = es.hrow[nw];
       for (int qb = 0; qb < nrows;) {
@@ -233,7 +239,10 @@ __global__ void __launch_bounds__(256) k_fwd_edge(const T* __restrict__ vol, con
 // window the four wavefronts' sums go to the pose's gradient with global
 // atomics.
 // ---------------------------------------------------------------------------
-constexpr int GRAD_WIN = 16;   // hits per window (with 16, the LDS and the registers allow four workgroups per CU)
+// hits per window: 32 with the cubic tile, 16 with the larger padded linear
+// one (four workgroups per CU fit the LDS either way)
+template <int NT>
+constexpr int GRAD_WIN = NT == 4 ? 32 : 16;
 constexpr int GRAD_NW = 4;
 
 template <int NT, bool CPLX, bool REAL>
@@ -247,8 +256,9 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
   using Tl = Tile<NT>;
   __shared__ float2 tc[CPLX ? Tl::SIZE : 1];
   __shared__ float tr[REAL ? Tl::SIZE : 1];
-  __shared__ EnumShared<GRAD_WIN, GRAD_NW> es;
-  __shared__ float gw[GRAD_WIN][8];
+  constexpr int WIN = GRAD_WIN<NT>;
+  __shared__ EnumShared<WIN, GRAD_NW> es;
+  __shared__ float gw[WIN][8];
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
   const int nh = counts[(int64_t)vsel * bg.nwork + w];
@@ -265,13 +275,13 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
   const int64_t nvol = (int64_t)g.D * g.D * g.W;
   if constexpr (CPLX) stage_tile_t<NT, GRAD_NW * 64>(tc, volc + (int64_t)vsel * nvol, g, lo);
   if constexpr (REAL) stage_tile_t<NT, GRAD_NW * 64>(tr, volr + (int64_t)vsel * nvol, g, lo);
-  for (int i = threadIdx.x; i < GRAD_WIN * 8; i += GRAD_NW * 64) (&gw[0][0])[i] = 0.f;
+  for (int i = threadIdx.x; i < WIN * 8; i += GRAD_NW * 64) (&gw[0][0])[i] = 0.f;
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   {
-    for (int hw = 0; hw < nh; hw += GRAD_WIN) {
-      const int nw = min(GRAD_WIN, nh - hw);
+    for (int hw = 0; hw < nh; hw += WIN) {
+      const int nw = min(WIN, nh - hw);
       window_setup(es, g, rot, CPLX ? shifts : nullptr, vsel, e0, hl + hw, nw, bl, bh);
       const int nrows = es.hrow[nw];
       for (int qb = 0; qb < nrows;) {
@@ -370,7 +380,7 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
         __syncthreads();
         qb += nr;
       }
-      grad_flush<GRAD_WIN>(g, es, gw, nw, grad_rot, CPLX ? grad_s : nullptr);
+      grad_flush<WIN>(g, es, gw, nw, grad_rot, CPLX ? grad_s : nullptr);
       __syncthreads();
     }
   }

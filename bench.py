@@ -34,7 +34,36 @@ UNIT = "projections/s"
 HBM_PEAK_GBS = 8000.0
 L2_PEAK_GBS = 8 * 16 * 128 * 2.4          # = 39321.6 GB/s
 LDS_PEAK_GBS = 256 * 128 * 2.4            # 256 CUs x 128 B/clk x 2.4 GHz = 78643.2 GB/s
-FP32_VECTOR_TFLOPS = 157.3
+FP32_VECTOR_TFLOPS = 157.3                # published; counts packed (two-wide) FP32 FMA
+# The kernels are built without packed FP32 instructions, so their FP32 ceiling
+# is one FMA per lane per clock: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz.
+FP32_FMA_TFLOPS = 256 * 4 * 16 * 2 * 2.4 / 1000.0   # = 78.64
+
+# Algorithmic fp32 flops per in-mask pixel of the separable tricubic
+# interpolation each kernel class performs (2 flops per multiply-add; the
+# contraction only, not the weights, coordinates or enumeration):
+#   forward   value: 64 taps x 2 (complex x weight) + 16 x 2 + 4 x 2 = 168 FMA
+#   gradient  value and three derivatives: 64 x 4 + 16 x 6 + 4 x 8 = 384 FMA
+#   backward  scatter: 64 taps x 2 (weight x complex, the fixed-point
+#             rounding multiply-add) + 16 column weights + 8 row factors = 152
+FLOPS_PER_PIXEL_CUBIC = {"forward": 2 * 168, "gradient": 2 * 384, "backward": 2 * 152, "fold": 0}
+# the same for the real weight channel (one multiply-add where the complex
+# channel has two): forward 64 + 16 + 4, gradient 64 x 2 + 16 x 3 + 4 x 4,
+# scatter 64 + 16 + 8
+FLOPS_PER_PIXEL_CUBIC_REAL = {"forward": 2 * 84, "gradient": 2 * 192, "backward": 2 * 88}
+
+
+def op_rates(ms, poses, n_in, tap_bytes_per_pixel, flops_per_pixel):
+    """ms, proj/s, tap-delivery rate and fraction of the L2 figure, and (when
+    a flop model is given) TFLOP/s and fraction of the fp32 FMA ceiling."""
+    sec = ms * 1e-3
+    r = {"ms": round(ms, 4), "proj_per_s": round(poses / sec, 1),
+         "tap_GBps": round(poses * n_in * tap_bytes_per_pixel / sec / 1e9, 1),
+         "l2_frac": round(poses * n_in * tap_bytes_per_pixel / sec / 1e9 / L2_PEAK_GBS, 4)}
+    if flops_per_pixel:
+        r["tflops"] = round(poses * n_in * flops_per_pixel / sec / 1e12, 2)
+        r["alu_frac"] = round(r["tflops"] / FP32_FMA_TFLOPS, 4)
+    return r
 
 
 # HBM traffic per launch of a kernel class, from two rocprofv3 PMC runs of this
@@ -44,14 +73,14 @@ FP32_VECTOR_TFLOPS = 157.3
 # reported when the digest of the 3D kernel sources matches, else null.
 TRAFFIC = {
     # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
-    "forward": {"sources_sha256": "76bf783eef7663ab042a9756cf04b7e02726406855a84dc4286e10df6c551925",
-               "fetch_bytes": 317611481, "write_bytes": 1183370645},
-    "backward": {"sources_sha256": "76bf783eef7663ab042a9756cf04b7e02726406855a84dc4286e10df6c551925",
-                "fetch_bytes": 2826245213, "write_bytes": 188940288},
-    "gradient": {"sources_sha256": "76bf783eef7663ab042a9756cf04b7e02726406855a84dc4286e10df6c551925",
-                "fetch_bytes": 2785186605, "write_bytes": 120424608},
-    "fold": {"sources_sha256": "76bf783eef7663ab042a9756cf04b7e02726406855a84dc4286e10df6c551925",
-            "fetch_bytes": 292601386, "write_bytes": 8519680},
+    "forward": {"sources_sha256": "b074b049d537aceb8c0b03659a35565774b70401840a823590693dfaf156da0b",
+               "fetch_bytes": 313602450, "write_bytes": 1183400845},
+    "backward": {"sources_sha256": "b074b049d537aceb8c0b03659a35565774b70401840a823590693dfaf156da0b",
+                "fetch_bytes": 2901277100, "write_bytes": 271601650},
+    "gradient": {"sources_sha256": "b074b049d537aceb8c0b03659a35565774b70401840a823590693dfaf156da0b",
+                "fetch_bytes": 2784170085, "write_bytes": 120424608},
+    "fold": {"sources_sha256": "b074b049d537aceb8c0b03659a35565774b70401840a823590693dfaf156da0b",
+            "fetch_bytes": 292597288, "write_bytes": 8519680},
 }
 
 
@@ -166,8 +195,9 @@ def kernel_model(w, kclass, ws_bytes=0):
            "backward": img + vol + params,
            "gradient": img + vol + params + npose * 11 * 4,
            "fold": ws_bytes + vol}[kclass]
+    flops_px = FLOPS_PER_PIXEL_CUBIC[kclass] if w.interp == 1 else 0
     return {"tap_bytes": npose * n_in * per_px, "tap_bytes_per_pixel": per_px, "hbm_bytes": hbm, "n_in": n_in,
-            "poses": npose, "taps": T}
+            "poses": npose, "taps": T, "flops": npose * n_in * flops_px, "flops_per_pixel": flops_px}
 
 
 def time_calls(fn, n, torch):
@@ -236,11 +266,10 @@ def run_workload_ops(cfg, steps, warmup, bp, workloads, torch, details):
         for _ in range(warmup):
             fn()
         ms, _ = time_calls(fn, steps, torch)
-        res["backproject_ms"] = ms
-        res["backproject_proj_per_s"] = w.P / (ms * 1e-3)
         n_in = in_mask_pixels(w.H, w.radius)
-        res["tap_bytes"] = w.P * n_in * 64 * 12
-        res["l2_frac"] = res["tap_bytes"] / (ms * 1e-3) / (L2_PEAK_GBS * 1e9)
+        F, FR = FLOPS_PER_PIXEL_CUBIC, FLOPS_PER_PIXEL_CUBIC_REAL
+        # taps: 8 B complex + 4 B real accumulated per tap
+        res["backproject"] = op_rates(ms, w.P, n_in, 64 * 12, F["backward"] + FR["backward"])
         # its backward (grad images, grad weights, grad rotations) for random
         # upstream volume gradients
         import numpy as np
@@ -251,12 +280,10 @@ def run_workload_ops(cfg, steps, warmup, bp, workloads, torch, details):
         for _ in range(warmup):
             fb()
         ms_b, _ = time_calls(fb, steps, torch)
-        res["backproject_backward_ms"] = ms_b
-        res["backproject_backward_proj_per_s"] = w.P / (ms_b * 1e-3)
         # gathers: grad images (8 B taps) and grad weights (4 B), then the
         # rotation gradient over both channels (12 B)
-        res["backward_tap_bytes"] = w.P * n_in * 64 * 24
-        res["backward_l2_frac"] = res["backward_tap_bytes"] / (ms_b * 1e-3) / (L2_PEAK_GBS * 1e9)
+        res["backproject_backward"] = op_rates(ms_b, w.P, n_in, 64 * 24,
+                                               F["forward"] + FR["forward"] + F["gradient"] + FR["gradient"])
     else:
         tv = torch.from_numpy(w.vol).to(dev)
         tr = torch.from_numpy(w.rot).to(dev)
@@ -267,10 +294,10 @@ def run_workload_ops(cfg, steps, warmup, bp, workloads, torch, details):
         for _ in range(warmup):
             f()
         ms, _ = time_calls(f, steps, torch)
-        m = kernel_model(w, "forward")
-        res["forward_ms"] = ms
-        res["forward_proj_per_s"] = npose / (ms * 1e-3)
-        res["forward_l2_frac"] = m["tap_bytes"] / (ms * 1e-3) / (L2_PEAK_GBS * 1e9)
+        n_in = in_mask_pixels(w.H, w.radius)
+        T = 64 if w.interp == 1 else 8
+        F = FLOPS_PER_PIXEL_CUBIC if w.interp == 1 else {}
+        res["forward"] = op_rates(ms, npose, n_in, T * 8, F.get("forward"))
         if w.grad_out is not None:
             tg = torch.from_numpy(w.grad_out).to(dev)
             need_s = "backward_shifts" in w.ops
@@ -282,8 +309,10 @@ def run_workload_ops(cfg, steps, warmup, bp, workloads, torch, details):
             for _ in range(warmup):
                 b()
             ms_b, _ = time_calls(b, steps, torch)
-            res["backward_ms"] = ms_b
-            res["fwd_bwd_proj_per_s"] = npose / ((ms + ms_b) * 1e-3)
+            # scatter (taps accumulated) and gradient (taps gathered)
+            fb = (F["backward"] + F["gradient"]) if F else None
+            res["backward"] = op_rates(ms_b, npose, n_in, 2 * T * 8, fb)
+            res["forward_backward"] = op_rates(ms + ms_b, npose, n_in, 3 * T * 8, (F["forward"] + fb) if F else None)
     eprint(f"[bench] workload {cfg}: {json.dumps(res)}")
     details.setdefault("workloads", {})[str(cfg)] = res
 
@@ -436,7 +465,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-sample", type=int, default=16384, help="poses of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--all-workloads", action="store_true", help="also time the other four workloads (stderr)")
+    ap.add_argument("--all-workloads", action="store_true", help="also time every workload per operation (stderr)")
     ap.add_argument("--sweep", action="store_true", help="also time the 3D ops over box size, poses and kernel (stderr)")
     ap.add_argument("--oversampling", action="store_true",
                     help="also run the interpolation vs oversampling accuracy study and timing (stderr)")
@@ -548,9 +577,11 @@ def main():
             "share_of_step": round(tot / (instr_ms * args.steps), 4),
             "tap_GBps": round(m["tap_bytes"] / (ms * 1e-3) / 1e9, 1),
             "hbm_GBps": round(m["hbm_bytes"] / (ms * 1e-3) / 1e9, 1),
+            "tflops": round(m["flops"] / (ms * 1e-3) / 1e12, 2),
             "l2_frac": round(m["tap_bytes"] / (ms * 1e-3) / 1e9 / L2_PEAK_GBS, 4),
             "lds_frac": round(m["tap_bytes"] / (ms * 1e-3) / 1e9 / LDS_PEAK_GBS, 4),
             "hbm_frac": round(m["hbm_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "alu_frac": round(m["flops"] / (ms * 1e-3) / 1e12 / FP32_FMA_TFLOPS, 4),
             **m,
         }
         eprint(f"[bench] kernel {k}: {kernels[k]}")
@@ -577,28 +608,47 @@ def main():
         if n:
             isolated[k] = tot / n
             eprint(f"[bench] kernel {k} alone: {tot / n:.4f} ms")
+    # The dominant kernel (largest live time in the step) is the gradient
+    # kernel, whose limit is fp32 VALU issue (SQ counters: VALU instructions
+    # and busy cycles, profiles/); its roofline is the fp32 FMA rate.  The
+    # tap-bandwidth figure of the L2 roofline and the LDS and HBM fractions go
+    # beside it, and the forward kernel's figures with them.
     dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
     kd = kernels[dom]
-    achieved = kd["tap_bytes"] / (kd["avg_ms"] * 1e-3) / 1e9
+    achieved = kd["flops"] / (kd["avg_ms"] * 1e-3) / 1e12
+    tap_gbps = kd["tap_bytes"] / (kd["avg_ms"] * 1e-3) / 1e9
     traffic = measured_traffic(dom)
     roofline = {
-        "bound": "l2",
-        "achieved": round(achieved, 1),
-        "peak": round(L2_PEAK_GBS, 1),
-        "unit": "GB/s",
-        "frac": round(achieved / L2_PEAK_GBS, 4),
+        "bound": "alu",
+        "achieved": round(achieved, 2),
+        "peak": round(FP32_FMA_TFLOPS, 2),
+        "unit": "TFLOP/s",
+        "frac": round(achieved / FP32_FMA_TFLOPS, 4),
         "traffic": traffic,
         "kernel": dom,
-        "hbm": {"achieved": round(kd["hbm_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["hbm_frac"]},
-        "lds": {"achieved": round(achieved, 1), "peak": round(LDS_PEAK_GBS, 1), "unit": "GB/s",
+        "flops_per_launch": kd["flops"],
+        "flops_per_pixel": kd["flops_per_pixel"],
+        "peak_note": ("fp32 FMA issue without packed math (256 CUs x 4 SIMD16 x 2 flop x 2.4 GHz); the published "
+                      f"{FP32_VECTOR_TFLOPS} TFLOP/s counts packed FMA, which these kernels do not use"),
+        "l2_tap": {"achieved": round(tap_gbps, 1), "peak": round(L2_PEAK_GBS, 1), "unit": "GB/s",
+                   "frac": kd["l2_frac"]},
+        "lds": {"achieved": round(tap_gbps, 1), "peak": round(LDS_PEAK_GBS, 1), "unit": "GB/s",
                 "frac": kd["lds_frac"]},
+        "hbm": {"achieved": round(kd["hbm_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["hbm_frac"]},
     }
     if dom in isolated:
-        a_iso = kd["tap_bytes"] / (isolated[dom] * 1e-3) / 1e9
+        iso = isolated[dom]
         roofline["overlap"] = ("runs beside the other backward kernel on a second stream; achieved uses "
                                "its live duration in the step")
-        roofline["alone"] = {"avg_ms": round(isolated[dom], 4), "achieved": round(a_iso, 1),
-                             "frac": round(a_iso / L2_PEAK_GBS, 4)}
+        roofline["alone"] = {"avg_ms": round(iso, 4),
+                             "achieved": round(kd["flops"] / (iso * 1e-3) / 1e12, 2),
+                             "frac": round(kd["flops"] / (iso * 1e-3) / 1e12 / FP32_FMA_TFLOPS, 4),
+                             "l2_tap_frac": round(kd["tap_bytes"] / (iso * 1e-3) / 1e9 / L2_PEAK_GBS, 4)}
+    if "forward" in kernels and dom != "forward":
+        kf = kernels["forward"]
+        roofline["forward"] = {"avg_ms": kf["avg_ms"], "tflops": kf["tflops"], "alu_frac": kf["alu_frac"],
+                               "l2_tap_frac": kf["l2_frac"], "lds_frac": kf["lds_frac"],
+                               "traffic": measured_traffic("forward")}
 
     details = {"kernels": kernels, "ms_per_step": ms_per_step, "instrumented_ms_per_step": instr_ms}
     cpu = None
@@ -607,7 +657,7 @@ def main():
     if args.all_workloads:
         del tg, out
         torch.cuda.empty_cache()
-        for cfg in (1, 2, 4, 5):
+        for cfg in (1, 2, 3, 4, 5):
             run_workload_ops(cfg, max(3, args.steps // 2), 1, bp, workloads, torch, details)
     if args.sweep:
         torch.cuda.empty_cache()
