@@ -36,8 +36,8 @@ __all__ = [
     "project_3d_to_2d", "project_3d_to_2d_backward", "backproject_2d_to_3d", "backproject_2d_to_3d_backward",
     "project_2d_to_2d", "project_2d_to_2d_backward", "backproject_2d_to_2d", "backproject_2d_to_2d_backward",
     "project_3d_to_2d_noalloc", "NOALLOC_SCRATCH_BYTES", "volume_rfft", "images_irfft", "weight_images", "finish_reconstruction",
-    "TprojError", "lib", "Geom", "LIB_PATH", "HEADER_SYMBOLS", "SPECTRAL_SYMBOLS", "timing_enable", "timing_read",
-    "KERNEL_CLASSES",
+    "TprojError", "lib", "Geom", "LIB_PATH", "HEADER_SYMBOLS", "SPECTRAL_SYMBOLS", "BOUNDS_SYMBOLS", "timing_enable",
+    "timing_read", "KERNEL_CLASSES",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +54,9 @@ HEADER_SYMBOLS = (
 # TP_NOALLOC_SCRATCH_BYTES of include/tproj.h: the static work area of
 # project_3d_to_2d_noalloc (per GPU).
 NOALLOC_SCRATCH_BYTES = 32 << 20
+
+# Every symbol that include/tproj_bounds.h declares.
+BOUNDS_SYMBOLS = ("tp_weight_sum_bound_3d", "tp_contrib_bound_3d", "tp_weight_sum_bound_2d", "tp_bounds_device")
 
 # Every symbol that include/tproj_spectral.h declares.
 SPECTRAL_SYMBOLS = (
@@ -126,6 +129,14 @@ def lib():
         L.tp_finish_reconstruction.argtypes = [ctypes.c_int64, _vp, _vp, ctypes.c_float, _vp, _vp]
         for f in ("tp_volume_rfft", "tp_images_irfft", "tp_weight_images", "tp_finish_reconstruction"):
             getattr(L, f).restype = ctypes.c_int
+        for f in ("tp_weight_sum_bound_3d", "tp_contrib_bound_3d"):
+            getattr(L, f).argtypes = [ctypes.c_int, ctypes.c_float, _vp]
+            getattr(L, f).restype = ctypes.c_float
+        L.tp_weight_sum_bound_2d.argtypes = [ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_int, _vp]
+        L.tp_weight_sum_bound_2d.restype = ctypes.c_float
+        L.tp_bounds_device.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_int, _vp,
+                                       ctypes.c_int64, _vp]
+        L.tp_bounds_device.restype = ctypes.c_int
         _lib = L
     return _lib
 

@@ -30,6 +30,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
+#include "fixed_point_bound.h"
 #include "gather_common.h"
 #include "kernels_2d.h"
 
@@ -329,29 +330,11 @@ __global__ void __launch_bounds__(256) k2_img_max(const float2* __restrict__ Y, 
 }
 
 // Bound on the sum of |weights| that one entry of E receives from all pixels
-// of one pose: over each unit cell of the (d_x, d_y) plane the kernel product
-// is at most CELLS, and the cell holds at most (floor(w1) + 1)(floor(w2) + 1)
-// pixels of the lattice A Z^2 (A = o R), w_r the sum of |row r of A^-1|.  E
-// is periodic, so an entry also collects the taps of its translates by D:
-// the samples lie within |p| <= kmax sigma_max(A), the taps within NT of
-// them, so at most n = floor(2 (kmax sigma_max + NT) / D) + 1 translates per
-// axis can be reached; the bound is multiplied by n^2.  Degenerate maps get
-// infinity (they take the direct kernel).
+// of one pose, its periodic translates included (fixed_point_bound.h).
+// Degenerate maps get infinity (they take the direct kernel).
 template <int NT>
 __device__ __forceinline__ float weight_sum_bound2(const KGeom& g, const float* R) {
-  constexpr float CELLS = NT == 4 ? 4.6152f : 4.0f;
-  const float a00 = g.o * R[0], a01 = g.o * R[1], a10 = g.o * R[2], a11 = g.o * R[3];
-  const float d = fabsf(a00 * a11 - a01 * a10);
-  if (!(d > 1e-6f * (fabsf(a00) + fabsf(a01)) * (fabsf(a10) + fabsf(a11)))) return __builtin_huge_valf();
-  const float rd = __builtin_amdgcn_rcpf(d);
-  const float w1 = (fabsf(a11) + fabsf(a01)) * rd * 1.0001f + 1e-4f;
-  const float w2 = (fabsf(a10) + fabsf(a00)) * rd * 1.0001f + 1e-4f;
-  // largest singular value of A (columns (a00, a10), (a01, a11))
-  const float g00 = fmaf(a00, a00, a10 * a10), g11 = fmaf(a01, a01, a11 * a11), g01 = fmaf(a00, a01, a10 * a11);
-  const float dd = g00 - g11;
-  const float smax = sqrtf(0.5f * (g00 + g11 + sqrtf(fmaf(dd, dd, 4.f * g01 * g01)))) * 1.0001f;
-  const float nt = floorf(2.0f * (g.kmax * smax + (float)NT) / (float)g.D) + 1.0f;
-  return CELLS * (floorf(w1) + 1.0f) * (floorf(w2) + 1.0f) * nt * nt;
+  return weight_sum_bound_2d<NT>(g.o, g.kmax, g.D, R);
 }
 
 __device__ __forceinline__ bool pose2_ok(float c) { return c <= 4096.0f; }

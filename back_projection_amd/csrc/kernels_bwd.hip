@@ -27,6 +27,7 @@
 #include "bwd_kernels.h"
 #include "device_common.h"
 #include "enum_block.h"
+#include "fixed_point_bound.h"
 #include "gather_common.h"
 
 namespace tproj {
@@ -105,57 +106,16 @@ __device__ __forceinline__ int acc_index(int idx) {
   else return z * TSZ + y * TSY + x;
 }
 
-// Bound on the pixels of one pose that can reach one voxel: the voxel's
-// support box (edge NT) cuts the slice in a disc of radius NT*sqrt(3)/2 in
-// sample space, i.e. an ellipse in pixel space whose semi-axes are that radius
-// over the singular values of A = o [R_:0 R_:1]; (2a+1)^2 bounds its pixels.
+// The bounds behind the window scales (fixed_point_bound.h): the pixels of
+// one pose that can reach a voxel (contrib_bound3) and the sum of |weights|
+// a voxel receives from one pose (weight_sum_bound3).
 template <int NT>
 __device__ __forceinline__ float contrib_bound(const KGeom& g, const float* R) {
-  float g00 = 0.f, g01 = 0.f, g11 = 0.f;
-#pragma unroll
-  for (int a = 0; a < 3; ++a) {
-    const float c0 = g.o * R[3 * a], c1 = g.o * R[3 * a + 1];
-    g00 = fmaf(c0, c0, g00); g01 = fmaf(c0, c1, g01); g11 = fmaf(c1, c1, g11);
-  }
-  const float d = g00 - g11;
-  const float lam = 0.5f * (g00 + g11 - sqrtf(fmaf(d, d, 4.f * g01 * g01)));
-  const float sig = sqrtf(fmaxf(lam, 0.f));
-  const float a = (0.8660254f * NT) * __builtin_amdgcn_rcpf(sig);   // inf for a degenerate map
-  const float c = 2.f * a + 1.f;
-  return c * c;                              // NaN map -> NaN
+  return contrib_bound3<NT>(g.o, R);
 }
-// Bound on the sum of |weights| one voxel receives from all pixels of one
-// pose: |w| = |K(d_x) K(d_y) K(d_z)| <= |K(d_i)| |K(d_j)| for any two axes
-// i, j, and the pixels' (d_i, d_j) form the lattice M Z^2 + shift, with M the
-// rows i, j of A = o [R_:0 R_:1].  Over each unit cell of the (d_i, d_j)
-// plane, |K| |K| is at most the product of the kernel's largest |value| over
-// the two unit intervals (summed over the cells: (2 + 2 * 0.0742)^2 for the
-// cubic kernel, whose side lobes reach 0.0741 at |t| = 4/3; 2^2 for the linear
-// one), and a half-open unit cell holds at most (floor(w_1) + 1)(floor(w_2) +
-// 1) lattice points, w_r being the sum of |row r of M^-1| (the range of pixel
-// coordinate r over the cell).  The best of the three axis pairs is taken.
-// About 18.5 for a rotation (the pixel count bound below gives 63).
 template <int NT>
 __device__ __forceinline__ float weight_sum_bound(const KGeom& g, const float* R) {
-  constexpr float CELLS = NT == 4 ? 4.6152f : 4.0f;   // (2 + 2 * 0.0742)^2 rounded up; 2^2
-  float a0[3], a1[3];
-#pragma unroll
-  for (int a = 0; a < 3; ++a) { a0[a] = g.o * R[3 * a]; a1[a] = g.o * R[3 * a + 1]; }
-  float best = 3.0e38f;
-#pragma unroll
-  for (int q = 0; q < 3; ++q) {
-    const int i = q == 2 ? 1 : 0, j = q == 0 ? 1 : 2;
-    const float d = fabsf(a0[i] * a1[j] - a1[i] * a0[j]);
-    if (d > 1e-6f * (fabsf(a0[i]) + fabsf(a1[i])) * (fabsf(a0[j]) + fabsf(a1[j]))) {
-      // rows of M^-1 = (1/d) [[a1_j, -a1_i], [-a0_j, a0_i]]; widths rounded up
-      // (the factor 1.0001 also covers the hardware reciprocal's ulp)
-      const float rd = __builtin_amdgcn_rcpf(d);
-      const float w1 = (fabsf(a1[j]) + fabsf(a1[i])) * rd * 1.0001f + 1e-4f;
-      const float w2 = (fabsf(a0[j]) + fabsf(a0[i])) * rd * 1.0001f + 1e-4f;
-      best = fminf(best, (floorf(w1) + 1.0f) * (floorf(w2) + 1.0f));
-    }
-  }
-  return CELLS * best;   // 3e38 * CELLS -> inf for a rank-deficient map
+  return weight_sum_bound3<NT>(g.o, R);
 }
 
 // Poses with a larger bound (degenerate maps) go to the edge kernel.

@@ -469,8 +469,8 @@ extern "C" {
 
 int tp_abi_version(void) { return TPROJ_ABI_VERSION; }
 
-const char* tp_status_string(tp_status s) {
-  switch (s) {
+const char* tp_status_string(int s) {
+  switch (s) {   // an int: a caller may pass any code
     case TP_OK: return "ok";
     case TP_E_NULL: return "required pointer is NULL";
     case TP_E_SHAPE: return "invalid shape";
@@ -550,19 +550,27 @@ Ws2 ws2_layout(const tp_geom* g, int op, void* base) {
   const bool ec = op != TP_OP_BACKPROJECT_2D;
   const bool er = op == TP_OP_BACKPROJECT_2D_BACKWARD;
   const bool bp = op == TP_OP_PROJECT_2D_BACKWARD || op == TP_OP_BACKPROJECT_2D;
-  Ws2 w;
-  char* p = (char*)base;
-  size_t off = 0;
-  if (ec) { w.ec = (float2*)(p + off); off += align_up(ne * sizeof(float2)); }
-  if (er) { w.er = (float*)(p + off); off += align_up(ne * sizeof(float)); }
+  // offsets first; pointers only into a real base (no arithmetic on NULL)
+  size_t off = 0, o_ec = 0, o_er = 0, o_mx = 0, o_parts = 0;
+  if (ec) { o_ec = off; off += align_up(ne * sizeof(float2)); }
+  if (er) { o_er = off; off += align_up(ne * sizeof(float)); }
   if (bp) {
-    w.mx = (float*)(p + off);
+    o_mx = off;
     off += align_up((size_t)g->B * g->P * sizeof(float));
-    w.parts = p + off;
+    o_parts = off;
     off += align_up(tproj::twod_bp_parts_bytes(k, op == TP_OP_BACKPROJECT_2D));
   }
+  Ws2 w;
   w.bytes = off;
-  if (!base) w.ec = nullptr, w.er = nullptr, w.mx = nullptr, w.parts = nullptr;
+  if (base) {
+    char* p = (char*)base;
+    if (ec) w.ec = (float2*)(p + o_ec);
+    if (er) w.er = (float*)(p + o_er);
+    if (bp) {
+      w.mx = (float*)(p + o_mx);
+      w.parts = p + o_parts;
+    }
+  }
   return w;
 }
 

@@ -237,7 +237,9 @@ tp_status tp_timing_read(int kernel_class, double* total_ms, int64_t* launches);
 /* Host-only argument check of a geometry (no GPU needed).                  */
 tp_status tp_validate(const tp_geom* geom);
 
-const char* tp_status_string(tp_status s);
+/* Text of a status code; any int (codes outside tp_status give "unknown
+ * status").                                                               */
+const char* tp_status_string(int s);
 /* Text of the last failure on the calling thread ("" if none).             */
 const char* tp_last_error_detail(void);
 int tp_abi_version(void);

@@ -56,6 +56,18 @@ def test_spectral_header_declares_the_binding_symbols(L):
         assert hasattr(L, f)
 
 
+BOUNDS_HEADER = os.path.join(ROOT, "include", "tproj_bounds.h")
+
+
+def test_bounds_header_declares_the_binding_symbols(L):
+    assert header_functions(BOUNDS_HEADER) == sorted(bp.BOUNDS_SYMBOLS)
+    out = subprocess.run(["nm", "-D", "--defined-only", bp.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    assert set(bp.BOUNDS_SYMBOLS) <= exported
+    for f in bp.BOUNDS_SYMBOLS:
+        assert hasattr(L, f)
+
+
 def test_spectral_entry_points_reject_bad_arguments(L):
     """Checked before anything is enqueued (no device needed)."""
     assert L.tp_volume_rfft(7, 1, 1, None, None, None, 0, None) == TP_E_SHAPE        # odd D
