@@ -102,15 +102,38 @@ size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 // FFT plans: one per (kind, size, batch, device), created on first use with
 // automatic work-area allocation off.  Creating a plan is the one place where
 // device memory is allocated on the library's behalf (hipFFT keeps its
-// tables there); executing one uses the caller's workspace.  The mutex keeps
-// the set-stream / set-work-area / exec triple of one call together.
+// tables there), so a first call for a new shape should not happen under
+// graph capture; executing one uses the caller's workspace.  The mutex keeps
+// the set-stream / set-work-area / exec triple of one call together.  At most
+// MAX_PLANS plans are kept: a new one beyond that replaces the least recently
+// used, whose device is first synchronised so that no queued transform still
+// reads its tables.
 // ---------------------------------------------------------------------------
 struct Plan {
   hipfftHandle h = nullptr;
   size_t work = 0;
+  uint64_t last_use = 0;
 };
+constexpr size_t MAX_PLANS = 16;
 std::mutex g_plan_mu;
 std::map<std::tuple<int, int, int64_t, int>, Plan> g_plans;
+uint64_t g_plan_clock = 0;
+
+// Drops the least recently used plan.  Caller holds g_plan_mu.
+void evict_plan() {
+  auto lru = g_plans.begin();
+  for (auto it = g_plans.begin(); it != g_plans.end(); ++it)
+    if (it->second.last_use < lru->second.last_use) lru = it;
+  const int pdev = std::get<3>(lru->first);
+  int cur = -1;
+  (void)hipGetDevice(&cur);
+  if (pdev != cur) (void)hipSetDevice(pdev);
+  (void)hipDeviceSynchronize();
+  hipfftDestroy(lru->second.h);
+  if (pdev != cur && cur >= 0) (void)hipSetDevice(cur);
+  (void)hipGetLastError();
+  g_plans.erase(lru);
+}
 
 enum { KIND_R2C_3D = 0, KIND_C2R_2D = 1 };
 
@@ -124,7 +147,10 @@ Plan* get_plan(int kind, int n, int64_t batch, const char** err) {
   }
   const auto key = std::make_tuple(kind, n, batch, dev);
   auto it = g_plans.find(key);
-  if (it != g_plans.end()) return &it->second;
+  if (it != g_plans.end()) {
+    it->second.last_use = ++g_plan_clock;
+    return &it->second;
+  }
   if (batch > 0x7fffffff) {
     *err = "FFT batch too large";
     return nullptr;
@@ -149,6 +175,8 @@ Plan* get_plan(int kind, int n, int64_t batch, const char** err) {
     *err = "hipFFT plan creation failed";
     return nullptr;
   }
+  while (g_plans.size() >= MAX_PLANS) evict_plan();
+  p.last_use = ++g_plan_clock;
   return &(g_plans[key] = p);
 }
 

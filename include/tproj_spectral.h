@@ -14,8 +14,12 @@
  * before anything is enqueued, tp_status results with tp_last_error_detail().
  * The FFTs are hipFFT plans cached per (kind, size, batch, device): creating
  * one (the first workspace query or call for a shape) allocates hipFFT's own
- * device tables; every call takes its scratch from the caller's workspace.
- * Calls that share a plan are serialised by a lock while they enqueue.
+ * device tables, so that first use belongs outside graph capture; every call
+ * takes its scratch from the caller's workspace.  Calls that share a plan
+ * are serialised by a lock while they enqueue.  At most 16 plans are kept;
+ * creating one more first waits for the device of the least recently used
+ * plan to go idle and destroys that plan (callers that cycle through many
+ * image counts pay this wait: a fixed batch size avoids it).
  */
 #ifndef TPROJ_SPECTRAL_H
 #define TPROJ_SPECTRAL_H

