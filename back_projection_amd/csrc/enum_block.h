@@ -46,8 +46,21 @@ struct EnumShared {
   int hky[WIN];                    // ky of each hit's first row
   unsigned short rstart[ROWS];     // first candidate of row r (< EB_CMAX)
   int rinfo[ROWS];                 // kx0 | (ky & 0xfff) << 11 | hit << 23
-  RowIndex crow[EB_CMAX];          // row of candidate i
+  alignas(4) RowIndex crow[EB_CMAX];   // row of candidate i
 };
+
+// crow[j0 .. j1) = row: single entries up to a 4-byte boundary, then whole
+// 32-bit words, then the tail (a row's run is about 15 entries).
+template <typename RowIndex>
+__device__ __forceinline__ void fill_rows(RowIndex* crow, int j0, int j1, int row) {
+  constexpr int PER = 4 / (int)sizeof(RowIndex);
+  int j = j0;
+  for (; j < j1 && (j & (PER - 1)) != 0; ++j) crow[j] = (RowIndex)row;
+  const unsigned rep = (unsigned)row * (PER == 4 ? 0x01010101u : 0x00010001u);
+  unsigned* words = reinterpret_cast<unsigned*>(crow);
+  for (; j + PER <= j1; j += PER) words[j / PER] = rep;
+  for (; j < j1; ++j) crow[j] = (RowIndex)row;
+}
 
 // ---------------------------------------------------------------------------
 // Hit lists.  Work item w of volume v is brick b with the pose chunk [e0, e1)
@@ -294,7 +307,7 @@ __device__ __forceinline__ int row_stage(EnumShared<WIN, NW>& es, const KGeom& g
   if (take) {
     es.rstart[tid] = start;
     es.rinfo[tid] = kx0 | ((ky & 0xfff) << 11) | (h << 23);
-    for (int j = 0; j < cnt; ++j) es.crow[start + j] = (typename EnumShared<WIN, NW>::RowIndex)tid;
+    fill_rows(es.crow, start, start + cnt, tid);
   }
   __syncthreads();
   if (all) {

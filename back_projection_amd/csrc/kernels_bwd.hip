@@ -22,6 +22,8 @@
 // whose scale is set, before the window, from per-image maxima in radial
 // bands of |k| and a bound on the contributions a voxel can receive; no sum
 // can overflow, and integer sums make the result deterministic.
+#include <algorithm>
+
 #include "brick_grid.h"
 #include "brick_kernels.h"
 #include "bwd_kernels.h"
@@ -190,7 +192,7 @@ __device__ __forceinline__ void window_sum_max(float& c, float& m) {
   m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
 }
 
-__device__ __forceinline__ int floor_div(int a, int b) {  // b > 0
+__host__ __device__ inline int floor_div(int a, int b) {  // b > 0
   return a >= 0 ? a / b : -((-a + b - 1) / b);
 }
 
@@ -209,15 +211,42 @@ __global__ void __launch_bounds__(256) k_band_max(const float2* __restrict__ Y, 
     for (int i = threadIdx.x; i < bw.nbands; i += blockDim.x) { bm[i] = 0u; bwm[i] = 0u; }
     __syncthreads();
     const float2* Yb = Y + (int64_t)bn * g.npix;
-    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
-      int ikx, iky;
-      pixel_freq(g, pix, ikx, iky);
-      const float kx = (float)ikx, ky = (float)iky;
-      if (!in_mask(g, kx, ky)) continue;
-      const int band = min((int)(sqrtf(fmaf(kx, kx, ky * ky)) * bw.inv_band_w), bw.nbands - 1);
-      const float2 v = Yb[pix];
-      atomicMax(&bm[band], __float_as_uint(fmaxf(fabsf(v.x), fabsf(v.y))));
-      if constexpr (WEIGHTS) atomicMax(&bwm[band], __float_as_uint(fabsf(Wimg[(int64_t)bn * g.npix + pix])));
+    const float* Wb = WEIGHTS ? Wimg + (int64_t)bn * g.npix : nullptr;
+    // pixel pix = threadIdx.x + 256 j: its row and column are stepped from the
+    // previous ones (no division per pixel); four pixels' loads are issued
+    // before their maxima go to LDS
+    constexpr int STEP = 256, U = 4;
+    const int drow = STEP / g.Wi, dcol = STEP - drow * g.Wi;
+    int iy = (int)threadIdx.x / g.Wi, ix = (int)threadIdx.x - iy * g.Wi;
+    for (int pix0 = threadIdx.x; pix0 < g.npix; pix0 += U * STEP) {
+      float2 v[U];
+      float wv[U];
+      int band[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int pix = pix0 + u * STEP;
+        band[u] = -1;
+        if (pix < g.npix) {
+          const float kx = (float)ix, ky = (float)(iy < (g.H >> 1) ? iy : iy - g.H);
+          if (in_mask(g, kx, ky)) {
+            band[u] = min((int)(sqrtf(fmaf(kx, kx, ky * ky)) * bw.inv_band_w), bw.nbands - 1);
+            v[u] = Yb[pix];
+            if constexpr (WEIGHTS) wv[u] = Wb[pix];
+          }
+        }
+        ix += dcol;
+        iy += drow;
+        if (ix >= g.Wi) {
+          ix -= g.Wi;
+          ++iy;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (band[u] < 0) continue;
+        atomicMax(&bm[band[u]], __float_as_uint(fmaxf(fabsf(v[u].x), fabsf(v[u].y))));
+        if constexpr (WEIGHTS) atomicMax(&bwm[band[u]], __float_as_uint(fabsf(wv[u])));
+      }
     }
     __syncthreads();
     for (int i = threadIdx.x; i < bw.nbands; i += blockDim.x) {
@@ -562,6 +591,103 @@ __global__ void __launch_bounds__(256) k_bwd_fold(float2* __restrict__ vol, floa
 }
 
 // ---------------------------------------------------------------------------
+// The same fold driven by a per-axis table.  All three axes share one brick
+// grid and the period D, so the tap-space preimages of a voxel factor into
+// per-axis lists: for every coordinate c in [0, D), the (brick index, tile
+// offset) pairs of the taps t = c (mod D) that some brick's tile holds,
+// translates ascending, bricks ascending.  Each workgroup builds the table in
+// LDS (D x FOLD_K entries); a voxel then walks the product of its three lists
+// (Friedel mates: the lists of -x, -y, -z) with no division in the loop.
+// Used when no coordinate has more than FOLD_K pairs (the launcher checks).
+// ---------------------------------------------------------------------------
+constexpr int FOLD_K = 8;
+
+template <int NT, bool WEIGHTS>
+__global__ void __launch_bounds__(256) k_bwd_fold_map(float2* __restrict__ vol, float* __restrict__ wvol,
+                                                      const float2* __restrict__ part_c,
+                                                      const float* __restrict__ part_w, KGeom g, BwdGrid bw,
+                                                      const int* __restrict__ prefix) {
+  extern __shared__ unsigned short fmap[];   // [D][FOLD_K] entries brick * 16 + offset, then [D] counts
+  unsigned short* fcnt = fmap + g.D * FOLD_K;
+  const BrickGrid& bg = bw.bg;
+  constexpr int HL = NT == 4 ? 1 : 0;
+  constexpr int SB = TE - NT + 1;   // brick edge (bg.S)
+  const int tlo = bg.origin - HL, thi = bg.origin + (bg.nb - 1) * SB - HL + TE - 1;   // covered taps
+  for (int c = threadIdx.x; c < g.D; c += blockDim.x) {
+    int n = 0;
+    for (int t = c + g.D * floor_div(tlo - c + g.D - 1, g.D); t <= thi; t += g.D) {
+      const int i0 = max(0, floor_div(t - bg.origin + HL - TE, SB) + 1), i1 = min(bg.nb - 1, floor_div(t - bg.origin + HL, SB));
+      for (int i = i0; i <= i1 && n < FOLD_K; ++i)
+        fmap[c * FOLD_K + n++] = (unsigned short)(i * 16 + (t - (bg.origin + i * SB - HL)));
+    }
+    fcnt[c] = (unsigned short)n;
+  }
+  __syncthreads();
+  const int nvol = g.D * g.D * g.W;
+  const int vsel = blockIdx.y;
+  const float2* pc = part_c + (int64_t)vsel * bg.nwork * TLOG;
+  const float* pw = WEIGHTS ? part_w + (int64_t)vsel * bg.nwork * TLOG : nullptr;
+  for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < nvol; v += gridDim.x * blockDim.x) {
+    const int xy = v % (g.W * g.D), z = v / (g.W * g.D);
+    const int x = xy % g.W, y = xy / g.W;
+    float2 a = make_float2(0.f, 0.f);
+    float aw = 0.f;
+    for (int kind = 0; kind < 2; ++kind) {
+      if (kind == 1 && !(x >= 1 && x <= g.half - 1)) break;
+      const int cx = kind ? g.D - x : x, cy = kind ? (g.D - y) % g.D : y, cz = kind ? (g.D - z) % g.D : z;
+      const unsigned short* mx = fmap + cx * FOLD_K;
+      const unsigned short* my = fmap + cy * FOLD_K;
+      const unsigned short* mz = fmap + cz * FOLD_K;
+      const int nx = fcnt[cx], ny = fcnt[cy], nz = fcnt[cz];
+      float2 part = make_float2(0.f, 0.f);
+      float partw = 0.f;
+      for (int jz = 0; jz < nz; ++jz) {
+        const int ez = mz[jz];
+        for (int jy = 0; jy < ny; ++jy) {
+          const int ey = my[jy];
+          const int bzy = ((ez >> 4) * bg.nb + (ey >> 4)) * bg.nb;
+          const int lzy = (ez & 15) * (TE * TE) + (ey & 15) * TE;
+          for (int jx = 0; jx < nx; ++jx) {
+            const int ex = mx[jx];
+            const int bb = bzy + (ex >> 4);
+            const int k0 = prefix[bb], k1 = prefix[bb + 1];
+            const int64_t li = lzy + (ex & 15);
+            // four chunks at a time, so that several loads are in flight
+            int c = k0;
+            for (; c + 4 <= k1; c += 4) {
+              float2 t[4];
+              float tw[4];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                t[j] = pc[(int64_t)(c + j) * TLOG + li];
+                if constexpr (WEIGHTS) tw[j] = pw[(int64_t)(c + j) * TLOG + li];
+              }
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                part.x += t[j].x;
+                part.y += t[j].y;
+                if constexpr (WEIGHTS) partw += tw[j];
+              }
+            }
+            for (; c < k1; ++c) {
+              const float2 t = pc[(int64_t)c * TLOG + li];
+              part.x += t.x;
+              part.y += t.y;
+              if constexpr (WEIGHTS) partw += pw[(int64_t)c * TLOG + li];
+            }
+          }
+        }
+      }
+      a.x += part.x;
+      a.y += kind ? -part.y : part.y;
+      aw += partw;
+    }
+    vol[(int64_t)nvol * vsel + v] = a;
+    if constexpr (WEIGHTS) wvol[(int64_t)nvol * vsel + v] = aw;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Pixels the bricks do not serve (degenerate maps, samples outside every
 // active brick): their taps with global atomics, after the fold.  One
 // workgroup per pose; a pose served whole by the bricks is skipped.
@@ -622,6 +748,25 @@ static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 int bwd_brick_edge(int interp) { return TE - (interp == 1 ? 4 : 2) + 1; }
 
+// Does every coordinate of the per-axis fold table hold at most FOLD_K
+// (brick, offset) pairs?  (The same count k_bwd_fold_map's table makes.)
+static bool fold_table_fits(const KGeom& g, const BwdGrid& bw, int interp) {
+  const BrickGrid& bg = bw.bg;
+  const int NT = interp == 1 ? 4 : 2, HL = interp == 1 ? 1 : 0, SB = TE - NT + 1;
+  if (bg.S != SB || g.D > 4096) return false;
+  const int tlo = bg.origin - HL, thi = bg.origin + (bg.nb - 1) * SB - HL + TE - 1;
+  for (int c = 0; c < g.D; ++c) {
+    int n = 0;
+    for (int t = c + g.D * floor_div(tlo - c + g.D - 1, g.D); t <= thi; t += g.D) {
+      const int i0 = std::max(0, floor_div(t - bg.origin + HL - TE, SB) + 1);
+      const int i1 = std::min(bg.nb - 1, floor_div(t - bg.origin + HL, SB));
+      n += i1 >= i0 ? i1 - i0 + 1 : 0;
+    }
+    if (n > FOLD_K) return false;
+  }
+  return true;
+}
+
 size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights) {
   const size_t work = brick_work_bytes(bw.bg, Bv);
   const size_t bands = align256((size_t)bw.npose * bw.nbands * sizeof(float) * (weights ? 2 : 1));
@@ -681,7 +826,16 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
     const int blocks = (int)((nvol + 255) / 256 < 8192 ? (nvol + 255) / 256 : 8192);
     const dim3 fg(blocks, g.Bv);
     ev_begin(ev_fold, st);
-    if (interp == 1) {
+    if (fold_table_fits(g, bw, interp)) {
+      const size_t shm = (size_t)g.D * (FOLD_K + 1) * sizeof(unsigned short);
+      if (interp == 1) {
+        if (weights) hipLaunchKernelGGL((k_bwd_fold_map<4, true>), fg, blk, shm, st, vol, wvol, part_c, part_w, g, bw, prefix);
+        else hipLaunchKernelGGL((k_bwd_fold_map<4, false>), fg, blk, shm, st, vol, wvol, part_c, part_w, g, bw, prefix);
+      } else {
+        if (weights) hipLaunchKernelGGL((k_bwd_fold_map<2, true>), fg, blk, shm, st, vol, wvol, part_c, part_w, g, bw, prefix);
+        else hipLaunchKernelGGL((k_bwd_fold_map<2, false>), fg, blk, shm, st, vol, wvol, part_c, part_w, g, bw, prefix);
+      }
+    } else if (interp == 1) {
       if (weights) hipLaunchKernelGGL((k_bwd_fold<4, true>), fg, blk, 0, st, vol, wvol, part_c, part_w, g, bw, prefix);
       else hipLaunchKernelGGL((k_bwd_fold<4, false>), fg, blk, 0, st, vol, wvol, part_c, part_w, g, bw, prefix);
     } else {

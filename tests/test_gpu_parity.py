@@ -34,6 +34,10 @@ SMALL = [
     ("cubic-oversampled-cut", 14, 16, 4, 1, 1, 1, 1, 1, 2.0, 7.0, True, "rot"),
     ("linear-bcast-shifts", 16, 18, 5, 2, 2, 2, 1, 0, 1.0, -1.0, False, "rot"),
     ("cubic-tiny-D", 8, 8, 6, 1, 1, 1, 1, 1, 1.0, -1.0, False, "rot"),
+    # images much larger than the box: every voxel has a dozen periodic
+    # preimages per axis, more than the fold's per-axis table holds, so the
+    # back-projection takes the untabled fold
+    ("cubic-many-aliases", 8, 48, 3, 1, 1, 1, 1, 1, 1.0, -1.0, False, "rot"),
 ]
 
 
