@@ -198,10 +198,10 @@ __device__ __forceinline__ int tile_addr(int x, int y, int z) {
 // The tap order of one lane in the bank-split tile, for the pixel whose first
 // tap is tile entry l: its slot (lane & 3, (lane >> 2) & 3) fixes the
 // rotations t (x) and r (z) that put the lane's step-(a, c) tap in bank pair
-// ((lane + a) & 3) + 4 (((lane >> 2) + c) & 3).  Step (a, b, c) reads entry
-// xo[a] + zo[c] + 64 b, i.e. the tap (l0 + ((a + t) & 3), l1 + b,
-// l2 + ((c + r) & 3)), whose x and z weights are those of index (a + t) & 3
-// and (c + r) & 3.
+// ((lane + a) & 3) + 4 (((lane >> 2) + c) & 3).  Step (a, b, c) reads the tap
+// (l0 + ((a + t) & 3), l1 + b, l2 + ((c + r) & 3)), whose x and z weights are
+// those of index (a + t) & 3 and (c + r) & 3, at tile entry xo[a] + zo[c] +
+// 64 b (zo includes l1).
 struct SplitTaps {
   int xo[4], zo[4];
   int t, r;
@@ -214,6 +214,28 @@ __device__ __forceinline__ void split_taps(const int l[3], SplitTaps& s) {
   for (int j = 0; j < 4; ++j) {
     s.xo[j] = split_x(l[0] + ((j + s.t) & 3));
     s.zo[j] = split_z(l[2] + ((j + s.r) & 3)) + 64 * l[1];
+  }
+}
+
+// The same tap order as byte offsets (ES bytes per entry), derived without a
+// shift per column: the step-a tap has x mod 4 = s = (lane + a) & 3 and lies
+// in [l0, l0 + 3], so x = 4 (l0 >> 2) + s + (s < (l0 & 3) ? 4 : 0), and
+// split_x(x) = s + 16 (x >> 2); likewise for z.  The residues s are lane
+// constants that the compiler keeps in registers: fewer instructions per
+// pixel, more registers (used by the forward, which has them to spare).
+template <int ES>
+__device__ __forceinline__ void split_taps_bytes(const int l[3], SplitTaps& s) {
+  const int lane = (int)threadIdx.x;
+  const int u = lane & 3, v = (lane >> 2) & 3;
+  s.t = (u - l[0]) & 3;
+  s.r = (v - l[2]) & 3;
+  const int x4 = l[0] & 3, z4 = l[2] & 3;
+  const int bx = (l[0] >> 2) * (16 * ES), bz = (l[2] >> 2) * (1024 * ES) + l[1] * (64 * ES);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int sx = (u + j) & 3, sz = (v + j) & 3;
+    s.xo[j] = bx + sx * ES + (sx < x4 ? 16 * ES : 0);
+    s.zo[j] = bz + sz * (4 * ES) + (sz < z4 ? 1024 * ES : 0);
   }
 }
 
@@ -330,8 +352,12 @@ template <bool DERIV, typename T>
 __device__ __forceinline__ void interp_split(const T* tile, const int l[3], const float wx_in[4], const float wy[4],
                                              const float wz_in[4], const float dx_in[4], const float dy[4],
                                              const float dz_in[4], T& I, T* dI) {
+  // tap offsets: in bytes for the value-only gather (fewer instructions, a
+  // few more registers), in entries for the derivative gather, which has no
+  // registers to spare (measured: the byte form made it 4 % slower)
   SplitTaps st;
-  split_taps(l, st);
+  if constexpr (DERIV) split_taps(l, st);
+  else split_taps_bytes<(int)sizeof(T)>(l, st);
   float wx[4], wz[4], dx[4], dz[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -354,7 +380,8 @@ __device__ __forceinline__ void interp_split(const T* tile, const int l[3], cons
     T p = z0, px = z0, py = z0;   // plane sums: wx*q, dx*q, wx*qy
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const T* col = tile + st.xo[a] + st.zo[c];
+      const T* col = DERIV ? tile + st.xo[a] + st.zo[c]
+                           : reinterpret_cast<const T*>(reinterpret_cast<const char*>(tile) + st.xo[a] + st.zo[c]);
       T q = z0, qy = z0;          // column sums: wy*v, dy*v
 #pragma unroll
       for (int b = 0; b < 4; ++b) {

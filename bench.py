@@ -73,14 +73,14 @@ def op_rates(ms, poses, n_in, tap_bytes_per_pixel, flops_per_pixel):
 # reported when the digest of the 3D kernel sources matches, else null.
 TRAFFIC = {
     # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
-    "forward": {"sources_sha256": "b074b049d537aceb8c0b03659a35565774b70401840a823590693dfaf156da0b",
-               "fetch_bytes": 313602450, "write_bytes": 1183400845},
-    "backward": {"sources_sha256": "b074b049d537aceb8c0b03659a35565774b70401840a823590693dfaf156da0b",
-                "fetch_bytes": 2901277100, "write_bytes": 271601650},
-    "gradient": {"sources_sha256": "b074b049d537aceb8c0b03659a35565774b70401840a823590693dfaf156da0b",
-                "fetch_bytes": 2784170085, "write_bytes": 120424608},
-    "fold": {"sources_sha256": "b074b049d537aceb8c0b03659a35565774b70401840a823590693dfaf156da0b",
-            "fetch_bytes": 292597288, "write_bytes": 8519680},
+    "forward": {"sources_sha256": "e733164d302f177de7bd7709498a898bdf63a13dd5e7139a5750eed152a3f79f",
+               "fetch_bytes": 313070946, "write_bytes": 1183370163},
+    "backward": {"sources_sha256": "e733164d302f177de7bd7709498a898bdf63a13dd5e7139a5750eed152a3f79f",
+                "fetch_bytes": 2900810531, "write_bytes": 271601564},
+    "gradient": {"sources_sha256": "e733164d302f177de7bd7709498a898bdf63a13dd5e7139a5750eed152a3f79f",
+                "fetch_bytes": 2783918464, "write_bytes": 120424608},
+    "fold": {"sources_sha256": "e733164d302f177de7bd7709498a898bdf63a13dd5e7139a5750eed152a3f79f",
+            "fetch_bytes": 311878525, "write_bytes": 8519680},
 }
 
 
