@@ -321,6 +321,10 @@ __device__ __forceinline__ void bwd_scatter_split(const int l[3], float fx, floa
   rotate4(wx, st.t);
   rotate4(wz, st.r);
   const float cr = v.x * scale, ci = v.y * scale;
+  // 4-byte weight words: two interleaved copies of the tile, one per 16-lane
+  // half of each 32-lane LDS pass, so that the halves use the even and the
+  // odd banks (the flush adds the two copies)
+  const int half = ((int)threadIdx.x >> 4) & 1;
   float yr[4], yi[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -336,7 +340,7 @@ __device__ __forceinline__ void bwd_scatter_split(const int l[3], float fx, floa
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if constexpr (CH == CH_DATA) atomicAdd(&acc_t[col + 64 * b], fixed_pair(wxz, yr[b], yi[b]));
-        else atomicAdd(&acc_w[col + 64 * b], (unsigned int)fixed_round(wxz, yr[b]));
+        else atomicAdd(&acc_w[2 * (col + 64 * b) + half], (unsigned int)fixed_round(wxz, yr[b]));
       }
     }
 }
@@ -351,8 +355,9 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
   constexpr bool SPLIT = AccTile<NT>::SPLIT;
   constexpr int ASIZE = AccTile<NT>::SIZE;
   const BrickGrid& bg = bw.bg;
+  constexpr int WSIZE = SPLIT ? 2 * ASIZE : ASIZE;   // bank-split weight tiles: two copies
   __shared__ unsigned long long acc_t[DATA ? ASIZE : 1];
-  __shared__ unsigned int acc_w[DATA ? 1 : ASIZE];
+  __shared__ unsigned int acc_w[DATA ? 1 : WSIZE];
   __shared__ EnumShared<WINDOW, BNW> es;
   __shared__ float win_scale;
 
@@ -384,7 +389,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
   float2 acc[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) acc[i] = make_float2(0.f, 0.f);
-  for (int i = tid; i < ASIZE; i += BTHREADS) {
+  for (int i = tid; i < (DATA ? ASIZE : WSIZE); i += BTHREADS) {
     if constexpr (DATA) acc_t[i] = 0ull;
     else acc_w[i] = 0u;
   }
@@ -490,6 +495,13 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
             acc[i].x = fmaf(re, inv, acc[i].x);
             acc[i].y = fmaf(im, inv, acc[i].y);
             acc_t[pi] = 0ull;
+          }
+        } else if constexpr (SPLIT) {
+          const unsigned int u0 = acc_w[2 * pi], u1 = acc_w[2 * pi + 1];
+          if ((u0 | u1) != 0u) {
+            acc[i].x = fmaf((float)((int)u0 + (int)u1), inv, acc[i].x);
+            acc_w[2 * pi] = 0u;
+            acc_w[2 * pi + 1] = 0u;
           }
         } else {
           const unsigned int u = acc_w[pi];
