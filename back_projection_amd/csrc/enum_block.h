@@ -414,11 +414,11 @@ __device__ __forceinline__ float2 lane_fetch(float2 v, int src) {
 }
 
 // ---------------------------------------------------------------------------
-// Per-hit rotation / shift gradient sums: a segmented sum over the lanes of
-// one hit leaves the hit's partial in its last lane, which adds it to the
-// hit's sum in LDS (an atomic add whose result is not waited for).  At the
-// end of a window the sums go to the pose's gradient with global atomics,
-// scaled by o (rotation) or 2 pi / H (shifts).
+// Per-hit rotation / shift gradient sums: the wavefront sums of each hit
+// (grad_collect, below) are added to the hit's sum in LDS (atomic adds whose
+// results are not waited for).  At the end of a window the sums go to the
+// pose's gradient with global atomics, scaled by o (rotation) or 2 pi / H
+// (shifts).
 // ---------------------------------------------------------------------------
 template <int WIN, int NW>
 __device__ __forceinline__ void grad_flush(const KGeom& g, const EnumShared<WIN, NW>& es, float (*gw)[8], int nw,

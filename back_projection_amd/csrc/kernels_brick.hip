@@ -233,11 +233,10 @@ __global__ void __launch_bounds__(256) k_fwd_edge(const T* __restrict__ vol, con
 // rotation / shift gradients
 //   gR[i][j] += o * sum_k M (Re(conj(U) phi dI_i(Vc)) + Ur dI_i(Vr)) k3_j
 //   gs       += (2 pi / H) sum_k M (kx, ky) Im(conj(U) phi I(Vc))
-// Each candidate lane computes its 8 terms; a segmented sum over the lanes of
-// one hit (candidates are ordered by hit) leaves the hit's partial in its last
-// lane, which adds it to a per-wavefront, per-hit sum in LDS.  At the end of a
-// window the four wavefronts' sums go to the pose's gradient with global
-// atomics.
+// Each candidate lane computes its 8 terms; a butterfly reduce-scatter over
+// the lanes of each hit (candidates are ordered by hit, grad_collect) leaves
+// the hit's 8 totals in lanes 0-7, which add them to the hit's sum in LDS.  At
+// the end of a window the sums go to the pose's gradient with global atomics.
 // ---------------------------------------------------------------------------
 // hits per window: 32 with the cubic tile, 16 with the larger padded linear
 // one (four workgroups per CU fit the LDS either way)
