@@ -458,6 +458,52 @@ def run_oversampling(bp, workloads, torch, details, D=128, P_acc=24, n_blobs=80)
     details["oversampling"] = res
 
 
+def brick_roofline(kernels, isolated):
+    """The JSON line's roofline object for the dominant brick kernel (largest
+    live time in the step): the gradient kernel, whose limit is fp32 VALU
+    issue (SQ counters: VALU instructions and busy cycles, profiles/); its
+    roofline is the fp32 FMA rate.  The tap-bandwidth figure of the L2
+    roofline and the LDS and HBM fractions go beside it, and the forward
+    kernel's figures with them."""
+    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
+    kd = kernels[dom]
+    achieved = kd["flops"] / (kd["avg_ms"] * 1e-3) / 1e12
+    tap_gbps = kd["tap_bytes"] / (kd["avg_ms"] * 1e-3) / 1e9
+    traffic = measured_traffic(dom)
+    roofline = {
+        "bound": "alu",
+        "achieved": round(achieved, 2),
+        "peak": round(FP32_FMA_TFLOPS, 2),
+        "unit": "TFLOP/s",
+        "frac": round(achieved / FP32_FMA_TFLOPS, 4),
+        "traffic": traffic,
+        "kernel": dom,
+        "flops_per_launch": kd["flops"],
+        "flops_per_pixel": kd["flops_per_pixel"],
+        "peak_note": ("fp32 FMA issue without packed math (256 CUs x 4 SIMD16 x 2 flop x 2.4 GHz); the published "
+                      f"{FP32_VECTOR_TFLOPS} TFLOP/s counts packed FMA, which these kernels do not use"),
+        "l2_tap": {"achieved": round(tap_gbps, 1), "peak": round(L2_PEAK_GBS, 1), "unit": "GB/s",
+                   "frac": kd["l2_frac"]},
+        "lds": {"achieved": round(tap_gbps, 1), "peak": round(LDS_PEAK_GBS, 1), "unit": "GB/s",
+                "frac": kd["lds_frac"]},
+        "hbm": {"achieved": round(kd["hbm_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["hbm_frac"]},
+    }
+    if dom in isolated:
+        iso = isolated[dom]
+        roofline["overlap"] = ("runs beside the other backward kernel on a second stream; achieved uses "
+                               "its live duration in the step")
+        roofline["alone"] = {"avg_ms": round(iso, 4),
+                             "achieved": round(kd["flops"] / (iso * 1e-3) / 1e12, 2),
+                             "frac": round(kd["flops"] / (iso * 1e-3) / 1e12 / FP32_FMA_TFLOPS, 4),
+                             "l2_tap_frac": round(kd["tap_bytes"] / (iso * 1e-3) / 1e9 / L2_PEAK_GBS, 4)}
+    if "forward" in kernels and dom != "forward":
+        kf = kernels["forward"]
+        roofline["forward"] = {"avg_ms": kf["avg_ms"], "tflops": kf["tflops"], "alu_frac": kf["alu_frac"],
+                               "l2_tap_frac": kf["l2_frac"], "lds_frac": kf["lds_frac"],
+                               "traffic": measured_traffic("forward")}
+    return roofline
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -608,48 +654,11 @@ def main():
         if n:
             isolated[k] = tot / n
             eprint(f"[bench] kernel {k} alone: {tot / n:.4f} ms")
-    # The dominant kernel (largest live time in the step) is the gradient
-    # kernel, whose limit is fp32 VALU issue (SQ counters: VALU instructions
-    # and busy cycles, profiles/); its roofline is the fp32 FMA rate.  The
-    # tap-bandwidth figure of the L2 roofline and the LDS and HBM fractions go
-    # beside it, and the forward kernel's figures with them.
-    dom = max(kernels, key=lambda k: kernels[k]["avg_ms"] * kernels[k]["launches"])
-    kd = kernels[dom]
-    achieved = kd["flops"] / (kd["avg_ms"] * 1e-3) / 1e12
-    tap_gbps = kd["tap_bytes"] / (kd["avg_ms"] * 1e-3) / 1e9
-    traffic = measured_traffic(dom)
-    roofline = {
-        "bound": "alu",
-        "achieved": round(achieved, 2),
-        "peak": round(FP32_FMA_TFLOPS, 2),
-        "unit": "TFLOP/s",
-        "frac": round(achieved / FP32_FMA_TFLOPS, 4),
-        "traffic": traffic,
-        "kernel": dom,
-        "flops_per_launch": kd["flops"],
-        "flops_per_pixel": kd["flops_per_pixel"],
-        "peak_note": ("fp32 FMA issue without packed math (256 CUs x 4 SIMD16 x 2 flop x 2.4 GHz); the published "
-                      f"{FP32_VECTOR_TFLOPS} TFLOP/s counts packed FMA, which these kernels do not use"),
-        "l2_tap": {"achieved": round(tap_gbps, 1), "peak": round(L2_PEAK_GBS, 1), "unit": "GB/s",
-                   "frac": kd["l2_frac"]},
-        "lds": {"achieved": round(tap_gbps, 1), "peak": round(LDS_PEAK_GBS, 1), "unit": "GB/s",
-                "frac": kd["lds_frac"]},
-        "hbm": {"achieved": round(kd["hbm_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["hbm_frac"]},
-    }
-    if dom in isolated:
-        iso = isolated[dom]
-        roofline["overlap"] = ("runs beside the other backward kernel on a second stream; achieved uses "
-                               "its live duration in the step")
-        roofline["alone"] = {"avg_ms": round(iso, 4),
-                             "achieved": round(kd["flops"] / (iso * 1e-3) / 1e12, 2),
-                             "frac": round(kd["flops"] / (iso * 1e-3) / 1e12 / FP32_FMA_TFLOPS, 4),
-                             "l2_tap_frac": round(kd["tap_bytes"] / (iso * 1e-3) / 1e9 / L2_PEAK_GBS, 4)}
-    if "forward" in kernels and dom != "forward":
-        kf = kernels["forward"]
-        roofline["forward"] = {"avg_ms": kf["avg_ms"], "tflops": kf["tflops"], "alu_frac": kf["alu_frac"],
-                               "l2_tap_frac": kf["l2_frac"], "lds_frac": kf["lds_frac"],
-                               "traffic": measured_traffic("forward")}
-
+    roofline = None
+    if not kernels:   # only the direct kernels ran (TPROJ_KERNELS=direct): no brick kernel timings
+        eprint("[bench] no brick-kernel timings (direct kernels): roofline not reported")
+    else:
+        roofline = brick_roofline(kernels, isolated)
     details = {"kernels": kernels, "ms_per_step": ms_per_step, "instrumented_ms_per_step": instr_ms}
     cpu = None
     if not args.no_cpu_baseline:
