@@ -80,6 +80,30 @@ __device__ __forceinline__ void pixel_freq(const KGeom& g, int pix, int& kx, int
   ky = iy < (g.H >> 1) ? iy : iy - g.H;
 }
 
+// The pixels start, start + stride, ... of one image with their frequency
+// indices, stepped without a division per pixel (pix = iy * Wi + ix; a step
+// adds stride / Wi rows and stride mod Wi columns, then carries one row).
+struct PixelWalk {
+  int pix, iy, ix, drow, dcol;
+  __device__ __forceinline__ PixelWalk(const KGeom& g, int start, int stride) : pix(start) {
+    iy = start / g.Wi;
+    ix = start - iy * g.Wi;
+    drow = stride / g.Wi;
+    dcol = stride - drow * g.Wi;
+  }
+  __device__ __forceinline__ void step(const KGeom& g, int stride) {
+    pix += stride;
+    ix += dcol;
+    iy += drow;
+    if (ix >= g.Wi) {
+      ix -= g.Wi;
+      ++iy;
+    }
+  }
+  __device__ __forceinline__ int kx() const { return ix; }
+  __device__ __forceinline__ int ky(const KGeom& g) const { return iy < (g.H >> 1) ? iy : iy - g.H; }
+};
+
 __device__ __forceinline__ bool in_mask(const KGeom& g, float kx, float ky) {
   return g.r2 < 0.0f || fmaf(kx, kx, ky * ky) <= g.r2;
 }

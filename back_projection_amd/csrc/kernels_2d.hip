@@ -165,10 +165,9 @@ __global__ void __launch_bounds__(T2) k2_gather(const T* __restrict__ E, const f
       sy = s[1];
     }
     T* O = out + ((int64_t)bimg * g.P + n) * g.npix;
-    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
-      int ikx, iky;
-      pixel_freq(g, pix, ikx, iky);
-      const float kx = (float)ikx, ky = (float)iky;
+    for (PixelWalk pw(g, threadIdx.x, blockDim.x); pw.pix < g.npix; pw.step(g, blockDim.x)) {
+      const int pix = pw.pix;
+      const float kx = (float)pw.kx(), ky = (float)pw.ky(g);
       if (!in_mask(g, kx, ky)) { O[pix] = zero2(T{}); continue; }
       float px, py, fx, fy, wx[NT], wy[NT];
       slice_coord2(g, R, kx, ky, px, py);
@@ -250,10 +249,9 @@ __global__ void __launch_bounds__(T2) k2_grad(const float2* __restrict__ Ec, con
     }
     const int64_t img = ((int64_t)bimg * g.P + n) * g.npix;
     float acc[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
-      int ikx, iky;
-      pixel_freq(g, pix, ikx, iky);
-      const float kx = (float)ikx, ky = (float)iky;
+    for (PixelWalk pw(g, threadIdx.x, blockDim.x); pw.pix < g.npix; pw.step(g, blockDim.x)) {
+      const int pix = pw.pix;
+      const float kx = (float)pw.kx(), ky = (float)pw.ky(g);
       if (!in_mask(g, kx, ky)) continue;
       float px, py, fx, fy, wx[NT], wy[NT], dx[NT], dy[NT];
       slice_coord2(g, R, kx, ky, px, py);
@@ -310,10 +308,9 @@ __global__ void __launch_bounds__(256) k2_img_max(const float2* __restrict__ Y, 
   __shared__ float red[4];
   for (int bn = blockIdx.x; bn < g.B * g.P; bn += gridDim.x) {
     float m = 0.f;
-    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
-      int ikx, iky;
-      pixel_freq(g, pix, ikx, iky);
-      if (!in_mask(g, (float)ikx, (float)iky)) continue;
+    for (PixelWalk pw(g, threadIdx.x, blockDim.x); pw.pix < g.npix; pw.step(g, blockDim.x)) {
+      const int pix = pw.pix;
+      if (!in_mask(g, (float)pw.kx(), (float)pw.ky(g))) continue;
       if constexpr (WEIGHTS) m = fmaxf(m, fabsf(Wimg[(int64_t)bn * g.npix + pix]));
       else {
         const float2 v = Y[(int64_t)bn * g.npix + pix];
@@ -421,10 +418,9 @@ __global__ void __launch_bounds__(T2) k2_bp(const float2* __restrict__ Y, const 
         sy = s[1];
       }
       const int64_t img = ((int64_t)bimg * g.P + n) * g.npix;
-      for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
-        int ikx, iky;
-        pixel_freq(g, pix, ikx, iky);
-        const float kx = (float)ikx, ky = (float)iky;
+      for (PixelWalk pw(g, threadIdx.x, blockDim.x); pw.pix < g.npix; pw.step(g, blockDim.x)) {
+        const int pix = pw.pix;
+        const float kx = (float)pw.kx(), ky = (float)pw.ky(g);
         if (!in_mask(g, kx, ky)) continue;
         float px, py, fx, fy, wx[NT], wy[NT];
           slice_coord2(g, R, kx, ky, px, py);
@@ -506,10 +502,9 @@ __global__ void __launch_bounds__(256) k2_bp_direct(const float2* __restrict__ Y
       sx = s[0];
       sy = s[1];
     }
-    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
-      int ikx, iky;
-      pixel_freq(g, pix, ikx, iky);
-      const float kx = (float)ikx, ky = (float)iky;
+    for (PixelWalk pw(g, threadIdx.x, blockDim.x); pw.pix < g.npix; pw.step(g, blockDim.x)) {
+      const int pix = pw.pix;
+      const float kx = (float)pw.kx(), ky = (float)pw.ky(g);
       if (!in_mask(g, kx, ky)) continue;
       float px, py, fx, fy, wx[NT], wy[NT];
       slice_coord2(g, R, kx, ky, px, py);

@@ -105,10 +105,9 @@ __global__ void __launch_bounds__(256) k_rot_shift_grad(const float2* __restrict
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-  for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
-    int ikx, iky;
-    pixel_freq(g, pix, ikx, iky);
-    const float kx = (float)ikx, ky = (float)iky;
+  for (PixelWalk pw(g, threadIdx.x, blockDim.x); pw.pix < g.npix; pw.step(g, blockDim.x)) {
+    const int pix = pw.pix;
+    const float kx = (float)pw.kx(), ky = (float)pw.ky(g);
     if (!in_mask(g, kx, ky)) continue;
     const float px = g.o * fmaf(R[1], ky, R[0] * kx);
     const float py = g.o * fmaf(R[4], ky, R[3] * kx);

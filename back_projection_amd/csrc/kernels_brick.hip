@@ -204,10 +204,9 @@ __global__ void __launch_bounds__(256) k_fwd_edge(const T* __restrict__ vol, con
     const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
     const bool inside = pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i;
     T* O = out + (int64_t)bn * g.npix;
-    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
-      int ikx, iky;
-      pixel_freq(g, pix, ikx, iky);
-      const float kx = (float)ikx, ky = (float)iky;
+    for (PixelWalk pw(g, threadIdx.x, blockDim.x); pw.pix < g.npix; pw.step(g, blockDim.x)) {
+      const int pix = pw.pix;
+      const float kx = (float)pw.kx(), ky = (float)pw.ky(g);
       if (!in_mask(g, kx, ky)) { O[pix] = zero_of(T{}); continue; }
       if (inside) continue;
       float p[3];
@@ -398,10 +397,9 @@ __global__ void __launch_bounds__(256) k_grad_edge(const float2* __restrict__ vo
     const int bimg = bn / g.P, n = bn - bimg * g.P;
     const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
     if (pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i) continue;
-    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
-      int ikx, iky;
-      pixel_freq(g, pix, ikx, iky);
-      const float kx = (float)ikx, ky = (float)iky;
+    for (PixelWalk pw(g, threadIdx.x, blockDim.x); pw.pix < g.npix; pw.step(g, blockDim.x)) {
+      const int pix = pw.pix;
+      const float kx = (float)pw.kx(), ky = (float)pw.ky(g);
       if (!in_mask(g, kx, ky)) continue;
       float p[3];
       slice_coord(g, R, kx, ky, p);

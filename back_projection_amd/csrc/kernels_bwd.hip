@@ -716,10 +716,9 @@ __global__ void __launch_bounds__(256) k_bwd_edge(const float2* __restrict__ Y, 
     const float* R = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
     const bool ok = pose_ok(contrib_bound<NT>(g, R));
     if (ok && pose_pmax(g, R) <= 0.9995f * (float)bg.pmax_i) continue;
-    for (int pix = threadIdx.x; pix < g.npix; pix += blockDim.x) {
-      int ikx, iky;
-      pixel_freq(g, pix, ikx, iky);
-      const float kx = (float)ikx, ky = (float)iky;
+    for (PixelWalk pw(g, threadIdx.x, blockDim.x); pw.pix < g.npix; pw.step(g, blockDim.x)) {
+      const int pix = pw.pix;
+      const float kx = (float)pw.kx(), ky = (float)pw.ky(g);
       if (!in_mask(g, kx, ky)) continue;
       float p[3];
       slice_coord(g, R, kx, ky, p);
