@@ -214,9 +214,10 @@ struct BwdPlan {
 
 BwdPlan bwd_plan(const tp_geom* g, bool weights) {
   BwdPlan pl;
-  // each work item writes a 16^3 partial tile that the fold reads back: fewer,
-  // larger items than the gather
-  const GatherPlan gp = gather_plan(g, 4096, 8192, tproj::bwd_brick_edge(g->interp));
+  // each work item writes a 16^3 partial tile (the chunks of a brick are
+  // summed before the fold): fewer, larger items than the gather at large
+  // sizes, at least 2048 pixels each
+  const GatherPlan gp = gather_plan(g, 4096, 2048, tproj::bwd_brick_edge(g->interp));
   if (!gp.ok) return pl;
   tproj::BwdGrid& bw = pl.bw;
   bw.bg = gp.bg;
