@@ -73,14 +73,14 @@ def op_rates(ms, poses, n_in, tap_bytes_per_pixel, flops_per_pixel):
 # reported when the digest of the 3D kernel sources matches, else null.
 TRAFFIC = {
     # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
-    "forward": {"sources_sha256": "e733164d302f177de7bd7709498a898bdf63a13dd5e7139a5750eed152a3f79f",
-               "fetch_bytes": 313070946, "write_bytes": 1183370163},
-    "backward": {"sources_sha256": "e733164d302f177de7bd7709498a898bdf63a13dd5e7139a5750eed152a3f79f",
-                "fetch_bytes": 2900810531, "write_bytes": 271601564},
-    "gradient": {"sources_sha256": "e733164d302f177de7bd7709498a898bdf63a13dd5e7139a5750eed152a3f79f",
-                "fetch_bytes": 2783918464, "write_bytes": 120424608},
-    "fold": {"sources_sha256": "e733164d302f177de7bd7709498a898bdf63a13dd5e7139a5750eed152a3f79f",
-            "fetch_bytes": 311878525, "write_bytes": 8519680},
+    "forward": {"sources_sha256": "86b5ac93c65c7c32721b0c14e2f244b1e810c5b1fc20d670e9b40805d3b5eb46",
+               "fetch_bytes": 313172728, "write_bytes": 1183378784},
+    "backward": {"sources_sha256": "86b5ac93c65c7c32721b0c14e2f244b1e810c5b1fc20d670e9b40805d3b5eb46",
+                "fetch_bytes": 2901289665, "write_bytes": 271601650},
+    "gradient": {"sources_sha256": "86b5ac93c65c7c32721b0c14e2f244b1e810c5b1fc20d670e9b40805d3b5eb46",
+                "fetch_bytes": 2783835915, "write_bytes": 120424608},
+    "fold": {"sources_sha256": "86b5ac93c65c7c32721b0c14e2f244b1e810c5b1fc20d670e9b40805d3b5eb46",
+            "fetch_bytes": 223225372, "write_bytes": 33390592},
 }
 
 
