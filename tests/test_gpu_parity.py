@@ -38,6 +38,10 @@ SMALL = [
     # preimages per axis, more than the fold's per-axis table holds, so the
     # back-projection takes the untabled fold
     ("cubic-many-aliases", 8, 48, 3, 1, 1, 1, 1, 1, 1.0, -1.0, False, "rot"),
+    # hundreds of poses per brick and two volumes: several chunks per brick,
+    # so the back-projection sums each brick's chunk tiles before the fold
+    ("cubic-multivolume-chunks", 24, 24, 512, 2, 2, 2, 2, 1, 1.0, -1.0, True, "rot"),
+    ("linear-multivolume-chunks", 32, 32, 1024, 2, 2, 1, 1, 0, 1.0, 15.0, False, "rot"),
 ]
 
 
