@@ -7,6 +7,9 @@
 //                    tile in LDS with padded strides (1, 17, 276 entries)
 //                    under controlled bank keys, or in the bank-split layout
 //                    with per-lane rotated tap order
+//   tpp_valu         FP32 FMA issue rate (independent chains, no packed
+//                    math), alone or beside bank-split 64-bit LDS atomics
+//                    whose values come from the FMAs (the scatter's mix)
 // Each kernel folds what it reads into one float per thread (sink), so that
 // nothing is optimised away.  Argument checks on the host; -1 on bad input,
 // else the HIP status of the launch.
@@ -167,6 +170,84 @@ __global__ void __launch_bounds__(THREADS) k_lds_taps(int iters, float* __restri
   sink[blockIdx.x * THREADS + threadIdx.x] = (float)acc;
 }
 
+
+// FP32 FMA issue: 8 independent chains per thread, 8 FMAs per chain per
+// iteration (64 per iteration), compiled without packed math so that every
+// FMA is one v_fma_f32 / v_fmac_f32.
+__global__ void __launch_bounds__(THREADS) k_valu_fma(int iters, float* __restrict__ sink) {
+  const unsigned t = blockIdx.x * THREADS + threadIdx.x;
+  float a[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = (float)((t + j) & 7) * 0.125f;
+  const float m = 0.999f, c = 1e-3f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] = fmaf(a[j], m, c);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += a[j];
+  sink[t] = s;
+}
+
+// The scatter's tap mix: per 4x4x4 footprint in a bank-split 16^3 tile of
+// 8-byte entries (random bases, rotated per-lane tap order, as mode 3 of
+// k_lds_taps), each tap's word comes from two magic-number FMAs packed with
+// one 64-bit subtraction, plus EXTRA further FMAs into independent
+// accumulators; ATOMIC = false forms the same words and tap indices in
+// registers and drops them (an empty asm statement consumes each pair).
+template <int EXTRA, bool ATOMIC>
+__global__ void __launch_bounds__(THREADS) k_tap_mix(int iters, float* __restrict__ sink) {
+  __shared__ unsigned long long tile[4096];
+  for (int i = threadIdx.x; i < 4096; i += THREADS) tile[i] = 0ull;
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  unsigned long long acc = 0ull;
+  float e[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+    const unsigned h = mix(blockIdx.x * 7919u + threadIdx.x * 131u + (unsigned)it * 977u);
+    const int x = (int)(h % 13u), y = (int)((h >> 8) % 13u), z = (int)((h >> 16) % 13u);
+    const float f = (float)(h & 1023u) * (1.0f / 1024.0f);
+    float w[4], u[4], v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = f + 0.25f * (float)j;
+      u[j] = 3.0f - f * (float)j;
+      v[j] = f * (float)j - 2.0f;
+    }
+    const int t = ((lane & 3) - x) & 3, r = (((lane >> 2) & 3) - z) & 3;
+    int xo[4], zo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      xo[j] = split_x(x + ((j + t) & 3));
+      zo[j] = split_z(z + ((j + r) & 3)) + 64 * y;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        unsigned long long* col = tile + xo[a] + zo[c];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const unsigned long long lo = __float_as_uint(fmaf(w[a], u[b], 12582912.0f));
+          const unsigned long long hi = __float_as_uint(fmaf(w[c], v[b], 12582912.0f));
+          const unsigned long long word = ((hi << 32) | lo) - 0x4B4000004B400000ull;
+#pragma unroll
+          for (int k = 0; k < EXTRA; ++k) e[k & 3] = fmaf(e[k & 3], w[b], u[a]);
+          if constexpr (ATOMIC) atomicAdd(&col[64 * b], word);
+          else asm volatile("" ::"v"(word), "v"(xo[a] + zo[c]));   // word and address formed, then dropped
+        }
+      }
+  }
+  if constexpr (ATOMIC) {
+    __syncthreads();
+    acc = tile[threadIdx.x];
+  }
+  sink[blockIdx.x * THREADS + threadIdx.x] = (float)acc + e[0] + e[1] + e[2] + e[3];
+}
+
 }  // namespace
 
 extern "C" {
@@ -202,6 +283,23 @@ int tpp_lds_taps(float* sink, int mode, int atomic, int iters, int blocks, void*
     else TPP_LDS(3, false);
   }
 #undef TPP_LDS
+  return (int)hipGetLastError();
+}
+
+int tpp_valu(float* sink, int mode, int iters, int blocks, void* stream) {
+  if (!sink || mode < 0 || mode > 6 || iters < 1 || blocks < 1 || blocks > 65535) return -1;
+  const hipStream_t st = (hipStream_t)stream;
+#define TPP_MIX(E, A) hipLaunchKernelGGL((k_tap_mix<E, A>), dim3(blocks), dim3(THREADS), 0, st, iters, sink)
+  switch (mode) {
+    case 0: hipLaunchKernelGGL(k_valu_fma, dim3(blocks), dim3(THREADS), 0, st, iters, sink); break;
+    case 1: TPP_MIX(0, true); break;
+    case 2: TPP_MIX(0, false); break;
+    case 3: TPP_MIX(2, true); break;
+    case 4: TPP_MIX(2, false); break;
+    case 5: TPP_MIX(6, true); break;
+    default: TPP_MIX(6, false); break;
+  }
+#undef TPP_MIX
   return (int)hipGetLastError();
 }
 

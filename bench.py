@@ -34,10 +34,12 @@ UNIT = "projections/s"
 HBM_PEAK_GBS = 8000.0
 L2_PEAK_GBS = 8 * 16 * 128 * 2.4          # = 39321.6 GB/s
 LDS_PEAK_GBS = 256 * 128 * 2.4            # 256 CUs x 128 B/clk x 2.4 GHz = 78643.2 GB/s
-FP32_VECTOR_TFLOPS = 157.3                # published; counts packed (two-wide) FP32 FMA
-# The kernels are built without packed FP32 instructions, so their FP32 ceiling
-# is one FMA per lane per clock: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz.
-FP32_FMA_TFLOPS = 256 * 4 * 16 * 2 * 2.4 / 1000.0   # = 78.64
+# fp32 vector: 256 CUs x 4 SIMDs x 32 lanes per clock x 2 flop x 2.4 GHz.  The
+# kernels are built without packed FP32 instructions; the FMA probe of
+# `--peaks` (non-packed v_fma_f32 only) issues 1.72 wave64 FMAs per CU clock,
+# 135.6 TFLOP/s, so the published figure is the ceiling of non-packed FMAs too.
+FP32_VECTOR_TFLOPS = 157.3
+FP32_FMA_PROBE_TFLOPS = 135.6             # measured, bench.py --peaks
 
 # Algorithmic fp32 flops per in-mask pixel of the separable tricubic
 # interpolation each kernel class performs (2 flops per multiply-add; the
@@ -62,7 +64,7 @@ def op_rates(ms, poses, n_in, tap_bytes_per_pixel, flops_per_pixel):
          "l2_frac": round(poses * n_in * tap_bytes_per_pixel / sec / 1e9 / L2_PEAK_GBS, 4)}
     if flops_per_pixel:
         r["tflops"] = round(poses * n_in * flops_per_pixel / sec / 1e12, 2)
-        r["alu_frac"] = round(r["tflops"] / FP32_FMA_TFLOPS, 4)
+        r["alu_frac"] = round(r["tflops"] / FP32_VECTOR_TFLOPS, 4)
     return r
 
 
@@ -118,8 +120,10 @@ def copy_calibration(torch, gib=1):
 def measure_peaks(torch):
     """The bandwidths the rooflines rest on, measured on this GPU with
     libtproj_probes.so (include/tproj_probes.h): HBM stream read, 8-byte
-    gathers from a cache-resident buffer, and LDS 4x4x4 tap reads / 64-bit
-    atomics under three bank-key regimes.  Printed to stderr as one JSON
+    gathers from a cache-resident buffer, LDS 4x4x4 tap reads / 64-bit
+    atomics under four bank-key regimes, the FP32 FMA issue rate, and the
+    scatter's tap mix (FMAs forming 64-bit words) with and without its LDS
+    atomics.  Printed to stderr as one JSON
     object; nothing here runs in the default benchmark."""
     from back_projection_amd import build_lib
     P = ctypes.CDLL(build_lib.PROBES_LIB)
@@ -162,6 +166,18 @@ def measure_peaks(torch):
             t = timed(lambda: P.tpp_lds_taps(vp(sink.data_ptr()), mode, atomic, iters, blocks, st))
             key = ("lds_atomic_" if atomic else "lds_read_") + name + "_taps_per_clk_cu"
             out[key] = round(blocks * 256 * iters * 64 / t / clk, 2)
+    P.tpp_valu.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    iters = 256
+    t = timed(lambda: P.tpp_valu(vp(sink.data_ptr()), 0, iters, blocks, st))
+    out["fp32_fma_TFLOPs"] = round(blocks * 256 * iters * 128 / t / 1e12, 2)
+    out["fp32_fma_wave_insts_per_clk_cu"] = round(blocks * 4 * iters * 64 / t / clk, 3)
+    # the scatter's mix: taps per clock per CU with and without the atomics
+    iters = 32
+    for mode, extra, atomic in ((1, 0, True), (2, 0, False), (3, 2, True), (4, 2, False), (5, 6, True),
+                                (6, 6, False)):
+        t = timed(lambda: P.tpp_valu(vp(sink.data_ptr()), mode, iters, blocks, st))
+        key = f"tap_mix_fma{2 + extra}_" + ("atomic" if atomic else "no_lds") + "_taps_per_clk_cu"
+        out[key] = round(blocks * 256 * iters * 64 / t / clk, 2)
     eprint("[bench] peaks " + json.dumps(out))
     return out
 
@@ -473,15 +489,16 @@ def brick_roofline(kernels, isolated):
     roofline = {
         "bound": "alu",
         "achieved": round(achieved, 2),
-        "peak": round(FP32_FMA_TFLOPS, 2),
+        "peak": round(FP32_VECTOR_TFLOPS, 2),
         "unit": "TFLOP/s",
-        "frac": round(achieved / FP32_FMA_TFLOPS, 4),
+        "frac": round(achieved / FP32_VECTOR_TFLOPS, 4),
         "traffic": traffic,
         "kernel": dom,
         "flops_per_launch": kd["flops"],
         "flops_per_pixel": kd["flops_per_pixel"],
-        "peak_note": ("fp32 FMA issue without packed math (256 CUs x 4 SIMD16 x 2 flop x 2.4 GHz); the published "
-                      f"{FP32_VECTOR_TFLOPS} TFLOP/s counts packed FMA, which these kernels do not use"),
+        "peak_note": (f"published fp32 vector peak ({FP32_VECTOR_TFLOPS} TFLOP/s: 256 CUs x 4 SIMDs x 32 lanes x "
+                      "2 flop x 2.4 GHz); the kernels use non-packed FMAs, which a probe on this GPU issues at "
+                      f"{FP32_FMA_PROBE_TFLOPS} TFLOP/s"),
         "l2_tap": {"achieved": round(tap_gbps, 1), "peak": round(L2_PEAK_GBS, 1), "unit": "GB/s",
                    "frac": kd["l2_frac"]},
         "lds": {"achieved": round(tap_gbps, 1), "peak": round(LDS_PEAK_GBS, 1), "unit": "GB/s",
@@ -494,7 +511,7 @@ def brick_roofline(kernels, isolated):
                                "its live duration in the step")
         roofline["alone"] = {"avg_ms": round(iso, 4),
                              "achieved": round(kd["flops"] / (iso * 1e-3) / 1e12, 2),
-                             "frac": round(kd["flops"] / (iso * 1e-3) / 1e12 / FP32_FMA_TFLOPS, 4),
+                             "frac": round(kd["flops"] / (iso * 1e-3) / 1e12 / FP32_VECTOR_TFLOPS, 4),
                              "l2_tap_frac": round(kd["tap_bytes"] / (iso * 1e-3) / 1e9 / L2_PEAK_GBS, 4)}
     if "forward" in kernels and dom != "forward":
         kf = kernels["forward"]
@@ -627,7 +644,7 @@ def main():
             "l2_frac": round(m["tap_bytes"] / (ms * 1e-3) / 1e9 / L2_PEAK_GBS, 4),
             "lds_frac": round(m["tap_bytes"] / (ms * 1e-3) / 1e9 / LDS_PEAK_GBS, 4),
             "hbm_frac": round(m["hbm_bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "alu_frac": round(m["flops"] / (ms * 1e-3) / 1e12 / FP32_FMA_TFLOPS, 4),
+            "alu_frac": round(m["flops"] / (ms * 1e-3) / 1e12 / FP32_VECTOR_TFLOPS, 4),
             **m,
         }
         eprint(f"[bench] kernel {k}: {kernels[k]}")

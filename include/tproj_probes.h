@@ -1,7 +1,8 @@
 /*
  * tproj_probes.h -- C ABI of libtproj_probes.so: microbenchmarks of the
  * bandwidths behind the projection kernels' rooflines on gfx950 (HBM stream
- * read, cache-resident 8-byte gathers, LDS tap reads and 64-bit atomics).
+ * read, cache-resident 8-byte gathers, LDS tap reads and 64-bit atomics,
+ * FP32 FMA issue alone and beside LDS atomics).
  * Measurement only; the projection library does not use them.
  *
  * Every function launches one kernel on `stream` (a hipStream_t, NULL = the
@@ -42,6 +43,18 @@ int tpp_l2_gather(const void* buf, int log2_entries, float* sink, int iters, int
  * visiting its x and z taps in the rotated order that gives lane l the bank
  * pair (l mod 16) plus the step's common offset.                          */
 int tpp_lds_taps(float* sink, int mode, int atomic, int iters, int blocks, void* stream);
+
+/* FP32 VALU issue, alone or beside LDS atomics.
+ * mode 0: each of blocks * 256 threads runs 8 independent FMA chains, 64
+ *         FMAs per iteration (128 flop), `iters` iterations.
+ * modes 1-6: each thread, `iters` times, takes a random 4x4x4 footprint in
+ *         a bank-split 16^3 tile of 8-byte entries (as tpp_lds_taps mode 3)
+ *         and for each of its 64 taps forms a 64-bit word from two FMAs and
+ *         one 64-bit subtraction, plus E further FMAs (E = 0 for modes 1-2,
+ *         2 for 3-4, 6 for 5-6); odd modes add the words to the tile with
+ *         64-bit LDS atomics, even modes form the words and tap indices and
+ *         drop them (no LDS access).                                     */
+int tpp_valu(float* sink, int mode, int iters, int blocks, void* stream);
 
 #ifdef __cplusplus
 }
