@@ -56,6 +56,8 @@ constexpr int BNW = BWD_NW;                 // wavefronts per workgroup of the b
 constexpr int BTHREADS = BNW * 64;
 constexpr int PER_LANE = (TLOG + BTHREADS - 1) / BTHREADS;   // partial-tile entries per thread
 constexpr int WINDOW = 32;                 // poses per fixed-point window
+constexpr int SCALE_BATCH = BTHREADS / WINDOW;   // windows whose scales one pass sets
+static_assert(WINDOW == 32, "a window's scale is reduced over a half wavefront");
 constexpr float FIX_RANGE = 0.9f * 2147483648.0f;
 constexpr int MAX_BANDS = 128;
 
@@ -174,10 +176,10 @@ __device__ __forceinline__ float box_band_max(const KGeom& g, const BwdGrid& bw,
   return m;
 }
 
-// c <- the sum of c over the wavefront, m <- the maximum of m (m >= 0), both
-// uniform: inclusive DPP scans (row shifts, then the row broadcasts of lanes
-// 15 and 31) leave the totals in lane 63.
-__device__ __forceinline__ void window_sum_max(float& c, float& m) {
+// Sum of c and maximum of m (m >= 0) over each 32-lane half of the wavefront:
+// inclusive DPP scans (row shifts, then the broadcast of lane 15 into rows 1
+// and 3) leave lanes 31 and 63 with their half's totals.
+__device__ __forceinline__ void half_sum_max(float& c, float& m) {
 #define TP_SCAN_STEP(CTRL, RM)                                                      \
   c += __int_as_float(dpp_int<CTRL, RM>(0, __float_as_int(c)));                  \
   m = fmaxf(m, __int_as_float(dpp_int<CTRL, RM>(0, __float_as_int(m))));
@@ -186,10 +188,7 @@ __device__ __forceinline__ void window_sum_max(float& c, float& m) {
   TP_SCAN_STEP(0x114, 0xf)
   TP_SCAN_STEP(0x118, 0xf)
   TP_SCAN_STEP(0x142, 0xa)
-  TP_SCAN_STEP(0x143, 0xc)
 #undef TP_SCAN_STEP
-  c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), 63));
-  m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), 63));
 }
 
 __host__ __device__ inline int floor_div(int a, int b) {  // b > 0
@@ -359,7 +358,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
   __shared__ unsigned long long acc_t[DATA ? ASIZE : 1];
   __shared__ unsigned int acc_w[DATA ? 1 : WSIZE];
   __shared__ EnumShared<WINDOW, BNW> es;
-  __shared__ float win_scale;
+  __shared__ float win_scale[SCALE_BATCH];
 
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
@@ -398,29 +397,38 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
   {
     for (int hb = 0; hb < nh; hb += WINDOW) {
       const int nw = min(WINDOW, nh - hb);
-      // the window's fixed-point scale, from every hit's bound on the
-      // contributions to one tap and the largest value it can bring to this
-      // brick (wavefront 0, one hit per lane)
-      window_setup(es, g, rot, DATA ? shifts : nullptr, vsel, e0, hl + hb, nw, bl, bh,
-                   [&](bool valid, const float* R, int pose) {
+      const int wslot = (hb / WINDOW) % SCALE_BATCH;
+      if (wslot == 0) {
+        // the fixed-point scales of the next SCALE_BATCH windows, one hit per
+        // thread: every hit's bound on the contributions to one tap and the
+        // largest value it can bring to this brick, summed and maximised over
+        // each window's 32 hits (a half wavefront)
+        const int i = hb + tid;
         float c = 0.f, m = 0.f;
-        if (valid) {
+        if (i < nh) {
+          int bimg, n;
+          list_entry(g, vsel, e0 + (int)hl[i], bimg, n);
+          const float* Rg = rot + 9 * ((int64_t)(g.Br == 1 ? 0 : bimg) * g.P + n);
+          float R[9];
+#pragma unroll
+          for (int a = 0; a < 9; ++a) R[a] = Rg[a];
           c = weight_sum_bound<NT>(g, R);
-          m = box_band_max(g, bw, R, vmax, pose, bl, bh);
+          m = box_band_max(g, bw, R, vmax, (int64_t)bimg * g.P + n, bl, bh);
         }
-        // window sum of c and maximum of m (DPP scans: lane 63 ends with both)
-        window_sum_max(c, m);
-        if (lane == 0) {
+        half_sum_max(c, m);
+        if ((lane & 31) == 31 && i - 31 < nh) {
           // data: |re|, |im| <= sqrt(2) M per unit weight (the phase
           // rotates), so no sum exceeds lim; every single contribution (weight
           // <= 1) also stays below 2^22 for the magic rounding; the 10 %
           // headroom of FIX_RANGE absorbs the rounding of the window's at most
           // a few thousand contributions per tap
           const float lim = fminf(FIX_RANGE, 0.99f * 4194304.0f * c);
-          win_scale = m > 0.f ? lim / ((DATA ? 1.41421356f : 1.0f) * m * c) : 0.f;
+          win_scale[tid >> 5] = m > 0.f ? lim / ((DATA ? 1.41421356f : 1.0f) * m * c) : 0.f;
         }
-      });
-      const float scale = win_scale;
+        // (window_setup's closing barrier publishes the scales)
+      }
+      window_setup(es, g, rot, DATA ? shifts : nullptr, vsel, e0, hl + hb, nw, bl, bh);
+      const float scale = win_scale[wslot];
       const int nrows = es.hrow[nw];
       for (int qb = 0; qb < nrows;) {
         int nr;
