@@ -437,34 +437,38 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
           constexpr int U = BWD_UNROLL;
           int mpk[U];
           float mf[U][3];
-          float2 mv[U];
-          // look up and load each pixel (and, for padded tiles, move it to its
-          // bank-spreading lane) ...
+          float2 mv[U], mph[U];
+          // look up each pixel and issue its load (and, for padded tiles, move
+          // it to its bank-spreading lane) ...
 #pragma unroll
           for (int u = 0; u < U; ++u) {
             Cand cu;
             cand_prep(es, g, c0 + u * BTHREADS + lane, ncand, lo, bg.S, cu);
-            float2 v = make_float2(0.f, 0.f);
+            // every candidate's element index is in range (0 past the
+            // stage's end), so the load needs no branch: the tap code then
+            // waits for this pixel's value only, not for the next one's
+            float2 v = make_float2(0.f, 0.f), ph = make_float2(1.f, 0.f);
+            if constexpr (DATA) v = Y[cu.k];
+            else v.x = Wimg[cu.k];
             float f[3] = {0.f, 0.f, 0.f};
             int pk = 0, key = -1;
             if (cu.act) {
-              if constexpr (DATA) {
-                v = Y[cu.k];
-                if (shifts) v = cmulc(shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h), v);   // conj(phi) * Y
-              } else {
-                v.x = Wimg[cu.k];
-              }
+              if (DATA && shifts) ph = shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h);
 #pragma unroll
               for (int a = 0; a < 3; ++a) f[a] = cu.p[a] - floorf(cu.p[a]);
               pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
               key = (cu.l[0] + cu.l[1] * TSY + cu.l[2] * TSZ) & 15;
             }
             if constexpr (SPLIT) {
+              // the phase is applied when the taps need the value, so that the
+              // next pixel's lookup and load overlap this one's memory latency
               mpk[u] = pk;
 #pragma unroll
               for (int a = 0; a < 3; ++a) mf[u][a] = f[a];
               mv[u] = v;
+              mph[u] = ph;
             } else {
+              if (DATA && shifts) v = cmulc(ph, v);   // conj(phi) * Y
               const int dest = spread_dest(key);
               mpk[u] = lane_send(pk, dest);
 #pragma unroll
@@ -479,7 +483,8 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
             if constexpr (SPLIT) {
               if (mpk[u] & 1) {
                 const int l[3] = {(mpk[u] >> 1) & 15, (mpk[u] >> 5) & 15, (mpk[u] >> 9) & 15};
-                bwd_scatter_split<CH>(l, mf[u][0], mf[u][1], mf[u][2], mv[u], acc_t, acc_w, scale);
+                const float2 v = DATA && shifts ? cmulc(mph[u], mv[u]) : mv[u];   // conj(phi) * Y
+                bwd_scatter_split<CH>(l, mf[u][0], mf[u][1], mf[u][2], v, acc_t, acc_w, scale);
               }
             } else {
               bwd_scatter<NT, CH>(mpk[u], mf[u][0], mf[u][1], mf[u][2], mv[u], acc_t, acc_w, scale);
