@@ -75,14 +75,14 @@ def op_rates(ms, poses, n_in, tap_bytes_per_pixel, flops_per_pixel):
 # reported when the digest of the 3D kernel sources matches, else null.
 TRAFFIC = {
     # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
-    "forward": {"sources_sha256": "86b5ac93c65c7c32721b0c14e2f244b1e810c5b1fc20d670e9b40805d3b5eb46",
-               "fetch_bytes": 313172728, "write_bytes": 1183378784},
-    "backward": {"sources_sha256": "86b5ac93c65c7c32721b0c14e2f244b1e810c5b1fc20d670e9b40805d3b5eb46",
-                "fetch_bytes": 2901289665, "write_bytes": 271601650},
-    "gradient": {"sources_sha256": "86b5ac93c65c7c32721b0c14e2f244b1e810c5b1fc20d670e9b40805d3b5eb46",
-                "fetch_bytes": 2783835915, "write_bytes": 120424608},
-    "fold": {"sources_sha256": "86b5ac93c65c7c32721b0c14e2f244b1e810c5b1fc20d670e9b40805d3b5eb46",
-            "fetch_bytes": 223225372, "write_bytes": 33390592},
+    "forward": {"sources_sha256": "6f57ff853af294621161080d076e14e8b31fa3f3d8641ab08afc1085dfa4e972",
+               "fetch_bytes": 312976319, "write_bytes": 1183316922},
+    "backward": {"sources_sha256": "6f57ff853af294621161080d076e14e8b31fa3f3d8641ab08afc1085dfa4e972",
+                "fetch_bytes": 3002324895, "write_bytes": 301123556},
+    "gradient": {"sources_sha256": "6f57ff853af294621161080d076e14e8b31fa3f3d8641ab08afc1085dfa4e972",
+                "fetch_bytes": 2783888289, "write_bytes": 120424608},
+    "fold": {"sources_sha256": "6f57ff853af294621161080d076e14e8b31fa3f3d8641ab08afc1085dfa4e972",
+            "fetch_bytes": 223195636, "write_bytes": 33390592},
 }
 
 

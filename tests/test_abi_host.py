@@ -94,7 +94,7 @@ def test_probe_library_exports_its_header():
         build_lib.build()
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "tproj_probes.h")).read(), flags=re.S)
     declared = sorted(set(re.findall(r"^int\s+([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)))
-    assert declared == ["tpp_l2_gather", "tpp_lds_taps", "tpp_stream_read"]
+    assert declared == ["tpp_l2_gather", "tpp_lds_taps", "tpp_stream_read", "tpp_valu"]
     out = subprocess.run(["nm", "-D", "--defined-only", build_lib.PROBES_LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
@@ -103,6 +103,10 @@ def test_probe_library_exports_its_header():
     P.tpp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     assert P.tpp_stream_read(None, 16, None, 1, None) == -1        # rejected on the host, nothing launched
     assert P.tpp_stream_read(ctypes.c_void_p(0x10000), 24, ctypes.c_void_p(0x10000), 1, None) == -1
+    P.tpp_valu.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert P.tpp_valu(None, 0, 1, 1, None) == -1                        # no sink
+    assert P.tpp_valu(ctypes.c_void_p(0x10000), 7, 1, 1, None) == -1   # no such mode
+    assert P.tpp_valu(ctypes.c_void_p(0x10000), 0, 0, 1, None) == -1   # iters
 
 
 def test_abi_version_and_strings(L):
