@@ -7,6 +7,8 @@
 //                    tile in LDS with padded strides (1, 17, 276 entries)
 //                    under controlled bank keys, or in the bank-split layout
 //                    with per-lane rotated tap order
+//   tpp_lds_width    LDS read rate by instruction width (4, 8, 16 bytes per
+//                    lane), conflict-free
 //   tpp_valu         FP32 FMA issue rate (independent chains, no packed
 //                    math), alone or beside bank-split 64-bit LDS atomics
 //                    whose values come from the FMAs (the scatter's mix)
@@ -248,6 +250,36 @@ __global__ void __launch_bounds__(THREADS) k_tap_mix(int iters, float* __restric
   sink[blockIdx.x * THREADS + threadIdx.x] = (float)acc + e[0] + e[1] + e[2] + e[3];
 }
 
+// LDS read width: each lane reads 16 consecutive-lane words of W bytes per
+// iteration (lane l, word j at (l + 64 j + 1024 it) W, wrapped to a 32 KB
+// tile): every access pattern is conflict-free, so the rate is the LDS's
+// delivery rate for that instruction width.
+template <int W>
+__global__ void __launch_bounds__(THREADS) k_lds_width(int iters, float* __restrict__ sink) {
+  constexpr int TB = 32768;
+  __shared__ __align__(16) unsigned char tile[TB];
+  for (int i = threadIdx.x; i < TB / 4; i += THREADS) reinterpret_cast<float*>(tile)[i] = (float)(i & 255);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  float acc = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int off = ((lane + 64 * j + 1024 * it) * W) & (TB - 1);
+      if constexpr (W == 4) {
+        acc += *reinterpret_cast<const float*>(tile + off);
+      } else if constexpr (W == 8) {
+        const float2 v = *reinterpret_cast<const float2*>(tile + off);
+        acc += v.x + v.y;
+      } else {
+        const float4 v = *reinterpret_cast<const float4*>(tile + off);
+        acc += (v.x + v.y) + (v.z + v.w);
+      }
+    }
+  }
+  sink[blockIdx.x * THREADS + threadIdx.x] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -283,6 +315,15 @@ int tpp_lds_taps(float* sink, int mode, int atomic, int iters, int blocks, void*
     else TPP_LDS(3, false);
   }
 #undef TPP_LDS
+  return (int)hipGetLastError();
+}
+
+int tpp_lds_width(float* sink, int width, int iters, int blocks, void* stream) {
+  if (!sink || (width != 4 && width != 8 && width != 16) || iters < 1 || blocks < 1 || blocks > 65535) return -1;
+  const hipStream_t st = (hipStream_t)stream;
+  if (width == 4) hipLaunchKernelGGL((k_lds_width<4>), dim3(blocks), dim3(THREADS), 0, st, iters, sink);
+  else if (width == 8) hipLaunchKernelGGL((k_lds_width<8>), dim3(blocks), dim3(THREADS), 0, st, iters, sink);
+  else hipLaunchKernelGGL((k_lds_width<16>), dim3(blocks), dim3(THREADS), 0, st, iters, sink);
   return (int)hipGetLastError();
 }
 

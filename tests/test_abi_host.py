@@ -94,7 +94,7 @@ def test_probe_library_exports_its_header():
         build_lib.build()
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "tproj_probes.h")).read(), flags=re.S)
     declared = sorted(set(re.findall(r"^int\s+([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)))
-    assert declared == ["tpp_l2_gather", "tpp_lds_taps", "tpp_stream_read", "tpp_valu"]
+    assert declared == ["tpp_l2_gather", "tpp_lds_taps", "tpp_lds_width", "tpp_stream_read", "tpp_valu"]
     out = subprocess.run(["nm", "-D", "--defined-only", build_lib.PROBES_LIB], capture_output=True, text=True,
                          check=True).stdout
     exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
