@@ -7,8 +7,8 @@
 //                    tile in LDS with padded strides (1, 17, 276 entries)
 //                    under controlled bank keys, or in the bank-split layout
 //                    with per-lane rotated tap order
-//   tpp_lds_width    LDS read rate by instruction width (4, 8, 16 bytes per
-//                    lane), conflict-free
+//   tpp_lds_width    LDS read (4, 8, 16 bytes per lane) and integer atomic
+//                    (4, 8 bytes) rates by width, conflict-free
 //   tpp_valu         FP32 FMA issue rate (independent chains, no packed
 //                    math), alone or beside bank-split 64-bit LDS atomics
 //                    whose values come from the FMAs (the scatter's mix)
@@ -250,11 +250,11 @@ __global__ void __launch_bounds__(THREADS) k_tap_mix(int iters, float* __restric
   sink[blockIdx.x * THREADS + threadIdx.x] = (float)acc + e[0] + e[1] + e[2] + e[3];
 }
 
-// LDS read width: each lane reads 16 consecutive-lane words of W bytes per
-// iteration (lane l, word j at (l + 64 j + 1024 it) W, wrapped to a 32 KB
-// tile): every access pattern is conflict-free, so the rate is the LDS's
-// delivery rate for that instruction width.
-template <int W>
+// LDS access width: each lane reads (or, ATOMIC, adds to) 16 consecutive-lane
+// words of W bytes per iteration (lane l, word j at (l + 64 j + 1024 it) W,
+// wrapped to a 32 KB tile): every access pattern is conflict-free, so the
+// rate is the LDS's rate for that instruction width.
+template <int W, bool ATOMIC>
 __global__ void __launch_bounds__(THREADS) k_lds_width(int iters, float* __restrict__ sink) {
   constexpr int TB = 32768;
   __shared__ __align__(16) unsigned char tile[TB];
@@ -266,7 +266,11 @@ __global__ void __launch_bounds__(THREADS) k_lds_width(int iters, float* __restr
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int off = ((lane + 64 * j + 1024 * it) * W) & (TB - 1);
-      if constexpr (W == 4) {
+      if constexpr (ATOMIC && W == 4) {
+        atomicAdd(reinterpret_cast<unsigned int*>(tile + off), 1u);
+      } else if constexpr (ATOMIC) {
+        atomicAdd(reinterpret_cast<unsigned long long*>(tile + off), 1ull);
+      } else if constexpr (W == 4) {
         acc += *reinterpret_cast<const float*>(tile + off);
       } else if constexpr (W == 8) {
         const float2 v = *reinterpret_cast<const float2*>(tile + off);
@@ -276,6 +280,10 @@ __global__ void __launch_bounds__(THREADS) k_lds_width(int iters, float* __restr
         acc += (v.x + v.y) + (v.z + v.w);
       }
     }
+  }
+  if constexpr (ATOMIC) {
+    __syncthreads();
+    acc = *reinterpret_cast<const float*>(tile + 4 * threadIdx.x);
   }
   sink[blockIdx.x * THREADS + threadIdx.x] = acc;
 }
@@ -318,12 +326,20 @@ int tpp_lds_taps(float* sink, int mode, int atomic, int iters, int blocks, void*
   return (int)hipGetLastError();
 }
 
-int tpp_lds_width(float* sink, int width, int iters, int blocks, void* stream) {
-  if (!sink || (width != 4 && width != 8 && width != 16) || iters < 1 || blocks < 1 || blocks > 65535) return -1;
+int tpp_lds_width(float* sink, int width, int atomic, int iters, int blocks, void* stream) {
+  if (!sink || (width != 4 && width != 8 && width != 16) || (atomic && width == 16) || iters < 1 || blocks < 1 ||
+      blocks > 65535)
+    return -1;
   const hipStream_t st = (hipStream_t)stream;
-  if (width == 4) hipLaunchKernelGGL((k_lds_width<4>), dim3(blocks), dim3(THREADS), 0, st, iters, sink);
-  else if (width == 8) hipLaunchKernelGGL((k_lds_width<8>), dim3(blocks), dim3(THREADS), 0, st, iters, sink);
-  else hipLaunchKernelGGL((k_lds_width<16>), dim3(blocks), dim3(THREADS), 0, st, iters, sink);
+  const dim3 g(blocks), b(THREADS);
+  if (atomic) {
+    if (width == 4) hipLaunchKernelGGL((k_lds_width<4, true>), g, b, 0, st, iters, sink);
+    else hipLaunchKernelGGL((k_lds_width<8, true>), g, b, 0, st, iters, sink);
+  } else {
+    if (width == 4) hipLaunchKernelGGL((k_lds_width<4, false>), g, b, 0, st, iters, sink);
+    else if (width == 8) hipLaunchKernelGGL((k_lds_width<8, false>), g, b, 0, st, iters, sink);
+    else hipLaunchKernelGGL((k_lds_width<16, false>), g, b, 0, st, iters, sink);
+  }
   return (int)hipGetLastError();
 }
 

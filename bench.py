@@ -166,11 +166,14 @@ def measure_peaks(torch):
             t = timed(lambda: P.tpp_lds_taps(vp(sink.data_ptr()), mode, atomic, iters, blocks, st))
             key = ("lds_atomic_" if atomic else "lds_read_") + name + "_taps_per_clk_cu"
             out[key] = round(blocks * 256 * iters * 64 / t / clk, 2)
-    P.tpp_lds_width.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
-    for width in (4, 8, 16):
+    P.tpp_lds_width.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    for width, atomic in ((4, 0), (8, 0), (16, 0), (4, 1), (8, 1)):
         iters = 64
-        t = timed(lambda: P.tpp_lds_width(vp(sink.data_ptr()), width, iters, blocks, st))
-        out[f"lds_read_b{8 * width}_bytes_per_clk_cu"] = round(blocks * 256 * iters * 16 * width / t / clk, 1)
+        t = timed(lambda: P.tpp_lds_width(vp(sink.data_ptr()), width, atomic, iters, blocks, st))
+        if atomic:
+            out[f"lds_atomic_u{8 * width}_lanes_per_clk_cu"] = round(blocks * 256 * iters * 16 / t / clk, 2)
+        else:
+            out[f"lds_read_b{8 * width}_bytes_per_clk_cu"] = round(blocks * 256 * iters * 16 * width / t / clk, 1)
     P.tpp_valu.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
     iters = 256
     t = timed(lambda: P.tpp_valu(vp(sink.data_ptr()), 0, iters, blocks, st))

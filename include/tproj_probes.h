@@ -44,10 +44,11 @@ int tpp_l2_gather(const void* buf, int log2_entries, float* sink, int iters, int
  * pair (l mod 16) plus the step's common offset.                          */
 int tpp_lds_taps(float* sink, int mode, int atomic, int iters, int blocks, void* stream);
 
-/* LDS read rate by width: each of blocks * 256 threads, `iters` times,
- * reads 16 words of `width` bytes (4, 8 or 16) from a 32 KB tile, the lanes
+/* LDS rate by access width: each of blocks * 256 threads, `iters` times,
+ * reads 16 words of `width` bytes (4, 8 or 16) from a 32 KB tile, or with
+ * atomic != 0 adds 1 to them with integer atomics (width 4 or 8), the lanes
  * of a wavefront at consecutive words (conflict-free).                     */
-int tpp_lds_width(float* sink, int width, int iters, int blocks, void* stream);
+int tpp_lds_width(float* sink, int width, int atomic, int iters, int blocks, void* stream);
 
 /* FP32 VALU issue, alone or beside LDS atomics.
  * mode 0: each of blocks * 256 threads runs 8 independent FMA chains, 64
