@@ -23,11 +23,17 @@ size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights);
 
 // Writes vol (and wvol when Wimg != NULL) completely with the adjoint of the
 // forward (the back-projection of Y, and of the weight images Wimg).
-// after_bands (optional) is recorded on st once the band maxima are queued,
-// i.e. just before the brick kernel.
+// side (optional): a second stream and two events on which the band-maximum
+// pass runs beside the work list and hit lists (st forks to it first and
+// joins it before the brick kernels); the caller keeps each record / wait
+// pair of the events together.
+struct SideRef {
+  hipStream_t s;
+  hipEvent_t fork, join;
+};
 hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* workspace, const float2* Y,
                       const float* Wimg, const float* rot, const float* shifts, float2* vol, float* wvol,
                       hipStream_t st, const EvPair* ev_brick = nullptr, const EvPair* ev_fold = nullptr,
-                      hipEvent_t after_bands = nullptr);
+                      const SideRef* side = nullptr);
 
 }  // namespace tproj

@@ -847,7 +847,7 @@ size_t bwd_ws_bytes(const BwdGrid& bw, int Bv, bool weights) {
 
 hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* workspace, const float2* Y,
                       const float* Wimg, const float* rot, const float* shifts, float2* vol, float* wvol,
-                      hipStream_t st, const EvPair* ev_brick, const EvPair* ev_fold, hipEvent_t after_bands) {
+                      hipStream_t st, const EvPair* ev_brick, const EvPair* ev_fold, const SideRef* side) {
   const bool weights = Wimg != nullptr;
   const BrickWork wk = brick_work(bw.bg, g.Bv, workspace);
   int* prefix = wk.prefix;
@@ -857,7 +857,23 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
   const size_t off_p = off_b + align256((size_t)bw.npose * bw.nbands * sizeof(float) * (weights ? 2 : 1));
   float2* part_c = (float2*)((char*)workspace + off_p);
   float* part_w = (float*)(part_c + (size_t)bw.bg.nwork * g.Bv * TLOG);
-  hipError_t e = launch_brick_prefix(bw.bg, prefix, st);
+  hipError_t e = hipSuccess;
+  // the band maxima read only the images: on the side stream they overlap the
+  // work list and the hit lists (HBM-bound beside latency-bound work)
+  hipStream_t sb = st;
+  if (side) {
+    e = hipEventRecord(side->fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return e;
+    sb = side->s;
+  }
+  const int nb = bw.npose < 65535 ? bw.npose : 65535;
+  if (weights) hipLaunchKernelGGL((k_band_max<true>), dim3(nb), dim3(256), 0, sb, Y, Wimg, ymax, wmax, g, bw);
+  else hipLaunchKernelGGL((k_band_max<false>), dim3(nb), dim3(256), 0, sb, Y, Wimg, ymax, wmax, g, bw);
+  e = hipGetLastError();
+  if (e == hipSuccess && side) e = hipEventRecord(side->join, side->s);
+  if (e != hipSuccess) return e;
+  e = launch_brick_prefix(bw.bg, prefix, st);
   if (e != hipSuccess) return e;
   if (bw.bg.nwork > 0) {
     const dim3 grid(bw.bg.nwork, g.Bv);
@@ -866,12 +882,10 @@ hipError_t launch_bwd(const KGeom& g, int interp, const BwdGrid& bw, void* works
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int nb = bw.npose < 65535 ? bw.npose : 65535;
-  if (weights) hipLaunchKernelGGL((k_band_max<true>), dim3(nb), dim3(256), 0, st, Y, Wimg, ymax, wmax, g, bw);
-  else hipLaunchKernelGGL((k_band_max<false>), dim3(nb), dim3(256), 0, st, Y, Wimg, ymax, wmax, g, bw);
-  e = hipGetLastError();
-  if (e == hipSuccess && after_bands) e = hipEventRecord(after_bands, st);
-  if (e != hipSuccess) return e;
+  if (side) {
+    e = hipStreamWaitEvent(st, side->join, 0);
+    if (e != hipSuccess) return e;
+  }
   const dim3 blk(256);
   ev_begin(ev_brick, st);   // recorded even when no brick kernel runs
   if (bw.bg.nwork > 0) {

@@ -404,14 +404,14 @@ tp_status run_forward_real(const tp_geom* geom, const tproj::KGeom& k, const flo
 }
 
 // Back-projection of Y (and of the weight images Wimg into wvol): bricks,
-// else zeroed volumes and direct atomics.  fork (optional) is recorded on st
-// before the main scatter kernel.
+// else zeroed volumes and direct atomics.  may_split: the caller does not use
+// the side stream in this call, so the band maxima may run on it (large calls
+// only, never under graph capture).
 tp_status run_bwd(const tp_geom* geom, const tproj::KGeom& k, const float2* Y, const float* Wimg, const float* rot,
                   const float* shifts, float2* vol, float* wvol, void* workspace, size_t ws_bytes, hipStream_t st,
-                  hipEvent_t fork = nullptr) {
+                  bool may_split = false) {
   const BwdPlan pl = bwd_plan(geom, Wimg != nullptr);
   if (!pl.ok) {
-    if (fork) LAUNCH(hipEventRecord(fork, st), "stream fork");
     LAUNCH(tproj::launch_zero((float*)vol, 2 * vol_elems(geom) * geom->Bv, st), "zero volume");
     if (wvol) LAUNCH(tproj::launch_zero(wvol, vol_elems(geom) * geom->Bv, st), "zero weight volume");
     LAUNCH(tproj::launch_spread_atomic(k, geom->interp, Y, Wimg, rot, shifts, vol, wvol, st), "scatter");
@@ -420,8 +420,18 @@ tp_status run_bwd(const tp_geom* geom, const tproj::KGeom& k, const float2* Y, c
   if (!workspace || ws_bytes < pl.ws_bytes)
     return fail(TP_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, pl.ws_bytes);
   const tproj::EvPair eb = kt_copy(TP_KT_BACKWARD), ef = kt_copy(TP_KT_FOLD);
+  if (may_split && worth_splitting(geom, 20, st)) {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    if (SideStream* ss = side_stream()) {
+      const tproj::SideRef side{ss->s, ss->fork, ss->join};
+      LAUNCH(tproj::launch_bwd(k, geom->interp, pl.bw, workspace, Y, Wimg, rot, shifts, vol, wvol, st,
+                               eb.a ? &eb : nullptr, ef.a ? &ef : nullptr, &side),
+             "back-projection (bricks)");
+      return TP_OK;
+    }
+  }
   LAUNCH(tproj::launch_bwd(k, geom->interp, pl.bw, workspace, Y, Wimg, rot, shifts, vol, wvol, st,
-                           eb.a ? &eb : nullptr, ef.a ? &ef : nullptr, fork),
+                           eb.a ? &eb : nullptr, ef.a ? &ef : nullptr),
          "back-projection (bricks)");
   return TP_OK;
 }
@@ -674,10 +684,11 @@ tp_status project_3d_to_2d_backward(const tp_geom* geom, const void* grad_out, c
       return ok();
     }
   }
-  // one after the other on the caller's stream
+  // one after the other on the caller's stream (the band maxima on the side
+  // stream when nothing else uses it)
   if (grad_vol)
     TRY(run_bwd(geom, k, (const float2*)grad_out, nullptr, rot, shifts, (float2*)grad_vol, nullptr, workspace,
-                ws_bytes, st));
+                ws_bytes, st, !grads));
   if (grads)
     TRY(run_grads(geom, k, (const float2*)vol, nullptr, (const float2*)grad_out, nullptr, rot, shifts, grad_rot,
                   grad_shifts, workspace, ws_bytes, st));
@@ -703,7 +714,7 @@ tp_status backproject_2d_to_3d(const tp_geom* geom, const void* images, const fl
   const tproj::KGeom k = kgeom(geom);
   hipStream_t st = (hipStream_t)stream;
   TRY(run_bwd(geom, k, (const float2*)images, weights, rot, shifts, (float2*)data_vol, weight_vol, workspace,
-              ws_bytes, st));
+              ws_bytes, st, true));
   return ok();
 }
 
