@@ -38,21 +38,24 @@ namespace tproj {
 // ---------------------------------------------------------------------------
 // prefix[0..nb3]: running sums of the bricks' chunk counts; prefix[nb3 + 1 +
 // b]: the active rank of brick b (bricks with chunks before it).  One
-// workgroup; both sums in one 64-bit scan (chunks low, bricks high).
+// workgroup; both sums in one 64-bit scan (chunks low, bricks high).  The
+// chunk counts (64-bit divisions) are computed first, with no barrier
+// between bricks, into prefix[b + 1]; the scan then reads them back (the
+// thread that wrote an entry is the one that reads and overwrites it).
 __global__ void __launch_bounds__(1024) k_brick_prefix(BrickGrid bg, int* __restrict__ prefix) {
   __shared__ long long warp_tot[16];
   __shared__ long long carry;
+  for (int b = threadIdx.x; b < bg.nb3; b += 1024) {
+    int bi, bj, bk;
+    brick_coords(bg, b, bi, bj, bk);
+    prefix[b + 1] = brick_chunks(bg, bi, bj, bk);
+  }
   if (threadIdx.x == 0) { carry = 0; prefix[0] = 0; }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int base = 0; base < bg.nb3; base += 1024) {
     const int b = base + threadIdx.x;
-    int k = 0;
-    if (b < bg.nb3) {
-      int bi, bj, bk;
-      brick_coords(bg, b, bi, bj, bk);
-      k = brick_chunks(bg, bi, bj, bk);
-    }
+    const int k = b < bg.nb3 ? prefix[b + 1] : 0;
     const long long own = (long long)k + (k > 0 ? (1ll << 32) : 0ll);
     long long v = own;
 #pragma unroll
