@@ -75,14 +75,14 @@ def op_rates(ms, poses, n_in, tap_bytes_per_pixel, flops_per_pixel):
 # reported when the digest of the 3D kernel sources matches, else null.
 TRAFFIC = {
     # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
-    "forward": {"sources_sha256": "6f57ff853af294621161080d076e14e8b31fa3f3d8641ab08afc1085dfa4e972",
-               "fetch_bytes": 312976319, "write_bytes": 1183316922},
-    "backward": {"sources_sha256": "6f57ff853af294621161080d076e14e8b31fa3f3d8641ab08afc1085dfa4e972",
-                "fetch_bytes": 3002324895, "write_bytes": 301123556},
-    "gradient": {"sources_sha256": "6f57ff853af294621161080d076e14e8b31fa3f3d8641ab08afc1085dfa4e972",
-                "fetch_bytes": 2783888289, "write_bytes": 120424608},
-    "fold": {"sources_sha256": "6f57ff853af294621161080d076e14e8b31fa3f3d8641ab08afc1085dfa4e972",
-            "fetch_bytes": 223195636, "write_bytes": 33390592},
+    "forward": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
+               "fetch_bytes": 313328357, "write_bytes": 1183363373},
+    "backward": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
+                "fetch_bytes": 3003352158, "write_bytes": 301123584},
+    "gradient": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
+                "fetch_bytes": 2783904331, "write_bytes": 120424608},
+    "fold": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
+            "fetch_bytes": 223195806, "write_bytes": 33390592},
 }
 
 
