@@ -57,7 +57,7 @@ FLOPS_PER_PIXEL_CUBIC_REAL = {"forward": 2 * 84, "gradient": 2 * 192, "backward"
 
 def op_rates(ms, poses, n_in, tap_bytes_per_pixel, flops_per_pixel):
     """ms, proj/s, tap-delivery rate and fraction of the L2 figure, and (when
-    a flop model is given) TFLOP/s and fraction of the fp32 FMA ceiling."""
+    a flop model is given) TFLOP/s and fraction of the fp32 vector peak."""
     sec = ms * 1e-3
     r = {"ms": round(ms, 4), "proj_per_s": round(poses / sec, 1),
          "tap_GBps": round(poses * n_in * tap_bytes_per_pixel / sec / 1e9, 1),
