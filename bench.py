@@ -85,6 +85,35 @@ TRAFFIC = {
             "fetch_bytes": 223195806, "write_bytes": 33390592},
 }
 
+# VALU issue per kernel class, from the SQ counter pass of the same sessions
+# (SQ_INSTS_VALU / SQ_BUSY_CU_CYCLES: wave64 VALU instructions per CU clock),
+# valid for the same kernel sources digest as the traffic figures.  A CU
+# issues at most 2 per clock (4 SIMDs, a wave64 fp32 instruction every two
+# clocks); the FMA probe of --peaks reaches 1.72.
+VALU_ISSUE = {
+    # profiles/brick_kernels_D128_cubic_counters.txt
+    "forward": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
+                "valu_per_cu_clock": 1.111},
+    "backward": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
+                 "valu_per_cu_clock": 0.847},
+    "gradient": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
+                 "valu_per_cu_clock": 1.355},
+}
+VALU_ISSUE_PEAK = 2.0
+VALU_ISSUE_PROBE = 1.72
+
+
+def valu_issue(kclass):
+    """The kernel class's counter-measured VALU issue rate against the CU's
+    issue limit, or None once the kernel sources have changed."""
+    t = VALU_ISSUE.get(kclass)
+    if not t or t["sources_sha256"] != sources_digest():
+        return None
+    a = t["valu_per_cu_clock"]
+    return {"achieved": a, "peak": VALU_ISSUE_PEAK, "probe": VALU_ISSUE_PROBE,
+            "unit": "wave64 VALU instructions per CU clock", "frac": round(a / VALU_ISSUE_PEAK, 4),
+            "scope": "kernel alone (the counter passes run one kernel at a time)"}
+
 
 def sources_digest():
     """Digest of the sources the 3D kernels are built and launched from (the
@@ -512,6 +541,7 @@ def brick_roofline(kernels, isolated):
         "lds": {"achieved": round(tap_gbps, 1), "peak": round(LDS_PEAK_GBS, 1), "unit": "GB/s",
                 "frac": kd["lds_frac"]},
         "hbm": {"achieved": round(kd["hbm_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": kd["hbm_frac"]},
+        "valu_issue": valu_issue(dom),
     }
     if dom in isolated:
         iso = isolated[dom]
@@ -525,7 +555,7 @@ def brick_roofline(kernels, isolated):
         kf = kernels["forward"]
         roofline["forward"] = {"avg_ms": kf["avg_ms"], "tflops": kf["tflops"], "alu_frac": kf["alu_frac"],
                                "l2_tap_frac": kf["l2_frac"], "lds_frac": kf["lds_frac"],
-                               "traffic": measured_traffic("forward")}
+                               "traffic": measured_traffic("forward"), "valu_issue": valu_issue("forward")}
     return roofline
 
 

@@ -45,6 +45,15 @@ def test_traffic_is_null_when_the_sources_changed(bench, monkeypatch):
     assert bench.measured_traffic("no-such-kernel") is None
 
 
+def test_valu_issue_follows_the_digest(bench, monkeypatch):
+    real = bench.sources_digest()
+    monkeypatch.setattr(bench, "VALU_ISSUE", {"gradient": {"sources_sha256": real, "valu_per_cu_clock": 1.5}})
+    v = bench.valu_issue("gradient")
+    assert v["achieved"] == 1.5 and v["peak"] == 2.0 and v["frac"] == pytest.approx(0.75)
+    monkeypatch.setattr(bench, "VALU_ISSUE", {"gradient": {"sources_sha256": "0" * 64, "valu_per_cu_clock": 1.5}})
+    assert bench.valu_issue("gradient") is None
+
+
 def _kernel(avg_ms, flops, tap_bytes, launches=20):
     return {"avg_ms": avg_ms, "launches": launches, "flops": flops, "flops_per_pixel": 768, "tap_bytes": tap_bytes,
             "l2_frac": 0.5, "lds_frac": 0.25, "hbm_GBps": 100.0, "hbm_frac": 0.0125, "tflops": 1.0,
@@ -64,7 +73,7 @@ def test_roofline_object(bench):
     assert r["alone"]["frac"] == pytest.approx(8.0e10 / 2.0e-3 / 1e12 / bench.FP32_VECTOR_TFLOPS, rel=1e-3)
     assert r["l2_tap"]["achieved"] == pytest.approx(5.0e10 / 4.0e-3 / 1e9, rel=1e-3)
     assert r["forward"]["avg_ms"] == 1.0
-    for key in ("achieved", "peak", "frac", "traffic"):
+    for key in ("achieved", "peak", "frac", "traffic", "valu_issue"):
         assert key in r
 
 
