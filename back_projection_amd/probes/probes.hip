@@ -11,7 +11,9 @@
 //                    (4, 8 bytes) rates by width, conflict-free
 //   tpp_valu         FP32 FMA issue rate (independent chains, no packed
 //                    math), alone or beside bank-split 64-bit LDS atomics
-//                    whose values come from the FMAs (the scatter's mix)
+//                    whose values come from the FMAs (the scatter's mix);
+//                    the issue rates of integer add, bitwise select,
+//                    compare-and-select and 64-bit add chains
 // Each kernel folds what it reads into one float per thread (sink), so that
 // nothing is optimised away.  Argument checks on the host; -1 on bad input,
 // else the HIP status of the launch.
@@ -194,6 +196,43 @@ __global__ void __launch_bounds__(THREADS) k_valu_fma(int iters, float* __restri
   sink[t] = s;
 }
 
+// Issue rate of one non-FP32 VALU instruction kind: 8 independent chains per
+// thread, 64 operations per iteration; an empty asm statement after each
+// operation keeps every step in a register, so the chains are not folded.
+// KIND 0: 32-bit integer add (v_add_u32); 1: bitwise select (v_and_b32 +
+// v_and_or_b32, two instructions); 2: compare and select (v_cmp +
+// v_cndmask_b32, two instructions); 3: 64-bit add (v_lshl_add_u64).
+template <int KIND>
+__global__ void __launch_bounds__(THREADS) k_valu_int(int iters, float* __restrict__ sink) {
+  const unsigned t = blockIdx.x * THREADS + threadIdx.x;
+  unsigned a[8];
+  unsigned long long q[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    a[j] = mix(t * 8u + (unsigned)j);
+    q[j] = ((unsigned long long)a[j] << 32) | (unsigned long long)(t + j);
+  }
+  const unsigned m = mix(t) | 0x0f0f0f0fu, c = 0x5555u + (t & 15u);
+  const unsigned long long c64 = 0x0000000100000003ull + (unsigned long long)(t & 7u);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (KIND == 0) a[j] = a[j] + c;
+        if constexpr (KIND == 1) a[j] = (a[j] & m) | (a[(j + 1) & 7] & ~m);
+        if constexpr (KIND == 2) a[j] = (int)a[j] < (int)c ? a[(j + 3) & 7] : m;
+        if constexpr (KIND == 3) q[j] = q[j] + c64;
+        if constexpr (KIND == 3) asm volatile("" : "+v"(q[j]));
+        else asm volatile("" : "+v"(a[j]));
+      }
+  }
+  unsigned s = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += a[j] + (unsigned)(q[j] >> 11);
+  sink[t] = (float)s;
+}
+
 // The scatter's tap mix: per 4x4x4 footprint in a bank-split 16^3 tile of
 // 8-byte entries (random bases, rotated per-lane tap order, as mode 3 of
 // k_lds_taps), each tap's word comes from two magic-number FMAs packed with
@@ -344,7 +383,7 @@ int tpp_lds_width(float* sink, int width, int atomic, int iters, int blocks, voi
 }
 
 int tpp_valu(float* sink, int mode, int iters, int blocks, void* stream) {
-  if (!sink || mode < 0 || mode > 6 || iters < 1 || blocks < 1 || blocks > 65535) return -1;
+  if (!sink || mode < 0 || mode > 10 || iters < 1 || blocks < 1 || blocks > 65535) return -1;
   const hipStream_t st = (hipStream_t)stream;
 #define TPP_MIX(E, A) hipLaunchKernelGGL((k_tap_mix<E, A>), dim3(blocks), dim3(THREADS), 0, st, iters, sink)
   switch (mode) {
@@ -354,7 +393,11 @@ int tpp_valu(float* sink, int mode, int iters, int blocks, void* stream) {
     case 3: TPP_MIX(2, true); break;
     case 4: TPP_MIX(2, false); break;
     case 5: TPP_MIX(6, true); break;
-    default: TPP_MIX(6, false); break;
+    case 6: TPP_MIX(6, false); break;
+    case 7: hipLaunchKernelGGL((k_valu_int<0>), dim3(blocks), dim3(THREADS), 0, st, iters, sink); break;
+    case 8: hipLaunchKernelGGL((k_valu_int<1>), dim3(blocks), dim3(THREADS), 0, st, iters, sink); break;
+    case 9: hipLaunchKernelGGL((k_valu_int<2>), dim3(blocks), dim3(THREADS), 0, st, iters, sink); break;
+    default: hipLaunchKernelGGL((k_valu_int<3>), dim3(blocks), dim3(THREADS), 0, st, iters, sink); break;
   }
 #undef TPP_MIX
   return (int)hipGetLastError();

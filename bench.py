@@ -208,6 +208,13 @@ def measure_peaks(torch):
     t = timed(lambda: P.tpp_valu(vp(sink.data_ptr()), 0, iters, blocks, st))
     out["fp32_fma_TFLOPs"] = round(blocks * 256 * iters * 128 / t / 1e12, 2)
     out["fp32_fma_wave_insts_per_clk_cu"] = round(blocks * 4 * iters * 64 / t / clk, 3)
+    # non-FP32 VALU issue: wave64 instructions per CU clock for one kind at a
+    # time (the select kinds take two instructions per operation)
+    iters = 256
+    for mode, name, insts in ((7, "int_add", 1), (8, "bitwise_select", 2), (9, "cmp_cndmask", 2),
+                              (10, "add_u64", 1)):
+        t = timed(lambda: P.tpp_valu(vp(sink.data_ptr()), mode, iters, blocks, st))
+        out[f"{name}_wave_insts_per_clk_cu"] = round(blocks * 4 * iters * 64 * insts / t / clk, 3)
     # the scatter's mix: taps per clock per CU with and without the atomics
     iters = 32
     for mode, extra, atomic in ((1, 0, True), (2, 0, False), (3, 2, True), (4, 2, False), (5, 6, True),

@@ -2,7 +2,7 @@
  * tproj_probes.h -- C ABI of libtproj_probes.so: microbenchmarks of the
  * bandwidths behind the projection kernels' rooflines on gfx950 (HBM stream
  * read, cache-resident 8-byte gathers, LDS tap reads and 64-bit atomics,
- * FP32 FMA issue alone and beside LDS atomics).
+ * FP32 FMA issue alone and beside LDS atomics, integer VALU issue).
  * Measurement only; the projection library does not use them.
  *
  * Every function launches one kernel on `stream` (a hipStream_t, NULL = the
@@ -59,7 +59,12 @@ int tpp_lds_width(float* sink, int width, int atomic, int iters, int blocks, voi
  *         one 64-bit subtraction, plus E further FMAs (E = 0 for modes 1-2,
  *         2 for 3-4, 6 for 5-6); odd modes add the words to the tile with
  *         64-bit LDS atomics, even modes form the words and tap indices and
- *         drop them (no LDS access).                                     */
+ *         drop them (no LDS access).
+ * modes 7-10: each thread runs 8 independent chains of one non-FP32 VALU
+ *         operation, 64 per iteration: 7 a 32-bit integer add (one
+ *         v_add_u32), 8 a bitwise select (v_and_b32 + v_and_or_b32), 9 a
+ *         compare and select (v_cmp + v_cndmask_b32), 10 a 64-bit add (one
+ *         v_lshl_add_u64).                                               */
 int tpp_valu(float* sink, int mode, int iters, int blocks, void* stream);
 
 #ifdef __cplusplus

@@ -105,7 +105,8 @@ def test_probe_library_exports_its_header():
     assert P.tpp_stream_read(ctypes.c_void_p(0x10000), 24, ctypes.c_void_p(0x10000), 1, None) == -1
     P.tpp_valu.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     assert P.tpp_valu(None, 0, 1, 1, None) == -1                        # no sink
-    assert P.tpp_valu(ctypes.c_void_p(0x10000), 7, 1, 1, None) == -1   # no such mode
+    assert P.tpp_valu(ctypes.c_void_p(0x10000), 11, 1, 1, None) == -1  # no such mode
+    assert P.tpp_valu(ctypes.c_void_p(0x10000), -1, 1, 1, None) == -1  # no such mode
     assert P.tpp_valu(ctypes.c_void_p(0x10000), 0, 0, 1, None) == -1   # iters
 
 
