@@ -239,6 +239,53 @@ __device__ __forceinline__ void split_taps_bytes(const int l[3], SplitTaps& s) {
   }
 }
 
+// The same tap order from two lane tables in LDS (byte offsets of 8-byte
+// entries), so that a pixel's 8 offsets cost two 16-byte LDS reads and a few
+// adds instead of per-step residue arithmetic and selects (which issue at
+// half the rate of FP32 FMAs): for lane slot u and x4 = l0 & 3, x[4 u + x4]
+// holds 8 (s + 16 [s < x4]) for the steps j = 0..3, s = (u + j) & 3, so the
+// step-j x tap of a pixel whose first tap is l0 lies at 128 (l0 >> 2) plus
+// that entry; z[4 v + z4] likewise holds 8 (4 s + 1024 [s < z4]) with
+// s = (v + j) & 3, added to 8192 (l2 >> 2) + 512 l1.
+struct SplitLut {
+  int4 x[16];
+  int4 z[16];
+};
+
+// Threads 0..31 write the tables; the caller's next barrier publishes them.
+__device__ __forceinline__ void split_lut_fill(SplitLut& t) {
+  const int i = (int)threadIdx.x;
+  if (i < 32) {
+    const int k = i & 15, u = k >> 2, r4 = k & 3;
+    int e[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sres = (u + j) & 3;
+      e[j] = i < 16 ? 8 * (sres + (sres < r4 ? 16 : 0)) : 8 * (4 * sres + (sres < r4 ? 1024 : 0));
+    }
+    const int4 v = make_int4(e[0], e[1], e[2], e[3]);
+    if (i < 16) t.x[k] = v;
+    else t.z[k] = v;
+  }
+}
+
+__device__ __forceinline__ void split_taps_lut(const SplitLut& lut, const int l[3], SplitTaps& s) {
+  const int lane = (int)threadIdx.x;
+  const int u = lane & 3, v = (lane >> 2) & 3;
+  s.t = (u - l[0]) & 3;
+  s.r = (v - l[2]) & 3;
+  const int4 xr = lut.x[4 * u + (l[0] & 3)], zr = lut.z[4 * v + (l[2] & 3)];
+  const int bx = (l[0] >> 2) * 128, bz = (l[2] >> 2) * 8192 + l[1] * 512;
+  s.xo[0] = bx + xr.x;
+  s.xo[1] = bx + xr.y;
+  s.xo[2] = bx + xr.z;
+  s.xo[3] = bx + xr.w;
+  s.zo[0] = bz + zr.x;
+  s.zo[1] = bz + zr.y;
+  s.zo[2] = bz + zr.z;
+  s.zo[3] = bz + zr.w;
+}
+
 // floor(p) relative to the brick's low corner; true if inside [0, S)^3.
 __device__ __forceinline__ bool owned(const float p[3], const int lo[3], int S, int l[3]) {
   bool in = true;
@@ -349,15 +396,22 @@ __device__ __forceinline__ void interp_tile_w(const T* tile, const int l[3], con
 // the axis weights (and derivatives) in tap order.  Contracts y within each
 // column, then x within each plane, then z.
 template <bool DERIV, typename T>
-__device__ __forceinline__ void interp_split(const T* tile, const int l[3], const float wx_in[4], const float wy[4],
-                                             const float wz_in[4], const float dx_in[4], const float dy[4],
-                                             const float dz_in[4], T& I, T* dI) {
+__device__ __forceinline__ void interp_split(const T* tile, const SplitLut& lut, const int l[3], const float wx_in[4],
+                                             const float wy[4], const float wz_in[4], const float dx_in[4],
+                                             const float dy[4], const float dz_in[4], T& I, T* dI) {
   // tap offsets: in bytes for the value-only gather (fewer instructions, a
   // few more registers), in entries for the derivative gather, which has no
   // registers to spare (measured: the byte form made it 4 % slower)
+  static_assert(sizeof(T) == 8 || sizeof(T) == 4, "complex or real tile entries");
   SplitTaps st;
-  if constexpr (DERIV) split_taps(l, st);
-  else split_taps_bytes<(int)sizeof(T)>(l, st);
+  split_taps_lut(lut, l, st);
+  if constexpr (sizeof(T) == 4) {   // the tables hold offsets of 8-byte entries
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      st.xo[j] >>= 1;
+      st.zo[j] >>= 1;
+    }
+  }
   float wx[4], wz[4], dx[4], dz[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -380,8 +434,7 @@ __device__ __forceinline__ void interp_split(const T* tile, const int l[3], cons
     T p = z0, px = z0, py = z0;   // plane sums: wx*q, dx*q, wx*qy
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const T* col = DERIV ? tile + st.xo[a] + st.zo[c]
-                           : reinterpret_cast<const T*>(reinterpret_cast<const char*>(tile) + st.xo[a] + st.zo[c]);
+      const T* col = reinterpret_cast<const T*>(reinterpret_cast<const char*>(tile) + st.xo[a] + st.zo[c]);
       T q = z0, qy = z0;          // column sums: wy*v, dy*v
 #pragma unroll
       for (int b = 0; b < 4; ++b) {

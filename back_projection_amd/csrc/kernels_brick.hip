@@ -108,6 +108,7 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
   constexpr bool CPLX = sizeof(T) == 8;
   __shared__ T tile[Tl::SIZE];
   __shared__ EnumShared<FWD_WIN<NT>, FWD_NW> es;
+  __shared__ std::conditional_t<Tl::SPLIT, SplitLut, char> lut;   // tap tables of the bank-split tile
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
   const int nh = counts[(int64_t)vsel * bg.nwork + w];
@@ -121,6 +122,7 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
   const int lo[3] = {bg.origin + bi * bg.S, bg.origin + bj * bg.S, bg.origin + bk * bg.S};
   const float bl[3] = {(float)lo[0], (float)lo[1], (float)lo[2]};
   const float bh[3] = {(float)(lo[0] + bg.S), (float)(lo[1] + bg.S), (float)(lo[2] + bg.S)};
+  if constexpr (Tl::SPLIT) split_lut_fill(lut);
   stage_tile_t<NT, FWD_NW * 64>(tile, vol + (int64_t)vsel * g.D * g.D * g.W, g, lo);
   __syncthreads();
 
@@ -144,7 +146,7 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
               axis_weights<4>(cu.p[1] - floorf(cu.p[1]), wy);
               axis_weights<4>(cu.p[2] - floorf(cu.p[2]), wz);
               T I;
-              interp_split<false>(tile, cu.l, wx, wy, wz, wx, wy, wz, I, (T*)nullptr);
+              interp_split<false>(tile, lut, cu.l, wx, wy, wz, wx, wy, wz, I, (T*)nullptr);
               if constexpr (CPLX) {
                 if (shifts) I = cmul(shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h), I);
               }
@@ -260,6 +262,7 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
   constexpr int WIN = GRAD_WIN<NT>;
   __shared__ EnumShared<WIN, GRAD_NW> es;
   __shared__ float gw[WIN][8];
+  __shared__ std::conditional_t<Tl::SPLIT, SplitLut, char> lut;   // tap tables of the bank-split tile
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
   const int nh = counts[(int64_t)vsel * bg.nwork + w];
@@ -277,6 +280,7 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
   if constexpr (CPLX) stage_tile_t<NT, GRAD_NW * 64>(tc, volc + (int64_t)vsel * nvol, g, lo);
   if constexpr (REAL) stage_tile_t<NT, GRAD_NW * 64>(tr, volr + (int64_t)vsel * nvol, g, lo);
   for (int i = threadIdx.x; i < WIN * 8; i += GRAD_NW * 64) (&gw[0][0])[i] = 0.f;
+  if constexpr (Tl::SPLIT) split_lut_fill(lut);
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -309,8 +313,8 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
               axis_dweights<4>(fx, dx);
               axis_dweights<4>(fy, dy);
               axis_dweights<4>(fz, dz);
-              if constexpr (CPLX) interp_split<true>(tc, cu.l, wx, wy, wz, dx, dy, dz, Ic, dIc);
-              if constexpr (REAL) interp_split<true>(tr, cu.l, wx, wy, wz, dx, dy, dz, Ir, dIr);
+              if constexpr (CPLX) interp_split<true>(tc, lut, cu.l, wx, wy, wz, dx, dy, dz, Ic, dIc);
+              if constexpr (REAL) interp_split<true>(tr, lut, cu.l, wx, wy, wz, dx, dy, dz, Ir, dIr);
             }
           } else {
             float f[3] = {0.f, 0.f, 0.f};

@@ -309,21 +309,22 @@ __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz
 // above.  The y weights are folded into the value once per row, the x and z
 // weights once per column.
 template <int CH>
-__device__ __forceinline__ void bwd_scatter_split(const int l[3], float fx, float fy, float fz, float2 v,
-                                                  unsigned long long* acc_t, unsigned int* acc_w, float scale) {
+__device__ __forceinline__ void bwd_scatter_split(const SplitLut& lut, const int l[3], float fx, float fy, float fz,
+                                                  float2 v, unsigned long long* acc_t, unsigned int* acc_w,
+                                                  float scale) {
   float wx[4], wy[4], wz[4];
   axis_weights<4>(fx, wx);
   axis_weights<4>(fy, wy);
   axis_weights<4>(fz, wz);
   SplitTaps st;
-  split_taps(l, st);
+  split_taps_lut(lut, l, st);   // byte offsets of 8-byte entries
   rotate4(wx, st.t);
   rotate4(wz, st.r);
   const float cr = v.x * scale, ci = v.y * scale;
   // 4-byte weight words: two interleaved copies of the tile, one per 16-lane
   // half of each 32-lane LDS pass, so that the halves use the even and the
   // odd banks (the flush adds the two copies)
-  const int half = ((int)threadIdx.x >> 4) & 1;
+  const int half = (((int)threadIdx.x >> 4) & 1) * 4;   // bytes
   float yr[4], yi[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -335,11 +336,15 @@ __device__ __forceinline__ void bwd_scatter_split(const int l[3], float fx, floa
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const float wxz = wx[a] * wz[c];
-      const int col = st.xo[a] + st.zo[c];
+      const int col = st.xo[a] + st.zo[c];   // bytes: entry 8 col of the data tile, word pair of the weights
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        if constexpr (CH == CH_DATA) atomicAdd(&acc_t[col + 64 * b], fixed_pair(wxz, yr[b], yi[b]));
-        else atomicAdd(&acc_w[2 * (col + 64 * b) + half], (unsigned int)fixed_round(wxz, yr[b]));
+        if constexpr (CH == CH_DATA)
+          atomicAdd(reinterpret_cast<unsigned long long*>(reinterpret_cast<char*>(acc_t) + col) + 64 * b,
+                    fixed_pair(wxz, yr[b], yi[b]));
+        else
+          atomicAdd(reinterpret_cast<unsigned int*>(reinterpret_cast<char*>(acc_w) + col + half) + 128 * b,
+                    (unsigned int)fixed_round(wxz, yr[b]));
       }
     }
 }
@@ -359,6 +364,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
   __shared__ unsigned int acc_w[DATA ? 1 : WSIZE];
   __shared__ EnumShared<WINDOW, BNW> es;
   __shared__ float win_scale[SCALE_BATCH];
+  __shared__ std::conditional_t<SPLIT, SplitLut, char> lut;   // tap tables of the bank-split tile
 
   const int w = blockIdx.x, vsel = blockIdx.y;
   if (w >= bg.nwork) return;
@@ -392,6 +398,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
     if constexpr (DATA) acc_t[i] = 0ull;
     else acc_w[i] = 0u;
   }
+  if constexpr (SPLIT) split_lut_fill(lut);
   __syncthreads();
 
   {
@@ -484,7 +491,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
               if (mpk[u] & 1) {
                 const int l[3] = {(mpk[u] >> 1) & 15, (mpk[u] >> 5) & 15, (mpk[u] >> 9) & 15};
                 const float2 v = DATA && shifts ? cmulc(mph[u], mv[u]) : mv[u];   // conj(phi) * Y
-                bwd_scatter_split<CH>(l, mf[u][0], mf[u][1], mf[u][2], v, acc_t, acc_w, scale);
+                bwd_scatter_split<CH>(lut, l, mf[u][0], mf[u][1], mf[u][2], v, acc_t, acc_w, scale);
               }
             } else {
               bwd_scatter<NT, CH>(mpk[u], mf[u][0], mf[u][1], mf[u][2], mv[u], acc_t, acc_w, scale);
