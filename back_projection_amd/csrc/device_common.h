@@ -31,6 +31,12 @@ __device__ __forceinline__ float safe_floor(float p) {
   return fminf(fmaxf(floorf(p), -16777216.0f), 16777216.0f);
 }
 
+// p - floor(p) in one instruction (v_fract_f32), for the finite sample
+// coordinates of owned pixels; where p - floor(p) rounds up to 1 (p a tiny
+// negative number) it returns the largest float below 1, a weight change of
+// one ulp.
+__device__ __forceinline__ float frac_of(float p) { return __builtin_amdgcn_fractf(p); }
+
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
   return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }

@@ -166,7 +166,7 @@ __device__ __forceinline__ float2 tap_value(const float2* __restrict__ V, const 
 // mod 16) is (x & 3) + 4 (z & 3), whatever y is.  A pixel's 4^3 taps cover
 // every (x & 3, z & 3) pair once per y row, and a lane may visit its x taps
 // and its z taps in any cyclic order: with the order chosen from the lane's
-// slot in its group of 16 (split_taps), the 16 lanes of a group touch 16
+// slot in its group of 16 (SplitTaps), the 16 lanes of a group touch 16
 // distinct bank pairs at every step of the tap loop, for any pixels they
 // hold.  Measured on random footprints: the conflict-free LDS rate (15.3
 // reads and 10.3 64-bit atomics per clock per CU, against 7.1 and 7.0 for
@@ -200,53 +200,22 @@ __device__ __forceinline__ int tile_addr(int x, int y, int z) {
 // rotations t (x) and r (z) that put the lane's step-(a, c) tap in bank pair
 // ((lane + a) & 3) + 4 (((lane >> 2) + c) & 3).  Step (a, b, c) reads the tap
 // (l0 + ((a + t) & 3), l1 + b, l2 + ((c + r) & 3)), whose x and z weights are
-// those of index (a + t) & 3 and (c + r) & 3, at tile entry xo[a] + zo[c] +
-// 64 b (zo includes l1).
+// those of index (a + t) & 3 and (c + r) & 3, at byte offset xo[a] + zo[c] +
+// 512 b in a tile of 8-byte entries (zo includes l1; split_taps_lut).
 struct SplitTaps {
   int xo[4], zo[4];
   int t, r;
 };
-__device__ __forceinline__ void split_taps(const int l[3], SplitTaps& s) {
-  const int lane = (int)threadIdx.x;
-  s.t = ((lane & 3) - l[0]) & 3;
-  s.r = (((lane >> 2) & 3) - l[2]) & 3;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    s.xo[j] = split_x(l[0] + ((j + s.t) & 3));
-    s.zo[j] = split_z(l[2] + ((j + s.r) & 3)) + 64 * l[1];
-  }
-}
 
-// The same tap order as byte offsets (ES bytes per entry), derived without a
-// shift per column: the step-a tap has x mod 4 = s = (lane + a) & 3 and lies
-// in [l0, l0 + 3], so x = 4 (l0 >> 2) + s + (s < (l0 & 3) ? 4 : 0), and
-// split_x(x) = s + 16 (x >> 2); likewise for z.  The residues s are lane
-// constants that the compiler keeps in registers: fewer instructions per
-// pixel, more registers (used by the forward, which has them to spare).
-template <int ES>
-__device__ __forceinline__ void split_taps_bytes(const int l[3], SplitTaps& s) {
-  const int lane = (int)threadIdx.x;
-  const int u = lane & 3, v = (lane >> 2) & 3;
-  s.t = (u - l[0]) & 3;
-  s.r = (v - l[2]) & 3;
-  const int x4 = l[0] & 3, z4 = l[2] & 3;
-  const int bx = (l[0] >> 2) * (16 * ES), bz = (l[2] >> 2) * (1024 * ES) + l[1] * (64 * ES);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int sx = (u + j) & 3, sz = (v + j) & 3;
-    s.xo[j] = bx + sx * ES + (sx < x4 ? 16 * ES : 0);
-    s.zo[j] = bz + sz * (4 * ES) + (sz < z4 ? 1024 * ES : 0);
-  }
-}
-
-// The same tap order from two lane tables in LDS (byte offsets of 8-byte
+// The offsets come from two lane tables in LDS (byte offsets of 8-byte
 // entries), so that a pixel's 8 offsets cost two 16-byte LDS reads and a few
 // adds instead of per-step residue arithmetic and selects (which issue at
-// half the rate of FP32 FMAs): for lane slot u and x4 = l0 & 3, x[4 u + x4]
-// holds 8 (s + 16 [s < x4]) for the steps j = 0..3, s = (u + j) & 3, so the
-// step-j x tap of a pixel whose first tap is l0 lies at 128 (l0 >> 2) plus
-// that entry; z[4 v + z4] likewise holds 8 (4 s + 1024 [s < z4]) with
-// s = (v + j) & 3, added to 8192 (l2 >> 2) + 512 l1.
+// half the rate of FP32 FMAs).  The step-j x tap has x mod 4 = s = (u + j) & 3
+// (u = lane & 3) and lies in [l0, l0 + 3], so x = 4 (l0 >> 2) + s + 4 [s < x4]
+// with x4 = l0 & 3: table entry x[4 u + x4] holds 8 (s + 16 [s < x4]) for
+// j = 0..3, added to 128 (l0 >> 2); z[4 v + z4] likewise holds
+// 8 (4 s + 1024 [s < z4]) with s = (v + j) & 3, added to 8192 (l2 >> 2) +
+// 512 l1.
 struct SplitLut {
   int4 x[16];
   int4 z[16];
@@ -392,7 +361,7 @@ __device__ __forceinline__ void interp_tile_w(const T* tile, const int l[3], con
 
 // Value (and, with DERIV, the partial derivatives along x, y, z) of the
 // cubic interpolant from a bank-split tile, in this lane's tap order
-// (split_taps); l = floor(p) - lo is the tile entry of the first tap, w* / d*
+// (SplitTaps); l = floor(p) - lo is the tile entry of the first tap, w* / d*
 // the axis weights (and derivatives) in tap order.  Contracts y within each
 // column, then x within each plane, then z.
 template <bool DERIV, typename T>

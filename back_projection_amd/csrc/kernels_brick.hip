@@ -142,9 +142,9 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
             // each lane interpolates its own pixel, in its slot's tap order
             if (cu.act) {
               float wx[4], wy[4], wz[4];
-              axis_weights<4>(cu.p[0] - floorf(cu.p[0]), wx);
-              axis_weights<4>(cu.p[1] - floorf(cu.p[1]), wy);
-              axis_weights<4>(cu.p[2] - floorf(cu.p[2]), wz);
+              axis_weights<4>(frac_of(cu.p[0]), wx);
+              axis_weights<4>(frac_of(cu.p[1]), wy);
+              axis_weights<4>(frac_of(cu.p[2]), wz);
               T I;
               interp_split<false>(tile, lut, cu.l, wx, wy, wz, wx, wy, wz, I, (T*)nullptr);
               if constexpr (CPLX) {
@@ -159,7 +159,7 @@ __global__ void __launch_bounds__(256) k_fwd_brick(const T* __restrict__ vol, co
             int pk = 0, key = -1;
             if (cu.act) {
 #pragma unroll
-              for (int a = 0; a < 3; ++a) f[a] = cu.p[a] - floorf(cu.p[a]);
+              for (int a = 0; a < 3; ++a) f[a] = frac_of(cu.p[a]);
               pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
               key = (cu.l[0] + cu.l[1] * Tl::SY + cu.l[2] * Tl::SZ) & 15;
             }
@@ -305,8 +305,7 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
               if constexpr (CPLX) uc = U[cu.k];
               if constexpr (REAL) ur = Ur[cu.k];
               float wx[4], wy[4], wz[4], dx[4], dy[4], dz[4];
-              const float fx = cu.p[0] - floorf(cu.p[0]), fy = cu.p[1] - floorf(cu.p[1]),
-                          fz = cu.p[2] - floorf(cu.p[2]);
+              const float fx = frac_of(cu.p[0]), fy = frac_of(cu.p[1]), fz = frac_of(cu.p[2]);
               axis_weights<4>(fx, wx);
               axis_weights<4>(fy, wy);
               axis_weights<4>(fz, wz);
@@ -323,7 +322,7 @@ __global__ void __launch_bounds__(256, (CPLX && REAL) ? 2 : 4) k_grad_brick(cons
               if constexpr (CPLX) uc = U[cu.k];
               if constexpr (REAL) ur = Ur[cu.k];
 #pragma unroll
-              for (int a = 0; a < 3; ++a) f[a] = cu.p[a] - floorf(cu.p[a]);
+              for (int a = 0; a < 3; ++a) f[a] = frac_of(cu.p[a]);
               pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
               key = (cu.l[0] + cu.l[1] * Tl::SY + cu.l[2] * Tl::SZ) & 15;
             }

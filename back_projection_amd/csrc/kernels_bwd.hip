@@ -305,7 +305,7 @@ __device__ __forceinline__ void bwd_scatter(int pk, float fx, float fy, float fz
 }
 
 // One cubic pixel into a bank-split accumulator tile, in this lane's own tap
-// order (split_taps): l = floor(p) - lo, f the fractional parts of p, v as
+// order (SplitTaps): l = floor(p) - lo, f the fractional parts of p, v as
 // above.  The y weights are folded into the value once per row, the x and z
 // weights once per column.
 template <int CH>
@@ -462,7 +462,7 @@ __global__ void __launch_bounds__(BTHREADS, CH == CH_DATA ? BWD_MIN_WAVES : BWD_
             if (cu.act) {
               if (DATA && shifts) ph = shift_phase(cu.kx, cu.ky, cu.sx, cu.sy, g.inv_h);
 #pragma unroll
-              for (int a = 0; a < 3; ++a) f[a] = cu.p[a] - floorf(cu.p[a]);
+              for (int a = 0; a < 3; ++a) f[a] = frac_of(cu.p[a]);
               pk = 1 | (cu.l[0] << 1) | (cu.l[1] << 5) | (cu.l[2] << 9);
               key = (cu.l[0] + cu.l[1] * TSY + cu.l[2] * TSZ) & 15;
             }

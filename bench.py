@@ -75,14 +75,14 @@ def op_rates(ms, poses, n_in, tap_bytes_per_pixel, flops_per_pixel):
 # reported when the digest of the 3D kernel sources matches, else null.
 TRAFFIC = {
     # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
-    "forward": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
-               "fetch_bytes": 313328357, "write_bytes": 1183363373},
-    "backward": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
-                "fetch_bytes": 3003352158, "write_bytes": 301123584},
-    "gradient": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
-                "fetch_bytes": 2783904331, "write_bytes": 120424608},
-    "fold": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
-            "fetch_bytes": 223195806, "write_bytes": 33390592},
+    "forward": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+               "fetch_bytes": 313479764, "write_bytes": 1183410253},
+    "backward": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+                "fetch_bytes": 3003110149, "write_bytes": 301123570},
+    "gradient": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+                "fetch_bytes": 2783879413, "write_bytes": 120424608},
+    "fold": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+            "fetch_bytes": 223195580, "write_bytes": 33390592},
 }
 
 # VALU issue per kernel class, from the SQ counter pass of the same sessions
@@ -92,12 +92,12 @@ TRAFFIC = {
 # clocks); the FMA probe of --peaks reaches 1.72.
 VALU_ISSUE = {
     # profiles/brick_kernels_D128_cubic_counters.txt
-    "forward": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
-                "valu_per_cu_clock": 1.111},
-    "backward": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
-                 "valu_per_cu_clock": 0.847},
-    "gradient": {"sources_sha256": "6f7ec322909f8689f33e14aa9e77d5d01c55f4798aad2dbf75f979cb1f38757e",
-                 "valu_per_cu_clock": 1.355},
+    "forward": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+                "valu_per_cu_clock": 1.056},
+    "backward": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+                 "valu_per_cu_clock": 0.799},
+    "gradient": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+                 "valu_per_cu_clock": 1.339},
 }
 VALU_ISSUE_PEAK = 2.0
 VALU_ISSUE_PROBE = 1.72
