@@ -368,9 +368,7 @@ template <bool DERIV, typename T>
 __device__ __forceinline__ void interp_split(const T* tile, const SplitLut& lut, const int l[3], const float wx_in[4],
                                              const float wy[4], const float wz_in[4], const float dx_in[4],
                                              const float dy[4], const float dz_in[4], T& I, T* dI) {
-  // tap offsets: in bytes for the value-only gather (fewer instructions, a
-  // few more registers), in entries for the derivative gather, which has no
-  // registers to spare (measured: the byte form made it 4 % slower)
+  // tap offsets in bytes from the lane tables (halved for 4-byte entries)
   static_assert(sizeof(T) == 8 || sizeof(T) == 4, "complex or real tile entries");
   SplitTaps st;
   split_taps_lut(lut, l, st);

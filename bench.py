@@ -75,13 +75,13 @@ def op_rates(ms, poses, n_in, tap_bytes_per_pixel, flops_per_pixel):
 # reported when the digest of the 3D kernel sources matches, else null.
 TRAFFIC = {
     # profiles/brick_kernels_D128_cubic_step_hbm_traffic.txt
-    "forward": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+    "forward": {"sources_sha256": "20cee6cd58dcf625671338898f6e16074eacfe26b088f23712dc2566fbc66e4a",
                "fetch_bytes": 313479764, "write_bytes": 1183410253},
-    "backward": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+    "backward": {"sources_sha256": "20cee6cd58dcf625671338898f6e16074eacfe26b088f23712dc2566fbc66e4a",
                 "fetch_bytes": 3003110149, "write_bytes": 301123570},
-    "gradient": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+    "gradient": {"sources_sha256": "20cee6cd58dcf625671338898f6e16074eacfe26b088f23712dc2566fbc66e4a",
                 "fetch_bytes": 2783879413, "write_bytes": 120424608},
-    "fold": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+    "fold": {"sources_sha256": "20cee6cd58dcf625671338898f6e16074eacfe26b088f23712dc2566fbc66e4a",
             "fetch_bytes": 223195580, "write_bytes": 33390592},
 }
 
@@ -92,11 +92,11 @@ TRAFFIC = {
 # clocks); the FMA probe of --peaks reaches 1.72.
 VALU_ISSUE = {
     # profiles/brick_kernels_D128_cubic_counters.txt
-    "forward": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+    "forward": {"sources_sha256": "20cee6cd58dcf625671338898f6e16074eacfe26b088f23712dc2566fbc66e4a",
                 "valu_per_cu_clock": 1.056},
-    "backward": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+    "backward": {"sources_sha256": "20cee6cd58dcf625671338898f6e16074eacfe26b088f23712dc2566fbc66e4a",
                  "valu_per_cu_clock": 0.799},
-    "gradient": {"sources_sha256": "d8520b028dff4a49f4b9b708e21faa498dafc708c96239191d33f6ca6b89f078",
+    "gradient": {"sources_sha256": "20cee6cd58dcf625671338898f6e16074eacfe26b088f23712dc2566fbc66e4a",
                  "valu_per_cu_clock": 1.339},
 }
 VALU_ISSUE_PEAK = 2.0
